@@ -1,0 +1,181 @@
+/*
+ * moe_layer.h - C ABI of the MI355X (gfx950) MoE-layer library.
+ *
+ * One sparse Mixture-of-Experts layer: a router picks the top-k of E routed
+ * experts per token, each expert is a SwiGLU MLP whose weights are affine
+ * int4/int8 group-quantized and stored as one fixed-stride blob in a device
+ * slot pool, and a sigmoid-gated shared expert is added to the weighted sum.
+ *
+ * Sources (the pages describe the Swiftlet expert-streaming runtime):
+ *   - Swiftlet README translation, section "How it works": every layer routes
+ *     each token to 10 of 512 (80B) or 8 of 256 (35B) experts; the router and
+ *     shared expert are resident; routed experts are fixed-stride blobs, one
+ *     fetch per expert; hot experts live in a bounded slot pool.
+ *   - same page, section "Relation to TurboFieldfare": MLX affine int4/int8
+ *     group quantization computed on the GPU, byte-addressed kernels with
+ *     64-bit offsets for multi-GB shards, explicit hazard management.
+ *   - same page, section "Correctness": placement (cache or disk) never changes
+ *     the answer.
+ *
+ * The pages leave the formulas open; this library computes (readings):
+ *   w[r,c] = s[r, c/64] * q[r,c] + b[r, c/64]     q unsigned, groups of 64 along
+ *                                                 the input axis, int4 low nibble
+ *                                                 first in little-endian words
+ *   l = R x;  S = first k experts by (-l, id)     ties go to the lower id
+ *   p_i = exp(l_{S_i} - m) / sum_{j in S} exp(l_j - m),  m = max_{j in S} l_j
+ *   E(x) = Wd (silu(Wg x) * (Wu x))
+ *   y = sum_{i<k} p_i E_{S_i}(x) + sigmoid(g . x) E_shared(x)
+ *
+ * Blob format (own format; the pages give none).  Offsets inside one blob of
+ * intermediate size I (Q = I*H*bits/8 bytes, S = I*H/64 * sizeof(scale)):
+ *   [0,Q) gate codes [I,H]   [Q,2Q) up codes [I,H]   [2Q,3Q) down codes [H,I]
+ *   then gate/up/down scales (S bytes each), then gate/up/down biases (S each).
+ * Matrices are row-major [out, in].  The stride is the blob size rounded up to
+ * 4096 bytes.  Expert e starts at pool_base + slot_table[e] (a 64-bit byte
+ * offset).  The shared-expert buffer holds one blob with the shared
+ * intermediate size and, at byte offset shared_stride, the gate vector [H] in
+ * the activation dtype.
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or retains them.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work on it and return; nothing is synchronous unless stated.
+ *   - Return 0 (MOE_OK) or a negative MOE_E* code; moe_last_error() gives the
+ *     text (thread-local).  Arguments are checked on the host before any
+ *     device call; a rejected call enqueues nothing.
+ *   - Work is deterministic: the same inputs give bitwise identical outputs on
+ *     every call, and the output does not depend on where in the pool a blob
+ *     sits (no floating-point atomics).
+ */
+#ifndef MOE_LAYER_H
+#define MOE_LAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define MOE_OK 0
+#define MOE_EINVAL (-1)   /* bad descriptor, size, pointer or alignment        */
+#define MOE_ENODEV (-2)   /* no usable gfx950 device                            */
+#define MOE_EHIP (-3)     /* a HIP call or kernel launch failed                 */
+#define MOE_ENOMEM (-4)   /* workspace smaller than moe_workspace_bytes()       */
+#define MOE_ERANGE (-5)   /* a kernel saw a slot offset outside the pool, or an
+                             expert id outside [0, E); that pair was skipped    */
+#define MOE_ENOSPC (-6)   /* residency manager: more experts than slots         */
+
+/* Storage dtypes. */
+#define MOE_F32 0
+#define MOE_BF16 1
+
+/*
+ * Layer descriptor (plain value, caller-owned).
+ *   hidden        H; a power of two, 64 .. 4096
+ *   n_experts     E; 1 .. 1024
+ *   top_k         k; 1 .. min(E, 64)
+ *   inter         I, routed-expert intermediate size; power of two, 64 .. 4096
+ *   shared_inter  shared-expert intermediate size; power of two, 64 .. 4096
+ *   bits          4 or 8
+ *   group_size    must be 64
+ *   act_dtype     dtype of x, the router matrix and the shared gate vector
+ *   sb_dtype      dtype of the quantization scales and biases
+ *   out_dtype     dtype of out
+ *   blob_stride   bytes between consecutive slots; >= moe_blob_bytes(d, 0)
+ *                 and a multiple of 256
+ *   shared_stride byte offset of the gate vector in the shared buffer;
+ *                 >= moe_blob_bytes(d, 1) and a multiple of 256
+ *   pool_bytes    size of the pool in bytes; every slot offset used must
+ *                 satisfy 0 <= off, off % 256 == 0, off + blob bytes <= pool_bytes
+ */
+typedef struct moe_desc {
+  int32_t hidden;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t inter;
+  int32_t shared_inter;
+  int32_t bits;
+  int32_t group_size;
+  int32_t act_dtype;
+  int32_t sb_dtype;
+  int32_t out_dtype;
+  int64_t blob_stride;
+  int64_t shared_stride;
+  int64_t pool_bytes;
+} moe_desc;
+
+/* Unpadded size in bytes of one routed (shared == 0) or shared (shared != 0)
+ * blob for this descriptor; -1 if the descriptor is invalid.  Pure function. */
+int64_t moe_blob_bytes(const moe_desc* d, int32_t shared);
+
+/* Workspace bytes needed for calls with up to T_max tokens; 0 if the
+ * descriptor is invalid.  Pure function. */
+size_t moe_workspace_bytes(const moe_desc* d, int32_t T_max);
+
+/*
+ * Prepare a workspace for first use: clears its control words (error flags,
+ * counters) with a kernel on `stream`.  Call once after allocating it; every
+ * later call leaves the control words ready for the next call.
+ */
+int moe_workspace_init(void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Forward pass of one MoE layer.
+ *   d           layer descriptor
+ *   T           number of tokens, >= 0 (T == 0 enqueues nothing)
+ *   x           [T, H] activations, act_dtype, 16-byte aligned
+ *   router_w    [E, H] router matrix, act_dtype, row-major, 16-byte aligned
+ *   slot_table  [E] int64 byte offsets of each expert's blob in the pool
+ *   pool_base   base of the slot pool, 256-byte aligned
+ *   shared_w    shared-expert blob + gate vector (see above), 256-byte aligned
+ *   out         [T, H] output, out_dtype
+ *   workspace   device scratch of ws_bytes >= moe_workspace_bytes(d, T),
+ *               256-byte aligned, prepared once by moe_workspace_init; must
+ *               not be used by two calls that may run concurrently
+ *   topk_ids    optional [T, k] int32 output: chosen experts, descending logit
+ *   topk_w      optional [T, k] float32 output: renormalised weights
+ * Errors: MOE_EINVAL, MOE_ENOMEM, MOE_EHIP as above.  Out-of-range slot
+ * offsets are detected on the device (see moe_status_check).
+ */
+int moe_layer_forward(const moe_desc* d, int32_t T, const void* x, const void* router_w,
+                      const int64_t* slot_table, const void* pool_base, const void* shared_w,
+                      void* out, void* workspace, size_t ws_bytes, int32_t* topk_ids,
+                      float* topk_w, void* stream);
+
+/*
+ * First half of moe_layer_forward: router logits, top-k and renormalised
+ * weights into topk_ids [T, k] / topk_w [T, k] (both required).
+ */
+int moe_router_topk(const moe_desc* d, int32_t T, const void* x, const void* router_w,
+                    int32_t* topk_ids, float* topk_w, void* workspace, size_t ws_bytes,
+                    void* stream);
+
+/*
+ * Second half: experts and combine from given routing (topk_ids / topk_w, as
+ * written by moe_router_topk).  moe_router_topk followed by this call gives
+ * the same bits as moe_layer_forward.  An id outside [0, E) contributes
+ * nothing and raises MOE_ERANGE in moe_status_check.
+ */
+int moe_experts_forward(const moe_desc* d, int32_t T, const void* x, const int32_t* topk_ids,
+                        const float* topk_w, const int64_t* slot_table, const void* pool_base,
+                        const void* shared_w, void* out, void* workspace, size_t ws_bytes,
+                        void* stream);
+
+/*
+ * Synchronises `stream`, then reports and clears the device-side error flags
+ * of `workspace`: MOE_ERANGE if any kernel since the last check skipped a pair
+ * for a bad slot offset or expert id, else MOE_OK.  Blocking.
+ */
+int moe_status_check(void* workspace, void* stream);
+
+/* Text of the last error on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LAYER_H */

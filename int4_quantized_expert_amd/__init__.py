@@ -1,0 +1,24 @@
+"""MI355X (gfx950) MoE layer with int4/int8 group-quantized experts.
+
+Thin Python binding over the C ABI of libmoe_layer.so (include/moe_layer.h).
+All compute runs in the library's HIP kernels; PyTorch only provides device
+memory and streams.  Importing this package never falls back to anything else:
+if the library is missing, every call raises.
+"""
+
+from ._lib import (  # noqa: F401
+    MOE_BF16,
+    MOE_F32,
+    MoeDesc,
+    MoeError,
+    blob_bytes,
+    desc_for,
+    experts_forward,
+    layer_forward,
+    last_error,
+    lib,
+    router_topk,
+    status_check,
+    workspace_bytes,
+    workspace_init,
+)

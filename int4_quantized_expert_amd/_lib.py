@@ -1,0 +1,174 @@
+"""ctypes binding of libmoe_layer.so: argument marshalling only.
+
+Each function takes torch tensors that live on the GPU, passes their device
+pointers and byte sizes to the C entry point of the same name, and raises
+MoeError on a non-zero return code.  `stream` defaults to torch's current
+stream on the tensors' device.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_layer.so")
+
+MOE_F32 = 0
+MOE_BF16 = 1
+
+ERRORS = {
+    -1: "MOE_EINVAL",
+    -2: "MOE_ENODEV",
+    -3: "MOE_EHIP",
+    -4: "MOE_ENOMEM",
+    -5: "MOE_ERANGE",
+    -6: "MOE_ENOSPC",
+}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {message}")
+        self.code = code
+
+
+class MoeDesc(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32),
+        ("n_experts", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("inter", ctypes.c_int32),
+        ("shared_inter", ctypes.c_int32),
+        ("bits", ctypes.c_int32),
+        ("group_size", ctypes.c_int32),
+        ("act_dtype", ctypes.c_int32),
+        ("sb_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("blob_stride", ctypes.c_int64),
+        ("shared_stride", ctypes.c_int64),
+        ("pool_bytes", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(hipcc --offload-arch=gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        dp = ctypes.POINTER(MoeDesc)
+        L.moe_blob_bytes.argtypes = [dp, i32]
+        L.moe_blob_bytes.restype = i64
+        L.moe_workspace_bytes.argtypes = [dp, i32]
+        L.moe_workspace_bytes.restype = sz
+        L.moe_workspace_init.argtypes = [vp, sz, vp]
+        L.moe_workspace_init.restype = ctypes.c_int
+        L.moe_layer_forward.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+        L.moe_layer_forward.restype = ctypes.c_int
+        L.moe_router_topk.argtypes = [dp, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_router_topk.restype = ctypes.c_int
+        L.moe_experts_forward.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_experts_forward.restype = ctypes.c_int
+        L.moe_status_check.argtypes = [vp, vp]
+        L.moe_status_check.restype = ctypes.c_int
+        L.moe_last_error.argtypes = []
+        L.moe_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise MoeError(rc, last_error())
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _stream(stream, like=None):
+    if stream is None:
+        import torch
+        dev = like.device if like is not None else None
+        return torch.cuda.current_stream(dev).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def desc_for(hidden, n_experts, top_k, inter, shared_inter, bits=4, act="bf16", sb="bf16", out="f32",
+             pool_bytes=0, blob_stride=None, shared_stride=None) -> MoeDesc:
+    """Descriptor with strides defaulting to the blob size rounded up to 4096 bytes."""
+    code = {"f32": MOE_F32, "bf16": MOE_BF16}
+    d = MoeDesc(hidden, n_experts, top_k, inter, shared_inter, bits, 64, code[act], code[sb], code[out],
+                0, 0, pool_bytes)
+    d.blob_stride = 1 << 40   # placeholder so the size query validates
+    d.shared_stride = 1 << 40
+    d.pool_bytes = max(pool_bytes, 1 << 40)
+    rb = blob_bytes(d, False)
+    sb_ = blob_bytes(d, True)
+    d.blob_stride = blob_stride if blob_stride is not None else (rb + 4095) // 4096 * 4096
+    d.shared_stride = shared_stride if shared_stride is not None else (sb_ + 4095) // 4096 * 4096
+    d.pool_bytes = pool_bytes
+    return d
+
+
+def blob_bytes(d: MoeDesc, shared: bool) -> int:
+    n = lib().moe_blob_bytes(ctypes.byref(d), 1 if shared else 0)
+    if n < 0:
+        raise MoeError(-1, "invalid descriptor")
+    return n
+
+
+def workspace_bytes(d: MoeDesc, T_max: int) -> int:
+    n = lib().moe_workspace_bytes(ctypes.byref(d), T_max)
+    if n == 0:
+        raise MoeError(-1, "invalid descriptor or T_max")
+    return n
+
+
+def workspace_init(ws, stream=None) -> None:
+    _check(lib().moe_workspace_init(_ptr(ws), _nbytes(ws), _stream(stream, ws)))
+
+
+def layer_forward(d: MoeDesc, T: int, x, router_w, slot_table, pool, shared_w, out, ws,
+                  topk_ids=None, topk_w=None, stream=None) -> None:
+    _check(lib().moe_layer_forward(ctypes.byref(d), T, _ptr(x), _ptr(router_w), _ptr(slot_table), _ptr(pool),
+                                   _ptr(shared_w), _ptr(out), _ptr(ws), _nbytes(ws), _ptr(topk_ids),
+                                   _ptr(topk_w), _stream(stream, ws)))
+
+
+def router_topk(d: MoeDesc, T: int, x, router_w, topk_ids, topk_w, ws, stream=None) -> None:
+    _check(lib().moe_router_topk(ctypes.byref(d), T, _ptr(x), _ptr(router_w), _ptr(topk_ids), _ptr(topk_w),
+                                 _ptr(ws), _nbytes(ws), _stream(stream, ws)))
+
+
+def experts_forward(d: MoeDesc, T: int, x, topk_ids, topk_w, slot_table, pool, shared_w, out, ws,
+                    stream=None) -> None:
+    _check(lib().moe_experts_forward(ctypes.byref(d), T, _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(slot_table),
+                                     _ptr(pool), _ptr(shared_w), _ptr(out), _ptr(ws), _nbytes(ws),
+                                     _stream(stream, ws)))
+
+
+def status_check(ws, stream=None) -> None:
+    """Blocking: raises MoeError(MOE_ERANGE) if a kernel skipped a pair since the last check."""
+    _check(lib().moe_status_check(_ptr(ws), _stream(stream, ws)))

@@ -1,0 +1,208 @@
+// Host side of the C ABI declared in include/moe_layer.h: argument checks,
+// workspace layout and kernel sequencing.  Nothing here touches the device
+// before every argument has been checked.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "moe_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int ok() {
+  g_error.clear();
+  return MOE_OK;
+}
+
+bool pow2_in(int32_t v, int32_t lo, int32_t hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int64_t blob_bytes_raw(const moe_desc& d, int32_t inter) {
+  const int64_t q = static_cast<int64_t>(d.hidden) * inter * d.bits / 8;
+  const int64_t s = static_cast<int64_t>(d.hidden) * (inter / 64) * (d.sb_dtype == MOE_F32 ? 4 : 2);
+  return 3 * q + 6 * s;
+}
+
+// Checks the descriptor; returns MOE_OK or MOE_EINVAL with the reason set.
+int check_desc(const moe_desc* d) {
+  if (!d) return fail(MOE_EINVAL, "descriptor is NULL");
+  if (!pow2_in(d->hidden, 64, 2048)) return fail(MOE_EINVAL, "hidden=%d must be a power of two in [64, 2048]", d->hidden);
+  if (!pow2_in(d->inter, 64, 2048)) return fail(MOE_EINVAL, "inter=%d must be a power of two in [64, 2048]", d->inter);
+  if (!pow2_in(d->shared_inter, 64, 2048))
+    return fail(MOE_EINVAL, "shared_inter=%d must be a power of two in [64, 2048]", d->shared_inter);
+  if (d->n_experts < 1 || d->n_experts > 1024) return fail(MOE_EINVAL, "n_experts=%d must be in [1, 1024]", d->n_experts);
+  if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > 64)
+    return fail(MOE_EINVAL, "top_k=%d must be in [1, min(n_experts, 64)]", d->top_k);
+  if (d->bits != 4 && d->bits != 8) return fail(MOE_EINVAL, "bits=%d must be 4 or 8", d->bits);
+  if (d->group_size != 64) return fail(MOE_EINVAL, "group_size=%d must be 64", d->group_size);
+  for (int32_t dt : {d->act_dtype, d->sb_dtype, d->out_dtype})
+    if (dt != MOE_F32 && dt != MOE_BF16) return fail(MOE_EINVAL, "dtype code %d is neither MOE_F32 nor MOE_BF16", dt);
+  const int64_t rb = blob_bytes_raw(*d, d->inter), sb = blob_bytes_raw(*d, d->shared_inter);
+  if (d->blob_stride < rb || d->blob_stride % 256)
+    return fail(MOE_EINVAL, "blob_stride=%lld must be >= %lld and a multiple of 256", (long long)d->blob_stride,
+                (long long)rb);
+  if (d->shared_stride < sb || d->shared_stride % 256)
+    return fail(MOE_EINVAL, "shared_stride=%lld must be >= %lld and a multiple of 256", (long long)d->shared_stride,
+                (long long)sb);
+  if (d->pool_bytes < rb) return fail(MOE_EINVAL, "pool_bytes=%lld smaller than one blob", (long long)d->pool_bytes);
+  return MOE_OK;
+}
+
+int check_T(int32_t T) {
+  if (T < 0) return fail(MOE_EINVAL, "T=%d is negative", T);
+  if (T > 65536) return fail(MOE_EINVAL, "T=%d exceeds 65536", T);
+  return MOE_OK;
+}
+
+int check_ws(const moe_desc& d, int32_t T, const void* ws, size_t ws_bytes, moe::WsLayout* L) {
+  if (!ws) return fail(MOE_EINVAL, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_EINVAL, "workspace must be 256-byte aligned");
+  *L = moe::ws_layout(d, T);
+  if (ws_bytes < L->total)
+    return fail(MOE_ENOMEM, "workspace has %zu bytes, %zu needed for T=%d", ws_bytes, L->total, T);
+  return MOE_OK;
+}
+
+int finish(int rc) {
+  if (rc != MOE_OK) {
+    hipError_t e = hipGetLastError();
+    return fail(MOE_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_blob_bytes(const moe_desc* d, int32_t shared) {
+  if (check_desc(d) != MOE_OK) return -1;
+  return blob_bytes_raw(*d, shared ? d->shared_inter : d->inter);
+}
+
+size_t moe_workspace_bytes(const moe_desc* d, int32_t T_max) {
+  if (check_desc(d) != MOE_OK || check_T(T_max) != MOE_OK) return 0;
+  return moe::ws_layout(*d, T_max).total;
+}
+
+int moe_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
+  if (!workspace || !aligned(workspace, 256)) return fail(MOE_EINVAL, "workspace is NULL or not 256-byte aligned");
+  if (ws_bytes < 256) return fail(MOE_ENOMEM, "workspace smaller than its control block");
+  return finish(moe::launch_ws_init(static_cast<uint8_t*>(workspace), ws_bytes, static_cast<hipStream_t>(stream)));
+}
+
+int moe_router_topk(const moe_desc* d, int32_t T, const void* x, const void* router_w, int32_t* topk_ids,
+                    float* topk_w, void* workspace, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_desc(d)) || (rc = check_T(T))) return rc;
+  if (!x || !router_w || !topk_ids || !topk_w) return fail(MOE_EINVAL, "NULL x, router_w, topk_ids or topk_w");
+  if (!aligned(x, 16) || !aligned(router_w, 16)) return fail(MOE_EINVAL, "x and router_w must be 16-byte aligned");
+  moe::WsLayout L;
+  if ((rc = check_ws(*d, T, workspace, ws_bytes, &L))) return rc;
+  if (T == 0) return ok();
+  moe::Call c{};
+  c.d = *d;
+  c.T = T;
+  c.x = x;
+  c.router_w = router_w;
+  c.ws = static_cast<uint8_t*>(workspace);
+  c.L = L;
+  c.stream = static_cast<hipStream_t>(stream);
+  return finish(moe::launch_router_topk(c, topk_ids, topk_w));
+}
+
+int moe_experts_forward(const moe_desc* d, int32_t T, const void* x, const int32_t* topk_ids, const float* topk_w,
+                        const int64_t* slot_table, const void* pool_base, const void* shared_w, void* out,
+                        void* workspace, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_desc(d)) || (rc = check_T(T))) return rc;
+  if (!x || !topk_ids || !topk_w || !slot_table || !pool_base || !shared_w || !out)
+    return fail(MOE_EINVAL, "NULL input or output pointer");
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(slot_table, 8) || !aligned(pool_base, 256) ||
+      !aligned(shared_w, 256) || !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+    return fail(MOE_EINVAL, "misaligned pointer (x/out 16, slot_table 8, pool_base/shared_w 256)");
+  moe::WsLayout L;
+  if ((rc = check_ws(*d, T, workspace, ws_bytes, &L))) return rc;
+  if (T == 0) return ok();
+  moe::Call c{};
+  c.d = *d;
+  c.T = T;
+  c.x = x;
+  c.slot_table = slot_table;
+  c.pool = static_cast<const uint8_t*>(pool_base);
+  c.shared = static_cast<const uint8_t*>(shared_w);
+  c.out = out;
+  c.ws = static_cast<uint8_t*>(workspace);
+  c.L = L;
+  c.ids = topk_ids;
+  c.wts = topk_w;
+  c.stream = static_cast<hipStream_t>(stream);
+  return finish(moe::launch_experts(c));
+}
+
+int moe_layer_forward(const moe_desc* d, int32_t T, const void* x, const void* router_w, const int64_t* slot_table,
+                      const void* pool_base, const void* shared_w, void* out, void* workspace, size_t ws_bytes,
+                      int32_t* topk_ids, float* topk_w, void* stream) {
+  int rc;
+  if ((rc = check_desc(d)) || (rc = check_T(T))) return rc;
+  if (!x || !router_w || !slot_table || !pool_base || !shared_w || !out)
+    return fail(MOE_EINVAL, "NULL input or output pointer");
+  if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(out, 16) || !aligned(slot_table, 8) ||
+      !aligned(pool_base, 256) || !aligned(shared_w, 256))
+    return fail(MOE_EINVAL, "misaligned pointer (x/router_w/out 16, slot_table 8, pool_base/shared_w 256)");
+  moe::WsLayout L;
+  if ((rc = check_ws(*d, T, workspace, ws_bytes, &L))) return rc;
+  if (T == 0) return ok();
+  moe::Call c{};
+  c.d = *d;
+  c.T = T;
+  c.x = x;
+  c.router_w = router_w;
+  c.slot_table = slot_table;
+  c.pool = static_cast<const uint8_t*>(pool_base);
+  c.shared = static_cast<const uint8_t*>(shared_w);
+  c.out = out;
+  c.ws = static_cast<uint8_t*>(workspace);
+  c.L = L;
+  c.ids = reinterpret_cast<const int32_t*>(c.ws + L.ids);
+  c.wts = reinterpret_cast<const float*>(c.ws + L.wts);
+  c.stream = static_cast<hipStream_t>(stream);
+  if ((rc = moe::launch_router_topk(c, topk_ids, topk_w))) return finish(rc);
+  return finish(moe::launch_experts(c));
+}
+
+int moe_status_check(void* workspace, void* stream) {
+  if (!workspace || !aligned(workspace, 256)) return fail(MOE_EINVAL, "workspace is NULL or not 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t flags = 0, zero = 0;
+  if (hipMemcpyAsync(&flags, workspace, 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return fail(MOE_EHIP, "status read failed: %s", hipGetErrorString(hipGetLastError()));
+  if (flags) {
+    if (hipMemcpyAsync(workspace, &zero, 4, hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return fail(MOE_EHIP, "status clear failed: %s", hipGetErrorString(hipGetLastError()));
+    return fail(MOE_ERANGE, "a kernel skipped a pair: slot offset outside the pool or expert id outside [0, E)");
+  }
+  return ok();
+}
+
+const char* moe_last_error(void) { return g_error.c_str(); }
+
+}  // extern "C"

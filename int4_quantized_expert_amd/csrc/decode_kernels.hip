@@ -1,0 +1,762 @@
+// Decode-path kernels of the MoE layer (gfx950, wave64).
+//
+// One call runs, on the caller's stream:
+//   router_logits -> topk -> dispatch -> gateup -> down -> combine
+// Routing follows the Swiftlet README translation ("How it works": each token
+// goes to k of E experts per layer, plus the always-on shared expert); the
+// expert weights are read from fixed-stride blobs through 64-bit slot offsets
+// ("Relation to TurboFieldfare": byte-addressed kernels, 64-bit offsets).
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Lane layout for a row of `cols` codes split into 32-code segments:
+// spr = cols / 32 segments per row.  If spr >= 64 one wave covers one row and
+// lane L takes segments L, L + 64, ... (nsl = spr / 64 of them).  Otherwise a
+// wave covers 64 / spr rows at once and lane L takes segment L % spr of row
+// L / spr.
+struct RowLanes {
+  int spr;      // segments per row
+  int rpp;      // rows per wave pass
+  int width;    // lanes summed per row
+  int sub_row;  // this lane's row within a pass
+  int seg0;     // this lane's first segment
+};
+
+__device__ __forceinline__ RowLanes row_lanes(int cols, int lane) {
+  RowLanes r;
+  r.spr = cols / kSegCodes;
+  if (r.spr >= kWave) {
+    r.rpp = 1;
+    r.width = kWave;
+    r.sub_row = 0;
+    r.seg0 = lane;
+  } else {
+    r.rpp = kWave / r.spr;
+    r.width = r.spr;
+    r.sub_row = lane / r.spr;
+    r.seg0 = lane % r.spr;
+  }
+  return r;
+}
+
+// Multi-token segment dot: converts each code once and feeds NT FMA chains per
+// parity; per token the result is bitwise the single-token seg_qdot.
+template <int BITS, int NT>
+__device__ __forceinline__ void seg_qdot_nt(const Seg<BITS>& s_in, const float (&v)[NT][kSegCodes], float (&out)[NT]) {
+  // Opaque copy of the packed codes: keeps the compiler from hoisting the
+  // code->float conversions out of the callers' token loops, which would hold
+  // 32 floats per segment in registers instead of 4 words.
+  Seg<BITS> s;
+#pragma unroll
+  for (int i = 0; i < BITS / 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t w = s_in.w[i][j];
+      asm volatile("" : "+v"(w));
+      s.w[i][j] = w;
+    }
+  }
+  float a0[NT], a1[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) { a0[t] = 0.f; a1[t] = 0.f; }
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w = s.w[0][k];
+      const uint32_t lo = w & 0x0f0f0f0fu;
+      const uint32_t hi = (w >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float qe = static_cast<float>((lo >> (8 * j)) & 0xffu);
+        const float qo = static_cast<float>((hi >> (8 * j)) & 0xffu);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          a0[t] = fmaf(qe, v[t][8 * k + 2 * j], a0[t]);
+          a1[t] = fmaf(qo, v[t][8 * k + 2 * j + 1], a1[t]);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t w = s.w[h][k];
+        const float q0 = static_cast<float>(w & 0xffu);
+        const float q1 = static_cast<float>((w >> 8) & 0xffu);
+        const float q2 = static_cast<float>((w >> 16) & 0xffu);
+        const float q3 = static_cast<float>(w >> 24);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          a0[t] = fmaf(q0, v[t][16 * h + 4 * k + 0], a0[t]);
+          a1[t] = fmaf(q1, v[t][16 * h + 4 * k + 1], a1[t]);
+          a0[t] = fmaf(q2, v[t][16 * h + 4 * k + 2], a0[t]);
+          a1[t] = fmaf(q3, v[t][16 * h + 4 * k + 3], a1[t]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) out[t] = a0[t] + a1[t];
+}
+
+// Blob plane offsets (see include/moe_layer.h): Q bytes of codes and S bytes
+// of scales per matrix, all three matrices the same size.
+struct Planes {
+  int64_t q;   // codes bytes of one matrix
+  int64_t s;   // scale bytes of one matrix
+  int64_t blob;
+};
+
+__host__ __device__ inline Planes planes_of(int hidden, int inter, int bits, int sb_dtype) {
+  Planes p;
+  p.q = static_cast<int64_t>(hidden) * inter * bits / 8;
+  p.s = static_cast<int64_t>(hidden) * (inter / 64) * (sb_dtype == kF32 ? 4 : 2);
+  p.blob = 3 * p.q + 6 * p.s;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// Router logits: l[t, e] = sum_h x[t, h] R[e, h] in float32 (FMA chain over
+// the lane's codes in order, then the lane butterfly).  Rows 0..E-1.
+template <int ACT, int NSL>
+__global__ __launch_bounds__(256) void k_router_logits(const void* __restrict__ x, const void* __restrict__ router,
+                                                      float* __restrict__ logits, int T, int H, int E) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const RowLanes rl = row_lanes(H, lane);
+  const int e = wave * rl.rpp + rl.sub_row;
+  const bool active = e < E;
+  const size_t act_sz = ACT == kF32 ? 4 : 2;
+  float r[NSL][kSegCodes];
+  if (active) {
+    const uint8_t* row = static_cast<const uint8_t*>(router) + static_cast<size_t>(e) * H * act_sz;
+#pragma unroll
+    for (int n = 0; n < NSL; ++n) load_act_seg<ACT>(row, rl.seg0 + n * kWave, r[n]);
+  }
+  for (int t = 0; t < T; ++t) {
+    float acc = 0.f;
+    if (active) {
+      const uint8_t* xr = static_cast<const uint8_t*>(x) + static_cast<size_t>(t) * H * act_sz;
+#pragma unroll
+      for (int n = 0; n < NSL; ++n) {
+        float v[kSegCodes];
+        load_act_seg<ACT>(xr, rl.seg0 + n * kWave, v);
+#pragma unroll
+        for (int c = 0; c < kSegCodes; ++c) acc = fmaf(v[c], r[n][c], acc);
+      }
+    }
+    acc = group_sum(acc, rl.width);
+    if (active && (lane % rl.width) == 0) logits[static_cast<size_t>(t) * E + e] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Top-k per token (one wave per token): k rounds of a wave arg-max over
+// (logit descending, id ascending), then p_i = exp(l_i - l_0) / sum_j exp(l_j - l_0)
+// with the sum taken in rank order.
+constexpr int kTopkPerLane = 16;   // E <= 1024
+
+__device__ __forceinline__ bool better(float v, int id, float bv, int bid) {
+  return v > bv || (v == bv && id < bid);
+}
+
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
+                                              int32_t* __restrict__ ids, float* __restrict__ wts,
+                                              int32_t* __restrict__ ids2, float* __restrict__ wts2) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  if (t >= T) return;
+  float v[kTopkPerLane];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int j = 0; j < kTopkPerLane; ++j) {
+    const int e = lane + j * kWave;
+    v[j] = e < E ? logits[static_cast<size_t>(t) * E + e] : -INFINITY;
+  }
+  float my_v = 0.f;
+  int my_id = -1;
+  float top = 0.f;
+  for (int i = 0; i < k; ++i) {
+    float bv = -INFINITY;
+    int bid = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < kTopkPerLane; ++j) {
+      const int e = lane + j * kWave;
+      if (e < E && !((taken >> j) & 1u) && better(v[j], e, bv, bid)) { bv = v[j]; bid = e; }
+    }
+#pragma unroll
+    for (int m = kWave / 2; m > 0; m >>= 1) {
+      const float ov = __shfl_xor(bv, m, kWave);
+      const int oid = __shfl_xor(bid, m, kWave);
+      if (better(ov, oid, bv, bid)) { bv = ov; bid = oid; }
+    }
+    if ((bid & (kWave - 1)) == lane) taken |= 1u << (bid / kWave);
+    if (lane == i) { my_v = bv; my_id = bid; }
+    if (i == 0) top = bv;
+  }
+  const float ex = lane < k ? expf(my_v - top) : 0.f;
+  float sum = 0.f;
+  for (int i = 0; i < k; ++i) sum += __shfl(ex, i, kWave);
+  if (lane < k) {
+    const float p = ex / sum;
+    const size_t o = static_cast<size_t>(t) * k + lane;
+    ids[o] = my_id;
+    wts[o] = p;
+    if (ids2) ids2[o] = my_id;
+    if (wts2) wts2[o] = p;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch (one block of 1024 threads): group the T*k (token, rank) pairs by
+// expert.  Distinct experts are listed in ascending id; within an expert the
+// pair order is unspecified (every pair writes its own output rows, so the
+// order does not change any value).  Also forms sigmoid(g . x_t) per token.
+constexpr int kDispatchThreads = 1024;
+
+template <int ACT, int NSL>
+__global__ __launch_bounds__(kDispatchThreads) void k_dispatch(const int32_t* __restrict__ ids, int T, int k, int E,
+                                                               int H, const void* __restrict__ x,
+                                                               const void* __restrict__ gvec, float* __restrict__ gate,
+                                                               int32_t* __restrict__ ucount, int32_t* __restrict__ uniq,
+                                                               int32_t* __restrict__ ustart, int32_t* __restrict__ plist,
+                                                               uint32_t* __restrict__ flags) {
+  __shared__ int hist[kDispatchThreads];
+  __shared__ int cursor[kDispatchThreads];
+  __shared__ int wsum_c[kDispatchThreads / kWave];
+  __shared__ int wsum_u[kDispatchThreads / kWave];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = tid / kWave;
+  const int npairs = T * k;
+  hist[tid] = 0;
+  __syncthreads();
+  for (int p = tid; p < npairs; p += kDispatchThreads) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    else raise_error(flags, kErrRange);
+  }
+  __syncthreads();
+  // exclusive scans of counts and of "expert used"
+  const int c = hist[tid];
+  const int u = c > 0 ? 1 : 0;
+  int ic = c, iu = u;
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    const int oc = __shfl_up(ic, m, kWave);
+    const int ou = __shfl_up(iu, m, kWave);
+    if (lane >= m) { ic += oc; iu += ou; }
+  }
+  if (lane == kWave - 1) { wsum_c[wid] = ic; wsum_u[wid] = iu; }
+  __syncthreads();
+  if (wid == 0) {
+    int vc = lane < kDispatchThreads / kWave ? wsum_c[lane] : 0;
+    int vu = lane < kDispatchThreads / kWave ? wsum_u[lane] : 0;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+      const int oc = __shfl_up(vc, m, kWave);
+      const int ou = __shfl_up(vu, m, kWave);
+      if (lane >= m) { vc += oc; vu += ou; }
+    }
+    if (lane < kDispatchThreads / kWave) { wsum_c[lane] = vc; wsum_u[lane] = vu; }
+  }
+  __syncthreads();
+  const int base_c = wid > 0 ? wsum_c[wid - 1] : 0;
+  const int base_u = wid > 0 ? wsum_u[wid - 1] : 0;
+  const int start = base_c + ic - c;
+  const int rank = base_u + iu - u;
+  if (u) {
+    uniq[rank] = tid;
+    ustart[rank] = start;
+  }
+  cursor[tid] = start;
+  if (tid == kDispatchThreads - 1) {
+    const int U = base_u + iu;
+    *ucount = U;
+    ustart[U] = base_c + ic;
+  }
+  __syncthreads();
+  for (int p = tid; p < npairs; p += kDispatchThreads) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) {
+      const int pos = atomicAdd(&cursor[e], 1);
+      plist[pos] = p;
+    }
+  }
+  // gate: sigmoid(g . x_t), lane L covers segments L, L + 64, ...
+  const size_t act_sz = ACT == kF32 ? 4 : 2;
+  const int nseg = H / kSegCodes;
+  for (int t = wid; t < T; t += kDispatchThreads / kWave) {
+    float acc = 0.f;
+    const uint8_t* xr = static_cast<const uint8_t*>(x) + static_cast<size_t>(t) * H * act_sz;
+#pragma unroll
+    for (int n = 0; n < NSL; ++n) {
+      const int sg = lane + n * kWave;
+      if (sg < nseg) {
+        float a[kSegCodes], g[kSegCodes];
+        load_act_seg<ACT>(xr, sg, a);
+        load_act_seg<ACT>(gvec, sg, g);
+#pragma unroll
+        for (int cc = 0; cc < kSegCodes; ++cc) acc = fmaf(a[cc], g[cc], acc);
+      }
+    }
+    acc = group_sum(acc, kWave);
+    if (lane == 0) gate[t] = sigmoid(acc);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gate/up GEMV + SwiGLU.  Block = 4 waves; a wave owns `npass` passes of
+// row_lanes rows of one expert and processes every token routed to it in
+// chunks of TOKC, writing h[pair, r] = silu(Wg x)_r * (Wu x)_r.
+// Blocks [0, umax * bpe_r) take routed experts (expert slot u = block / bpe_r,
+// idle if u >= U); the rest take the shared expert for all T tokens.
+struct GateUpArgs {
+  const void* x;
+  const int64_t* slot_table;
+  const uint8_t* pool;
+  const uint8_t* shared;
+  const int32_t* ucount;
+  const int32_t* uniq;
+  const int32_t* ustart;
+  const int32_t* plist;
+  float* h;
+  uint32_t* flags;
+  int64_t pool_bytes;
+  int T, k, H, I, SI, umax, bpe_r, bpe_s, hstride;
+};
+
+constexpr int kMaxPass = 4;
+
+template <int BITS, int SB, int ACT, int NSL, int TOKC>
+__global__ __launch_bounds__(256) void k_gateup(GateUpArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const bool shared = blockIdx.x >= a.umax * a.bpe_r;
+  int rb, u = 0, e = -1;
+  if (!shared) {
+    u = blockIdx.x / a.bpe_r;
+    rb = blockIdx.x % a.bpe_r;
+    if (u >= *a.ucount) return;
+    e = a.uniq[u];
+  } else {
+    rb = blockIdx.x - a.umax * a.bpe_r;
+  }
+  const int rows = shared ? a.SI : a.I;
+  const Planes pl = planes_of(a.H, rows, BITS, SB);
+  const uint8_t* blob;
+  bool valid = true;
+  if (shared) {
+    blob = a.shared;
+  } else {
+    const int64_t off = a.slot_table[e];
+    valid = slot_ok(off, pl.blob, a.pool_bytes);
+    blob = a.pool + (valid ? off : 0);
+    if (!valid && threadIdx.x == 0) raise_error(a.flags, kErrRange);
+  }
+  const RowLanes rl = row_lanes(a.H, lane);
+  const int npass = rl.rpp >= kMaxPass ? 1 : kMaxPass / rl.rpp;
+  const int rows_per_wave = npass * rl.rpp;
+  const int row0 = (rb * 4 + wave) * rows_per_wave;
+  const int64_t row_bytes = static_cast<int64_t>(a.H) * BITS / 8;
+  const int seg_bytes = kSegCodes * BITS / 8;
+  const int gpr = a.H / 64;   // groups per row
+
+  Seg<BITS> cg[kMaxPass][NSL], cu[kMaxPass][NSL];
+  float sg[kMaxPass][NSL], bg[kMaxPass][NSL], su[kMaxPass][NSL], bu[kMaxPass][NSL];
+#pragma unroll
+  for (int p = 0; p < kMaxPass; ++p) {
+    const int r = row0 + p * rl.rpp + rl.sub_row;
+    if (p < npass && r < rows && valid) {
+#pragma unroll
+      for (int n = 0; n < NSL; ++n) {
+        const int seg = rl.seg0 + n * kWave;
+        const int64_t qo = r * row_bytes + static_cast<int64_t>(seg) * seg_bytes;
+        cg[p][n] = load_codes<BITS>(blob + qo);
+        cu[p][n] = load_codes<BITS>(blob + pl.q + qo);
+        const size_t si = static_cast<size_t>(r) * gpr + seg / 2;
+        sg[p][n] = load_scalar<SB>(blob + 3 * pl.q, si);
+        su[p][n] = load_scalar<SB>(blob + 3 * pl.q + pl.s, si);
+        bg[p][n] = load_scalar<SB>(blob + 3 * pl.q + 3 * pl.s, si);
+        bu[p][n] = load_scalar<SB>(blob + 3 * pl.q + 4 * pl.s, si);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < NSL; ++n) {
+#pragma unroll
+        for (int i = 0; i < BITS / 4; ++i) { cg[p][n].w[i] = u32x4{0, 0, 0, 0}; cu[p][n].w[i] = u32x4{0, 0, 0, 0}; }
+        sg[p][n] = su[p][n] = bg[p][n] = bu[p][n] = 0.f;
+      }
+    }
+  }
+  // token list
+  int n_tok, first = 0;
+  if (shared) {
+    n_tok = a.T;
+  } else {
+    first = a.ustart[u];
+    n_tok = a.ustart[u + 1] - first;
+  }
+  const size_t act_sz = ACT == kF32 ? 4 : 2;
+  for (int c0 = 0; c0 < n_tok; c0 += TOKC) {
+    float xv[TOKC][kSegCodes];
+    float xs[TOKC][NSL];
+    int hrow[TOKC];
+    float accg[kMaxPass][TOKC], accu[kMaxPass][TOKC];
+#pragma unroll
+    for (int p = 0; p < kMaxPass; ++p)
+#pragma unroll
+      for (int t = 0; t < TOKC; ++t) { accg[p][t] = 0.f; accu[p][t] = 0.f; }
+#pragma unroll
+    for (int n = 0; n < NSL; ++n) {
+      const int seg = rl.seg0 + n * kWave;
+#pragma unroll
+      for (int t = 0; t < TOKC; ++t) {
+        const int ci = c0 + t < n_tok ? c0 + t : n_tok - 1;
+        int tok;
+        if (shared) {
+          tok = ci;
+          hrow[t] = a.T * a.k + ci;
+        } else {
+          const int pair = a.plist[first + ci];
+          tok = pair / a.k;
+          hrow[t] = pair;
+        }
+        load_act_seg<ACT>(static_cast<const uint8_t*>(a.x) + static_cast<size_t>(tok) * a.H * act_sz, seg, xv[t]);
+        xs[t][n] = seg_sum(xv[t]);
+      }
+#pragma unroll
+      for (int p = 0; p < kMaxPass; ++p) {
+        if (p < npass) {
+          float qg[TOKC], qu[TOKC];
+          seg_qdot_nt<BITS, TOKC>(cg[p][n], xv, qg);
+          seg_qdot_nt<BITS, TOKC>(cu[p][n], xv, qu);
+#pragma unroll
+          for (int t = 0; t < TOKC; ++t) {
+            accg[p][t] += seg_value(sg[p][n], bg[p][n], qg[t], xs[t][n]);
+            accu[p][t] += seg_value(su[p][n], bu[p][n], qu[t], xs[t][n]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < kMaxPass; ++p) {
+      if (p < npass) {
+        const int r = row0 + p * rl.rpp + rl.sub_row;
+#pragma unroll
+        for (int t = 0; t < TOKC; ++t) {
+          const float g = group_sum(accg[p][t], rl.width);
+          const float v = group_sum(accu[p][t], rl.width);
+          if (c0 + t < n_tok && r < rows && (lane % rl.width) == 0) {
+            a.h[static_cast<size_t>(hrow[t]) * a.hstride + r] = valid ? silu(g) * v : 0.f;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Down projection per (expert, row block): partial[pair, n] = Wd[n, :] . h[pair, :].
+// Same lane layout over rows of `inter` codes.
+struct DownArgs {
+  const int64_t* slot_table;
+  const uint8_t* pool;
+  const uint8_t* shared;
+  const int32_t* ucount;
+  const int32_t* uniq;
+  const int32_t* ustart;
+  const int32_t* plist;
+  const float* h;
+  float* partial;
+  uint32_t* flags;
+  int64_t pool_bytes;
+  int T, k, H, I, SI, umax, bpe, hstride;
+};
+
+template <int BITS, int SB, int NSL>
+__global__ __launch_bounds__(256) void k_down(DownArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const bool shared = blockIdx.x >= a.umax * a.bpe;
+  int rb, u = 0, e = -1;
+  if (!shared) {
+    u = blockIdx.x / a.bpe;
+    rb = blockIdx.x % a.bpe;
+    if (u >= *a.ucount) return;
+    e = a.uniq[u];
+  } else {
+    rb = blockIdx.x - a.umax * a.bpe;
+  }
+  const int inter = shared ? a.SI : a.I;
+  const Planes pl = planes_of(a.H, inter, BITS, SB);
+  const uint8_t* blob;
+  bool valid = true;
+  if (shared) {
+    blob = a.shared;
+  } else {
+    const int64_t off = a.slot_table[e];
+    valid = slot_ok(off, pl.blob, a.pool_bytes);
+    blob = a.pool + (valid ? off : 0);
+  }
+  const RowLanes rl = row_lanes(inter, lane);
+  const int npass = rl.rpp >= kMaxPass ? 1 : kMaxPass / rl.rpp;
+  const int rows_per_wave = npass * rl.rpp;
+  const int row0 = (rb * 4 + wave) * rows_per_wave;
+  const int64_t row_bytes = static_cast<int64_t>(inter) * BITS / 8;
+  const int seg_bytes = kSegCodes * BITS / 8;
+  const int gpr = inter / 64;
+  const uint8_t* dq = blob + 2 * pl.q;
+  const uint8_t* ds = blob + 3 * pl.q + 2 * pl.s;
+  const uint8_t* db = blob + 3 * pl.q + 5 * pl.s;
+
+  Seg<BITS> cd[kMaxPass][NSL];
+  float sd[kMaxPass][NSL], bd[kMaxPass][NSL];
+#pragma unroll
+  for (int p = 0; p < kMaxPass; ++p) {
+    const int r = row0 + p * rl.rpp + rl.sub_row;
+    if (p < npass && r < a.H && valid) {
+#pragma unroll
+      for (int n = 0; n < NSL; ++n) {
+        const int seg = rl.seg0 + n * kWave;
+        cd[p][n] = load_codes<BITS>(dq + r * row_bytes + static_cast<int64_t>(seg) * seg_bytes);
+        const size_t si = static_cast<size_t>(r) * gpr + seg / 2;
+        sd[p][n] = load_scalar<SB>(ds, si);
+        bd[p][n] = load_scalar<SB>(db, si);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < NSL; ++n) {
+#pragma unroll
+        for (int i = 0; i < BITS / 4; ++i) cd[p][n].w[i] = u32x4{0, 0, 0, 0};
+        sd[p][n] = bd[p][n] = 0.f;
+      }
+    }
+  }
+  int n_pair, first = 0;
+  if (shared) {
+    n_pair = a.T;
+  } else {
+    first = a.ustart[u];
+    n_pair = a.ustart[u + 1] - first;
+  }
+  for (int ci = 0; ci < n_pair; ++ci) {
+    const int hrow = shared ? a.T * a.k + ci : a.plist[first + ci];
+    const float* hr = a.h + static_cast<size_t>(hrow) * a.hstride;
+    float acc[kMaxPass];
+#pragma unroll
+    for (int p = 0; p < kMaxPass; ++p) acc[p] = 0.f;
+#pragma unroll
+    for (int n = 0; n < NSL; ++n) {
+      float hv[1][kSegCodes];
+      load_f32_seg(hr, rl.seg0 + n * kWave, hv[0]);
+      const float hs = seg_sum(hv[0]);
+#pragma unroll
+      for (int p = 0; p < kMaxPass; ++p) {
+        if (p < npass) {
+          float q[1];
+          seg_qdot_nt<BITS, 1>(cd[p][n], hv, q);
+          acc[p] += seg_value(sd[p][n], bd[p][n], q[0], hs);
+        }
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < kMaxPass; ++p) {
+      if (p < npass) {
+        const int r = row0 + p * rl.rpp + rl.sub_row;
+        const float v = group_sum(acc[p], rl.width);
+        if (r < a.H && (lane % rl.width) == 0) {
+          a.partial[static_cast<size_t>(hrow) * a.H + r] = valid ? v : 0.f;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine: y[t, n] = sum_{i<k} p[t,i] partial[t k + i, n] (i ascending, FMA
+// chain) then + sigmoid(g.x_t) partial_shared[t, n].  Pairs whose id is out of
+// range contribute nothing.
+template <int OUT>
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ partial, const int32_t* __restrict__ ids,
+                                                 const float* __restrict__ wts, const float* __restrict__ gate,
+                                                 void* __restrict__ out, int T, int k, int H, int E) {
+  const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<size_t>(T) * H) return;
+  const int t = static_cast<int>(idx / H);
+  const int n = static_cast<int>(idx % H);
+  float acc = 0.f;
+  for (int i = 0; i < k; ++i) {
+    const int e = ids[t * k + i];
+    if (e >= 0 && e < E) acc = fmaf(wts[t * k + i], partial[(static_cast<size_t>(t) * k + i) * H + n], acc);
+  }
+  acc = fmaf(gate[t], partial[(static_cast<size_t>(T) * k + t) * H + n], acc);
+  if constexpr (OUT == kF32) {
+    static_cast<float*>(out)[idx] = acc;
+  } else {
+    static_cast<uint16_t*>(out)[idx] = f32_to_bf16(acc);
+  }
+}
+
+__global__ void k_fill_u32(uint32_t* p, size_t n, uint32_t v) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers.
+
+static int last_launch_error() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int launch_ws_init(uint8_t* ws, size_t bytes, hipStream_t stream) {
+  const size_t n = 256 / 4;
+  (void)bytes;
+  hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, stream, reinterpret_cast<uint32_t*>(ws), n, 0u);
+  return last_launch_error();
+}
+
+int launch_router_topk(const Call& c, int32_t* ids2, float* wts2) {
+  const moe_desc& d = c.d;
+  float* logits = reinterpret_cast<float*>(c.ws + c.L.logits);
+  int32_t* ids = reinterpret_cast<int32_t*>(c.ws + c.L.ids);
+  float* wts = reinterpret_cast<float*>(c.ws + c.L.wts);
+  const int spr = d.hidden / kSegCodes;
+  const int rpp = spr >= kWave ? 1 : kWave / spr;
+  const int nsl = spr > kWave ? spr / kWave : 1;
+  const int waves = (d.n_experts + rpp - 1) / rpp;
+  const dim3 grid((waves + 3) / 4), block(256);
+#define ROUTER(ACT, NSL) \
+  hipLaunchKernelGGL((k_router_logits<ACT, NSL>), grid, block, 0, c.stream, c.x, c.router_w, logits, c.T, d.hidden, d.n_experts)
+  (void)nsl;
+  if (d.act_dtype == kF32) ROUTER(kF32, 1); else ROUTER(kBF16, 1);
+#undef ROUTER
+  hipLaunchKernelGGL(k_topk, dim3((c.T + 3) / 4), dim3(256), 0, c.stream, logits, c.T, d.n_experts, d.top_k, ids, wts,
+                     ids2, wts2);
+  return last_launch_error();
+}
+
+int launch_experts(const Call& c) {
+  const moe_desc& d = c.d;
+  uint32_t* flags = reinterpret_cast<uint32_t*>(c.ws + c.L.ctrl);
+  float* gate = reinterpret_cast<float*>(c.ws + c.L.gate);
+  int32_t* ucount = reinterpret_cast<int32_t*>(c.ws + c.L.ucount);
+  int32_t* uniq = reinterpret_cast<int32_t*>(c.ws + c.L.uniq);
+  int32_t* ustart = reinterpret_cast<int32_t*>(c.ws + c.L.ustart);
+  int32_t* plist = reinterpret_cast<int32_t*>(c.ws + c.L.plist);
+  float* h = reinterpret_cast<float*>(c.ws + c.L.h);
+  float* partial = reinterpret_cast<float*>(c.ws + c.L.partial);
+  const void* gvec = c.shared + d.shared_stride;
+
+  // dispatch + gate
+#define DISPATCH(ACT, NSL)                                                                                      \
+  hipLaunchKernelGGL((k_dispatch<ACT, NSL>), dim3(1), dim3(kDispatchThreads), 0, c.stream, c.ids, c.T, d.top_k, \
+                     d.n_experts, d.hidden, c.x, gvec, gate, ucount, uniq, ustart, plist, flags)
+  if (d.act_dtype == kF32) DISPATCH(kF32, 1); else DISPATCH(kBF16, 1);
+#undef DISPATCH
+
+  // gate/up
+  {
+    const int spr = d.hidden / kSegCodes;
+    const int rpp = spr >= kWave ? 1 : kWave / spr;
+    const int npass = rpp >= kMaxPass ? 1 : kMaxPass / rpp;
+    const int rpb = 4 * npass * rpp;
+    GateUpArgs a;
+    a.x = c.x;
+    a.slot_table = c.slot_table;
+    a.pool = c.pool;
+    a.shared = c.shared;
+    a.ucount = ucount;
+    a.uniq = uniq;
+    a.ustart = ustart;
+    a.plist = plist;
+    a.h = h;
+    a.flags = flags;
+    a.pool_bytes = d.pool_bytes;
+    a.T = c.T;
+    a.k = d.top_k;
+    a.H = d.hidden;
+    a.I = d.inter;
+    a.SI = d.shared_inter;
+    a.umax = c.L.umax;
+    a.bpe_r = (d.inter + rpb - 1) / rpb;
+    a.bpe_s = (d.shared_inter + rpb - 1) / rpb;
+    a.hstride = c.L.hstride;
+    const dim3 grid(a.umax * a.bpe_r + a.bpe_s), block(256);
+#define GATEUP(BITS, SB, ACT, NSL, TOKC) hipLaunchKernelGGL((k_gateup<BITS, SB, ACT, NSL, TOKC>), grid, block, 0, c.stream, a)
+#define GATEUP_T(BITS, SB, ACT, NSL) \
+  do { if (c.T == 1) GATEUP(BITS, SB, ACT, NSL, 1); else GATEUP(BITS, SB, ACT, NSL, 2); } while (0)
+#define GATEUP_N(BITS, SB, ACT) GATEUP_T(BITS, SB, ACT, 1)
+#define GATEUP_A(BITS, SB) \
+  do { if (d.act_dtype == kF32) GATEUP_N(BITS, SB, kF32); else GATEUP_N(BITS, SB, kBF16); } while (0)
+#define GATEUP_S(BITS) \
+  do { if (d.sb_dtype == kF32) GATEUP_A(BITS, kF32); else GATEUP_A(BITS, kBF16); } while (0)
+    if (d.bits == 4) GATEUP_S(4); else GATEUP_S(8);
+#undef GATEUP_S
+#undef GATEUP_A
+#undef GATEUP_N
+#undef GATEUP_T
+#undef GATEUP
+  }
+  // down
+  {
+    const int rpp_r = (d.inter / kSegCodes) >= kWave ? 1 : kWave / (d.inter / kSegCodes);
+    const int rpp_s = (d.shared_inter / kSegCodes) >= kWave ? 1 : kWave / (d.shared_inter / kSegCodes);
+    const int np_r = rpp_r >= kMaxPass ? 1 : kMaxPass / rpp_r;
+    const int np_s = rpp_s >= kMaxPass ? 1 : kMaxPass / rpp_s;
+    const int rpb_r = 4 * np_r * rpp_r, rpb_s = 4 * np_s * rpp_s;
+    DownArgs a;
+    a.slot_table = c.slot_table;
+    a.pool = c.pool;
+    a.shared = c.shared;
+    a.ucount = ucount;
+    a.uniq = uniq;
+    a.ustart = ustart;
+    a.plist = plist;
+    a.h = h;
+    a.partial = partial;
+    a.flags = flags;
+    a.pool_bytes = d.pool_bytes;
+    a.T = c.T;
+    a.k = d.top_k;
+    a.H = d.hidden;
+    a.I = d.inter;
+    a.SI = d.shared_inter;
+    a.umax = c.L.umax;
+    a.bpe = (d.hidden + rpb_r - 1) / rpb_r;
+    a.hstride = c.L.hstride;
+    const int bpe_s = (d.hidden + rpb_s - 1) / rpb_s;
+    const dim3 grid(a.umax * a.bpe + bpe_s), block(256);
+#define DOWN(BITS, SB) hipLaunchKernelGGL((k_down<BITS, SB, 1>), grid, block, 0, c.stream, a)
+#define DOWN_S(BITS) do { if (d.sb_dtype == kF32) DOWN(BITS, kF32); else DOWN(BITS, kBF16); } while (0)
+    if (d.bits == 4) DOWN_S(4); else DOWN_S(8);
+#undef DOWN_S
+#undef DOWN
+  }
+  // combine
+  {
+    const size_t n = static_cast<size_t>(c.T) * d.hidden;
+    const dim3 grid(static_cast<unsigned>((n + 255) / 256)), block(256);
+    if (d.out_dtype == kF32)
+      hipLaunchKernelGGL(k_combine<kF32>, grid, block, 0, c.stream, partial, c.ids, c.wts, gate, c.out, c.T, d.top_k,
+                         d.hidden, d.n_experts);
+    else
+      hipLaunchKernelGGL(k_combine<kBF16>, grid, block, 0, c.stream, partial, c.ids, c.wts, gate, c.out, c.T,
+                         d.top_k, d.hidden, d.n_experts);
+  }
+  return last_launch_error();
+}
+
+}  // namespace moe

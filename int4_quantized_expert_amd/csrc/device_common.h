@@ -1,0 +1,180 @@
+// Device helpers shared by the MoE-layer kernels (gfx950, wave64).
+//
+// Numerics contract used by every kernel, so that different launch shapes of
+// the same step give the same bits:
+//   * A "segment" is 32 consecutive codes of one matrix row: 16 bytes of int4
+//     (four little-endian words, low nibble first) or 32 bytes of int8.  A
+//     group of 64 codes is two segments, so one segment has one scale/bias.
+//   * Segment value = fmaf(s, qx, b * xs), where qx = sum_c q_c v_c is formed
+//     as two float32 FMA chains (even and odd codes, each in code order) added
+//     at the end, and xs = sum_c v_c is a float32 add chain in code order.
+//     This is w.v with w = s q + b regrouped per group (affine dequantisation,
+//     Swiftlet README translation, "Relation to TurboFieldfare").
+//   * A row's segments are summed per lane in segment order, then across the
+//     lanes of the row with an xor butterfly, which leaves the bitwise same
+//     total on every lane of the row.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum : int { kF32 = 0, kBF16 = 1 };
+
+constexpr int kWave = 64;
+constexpr int kSegCodes = 32;
+
+// Error flag bits kept in the workspace control words.
+constexpr uint32_t kErrRange = 1u;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float32 -> bfloat16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <int DT>
+__device__ __forceinline__ float load_scalar(const void* base, size_t idx) {
+  if constexpr (DT == kF32) {
+    return static_cast<const float*>(base)[idx];
+  } else {
+    return bf16_to_f32(static_cast<const uint16_t*>(base)[idx]);
+  }
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *static_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+}
+
+// 32 activation values of one segment -> float registers.
+template <int ACT>
+__device__ __forceinline__ void load_act_seg(const void* row, int seg, float (&v)[kSegCodes]) {
+  if constexpr (ACT == kF32) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(row) + seg * kSegCodes);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      u32x4 w = p[i];
+      v[4 * i + 0] = __uint_as_float(w[0]);
+      v[4 * i + 1] = __uint_as_float(w[1]);
+      v[4 * i + 2] = __uint_as_float(w[2]);
+      v[4 * i + 3] = __uint_as_float(w[3]);
+    }
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(row) + seg * kSegCodes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x4 w = p[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * i + 2 * j + 0] = __uint_as_float(w[j] << 16);
+        v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+      }
+    }
+  }
+}
+
+// 32 float32 values (e.g. an h segment) from global memory.
+__device__ __forceinline__ void load_f32_seg(const float* row, int seg, float (&v)[kSegCodes]) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(row + seg * kSegCodes);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    u32x4 w = p[i];
+    v[4 * i + 0] = __uint_as_float(w[0]);
+    v[4 * i + 1] = __uint_as_float(w[1]);
+    v[4 * i + 2] = __uint_as_float(w[2]);
+    v[4 * i + 3] = __uint_as_float(w[3]);
+  }
+}
+
+__device__ __forceinline__ float seg_sum(const float (&v)[kSegCodes]) {
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kSegCodes; ++c) s += v[c];
+  return s;
+}
+
+// Packed codes of one segment: one u32x4 for int4, two for int8.
+template <int BITS>
+struct Seg {
+  u32x4 w[BITS / 4];
+};
+
+template <int BITS>
+__device__ __forceinline__ Seg<BITS> load_codes(const uint8_t* p) {
+  Seg<BITS> s;
+#pragma unroll
+  for (int i = 0; i < BITS / 4; ++i) s.w[i] = load16_stream(p + 16 * i);
+  return s;
+}
+
+// qx = sum_c q_c v_c (two FMA chains: even and odd codes).
+template <int BITS>
+__device__ __forceinline__ float seg_qdot(const Seg<BITS>& s, const float (&v)[kSegCodes]) {
+  float a0 = 0.f, a1 = 0.f;
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w = s.w[0][k];
+      const uint32_t lo = w & 0x0f0f0f0fu;          // codes 8k, 8k+2, 8k+4, 8k+6
+      const uint32_t hi = (w >> 4) & 0x0f0f0f0fu;   // codes 8k+1, 8k+3, 8k+5, 8k+7
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a0 = fmaf(static_cast<float>((lo >> (8 * j)) & 0xffu), v[8 * k + 2 * j], a0);
+        a1 = fmaf(static_cast<float>((hi >> (8 * j)) & 0xffu), v[8 * k + 2 * j + 1], a1);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t w = s.w[h][k];   // codes 16h+4k .. 16h+4k+3
+        a0 = fmaf(static_cast<float>(w & 0xffu), v[16 * h + 4 * k + 0], a0);
+        a1 = fmaf(static_cast<float>((w >> 8) & 0xffu), v[16 * h + 4 * k + 1], a1);
+        a0 = fmaf(static_cast<float>((w >> 16) & 0xffu), v[16 * h + 4 * k + 2], a0);
+        a1 = fmaf(static_cast<float>(w >> 24), v[16 * h + 4 * k + 3], a1);
+      }
+    }
+  }
+  return a0 + a1;
+}
+
+__device__ __forceinline__ float seg_value(float s, float b, float qx, float xs) {
+  return fmaf(s, qx, b * xs);
+}
+
+// Sum over aligned groups of `width` lanes (power of two <= 64); every lane of
+// a group ends with the same bits.
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int m = width >> 1; m > 0; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
+
+__device__ __forceinline__ float sigmoid(float a) { return 1.0f / (1.0f + expf(-a)); }
+
+__device__ __forceinline__ void raise_error(uint32_t* flags, uint32_t bit) {
+  __hip_atomic_fetch_or(flags, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A blob offset is usable if it is non-negative, 256-byte aligned and the
+// whole blob fits in the pool.
+__device__ __forceinline__ bool slot_ok(int64_t off, int64_t blob_bytes, int64_t pool_bytes) {
+  return off >= 0 && (off & 255) == 0 && off <= pool_bytes - blob_bytes;
+}
+
+}  // namespace moe

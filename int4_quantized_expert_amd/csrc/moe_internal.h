@@ -1,0 +1,80 @@
+// Internal declarations shared by the host API and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_layer.h"
+
+namespace moe {
+
+// Byte layout of the caller's workspace for calls with up to T_max tokens.
+// Every region starts on a 256-byte boundary.
+struct WsLayout {
+  size_t ctrl;       // uint32 control words: [0] error flags
+  size_t logits;     // [T, E] float32 router logits
+  size_t ids;        // [T, k] int32 chosen experts
+  size_t wts;        // [T, k] float32 renormalised weights
+  size_t gate;       // [T] float32 sigmoid(g . x)
+  size_t ucount;     // int32 number of distinct experts U
+  size_t uniq;       // [min(T k, E)] int32 distinct experts, ascending id
+  size_t ustart;     // [min(T k, E) + 1] int32 start of each expert's pair list
+  size_t plist;      // [T k] int32 pair indices (t * k + i) grouped by expert
+  size_t h;          // [T k + T, max(I, SI)] float32 SwiGLU activations
+  size_t partial;    // [T k + T, H] float32 per-pair down projections
+  size_t total;
+  int32_t umax;      // min(T k, E)
+  int32_t hstride;   // max(I, SI)
+};
+
+inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+inline WsLayout ws_layout(const moe_desc& d, int32_t T) {
+  WsLayout L{};
+  const size_t Tk = static_cast<size_t>(T) * d.top_k;
+  const int32_t umax = static_cast<int32_t>(Tk < static_cast<size_t>(d.n_experts) ? Tk : d.n_experts);
+  const int32_t hs = d.inter > d.shared_inter ? d.inter : d.shared_inter;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes > 0 ? bytes : 1); return at; };
+  L.ctrl = take(256);
+  L.logits = take(static_cast<size_t>(T) * d.n_experts * 4);
+  L.ids = take(Tk * 4);
+  L.wts = take(Tk * 4);
+  L.gate = take(static_cast<size_t>(T) * 4);
+  L.ucount = take(4);
+  L.uniq = take(static_cast<size_t>(umax) * 4);
+  L.ustart = take((static_cast<size_t>(umax) + 1) * 4);
+  L.plist = take(Tk * 4);
+  L.h = take((Tk + T) * static_cast<size_t>(hs) * 4);
+  L.partial = take((Tk + T) * static_cast<size_t>(d.hidden) * 4);
+  L.total = o;
+  L.umax = umax;
+  L.hstride = hs;
+  return L;
+}
+
+// Per-call view of the inputs handed to the launchers.
+struct Call {
+  moe_desc d;
+  int32_t T;
+  const void* x;
+  const void* router_w;
+  const int64_t* slot_table;
+  const uint8_t* pool;
+  const uint8_t* shared;
+  void* out;
+  uint8_t* ws;
+  WsLayout L;
+  const int32_t* ids;     // routing used by the expert kernels
+  const float* wts;
+  int32_t* ids_out;       // optional extra copies of the routing
+  float* wts_out;
+  hipStream_t stream;
+};
+
+int launch_router_topk(const Call& c, int32_t* ids_dst, float* wts_dst);
+int launch_experts(const Call& c);
+int launch_ws_init(uint8_t* ws, size_t bytes, hipStream_t stream);
+
+}  // namespace moe

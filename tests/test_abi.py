@@ -1,0 +1,101 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/moe_layer.h, and rejects bad arguments on the host before
+any device call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import int4_quantized_expert_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for f in sorted(os.listdir(inc)):
+        if f.endswith(".h"):
+            text = open(os.path.join(inc, f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "moe_layer_forward" in names and len(names) >= 8
+    lib = M.lib()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+
+
+def good_desc(**kw):
+    d = M.desc_for(2048, 512, 10, 512, 512, 4, "bf16", "bf16", "f32", pool_bytes=512 * 1769472)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_sizes_of_named_shapes():
+    d = good_desc()
+    assert M.blob_bytes(d, False) == 1769472
+    assert d.blob_stride == 1769472
+    d8 = M.desc_for(2048, 256, 8, 512, 512, 8, "bf16", "bf16", "f32", pool_bytes=1 << 34)
+    assert M.blob_bytes(d8, False) == 3342336
+    dt = M.desc_for(256, 16, 2, 128, 128, 4, "f32", "f32", "f32", pool_bytes=1 << 20)
+    assert M.blob_bytes(dt, True) == 61440
+    assert M.workspace_bytes(d, 8) > M.workspace_bytes(d, 1) > 0
+
+
+@pytest.mark.parametrize("field,value", [
+    ("hidden", 1000), ("hidden", 4096), ("inter", 96), ("n_experts", 0), ("n_experts", 2048),
+    ("top_k", 0), ("top_k", 513), ("bits", 2), ("group_size", 32), ("act_dtype", 7),
+    ("blob_stride", 1769472 - 256), ("blob_stride", 1769472 + 100), ("shared_stride", 4096),
+    ("pool_bytes", 100),
+])
+def test_bad_descriptor_rejected(field, value):
+    d = good_desc(**{field: value})
+    buf = ctypes.create_string_buffer(1 << 16)
+    p = ctypes.addressof(buf) // 256 * 256 + 256
+    rc = M.lib().moe_layer_forward(ctypes.byref(d), 1, p, p, p, p, p, p, p, 1 << 10, None, None, None)
+    assert rc == -1
+    assert M.last_error()
+
+
+def test_null_and_misaligned_pointers_rejected():
+    d = good_desc()
+    buf = ctypes.create_string_buffer(1 << 16)
+    p = ctypes.addressof(buf) // 256 * 256 + 256
+    L = M.lib()
+    assert L.moe_layer_forward(ctypes.byref(d), 1, None, p, p, p, p, p, p, 1 << 12, None, None, None) == -1
+    assert L.moe_layer_forward(ctypes.byref(d), 1, p + 2, p, p, p, p, p, p, 1 << 12, None, None, None) == -1
+    assert L.moe_layer_forward(ctypes.byref(d), 1, p, p, p, p + 16, p, p, p, 1 << 12, None, None, None) == -1
+    assert L.moe_router_topk(ctypes.byref(d), 1, p, p, None, p, p, 1 << 12, None) == -1
+
+
+def test_small_workspace_is_enomem_and_negative_T_einval():
+    d = good_desc()
+    buf = ctypes.create_string_buffer(1 << 16)
+    p = ctypes.addressof(buf) // 256 * 256 + 256
+    L = M.lib()
+    need = M.workspace_bytes(d, 8)
+    assert L.moe_layer_forward(ctypes.byref(d), 8, p, p, p, p, p, p, p, need - 1, None, None, None) == -4
+    assert L.moe_layer_forward(ctypes.byref(d), -1, p, p, p, p, p, p, p, need, None, None, None) == -1
+    assert M.lib().moe_workspace_bytes(ctypes.byref(d), -3) == 0
+
+
+def test_zero_tokens_enqueue_nothing():
+    """T == 0 returns MOE_OK after validation without any device call."""
+    d = good_desc()
+    buf = ctypes.create_string_buffer(1 << 16)
+    p = ctypes.addressof(buf) // 256 * 256 + 256
+    need = M.workspace_bytes(d, 0)
+    assert M.lib().moe_layer_forward(ctypes.byref(d), 0, p, p, p, p, p, p, p, need, None, None, None) == 0
+
+
+def test_synth_device_fill_library_loads():
+    from synth import gpu
+    assert hasattr(gpu.lib(), "synth_fill_blobs")
