@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""MoE-layer decode benchmark on one MI355X.
+
+Workload (default): the 80B-A3B-shaped stack decode -- 48 layers, each with 512
+routed int4 g64 experts (bf16 scales/biases, 1,769,472-byte blobs) resident in
+one 43.5 GB HBM pool, top-10 routing with Zipf(1.1)-skewed popularity, a shared
+expert with a sigmoid gate, T tokens per step (default 1).  One step is one
+token step through all 48 layers in order, each layer one moe_layer_forward
+call; steps are captured as HIP graphs and replayed.  Inputs are synthetic and
+seeded (synth); the pool is filled in place by the device-side generator.
+
+Prints one JSON line: layer-tokens/s as `value`, the roofline of the timed
+launch unit (algorithmic bytes / HIP-event duration against 8 TB/s) and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s (% of 8 TB/s) at 80B-shape decode"
+
+WORKLOADS = {
+    "80b_stack_decode": ("80b", 48),
+    "35b_rotation_decode": ("35b", 40),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64, help="timed token steps (each through every layer)")
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--tokens", type=int, default=1, help="tokens per step (decode batch)")
+    ap.add_argument("--workload", default="80b_stack_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                          "(the multi-GPU expert-parallel layout is a design note only)"}))
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "launched with WORLD_SIZE > 1; this benchmark is single-GPU"}))
+        sys.exit(2)
+
+    import torch
+
+    import int4_quantized_expert_amd as M
+    import synth
+    from synth import gpu as sgpu
+
+    preset, n_layers = WORKLOADS[args.workload]
+    geo = synth.PRESETS[preset]
+    T, K, W = args.tokens, args.steps, args.warmup
+    S = K + W
+    H, E, k = geo.hidden, geo.n_experts, geo.top_k
+    stride = geo.blob_stride
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---------------------------------------------------------------- inputs
+    t0 = time.time()
+    pool = torch.empty(n_layers * E * stride, dtype=torch.uint8, device=dev)
+    for l in range(n_layers):
+        sgpu.fill_blobs(geo, pool.data_ptr() + l * E * stride, E, args.seed, l, 0, stream=stream.cuda_stream)
+    shared_bytes = geo.shared_bytes
+    shared_host = np.concatenate([synth.make_shared(geo, args.seed, l) for l in range(n_layers)])
+    shared = torch.from_numpy(shared_host).to(dev)
+    x_host = np.empty((n_layers, S * T, H), dtype=np.uint16)
+    r_host = np.empty((n_layers, E, H), dtype=np.uint16)
+    for l in range(n_layers):
+        x_host[l] = synth.tokens(geo, args.seed, l, S * T)
+        r_host[l] = synth.router_zipf(geo, args.seed, l, x_host[l])
+    x = torch.from_numpy(x_host.view(np.uint8)).to(dev)
+    routers = torch.from_numpy(r_host.view(np.uint8)).to(dev)
+    slots = torch.arange(E, dtype=torch.int64, device=dev) * stride
+    out = torch.empty(n_layers, T, H, dtype=torch.float32, device=dev)
+    ids = torch.full((n_layers, S, T, k), -1, dtype=torch.int32, device=dev)
+    desc = M.desc_for(H, E, k, geo.inter, geo.shared_inter, geo.bits, geo.act, geo.sb, "f32", pool_bytes=E * stride)
+    ws = torch.zeros(M.workspace_bytes(desc, T), dtype=torch.uint8, device=dev)
+    M.workspace_init(ws)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s: pool {pool.numel() / 1e9:.2f} GB, {n_layers} layers, T={T}")
+
+    x_row = T * H * 2
+    r_bytes = E * H * 2
+
+    def layer_call(l, s, strm):
+        M.layer_forward(desc, T, x.data_ptr() + (l * S * T + s * T) * H * 2, routers.data_ptr() + l * r_bytes,
+                        slots, pool.data_ptr() + l * E * stride, shared.data_ptr() + l * shared_bytes,
+                        out[l], ws, ids[l, s], None, stream=strm)
+
+    def step(s, strm):
+        for l in range(n_layers):
+            layer_call(l, s, strm)
+
+    # ---------------------------------------------------------------- timed run
+    graphs = []
+    if not args.eager:
+        for s in range(S):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(s, torch.cuda.current_stream().cuda_stream)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run_step(s):
+        if args.eager:
+            step(s, stream.cuda_stream)
+        else:
+            graphs[s].replay()
+
+    for s in range(W):
+        run_step(s)
+    torch.cuda.synchronize()
+    M.status_check(ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for s in range(W, S):
+        run_step(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = e0.elapsed_time(e1)
+    M.status_check(ws)
+    ms_per_step = total_ms / K
+    layer_tokens = K * n_layers * T
+    value = layer_tokens / (total_ms * 1e-3)
+    log(f"timed {K} steps: {total_ms:.2f} ms (wall {wall * 1e3:.2f} ms), {ms_per_step * 1e3 / n_layers:.2f} us/layer")
+
+    # algorithmic bytes from the realised routing
+    ids_h = ids.cpu().numpy()
+    blob = M.blob_bytes(desc, False)
+    fixed = M.blob_bytes(desc, True) + r_bytes + H * 2 + x_row + T * H * 4
+    per_ls = np.array([[len(np.unique(ids_h[l, s])) for s in range(W, S)] for l in range(n_layers)])
+    bytes_total = float(per_ls.sum() * blob + fixed * per_ls.size)
+    bytes_per_layer = bytes_total / per_ls.size
+    stack_gbs = bytes_total / (total_ms * 1e-3) / 1e9
+
+    # ---------------------------------------------------------------- launch unit timing (eager, events)
+    n_inst = min(8, K)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_inst * n_layers)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_inst * n_layers)]
+    torch.cuda.synchronize()
+    i = 0
+    for s in range(W, W + n_inst):
+        for l in range(n_layers):
+            starts[i].record(stream)
+            layer_call(l, s, stream.cuda_stream)
+            ends[i].record(stream)
+            i += 1
+    torch.cuda.synchronize()
+    durs = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)]) * 1e3   # us
+    unit_us = float(np.mean(durs))
+    inst_bytes = per_ls[:, :n_inst].T.reshape(-1) * blob + fixed
+    achieved = float(np.mean(inst_bytes) / (unit_us * 1e-6) / 1e9)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "layers": n_layers, "tokens_per_step": T, "hidden": H,
+            "experts": E, "top_k": k, "inter": geo.inter, "shared_inter": geo.shared_inter,
+            "bits": geo.bits, "group": 64, "scale_dtype": geo.sb, "act_dtype": geo.act,
+            "pool_gb": round(pool.numel() / 1e9, 2), "graphs": not args.eager,
+        },
+        "hbm": {
+            "algorithmic_bytes_per_layer": round(bytes_per_layer),
+            "stack_gbs": round(stack_gbs, 1),
+            "stack_frac_of_8tbs": round(stack_gbs / HBM_PEAK_GBS, 4),
+            "mean_unique_experts": round(float(per_ls.mean()), 2),
+        },
+        "roofline": {
+            "kernel": "moe_layer_forward (router, topk, dispatch, gateup, down, combine launches)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "launch_us": round(unit_us, 3),
+        },
+    }
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(geo, args, x_host, r_host, shared_host, n_layers, S, T,
+                                              shared_bytes)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(geo, args, x_host, r_host, shared_host, n_layers, S, T, shared_bytes):
+    """The oracle (float64, unmodified) on a bounded sample: one token of the
+    first timed step per layer, until the time budget is spent."""
+    import synth
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    shape = O.LayerShape(geo.hidden, geo.n_experts, geo.top_k, geo.inter, geo.shared_inter, geo.bits,
+                         geo.act, geo.sb)
+    stride = geo.blob_stride
+    pool = np.zeros(geo.n_experts * stride, dtype=np.uint8)
+    slots = np.arange(geo.n_experts, dtype=np.int64) * stride
+    s = args.warmup
+    spent, done = 0.0, 0
+    for l in range(n_layers):
+        x1 = x_host[l, s * T: s * T + 1]
+        xs = O.decode_dense(x1, geo.act).reshape(1, -1)
+        rs = O.decode_dense(r_host[l], geo.act).reshape(geo.n_experts, -1)
+        for e in O.select_topk(O.router_logits(xs, rs)[0], geo.top_k):
+            e = int(e)
+            synth.fill_blob(geo, geo.inter, synth.blob_key(args.seed, l, e), pool[e * stride:(e + 1) * stride])
+        sh = shared_host[l * shared_bytes:(l + 1) * shared_bytes]
+        t0 = time.perf_counter()
+        O.moe_layer(shape, 1, x1, r_host[l], slots, pool, sh)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= args.cpu_seconds:
+            break
+    return {
+        "value": round(done / spent, 3),
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} layer-tokens (token 0 of the first timed step, layers 0..{done - 1}), "
+                  f"{spent:.1f} s of float64 numpy",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -67,6 +67,9 @@ extern "C" {
 #define MOE_ERANGE (-5)   /* a kernel saw a slot offset outside the pool, or an
                              expert id outside [0, E); that pair was skipped    */
 #define MOE_ENOSPC (-6)   /* residency manager: more experts than slots         */
+#define MOE_ETIMEOUT (-7) /* the fused decode kernel's bounded wait expired: some
+                             of its blocks never became resident (the GPU was
+                             shared with other work); the output is invalid    */
 
 /* Storage dtypes. */
 #define MOE_F32 0
@@ -74,11 +77,11 @@ extern "C" {
 
 /*
  * Layer descriptor (plain value, caller-owned).
- *   hidden        H; a power of two, 64 .. 4096
+ *   hidden        H; a power of two, 64 .. 2048
  *   n_experts     E; 1 .. 1024
  *   top_k         k; 1 .. min(E, 64)
- *   inter         I, routed-expert intermediate size; power of two, 64 .. 4096
- *   shared_inter  shared-expert intermediate size; power of two, 64 .. 4096
+ *   inter         I, routed-expert intermediate size; power of two, 64 .. 2048
+ *   shared_inter  shared-expert intermediate size; power of two, 64 .. 2048
  *   bits          4 or 8
  *   group_size    must be 64
  *   act_dtype     dtype of x, the router matrix and the shared gate vector
@@ -116,9 +119,12 @@ int64_t moe_blob_bytes(const moe_desc* d, int32_t shared);
 size_t moe_workspace_bytes(const moe_desc* d, int32_t T_max);
 
 /*
- * Prepare a workspace for first use: clears its control words (error flags,
- * counters) with a kernel on `stream`.  Call once after allocating it; every
- * later call leaves the control words ready for the next call.
+ * Prepare a workspace for first use: clears all of it with a kernel on
+ * `stream` (no memset, so this may run inside a captured graph).  Call once
+ * after allocating it; every later call leaves it ready for the next call.
+ * The fused path tags its exchange words with a 32-bit per-workspace call
+ * counter: re-initialise a workspace at least every 2^31 calls if calls with
+ * different T share it.
  */
 int moe_workspace_init(void* workspace, size_t ws_bytes, void* stream);
 
@@ -146,6 +152,22 @@ int moe_layer_forward(const moe_desc* d, int32_t T, const void* x, const void* r
                       float* topk_w, void* stream);
 
 /*
+ * Which kernels run.  For 1 <= T <= 8 with bf16 activations and scales (or
+ * float32 activations, scales and output) moe_layer_forward runs ONE fused
+ * launch per layer: a grid whose blocks are all resident at once computes the
+ * router, top-k, gate/up and down/combine, handing logits and activations
+ * between blocks as tagged 64-bit words (no fences).  It needs every block
+ * resident, i.e. the GPU's compute units not taken by other work; a wait that
+ * expires raises MOE_ETIMEOUT in moe_status_check.  Larger T runs the staged
+ * path (six launches).  moe_layer_forward_staged always runs the staged path;
+ * both paths give bitwise identical results.
+ */
+int moe_layer_forward_staged(const moe_desc* d, int32_t T, const void* x, const void* router_w,
+                             const int64_t* slot_table, const void* pool_base, const void* shared_w,
+                             void* out, void* workspace, size_t ws_bytes, int32_t* topk_ids,
+                             float* topk_w, void* stream);
+
+/*
  * First half of moe_layer_forward: router logits, top-k and renormalised
  * weights into topk_ids [T, k] / topk_w [T, k] (both required).
  */
@@ -166,8 +188,9 @@ int moe_experts_forward(const moe_desc* d, int32_t T, const void* x, const int32
 
 /*
  * Synchronises `stream`, then reports and clears the device-side error flags
- * of `workspace`: MOE_ERANGE if any kernel since the last check skipped a pair
- * for a bad slot offset or expert id, else MOE_OK.  Blocking.
+ * of `workspace`: MOE_ETIMEOUT if a fused-kernel wait expired, else MOE_ERANGE
+ * if any kernel since the last check skipped a pair for a bad slot offset or
+ * expert id, else MOE_OK.  Blocking.
  */
 int moe_status_check(void* workspace, void* stream);
 

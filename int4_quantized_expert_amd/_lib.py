@@ -24,6 +24,7 @@ ERRORS = {
     -4: "MOE_ENOMEM",
     -5: "MOE_ERANGE",
     -6: "MOE_ENOSPC",
+    -7: "MOE_ETIMEOUT",
 }
 
 
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_init.restype = ctypes.c_int
         L.moe_layer_forward.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
         L.moe_layer_forward.restype = ctypes.c_int
+        L.moe_layer_forward_staged.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+        L.moe_layer_forward_staged.restype = ctypes.c_int
         L.moe_router_topk.argtypes = [dp, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moe_router_topk.restype = ctypes.c_int
         L.moe_experts_forward.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -155,6 +158,14 @@ def layer_forward(d: MoeDesc, T: int, x, router_w, slot_table, pool, shared_w, o
     _check(lib().moe_layer_forward(ctypes.byref(d), T, _ptr(x), _ptr(router_w), _ptr(slot_table), _ptr(pool),
                                    _ptr(shared_w), _ptr(out), _ptr(ws), _nbytes(ws), _ptr(topk_ids),
                                    _ptr(topk_w), _stream(stream, ws)))
+
+
+def layer_forward_staged(d: MoeDesc, T: int, x, router_w, slot_table, pool, shared_w, out, ws,
+                         topk_ids=None, topk_w=None, stream=None) -> None:
+    """Same as layer_forward but always on the staged (multi-launch) kernels."""
+    _check(lib().moe_layer_forward_staged(ctypes.byref(d), T, _ptr(x), _ptr(router_w), _ptr(slot_table),
+                                          _ptr(pool), _ptr(shared_w), _ptr(out), _ptr(ws), _nbytes(ws),
+                                          _ptr(topk_ids), _ptr(topk_w), _stream(stream, ws)))
 
 
 def router_topk(d: MoeDesc, T: int, x, router_w, topk_ids, topk_w, ws, stream=None) -> None:

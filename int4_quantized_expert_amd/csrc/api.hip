@@ -6,7 +6,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
+#include <tuple>
 
 #include "moe_internal.h"
 
@@ -77,6 +80,23 @@ int check_ws(const moe_desc& d, int32_t T, const void* ws, size_t ws_bytes, moe:
   if (ws_bytes < L->total)
     return fail(MOE_ENOMEM, "workspace has %zu bytes, %zu needed for T=%d", ws_bytes, L->total, T);
   return MOE_OK;
+}
+
+// Fused-kernel plans, cached per (device, shape, T): the occupancy query is
+// host work that should not repeat on every call.
+int cached_plan(const moe_desc& d, int T, moe::FusedPlan* plan) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int, int, int, int, int, int, int, int, int>, moe::FusedPlan> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ENODEV;
+  const auto key = std::make_tuple(dev, d.hidden, d.n_experts, d.top_k, d.inter, d.shared_inter, d.bits,
+                                   d.act_dtype, d.sb_dtype, d.out_dtype, T);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) { *plan = it->second; return MOE_OK; }
+  const int rc = moe::fused_plan(d, T, plan);
+  if (rc == MOE_OK) cache[key] = *plan;
+  return rc;
 }
 
 int finish(int rc) {
@@ -156,9 +176,10 @@ int moe_experts_forward(const moe_desc* d, int32_t T, const void* x, const int32
   return finish(moe::launch_experts(c));
 }
 
-int moe_layer_forward(const moe_desc* d, int32_t T, const void* x, const void* router_w, const int64_t* slot_table,
-                      const void* pool_base, const void* shared_w, void* out, void* workspace, size_t ws_bytes,
-                      int32_t* topk_ids, float* topk_w, void* stream) {
+static int layer_forward(const moe_desc* d, int32_t T, const void* x, const void* router_w,
+                         const int64_t* slot_table, const void* pool_base, const void* shared_w, void* out,
+                         void* workspace, size_t ws_bytes, int32_t* topk_ids, float* topk_w, void* stream,
+                         bool allow_fused) {
   int rc;
   if ((rc = check_desc(d)) || (rc = check_T(T))) return rc;
   if (!x || !router_w || !slot_table || !pool_base || !shared_w || !out)
@@ -182,9 +203,29 @@ int moe_layer_forward(const moe_desc* d, int32_t T, const void* x, const void* r
   c.L = L;
   c.ids = reinterpret_cast<const int32_t*>(c.ws + L.ids);
   c.wts = reinterpret_cast<const float*>(c.ws + L.wts);
+  c.ids_out = topk_ids;
+  c.wts_out = topk_w;
   c.stream = static_cast<hipStream_t>(stream);
+  if (allow_fused && moe::fused_supported(*d, T)) {
+    moe::FusedPlan plan;
+    if (cached_plan(*d, T, &plan) == MOE_OK) return finish(moe::launch_decode_fused(c, plan));
+  }
   if ((rc = moe::launch_router_topk(c, topk_ids, topk_w))) return finish(rc);
   return finish(moe::launch_experts(c));
+}
+
+int moe_layer_forward(const moe_desc* d, int32_t T, const void* x, const void* router_w, const int64_t* slot_table,
+                      const void* pool_base, const void* shared_w, void* out, void* workspace, size_t ws_bytes,
+                      int32_t* topk_ids, float* topk_w, void* stream) {
+  return layer_forward(d, T, x, router_w, slot_table, pool_base, shared_w, out, workspace, ws_bytes, topk_ids,
+                       topk_w, stream, true);
+}
+
+int moe_layer_forward_staged(const moe_desc* d, int32_t T, const void* x, const void* router_w,
+                             const int64_t* slot_table, const void* pool_base, const void* shared_w, void* out,
+                             void* workspace, size_t ws_bytes, int32_t* topk_ids, float* topk_w, void* stream) {
+  return layer_forward(d, T, x, router_w, slot_table, pool_base, shared_w, out, workspace, ws_bytes, topk_ids,
+                       topk_w, stream, false);
 }
 
 int moe_status_check(void* workspace, void* stream) {
@@ -198,6 +239,8 @@ int moe_status_check(void* workspace, void* stream) {
     if (hipMemcpyAsync(workspace, &zero, 4, hipMemcpyHostToDevice, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)
       return fail(MOE_EHIP, "status clear failed: %s", hipGetErrorString(hipGetLastError()));
+    if (flags & 2u)
+      return fail(MOE_ETIMEOUT, "a bounded in-kernel wait of the fused decode kernel expired; its output is invalid");
     return fail(MOE_ERANGE, "a kernel skipped a pair: slot offset outside the pool or expert id outside [0, E)");
   }
   return ok();

@@ -16,114 +16,6 @@ namespace moe {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Lane layout for a row of `cols` codes split into 32-code segments:
-// spr = cols / 32 segments per row.  If spr >= 64 one wave covers one row and
-// lane L takes segments L, L + 64, ... (nsl = spr / 64 of them).  Otherwise a
-// wave covers 64 / spr rows at once and lane L takes segment L % spr of row
-// L / spr.
-struct RowLanes {
-  int spr;      // segments per row
-  int rpp;      // rows per wave pass
-  int width;    // lanes summed per row
-  int sub_row;  // this lane's row within a pass
-  int seg0;     // this lane's first segment
-};
-
-__device__ __forceinline__ RowLanes row_lanes(int cols, int lane) {
-  RowLanes r;
-  r.spr = cols / kSegCodes;
-  if (r.spr >= kWave) {
-    r.rpp = 1;
-    r.width = kWave;
-    r.sub_row = 0;
-    r.seg0 = lane;
-  } else {
-    r.rpp = kWave / r.spr;
-    r.width = r.spr;
-    r.sub_row = lane / r.spr;
-    r.seg0 = lane % r.spr;
-  }
-  return r;
-}
-
-// Multi-token segment dot: converts each code once and feeds NT FMA chains per
-// parity; per token the result is bitwise the single-token seg_qdot.
-template <int BITS, int NT>
-__device__ __forceinline__ void seg_qdot_nt(const Seg<BITS>& s_in, const float (&v)[NT][kSegCodes], float (&out)[NT]) {
-  // Opaque copy of the packed codes: keeps the compiler from hoisting the
-  // code->float conversions out of the callers' token loops, which would hold
-  // 32 floats per segment in registers instead of 4 words.
-  Seg<BITS> s;
-#pragma unroll
-  for (int i = 0; i < BITS / 4; ++i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t w = s_in.w[i][j];
-      asm volatile("" : "+v"(w));
-      s.w[i][j] = w;
-    }
-  }
-  float a0[NT], a1[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) { a0[t] = 0.f; a1[t] = 0.f; }
-  if constexpr (BITS == 4) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t w = s.w[0][k];
-      const uint32_t lo = w & 0x0f0f0f0fu;
-      const uint32_t hi = (w >> 4) & 0x0f0f0f0fu;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float qe = static_cast<float>((lo >> (8 * j)) & 0xffu);
-        const float qo = static_cast<float>((hi >> (8 * j)) & 0xffu);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          a0[t] = fmaf(qe, v[t][8 * k + 2 * j], a0[t]);
-          a1[t] = fmaf(qo, v[t][8 * k + 2 * j + 1], a1[t]);
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t w = s.w[h][k];
-        const float q0 = static_cast<float>(w & 0xffu);
-        const float q1 = static_cast<float>((w >> 8) & 0xffu);
-        const float q2 = static_cast<float>((w >> 16) & 0xffu);
-        const float q3 = static_cast<float>(w >> 24);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          a0[t] = fmaf(q0, v[t][16 * h + 4 * k + 0], a0[t]);
-          a1[t] = fmaf(q1, v[t][16 * h + 4 * k + 1], a1[t]);
-          a0[t] = fmaf(q2, v[t][16 * h + 4 * k + 2], a0[t]);
-          a1[t] = fmaf(q3, v[t][16 * h + 4 * k + 3], a1[t]);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < NT; ++t) out[t] = a0[t] + a1[t];
-}
-
-// Blob plane offsets (see include/moe_layer.h): Q bytes of codes and S bytes
-// of scales per matrix, all three matrices the same size.
-struct Planes {
-  int64_t q;   // codes bytes of one matrix
-  int64_t s;   // scale bytes of one matrix
-  int64_t blob;
-};
-
-__host__ __device__ inline Planes planes_of(int hidden, int inter, int bits, int sb_dtype) {
-  Planes p;
-  p.q = static_cast<int64_t>(hidden) * inter * bits / 8;
-  p.s = static_cast<int64_t>(hidden) * (inter / 64) * (sb_dtype == kF32 ? 4 : 2);
-  p.blob = 3 * p.q + 6 * p.s;
-  return p;
-}
-
-// ---------------------------------------------------------------------------
 // Router logits: l[t, e] = sum_h x[t, h] R[e, h] in float32 (FMA chain over
 // the lane's codes in order, then the lane butterfly).  Rows 0..E-1.
 template <int ACT, int NSL>
@@ -333,8 +225,6 @@ struct GateUpArgs {
   int64_t pool_bytes;
   int T, k, H, I, SI, umax, bpe_r, bpe_s, hstride;
 };
-
-constexpr int kMaxPass = 4;
 
 template <int BITS, int SB, int ACT, int NSL, int TOKC>
 __global__ __launch_bounds__(256) void k_gateup(GateUpArgs a) {
@@ -622,9 +512,10 @@ static int last_launch_error() {
 }
 
 int launch_ws_init(uint8_t* ws, size_t bytes, hipStream_t stream) {
-  const size_t n = 256 / 4;
-  (void)bytes;
-  hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, stream, reinterpret_cast<uint32_t*>(ws), n, 0u);
+  const size_t n = bytes / 4;
+  const size_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(k_fill_u32, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     reinterpret_cast<uint32_t*>(ws), n, 0u);
   return last_launch_error();
 }
 

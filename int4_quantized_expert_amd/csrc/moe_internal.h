@@ -5,14 +5,17 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/moe_layer.h"
+#include "moe_layer.h"
+#include "fused_common.h"
 
 namespace moe {
+
+constexpr int kFusedMaxBlocks = 2048;
 
 // Byte layout of the caller's workspace for calls with up to T_max tokens.
 // Every region starts on a 256-byte boundary.
 struct WsLayout {
-  size_t ctrl;       // uint32 control words: [0] error flags
+  size_t ctrl;       // uint32 control words: [0] error flags, [1] fused-path epoch
   size_t logits;     // [T, E] float32 router logits
   size_t ids;        // [T, k] int32 chosen experts
   size_t wts;        // [T, k] float32 renormalised weights
@@ -23,6 +26,9 @@ struct WsLayout {
   size_t plist;      // [T k] int32 pair indices (t * k + i) grouped by expert
   size_t h;          // [T k + T, max(I, SI)] float32 SwiGLU activations
   size_t partial;    // [T k + T, H] float32 per-pair down projections
+  size_t f_lg;       // fused path: [T, E] tagged logits (uint64)
+  size_t f_hx;       // fused path: [T k + T, max(I, SI)] tagged activations (uint64)
+  size_t f_arrive;   // fused path: [2][kFusedMaxBlocks] uint32 per-block phase flags
   size_t total;
   int32_t umax;      // min(T k, E)
   int32_t hstride;   // max(I, SI)
@@ -38,6 +44,7 @@ inline WsLayout ws_layout(const moe_desc& d, int32_t T) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes > 0 ? bytes : 1); return at; };
   L.ctrl = take(256);
+  L.f_arrive = take(2 * kFusedMaxBlocks * 4);
   L.logits = take(static_cast<size_t>(T) * d.n_experts * 4);
   L.ids = take(Tk * 4);
   L.wts = take(Tk * 4);
@@ -48,6 +55,8 @@ inline WsLayout ws_layout(const moe_desc& d, int32_t T) {
   L.plist = take(Tk * 4);
   L.h = take((Tk + T) * static_cast<size_t>(hs) * 4);
   L.partial = take((Tk + T) * static_cast<size_t>(d.hidden) * 4);
+  L.f_lg = take(static_cast<size_t>(T) * d.n_experts * 8);
+  L.f_hx = take((Tk + T) * static_cast<size_t>(hs) * 8);
   L.total = o;
   L.umax = umax;
   L.hstride = hs;
@@ -76,5 +85,10 @@ struct Call {
 int launch_router_topk(const Call& c, int32_t* ids_dst, float* wts_dst);
 int launch_experts(const Call& c);
 int launch_ws_init(uint8_t* ws, size_t bytes, hipStream_t stream);
+
+// Fused single-launch decode (T <= kFusedMaxT).
+bool fused_supported(const moe_desc& d, int T);
+int fused_plan(const moe_desc& d, int T, FusedPlan* plan);
+int launch_decode_fused(const Call& c, const FusedPlan& plan);
 
 }  // namespace moe

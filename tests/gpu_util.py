@@ -129,8 +129,9 @@ def upload(data: LayerData, out: str = "f32", pool=None, slots=None) -> DeviceLa
     return DeviceLayer(d, put(data.x), put(data.R), pool_d, slots_d, put(data.shared))
 
 
-def run(dl: DeviceLayer, T: int, x: torch.Tensor | None = None, ws: torch.Tensor | None = None):
-    """moe_layer_forward through the binding; returns (out tensor, ids, wts)."""
+def run(dl: DeviceLayer, T: int, x: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+        staged: bool = False):
+    """moe_layer_forward (or the staged variant) through the binding; returns (out tensor, ids, wts)."""
     g_out = torch.float32 if dl.desc.out_dtype == M.MOE_F32 else torch.bfloat16
     H, k = dl.desc.hidden, dl.desc.top_k
     out = torch.full((max(T, 1), H), float("nan"), dtype=g_out, device=DEV)
@@ -139,7 +140,8 @@ def run(dl: DeviceLayer, T: int, x: torch.Tensor | None = None, ws: torch.Tensor
     if ws is None:
         ws = torch.zeros(M.workspace_bytes(dl.desc, max(T, 1)), dtype=torch.uint8, device=DEV)
         M.workspace_init(ws)
-    M.layer_forward(dl.desc, T, dl.x if x is None else x, dl.R, dl.slots, dl.pool, dl.shared, out, ws, ids, wts)
+    fwd = M.layer_forward_staged if staged else M.layer_forward
+    fwd(dl.desc, T, dl.x if x is None else x, dl.R, dl.slots, dl.pool, dl.shared, out, ws, ids, wts)
     torch.cuda.synchronize()
     M.status_check(ws)
     return out, ids, wts

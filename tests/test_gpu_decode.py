@@ -13,9 +13,9 @@ from gpu_util import DEV, check_close, check_routing, make_layer, oracle_run, pu
 pytestmark = pytest.mark.gpu
 
 
-def _parity(data, out="f32", tokens=None):
+def _parity(data, out="f32", tokens=None, staged=False):
     dl = upload(data, out)
-    y, ids, wts = run(dl, data.T)
+    y, ids, wts = run(dl, data.T, staged=staged)
     y_ref, ids_ref, w_ref, _ = oracle_run(data, tokens=tokens)
     check_routing(ids, wts, ids_ref, w_ref, tokens=tokens)
     return check_close(y, y_ref, data.geo.act, tokens=tokens)
@@ -31,6 +31,29 @@ def test_80b_decode_full_layer(T):
     """80B-A3B-shaped layer, all 512 experts resident, Zipf-skewed routing."""
     data = make_layer(synth.PRESETS["80b"], 2, 5, T, routing="zipf", n_cand=96)
     assert _parity(data) <= 2e-3
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_80b_decode_staged_path(T):
+    data = make_layer(synth.PRESETS["80b"], 2, 6, T, routing="zipf", n_cand=96)
+    assert _parity(data, staged=True) <= 2e-3
+
+
+@pytest.mark.parametrize("preset,T,out", [("80b", 1, "f32"), ("80b", 3, "bf16"), ("80b", 8, "f32"),
+                                          ("35b", 2, "f32"), ("35b_int8", 8, "bf16"), ("35b_int8", 1, "f32"),
+                                          ("tiny", 5, "f32")])
+def test_fused_and_staged_paths_bitwise_equal(preset, T, out):
+    """The single-launch decode kernel and the staged kernels give the same bits."""
+    data = make_layer(synth.PRESETS[preset], 21, T, T, routing="zipf" if preset != "tiny" else "normal",
+                      n_cand=64, filter_margin=False)
+    dl = upload(data, out)
+    ws = torch.zeros(M.workspace_bytes(dl.desc, T), dtype=torch.uint8, device=DEV)
+    M.workspace_init(ws)
+    a = run(dl, T, ws=ws)
+    b = run(dl, T, ws=ws, staged=True)
+    c = run(dl, T, ws=ws)            # fused again after a staged call on the same workspace
+    for p, q, r in zip(a, b, c):
+        assert torch.equal(p, q) and torch.equal(p, r)
 
 
 def test_35b_decode_full_layer():
