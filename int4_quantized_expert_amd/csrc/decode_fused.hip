@@ -1,28 +1,33 @@
-// Fused single-launch decode of one MoE layer (T <= 8 tokens), gfx950.
+// Decode of one MoE layer (T <= 8 tokens) in two launches, gfx950.
 //
-// The staged path needs six dependent launches per layer; at decode sizes the
-// launch gaps and the dependent-load chains between them cost more than the
-// 21.6 MB the 80B-shaped layer has to stream.  Here one persistent grid whose
-// blocks are all resident at once runs the whole layer:
+// The staged path needs six dependent launches per layer, and each of them
+// starts with a chain of dependent loads; at decode sizes that costs far more
+// than streaming the 21.6 MB of the 80B-shaped layer.  Here:
 //
-//   R  router rows (logits), shared-expert gate/up rows, sigmoid(g . x)
+// Launch A (persistent grid, every block resident):
+//   R  router rows (one logit per wave and token), shared-expert gate/up rows,
+//      sigmoid(g . x) -- everything that does not depend on the routing
 //   K  every block gathers all logits and computes top-k, the renormalised
-//      weights and the expert -> token dispatch itself (no extra exchange)
-//   G  routed gate/up rows + SwiGLU, spread over all waves; the down-projection
-//      codes each block will need are requested before this compute starts
-//   D  each block owns a slice of output rows: down rows of every chosen
-//      expert + the shared one, then the ordered combine, written to out
+//      weights and the expert -> token dispatch itself (no further exchange)
+//   G  routed gate/up rows + SwiGLU, flattened over (expert, row) across all
+//      waves; h goes to the workspace with plain stores
+// Launch B (one block per slice of output rows):
+//   D  down rows of every chosen expert and the shared one for the slice,
+//      then the ordered combine; h is read through the caches, which the
+//      launch boundary makes coherent
 //
-// Data crossing blocks (logits, h) travels as 64-bit words holding the float
-// bits and a per-call tag, written and read with relaxed device-scope atomics.
-// A word is valid when its tag matches, so no fence is needed (an agent-scope
-// release on this chip writes back the L2 and costs microseconds).  The tag is
-// the workspace epoch + 1; block 0 advances the epoch at its end, after it has
-// seen every block's arrival word, so the next call gets a fresh tag.  Every
-// wait is bounded: on expiry the kernel raises kErrTimeout and finishes.
+// Inside launch A only the logits cross blocks.  They travel as 64-bit words
+// holding the float bits and a per-call tag, written and read with relaxed
+// device-scope atomics; each block raises a flag word once its phase-R stores
+// are acknowledged, and waits for every block's flag before reading the
+// logits.  A word is valid when its tag matches, so no fence is needed (an
+// agent-scope release on this chip writes back the L2 and costs microseconds).
+// The tag is the workspace epoch + 1; block 0 retires it at its end, after it
+// has seen every block's flag.  Every wait is bounded: on expiry the kernel
+// raises kErrTimeout and finishes.
 //
-// Per-row arithmetic uses the same helpers and the same orders as the staged
-// kernels, so the two paths give bitwise identical results.
+// Per-row arithmetic uses the same helpers and orders as the staged kernels,
+// so both paths give bitwise identical results.
 //
 // Sources: routing to k of E experts per layer plus the shared expert
 // (Swiftlet README translation, "How it works"); int4/int8 affine group
@@ -41,7 +46,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kCandMax = 64;
-constexpr int kMaxDownPerWave = 8;    // down tasks per wave per round in phase D
+constexpr int kMaxDownPerWave = 4;    // down tasks per wave per round in launch B
+constexpr int kRouterRowsPerWave = 2; // router row groups per wave in phase R
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t b = __float_as_uint(f);
@@ -49,143 +55,88 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t tagged(float v, uint32_t tag) {
-  return (static_cast<uint64_t>(tag) << 32) | __float_as_uint(v);
-}
-
 __device__ __forceinline__ void store_tagged(uint64_t* p, float v, uint32_t tag) {
-  __hip_atomic_store(p, tagged(v, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p, (static_cast<uint64_t>(tag) << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ uint64_t load_tagged(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ uint64_t lane_mask_lt(int lane) { return lane == 0 ? 0ull : (~0ull >> (64 - lane)); }
+
 // One wave waits until flags[0..n) all equal `tag` (bounded, with backoff).
-__device__ bool wait_block_flags(const uint32_t* f, int n, uint32_t tag, int lane, uint32_t& spins, uint32_t limit) {
+__device__ __forceinline__ bool wait_block_flags(const uint32_t* f, int n, uint32_t tag, int lane, uint32_t& spins, uint32_t limit) {
   for (;;) {
     bool mine = true;
     for (int b = lane; b < n; b += kWave)
       mine &= __hip_atomic_load(const_cast<uint32_t*>(f) + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
     if (__all(mine)) return true;
     if (++spins > limit) return false;
-    __builtin_amdgcn_s_sleep(8);
+    __builtin_amdgcn_s_sleep(2);
   }
 }
 
-// All stores of this block are acknowledged, then thread 0 raises the block's
-// flag.  The flag is only a hint that the tagged words are there: readers
-// still check every word's tag.
+// All of this block's stores are acknowledged, then thread 0 raises its flag.
+// The flag only says the tagged words should be there: readers still check
+// every word's tag.
 __device__ __forceinline__ void publish_block_flag(uint32_t* f, uint32_t tag) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) __hip_atomic_store(f + blockIdx.x, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ uint64_t lane_mask_lt(int lane) { return lane == 0 ? 0ull : (~0ull >> (64 - lane)); }
-
-// Activation segment from LDS in its storage dtype.
-template <int ACT>
-__device__ __forceinline__ void lds_act_seg(const uint8_t* row, int seg, float (&v)[kSegCodes]) {
-  load_act_seg<ACT>(row, seg, v);   // plain loads; `row` points into LDS
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-struct Lds {
+struct LdsA {
   uint8_t* x;        // [T][H] activations, storage dtype
   float* lg;         // [T][E] logits
   int32_t* ids;      // [T][k]
-  float* wts;        // [T][k]
-  float* sig;        // [T]
+  float* vals;       // [T][k] chosen logits, then weights
+  float* ev;         // [kWaves][64] exp values for the ordered sum
   int64_t* slot;     // [E]
-  int32_t* umap;     // [E] expert -> distinct index (or mark)
+  int32_t* umap;     // [E] expert -> distinct index
   int32_t* uniq;     // [umax]
   int32_t* pidx;     // [umax][T] rank i of the expert for token t, or -1
-  float* part;       // [(T k + T)][rb]
   uint32_t* cand_k;  // [kWaves][kCandMax]
   int32_t* cand_i;   // [kWaves][kCandMax]
-  int32_t* misc;     // [0] U, [1] tag, [2] timeout seen
+  int32_t* misc;     // [0] U, [1] tag
 };
 
-__device__ inline Lds carve(uint8_t* base, const FusedArgs& a) {
-  Lds s;
+__device__ inline LdsA carve_a(uint8_t* base, const FusedArgs& a) {
+  LdsA s;
   size_t o = 0;
   auto take = [&](size_t n) { uint8_t* p = base + o; o += (n + 15) / 16 * 16; return p; };
   s.x = take(static_cast<size_t>(a.T) * a.H * a.act_sz);
   s.lg = reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * a.E * 4));
   s.ids = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.T) * a.k * 4));
-  s.wts = reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * a.k * 4));
-  s.sig = reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * 4));
+  s.vals = reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * a.k * 4));
+  s.ev = reinterpret_cast<float*>(take(kWaves * 64 * 4));
   s.slot = reinterpret_cast<int64_t*>(take(static_cast<size_t>(a.E) * 8));
   s.umap = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.E) * 4));
   s.uniq = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.umax) * 4));
   s.pidx = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.umax) * a.T * 4));
-  s.part = reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * (a.k + 1) * a.rb * 4));
   s.cand_k = reinterpret_cast<uint32_t*>(take(kWaves * kCandMax * 4));
   s.cand_i = reinterpret_cast<int32_t*>(take(kWaves * kCandMax * 4));
   s.misc = reinterpret_cast<int32_t*>(take(16 * 4));
   return s;
 }
 
-// One down-projection task of a wave: `rpp` rows of one expert's Wd for this
-// block's output rows (lane: one segment of one row).
-template <int BITS>
-struct DownTask {
-  Seg<BITS> code;
-  float sc, bi;
-  int j;        // distinct-expert index (U = shared), -1 if none
-  int rloc;     // this lane's row within the block, -1 if outside
-  bool valid;   // blob offset usable
-};
-
-template <int BITS, int SB>
-__device__ __forceinline__ void load_down_task(DownTask<BITS>& d, int task, int ntask, int np, int U, int row_lo,
-                                               const FusedArgs& a, const Lds& s, const RowLanes& rli,
-                                               const RowLanes& rls, int lane, uint32_t* flags) {
-  d.j = -1;
-  d.rloc = -1;
-  d.valid = false;
-  d.sc = 0.f;
-  d.bi = 0.f;
-#pragma unroll
-  for (int i = 0; i < BITS / 4; ++i) d.code.w[i] = u32x4{0, 0, 0, 0};
-  if (task >= ntask) return;
-  const int j = task / np, p = task % np;
-  const bool is_sh = j == U;
-  const RowLanes& rl = is_sh ? rls : rli;
-  const int inter = is_sh ? a.SI : a.I;
-  const Planes pl = planes_of(a.H, inter, BITS, SB);
-  const uint8_t* blob = a.shared;
-  bool valid = true;
-  if (!is_sh) {
-    const int64_t off = s.slot[s.uniq[j]];
-    valid = slot_ok(off, pl.blob, a.pool_bytes);
-    blob = a.pool + (valid ? off : 0);
-    if (!valid && lane == 0) raise_error(flags, kErrRange);
-  }
-  d.j = j;
-  d.valid = valid;
-  const int rloc = p * rl.rpp + rl.sub_row;
-  const int r = row_lo + rloc;
-  if (rloc < a.rb && r < a.H) {
-    d.rloc = rloc;
-    if (valid) {
-      const int64_t row_bytes = static_cast<int64_t>(inter) * BITS / 8;
-      d.code = load_codes<BITS>(blob + 2 * pl.q + r * row_bytes + static_cast<int64_t>(rl.seg0) * (kSegCodes * BITS / 8));
-      const size_t si = static_cast<size_t>(r) * (inter / 64) + rl.seg0 / 2;
-      d.sc = load_scalar<SB>(blob + 3 * pl.q + 2 * pl.s, si);
-      d.bi = load_scalar<SB>(blob + 3 * pl.q + 5 * pl.s, si);
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Top-k of one token on one wave.  The k-th largest per-lane maximum is a
 // lower bound of the k-th largest logit, so every top-k logit is at least it;
-// the (few) candidates above the bound are ranked exactly by (logit desc, id
-// asc).  If more than kCandMax candidates tie above the bound, k rounds of a
-// wave arg-max finish the job.
-__device__ void topk_wave(const float* lg, int E, int k, int lane, uint32_t* ck, int32_t* ci, int32_t* ids_out,
-                          float* wts_out) {
+// the candidates above the bound (usually a few more than k) are ranked
+// exactly by (logit desc, id asc).  If more than kCandMax candidates lie above
+// the bound, k rounds of a wave arg-max finish the job.
+// Output: ids[0..k) and vals[0..k) = renormalised weights p_i, computed with
+// the same operations and order as the staged kernel.
+__device__ __forceinline__ void topk_wave(const float* lg, int E, int k, int lane, uint32_t* ck, int32_t* ci, float* ev,
+                          int32_t* ids, float* vals) {
   uint32_t key[16];
   uint32_t lm = 0;
 #pragma unroll
@@ -209,27 +160,26 @@ __device__ void topk_wave(const float* lg, int E, int k, int lane, uint32_t* ck,
     if (in && pos < kCandMax) { ck[pos] = key[j]; ci[pos] = lane + j * kWave; }
     cnt += __popcll(m);
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  int my_id = -1;
-  float my_v = 0.f;
   if (cnt <= kCandMax) {
-    if (lane < cnt) {
-      const uint32_t kc = ck[lane];
-      const int ic = ci[lane];
-      int rank = 0;
-      for (int d = 0; d < cnt; ++d) {
-        const uint32_t kd = ck[d];
-        rank += (kd > kc || (kd == kc && ci[d] < ic)) ? 1 : 0;
+    wave_sync_lds();
+    if (lane >= cnt) { ck[lane] = 0u; ci[lane] = 0x7fffffff; }   // padding never outranks a candidate
+    wave_sync_lds();
+    const uint32_t kc = ck[lane];
+    const int ic = ci[lane];
+    int rank = 0;
+    const int cnt16 = (cnt + 15) & ~15;
+    for (int d0 = 0; d0 < cnt16; d0 += 16) {
+#pragma unroll
+      for (int d = 0; d < 16; ++d) {
+        const uint32_t kd = ck[d0 + d];
+        const int id = ci[d0 + d];
+        rank += (kd > kc || (kd == kc && id < ic)) ? 1 : 0;
       }
-      if (rank < k) { ids_out[rank] = ic; wts_out[rank] = lg[ic]; }
     }
+    if (lane < cnt && rank < k) { ids[rank] = ic; vals[rank] = lg[ic]; }
   } else {
-    // rare: too many candidates tie above the bound
-    uint64_t taken_lo = 0;
+    // rare: many candidates lie above the bound
     uint32_t taken = 0;
-    (void)taken_lo;
     for (int i = 0; i < k; ++i) {
       uint32_t bk = 0;
       int bid = 0x7fffffff;
@@ -245,41 +195,38 @@ __device__ void topk_wave(const float* lg, int E, int k, int lane, uint32_t* ck,
         if (ok > bk || (ok == bk && oid < bid)) { bk = ok; bid = oid; }
       }
       if ((bid & (kWave - 1)) == lane) taken |= 1u << (bid / kWave);
-      if (lane == 0) { ids_out[i] = bid; wts_out[i] = lg[bid]; }
+      if (lane == 0) { ids[i] = bid; vals[i] = lg[bid]; }
     }
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // renormalised weights, summed in rank order (same operations as the staged path)
-  if (lane < k) { my_v = wts_out[lane]; my_id = ids_out[lane]; }
-  const float top = wts_out[0];
-  const float ex = lane < k ? expf(my_v - top) : 0.f;
+  wave_sync_lds();
+  // p_i = exp(l_i - l_0) / sum_j exp(l_j - l_0), the sum in rank order from 0
+  const float top = vals[0];
+  const float ex = lane < k ? expf(vals[lane] - top) : 0.f;
+  ev[lane] = ex;
+  wave_sync_lds();
   float sum = 0.f;
-  for (int i = 0; i < k; ++i) sum += __shfl(ex, i, kWave);
-  __builtin_amdgcn_wave_barrier();
-  if (lane < k) wts_out[lane] = ex / sum;
-  (void)my_id;
+  for (int i = 0; i < k; ++i) sum += ev[i];
+  wave_sync_lds();
+  if (lane < k) vals[lane] = ex / sum;
 }
 
-template <int BITS, int SB, int ACT, int OUT>
-__global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
+// ---------------------------------------------------------------------------
+// Launch A: phases R, K, G.
+template <int BITS, int SB, int ACT>
+__global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
-  const Lds s = carve(lds_raw, a);
+  const LdsA s = carve_a(lds_raw, a);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int T = a.T, H = a.H, E = a.E, k = a.k;
-  uint32_t* flags = a.ctrl;
   uint32_t spins = 0;
   bool timed_out = false;
 
-  // ---- start: tag, arrival, x and slot table into LDS
   if (tid == 0) {
     const uint32_t ep = __hip_atomic_load(a.ctrl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t tag = ep + 1u;
-    s.misc[1] = static_cast<int32_t>(tag);
-    s.misc[2] = 0;
+    s.misc[1] = static_cast<int32_t>(ep + 1u);
+    __hip_atomic_store(a.arrive + blockIdx.x, ep + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   {
     const int n16 = T * H * a.act_sz / 16;
@@ -292,17 +239,21 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
   const uint32_t tag = static_cast<uint32_t>(s.misc[1]);
   const size_t xrow = static_cast<size_t>(H) * a.act_sz;
 
-  // ---- phase R: router rows, shared gate/up rows (wave-major task order)
-  const int gwave = wave * a.nb + blockIdx.x;          // spreads tasks over blocks first
+  // ---- phase R: router rows on the first blocks (block-major, kRouterRowsPerWave
+  // row groups per wave, so only a few blocks produce logits); shared gate/up
+  // rows on the waves of the other blocks (wave-major, spread over the machine)
+  const int gwave = wave * a.nb + blockIdx.x;
   const int nwaves = a.nb * kWaves;
   const RowLanes rlh = row_lanes(H, lane);
   const int router_tasks = (E + rlh.rpp - 1) / rlh.rpp;
-  const int npass_h = rlh.rpp >= kMaxPass ? 1 : kMaxPass / rlh.rpp;
-  const int sh_rows_per_task = npass_h * rlh.rpp;
-  const int sh_tasks = (a.SI + sh_rows_per_task - 1) / sh_rows_per_task;
-  for (int task = gwave; task < router_tasks + sh_tasks; task += nwaves) {
-    if (task < router_tasks) {
-      const int e = task * rlh.rpp + rlh.sub_row;
+  const int router_waves = (router_tasks + kRouterRowsPerWave - 1) / kRouterRowsPerWave;
+  const int router_blocks = min(a.nb, (router_waves + kWaves - 1) / kWaves);
+  const int sh_tasks = (a.SI + rlh.rpp - 1) / rlh.rpp;
+  const int bwave = blockIdx.x * kWaves + wave;
+  for (int task = bwave * kRouterRowsPerWave; task < router_tasks; task += nwaves * kRouterRowsPerWave) {
+    for (int j = 0; j < kRouterRowsPerWave; ++j) {
+      const int e = (task + j) * rlh.rpp + rlh.sub_row;
+      if (task + j >= router_tasks) break;
       const bool active = e < E;
       float r[kSegCodes];
       if (active) load_act_seg<ACT>(static_cast<const uint8_t*>(a.router) + static_cast<size_t>(e) * xrow, rlh.seg0, r);
@@ -310,77 +261,78 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
         float acc = 0.f;
         if (active) {
           float v[kSegCodes];
-          lds_act_seg<ACT>(s.x + t * xrow, rlh.seg0, v);
+          load_act_seg<ACT>(s.x + t * xrow, rlh.seg0, v);
 #pragma unroll
           for (int c = 0; c < kSegCodes; ++c) acc = fmaf(v[c], r[c], acc);
         }
         acc = group_sum(acc, rlh.width);
         if (active && (lane % rlh.width) == 0) store_tagged(a.lg + static_cast<size_t>(t) * E + e, acc, tag);
       }
-    } else {
-      // shared expert gate/up rows for every token
-      const int row0 = (task - router_tasks) * sh_rows_per_task;
-      const Planes pl = planes_of(H, a.SI, BITS, SB);
-      const int64_t row_bytes = static_cast<int64_t>(H) * BITS / 8;
-      const int seg_bytes = kSegCodes * BITS / 8;
-      const int gpr = H / 64;
-      for (int p = 0; p < npass_h; ++p) {
-        const int rr = row0 + p * rlh.rpp + rlh.sub_row;
-        const bool ok = rr < a.SI;
-        Seg<BITS> cg, cu;
-        float sg = 0.f, su = 0.f, bg = 0.f, bu = 0.f;
-        if (ok) {
-          const int64_t qo = rr * row_bytes + static_cast<int64_t>(rlh.seg0) * seg_bytes;
-          cg = load_codes<BITS>(a.shared + qo);
-          cu = load_codes<BITS>(a.shared + pl.q + qo);
-          const size_t si = static_cast<size_t>(rr) * gpr + rlh.seg0 / 2;
-          sg = load_scalar<SB>(a.shared + 3 * pl.q, si);
-          su = load_scalar<SB>(a.shared + 3 * pl.q + pl.s, si);
-          bg = load_scalar<SB>(a.shared + 3 * pl.q + 3 * pl.s, si);
-          bu = load_scalar<SB>(a.shared + 3 * pl.q + 4 * pl.s, si);
-        } else {
+    }
+  }
+  {
+    const Planes pl = planes_of(H, a.SI, BITS, SB);
+    const int64_t row_bytes = static_cast<int64_t>(H) * BITS / 8;
+    const int seg_bytes = kSegCodes * BITS / 8;
+    const int gpr = H / 64;
+    // waves of blocks past the router blocks (all waves if there are none)
+    const int sh_blocks = a.nb > router_blocks ? a.nb - router_blocks : a.nb;
+    const int sh_b = a.nb > router_blocks ? static_cast<int>(blockIdx.x) - router_blocks : static_cast<int>(blockIdx.x);
+    for (int task = sh_b >= 0 ? wave * sh_blocks + sh_b : sh_tasks; task < sh_tasks; task += sh_blocks * kWaves) {
+      const int rr = task * rlh.rpp + rlh.sub_row;
+      const bool ok = rr < a.SI;
+      Seg<BITS> cg, cu;
+      float sg = 0.f, su = 0.f, bg = 0.f, bu = 0.f;
+      if (ok) {
+        const int64_t qo = rr * row_bytes + static_cast<int64_t>(rlh.seg0) * seg_bytes;
+        cg = load_codes<BITS>(a.shared + qo);
+        cu = load_codes<BITS>(a.shared + pl.q + qo);
+        const size_t si = static_cast<size_t>(rr) * gpr + rlh.seg0 / 2;
+        sg = load_scalar<SB>(a.shared + 3 * pl.q, si);
+        su = load_scalar<SB>(a.shared + 3 * pl.q + pl.s, si);
+        bg = load_scalar<SB>(a.shared + 3 * pl.q + 3 * pl.s, si);
+        bu = load_scalar<SB>(a.shared + 3 * pl.q + 4 * pl.s, si);
+      } else {
 #pragma unroll
-          for (int i = 0; i < BITS / 4; ++i) { cg.w[i] = u32x4{0, 0, 0, 0}; cu.w[i] = u32x4{0, 0, 0, 0}; }
-        }
-        for (int t = 0; t < T; ++t) {
-          float v[1][kSegCodes];
-          lds_act_seg<ACT>(s.x + t * xrow, rlh.seg0, v[0]);
-          const float xs = seg_sum(v[0]);
-          float qg[1], qu[1];
-          seg_qdot_nt<BITS, 1>(cg, v, qg);
-          seg_qdot_nt<BITS, 1>(cu, v, qu);
-          float accg = 0.f, accu = 0.f;
-          accg += seg_value(sg, bg, qg[0], xs);
-          accu += seg_value(su, bu, qu[0], xs);
-          const float g = group_sum(accg, rlh.width);
-          const float u = group_sum(accu, rlh.width);
-          if (ok && (lane % rlh.width) == 0)
-            store_tagged(a.hx + (static_cast<size_t>(T) * k + t) * a.hs + rr, silu(g) * u, tag);
-        }
+        for (int i = 0; i < BITS / 4; ++i) { cg.w[i] = u32x4{0, 0, 0, 0}; cu.w[i] = u32x4{0, 0, 0, 0}; }
+      }
+      for (int t = 0; t < T; ++t) {
+        float v[1][kSegCodes];
+        load_act_seg<ACT>(s.x + t * xrow, rlh.seg0, v[0]);
+        const float xs = seg_sum(v[0]);
+        float qg[1], qu[1];
+        seg_qdot_nt<BITS, 1>(cg, v, qg);
+        seg_qdot_nt<BITS, 1>(cu, v, qu);
+        float accg = 0.f, accu = 0.f;
+        accg += seg_value(sg, bg, qg[0], xs);
+        accu += seg_value(su, bu, qu[0], xs);
+        const float g = group_sum(accg, rlh.width);
+        const float u = group_sum(accu, rlh.width);
+        if (ok && (lane % rlh.width) == 0) a.h[(static_cast<size_t>(T) * k + t) * a.hs + rr] = silu(g) * u;
       }
     }
   }
-  // sigmoid(g . x_t), same lane order as the staged path (lane covers segments L, L+64, ...)
-  if (wave == kWaves - 1) {
+  // sigmoid(g . x_t) on block 0 (lane covers segments L, L + 64, ... as in the staged path)
+  if (blockIdx.x == 0 && wave == kWaves - 1) {
     const uint8_t* gvec = a.shared + a.shared_stride;
     const int nseg = H / kSegCodes;
     for (int t = 0; t < T; ++t) {
       float acc = 0.f;
       if (lane < nseg) {
         float xv[kSegCodes], gv[kSegCodes];
-        lds_act_seg<ACT>(s.x + t * xrow, lane, xv);
+        load_act_seg<ACT>(s.x + t * xrow, lane, xv);
         load_act_seg<ACT>(gvec, lane, gv);
 #pragma unroll
         for (int c = 0; c < kSegCodes; ++c) acc = fmaf(xv[c], gv[c], acc);
       }
       acc = group_sum(acc, kWave);
-      if (lane == 0) s.sig[t] = sigmoid(acc);
+      if (lane == 0) a.sig[t] = sigmoid(acc);
     }
   }
 
   // ---- phase K: gather all logits (tag-checked), top-k, dispatch
-  publish_block_flag(a.flag_r, tag);
-  if (wave == 0 && !wait_block_flags(a.flag_r, a.nb, tag, lane, spins, a.spin_limit)) timed_out = true;
+  if (blockIdx.x < router_blocks) publish_block_flag(a.flag_r, tag);
+  if (wave == 0 && !wait_block_flags(a.flag_r, router_blocks, tag, lane, spins, a.spin_limit)) timed_out = true;
   __syncthreads();
   for (;;) {
     int missing = 0;
@@ -391,11 +343,11 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
     }
     if (!__syncthreads_or(missing)) break;
     if (++spins > a.spin_limit) { timed_out = true; break; }
-    __builtin_amdgcn_s_sleep(8);
+    __builtin_amdgcn_s_sleep(2);
   }
   for (int t = wave; t < T; t += kWaves)
     topk_wave(s.lg + static_cast<size_t>(t) * E, E, k, lane, s.cand_k + wave * kCandMax, s.cand_i + wave * kCandMax,
-              s.ids + t * k, s.wts + t * k);
+              s.ev + wave * 64, s.ids + t * k, s.vals + t * k);
   for (int e = tid; e < E; e += kThreads) s.umap[e] = -1;
   __syncthreads();
   for (int p = tid; p < T * k; p += kThreads) {
@@ -420,32 +372,22 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
   const int U = s.misc[0];
   for (int i = tid; i < U * T; i += kThreads) s.pidx[i] = -1;
   __syncthreads();
-  for (int p = tid; p < T * k; p += kThreads) {
-    const int t = p / k, i = p % k;
-    s.pidx[s.umap[s.ids[p]] * T + t] = i;
-  }
-  if (blockIdx.x == 0) {
-    for (int p = tid; p < T * k; p += kThreads) {
-      if (a.ids_out) a.ids_out[p] = s.ids[p];
-      if (a.wts_out) a.wts_out[p] = s.wts[p];
-    }
-  }
+  for (int p = tid; p < T * k; p += kThreads) s.pidx[s.umap[s.ids[p]] * T + p / k] = p % k;
   __syncthreads();
-
-  // ---- phase D prefetch: this block's output rows.  Down tasks are (expert j, pass p)
-  // for j < U (routed, distinct) and j == U (shared), passes of rpp rows each;
-  // wave w takes tasks w, w + 4, ... in rounds of kMaxDownPerWave.
-  const RowLanes rli = row_lanes(a.I, lane);
-  const RowLanes rls = row_lanes(a.SI, lane);
-  const int row_lo = blockIdx.x * a.rb;
-  const int nd = U + 1;
-  const int rpp_min = rli.rpp < rls.rpp ? rli.rpp : rls.rpp;
-  const int np = (a.rb + rpp_min - 1) / rpp_min;
-  const int ntask = nd * np;
-  DownTask<BITS> dt[kMaxDownPerWave];
-#pragma unroll
-  for (int q = 0; q < kMaxDownPerWave; ++q)
-    load_down_task<BITS, SB>(dt[q], wave + q * kWaves, ntask, np, U, row_lo, a, s, rli, rls, lane, flags);
+  if (blockIdx.x == 0) {
+    // routing record for launch B (and the optional outputs)
+    for (int p = tid; p < T * k; p += kThreads) {
+      a.wts[p] = s.vals[p];
+      if (a.ids_out) a.ids_out[p] = s.ids[p];
+      if (a.wts_out) a.wts_out[p] = s.vals[p];
+    }
+    for (int i = tid; i < U * T; i += kThreads) a.pidx[i] = s.pidx[i];
+    for (int i = tid; i < U; i += kThreads) {
+      a.uniq[i] = s.uniq[i];
+      a.uoff[i] = s.slot[s.uniq[i]];
+    }
+    if (tid == 0) *a.ucount = U;
+  }
 
   // ---- phase G: routed gate/up rows, flattened over (expert, row group)
   {
@@ -468,6 +410,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
       for (int b = 0; b < kBatch; ++b) {
         const int g = g0 + b;
         uu[b] = -1;
+        rr[b] = 0;
         vv[b] = false;
         if (g < g_hi) {
           const int u = g / groups_per_expert;
@@ -488,7 +431,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
             bg[b] = load_scalar<SB>(blob + 3 * pl.q + 3 * pl.s, si);
             bu[b] = load_scalar<SB>(blob + 3 * pl.q + 4 * pl.s, si);
           } else if (lane == 0) {
-            raise_error(flags, kErrRange);
+            raise_error(a.ctrl, kErrRange);
           }
         }
         if (!vv[b]) {
@@ -499,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
       }
       for (int t = 0; t < T; ++t) {
         float v[1][kSegCodes];
-        lds_act_seg<ACT>(s.x + t * xrow, rlh.seg0, v[0]);
+        load_act_seg<ACT>(s.x + t * xrow, rlh.seg0, v[0]);
         const float xs = seg_sum(v[0]);
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
@@ -515,48 +458,148 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
           const float g = group_sum(accg, rlh.width);
           const float u = group_sum(accu, rlh.width);
           if ((lane % rlh.width) == 0)
-            store_tagged(a.hx + (static_cast<size_t>(t) * k + i) * a.hs + rr[b], vv[b] ? silu(g) * u : 0.f, tag);
+            a.h[(static_cast<size_t>(t) * k + i) * a.hs + rr[b]] = vv[b] ? silu(g) * u : 0.f;
         }
       }
     }
   }
+  if (timed_out && lane == 0) raise_error(a.ctrl, kErrTimeout);
+  // Block 0 retires the tag once every block's arrival word shows that it has
+  // read the epoch (by now they all have; the check makes it certain).
+  if (blockIdx.x == 0 && wave == 0) {
+    if (!wait_block_flags(a.arrive, a.nb, tag, lane, spins, a.spin_limit) && lane == 0) raise_error(a.ctrl, kErrTimeout);
+    if (lane == 0) __hip_atomic_store(a.ctrl + 1, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
 
-  // ---- phase D: down rows of this block for every (token, expert) pair
-  publish_block_flag(a.flag_g, tag);
-  if (wave == 0 && !wait_block_flags(a.flag_g, a.nb, tag, lane, spins, a.spin_limit)) timed_out = true;
-  __syncthreads();
-  for (int base = 0; base < ntask; base += kWaves * kMaxDownPerWave) {
-    if (base > 0) {
+// ---------------------------------------------------------------------------
+// Launch B: down projection of this block's output rows for every (token,
+// expert) pair and the shared expert, then the ordered combine.
+// One task = `rpp` rows of one expert's Wd (lane: one segment of one row).
+template <int BITS>
+struct DownTask {
+  Seg<BITS> code;
+  float sc, bi;
+  int j;        // distinct-expert index (U = shared), -1 if none
+  int rloc;     // this lane's row within the block, -1 if outside
+  bool valid;   // blob offset usable
+};
+
+struct LdsB {
+  int64_t* uoff;     // [umax] blob offsets of the distinct experts
+  int32_t* pidx;     // [umax][T]
+  float* wts;        // [T][k]
+  float* sig;        // [T]
+  float* part;       // [(T k + T)][rb]
+};
+
+__device__ inline LdsB carve_b(uint8_t* base, const FusedArgs& a) {
+  LdsB s;
+  size_t o = 0;
+  auto take = [&](size_t n) { uint8_t* p = base + o; o += (n + 15) / 16 * 16; return p; };
+  s.uoff = reinterpret_cast<int64_t*>(take(static_cast<size_t>(a.umax) * 8));
+  s.pidx = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.umax) * a.T * 4));
+  s.wts = reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * a.k * 4));
+  s.sig = reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * 4));
+  s.part = reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * (a.k + 1) * a.rb * 4));
+  return s;
+}
+
+template <int BITS, int SB>
+__device__ __forceinline__ void load_down_task(DownTask<BITS>& d, int task, int ntask, int np, int U, int row_lo,
+                                               const FusedArgs& a, const LdsB& s, const RowLanes& rli,
+                                               const RowLanes& rls) {
+  d.j = -1;
+  d.rloc = -1;
+  d.valid = false;
+  d.sc = 0.f;
+  d.bi = 0.f;
 #pragma unroll
-      for (int q = 0; q < kMaxDownPerWave; ++q)
-        load_down_task<BITS, SB>(dt[q], base + wave + q * kWaves, ntask, np, U, row_lo, a, s, rli, rls, lane, flags);
+  for (int i = 0; i < BITS / 4; ++i) d.code.w[i] = u32x4{0, 0, 0, 0};
+  if (task >= ntask) return;
+  const int j = task / np, p = task % np;
+  const bool is_sh = j == U;
+  const RowLanes& rl = is_sh ? rls : rli;
+  const int inter = is_sh ? a.SI : a.I;
+  const Planes pl = planes_of(a.H, inter, BITS, SB);
+  const uint8_t* blob = a.shared;
+  bool valid = true;
+  if (!is_sh) {
+    const int64_t off = s.uoff[j];
+    valid = slot_ok(off, pl.blob, a.pool_bytes);
+    blob = a.pool + (valid ? off : 0);
+  }
+  d.j = j;
+  d.valid = valid;
+  const int rloc = p * rl.rpp + rl.sub_row;
+  const int r = row_lo + rloc;
+  if (rloc < a.rb && r < a.H) {
+    d.rloc = rloc;
+    if (valid) {
+      const int64_t row_bytes = static_cast<int64_t>(inter) * BITS / 8;
+      d.code = load_codes<BITS>(blob + 2 * pl.q + r * row_bytes + static_cast<int64_t>(rl.seg0) * (kSegCodes * BITS / 8));
+      const size_t si = static_cast<size_t>(r) * (inter / 64) + rl.seg0 / 2;
+      d.sc = load_scalar<SB>(blob + 3 * pl.q + 2 * pl.s, si);
+      d.bi = load_scalar<SB>(blob + 3 * pl.q + 5 * pl.s, si);
+    }
+  }
+}
+
+template <int BITS, int SB, int OUT>
+__global__ __launch_bounds__(kThreads) void k_decode_b(FusedArgs a) {
+  extern __shared__ __align__(16) uint8_t lds_raw[];
+  const LdsB s = carve_b(lds_raw, a);
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int T = a.T, k = a.k;
+  const int U = *a.ucount;
+  for (int i = tid; i < U; i += kThreads) s.uoff[i] = a.uoff[i];
+  for (int i = tid; i < U * T; i += kThreads) s.pidx[i] = a.pidx[i];
+  for (int i = tid; i < T * k; i += kThreads) s.wts[i] = a.wts[i];
+  for (int i = tid; i < T; i += kThreads) s.sig[i] = a.sig[i];
+  __syncthreads();
+
+  const RowLanes rli = row_lanes(a.I, lane);
+  const RowLanes rls = row_lanes(a.SI, lane);
+  const int row_lo = blockIdx.x * a.rb;
+  const int nd = U + 1;
+  const int rpp_min = rli.rpp < rls.rpp ? rli.rpp : rls.rpp;
+  const int np = (a.rb + rpp_min - 1) / rpp_min;
+  const int ntask = nd * np;
+  DownTask<BITS> dt[kMaxDownPerWave];
+  float hv[kMaxDownPerWave][1][kSegCodes];
+  int t0[kMaxDownPerWave];
+  for (int base = 0; base < ntask; base += kWaves * kMaxDownPerWave) {
+    // codes of this round's tasks and the h segment of each task's first pair,
+    // all requested before any compute
+#pragma unroll
+    for (int q = 0; q < kMaxDownPerWave; ++q) {
+      load_down_task<BITS, SB>(dt[q], base + wave + q * kWaves, ntask, np, U, row_lo, a, s, rli, rls);
+      t0[q] = -1;
+      if (dt[q].j >= 0) {
+        const bool is_sh = dt[q].j == U;
+        int t = 0;
+        if (!is_sh)
+          while (t < T && s.pidx[dt[q].j * T + t] < 0) ++t;
+        t0[q] = t;
+        const size_t pair = is_sh ? static_cast<size_t>(T) * k : static_cast<size_t>(t) * k + s.pidx[dt[q].j * T + t];
+        load_f32_seg(a.h + pair * a.hs, (is_sh ? rls : rli).seg0, hv[q][0]);
+      }
     }
 #pragma unroll
     for (int q = 0; q < kMaxDownPerWave; ++q) {
       if (dt[q].j < 0) continue;
       const bool is_sh = dt[q].j == U;
       const RowLanes& rl = is_sh ? rls : rli;
-      for (int t = 0; t < T; ++t) {
+      for (int t = t0[q]; t < T; ++t) {
         const int i = is_sh ? k : s.pidx[dt[q].j * T + t];
         if (i < 0) continue;
         const size_t pair = is_sh ? static_cast<size_t>(T) * k + t : static_cast<size_t>(t) * k + i;
-        const uint64_t* hp = a.hx + pair * a.hs + rl.seg0 * kSegCodes;
-        float hv[1][kSegCodes];
-        for (;;) {
-          bool ready = true;
-#pragma unroll
-          for (int c = 0; c < kSegCodes; ++c) {
-            const uint64_t w = load_tagged(hp + c);
-            ready &= static_cast<uint32_t>(w >> 32) == tag;
-            hv[0][c] = __uint_as_float(static_cast<uint32_t>(w));
-          }
-          if (__all(ready)) break;
-          if (++spins > a.spin_limit) { timed_out = true; break; }
-          __builtin_amdgcn_s_sleep(8);
-        }
-        const float hs = seg_sum(hv[0]);
+        if (t != t0[q]) load_f32_seg(a.h + pair * a.hs, rl.seg0, hv[q][0]);
+        const float hs = seg_sum(hv[q][0]);
         float qv[1];
-        seg_qdot_nt<BITS, 1>(dt[q].code, hv, qv);
+        seg_qdot_nt<BITS, 1>(dt[q].code, hv[q], qv);
         float acc = 0.f;
         acc += seg_value(dt[q].sc, dt[q].bi, qv[0], hs);
         const float v = group_sum(acc, rl.width);
@@ -564,60 +607,65 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
       }
     }
   }
-  if (timed_out) s.misc[2] = 1;
   __syncthreads();
-  // ordered combine for this block's rows
   for (int idx = tid; idx < T * a.rb; idx += kThreads) {
     const int t = idx / a.rb, rloc = idx % a.rb;
     const int n = row_lo + rloc;
-    if (n >= H) continue;
+    if (n >= a.H) continue;
     float acc = 0.f;
     for (int i = 0; i < k; ++i) acc = fmaf(s.wts[t * k + i], s.part[(static_cast<size_t>(t) * k + i) * a.rb + rloc], acc);
     acc = fmaf(s.sig[t], s.part[(static_cast<size_t>(T) * k + t) * a.rb + rloc], acc);
     if constexpr (OUT == kF32) {
-      static_cast<float*>(a.out)[static_cast<size_t>(t) * H + n] = acc;
+      static_cast<float*>(a.out)[static_cast<size_t>(t) * a.H + n] = acc;
     } else {
-      static_cast<uint16_t*>(a.out)[static_cast<size_t>(t) * H + n] = f32_to_bf16(acc);
+      static_cast<uint16_t*>(a.out)[static_cast<size_t>(t) * a.H + n] = f32_to_bf16(acc);
     }
   }
-  if (tid == 0 && s.misc[2]) raise_error(flags, kErrTimeout);
-  // Every block read the epoch before raising its phase-R flag, and block 0
-  // saw all those flags in phase K, so it can retire the tag now.
-  if (blockIdx.x == 0 && tid == 0) __hip_atomic_store(a.ctrl + 1, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-}  // namespace
-
-size_t fused_lds_bytes(int T, int H, int E, int k, int umax, int rb, int act_sz) {
+size_t lds_bytes_a(int T, int H, int E, int k, int umax, int act_sz) {
   size_t o = 0;
   auto take = [&](size_t n) { o += (n + 15) / 16 * 16; };
   take(static_cast<size_t>(T) * H * act_sz);
   take(static_cast<size_t>(T) * E * 4);
   take(static_cast<size_t>(T) * k * 4);
   take(static_cast<size_t>(T) * k * 4);
-  take(static_cast<size_t>(T) * 4);
+  take(kWaves * 64 * 4);
   take(static_cast<size_t>(E) * 8);
   take(static_cast<size_t>(E) * 4);
   take(static_cast<size_t>(umax) * 4);
   take(static_cast<size_t>(umax) * T * 4);
-  take(static_cast<size_t>(T) * (k + 1) * rb * 4);
   take(kWaves * kCandMax * 4);
   take(kWaves * kCandMax * 4);
   take(16 * 4);
   return o;
 }
 
+size_t lds_bytes_b(int T, int k, int umax, int rb) {
+  size_t o = 0;
+  auto take = [&](size_t n) { o += (n + 15) / 16 * 16; };
+  take(static_cast<size_t>(umax) * 8);
+  take(static_cast<size_t>(umax) * T * 4);
+  take(static_cast<size_t>(T) * k * 4);
+  take(static_cast<size_t>(T) * 4);
+  take(static_cast<size_t>(T) * (k + 1) * rb * 4);
+  return o;
+}
+
+}  // namespace
+
 template <int BITS, int SB, int ACT, int OUT>
-static int launch_variant(const FusedArgs& a, size_t lds, hipStream_t stream) {
-  auto kern = k_decode_fused<BITS, SB, ACT, OUT>;
-  hipLaunchKernelGGL(kern, dim3(a.nb), dim3(kThreads), lds, stream, a);
+static int launch_variant(const FusedArgs& a, const FusedPlan& p, hipStream_t stream) {
+  hipLaunchKernelGGL((k_decode_a<BITS, SB, ACT>), dim3(p.nb), dim3(kThreads), p.lds, stream, a);
+  FusedArgs b = a;
+  b.rb = p.rb_b;
+  hipLaunchKernelGGL((k_decode_b<BITS, SB, OUT>), dim3(p.nb_b), dim3(kThreads), p.lds_b, stream, b);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 template <int BITS, int SB, int ACT, int OUT>
 static int occupancy_variant(size_t lds, int* blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_decode_fused<BITS, SB, ACT, OUT>, kThreads, lds) ==
-                 hipSuccess
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_decode_a<BITS, SB, ACT>, kThreads, lds) == hipSuccess
              ? MOE_OK
              : MOE_EHIP;
 }
@@ -636,16 +684,14 @@ static int occupancy_variant(size_t lds, int* blocks) {
 
 static int fused_occupancy(const moe_desc& d, size_t lds, int* blocks) { FUSED_DISPATCH(occupancy_variant, lds, blocks); }
 
-static int fused_launch(const moe_desc& d, const FusedArgs& a, size_t lds, hipStream_t s) {
-  FUSED_DISPATCH(launch_variant, a, lds, s);
+static int fused_launch(const moe_desc& d, const FusedArgs& a, const FusedPlan& p, hipStream_t s) {
+  FUSED_DISPATCH(launch_variant, a, p, s);
 }
 
 bool fused_supported(const moe_desc& d, int T) {
   if (T < 1 || T > kFusedMaxT) return false;
-  const int b = d.bits, s = d.sb_dtype, a = d.act_dtype;
-  const bool combo = (s == kBF16 && a == kBF16) || (s == kF32 && a == kF32 && d.out_dtype == kF32);
-  (void)b;
-  return combo;
+  const int s = d.sb_dtype, a = d.act_dtype;
+  return (s == kBF16 && a == kBF16) || (s == kF32 && a == kF32 && d.out_dtype == kF32);
 }
 
 int fused_plan(const moe_desc& d, int T, FusedPlan* plan) {
@@ -655,20 +701,23 @@ int fused_plan(const moe_desc& d, int T, FusedPlan* plan) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MOE_ENODEV;
   const int act_sz = d.act_dtype == kF32 ? 4 : 2;
   const int umax = T * d.top_k < d.n_experts ? T * d.top_k : d.n_experts;
-  // blocks: two per CU when they fit, else one; each block owns rb output rows
+  const size_t lds = lds_bytes_a(T, d.hidden, d.n_experts, d.top_k, umax, act_sz);
+  if (lds > 64 * 1024) return MOE_EINVAL;
+  // launch A: two resident blocks per CU when they fit, else one
   for (int per_cu = 2; per_cu >= 1; --per_cu) {
     const int nb = cus * per_cu;
     if (nb > kFusedMaxBlocks) continue;
-    const int rb = (d.hidden + nb - 1) / nb;
-    const size_t lds = fused_lds_bytes(T, d.hidden, d.n_experts, d.top_k, umax, rb, act_sz);
     int fit = 0;
-    if (lds > 160 * 1024) continue;
     if (fused_occupancy(d, lds, &fit) != MOE_OK) return MOE_EHIP;
     if (fit >= per_cu) {
       plan->nb = nb;
-      plan->rb = rb;
       plan->lds = lds;
       plan->umax = umax;
+      // launch B: a few output rows per block, two blocks per CU
+      plan->nb_b = cus * 2;
+      plan->rb_b = (d.hidden + plan->nb_b - 1) / plan->nb_b;
+      plan->nb_b = (d.hidden + plan->rb_b - 1) / plan->rb_b;
+      plan->lds_b = lds_bytes_b(T, d.top_k, umax, plan->rb_b);
       return MOE_OK;
     }
   }
@@ -687,10 +736,16 @@ int launch_decode_fused(const Call& c, const FusedPlan& plan) {
   a.ids_out = c.ids_out;
   a.wts_out = c.wts_out;
   a.lg = reinterpret_cast<uint64_t*>(c.ws + c.L.f_lg);
-  a.hx = reinterpret_cast<uint64_t*>(c.ws + c.L.f_hx);
+  a.h = reinterpret_cast<float*>(c.ws + c.L.h);
+  a.wts = reinterpret_cast<float*>(c.ws + c.L.wts);
+  a.sig = reinterpret_cast<float*>(c.ws + c.L.gate);
+  a.ucount = reinterpret_cast<int32_t*>(c.ws + c.L.ucount);
+  a.uniq = reinterpret_cast<int32_t*>(c.ws + c.L.uniq);
+  a.uoff = reinterpret_cast<int64_t*>(c.ws + c.L.f_uoff);
+  a.pidx = reinterpret_cast<int32_t*>(c.ws + c.L.f_pidx);
   a.ctrl = reinterpret_cast<uint32_t*>(c.ws + c.L.ctrl);
   a.flag_r = reinterpret_cast<uint32_t*>(c.ws + c.L.f_arrive);
-  a.flag_g = a.flag_r + kFusedMaxBlocks;
+  a.arrive = a.flag_r + kFusedMaxBlocks;
   a.pool_bytes = d.pool_bytes;
   a.shared_stride = d.shared_stride;
   a.T = c.T;
@@ -701,11 +756,11 @@ int launch_decode_fused(const Call& c, const FusedPlan& plan) {
   a.SI = d.shared_inter;
   a.hs = c.L.hstride;
   a.nb = plan.nb;
-  a.rb = plan.rb;
+  a.rb = plan.rb_b;
   a.umax = plan.umax;
   a.act_sz = d.act_dtype == kF32 ? 4 : 2;
   a.spin_limit = 1u << 20;
-  return fused_launch(d, a, plan.lds, c.stream);
+  return fused_launch(d, a, plan, c.stream);
 }
 
 }  // namespace moe

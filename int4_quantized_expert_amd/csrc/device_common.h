@@ -11,8 +11,8 @@
 //     This is w.v with w = s q + b regrouped per group (affine dequantisation,
 //     Swiftlet README translation, "Relation to TurboFieldfare").
 //   * A row's segments are summed per lane in segment order, then across the
-//     lanes of the row with an xor butterfly, which leaves the bitwise same
-//     total on every lane of the row.
+//     lanes of the row with symmetric pairwise steps (group_sum), which leave
+//     the bitwise same total on every lane of the row.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -125,10 +125,24 @@ __device__ __forceinline__ float seg_value(float s, float b, float qx, float xs)
   return fmaf(s, qx, b * xs);
 }
 
-// Sum over aligned groups of `width` lanes (power of two <= 64); every lane of
-// a group ends with the same bits.
+// DPP move of a float within a row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of `width` lanes (power of two <= 64).  Each step
+// adds the value of a partner lane that adds ours back (mirror within 16,
+// mirror within 8, reversal within 4, swap of neighbours; then xor 16, 32),
+// so every lane of a group ends with the bitwise same total.  The first four
+// steps are DPP moves, which cost a few cycles instead of an LDS round trip.
 __device__ __forceinline__ float group_sum(float v, int width) {
-  for (int m = width >> 1; m > 0; m >>= 1) v += __shfl_xor(v, m, kWave);
+  if (width >= 16) v += dpp_f32<0x140>(v);   // row_mirror
+  if (width >= 8) v += dpp_f32<0x141>(v);    // row_half_mirror
+  if (width >= 4) v += dpp_f32<0x1B>(v);     // quad_perm [3, 2, 1, 0]
+  if (width >= 2) v += dpp_f32<0xB1>(v);     // quad_perm [1, 0, 3, 2]
+  if (width >= 32) v += __shfl_xor(v, 16, kWave);
+  if (width >= 64) v += __shfl_xor(v, 32, kWave);
   return v;
 }
 

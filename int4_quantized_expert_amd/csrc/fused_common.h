@@ -1,4 +1,4 @@
-// Arguments and launch plan of the fused decode kernel.
+// Arguments and launch plan of the two-launch decode path.
 #pragma once
 
 #include <stddef.h>
@@ -6,7 +6,7 @@
 
 namespace moe {
 
-constexpr int kFusedMaxT = 8;   // tokens per call handled by the fused decode kernel
+constexpr int kFusedMaxT = 8;   // tokens per call handled by the two-launch decode path
 
 struct FusedArgs {
   const void* x;
@@ -18,25 +18,33 @@ struct FusedArgs {
   int32_t* ids_out;     // optional [T, k]
   float* wts_out;       // optional [T, k]
   uint64_t* lg;         // [T, E] tagged logits
-  uint64_t* hx;         // [T k + T, hs] tagged SwiGLU activations
+  float* h;             // [T k + T, hs] SwiGLU activations
+  float* wts;           // [T, k] renormalised weights (routing record)
+  float* sig;           // [T] sigmoid(g . x)
+  int32_t* ucount;      // number of distinct experts U
+  int32_t* uniq;        // [umax] distinct experts, ascending id
+  int64_t* uoff;        // [umax] their blob offsets
+  int32_t* pidx;        // [umax, T] rank of expert u for token t, or -1
   uint32_t* ctrl;       // [0] error flags, [1] epoch
   uint32_t* flag_r;     // [nb] per-block "phase R stores done" tags
-  uint32_t* flag_g;     // [nb] per-block "phase G stores done" tags
+  uint32_t* arrive;     // [nb] per-block "epoch read" tags
   int64_t pool_bytes;
   int64_t shared_stride;
   int T, H, E, k, I, SI, hs;
-  int nb;               // blocks (all resident)
-  int rb;               // output rows per block
+  int nb;               // launch A blocks (all resident)
+  int rb;               // launch B output rows per block
   int umax;             // min(T k, E)
   int act_sz;
   uint32_t spin_limit;
 };
 
 struct FusedPlan {
-  int nb;
-  int rb;
+  int nb;       // launch A grid
+  size_t lds;   // launch A dynamic LDS
   int umax;
-  size_t lds;
+  int nb_b;     // launch B grid
+  int rb_b;     // launch B rows per block
+  size_t lds_b; // launch B dynamic LDS
 };
 
 }  // namespace moe

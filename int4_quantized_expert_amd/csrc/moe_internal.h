@@ -27,8 +27,9 @@ struct WsLayout {
   size_t h;          // [T k + T, max(I, SI)] float32 SwiGLU activations
   size_t partial;    // [T k + T, H] float32 per-pair down projections
   size_t f_lg;       // fused path: [T, E] tagged logits (uint64)
-  size_t f_hx;       // fused path: [T k + T, max(I, SI)] tagged activations (uint64)
-  size_t f_arrive;   // fused path: [2][kFusedMaxBlocks] uint32 per-block phase flags
+  size_t f_uoff;     // two-launch path: [min(T k, E)] int64 blob offsets of the distinct experts
+  size_t f_pidx;     // two-launch path: [min(T k, E), T] int32 rank of expert u for token t
+  size_t f_arrive;   // two-launch path: [2][kFusedMaxBlocks] uint32 per-block flags and arrival tags
   size_t total;
   int32_t umax;      // min(T k, E)
   int32_t hstride;   // max(I, SI)
@@ -56,7 +57,8 @@ inline WsLayout ws_layout(const moe_desc& d, int32_t T) {
   L.h = take((Tk + T) * static_cast<size_t>(hs) * 4);
   L.partial = take((Tk + T) * static_cast<size_t>(d.hidden) * 4);
   L.f_lg = take(static_cast<size_t>(T) * d.n_experts * 8);
-  L.f_hx = take((Tk + T) * static_cast<size_t>(hs) * 8);
+  L.f_uoff = take(static_cast<size_t>(umax) * 8);
+  L.f_pidx = take(static_cast<size_t>(umax) * T * 4);
   L.total = o;
   L.umax = umax;
   L.hstride = hs;
@@ -86,7 +88,7 @@ int launch_router_topk(const Call& c, int32_t* ids_dst, float* wts_dst);
 int launch_experts(const Call& c);
 int launch_ws_init(uint8_t* ws, size_t bytes, hipStream_t stream);
 
-// Fused single-launch decode (T <= kFusedMaxT).
+// Two-launch decode (T <= kFusedMaxT).
 bool fused_supported(const moe_desc& d, int T);
 int fused_plan(const moe_desc& d, int T, FusedPlan* plan);
 int launch_decode_fused(const Call& c, const FusedPlan& plan);
