@@ -18,9 +18,11 @@
 //
 // Inside launch A only the logits cross blocks.  They travel as 64-bit words
 // holding the float bits and a per-call tag, written and read with relaxed
-// device-scope atomics; each block raises a flag word once its phase-R stores
-// are acknowledged, and waits for every block's flag before reading the
-// logits.  A word is valid when its tag matches, so no fence is needed (an
+// device-scope atomics; each router block raises a flag word once its phase-R
+// stores are acknowledged, and every block waits for those flags before
+// reading the logits.  Logits and flags are written in kFusedReplicas copies
+// and each block reads the copy of its index modulo kFusedReplicas: hundreds of
+// blocks polling the same few cache lines otherwise queue up behind each other.  A word is valid when its tag matches, so no fence is needed (an
 // agent-scope release on this chip writes back the L2 and costs microseconds).
 // The tag is the workspace epoch + 1; block 0 retires it at its end, after it
 // has seen every block's flag.  Every wait is bounded: on expiry the kernel
@@ -81,10 +83,13 @@ __device__ __forceinline__ bool wait_block_flags(const uint32_t* f, int n, uint3
 // All of this block's stores are acknowledged, then thread 0 raises its flag.
 // The flag only says the tagged words should be there: readers still check
 // every word's tag.
+// The flag is written to kFusedReplicas copies (kFusedMaxBlocks words apart),
+// so that each copy is read by only a fraction of the blocks.
 __device__ __forceinline__ void publish_block_flag(uint32_t* f, uint32_t tag) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(f + blockIdx.x, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x < kFusedReplicas)
+    __hip_atomic_store(f + threadIdx.x * kFusedMaxBlocks + blockIdx.x, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void wave_sync_lds() {
@@ -103,8 +108,7 @@ struct LdsA {
   int32_t* umap;     // [E] expert -> distinct index
   int32_t* uniq;     // [umax]
   int32_t* pidx;     // [umax][T] rank i of the expert for token t, or -1
-  uint32_t* cand_k;  // [kWaves][kCandMax]
-  int32_t* cand_i;   // [kWaves][kCandMax]
+  uint64_t* cand;    // [kWaves][kCandMax] packed candidates
   int32_t* misc;     // [0] U, [1] tag
 };
 
@@ -121,62 +125,82 @@ __device__ inline LdsA carve_a(uint8_t* base, const FusedArgs& a) {
   s.umap = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.E) * 4));
   s.uniq = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.umax) * 4));
   s.pidx = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.umax) * a.T * 4));
-  s.cand_k = reinterpret_cast<uint32_t*>(take(kWaves * kCandMax * 4));
-  s.cand_i = reinterpret_cast<int32_t*>(take(kWaves * kCandMax * 4));
+  s.cand = reinterpret_cast<uint64_t*>(take(kWaves * kCandMax * 8));
   s.misc = reinterpret_cast<int32_t*>(take(16 * 4));
   return s;
 }
 
 // ---------------------------------------------------------------------------
-// Top-k of one token on one wave.  The k-th largest per-lane maximum is a
-// lower bound of the k-th largest logit, so every top-k logit is at least it;
-// the candidates above the bound (usually a few more than k) are ranked
-// exactly by (logit desc, id asc).  If more than kCandMax candidates lie above
-// the bound, k rounds of a wave arg-max finish the job.
-// Output: ids[0..k) and vals[0..k) = renormalised weights p_i, computed with
-// the same operations and order as the staged kernel.
-__device__ __forceinline__ void topk_wave(const float* lg, int E, int k, int lane, uint32_t* ck, int32_t* ci, float* ev,
-                          int32_t* ids, float* vals) {
+// Top-k of one token on one wave.
+//  1. A threshold from the per-lane maxima: the k-th largest lane maximum,
+//     found by bisection on the top 16 bits of the order key, is a lower
+//     bound of the k-th largest logit, so every top-k logit is at or above it.
+//  2. The candidates at or above it (usually a few more than k) are packed as
+//     64-bit (key << 32 | ~id) words, so that "larger word" means "larger
+//     logit, then lower id", and ranked exactly against each other.
+//  3. If more than kCandMax candidates qualify, k rounds of a wave arg-max
+//     finish the job.
+// Output: ids[0..k) and vals[0..k) = renormalised weights p_i, formed with the
+// same operations and order as the staged kernel.
+__device__ __forceinline__ void topk_wave(const float* lg, int E, int k, int lane, uint64_t* cand, float* ev,
+                                          int32_t* ids, float* vals) {
+  const int nj = (E + kWave - 1) / kWave;   // <= 16
   uint32_t key[16];
   uint32_t lm = 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int e = lane + j * kWave;
-    const uint32_t kv = order_key(lg[e < E ? e : 0]);
-    key[j] = e < E ? (kv > 1u ? kv : 1u) : 0u;   // every real entry ranks above "no entry"
-    lm = key[j] > lm ? key[j] : lm;
+    uint32_t kv = 0u;
+    if (j < nj) {
+      kv = order_key(lg[e < E ? e : 0]);
+      kv = e < E ? (kv > 1u ? kv : 1u) : 0u;   // every real entry ranks above "no entry"
+    }
+    key[j] = kv;
+    lm = kv > lm ? kv : lm;
   }
   uint32_t theta = 0;
-  for (int b = 31; b >= 0; --b) {
+  for (int b = 31; b >= 16; --b) {
     const uint32_t c = theta | (1u << b);
     if (__popcll(__ballot(lm >= c)) >= static_cast<unsigned>(k)) theta = c;
   }
   int cnt = 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const bool in = key[j] != 0u && key[j] >= theta;
-    const uint64_t m = __ballot(in);
-    const int pos = cnt + __popcll(m & lane_mask_lt(lane));
-    if (in && pos < kCandMax) { ck[pos] = key[j]; ci[pos] = lane + j * kWave; }
-    cnt += __popcll(m);
+    if (j < nj) {
+      const bool in = key[j] != 0u && key[j] >= theta;
+      const uint64_t m = __ballot(in);
+      const int pos = cnt + __popcll(m & lane_mask_lt(lane));
+      const int id = lane + j * kWave;
+      const uint64_t w = (static_cast<uint64_t>(key[j]) << 32) | static_cast<uint32_t>(~id);
+      if (in && pos < kCandMax) cand[pos] = w;
+      cnt += __popcll(m);
+    }
   }
   if (cnt <= kCandMax) {
     wave_sync_lds();
-    if (lane >= cnt) { ck[lane] = 0u; ci[lane] = 0x7fffffff; }   // padding never outranks a candidate
+    if (lane >= cnt) cand[lane] = 0ull;                 // padding never outranks a candidate
     wave_sync_lds();
-    const uint32_t kc = ck[lane];
-    const int ic = ci[lane];
+    const uint64_t mine = cand[lane];
     int rank = 0;
-    const int cnt16 = (cnt + 15) & ~15;
-    for (int d0 = 0; d0 < cnt16; d0 += 16) {
+    const int cnt8 = (cnt + 7) & ~7;
+    const u32x4* c4 = reinterpret_cast<const u32x4*>(cand);
+    for (int d0 = 0; d0 < cnt8; d0 += 8) {
+      u32x4 q[4];
 #pragma unroll
-      for (int d = 0; d < 16; ++d) {
-        const uint32_t kd = ck[d0 + d];
-        const int id = ci[d0 + d];
-        rank += (kd > kc || (kd == kc && id < ic)) ? 1 : 0;
+      for (int i = 0; i < 4; ++i) q[i] = c4[d0 / 2 + i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint64_t w0 = (static_cast<uint64_t>(q[i][1]) << 32) | q[i][0];
+        const uint64_t w1 = (static_cast<uint64_t>(q[i][3]) << 32) | q[i][2];
+        rank += (w0 > mine) ? 1 : 0;
+        rank += (w1 > mine) ? 1 : 0;
       }
     }
-    if (lane < cnt && rank < k) { ids[rank] = ic; vals[rank] = lg[ic]; }
+    if (lane < cnt && rank < k) {
+      const int id = static_cast<int>(~static_cast<uint32_t>(mine));
+      ids[rank] = id;
+      vals[rank] = lg[id];
+    }
   } else {
     // rare: many candidates lie above the bound
     uint32_t taken = 0;
@@ -266,7 +290,9 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
           for (int c = 0; c < kSegCodes; ++c) acc = fmaf(v[c], r[c], acc);
         }
         acc = group_sum(acc, rlh.width);
-        if (active && (lane % rlh.width) == 0) store_tagged(a.lg + static_cast<size_t>(t) * E + e, acc, tag);
+        if (active)   // every lane of the row holds the sum: each stores some of the copies
+          for (int rep = lane % rlh.width; rep < kFusedReplicas; rep += rlh.width)
+            store_tagged(a.lg + (static_cast<size_t>(rep) * T + t) * E + e, acc, tag);
       }
     }
   }
@@ -332,12 +358,14 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
 
   // ---- phase K: gather all logits (tag-checked), top-k, dispatch
   if (blockIdx.x < router_blocks) publish_block_flag(a.flag_r, tag);
-  if (wave == 0 && !wait_block_flags(a.flag_r, router_blocks, tag, lane, spins, a.spin_limit)) timed_out = true;
+  const int rep = blockIdx.x % kFusedReplicas;
+  if (wave == 0 && !wait_block_flags(a.flag_r + rep * kFusedMaxBlocks, router_blocks, tag, lane, spins, a.spin_limit))
+    timed_out = true;
   __syncthreads();
   for (;;) {
     int missing = 0;
     for (int i = tid; i < T * E; i += kThreads) {
-      const uint64_t w = load_tagged(a.lg + i);
+      const uint64_t w = load_tagged(a.lg + static_cast<size_t>(rep) * T * E + i);
       if (static_cast<uint32_t>(w >> 32) != tag) missing = 1;
       else s.lg[i] = __uint_as_float(static_cast<uint32_t>(w));
     }
@@ -346,34 +374,51 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
     __builtin_amdgcn_s_sleep(2);
   }
   for (int t = wave; t < T; t += kWaves)
-    topk_wave(s.lg + static_cast<size_t>(t) * E, E, k, lane, s.cand_k + wave * kCandMax, s.cand_i + wave * kCandMax,
-              s.ev + wave * 64, s.ids + t * k, s.vals + t * k);
-  for (int e = tid; e < E; e += kThreads) s.umap[e] = -1;
-  __syncthreads();
-  for (int p = tid; p < T * k; p += kThreads) {
-    const int e = s.ids[p];
-    s.ids[p] = e >= 0 && e < E ? e : 0;           // ids come from [0, E) by construction
-    s.umap[s.ids[p]] = 0;                         // mark
-  }
-  __syncthreads();
-  if (wave == 0) {
-    int base = 0;
-    for (int c0 = 0; c0 < E; c0 += kWave) {
-      const int e = c0 + lane;
-      const bool used = e < E && s.umap[e] == 0;
-      const uint64_t m = __ballot(used);
-      const int pos = base + __popcll(m & lane_mask_lt(lane));
-      if (used) { s.uniq[pos] = e; s.umap[e] = pos; }
-      base += __popcll(m);
+    topk_wave(s.lg + static_cast<size_t>(t) * E, E, k, lane, s.cand + wave * kCandMax, s.ev + wave * 64,
+              s.ids + t * k, s.vals + t * k);
+  if (T == 1) {
+    // one token: its k experts are distinct; order them by id with a rank count
+    if (wave == 0) {
+      int e = lane < k ? s.ids[lane] : 0x7fffffff;
+      e = e >= 0 && e < E ? e : 0;
+      int r = 0;
+      for (int j = 0; j < k; ++j) r += s.ids[j] < e ? 1 : 0;
+      if (lane < k) {
+        s.uniq[r] = e;
+        s.pidx[r] = lane;
+      }
+      if (lane == 0) s.misc[0] = k;
     }
-    if (lane == 0) s.misc[0] = base;
+    __syncthreads();
+  } else {
+    for (int e = tid; e < E; e += kThreads) s.umap[e] = -1;
+    __syncthreads();
+    for (int p = tid; p < T * k; p += kThreads) {
+      const int e = s.ids[p];
+      s.ids[p] = e >= 0 && e < E ? e : 0;           // ids come from [0, E) by construction
+      s.umap[s.ids[p]] = 0;                         // mark
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int base = 0;
+      for (int c0 = 0; c0 < E; c0 += kWave) {
+        const int e = c0 + lane;
+        const bool used = e < E && s.umap[e] == 0;
+        const uint64_t m = __ballot(used);
+        const int pos = base + __popcll(m & lane_mask_lt(lane));
+        if (used) { s.uniq[pos] = e; s.umap[e] = pos; }
+        base += __popcll(m);
+      }
+      if (lane == 0) s.misc[0] = base;
+    }
+    __syncthreads();
+    const int Ud = s.misc[0];
+    for (int i = tid; i < Ud * T; i += kThreads) s.pidx[i] = -1;
+    __syncthreads();
+    for (int p = tid; p < T * k; p += kThreads) s.pidx[s.umap[s.ids[p]] * T + p / k] = p % k;
+    __syncthreads();
   }
-  __syncthreads();
   const int U = s.misc[0];
-  for (int i = tid; i < U * T; i += kThreads) s.pidx[i] = -1;
-  __syncthreads();
-  for (int p = tid; p < T * k; p += kThreads) s.pidx[s.umap[s.ids[p]] * T + p / k] = p % k;
-  __syncthreads();
   if (blockIdx.x == 0) {
     // routing record for launch B (and the optional outputs)
     for (int p = tid; p < T * k; p += kThreads) {
@@ -635,8 +680,7 @@ size_t lds_bytes_a(int T, int H, int E, int k, int umax, int act_sz) {
   take(static_cast<size_t>(E) * 4);
   take(static_cast<size_t>(umax) * 4);
   take(static_cast<size_t>(umax) * T * 4);
-  take(kWaves * kCandMax * 4);
-  take(kWaves * kCandMax * 4);
+  take(kWaves * kCandMax * 8);
   take(16 * 4);
   return o;
 }
@@ -745,7 +789,7 @@ int launch_decode_fused(const Call& c, const FusedPlan& plan) {
   a.pidx = reinterpret_cast<int32_t*>(c.ws + c.L.f_pidx);
   a.ctrl = reinterpret_cast<uint32_t*>(c.ws + c.L.ctrl);
   a.flag_r = reinterpret_cast<uint32_t*>(c.ws + c.L.f_arrive);
-  a.arrive = a.flag_r + kFusedMaxBlocks;
+  a.arrive = a.flag_r + kFusedReplicas * kFusedMaxBlocks;
   a.pool_bytes = d.pool_bytes;
   a.shared_stride = d.shared_stride;
   a.T = c.T;

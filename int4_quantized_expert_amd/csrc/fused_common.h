@@ -6,7 +6,8 @@
 
 namespace moe {
 
-constexpr int kFusedMaxT = 8;   // tokens per call handled by the two-launch decode path
+constexpr int kFusedMaxT = 8;       // tokens per call handled by the two-launch decode path
+constexpr int kFusedReplicas = 16;  // copies of the exchanged logits and flags
 
 struct FusedArgs {
   const void* x;
@@ -17,7 +18,7 @@ struct FusedArgs {
   void* out;
   int32_t* ids_out;     // optional [T, k]
   float* wts_out;       // optional [T, k]
-  uint64_t* lg;         // [T, E] tagged logits
+  uint64_t* lg;         // [kFusedReplicas][T, E] tagged logits
   float* h;             // [T k + T, hs] SwiGLU activations
   float* wts;           // [T, k] renormalised weights (routing record)
   float* sig;           // [T] sigmoid(g . x)
@@ -26,7 +27,7 @@ struct FusedArgs {
   int64_t* uoff;        // [umax] their blob offsets
   int32_t* pidx;        // [umax, T] rank of expert u for token t, or -1
   uint32_t* ctrl;       // [0] error flags, [1] epoch
-  uint32_t* flag_r;     // [nb] per-block "phase R stores done" tags
+  uint32_t* flag_r;     // [kFusedReplicas][kFusedMaxBlocks] "phase R stores done" tags
   uint32_t* arrive;     // [nb] per-block "epoch read" tags
   int64_t pool_bytes;
   int64_t shared_stride;

@@ -26,10 +26,10 @@ struct WsLayout {
   size_t plist;      // [T k] int32 pair indices (t * k + i) grouped by expert
   size_t h;          // [T k + T, max(I, SI)] float32 SwiGLU activations
   size_t partial;    // [T k + T, H] float32 per-pair down projections
-  size_t f_lg;       // fused path: [T, E] tagged logits (uint64)
+  size_t f_lg;       // two-launch path: [kFusedReplicas][T, E] tagged logits (uint64)
   size_t f_uoff;     // two-launch path: [min(T k, E)] int64 blob offsets of the distinct experts
   size_t f_pidx;     // two-launch path: [min(T k, E), T] int32 rank of expert u for token t
-  size_t f_arrive;   // two-launch path: [2][kFusedMaxBlocks] uint32 per-block flags and arrival tags
+  size_t f_arrive;   // two-launch path: [kFusedReplicas + 1][kFusedMaxBlocks] uint32 flags, then arrival tags
   size_t total;
   int32_t umax;      // min(T k, E)
   int32_t hstride;   // max(I, SI)
@@ -45,7 +45,7 @@ inline WsLayout ws_layout(const moe_desc& d, int32_t T) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes > 0 ? bytes : 1); return at; };
   L.ctrl = take(256);
-  L.f_arrive = take(2 * kFusedMaxBlocks * 4);
+  L.f_arrive = take((kFusedReplicas + 1) * kFusedMaxBlocks * 4);
   L.logits = take(static_cast<size_t>(T) * d.n_experts * 4);
   L.ids = take(Tk * 4);
   L.wts = take(Tk * 4);
@@ -56,7 +56,7 @@ inline WsLayout ws_layout(const moe_desc& d, int32_t T) {
   L.plist = take(Tk * 4);
   L.h = take((Tk + T) * static_cast<size_t>(hs) * 4);
   L.partial = take((Tk + T) * static_cast<size_t>(d.hidden) * 4);
-  L.f_lg = take(static_cast<size_t>(T) * d.n_experts * 8);
+  L.f_lg = take(static_cast<size_t>(kFusedReplicas) * T * d.n_experts * 8);
   L.f_uoff = take(static_cast<size_t>(umax) * 8);
   L.f_pidx = take(static_cast<size_t>(umax) * T * 4);
   L.total = o;
