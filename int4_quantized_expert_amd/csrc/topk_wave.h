@@ -1,0 +1,140 @@
+// Top-k selection of one token's router logits on one wave (gfx950, wave64).
+//
+// Ranks the experts by (logit descending, id ascending), so ties go to the
+// lower id, and forms the renormalised weights p_i = exp(l_i - l_0) /
+// sum_j exp(l_j - l_0) over the chosen logits in rank order.  Reading of the
+// pages: the router picks the top k of E experts per token (Swiftlet README
+// translation, "How it works"); the weights are the softmax over all experts
+// renormalised over the chosen ones, whose full denominator cancels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+
+namespace moe {
+
+constexpr int kCandMax = 64;   // candidates ranked exactly before the fallback
+
+// Monotone map from float to uint32 order keys (larger float, larger key);
+// +0 and -0 map to the same key.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) == 0) return 0x80000000u;          // +0 and -0 rank equal
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t lane_mask_lt(int lane) { return lane == 0 ? 0ull : (~0ull >> (64 - lane)); }
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------------------
+// Top-k of one token on one wave.
+//  1. A threshold from the per-lane maxima: the k-th largest lane maximum,
+//     found by bisection on the top 16 bits of the order key, is a lower
+//     bound of the k-th largest logit, so every top-k logit is at or above it.
+//  2. The candidates at or above it (usually a few more than k) are packed as
+//     64-bit (key << 32 | ~id) words, so that "larger word" means "larger
+//     logit, then lower id", and ranked exactly against each other.
+//  3. If more than kCandMax candidates qualify, k rounds of a wave arg-max
+//     finish the job.
+// Output: ids[0..k) and vals[0..k) = renormalised weights p_i, formed with the
+// same operations and order as the staged kernel.
+__device__ __forceinline__ void topk_wave(const float* lg, int E, int k, int lane, uint64_t* cand, float* ev,
+                                          int32_t* ids, float* vals) {
+  const int nj = (E + kWave - 1) / kWave;   // <= 16
+  uint32_t key[16];
+  uint32_t lm = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int e = lane + j * kWave;
+    uint32_t kv = 0u;
+    if (j < nj) {
+      kv = order_key(lg[e < E ? e : 0]);
+      kv = e < E ? (kv > 1u ? kv : 1u) : 0u;   // every real entry ranks above "no entry"
+    }
+    key[j] = kv;
+    lm = kv > lm ? kv : lm;
+  }
+  uint32_t theta = 0;
+  for (int b = 31; b >= 16; --b) {
+    const uint32_t c = theta | (1u << b);
+    if (__popcll(__ballot(lm >= c)) >= static_cast<unsigned>(k)) theta = c;
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j < nj) {
+      const bool in = key[j] != 0u && key[j] >= theta;
+      const uint64_t m = __ballot(in);
+      const int pos = cnt + __popcll(m & lane_mask_lt(lane));
+      const int id = lane + j * kWave;
+      const uint64_t w = (static_cast<uint64_t>(key[j]) << 32) | static_cast<uint32_t>(~id);
+      if (in && pos < kCandMax) cand[pos] = w;
+      cnt += __popcll(m);
+    }
+  }
+  if (cnt <= kCandMax) {
+    wave_sync_lds();
+    if (lane >= cnt) cand[lane] = 0ull;                 // padding never outranks a candidate
+    wave_sync_lds();
+    const uint64_t mine = cand[lane];
+    int rank = 0;
+    const int cnt8 = (cnt + 7) & ~7;
+    const u32x4* c4 = reinterpret_cast<const u32x4*>(cand);
+    for (int d0 = 0; d0 < cnt8; d0 += 8) {
+      u32x4 q[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = c4[d0 / 2 + i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint64_t w0 = (static_cast<uint64_t>(q[i][1]) << 32) | q[i][0];
+        const uint64_t w1 = (static_cast<uint64_t>(q[i][3]) << 32) | q[i][2];
+        rank += (w0 > mine) ? 1 : 0;
+        rank += (w1 > mine) ? 1 : 0;
+      }
+    }
+    if (lane < cnt && rank < k) {
+      const int id = static_cast<int>(~static_cast<uint32_t>(mine));
+      ids[rank] = id;
+      vals[rank] = lg[id];
+    }
+  } else {
+    // rare: many candidates lie above the bound
+    uint32_t taken = 0;
+    for (int i = 0; i < k; ++i) {
+      uint32_t bk = 0;
+      int bid = 0x7fffffff;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int e = lane + j * kWave;
+        if (!((taken >> j) & 1u) && e < E && (key[j] > bk || (key[j] == bk && e < bid))) { bk = key[j]; bid = e; }
+      }
+#pragma unroll
+      for (int m = kWave / 2; m > 0; m >>= 1) {
+        const uint32_t ok = __shfl_xor(bk, m, kWave);
+        const int oid = __shfl_xor(bid, m, kWave);
+        if (ok > bk || (ok == bk && oid < bid)) { bk = ok; bid = oid; }
+      }
+      if ((bid & (kWave - 1)) == lane) taken |= 1u << (bid / kWave);
+      if (lane == 0) { ids[i] = bid; vals[i] = lg[bid]; }
+    }
+  }
+  wave_sync_lds();
+  // p_i = exp(l_i - l_0) / sum_j exp(l_j - l_0), the sum in rank order from 0
+  const float top = vals[0];
+  const float ex = lane < k ? expf(vals[lane] - top) : 0.f;
+  ev[lane] = ex;
+  wave_sync_lds();
+  float sum = 0.f;
+  for (int i = 0; i < k; ++i) sum += ev[i];
+  wave_sync_lds();
+  if (lane < k) vals[lane] = ex / sum;
+}
+
+}  // namespace moe
