@@ -153,14 +153,17 @@ int moe_layer_forward(const moe_desc* d, int32_t T, const void* x, const void* r
 
 /*
  * Which kernels run.  For 1 <= T <= 8 with bf16 activations and scales (or
- * float32 activations, scales and output) moe_layer_forward runs ONE fused
- * launch per layer: a grid whose blocks are all resident at once computes the
- * router, top-k, gate/up and down/combine, handing logits and activations
- * between blocks as tagged 64-bit words (no fences).  It needs every block
- * resident, i.e. the GPU's compute units not taken by other work; a wait that
- * expires raises MOE_ETIMEOUT in moe_status_check.  Larger T runs the staged
- * path (six launches).  moe_layer_forward_staged always runs the staged path;
- * both paths give bitwise identical results.
+ * float32 activations, scales and output) moe_layer_forward runs TWO launches
+ * per layer.  The first grid (all blocks resident at once) computes router
+ * logits, the shared expert's gate/up rows and the sigmoid gate, exchanges the
+ * logits between blocks as tagged 64-bit words (no fences), then every block
+ * takes top-k and dispatch redundantly and computes its share of the routed
+ * gate/up rows.  The second launch does the down projections and the ordered
+ * combine.  The first launch needs every block resident, i.e. the GPU's
+ * compute units not taken by other work; a bounded wait that expires raises
+ * MOE_ETIMEOUT in moe_status_check.  Larger T runs the staged path (six
+ * launches).  moe_layer_forward_staged always runs the staged path; both paths
+ * give bitwise identical results.
  */
 int moe_layer_forward_staged(const moe_desc* d, int32_t T, const void* x, const void* router_w,
                              const int64_t* slot_table, const void* pool_base, const void* shared_w,
@@ -185,6 +188,22 @@ int moe_experts_forward(const moe_desc* d, int32_t T, const void* x, const int32
                         const float* topk_w, const int64_t* slot_table, const void* pool_base,
                         const void* shared_w, void* out, void* workspace, size_t ws_bytes,
                         void* stream);
+
+/*
+ * Timing hook for profilers and benchmarks: the next moe_layer_forward,
+ * moe_layer_forward_staged, moe_router_topk or moe_experts_forward call made
+ * on this host thread launches its j-th kernel (j = 0, 1, ...) with events[2j]
+ * and events[2j+1] attached (hipExtLaunchKernel), so the runtime stamps them
+ * with that dispatch's own start and end: hipEventElapsedTime of the pair is
+ * the kernel's execution time.  Kernels beyond capacity / 2 launch untimed.
+ * The number of events used (2 per timed kernel) is stored in *n_recorded
+ * (host memory, written before that call returns).  The setting applies to
+ * that one call only and is cleared by it (also when it fails); events == NULL
+ * clears it now.  `events` holds hipEvent_t handles created by the caller with
+ * timing enabled; they stay owned by the caller.  Returns MOE_EINVAL if
+ * capacity < 1 or n_recorded is NULL while events is not.
+ */
+int moe_set_launch_events(void* const* events, int32_t capacity, int32_t* n_recorded);
 
 /*
  * Synchronises `stream`, then reports and clears the device-side error flags

@@ -9,9 +9,11 @@ if the library is missing, every call raises.
 from ._lib import (  # noqa: F401
     MOE_BF16,
     MOE_F32,
+    LaunchTimer,
     MoeDesc,
     MoeError,
     blob_bytes,
+    clear_launch_events,
     desc_for,
     experts_forward,
     layer_forward,

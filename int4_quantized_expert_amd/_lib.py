@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.moe_experts_forward.restype = ctypes.c_int
         L.moe_status_check.argtypes = [vp, vp]
         L.moe_status_check.restype = ctypes.c_int
+        L.moe_set_launch_events.argtypes = [ctypes.POINTER(vp), i32, ctypes.POINTER(i32)]
+        L.moe_set_launch_events.restype = ctypes.c_int
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -183,3 +185,36 @@ def experts_forward(d: MoeDesc, T: int, x, topk_ids, topk_w, slot_table, pool, s
 def status_check(ws, stream=None) -> None:
     """Blocking: raises MoeError(MOE_ERANGE) if a kernel skipped a pair since the last check."""
     _check(lib().moe_status_check(_ptr(ws), _stream(stream, ws)))
+
+
+class LaunchTimer:
+    """Per-kernel execution times of one library call, from moe_set_launch_events.
+
+    Holds `capacity` timing events (torch.cuda.Event objects, so their lifetime
+    is torch's); kernel j of the call gets events 2j and 2j+1, stamped by its
+    own dispatch.  arm() must directly precede the library call to be timed;
+    after a synchronize, kernel_us() gives one duration per kernel.
+    """
+
+    def __init__(self, capacity: int = 8):
+        import torch
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(capacity)]
+        for e in self.events:      # torch creates the HIP event lazily, at the first record
+            e.record()
+        self._handles = (ctypes.c_void_p * capacity)(*[e.cuda_event for e in self.events])
+        self._n = ctypes.c_int32(0)
+
+    def arm(self) -> None:
+        _check(lib().moe_set_launch_events(self._handles, len(self.events), ctypes.byref(self._n)))
+
+    @property
+    def n_recorded(self) -> int:
+        return self._n.value
+
+    def kernel_us(self) -> list[float]:
+        n = self._n.value
+        return [self.events[j].elapsed_time(self.events[j + 1]) * 1e3 for j in range(0, n - 1, 2)]
+
+
+def clear_launch_events() -> None:
+    _check(lib().moe_set_launch_events(None, 0, None))

@@ -17,6 +17,27 @@ namespace {
 
 thread_local std::string g_error;
 
+// Caller-supplied timing events for the next forward call on this thread.
+struct LaunchMarks {
+  hipEvent_t ev[64];
+  int32_t cap = 0;
+  int32_t used = 0;
+  int32_t* n_out = nullptr;
+};
+thread_local LaunchMarks g_marks;
+
+// Scope of one API call that may consume the timing events: the destructor
+// publishes the count and clears the setting when the call ends, whichever
+// way it ends.
+struct MarkScope {
+  ~MarkScope() {
+    if (g_marks.cap > 0 && g_marks.n_out) *g_marks.n_out = g_marks.used;
+    g_marks.cap = 0;
+    g_marks.used = 0;
+    g_marks.n_out = nullptr;
+  }
+};
+
 int fail(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -109,6 +130,16 @@ int finish(int rc) {
 
 }  // namespace
 
+namespace moe {
+bool next_launch_events(hipEvent_t* start, hipEvent_t* stop) {
+  if (g_marks.used + 2 > g_marks.cap) return false;
+  *start = g_marks.ev[g_marks.used];
+  *stop = g_marks.ev[g_marks.used + 1];
+  g_marks.used += 2;
+  return true;
+}
+}  // namespace moe
+
 extern "C" {
 
 int64_t moe_blob_bytes(const moe_desc* d, int32_t shared) {
@@ -129,6 +160,7 @@ int moe_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
 
 int moe_router_topk(const moe_desc* d, int32_t T, const void* x, const void* router_w, int32_t* topk_ids,
                     float* topk_w, void* workspace, size_t ws_bytes, void* stream) {
+  MarkScope marks;
   int rc;
   if ((rc = check_desc(d)) || (rc = check_T(T))) return rc;
   if (!x || !router_w || !topk_ids || !topk_w) return fail(MOE_EINVAL, "NULL x, router_w, topk_ids or topk_w");
@@ -150,6 +182,7 @@ int moe_router_topk(const moe_desc* d, int32_t T, const void* x, const void* rou
 int moe_experts_forward(const moe_desc* d, int32_t T, const void* x, const int32_t* topk_ids, const float* topk_w,
                         const int64_t* slot_table, const void* pool_base, const void* shared_w, void* out,
                         void* workspace, size_t ws_bytes, void* stream) {
+  MarkScope marks;
   int rc;
   if ((rc = check_desc(d)) || (rc = check_T(T))) return rc;
   if (!x || !topk_ids || !topk_w || !slot_table || !pool_base || !shared_w || !out)
@@ -180,6 +213,7 @@ static int layer_forward(const moe_desc* d, int32_t T, const void* x, const void
                          const int64_t* slot_table, const void* pool_base, const void* shared_w, void* out,
                          void* workspace, size_t ws_bytes, int32_t* topk_ids, float* topk_w, void* stream,
                          bool allow_fused) {
+  MarkScope marks;
   int rc;
   if ((rc = check_desc(d)) || (rc = check_T(T))) return rc;
   if (!x || !router_w || !slot_table || !pool_base || !shared_w || !out)
@@ -243,6 +277,20 @@ int moe_status_check(void* workspace, void* stream) {
       return fail(MOE_ETIMEOUT, "a bounded in-kernel wait of the fused decode kernel expired; its output is invalid");
     return fail(MOE_ERANGE, "a kernel skipped a pair: slot offset outside the pool or expert id outside [0, E)");
   }
+  return ok();
+}
+
+int moe_set_launch_events(void* const* events, int32_t capacity, int32_t* n_recorded) {
+  g_marks.cap = 0;
+  g_marks.used = 0;
+  g_marks.n_out = nullptr;
+  if (!events) return ok();
+  if (capacity < 1 || !n_recorded) return fail(MOE_EINVAL, "capacity must be >= 1 and n_recorded non-NULL");
+  const int32_t n = capacity < 64 ? capacity : 64;
+  for (int32_t i = 0; i < n; ++i) g_marks.ev[i] = static_cast<hipEvent_t>(events[i]);
+  *n_recorded = 0;
+  g_marks.cap = n;
+  g_marks.n_out = n_recorded;
   return ok();
 }
 

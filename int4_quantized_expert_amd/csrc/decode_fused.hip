@@ -582,10 +582,10 @@ size_t lds_bytes_b(int T, int k, int umax, int rb) {
 
 template <int BITS, int SB, int ACT, int OUT>
 static int launch_variant(const FusedArgs& a, const FusedPlan& p, hipStream_t stream) {
-  hipLaunchKernelGGL((k_decode_a<BITS, SB, ACT>), dim3(p.nb), dim3(kThreads), p.lds, stream, a);
+  launch_kernel(k_decode_a<BITS, SB, ACT>, dim3(p.nb), dim3(kThreads), p.lds, stream, a);
   FusedArgs b = a;
   b.rb = p.rb_b;
-  hipLaunchKernelGGL((k_decode_b<BITS, SB, OUT>), dim3(p.nb_b), dim3(kThreads), p.lds_b, stream, b);
+  launch_kernel(k_decode_b<BITS, SB, OUT>, dim3(p.nb_b), dim3(kThreads), p.lds_b, stream, b);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 

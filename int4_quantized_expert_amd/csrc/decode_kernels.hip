@@ -530,11 +530,11 @@ int launch_router_topk(const Call& c, int32_t* ids2, float* wts2) {
   const int waves = (d.n_experts + rpp - 1) / rpp;
   const dim3 grid((waves + 3) / 4), block(256);
 #define ROUTER(ACT, NSL) \
-  hipLaunchKernelGGL((k_router_logits<ACT, NSL>), grid, block, 0, c.stream, c.x, c.router_w, logits, c.T, d.hidden, d.n_experts)
+  launch_kernel(k_router_logits<ACT, NSL>, grid, block, 0, c.stream, c.x, c.router_w, logits, c.T, d.hidden, d.n_experts)
   (void)nsl;
   if (d.act_dtype == kF32) ROUTER(kF32, 1); else ROUTER(kBF16, 1);
 #undef ROUTER
-  hipLaunchKernelGGL(k_topk, dim3((c.T + 3) / 4), dim3(256), 0, c.stream, logits, c.T, d.n_experts, d.top_k, ids, wts,
+  launch_kernel(k_topk, dim3((c.T + 3) / 4), dim3(256), 0, c.stream, logits, c.T, d.n_experts, d.top_k, ids, wts,
                      ids2, wts2);
   return last_launch_error();
 }
@@ -553,7 +553,7 @@ int launch_experts(const Call& c) {
 
   // dispatch + gate
 #define DISPATCH(ACT, NSL)                                                                                      \
-  hipLaunchKernelGGL((k_dispatch<ACT, NSL>), dim3(1), dim3(kDispatchThreads), 0, c.stream, c.ids, c.T, d.top_k, \
+  launch_kernel(k_dispatch<ACT, NSL>, dim3(1), dim3(kDispatchThreads), 0, c.stream, c.ids, c.T, d.top_k, \
                      d.n_experts, d.hidden, c.x, gvec, gate, ucount, uniq, ustart, plist, flags)
   if (d.act_dtype == kF32) DISPATCH(kF32, 1); else DISPATCH(kBF16, 1);
 #undef DISPATCH
@@ -586,7 +586,7 @@ int launch_experts(const Call& c) {
     a.bpe_s = (d.shared_inter + rpb - 1) / rpb;
     a.hstride = c.L.hstride;
     const dim3 grid(a.umax * a.bpe_r + a.bpe_s), block(256);
-#define GATEUP(BITS, SB, ACT, NSL, TOKC) hipLaunchKernelGGL((k_gateup<BITS, SB, ACT, NSL, TOKC>), grid, block, 0, c.stream, a)
+#define GATEUP(BITS, SB, ACT, NSL, TOKC) launch_kernel(k_gateup<BITS, SB, ACT, NSL, TOKC>, grid, block, 0, c.stream, a)
 #define GATEUP_T(BITS, SB, ACT, NSL) \
   do { if (c.T == 1) GATEUP(BITS, SB, ACT, NSL, 1); else GATEUP(BITS, SB, ACT, NSL, 2); } while (0)
 #define GATEUP_N(BITS, SB, ACT) GATEUP_T(BITS, SB, ACT, 1)
@@ -630,7 +630,7 @@ int launch_experts(const Call& c) {
     a.hstride = c.L.hstride;
     const int bpe_s = (d.hidden + rpb_s - 1) / rpb_s;
     const dim3 grid(a.umax * a.bpe + bpe_s), block(256);
-#define DOWN(BITS, SB) hipLaunchKernelGGL((k_down<BITS, SB, 1>), grid, block, 0, c.stream, a)
+#define DOWN(BITS, SB) launch_kernel(k_down<BITS, SB, 1>, grid, block, 0, c.stream, a)
 #define DOWN_S(BITS) do { if (d.sb_dtype == kF32) DOWN(BITS, kF32); else DOWN(BITS, kBF16); } while (0)
     if (d.bits == 4) DOWN_S(4); else DOWN_S(8);
 #undef DOWN_S
@@ -641,10 +641,10 @@ int launch_experts(const Call& c) {
     const size_t n = static_cast<size_t>(c.T) * d.hidden;
     const dim3 grid(static_cast<unsigned>((n + 255) / 256)), block(256);
     if (d.out_dtype == kF32)
-      hipLaunchKernelGGL(k_combine<kF32>, grid, block, 0, c.stream, partial, c.ids, c.wts, gate, c.out, c.T, d.top_k,
+      launch_kernel(k_combine<kF32>, grid, block, 0, c.stream, partial, c.ids, c.wts, gate, c.out, c.T, d.top_k,
                          d.hidden, d.n_experts);
     else
-      hipLaunchKernelGGL(k_combine<kBF16>, grid, block, 0, c.stream, partial, c.ids, c.wts, gate, c.out, c.T,
+      launch_kernel(k_combine<kBF16>, grid, block, 0, c.stream, partial, c.ids, c.wts, gate, c.out, c.T,
                          d.top_k, d.hidden, d.n_experts);
   }
   return last_launch_error();

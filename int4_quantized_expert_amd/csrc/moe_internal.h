@@ -1,6 +1,7 @@
 // Internal declarations shared by the host API and the kernel launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -83,6 +84,23 @@ struct Call {
   float* wts_out;
   hipStream_t stream;
 };
+
+// Takes the next pair of caller-supplied timing events (moe_set_launch_events)
+// for the kernel about to launch; false when none is armed.
+bool next_launch_events(hipEvent_t* start, hipEvent_t* stop);
+
+// Every kernel of a forward call launches through here.  With timing events
+// armed, the launch carries them (hipExtLaunchKernel), so the runtime stamps
+// them with that dispatch's own start and end.
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
+                          Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (next_launch_events(&e0, &e1))
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, e0, e1, 0u, static_cast<KArgs>(args)...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, static_cast<KArgs>(args)...);
+}
 
 int launch_router_topk(const Call& c, int32_t* ids_dst, float* wts_dst);
 int launch_experts(const Call& c);

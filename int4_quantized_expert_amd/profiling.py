@@ -1,0 +1,137 @@
+"""HBM traffic of the library's kernels from rocprofv3 counter passes.
+
+Two `rocprofv3 --pmc` passes over the same benchmark command, one reading
+FETCH_SIZE and one reading WRITE_SIZE (KiB per dispatch), are turned into
+bytes per launch.  Each counter is scaled by what it reads for a plain device
+copy of known size run in the same process (bench.py --copy-probe): on gfx950
+FETCH_SIZE reads about half of the bytes a copy moves, WRITE_SIZE all of them.
+
+The summary is a small markdown file with one JSON block.  It carries a digest
+of the kernel sources, so a reader can tell whether the counters still describe
+the code as it stands (bench.py reports `traffic` only when they do).
+
+    python -m int4_quantized_expert_amd.profiling --fetch F.csv --write W.csv \\
+        --copy-bytes 268435456 --workload 80b_stack_decode --tokens 1 --out profiles/X.md \\
+        --command "the rocprofv3 command line"
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources, the public header and the build flags."""
+    h = hashlib.sha256()
+    files = [os.path.join(PKG, "build.py"), os.path.join(ROOT, "include", "moe_layer.h")]
+    csrc = os.path.join(PKG, "csrc")
+    files += [os.path.join(csrc, f) for f in sorted(os.listdir(csrc)) if f.endswith((".hip", ".h"))]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def short_name(kernel: str) -> str:
+    """`void moe::(anonymous namespace)::k_decode_a<4, 1, 1>(moe::FusedArgs)` -> `k_decode_a<4, 1, 1>`."""
+    name = kernel.split("(moe::")[0].split("(anonymous namespace)::")[-1]
+    name = re.sub(r"^void ", "", name).strip()
+    return name.split("(")[0] if "<" not in name else name
+
+
+def read_counter(path: str) -> dict[str, list[float]]:
+    per = defaultdict(list)
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return per
+
+
+def traffic_table(fetch_csv: str, write_csv: str, copy_bytes: int) -> dict:
+    f, w = read_counter(fetch_csv), read_counter(write_csv)
+    if COPY_KERNEL not in f or COPY_KERNEL not in w:
+        raise ValueError(f"no {COPY_KERNEL} dispatch in the counter files (run with --copy-probe)")
+    kib = copy_bytes / 1024.0
+    f_scale, w_scale = max(f[COPY_KERNEL]) / kib, max(w[COPY_KERNEL]) / kib
+    rows = {}
+    for name in f:
+        if not (name.startswith("void moe::") or name.startswith("moe::")) or name not in w:
+            continue
+        fk = sum(f[name]) / len(f[name])
+        wk = sum(w[name]) / len(w[name])
+        rows[short_name(name)] = {
+            "dispatches": len(f[name]),
+            "fetch_kib": round(fk, 2),
+            "write_kib": round(wk, 2),
+            "read_bytes": round(fk * 1024 / f_scale),
+            "write_bytes": round(wk * 1024 / w_scale),
+            "traffic_bytes": round(fk * 1024 / f_scale + wk * 1024 / w_scale),
+        }
+    return {"fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5), "kernels": rows}
+
+
+def write_summary(out: str, table: dict, workload: str, tokens: int, command: str) -> None:
+    blob = {"workload": workload, "tokens": tokens, "source_digest": source_digest(), **table}
+    lines = [f"# HBM traffic per launch: {workload}, T={tokens}\n\n",
+             "Commands (from the repository root; rocprofv3 run from /tmp with TMPDIR=/tmp):\n\n",
+             "```\n" + command.strip() + "\n```\n\n",
+             f"Scaling by a {COPY_KERNEL} of known size in the same process: FETCH_SIZE reads "
+             f"{table['fetch_scale']} x the bytes copied, WRITE_SIZE {table['write_scale']} x.\n\n",
+             "| Kernel | Dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | Read bytes | Written bytes |\n",
+             "|---|---|---|---|---|---|\n"]
+    for k, r in table["kernels"].items():
+        lines.append(f"| {k} | {r['dispatches']} | {r['fetch_kib']} | {r['write_kib']} | {r['read_bytes']} | "
+                     f"{r['write_bytes']} |\n")
+    lines.append("\n```json\n" + json.dumps(blob, indent=1) + "\n```\n")
+    with open(out, "w") as fh:
+        fh.writelines(lines)
+
+
+def load_traffic(profiles_dir: str, workload: str, tokens: int) -> dict | None:
+    """The counter table for this workload if one matches the current sources, else None."""
+    if not os.path.isdir(profiles_dir):
+        return None
+    digest = source_digest()
+    for f in sorted(os.listdir(profiles_dir)):
+        if not f.endswith(".md"):
+            continue
+        with open(os.path.join(profiles_dir, f)) as fh:
+            text = fh.read()
+        m = re.search(r"```json\n(.*?)\n```", text, re.S)
+        if not m:
+            continue
+        try:
+            blob = json.loads(m.group(1))
+        except json.JSONDecodeError:
+            continue
+        if blob.get("workload") == workload and blob.get("tokens") == tokens and blob.get("source_digest") == digest:
+            return blob
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--copy-bytes", type=int, default=256 << 20)
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--tokens", type=int, required=True)
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--command", required=True)
+    a = ap.parse_args()
+    write_summary(a.out, traffic_table(a.fetch, a.write, a.copy_bytes), a.workload, a.tokens, a.command)
+
+
+if __name__ == "__main__":
+    main()

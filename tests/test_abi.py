@@ -99,3 +99,24 @@ def test_zero_tokens_enqueue_nothing():
 def test_synth_device_fill_library_loads():
     from synth import gpu
     assert hasattr(gpu.lib(), "synth_fill_blobs")
+
+
+def test_launch_event_hook_argument_checks():
+    """moe_set_launch_events validates on the host and NULL events clear it."""
+    L = M.lib()
+    n = ctypes.c_int32(-5)
+    ev = (ctypes.c_void_p * 2)(None, None)
+    assert L.moe_set_launch_events(None, 0, None) == 0
+    assert L.moe_set_launch_events(ev, 0, ctypes.byref(n)) == -1
+    assert L.moe_set_launch_events(ev, 2, None) == -1
+    # A call rejected before any launch records nothing and clears the setting.
+    assert L.moe_set_launch_events(ev, 2, ctypes.byref(n)) == 0
+    assert n.value == 0
+    d = good_desc()
+    assert L.moe_layer_forward(ctypes.byref(d), -1, None, None, None, None, None, None, None, 0, None, None,
+                               None) == -1
+    assert n.value == 0
+    n.value = 7
+    assert L.moe_layer_forward(ctypes.byref(d), -1, None, None, None, None, None, None, None, 0, None, None,
+                               None) == -1
+    assert n.value == 7, "a consumed setting must not be written again"

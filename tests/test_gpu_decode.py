@@ -209,3 +209,23 @@ def test_device_fill_matches_host_generator():
         torch.cuda.synchronize()
         ref = synth.fill_blob(geo, geo.shared_inter, synth.blob_key(5, 9, synth.SHARED_BLOB_ID))
         assert np.array_equal(sh.cpu().numpy(), ref)
+
+
+def test_launch_event_hook_times_each_kernel():
+    """moe_set_launch_events: a start and an end event per kernel, consumed by exactly one
+    call; timing does not change the result."""
+    data = make_layer(synth.PRESETS["80b"], 4, 9, 1, routing="zipf", n_cand=32)
+    dl = upload(data, "f32")
+    ref = run(dl, 1)
+    for staged, kernels in ((False, 2), (True, 6)):
+        timer = M.LaunchTimer(16)
+        timer.arm()
+        got = run(dl, 1, staged=staged)
+        assert timer.n_recorded == 2 * kernels
+        us = timer.kernel_us()
+        assert len(us) == kernels and all(u > 0 for u in us), us
+        for p, q in zip(ref, got):
+            assert torch.equal(p, q)
+        n_before = timer.n_recorded
+        run(dl, 1, staged=staged)          # not armed: records nothing more
+        assert timer.n_recorded == n_before

@@ -1,0 +1,37 @@
+"""Host logic of the counter-to-traffic conversion (no GPU)."""
+
+import csv
+
+from int4_quantized_expert_amd import profiling as P
+
+FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _csv(path, rows):
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (k, c, v) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+
+
+def test_traffic_scaled_by_copy_and_keyed_by_digest(tmp_path):
+    copy = 1 << 20
+    ka = "void moe::(anonymous namespace)::k_decode_a<4, 1, 1>(moe::FusedArgs)"
+    f, w = tmp_path / "f.csv", tmp_path / "w.csv"
+    # FETCH_SIZE reads half of the copied bytes, WRITE_SIZE all of them.
+    _csv(f, [(P.COPY_KERNEL, "FETCH_SIZE", 512.0), (ka, "FETCH_SIZE", 100.0), (ka, "FETCH_SIZE", 300.0)])
+    _csv(w, [(P.COPY_KERNEL, "WRITE_SIZE", 1024.0), (ka, "WRITE_SIZE", 8.0), (ka, "WRITE_SIZE", 8.0)])
+    t = P.traffic_table(str(f), str(w), copy)
+    assert t["fetch_scale"] == 0.5 and t["write_scale"] == 1.0
+    r = t["kernels"]["k_decode_a<4, 1, 1>"]
+    assert r["dispatches"] == 2
+    assert r["read_bytes"] == 200 * 1024 * 2 and r["write_bytes"] == 8 * 1024
+    out = tmp_path / "prof"
+    out.mkdir()
+    P.write_summary(str(out / "x.md"), t, "wl", 1, "cmd")
+    assert P.load_traffic(str(out), "wl", 1)["kernels"]["k_decode_a<4, 1, 1>"]["traffic_bytes"] == r["traffic_bytes"]
+    assert P.load_traffic(str(out), "wl", 8) is None
+    text = (out / "x.md").read_text().replace(P.source_digest(), "0" * 64)
+    (out / "x.md").write_text(text)
+    assert P.load_traffic(str(out), "wl", 1) is None, "a summary of other sources must not be used"
