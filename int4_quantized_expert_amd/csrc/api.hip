@@ -176,6 +176,7 @@ int moe_router_topk(const moe_desc* d, int32_t T, const void* x, const void* rou
   c.ws = static_cast<uint8_t*>(workspace);
   c.L = L;
   c.stream = static_cast<hipStream_t>(stream);
+  if (moe::prefill_supported(*d, T)) return finish(moe::launch_prefill_router(c, topk_ids, topk_w));
   return finish(moe::launch_router_topk(c, topk_ids, topk_w));
 }
 
@@ -206,6 +207,7 @@ int moe_experts_forward(const moe_desc* d, int32_t T, const void* x, const int32
   c.ids = topk_ids;
   c.wts = topk_w;
   c.stream = static_cast<hipStream_t>(stream);
+  if (moe::prefill_supported(*d, T)) return finish(moe::launch_prefill_experts(c));
   return finish(moe::launch_experts(c));
 }
 
@@ -243,6 +245,10 @@ static int layer_forward(const moe_desc* d, int32_t T, const void* x, const void
   if (allow_fused && moe::fused_supported(*d, T)) {
     moe::FusedPlan plan;
     if (cached_plan(*d, T, &plan) == MOE_OK) return finish(moe::launch_decode_fused(c, plan));
+  }
+  if (allow_fused && moe::prefill_supported(*d, T)) {
+    if ((rc = moe::launch_prefill_router(c, topk_ids, topk_w))) return finish(rc);
+    return finish(moe::launch_prefill_experts(c));
   }
   if ((rc = moe::launch_router_topk(c, topk_ids, topk_w))) return finish(rc);
   return finish(moe::launch_experts(c));

@@ -534,8 +534,12 @@ int launch_router_topk(const Call& c, int32_t* ids2, float* wts2) {
   (void)nsl;
   if (d.act_dtype == kF32) ROUTER(kF32, 1); else ROUTER(kBF16, 1);
 #undef ROUTER
-  launch_kernel(k_topk, dim3((c.T + 3) / 4), dim3(256), 0, c.stream, logits, c.T, d.n_experts, d.top_k, ids, wts,
-                     ids2, wts2);
+  return launch_topk(c, logits, ids, wts, ids2, wts2);
+}
+
+int launch_topk(const Call& c, const float* logits, int32_t* ids, float* wts, int32_t* ids2, float* wts2) {
+  launch_kernel(k_topk, dim3((c.T + 3) / 4), dim3(256), 0, c.stream, logits, c.T, c.d.n_experts, c.d.top_k, ids,
+                wts, ids2, wts2);
   return last_launch_error();
 }
 
@@ -636,17 +640,19 @@ int launch_experts(const Call& c) {
 #undef DOWN_S
 #undef DOWN
   }
-  // combine
-  {
-    const size_t n = static_cast<size_t>(c.T) * d.hidden;
-    const dim3 grid(static_cast<unsigned>((n + 255) / 256)), block(256);
-    if (d.out_dtype == kF32)
-      launch_kernel(k_combine<kF32>, grid, block, 0, c.stream, partial, c.ids, c.wts, gate, c.out, c.T, d.top_k,
-                         d.hidden, d.n_experts);
-    else
-      launch_kernel(k_combine<kBF16>, grid, block, 0, c.stream, partial, c.ids, c.wts, gate, c.out, c.T,
-                         d.top_k, d.hidden, d.n_experts);
-  }
+  return launch_combine(c, partial, gate);
+}
+
+int launch_combine(const Call& c, const float* partial, const float* gate) {
+  const moe_desc& d = c.d;
+  const size_t n = static_cast<size_t>(c.T) * d.hidden;
+  const dim3 grid(static_cast<unsigned>((n + 255) / 256)), block(256);
+  if (d.out_dtype == kF32)
+    launch_kernel(k_combine<kF32>, grid, block, 0, c.stream, partial, c.ids, c.wts, gate, c.out, c.T, d.top_k,
+                  d.hidden, d.n_experts);
+  else
+    launch_kernel(k_combine<kBF16>, grid, block, 0, c.stream, partial, c.ids, c.wts, gate, c.out, c.T, d.top_k,
+                  d.hidden, d.n_experts);
   return last_launch_error();
 }
 

@@ -31,10 +31,18 @@ struct WsLayout {
   size_t f_uoff;     // two-launch path: [min(T k, E)] int64 blob offsets of the distinct experts
   size_t f_pidx;     // two-launch path: [min(T k, E), T] int32 rank of expert u for token t
   size_t f_arrive;   // two-launch path: [kFusedReplicas + 1][kFusedMaxBlocks] uint32 flags, then arrival tags
+  size_t p_x16;      // prefill: [T, H] float16 activations in MFMA k order
+  size_t p_meta;     // prefill: int32 [0] number of expert tiles
+  size_t p_tstart;   // prefill: [min(T k, E) + 2] int32 first tile of each distinct expert, then of the shared one
+  size_t p_tile;     // prefill: [max tiles] int32 distinct-expert rank of each tile (the shared expert is rank U)
   size_t total;
   int32_t umax;      // min(T k, E)
   int32_t hstride;   // max(I, SI)
+  int32_t max_tiles; // bound on prefill tiles of up to kPrefillChunk tokens
 };
+
+constexpr int kPrefillChunk = 64;   // tokens per prefill tile
+constexpr int kPrefillMinT = 16;    // fewest tokens that take the prefill path
 
 inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
@@ -60,6 +68,12 @@ inline WsLayout ws_layout(const moe_desc& d, int32_t T) {
   L.f_lg = take(static_cast<size_t>(kFusedReplicas) * T * d.n_experts * 8);
   L.f_uoff = take(static_cast<size_t>(umax) * 8);
   L.f_pidx = take(static_cast<size_t>(umax) * T * 4);
+  const size_t chunks = (Tk + kPrefillChunk - 1) / kPrefillChunk + (static_cast<size_t>(T) + kPrefillChunk - 1) / kPrefillChunk;
+  L.max_tiles = static_cast<int32_t>(umax + chunks);
+  L.p_x16 = take(static_cast<size_t>(T) * d.hidden * 2);
+  L.p_meta = take(16);
+  L.p_tstart = take((static_cast<size_t>(umax) + 2) * 4);
+  L.p_tile = take(static_cast<size_t>(L.max_tiles) * 4);
   L.total = o;
   L.umax = umax;
   L.hstride = hs;
@@ -104,7 +118,16 @@ inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint3
 
 int launch_router_topk(const Call& c, int32_t* ids_dst, float* wts_dst);
 int launch_experts(const Call& c);
+// Pieces of the staged path the prefill path shares: per-token top-k of given
+// logits, and the ordered combine of per-pair partial rows.
+int launch_topk(const Call& c, const float* logits, int32_t* ids, float* wts, int32_t* ids2, float* wts2);
+int launch_combine(const Call& c, const float* partial, const float* gate);
 int launch_ws_init(uint8_t* ws, size_t bytes, hipStream_t stream);
+
+// Prefill path (many tokens): MFMA router and grouped expert GEMMs.
+bool prefill_supported(const moe_desc& d, int T);
+int launch_prefill_router(const Call& c, int32_t* ids_dst, float* wts_dst);
+int launch_prefill_experts(const Call& c);
 
 // Two-launch decode (T <= kFusedMaxT).
 bool fused_supported(const moe_desc& d, int T);

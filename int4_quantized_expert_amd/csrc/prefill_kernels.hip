@@ -1,0 +1,704 @@
+// Prefill path: one MoE layer over many tokens at once (gfx950).
+//
+// The pages' method is the same as in decode -- softmax router, top-k, expert
+// SwiGLU with MLX-affine group-quantized weights, a weighted combine plus a
+// sigmoid-gated shared expert (Swiftlet README translation, "How it works";
+// Qwen3-Next model card, "Model Overview") -- but with ~40 tokens per expert
+// the expert products become small dense GEMMs, so they run on MFMA:
+//
+//   k_pf_router    logits = x R^T on v_mfma_f32_16x16x32_bf16 (exact bf16
+//                  products, fp32 accumulation)
+//   k_pf_gate      sigmoid(g . x) per token, fp32
+//   (k_topk)       the staged path's per-token top-k and renormalisation
+//   k_pf_dispatch  stable counting sort of the (token, rank) pairs by expert
+//                  and a table of tiles of up to 64 pairs of one expert
+//   k_pf_xprep     x to float16, stored in the k order the MFMA operands use
+//   k_pf_gateup    per tile: h = silu(Wg x) * (Wu x), h in float16
+//   k_pf_down      per tile: partial = Wd h, fp32 per (pair, output row)
+//   (k_combine)    the staged path's ordered combine with the shared expert
+//
+// Expert weights are dequantized straight into MFMA A operands: each int4/int8
+// code becomes 1024 + q in float16 by OR-ing it into the mantissa of 1024
+// (exact), 1024 is subtracted (exact) and w = s * q + b is formed by one
+// float16 FMA, i.e. rounded once.  Activations (bf16 inputs, exact in float16
+// within its range) and h are float16; every product accumulates in fp32.
+//
+// MFMA 16x16x32 operand layout (gfx950): lane l supplies row/column l % 16 and
+// eight k values 8 (l / 16) .. +7 of A and B; D row 4 (l / 16) + i, column
+// l % 16 lands in lane l, element i.  The sum over k does not care which k a
+// slot stands for, as long as A and B agree, so within each 128-wide step of k
+// lane quarter q takes k = 32 q .. 32 q + 31 (contiguous bytes per lane) and
+// within each 8 codes the slot order is the one the dequantization produces.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "moe_internal.h"
+#include "topk_wave.h"
+
+namespace moe {
+namespace {
+
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef __bf16 b8v __attribute__((ext_vector_type(8)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kChunk = kPrefillChunk;   // pairs per tile (4 MFMA column blocks)
+constexpr int kGuRows = 128;            // gate/up rows (each) per block: 4 waves x 32
+constexpr int kDnRows = 256;            // down rows per block: 4 waves x 64
+constexpr int kSlice = 256;             // k staged in LDS per step
+constexpr int kRowBytes = kSlice * 2 + 16;   // one token's float16 slice + bank padding
+constexpr int kDispThreads = 1024;
+
+__device__ __forceinline__ uint32_t h2_bits(h2v v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ h2v bits_h2(uint32_t v) { return __builtin_bit_cast(h2v, v); }
+
+// Slot order of 8 consecutive k inside one MFMA operand, as produced by the
+// dequantization: int4 words give pairs (k0,k4) (k1,k5) (k2,k6) (k3,k7); int8
+// words give (k0,k2) (k1,k3) (k4,k6) (k5,k7).  permute8 puts float16
+// activations in the same order.
+
+// Position of the 16-byte chunk holding natural 8-group g8 (k = 8 g8 ..) in
+// the MFMA k order: inside each 128-wide step (16 groups), group 4 q + j goes
+// to 4 j + q, so lane quarter q reads chunk 4 j + q for MFMA step j.
+__device__ __forceinline__ int chunk_of(int g8) { return (g8 & ~15) | ((g8 & 3) << 2) | ((g8 >> 2) & 3); }
+
+// Eight float16 values in natural k order -> slot order.
+template <int BITS>
+__device__ __forceinline__ u32x4 permute8(u32x4 v) {
+  const uint32_t a = v[0], b = v[1], c = v[2], d = v[3];   // (k0,k1) (k2,k3) (k4,k5) (k6,k7)
+  u32x4 o;
+  if constexpr (BITS == 4) {
+    o[0] = (a & 0xffffu) | (c << 16);            // (k0, k4)
+    o[1] = (a >> 16) | (c & 0xffff0000u);        // (k1, k5)
+    o[2] = (b & 0xffffu) | (d << 16);            // (k2, k6)
+    o[3] = (b >> 16) | (d & 0xffff0000u);        // (k3, k7)
+  } else {
+    o[0] = (a & 0xffffu) | (b << 16);            // (k0, k2)
+    o[1] = (a >> 16) | (b & 0xffff0000u);        // (k1, k3)
+    o[2] = (c & 0xffffu) | (d << 16);            // (k4, k6)
+    o[3] = (c >> 16) | (d & 0xffff0000u);        // (k5, k7)
+  }
+  return o;
+}
+
+// Dequantize 8 int4 codes (one word, low nibble first) into an A operand.
+__device__ __forceinline__ h8v dq_int4(uint32_t w, h2v s, h2v b) {
+  const uint32_t hi = w >> 8;
+  const h2v m1024 = {-1024.0f16, -1024.0f16}, r16 = {0.0625f16, 0.0625f16}, m64 = {-64.0f16, -64.0f16};
+  const h2v q0 = bits_h2((w & 0x000F000Fu) | 0x64006400u) + m1024;                          // (q0, q4)
+  const h2v q1 = __builtin_elementwise_fma(bits_h2((w & 0x00F000F0u) | 0x64006400u), r16, m64);   // (q1, q5)
+  const h2v q2 = bits_h2((hi & 0x000F000Fu) | 0x64006400u) + m1024;                         // (q2, q6)
+  const h2v q3 = __builtin_elementwise_fma(bits_h2((hi & 0x00F000F0u) | 0x64006400u), r16, m64);  // (q3, q7)
+  u32x4 o;
+  o[0] = h2_bits(__builtin_elementwise_fma(q0, s, b));
+  o[1] = h2_bits(__builtin_elementwise_fma(q1, s, b));
+  o[2] = h2_bits(__builtin_elementwise_fma(q2, s, b));
+  o[3] = h2_bits(__builtin_elementwise_fma(q3, s, b));
+  return __builtin_bit_cast(h8v, o);
+}
+
+// Dequantize 8 int8 codes (two words, low byte first) into an A operand.
+__device__ __forceinline__ h8v dq_int8(uint32_t w0, uint32_t w1, h2v s, h2v b) {
+  const h2v m1024 = {-1024.0f16, -1024.0f16};
+  const h2v q0 = bits_h2((w0 & 0x00FF00FFu) | 0x64006400u) + m1024;          // (q0, q2)
+  const h2v q1 = bits_h2(((w0 >> 8) & 0x00FF00FFu) | 0x64006400u) + m1024;   // (q1, q3)
+  const h2v q2 = bits_h2((w1 & 0x00FF00FFu) | 0x64006400u) + m1024;          // (q4, q6)
+  const h2v q3 = bits_h2(((w1 >> 8) & 0x00FF00FFu) | 0x64006400u) + m1024;   // (q5, q7)
+  u32x4 o;
+  o[0] = h2_bits(__builtin_elementwise_fma(q0, s, b));
+  o[1] = h2_bits(__builtin_elementwise_fma(q1, s, b));
+  o[2] = h2_bits(__builtin_elementwise_fma(q2, s, b));
+  o[3] = h2_bits(__builtin_elementwise_fma(q3, s, b));
+  return __builtin_bit_cast(h8v, o);
+}
+
+template <int SB>
+__device__ __forceinline__ h2v load_h2(const uint8_t* base, size_t idx) {
+  const _Float16 v = static_cast<_Float16>(load_scalar<SB>(base, idx));
+  return h2v{v, v};
+}
+
+__device__ __forceinline__ f4v mfma16(h8v a, h8v b, f4v c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+
+// ---------------------------------------------------------------------------
+// Router logits [T, E] = x [T, H] . R [E, H]^T, bf16 operands, fp32 sums.
+// Block: 64 experts x 64 tokens; wave w owns experts 16 w .. +15.
+__global__ __launch_bounds__(kThreads) void k_pf_router(const uint16_t* __restrict__ x, const uint16_t* __restrict__ R,
+                                                       float* __restrict__ logits, int T, int H, int E) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int r = lane & 15, q = lane >> 4;
+  const int e = blockIdx.x * 64 + w * 16 + r;
+  const bool e_ok = e < E;
+  const uint16_t* ra = R + static_cast<size_t>(e_ok ? e : 0) * H;
+  const int t0 = blockIdx.y * 64;
+  const uint16_t* xa[4];
+  bool t_ok[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const int t = t0 + 16 * ct + r;
+    t_ok[ct] = t < T;
+    xa[ct] = x + static_cast<size_t>(t_ok[ct] ? t : 0) * H;
+  }
+  f4v acc[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) acc[ct] = f4v{0.f, 0.f, 0.f, 0.f};
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int k0 = 0; k0 < H; k0 += 128) {
+    const int kk = k0 + 32 * q;
+    u32x4 a[4], b[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = e_ok ? load16(ra + kk + 8 * j) : zero;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[ct][j] = t_ok[ct] ? load16(xa[ct] + kk + 8 * j) : zero;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8v, a[j]), __builtin_bit_cast(b8v, b[ct][j]),
+                                                          acc[ct], 0, 0, 0);
+  }
+  const int e0 = blockIdx.x * 64 + w * 16 + 4 * q;
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const int t = t0 + 16 * ct + r;
+    if (t < T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (e0 + i < E) logits[static_cast<size_t>(t) * E + e0 + i] = acc[ct][i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared-expert gate sigmoid(g . x_t), one wave per token, fp32.
+__global__ __launch_bounds__(kThreads) void k_pf_gate(const void* __restrict__ x, const void* __restrict__ gvec,
+                                                     float* __restrict__ gate, int T, int H) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  if (t >= T) return;
+  const uint8_t* xr = static_cast<const uint8_t*>(x) + static_cast<size_t>(t) * H * 2;
+  float acc = 0.f;
+  for (int sg = lane; sg < H / kSegCodes; sg += kWave) {
+    float a[kSegCodes], g[kSegCodes];
+    load_act_seg<kBF16>(xr, sg, a);
+    load_act_seg<kBF16>(gvec, sg, g);
+#pragma unroll
+    for (int c = 0; c < kSegCodes; ++c) acc = fmaf(a[c], g[c], acc);
+  }
+  acc = group_sum(acc, kWave);
+  if (lane == 0) gate[t] = sigmoid(acc);
+}
+
+// ---------------------------------------------------------------------------
+// Stable counting sort of the T k (token, rank) pairs by expert.
+//
+// Waves w < nsl each own a contiguous slice of pairs.  Pass 1 counts per
+// (slice, expert); a scan turns the counts into each slice's first position
+// in each expert's list; pass 2 walks every slice in order, 64 pairs at a
+// time, and places each pair after the earlier pairs of its expert (found by
+// matching the expert id bit by bit across the wave), so lists keep token
+// order.  Also writes the distinct experts (ascending id), their list starts,
+// and the tile table: expert rank u gets ceil(n_u / 64) tiles, then the shared
+// expert ceil(T / 64) tiles of consecutive tokens.
+__global__ __launch_bounds__(kDispThreads) void k_pf_dispatch(const int32_t* __restrict__ ids, int T, int k, int E,
+                                                             int nsl, int32_t* __restrict__ ucount,
+                                                             int32_t* __restrict__ uniq, int32_t* __restrict__ ustart,
+                                                             int32_t* __restrict__ plist, int32_t* __restrict__ tstart,
+                                                             int32_t* __restrict__ tile_u, int32_t* __restrict__ meta,
+                                                             uint32_t* __restrict__ flags) {
+  extern __shared__ int32_t cnt[];   // [nsl][E]
+  __shared__ int ws_c[kDispThreads / kWave], ws_u[kDispThreads / kWave], ws_t[kDispThreads / kWave];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int np = T * k;
+  const int per = (np + nsl - 1) / nsl;
+  for (int i = tid; i < nsl * E; i += kDispThreads) cnt[i] = 0;
+  __syncthreads();
+  const int p_lo = w * per, p_hi = min(np, p_lo + per);
+  if (w < nsl) {
+    for (int p = p_lo + lane; p < p_hi; p += kWave) {
+      const int e = ids[p];
+      if (e >= 0 && e < E) atomicAdd(&cnt[w * E + e], 1);
+      else raise_error(flags, kErrRange);
+    }
+  }
+  __syncthreads();
+  int c = 0;
+  if (tid < E) {
+    for (int s = 0; s < nsl; ++s) {
+      const int v = cnt[s * E + tid];
+      cnt[s * E + tid] = c;
+      c += v;
+    }
+  }
+  const int u = c > 0 ? 1 : 0;
+  const int nt = (c + kChunk - 1) / kChunk;
+  int ic = c, iu = u, it = nt;
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    const int oc = __shfl_up(ic, m, kWave), ou = __shfl_up(iu, m, kWave), ot = __shfl_up(it, m, kWave);
+    if (lane >= m) { ic += oc; iu += ou; it += ot; }
+  }
+  if (lane == kWave - 1) { ws_c[w] = ic; ws_u[w] = iu; ws_t[w] = it; }
+  __syncthreads();
+  if (w == 0) {
+    const int nw = kDispThreads / kWave;
+    int vc = lane < nw ? ws_c[lane] : 0, vu = lane < nw ? ws_u[lane] : 0, vt = lane < nw ? ws_t[lane] : 0;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+      const int oc = __shfl_up(vc, m, kWave), ou = __shfl_up(vu, m, kWave), ot = __shfl_up(vt, m, kWave);
+      if (lane >= m) { vc += oc; vu += ou; vt += ot; }
+    }
+    if (lane < nw) { ws_c[lane] = vc; ws_u[lane] = vu; ws_t[lane] = vt; }
+  }
+  __syncthreads();
+  const int start = (w > 0 ? ws_c[w - 1] : 0) + ic - c;
+  const int rank = (w > 0 ? ws_u[w - 1] : 0) + iu - u;
+  const int tile0 = (w > 0 ? ws_t[w - 1] : 0) + it - nt;
+  if (tid < E) {
+    for (int s = 0; s < nsl; ++s) cnt[s * E + tid] += start;
+    if (u) {
+      uniq[rank] = tid;
+      ustart[rank] = start;
+      tstart[rank] = tile0;
+      for (int i = 0; i < nt; ++i) tile_u[tile0 + i] = rank;
+    }
+  }
+  if (tid == kDispThreads - 1) {
+    const int U = ws_u[kDispThreads / kWave - 1];
+    const int routed = ws_t[kDispThreads / kWave - 1];
+    const int shared_tiles = (T + kChunk - 1) / kChunk;
+    *ucount = U;
+    ustart[U] = ws_c[kDispThreads / kWave - 1];
+    tstart[U] = routed;
+    tstart[U + 1] = routed + shared_tiles;
+    for (int i = 0; i < shared_tiles; ++i) tile_u[routed + i] = U;
+    meta[0] = routed + shared_tiles;
+  }
+  __syncthreads();
+  if (w < nsl) {
+    for (int base = p_lo; base < p_hi; base += kWave) {
+      const int p = base + lane;
+      const int e = p < p_hi ? ids[p] : -1;
+      const bool ok = e >= 0 && e < E;
+      uint64_t m = __ballot(ok);
+      for (int b = 0; (1 << b) < E; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+      }
+      const int before = __popcll(m & lane_mask_lt(lane));
+      int pos = 0;
+      if (ok) pos = cnt[w * E + e] + before;
+      wave_sync_lds();
+      if (ok) {
+        plist[pos] = p;
+        if (before == __popcll(m) - 1) cnt[w * E + e] = pos + 1;   // last of its group moves the cursor
+      }
+      wave_sync_lds();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// x [T, H] bf16 -> float16 in MFMA k order, one thread per 8 values.
+template <int BITS>
+__global__ __launch_bounds__(kThreads) void k_pf_xprep(const uint16_t* __restrict__ x, u32x4* __restrict__ x16, int T,
+                                                      int H) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int g_row = H / 8;
+  if (i >= static_cast<size_t>(T) * g_row) return;
+  const size_t t = i / g_row;
+  const int g8 = static_cast<int>(i % g_row);
+  const u32x4 v = load16(x + t * H + 8 * g8);
+  u32x4 h;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const _Float16 lo = static_cast<_Float16>(__uint_as_float(v[m] << 16));
+    const _Float16 hi = static_cast<_Float16>(__uint_as_float(v[m] & 0xffff0000u));
+    h[m] = h2_bits(h2v{lo, hi});
+  }
+  x16[t * g_row + chunk_of(g8)] = permute8<BITS>(h);
+}
+
+// ---------------------------------------------------------------------------
+// Expert tiles.
+struct PfArgs {
+  const u32x4* x16;        // [T, H / 8] chunks in MFMA k order
+  const int64_t* slot_table;
+  const uint8_t* pool;
+  const uint8_t* shared;
+  const int32_t* ucount;
+  const int32_t* uniq;
+  const int32_t* ustart;
+  const int32_t* plist;
+  const int32_t* tstart;
+  const int32_t* tile_u;
+  const int32_t* meta;
+  _Float16* h;             // [T k + T, hs] natural k order
+  float* partial;          // [T k + T, H]
+  uint32_t* flags;
+  int64_t pool_bytes;
+  int T, k, H, E, I, SI, hs;
+  int n_rt;                // row blocks per tile in this launch
+};
+
+struct Tile {
+  const uint8_t* blob;
+  int rows_or_k;   // gate/up rows (I or SI), or the down contraction length
+  int n;           // pairs in the tile
+  int first;       // first plist position (routed) or first token (shared)
+  bool shared;
+  bool ok;
+};
+
+// Uniform per block: which expert and which pairs this tile covers.
+template <int BITS, int SB>
+__device__ __forceinline__ bool tile_of(const PfArgs& a, int ti, Tile* tl) {
+  if (ti >= a.meta[0]) return false;
+  const int u = a.tile_u[ti];
+  const int U = *a.ucount;
+  const int chunk = ti - a.tstart[u];
+  tl->shared = u == U;
+  if (tl->shared) {
+    tl->blob = a.shared;
+    tl->rows_or_k = a.SI;
+    tl->first = chunk * kChunk;
+    tl->n = min(kChunk, a.T - tl->first);
+    tl->ok = true;
+  } else {
+    const int beg = a.ustart[u] + chunk * kChunk;
+    tl->first = beg;
+    tl->n = min(kChunk, a.ustart[u + 1] - beg);
+    tl->rows_or_k = a.I;
+    const int64_t off = a.slot_table[a.uniq[u]];
+    tl->ok = slot_ok(off, planes_of(a.H, a.I, BITS, SB).blob, a.pool_bytes);
+    tl->blob = a.pool + (tl->ok ? off : 0);
+  }
+  return true;
+}
+
+__device__ __forceinline__ void tile_pairs(const PfArgs& a, const Tile& tl, int tid, int* s_pair, int* s_tok) {
+  if (tid < tl.n) {
+    const int p = tl.shared ? a.T * a.k + tl.first + tid : a.plist[tl.first + tid];
+    s_pair[tid] = p;
+    s_tok[tid] = tl.shared ? tl.first + tid : p / a.k;
+  }
+}
+
+// Gate/up: block = (tile, 128-row block); wave w owns rows 32 w .. +31 of gate
+// and of up (two 16-row MFMA blocks each) for up to 64 pairs (4 column blocks).
+template <int BITS, int SB>
+__global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
+  __shared__ __align__(16) uint8_t xs[kChunk * kRowBytes];
+  __shared__ int s_pair[kChunk], s_tok[kChunk];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int ti = blockIdx.x / a.n_rt, rb = blockIdx.x % a.n_rt;
+  Tile tl;
+  if (!tile_of<BITS, SB>(a, ti, &tl)) return;
+  const int rows = tl.rows_or_k;
+  if (rb * kGuRows >= rows) return;
+  if (!tl.ok) {
+    if (tid == 0 && rb == 0) raise_error(a.flags, kErrRange);
+    return;
+  }
+  tile_pairs(a, tl, tid, s_pair, s_tok);
+  const int n = tl.n, NT = (n + 15) / 16;
+  const Planes P = planes_of(a.H, rows, BITS, SB);
+  const int r = lane & 15, q = lane >> 4;
+  const int row0 = rb * kGuRows + w * 32 + r;   // this lane's A row in MFMA block 0; block 1 is +16
+  const bool w_on = rb * kGuRows + w * 32 < rows;
+  const size_t rbytes = static_cast<size_t>(a.H) * BITS / 8;
+  const int ng = a.H / 64;
+  const uint8_t* code[2] = {tl.blob, tl.blob + P.q};
+  const uint8_t* scl[2] = {tl.blob + 3 * P.q, tl.blob + 3 * P.q + P.s};
+  const uint8_t* bia[2] = {tl.blob + 3 * P.q + 3 * P.s, tl.blob + 3 * P.q + 4 * P.s};
+  f4v acc[2][2][4];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[m][rr][ct] = f4v{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();   // s_tok ready
+  const int st_c = tid >> 2, st_part = tid & 3;   // staging: token, quarter of the slice
+  for (int ks = 0; ks < a.H; ks += kSlice) {
+    // stage 64 tokens x 256 k of float16 x (already in MFMA order)
+    {
+      u32x4 v[8];
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      if (st_c < n) {
+        const u32x4* src = a.x16 + static_cast<size_t>(s_tok[st_c]) * (a.H / 8) + ks / 8 + st_part * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = src[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = zero;
+      }
+      __syncthreads();   // the previous slice has been consumed
+      u32x4* dst = reinterpret_cast<u32x4*>(xs + st_c * kRowBytes) + st_part * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dst[i] = v[i];
+      __syncthreads();
+    }
+    if (!w_on) continue;
+#pragma unroll
+    for (int S = 0; S < 2; ++S) {
+      const int kb = ks + 128 * S;
+      const int g = kb / 64 + (q >> 1);
+      h8v B[4][4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          B[ct][j] = ct < NT ? *reinterpret_cast<const h8v*>(xs + (16 * ct + r) * kRowBytes + (16 * S + 4 * j + q) * 16)
+                             : h8v{};
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const int row = row0 + 16 * rr;
+          const uint8_t* cp = code[m] + row * rbytes + static_cast<size_t>(kb + 32 * q) * BITS / 8;
+          const h2v s = load_h2<SB>(scl[m], static_cast<size_t>(row) * ng + g);
+          const h2v b = load_h2<SB>(bia[m], static_cast<size_t>(row) * ng + g);
+          u32x4 c0 = load16_stream(cp), c1 = c0;
+          if constexpr (BITS == 8) c1 = load16_stream(cp + 16);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            h8v A;
+            if constexpr (BITS == 4) {
+              A = dq_int4(c0[j], s, b);
+            } else {
+              const u32x4& cw = j < 2 ? c0 : c1;
+              A = dq_int8(cw[(2 * j) & 3], cw[(2 * j + 1) & 3], s, b);
+            }
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+              if (ct < NT) acc[m][rr][ct] = mfma16(A, B[ct][j], acc[m][rr][ct]);
+          }
+        }
+      }
+    }
+  }
+  if (!w_on) return;
+  // h = silu(gate) * up, float16, rows 4 q .. 4 q + 3 of each 16-row block
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const int c = 16 * ct + r;
+    if (ct < NT && c < n) {
+      _Float16* hr = a.h + static_cast<size_t>(s_pair[c]) * a.hs;
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int rw = rb * kGuRows + w * 32 + 16 * rr + 4 * q;
+        uint32_t o[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const _Float16 h0 = static_cast<_Float16>(silu(acc[0][rr][ct][2 * i]) * acc[1][rr][ct][2 * i]);
+          const _Float16 h1 = static_cast<_Float16>(silu(acc[0][rr][ct][2 * i + 1]) * acc[1][rr][ct][2 * i + 1]);
+          o[i] = h2_bits(h2v{h0, h1});
+        }
+        *reinterpret_cast<uint2*>(hr + rw) = make_uint2(o[0], o[1]);
+      }
+    }
+  }
+}
+
+// Down: block = (tile, 256-row block of H); wave w owns rows 64 w .. +63 (four
+// 16-row MFMA blocks) for up to 64 pairs.  Writes fp32 partial rows; a tile of
+// an unusable blob writes zeros, so that expert contributes nothing.
+template <int BITS, int SB>
+__global__ __launch_bounds__(kThreads, 2) void k_pf_down(PfArgs a) {
+  __shared__ __align__(16) uint8_t hsm[kChunk * kRowBytes];
+  __shared__ int s_pair[kChunk], s_tok[kChunk];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int ti = blockIdx.x / a.n_rt, rb = blockIdx.x % a.n_rt;
+  Tile tl;
+  if (!tile_of<BITS, SB>(a, ti, &tl)) return;
+  const int K = tl.rows_or_k;
+  const int n = tl.n, NT = (n + 15) / 16;
+  tile_pairs(a, tl, tid, s_pair, s_tok);
+  __syncthreads();
+  const int r = lane & 15, q = lane >> 4;
+  if (!tl.ok) {
+    // zero this block's output rows of the tile's pairs
+    for (int i = tid; i < n * (kDnRows / 4); i += kThreads) {
+      const int c = i / (kDnRows / 4), col = (i % (kDnRows / 4)) * 4;
+      *reinterpret_cast<float4*>(a.partial + static_cast<size_t>(s_pair[c]) * a.H + rb * kDnRows + col) =
+          make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
+  const Planes P = planes_of(a.H, K, BITS, SB);   // down is [H, K]
+  const uint8_t* code = tl.blob + 2 * P.q;
+  const uint8_t* scl = tl.blob + 3 * P.q + 2 * P.s;
+  const uint8_t* bia = tl.blob + 3 * P.q + 5 * P.s;
+  const size_t rbytes = static_cast<size_t>(K) * BITS / 8;
+  const int ng = K / 64;
+  const int row0 = rb * kDnRows + w * 64 + r;
+  f4v acc[4][4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[rr][ct] = f4v{0.f, 0.f, 0.f, 0.f};
+  const int st_c = tid >> 2, st_part = tid & 3;
+  for (int ks = 0; ks < K; ks += kSlice) {
+    {
+      // stage 64 pairs x 256 k of h, permuting each 8 values into slot order
+      u32x4 v[8];
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      if (st_c < n) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(a.h + static_cast<size_t>(s_pair[st_c]) * a.hs + ks) + st_part * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = src[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = zero;
+      }
+      __syncthreads();
+      u32x4* dst = reinterpret_cast<u32x4*>(hsm + st_c * kRowBytes);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dst[chunk_of(st_part * 8 + i)] = permute8<BITS>(v[i]);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int S = 0; S < 2; ++S) {
+      const int kb = ks + 128 * S;
+      const int g = kb / 64 + (q >> 1);
+      h8v B[4][4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          B[ct][j] = ct < NT ? *reinterpret_cast<const h8v*>(hsm + (16 * ct + r) * kRowBytes + (16 * S + 4 * j + q) * 16)
+                             : h8v{};
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = row0 + 16 * rr;
+        const uint8_t* cp = code + row * rbytes + static_cast<size_t>(kb + 32 * q) * BITS / 8;
+        const h2v s = load_h2<SB>(scl, static_cast<size_t>(row) * ng + g);
+        const h2v b = load_h2<SB>(bia, static_cast<size_t>(row) * ng + g);
+        u32x4 c0 = load16_stream(cp), c1 = c0;
+        if constexpr (BITS == 8) c1 = load16_stream(cp + 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          h8v A;
+          if constexpr (BITS == 4) {
+            A = dq_int4(c0[j], s, b);
+          } else {
+            const u32x4& cw = j < 2 ? c0 : c1;
+            A = dq_int8(cw[(2 * j) & 3], cw[(2 * j + 1) & 3], s, b);
+          }
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            if (ct < NT) acc[rr][ct] = mfma16(A, B[ct][j], acc[rr][ct]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const int c = 16 * ct + r;
+    if (ct < NT && c < n) {
+      float* pr = a.partial + static_cast<size_t>(s_pair[c]) * a.H + rb * kDnRows + w * 64 + 4 * q;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        *reinterpret_cast<float4*>(pr + 16 * rr) =
+            make_float4(acc[rr][ct][0], acc[rr][ct][1], acc[rr][ct][2], acc[rr][ct][3]);
+    }
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers.
+
+bool prefill_supported(const moe_desc& d, int T) {
+  return T >= kPrefillMinT && d.act_dtype == kBF16 && d.hidden % kSlice == 0 && d.inter % kSlice == 0 &&
+         d.shared_inter % kSlice == 0 && d.n_experts <= 1024;
+}
+
+static int last_error() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+int launch_prefill_router(const Call& c, int32_t* ids2, float* wts2) {
+  const moe_desc& d = c.d;
+  float* logits = reinterpret_cast<float*>(c.ws + c.L.logits);
+  int32_t* ids = reinterpret_cast<int32_t*>(c.ws + c.L.ids);
+  float* wts = reinterpret_cast<float*>(c.ws + c.L.wts);
+  const dim3 grid((d.n_experts + 63) / 64, (c.T + 63) / 64);
+  launch_kernel(k_pf_router, grid, dim3(kThreads), 0, c.stream, static_cast<const uint16_t*>(c.x),
+                static_cast<const uint16_t*>(c.router_w), logits, c.T, d.hidden, d.n_experts);
+  if (last_error()) return MOE_EHIP;
+  return launch_topk(c, logits, ids, wts, ids2, wts2);
+}
+
+template <int BITS, int SB>
+static void launch_tiles(const PfArgs& base, const Call& c) {
+  const moe_desc& d = c.d;
+  PfArgs a = base;
+  a.n_rt = (d.inter > d.shared_inter ? d.inter : d.shared_inter) / kGuRows;
+  launch_kernel(k_pf_gateup<BITS, SB>, dim3(static_cast<unsigned>(c.L.max_tiles) * a.n_rt), dim3(kThreads), 0,
+                c.stream, a);
+  a.n_rt = d.hidden / kDnRows;
+  launch_kernel(k_pf_down<BITS, SB>, dim3(static_cast<unsigned>(c.L.max_tiles) * a.n_rt), dim3(kThreads), 0,
+                c.stream, a);
+}
+
+int launch_prefill_experts(const Call& c) {
+  const moe_desc& d = c.d;
+  uint8_t* ws = c.ws;
+  const WsLayout& L = c.L;
+  uint32_t* flags = reinterpret_cast<uint32_t*>(ws + L.ctrl);
+  float* gate = reinterpret_cast<float*>(ws + L.gate);
+  float* partial = reinterpret_cast<float*>(ws + L.partial);
+  PfArgs a;
+  a.x16 = reinterpret_cast<const u32x4*>(ws + L.p_x16);
+  a.slot_table = c.slot_table;
+  a.pool = c.pool;
+  a.shared = c.shared;
+  a.ucount = reinterpret_cast<const int32_t*>(ws + L.ucount);
+  a.uniq = reinterpret_cast<const int32_t*>(ws + L.uniq);
+  a.ustart = reinterpret_cast<const int32_t*>(ws + L.ustart);
+  a.plist = reinterpret_cast<const int32_t*>(ws + L.plist);
+  a.tstart = reinterpret_cast<const int32_t*>(ws + L.p_tstart);
+  a.tile_u = reinterpret_cast<const int32_t*>(ws + L.p_tile);
+  a.meta = reinterpret_cast<const int32_t*>(ws + L.p_meta);
+  a.h = reinterpret_cast<_Float16*>(ws + L.h);
+  a.partial = partial;
+  a.flags = flags;
+  a.pool_bytes = d.pool_bytes;
+  a.T = c.T;
+  a.k = d.top_k;
+  a.H = d.hidden;
+  a.E = d.n_experts;
+  a.I = d.inter;
+  a.SI = d.shared_inter;
+  a.hs = L.hstride;
+  a.n_rt = 1;
+
+  const void* gvec = c.shared + d.shared_stride;
+  launch_kernel(k_pf_gate, dim3((c.T + 3) / 4), dim3(kThreads), 0, c.stream, c.x, gvec, gate, c.T, d.hidden);
+  const int nsl_cap = (60 * 1024) / (4 * d.n_experts);
+  const int nsl = nsl_cap < kDispThreads / kWave ? nsl_cap : kDispThreads / kWave;
+  launch_kernel(k_pf_dispatch, dim3(1), dim3(kDispThreads), static_cast<uint32_t>(nsl * d.n_experts * 4), c.stream,
+                c.ids, c.T, d.top_k, d.n_experts, nsl, const_cast<int32_t*>(a.ucount), const_cast<int32_t*>(a.uniq),
+                const_cast<int32_t*>(a.ustart), const_cast<int32_t*>(a.plist), const_cast<int32_t*>(a.tstart),
+                const_cast<int32_t*>(a.tile_u), const_cast<int32_t*>(a.meta), flags);
+  const size_t nchunk = static_cast<size_t>(c.T) * d.hidden / 8;
+  const dim3 xgrid(static_cast<unsigned>((nchunk + kThreads - 1) / kThreads));
+  u32x4* x16 = reinterpret_cast<u32x4*>(ws + L.p_x16);
+  const uint16_t* x = static_cast<const uint16_t*>(c.x);
+  if (d.bits == 4) launch_kernel(k_pf_xprep<4>, xgrid, dim3(kThreads), 0, c.stream, x, x16, c.T, d.hidden);
+  else launch_kernel(k_pf_xprep<8>, xgrid, dim3(kThreads), 0, c.stream, x, x16, c.T, d.hidden);
+  if (d.bits == 4 && d.sb_dtype == kBF16) launch_tiles<4, kBF16>(a, c);
+  else if (d.bits == 4) launch_tiles<4, kF32>(a, c);
+  else if (d.sb_dtype == kBF16) launch_tiles<8, kBF16>(a, c);
+  else launch_tiles<8, kF32>(a, c);
+  if (last_error()) return MOE_EHIP;
+  return launch_combine(c, partial, gate);
+}
+
+}  // namespace moe

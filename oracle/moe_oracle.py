@@ -306,9 +306,10 @@ def summation_bound(x_row: np.ndarray, router: np.ndarray, exact_products: bool)
     gamma_m = m u / (1 - m u), u = 2^-24 (Higham, Accuracy and Stability of
     Numerical Algorithms, Lemma 3.1 / eq. 3.5).  When products are themselves
     rounded (float32 x float32), one more rounding per term gives gamma_n.
+    x_row may also be a [T, H] batch of tokens; the result is then [T, E].
     """
-    n = x_row.shape[0]
+    n = x_row.shape[-1]
     m = n if not exact_products else n - 1
     u = 2.0 ** -24
     gamma = m * u / (1.0 - m * u)
-    return gamma * (np.abs(router) @ np.abs(x_row))
+    return gamma * (np.abs(x_row) @ np.abs(router).T)

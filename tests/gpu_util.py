@@ -43,32 +43,36 @@ def oracle_shape(geo: synth.Geometry) -> O.LayerShape:
                         geo.sb)
 
 
-def unambiguous(geo: synth.Geometry, x_raw: np.ndarray, R_raw: np.ndarray) -> np.ndarray:
-    """Per token: True if every adjacent gap among the top k+1 logits exceeds the
-    sum of both experts' worst-case float32 summation errors."""
+def unambiguous(geo: synth.Geometry, x_raw: np.ndarray, R_raw: np.ndarray, margin_scale: float = 1.0) -> np.ndarray:
+    """Per token: True if every adjacent gap among the top k+1 logits exceeds
+    margin_scale times the sum of both experts' worst-case float32 summation
+    errors (2 for logits summed on MFMA, whose internal rounding is not
+    specified as round-to-nearest per addition)."""
     shape = oracle_shape(geo)
     xs = O.decode_dense(x_raw, geo.act).reshape(-1, geo.hidden)
     rs = O.decode_dense(R_raw, geo.act).reshape(geo.n_experts, geo.hidden)
-    logits = O.router_logits(xs, rs)
     k = min(shape.top_k + 1, geo.n_experts)
-    ok = np.ones(xs.shape[0], dtype=bool)
-    for t in range(xs.shape[0]):
-        order = O.select_topk(logits[t], k)
-        bound = O.summation_bound(xs[t], rs, exact_products=(geo.act == "bf16"))
-        gaps = logits[t, order[:-1]] - logits[t, order[1:]]
-        ok[t] = bool(np.all(gaps > bound[order[:-1]] + bound[order[1:]])) if k > 1 else True
-    return ok
+    if k < 2:
+        return np.ones(xs.shape[0], dtype=bool)
+    logits = O.router_logits(xs, rs)
+    bound = O.summation_bound(xs, rs, exact_products=(geo.act == "bf16"))
+    # a stable sort of -logit keeps lower ids first among equal logits, the oracle's order
+    order = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+    top = np.take_along_axis(logits, order, 1)
+    b = np.take_along_axis(bound, order, 1)
+    return np.all(top[:, :-1] - top[:, 1:] > margin_scale * (b[:, :-1] + b[:, 1:]), axis=1)
 
 
 HOST_POOL_LIMIT = 64 << 20
 
 
 def make_layer(geo: synth.Geometry, seed: int, layer: int, T: int, routing: str = "normal",
-               n_cand: int | None = None, filter_margin: bool = True) -> LayerData:
+               n_cand: int | None = None, filter_margin: bool = True, margin_scale: float = 1.0,
+               oracle_tokens=None) -> LayerData:
     """Seeded layer inputs.  Pools above 64 MiB are generated on the device by
     the counter-based generator (bit-identical to the host one, which a test
     checks); the host copy then only holds the blobs of the experts that the
-    oracle's own routing of these tokens selects."""
+    oracle's own routing of these tokens (or of oracle_tokens only) selects."""
     n_cand = n_cand or max(4 * T, 16)
     cand = synth.tokens(geo, seed, layer, n_cand)
     if routing == "zipf":
@@ -76,7 +80,7 @@ def make_layer(geo: synth.Geometry, seed: int, layer: int, T: int, routing: str 
     else:
         R = synth.router_normal(geo, seed, layer)
     if filter_margin:
-        ok = unambiguous(geo, cand, R)
+        ok = unambiguous(geo, cand, R, margin_scale)
         idx = np.nonzero(ok)[0]
         assert idx.size >= T, f"only {idx.size} of {n_cand} candidate tokens have unambiguous routing"
         x = cand[idx[:T]]
@@ -92,7 +96,8 @@ def make_layer(geo: synth.Geometry, seed: int, layer: int, T: int, routing: str 
     xs = O.decode_dense(x, geo.act).reshape(-1, geo.hidden)
     rs = O.decode_dense(R, geo.act).reshape(geo.n_experts, geo.hidden)
     logits = O.router_logits(xs, rs)
-    needed = sorted({int(e) for t in range(xs.shape[0]) for e in O.select_topk(logits[t], geo.top_k)})
+    rows = range(xs.shape[0]) if oracle_tokens is None else oracle_tokens
+    needed = sorted({int(e) for t in rows for e in O.select_topk(logits[t], geo.top_k)})
     for e in needed:
         synth.fill_blob(geo, geo.inter, synth.blob_key(seed, layer, e), pool[e * stride:(e + 1) * stride])
     return LayerData(geo, np.ascontiguousarray(x), R, pool, slots, shared, seed, layer, True)
@@ -145,6 +150,17 @@ def run(dl: DeviceLayer, T: int, x: torch.Tensor | None = None, ws: torch.Tensor
     torch.cuda.synchronize()
     M.status_check(ws)
     return out, ids, wts
+
+
+def oracle_routing(data: LayerData):
+    """The oracle's ids and renormalised weights for every token (cheap: no experts)."""
+    g = data.geo
+    xs = O.decode_dense(data.x, g.act).reshape(-1, g.hidden)
+    rs = O.decode_dense(data.R, g.act).reshape(g.n_experts, g.hidden)
+    logits = O.router_logits(xs, rs)
+    ids = np.stack([O.select_topk(logits[t], g.top_k) for t in range(xs.shape[0])])
+    w = np.stack([O.renormalised_weights(logits[t, ids[t]]) for t in range(xs.shape[0])])
+    return ids, w
 
 
 def oracle_run(data: LayerData, tokens=None):

@@ -1,0 +1,136 @@
+"""GPU parity of the prefill path against the CPU oracle.
+
+Calls with T >= 16 tokens and bf16 activations run the router and the expert
+products on MFMA (float16 dequantized weights, float16 activations and h, fp32
+sums): the pages' expert computation (Swiftlet README translation, "How it
+works") at a batch size where each expert sees many tokens.  Routing is
+compared exactly on margin-filtered tokens (2x the float32 summation bound,
+since MFMA's internal rounding is not specified per addition); outputs within
+2e-3 of max|y| (+ half a bf16 ulp for bf16 outputs).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import int4_quantized_expert_amd as M
+import synth
+from gpu_util import DEV, check_close, check_routing, make_layer, oracle_routing, oracle_run, run, upload
+
+pytestmark = pytest.mark.gpu
+
+PF = 2.0   # margin scale for MFMA router logits
+
+
+def _parity(data, out="f32", tokens=None):
+    """Checks routing and outputs (check_close asserts the tolerance, with half a
+    bf16 ulp per element for bf16 outputs); returns max error / max|y_ref| of
+    float32 outputs, 0 for bf16 ones, whose rounding alone can exceed 2e-3."""
+    dl = upload(data, out)
+    y, ids, wts = run(dl, data.T)
+    ids_all, w_all = oracle_routing(data)
+    check_routing(ids, wts, ids_all, w_all)
+    y_ref, _, _, _ = oracle_run(data, tokens=tokens)
+    r = check_close(y, y_ref, data.geo.act, tokens=tokens)
+    return r if out == "f32" else 0.0
+
+
+@pytest.mark.parametrize("bits,out,T", [(4, "f32", 100), (4, "bf16", 16), (8, "f32", 77), (8, "bf16", 130)])
+def test_small_prefill_every_token(bits, out, T):
+    """H = 256, 16 experts, I = 256, SI = 512: several tiles, ragged tails, every token checked."""
+    geo = synth.Geometry(256, 16, 2, 256, 512, bits, "bf16", "bf16")
+    data = make_layer(geo, 13, bits, T, n_cand=4 * T, margin_scale=PF)
+    assert _parity(data, out) <= 2e-3
+
+
+def test_small_prefill_f32_scales():
+    geo = synth.Geometry(512, 32, 4, 256, 256, 4, "bf16", "f32")
+    data = make_layer(geo, 14, 0, 48, n_cand=256, margin_scale=PF)
+    assert _parity(data) <= 2e-3
+
+
+def test_80b_prefill_T2048_bf16_out():
+    """80B-A3B layer shape at T = 2048 with near-uniform routing (~40 tokens per
+    expert, all 512 experts used), bf16 output; routing checked for every token,
+    outputs on a sample the oracle evaluates one by one."""
+    T = 2048
+    sample = [0, 1, 2, 511, 777, 1024, 1500, 2046, 2047] + list(range(64, 2048, 160))
+    data = make_layer(synth.PRESETS["80b"], 15, 0, T, n_cand=16000, margin_scale=PF, oracle_tokens=sample)
+    assert _parity(data, "bf16", tokens=sample) <= 2e-3
+
+
+def test_80b_prefill_hot_experts_span_tiles():
+    """Zipf routing over 40 distinct tokens repeated to T = 256: the hottest experts
+    get several 64-pair tiles, and a repeated token gives bitwise equal rows
+    wherever its pairs land in the tiles."""
+    T, U = 256, 40
+    data = make_layer(synth.PRESETS["80b"], 16, 2, U, routing="zipf", n_cand=600, margin_scale=PF,
+                      oracle_tokens=[0, 7, 13, 39])
+    data.x = np.ascontiguousarray(np.tile(data.x, (T // U + 1, 1))[:T])
+    ids_all, _ = oracle_routing(data)
+    counts = np.bincount(ids_all.reshape(-1), minlength=data.geo.n_experts)
+    assert counts.max() > 128, "routing should put more than two tiles on one expert"
+    dl = upload(data)
+    y, ids, wts = run(dl, T)
+    check_routing(ids, wts, ids_all, oracle_routing(data)[1])
+    for t in (0, 7, 13, 39):
+        for rep in (t + U, t + 4 * U):
+            assert torch.equal(y[rep], y[t])
+    sample = [0, 7, 13, 39]
+    y_ref, _, _, _ = oracle_run(data, tokens=sample)
+    assert check_close(y, y_ref, "bf16", tokens=sample) <= 2e-3
+
+
+def test_35b_prefill_int8():
+    T = 64
+    sample = list(range(0, T, 7)) + [T - 1]
+    data = make_layer(synth.PRESETS["35b_int8"], 17, 3, T, routing="zipf", n_cand=4 * T, margin_scale=PF,
+                      oracle_tokens=sample)
+    assert _parity(data, "bf16", tokens=sample) <= 2e-3
+
+
+def test_prefill_split_api_and_repeat_bitwise():
+    data = make_layer(synth.PRESETS["35b"], 18, 1, 64, routing="zipf", n_cand=256, margin_scale=PF,
+                      oracle_tokens=[0])
+    dl = upload(data)
+    T, k, H = data.T, dl.desc.top_k, dl.desc.hidden
+    ws = torch.zeros(M.workspace_bytes(dl.desc, T), dtype=torch.uint8, device=DEV)
+    M.workspace_init(ws)
+    y0, i0, w0 = run(dl, T, ws=ws)
+    y1, i1, w1 = run(dl, T, ws=ws)
+    assert torch.equal(y0, y1) and torch.equal(i0, i1) and torch.equal(w0, w1)
+    ids = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    wts = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    out = torch.empty(T, H, dtype=torch.float32, device=DEV)
+    M.router_topk(dl.desc, T, dl.x, dl.R, ids, wts, ws)
+    M.experts_forward(dl.desc, T, dl.x, ids, wts, dl.slots, dl.pool, dl.shared, out, ws)
+    torch.cuda.synchronize()
+    M.status_check(ws)
+    assert torch.equal(ids, i0) and torch.equal(wts, w0) and torch.equal(out, y0)
+
+
+def test_prefill_tokens_match_single_token_decode():
+    """Per-token invariance across paths: the prefill rows equal T = 1 decode calls
+    within the tolerance, with identical ids."""
+    data = make_layer(synth.PRESETS["80b"], 19, 4, 32, n_cand=400, margin_scale=PF, oracle_tokens=[0])
+    dl = upload(data)
+    yp, ip, _ = run(dl, 32)
+    H = data.geo.hidden
+    scale = yp.abs().max().item()
+    for t in (0, 5, 31):
+        y1, i1, _ = run(dl, 1, x=dl.x[t * H * 2:(t + 1) * H * 2].clone())
+        assert torch.equal(i1[0], ip[t])
+        assert (y1[0] - yp[t]).abs().max().item() <= 2e-3 * scale
+
+
+def test_prefill_bad_slot_reports_erange_and_drops_the_expert():
+    geo = synth.Geometry(256, 16, 2, 256, 256, 4, "bf16", "bf16")
+    data = make_layer(geo, 20, 0, 32, n_cand=128, margin_scale=PF)
+    dl = upload(data)
+    _, ids, _ = run(dl, 32)
+    used = int(ids[0, 0].item())
+    slots = data.slots.copy()
+    slots[used] = dl.pool.numel()
+    with pytest.raises(M.MoeError) as ei:
+        run(upload(data, pool=dl.pool, slots=slots), 32)
+    assert ei.value.code == -5
