@@ -1,17 +1,25 @@
 #!/usr/bin/env python3
-"""MoE-layer decode benchmark on one MI355X.
+"""MoE-layer benchmark on one MI355X.
 
-Workload (default): the 80B-A3B-shaped stack decode -- 48 layers, each with 512
-routed int4 g64 experts (bf16 scales/biases, 1,769,472-byte blobs) resident in
-one 43.5 GB HBM pool, top-10 routing with Zipf(1.1)-skewed popularity, a shared
-expert with a sigmoid gate, T tokens per step (default 1).  One step is one
-token step through all 48 layers in order, each layer one moe_layer_forward
-call; steps are captured as HIP graphs and replayed.  Inputs are synthetic and
-seeded (synth); the pool is filled in place by the device-side generator.
+Workloads (synthetic, seeded; pools filled in place by the device generator):
 
-Prints one JSON line: layer-tokens/s as `value`, the roofline of the dominant
-kernel (algorithmic bytes / its HIP-event duration against 8 TB/s) and the
-CPU oracle timed on a bounded sample of the same workload.
+  80b_stack_decode (default)  80B-A3B-shaped stack decode: 48 layers, each with
+      512 routed int4 g64 experts (bf16 scales/biases, 1,769,472-byte blobs)
+      resident in one 43.5 GB HBM pool, top-10 routing with Zipf(1.1)-skewed
+      popularity, a sigmoid-gated shared expert, T tokens per step (--tokens,
+      default 1), float32 output.  One step = one token step through all 48
+      layers in order, each layer one moe_layer_forward call.
+  35b_rotation_decode  35B-A3B shape (256 experts, top-8) over 40 layers.
+  80b_prefill  the 80B layer shape at T = 2048 tokens per call with near-uniform
+      routing (about 40 tokens per expert, every expert used), bf16 output; one
+      step = all 48 layers once.
+
+Steps are captured as HIP graphs and replayed (--eager launches directly).
+Prints one JSON line: layer-tokens/s as `value`; the roofline of the dominant
+kernel (algorithmic bytes or flops / its dispatch-stamped HIP-event duration);
+the HBM traffic of that kernel from rocprofv3 counters when a summary under
+profiles/ matches the current kernel sources; and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -30,21 +38,24 @@ sys.path.insert(0, ROOT)
 from int4_quantized_expert_amd.profiling import load_traffic  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0     # dense fp16/bf16 MFMA peak of MI355X
 COPY_PROBE_BYTES = 256 << 20
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (% of 8 TB/s) at 80B-shape decode"
 
+# name: (preset, layers, tokens per call (None = --tokens), routing, output dtype)
 WORKLOADS = {
-    "80b_stack_decode": ("80b", 48),
-    "35b_rotation_decode": ("35b", 40),
+    "80b_stack_decode": ("80b", 48, None, "zipf", "f32"),
+    "35b_rotation_decode": ("35b", 40, None, "zipf", "f32"),
+    "80b_prefill": ("80b", 48, 2048, "normal", "bf16"),
 }
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=64, help="timed token steps (each through every layer)")
+    ap.add_argument("--steps", type=int, default=64, help="timed steps (each through every layer)")
     ap.add_argument("--warmup", type=int, default=4)
-    ap.add_argument("--tokens", type=int, default=1, help="tokens per step (decode batch)")
+    ap.add_argument("--tokens", type=int, default=1, help="tokens per call for the decode workloads")
     ap.add_argument("--workload", default="80b_stack_decode", choices=sorted(WORKLOADS))
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying HIP graphs")
@@ -76,10 +87,13 @@ def main():
     import synth
     from synth import gpu as sgpu
 
-    preset, n_layers = WORKLOADS[args.workload]
+    preset, n_layers, T_fixed, routing, out_dt = WORKLOADS[args.workload]
     geo = synth.PRESETS[preset]
-    T, K, W = args.tokens, args.steps, args.warmup
+    T = T_fixed or args.tokens
+    prefill = T_fixed is not None
+    K, W = args.steps, args.warmup
     S = K + W
+    XS = 1 if prefill else S          # distinct token batches per layer
     H, E, k = geo.hidden, geo.n_experts, geo.top_k
     stride = geo.blob_stride
     dev = torch.device("cuda:0")
@@ -101,29 +115,36 @@ def main():
     shared_bytes = geo.shared_bytes
     shared_host = np.concatenate([synth.make_shared(geo, args.seed, l) for l in range(n_layers)])
     shared = torch.from_numpy(shared_host).to(dev)
-    x_host = np.empty((n_layers, S * T, H), dtype=np.uint16)
+    # prefill: 8 distinct 2048-token batches cycle over the layers (each layer has its own router)
+    NX = min(n_layers, 8) if prefill else n_layers
+    x_host = np.empty((NX, XS * T, H), dtype=np.uint16)
     r_host = np.empty((n_layers, E, H), dtype=np.uint16)
+    for l in range(NX):
+        x_host[l] = synth.tokens(geo, args.seed, l, XS * T)
     for l in range(n_layers):
-        x_host[l] = synth.tokens(geo, args.seed, l, S * T)
-        r_host[l] = synth.router_zipf(geo, args.seed, l, x_host[l])
+        r_host[l] = (synth.router_zipf(geo, args.seed, l, x_host[l]) if routing == "zipf"
+                     else synth.router_normal(geo, args.seed, l))
     x = torch.from_numpy(x_host.view(np.uint8)).to(dev)
     routers = torch.from_numpy(r_host.view(np.uint8)).to(dev)
     slots = torch.arange(E, dtype=torch.int64, device=dev) * stride
-    out = torch.empty(n_layers, T, H, dtype=torch.float32, device=dev)
-    ids = torch.full((n_layers, S, T, k), -1, dtype=torch.int32, device=dev)
-    desc = M.desc_for(H, E, k, geo.inter, geo.shared_inter, geo.bits, geo.act, geo.sb, "f32", pool_bytes=E * stride)
+    out = torch.empty(n_layers, T, H, dtype=torch.float32 if out_dt == "f32" else torch.bfloat16, device=dev)
+    ids = torch.full((n_layers, XS, T, k), -1, dtype=torch.int32, device=dev)
+    desc = M.desc_for(H, E, k, geo.inter, geo.shared_inter, geo.bits, geo.act, geo.sb, out_dt,
+                      pool_bytes=E * stride)
     ws = torch.zeros(M.workspace_bytes(desc, T), dtype=torch.uint8, device=dev)
     M.workspace_init(ws)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s: pool {pool.numel() / 1e9:.2f} GB, {n_layers} layers, T={T}")
 
-    x_row = T * H * 2
-    r_bytes = E * H * 2
+    act_sz = 2 if geo.act == "bf16" else 4
+    r_bytes = E * H * act_sz
 
     def layer_call(l, s, strm):
-        M.layer_forward(desc, T, x.data_ptr() + (l * S * T + s * T) * H * 2, routers.data_ptr() + l * r_bytes,
+        xs = s % XS
+        M.layer_forward(desc, T, x.data_ptr() + ((l % NX) * XS * T + xs * T) * H * act_sz,
+                        routers.data_ptr() + l * r_bytes,
                         slots, pool.data_ptr() + l * E * stride, shared.data_ptr() + l * shared_bytes,
-                        out[l], ws, ids[l, s], None, stream=strm)
+                        out[l], ws, ids[l, xs], None, stream=strm)
 
     def step(s, strm):
         for l in range(n_layers):
@@ -165,11 +186,12 @@ def main():
     value = layer_tokens / (total_ms * 1e-3)
     log(f"timed {K} steps: {total_ms:.2f} ms (wall {wall * 1e3:.2f} ms), {ms_per_step * 1e3 / n_layers:.2f} us/layer")
 
-    # algorithmic bytes from the realised routing
+    # algorithmic bytes from the realised routing (distinct experts per layer call)
     ids_h = ids.cpu().numpy()
+    steps_timed = [s % XS for s in range(W, S)]
+    per_ls = np.array([[len(np.unique(ids_h[l, xs])) for xs in steps_timed] for l in range(n_layers)])
     blob = M.blob_bytes(desc, False)
-    fixed = M.blob_bytes(desc, True) + r_bytes + H * 2 + x_row + T * H * 4
-    per_ls = np.array([[len(np.unique(ids_h[l, s])) for s in range(W, S)] for l in range(n_layers)])
+    fixed = M.blob_bytes(desc, True) + r_bytes + H * act_sz + T * H * act_sz + T * H * out.element_size()
     bytes_total = float(per_ls.sum() * blob + fixed * per_ls.size)
     bytes_per_layer = bytes_total / per_ls.size
     stack_gbs = bytes_total / (total_ms * 1e-3) / 1e9
@@ -177,7 +199,7 @@ def main():
     # ---------------------------------------------------------------- per-kernel timing (eager, HIP events)
     # The library attaches a start/end event pair to each kernel dispatch of one call
     # (moe_set_launch_events); the runtime stamps them with that dispatch's execution.
-    n_inst = min(8, K)
+    n_inst = min(8 if not prefill else 2, K)
     timers = [M.LaunchTimer(16) for _ in range(n_inst * n_layers)]
     torch.cuda.synchronize()
     i = 0
@@ -193,22 +215,27 @@ def main():
         raise RuntimeError(f"calls launched differing kernel counts: {sorted(n_k)}")
     n_k = n_k.pop()
     durs = np.array([t.kernel_us() for t in timers])                       # [calls, kernels] us
-    uniq_inst = per_ls[:, :n_inst].T.reshape(-1).astype(np.float64)        # same call order
-    kernels = kernel_bytes(desc, geo, T, n_k, uniq_inst)
+    uniq_inst = np.array([per_ls[l, s - W] for s in range(W, W + n_inst) for l in range(n_layers)],
+                         dtype=np.float64)
+    kernels = kernel_work(desc, geo, T, n_k, uniq_inst, prefill, out.element_size())
     table = []
-    for j, (name, nbytes) in enumerate(kernels):
+    for j, (name, nbytes, flops) in enumerate(kernels):
         us = float(durs[:, j].mean())
-        gbs = float(np.mean(nbytes) / (us * 1e-6) / 1e9) if nbytes is not None else None
-        table.append({"kernel": name, "avg_us": round(us, 3), "min_us": round(float(durs[:, j].min()), 3),
-                      "bytes_per_launch": None if nbytes is None else round(float(np.mean(nbytes))),
-                      "gbs": None if gbs is None else round(gbs, 1)})
+        row = {"kernel": name, "avg_us": round(us, 3), "min_us": round(float(durs[:, j].min()), 3)}
+        if nbytes is not None:
+            row["bytes_per_launch"] = round(float(np.mean(nbytes)))
+            row["gbs"] = round(float(np.mean(nbytes) / (us * 1e-6) / 1e9), 1)
+        if flops is not None:
+            row["tflops"] = round(float(np.mean(flops) / (us * 1e-6) / 1e12), 1)
+            row["mfma_frac"] = round(row["tflops"] / MFMA_F16_PEAK_TFLOPS, 4)
+        table.append(row)
     dom = max(range(n_k), key=lambda j: durs[:, j].mean())
     achieved = table[dom]["gbs"]
     traffic = None
     counters = load_traffic(os.path.join(ROOT, "profiles"), args.workload, T)
     if counters is not None:
         stem = table[dom]["kernel"].split(" ")[0]
-        hits = [r for k, r in counters["kernels"].items() if k.split("<")[0] == stem]
+        hits = [r for kname, r in counters["kernels"].items() if kname.split("<")[0] == stem]
         if len(hits) == 1:
             traffic = hits[0]["traffic_bytes"]
     unit_us = float(durs.sum(axis=1).mean())
@@ -224,13 +251,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32" if not prefill else "f16",
         "data": "synthetic",
         "config": {
-            "workload": args.workload, "layers": n_layers, "tokens_per_step": T, "hidden": H,
+            "workload": args.workload, "layers": n_layers, "tokens_per_call": T, "hidden": H,
             "experts": E, "top_k": k, "inter": geo.inter, "shared_inter": geo.shared_inter,
-            "bits": geo.bits, "group": 64, "scale_dtype": geo.sb, "act_dtype": geo.act,
-            "pool_gb": round(pool.numel() / 1e9, 2), "graphs": not args.eager,
+            "bits": geo.bits, "group": 64, "scale_dtype": geo.sb, "act_dtype": geo.act, "out_dtype": out_dt,
+            "routing": routing, "pool_gb": round(pool.numel() / 1e9, 2), "graphs": not args.eager,
         },
         "hbm": {
             "algorithmic_bytes_per_layer": round(bytes_per_layer),
@@ -252,26 +279,25 @@ def main():
         "kernels": table,
         "kernels_sum_us": round(unit_us, 3),
     }
+    if "tflops" in table[dom]:
+        result["roofline"]["mfma"] = {"achieved": table[dom]["tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
+                                      "unit": "TFLOP/s", "frac": table[dom]["mfma_frac"]}
 
     # ---------------------------------------------------------------- CPU oracle baseline
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(geo, args, x_host, r_host, shared_host, n_layers, S, T,
-                                              shared_bytes)
+        result["cpu_baseline"] = cpu_baseline(geo, args, x_host, r_host, shared_host, n_layers, XS, T,
+                                              shared_bytes, NX)
     print(json.dumps(result), flush=True)
 
 
-def kernel_bytes(desc, geo, T, n_kernels, uniq):
-    """Algorithmic HBM bytes of each kernel of one layer call, per call (array over calls).
-
-    A plane is one matrix of a blob: its codes, scales and biases.  Gate/up planes of the
-    distinct routed experts and of the shared expert, the router matrix, the gate vector and
-    x are read by the launch that computes the gate/up rows; the down planes and the output
-    belong to the launch with the down projections.  Workspace traffic is not counted.
+def kernel_work(desc, geo, T, n_kernels, uniq, prefill, out_bytes):
+    """(name, algorithmic HBM bytes, MFMA flops) of each kernel of one layer call, per call
+    (arrays over calls).  A plane is one matrix of a blob: its codes, scales and biases.
+    Workspace traffic (logits, h, partial rows) is not counted.
     """
-    H, E, I, SI = desc.hidden, desc.n_experts, desc.inter, desc.shared_inter
+    H, E, I, SI, k = desc.hidden, desc.n_experts, desc.inter, desc.shared_inter, desc.top_k
     sb = 4 if geo.sb == "f32" else 2
     act = 4 if geo.act == "f32" else 2
-    outb = 4 if desc.out_dtype == 0 else 2      # MOE_F32 = 0
 
     def plane(rows, cols):
         return rows * cols * geo.bits // 8 + 2 * rows * (cols // 64) * sb
@@ -279,18 +305,32 @@ def kernel_bytes(desc, geo, T, n_kernels, uniq):
     p_r, p_s = plane(I, H), plane(SI, H)       # a down plane [H, I] has the same size
     router = E * H * act + T * H * act
     gvec = H * act
+    out = T * H * out_bytes
+    if prefill:
+        pairs = T * k
+        table = [
+            ("k_pf_router", router, 2.0 * T * E * H),
+            ("k_topk", None, None),
+            ("k_pf_gate", gvec + T * H * act, None),
+            ("k_pf_dispatch", None, None),
+            ("k_pf_xprep", T * H * act, None),
+            ("k_pf_gateup", 2 * p_s + 2 * p_r * uniq, 4.0 * (pairs * I + T * SI) * H),
+            ("k_pf_down", p_s + p_r * uniq, 2.0 * (pairs * I + T * SI) * H),
+            ("k_combine", out, None),
+        ]
+        return table[:n_kernels]
     if n_kernels == 2:
         return [("k_decode_a (router, shared gate/up, top-k, dispatch, routed gate/up)",
-                 router + gvec + 2 * p_s + 2 * p_r * uniq),
-                ("k_decode_b (down projections, ordered combine)", p_s + p_r * uniq + T * H * outb)]
+                 router + gvec + 2 * p_s + 2 * p_r * uniq, None),
+                ("k_decode_b (down projections, ordered combine)", p_s + p_r * uniq + out, None)]
     names = ["k_router_logits", "k_topk", "k_dispatch", "k_gateup", "k_down", "k_combine"]
-    nb = [router, None, gvec + T * H * act, 2 * p_s + 2 * p_r * uniq, p_s + p_r * uniq, T * H * outb]
-    return list(zip(names, nb))[:n_kernels]
+    nb = [router, None, gvec + T * H * act, 2 * p_s + 2 * p_r * uniq, p_s + p_r * uniq, out]
+    return [(n, b, None) for n, b in zip(names, nb)][:n_kernels]
 
 
-def cpu_baseline(geo, args, x_host, r_host, shared_host, n_layers, S, T, shared_bytes):
+def cpu_baseline(geo, args, x_host, r_host, shared_host, n_layers, XS, T, shared_bytes, NX):
     """The oracle (float64, unmodified) on a bounded sample: one token of the
-    first timed step per layer, until the time budget is spent."""
+    first timed batch per layer, until the time budget is spent."""
     import synth
     from oracle import moe_oracle as O
     try:
@@ -303,10 +343,10 @@ def cpu_baseline(geo, args, x_host, r_host, shared_host, n_layers, S, T, shared_
     stride = geo.blob_stride
     pool = np.zeros(geo.n_experts * stride, dtype=np.uint8)
     slots = np.arange(geo.n_experts, dtype=np.int64) * stride
-    s = args.warmup
+    s = args.warmup % XS
     spent, done = 0.0, 0
     for l in range(n_layers):
-        x1 = x_host[l, s * T: s * T + 1]
+        x1 = x_host[l % NX, s * T: s * T + 1]
         xs = O.decode_dense(x1, geo.act).reshape(1, -1)
         rs = O.decode_dense(r_host[l], geo.act).reshape(geo.n_experts, -1)
         for e in O.select_topk(O.router_logits(xs, rs)[0], geo.top_k):
@@ -324,7 +364,7 @@ def cpu_baseline(geo, args, x_host, r_host, shared_host, n_layers, S, T, shared_
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{done} layer-tokens (token 0 of the first timed step, layers 0..{done - 1}), "
+        "sample": f"{done} layer-tokens (token 0 of the first timed batch, layers 0..{done - 1}), "
                   f"{spent:.1f} s of float64 numpy",
     }
 
