@@ -216,6 +216,75 @@ int moe_status_check(void* workspace, void* stream);
 /* Text of the last error on this thread ("" if none). */
 const char* moe_last_error(void);
 
+/* ------------------------------------------------------------------------
+ * Partial residency (expert streaming from pinned host memory).
+ *
+ * The pages keep only part of the experts in fast memory and stream the rest
+ * from a larger store on demand, with a cache that favours frequently and
+ * recently used experts and explicit ordering of copies against the compute
+ * that reads them (Swiftlet README translation, "Design" sections on expert
+ * streaming and the expert cache; flash-moe paper, sections on the expert
+ * cache and hazard management).  Here: a pool of n_slots fixed-stride HBM
+ * slots (pool_base, caller-owned, n_slots * stride bytes, 256-aligned) caching
+ * blobs of a pinned host store (host_pinned, caller-owned, laid out
+ * [n_layers][n_experts][stride], allocated with hipHostMalloc).
+ *
+ * Use per layer call:
+ *   1. moe_router_topk(...) then copy topk_ids to the host (after a sync);
+ *   2. moe_cache_acquire(cache, layer, ids_host, T*k, slot_table_host,
+ *      copy_stream, ready): fills slot_table_host[e] (byte offsets into
+ *      pool_base) for every expert the ids name, enqueues the host->HBM
+ *      copies of the misses on copy_stream and records `ready` after them;
+ *   3. on the compute stream: hipStreamWaitEvent(ready), copy the slot table
+ *      to the device, moe_experts_forward(...), record compute_done;
+ *   4. moe_cache_release(cache, layer, compute_done).
+ * The output equals that of a fully resident pool bit for bit (placement
+ * never changes results).
+ *
+ * Policy: a miss takes an empty slot (lowest first), else evicts the resident
+ * blob with the fewest uses, ties to the oldest last use, then the lower
+ * (layer, id).  Uses count once per acquire that needs the blob and restart
+ * when it is evicted.  Blobs the current call needs are never evicted by it,
+ * nor are blobs of acquires not yet released.
+ * Ordering (no host waits): a victim slot is overwritten only after the
+ * compute_done event of the last released call that read it (if that event
+ * was recorded again since, the wait covers the later work too, which is
+ * still correct); copies of one cache run in issue order even when
+ * copy_stream changes between calls, so `ready` also covers hits on blobs
+ * whose copies are still in flight.
+ *
+ * Planning mode: pool_base = host_pinned = NULL runs the policy alone (no
+ * device calls; copy_stream and the events are ignored and may be NULL).
+ * Not thread-safe: one host thread per cache.
+ */
+typedef struct moe_cache moe_cache;
+
+/* NULL on bad arguments (n_slots < 1, stride not a positive multiple of 256,
+ * pool_base unaligned, exactly one of pool_base / host_pinned NULL). */
+moe_cache* moe_cache_create(int32_t n_slots, int64_t stride, void* pool_base, const void* host_pinned,
+                            int32_t n_layers, int32_t n_experts);
+
+/* ids_host: n expert ids (duplicates allowed).  Returns MOE_OK, MOE_EINVAL
+ * (bad argument or id outside [0, n_experts)), MOE_ENOSPC (more distinct
+ * experts than slots, or too few slots free of unreleased acquires) or
+ * MOE_EHIP; after MOE_EHIP the cache must be destroyed. */
+int moe_cache_acquire(moe_cache* cache, int32_t layer, const int32_t* ids_host, int32_t n,
+                      int64_t* slot_table_host, void* copy_stream, void* ready);
+
+/* Ends the oldest unreleased acquire of `layer`: its slots become evictable,
+ * each after compute_done (a hipEvent_t the caller keeps alive). */
+int moe_cache_release(moe_cache* cache, int32_t layer, void* compute_done);
+
+void moe_cache_stats(const moe_cache* cache, int64_t* hits, int64_t* misses, int64_t* evictions);
+
+/* Slot index holding (layer, id), or -1. */
+int moe_cache_slot_of(const moe_cache* cache, int32_t layer, int32_t id);
+
+void moe_cache_destroy(moe_cache* cache);
+
+/* Text of the last moe_cache_* error on this thread. */
+const char* moe_cache_last_error(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,6 +9,7 @@ if the library is missing, every call raises.
 from ._lib import (  # noqa: F401
     MOE_BF16,
     MOE_F32,
+    ExpertCache,
     LaunchTimer,
     MoeDesc,
     MoeError,

@@ -81,6 +81,20 @@ def lib() -> ctypes.CDLL:
         L.moe_experts_forward.restype = ctypes.c_int
         L.moe_status_check.argtypes = [vp, vp]
         L.moe_status_check.restype = ctypes.c_int
+        L.moe_cache_create.argtypes = [i32, i64, vp, vp, i32, i32]
+        L.moe_cache_create.restype = vp
+        L.moe_cache_acquire.argtypes = [vp, i32, vp, i32, vp, vp, vp]
+        L.moe_cache_acquire.restype = ctypes.c_int
+        L.moe_cache_release.argtypes = [vp, i32, vp]
+        L.moe_cache_release.restype = ctypes.c_int
+        L.moe_cache_stats.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        L.moe_cache_stats.restype = None
+        L.moe_cache_slot_of.argtypes = [vp, i32, i32]
+        L.moe_cache_slot_of.restype = ctypes.c_int
+        L.moe_cache_destroy.argtypes = [vp]
+        L.moe_cache_destroy.restype = None
+        L.moe_cache_last_error.argtypes = []
+        L.moe_cache_last_error.restype = ctypes.c_char_p
         L.moe_set_launch_events.argtypes = [ctypes.POINTER(vp), i32, ctypes.POINTER(i32)]
         L.moe_set_launch_events.restype = ctypes.c_int
         L.moe_last_error.argtypes = []
@@ -218,3 +232,66 @@ class LaunchTimer:
 
 def clear_launch_events() -> None:
     _check(lib().moe_set_launch_events(None, 0, None))
+
+
+def _event_handle(ev) -> int | None:
+    if ev is None or isinstance(ev, int):
+        return ev
+    if ev.cuda_event == 0:      # torch creates the HIP event lazily, at the first record
+        ev.record()
+    return ev.cuda_event
+
+
+def _stream_handle(st) -> int | None:
+    if st is None or isinstance(st, int):
+        return st
+    return st.cuda_stream
+
+
+class ExpertCache:
+    """HBM slot pool caching expert blobs of a pinned host store (moe_cache_*).
+
+    pool / host may be torch tensors or raw addresses; both None gives the
+    policy-only planning mode (no device work).  ids and slot tables are numpy
+    arrays on the host.
+    """
+
+    def __init__(self, n_slots: int, stride: int, pool, host, n_layers: int, n_experts: int):
+        self.n_experts = n_experts
+        self._h = lib().moe_cache_create(n_slots, stride, _ptr(pool), _ptr(host), n_layers, n_experts)
+        if not self._h:
+            raise MoeError(-1, "moe_cache_create rejected its arguments")
+
+    def _check(self, rc: int) -> None:
+        if rc != 0:
+            raise MoeError(rc, lib().moe_cache_last_error().decode())
+
+    def acquire(self, layer: int, ids_host, slot_table_host, copy_stream=None, ready=None) -> None:
+        import numpy as np
+        ids = np.ascontiguousarray(ids_host, dtype=np.int32).reshape(-1)
+        assert slot_table_host.dtype == np.int64 and slot_table_host.size >= self.n_experts
+        assert slot_table_host.flags["C_CONTIGUOUS"]
+        self._check(lib().moe_cache_acquire(self._h, layer, ids.ctypes.data, ids.size, slot_table_host.ctypes.data,
+                                            _stream_handle(copy_stream), _event_handle(ready)))
+
+    def release(self, layer: int, compute_done=None) -> None:
+        self._check(lib().moe_cache_release(self._h, layer, _event_handle(compute_done)))
+
+    def stats(self) -> tuple[int, int, int]:
+        h, m, e = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        lib().moe_cache_stats(self._h, ctypes.byref(h), ctypes.byref(m), ctypes.byref(e))
+        return h.value, m.value, e.value
+
+    def slot_of(self, layer: int, expert: int) -> int:
+        return lib().moe_cache_slot_of(self._h, layer, expert)
+
+    def close(self) -> None:
+        if self._h:
+            lib().moe_cache_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
