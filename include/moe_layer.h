@@ -220,11 +220,11 @@ const char* moe_last_error(void);
  * Partial residency (expert streaming from pinned host memory).
  *
  * The pages keep only part of the experts in fast memory and stream the rest
- * from a larger store on demand, with a cache that favours frequently and
- * recently used experts and explicit ordering of copies against the compute
- * that reads them (Swiftlet README translation, "Design" sections on expert
- * streaming and the expert cache; flash-moe paper, sections on the expert
- * cache and hazard management).  Here: a pool of n_slots fixed-stride HBM
+ * from a larger store on demand, with a bounded cache pool that favours
+ * frequently and recently used experts, and order GPU work with explicit
+ * hazard management (linlog.top article, core design 3, the expert cache
+ * pool; Swiftlet README translation, "How it works" and "Relation to
+ * TurboFieldfare"; kerneldigest.dev article, inference flow, the cache step).  Here: a pool of n_slots fixed-stride HBM
  * slots (pool_base, caller-owned, n_slots * stride bytes, 256-aligned) caching
  * blobs of a pinned host store (host_pinned, caller-owned, laid out
  * [n_layers][n_experts][stride], allocated with hipHostMalloc).

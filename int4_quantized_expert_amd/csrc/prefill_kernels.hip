@@ -3,7 +3,7 @@
 // The pages' method is the same as in decode -- softmax router, top-k, expert
 // SwiGLU with MLX-affine group-quantized weights, a weighted combine plus a
 // sigmoid-gated shared expert (Swiftlet README translation, "How it works";
-// Qwen3-Next model card, "Model Overview") -- but with ~40 tokens per expert
+// linlog.top article, "Why MoE can stream") -- but with ~40 tokens per expert
 // the expert products become small dense GEMMs, so they run on MFMA:
 //
 //   k_pf_router    logits = x R^T on v_mfma_f32_16x16x32_bf16 (exact bf16

@@ -2,13 +2,14 @@
 // in pinned host memory (host code only; the C ABI is in include/moe_layer.h).
 //
 // The pages stream experts that do not fit in fast memory from a larger,
-// slower store, keep the frequently used ones resident with a frequency plus
-// recency policy, and order the copies explicitly against the compute that
-// reads them (Swiftlet README translation, "Design" sections on expert
-// streaming and caching; flash-moe paper, sections on the expert cache and on
-// hazard management).  Here the store is pinned host memory, the fast memory
-// is a slot pool in HBM, copies run on a caller-given side stream, and every
-// ordering is expressed with HIP events, never with host waits:
+// slower store, keep the frequently used ones resident in a bounded pool with
+// a frequency plus recency policy, and order the GPU work with explicit hazard
+// management (linlog.top article, core design 3, the expert cache pool;
+// Swiftlet README translation, "How it works" and "Relation to
+// TurboFieldfare"; kerneldigest.dev article, inference flow, the cache step).
+// Here the store is pinned host memory, the fast memory is a slot pool in
+// HBM, copies run on a caller-given side stream, and every ordering is
+// expressed with HIP events, never with host waits:
 //   - a slot is overwritten only after the compute_done event of the last
 //     call that read it (write-after-read);
 //   - compute waits on `ready`, recorded after all copies issued so far, and

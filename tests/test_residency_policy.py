@@ -5,8 +5,9 @@ uses, then oldest last use, then lower (layer, id); empty slots first, lowest
 first; blobs of the current call and of unreleased calls are never victims)
 is replayed beside the library on random call sequences, and every slot
 assignment and counter must agree.  The pages name the policy only as
-frequency plus recency (Swiftlet README translation, expert cache; flash-moe
-paper, expert cache), so this pins our stated reading, not the pages.
+frequency plus recency (linlog.top article, core design 3, the expert cache
+pool; Swiftlet README translation, "How it works"), so this pins our stated
+reading, not the pages.
 """
 
 import numpy as np
