@@ -60,30 +60,6 @@ __device__ __forceinline__ uint64_t load_tagged(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One wave waits until flags[0..n) all equal `tag` (bounded, with backoff).
-__device__ __forceinline__ bool wait_block_flags(const uint32_t* f, int n, uint32_t tag, int lane, uint32_t& spins, uint32_t limit) {
-  for (;;) {
-    bool mine = true;
-    for (int b = lane; b < n; b += kWave)
-      mine &= __hip_atomic_load(const_cast<uint32_t*>(f) + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
-    if (__all(mine)) return true;
-    if (++spins > limit) return false;
-    __builtin_amdgcn_s_sleep(2);
-  }
-}
-
-// All of this block's stores are acknowledged, then thread 0 raises its flag.
-// The flag only says the tagged words should be there: readers still check
-// every word's tag.
-// The flag is written to kFusedReplicas copies (kFusedMaxBlocks words apart),
-// so that each copy is read by only a fraction of the blocks.
-__device__ __forceinline__ void publish_block_flag(uint32_t* f, uint32_t tag) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x < kFusedReplicas)
-    __hip_atomic_store(f + threadIdx.x * kFusedMaxBlocks + blockIdx.x, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 struct LdsA {
   uint8_t* x;        // [T][H] activations, storage dtype
   float* lg;         // [T][E] logits
@@ -129,17 +105,35 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
   uint32_t spins = 0;
   bool timed_out = false;
 
+  // This call's tag: the epoch word plus one.  Launch B advances the word, so
+  // it cannot change while any block of this launch still has to read it.
   if (tid == 0) {
     const uint32_t ep = __hip_atomic_load(a.ctrl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s.misc[1] = static_cast<int32_t>(ep + 1u);
-    __hip_atomic_store(a.arrive + blockIdx.x, ep + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   {
+    // x and the slot table into LDS; each round requests its elements of both
+    // before storing any, so the copy costs one memory round trip per round
     const int n16 = T * H * a.act_sz / 16;
     const u32x4* src = static_cast<const u32x4*>(a.x);
     u32x4* dst = reinterpret_cast<u32x4*>(s.x);
-    for (int i = tid; i < n16; i += kThreads) dst[i] = src[i];
-    for (int e = tid; e < E; e += kThreads) s.slot[e] = a.slot_table[e];
+    const int n = n16 > E ? n16 : E;
+    for (int i0 = 0; i0 < n; i0 += 2 * kThreads) {
+      u32x4 xv[2];
+      int64_t sv[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = i0 + u * kThreads + tid;
+        xv[u] = src[i < n16 ? i : 0];
+        sv[u] = a.slot_table[i < E ? i : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = i0 + u * kThreads + tid;
+        if (i < n16) dst[i] = xv[u];
+        if (i < E) s.slot[i] = sv[u];
+      }
+    }
   }
   __syncthreads();
   const uint32_t tag = static_cast<uint32_t>(s.misc[1]);
@@ -157,12 +151,22 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
   const int sh_tasks = (a.SI + rlh.rpp - 1) / rlh.rpp;
   const int bwave = blockIdx.x * kWaves + wave;
   for (int task = bwave * kRouterRowsPerWave; task < router_tasks; task += nwaves * kRouterRowsPerWave) {
+    // both rows requested before either is used (a dead row re-reads row 0)
+    ActRaw<ACT> rw[kRouterRowsPerWave];
+    int ee[kRouterRowsPerWave];
+#pragma unroll
     for (int j = 0; j < kRouterRowsPerWave; ++j) {
       const int e = (task + j) * rlh.rpp + rlh.sub_row;
+      ee[j] = task + j < router_tasks && e < E ? e : -1;
+      load_act_raw<ACT>(static_cast<const uint8_t*>(a.router) + static_cast<size_t>(ee[j] < 0 ? 0 : e) * xrow,
+                        rlh.seg0, rw[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kRouterRowsPerWave; ++j) {
       if (task + j >= router_tasks) break;
-      const bool active = e < E;
+      const bool active = ee[j] >= 0;
       float r[kSegCodes];
-      if (active) load_act_seg<ACT>(static_cast<const uint8_t*>(a.router) + static_cast<size_t>(e) * xrow, rlh.seg0, r);
+      act_raw_f32<ACT>(rw[j], r);
       for (int t = 0; t < T; ++t) {
         float acc = 0.f;
         if (active) {
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
         acc = group_sum(acc, rlh.width);
         if (active)   // every lane of the row holds the sum: each stores some of the copies
           for (int rep = lane % rlh.width; rep < kFusedReplicas; rep += rlh.width)
-            store_tagged(a.lg + (static_cast<size_t>(rep) * T + t) * E + e, acc, tag);
+            store_tagged(a.lg + (static_cast<size_t>(rep) * T + t) * E + ee[j], acc, tag);
       }
     }
   }
@@ -187,23 +191,17 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
     const int sh_blocks = a.nb > router_blocks ? a.nb - router_blocks : a.nb;
     const int sh_b = a.nb > router_blocks ? static_cast<int>(blockIdx.x) - router_blocks : static_cast<int>(blockIdx.x);
     for (int task = sh_b >= 0 ? wave * sh_blocks + sh_b : sh_tasks; task < sh_tasks; task += sh_blocks * kWaves) {
-      const int rr = task * rlh.rpp + rlh.sub_row;
-      const bool ok = rr < a.SI;
-      Seg<BITS> cg, cu;
-      float sg = 0.f, su = 0.f, bg = 0.f, bu = 0.f;
-      if (ok) {
-        const int64_t qo = rr * row_bytes + static_cast<int64_t>(rlh.seg0) * seg_bytes;
-        cg = load_codes<BITS>(a.shared + qo);
-        cu = load_codes<BITS>(a.shared + pl.q + qo);
-        const size_t si = static_cast<size_t>(rr) * gpr + rlh.seg0 / 2;
-        sg = load_scalar<SB>(a.shared + 3 * pl.q, si);
-        su = load_scalar<SB>(a.shared + 3 * pl.q + pl.s, si);
-        bg = load_scalar<SB>(a.shared + 3 * pl.q + 3 * pl.s, si);
-        bu = load_scalar<SB>(a.shared + 3 * pl.q + 4 * pl.s, si);
-      } else {
-#pragma unroll
-        for (int i = 0; i < BITS / 4; ++i) { cg.w[i] = u32x4{0, 0, 0, 0}; cu.w[i] = u32x4{0, 0, 0, 0}; }
-      }
+      const int rr0 = task * rlh.rpp + rlh.sub_row;
+      const bool ok = rr0 < a.SI;
+      const int rr = ok ? rr0 : 0;   // loads stay unconditional; the store is masked
+      const int64_t qo = rr * row_bytes + static_cast<int64_t>(rlh.seg0) * seg_bytes;
+      const Seg<BITS> cg = load_codes<BITS>(a.shared + qo);
+      const Seg<BITS> cu = load_codes<BITS>(a.shared + pl.q + qo);
+      const size_t si = static_cast<size_t>(rr) * gpr + rlh.seg0 / 2;
+      const uint32_t sg = load_raw<SB>(a.shared + 3 * pl.q, si);
+      const uint32_t su = load_raw<SB>(a.shared + 3 * pl.q + pl.s, si);
+      const uint32_t bg = load_raw<SB>(a.shared + 3 * pl.q + 3 * pl.s, si);
+      const uint32_t bu = load_raw<SB>(a.shared + 3 * pl.q + 4 * pl.s, si);
       for (int t = 0; t < T; ++t) {
         float v[1][kSegCodes];
         load_act_seg<ACT>(s.x + t * xrow, rlh.seg0, v[0]);
@@ -212,8 +210,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
         seg_qdot_nt<BITS, 1>(cg, v, qg);
         seg_qdot_nt<BITS, 1>(cu, v, qu);
         float accg = 0.f, accu = 0.f;
-        accg += seg_value(sg, bg, qg[0], xs);
-        accu += seg_value(su, bu, qu[0], xs);
+        accg += seg_value(raw_value<SB>(sg), raw_value<SB>(bg), qg[0], xs);
+        accu += seg_value(raw_value<SB>(su), raw_value<SB>(bu), qu[0], xs);
         const float g = group_sum(accg, rlh.width);
         const float u = group_sum(accu, rlh.width);
         if (ok && (lane % rlh.width) == 0) a.h[(static_cast<size_t>(T) * k + t) * a.hs + rr] = silu(g) * u;
@@ -238,12 +236,9 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
     }
   }
 
-  // ---- phase K: gather all logits (tag-checked), top-k, dispatch
-  if (blockIdx.x < router_blocks) publish_block_flag(a.flag_r, tag);
+  // ---- phase K: gather all logits (each word checked against this call's
+  // tag, re-read until every one has arrived), top-k, dispatch
   const int rep = blockIdx.x % kFusedReplicas;
-  if (wave == 0 && !wait_block_flags(a.flag_r + rep * kFusedMaxBlocks, router_blocks, tag, lane, spins, a.spin_limit))
-    timed_out = true;
-  __syncthreads();
   for (;;) {
     int missing = 0;
     for (int i = tid; i < T * E; i += kThreads) {
@@ -329,43 +324,35 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
     const int g_hi = min(total, g_lo + per_wave);
     constexpr int kBatch = 4;
     for (int g0 = g_lo; g0 < g_hi; g0 += kBatch) {
+      // every row of the batch is requested before any is used: no branches on
+      // the loads (a row past the end repeats the first one, an unusable blob
+      // reads blob 0; both are masked at the store) and raw scale bits
       Seg<BITS> cg[kBatch], cu[kBatch];
-      float sg[kBatch], su[kBatch], bg[kBatch], bu[kBatch];
+      uint32_t sg[kBatch], su[kBatch], bg[kBatch], bu[kBatch];
       int uu[kBatch], rr[kBatch];
       bool vv[kBatch];
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
         const int g = g0 + b;
-        uu[b] = -1;
-        rr[b] = 0;
-        vv[b] = false;
-        if (g < g_hi) {
-          const int u = g / groups_per_expert;
-          const int r = (g % groups_per_expert) * rlh.rpp + rlh.sub_row;
-          const int64_t off = s.slot[s.uniq[u]];
-          const bool valid = slot_ok(off, pl.blob, a.pool_bytes);
-          uu[b] = u;
-          rr[b] = r;
-          vv[b] = valid;
-          if (valid) {
-            const uint8_t* blob = a.pool + off;
-            const int64_t qo = r * row_bytes + static_cast<int64_t>(rlh.seg0) * seg_bytes;
-            cg[b] = load_codes<BITS>(blob + qo);
-            cu[b] = load_codes<BITS>(blob + pl.q + qo);
-            const size_t si = static_cast<size_t>(r) * gpr + rlh.seg0 / 2;
-            sg[b] = load_scalar<SB>(blob + 3 * pl.q, si);
-            su[b] = load_scalar<SB>(blob + 3 * pl.q + pl.s, si);
-            bg[b] = load_scalar<SB>(blob + 3 * pl.q + 3 * pl.s, si);
-            bu[b] = load_scalar<SB>(blob + 3 * pl.q + 4 * pl.s, si);
-          } else if (lane == 0) {
-            raise_error(a.ctrl, kErrRange);
-          }
-        }
-        if (!vv[b]) {
-#pragma unroll
-          for (int i = 0; i < BITS / 4; ++i) { cg[b].w[i] = u32x4{0, 0, 0, 0}; cu[b].w[i] = u32x4{0, 0, 0, 0}; }
-          sg[b] = su[b] = bg[b] = bu[b] = 0.f;
-        }
+        const bool live = g < g_hi;
+        const int gc = live ? g : g_lo;
+        const int u = gc / groups_per_expert;
+        const int r = (gc % groups_per_expert) * rlh.rpp + rlh.sub_row;
+        const int64_t off = s.slot[s.uniq[u]];
+        const bool valid = slot_ok(off, pl.blob, a.pool_bytes);
+        uu[b] = live ? u : -1;
+        rr[b] = r;
+        vv[b] = valid;
+        if (live && !valid && lane == 0) raise_error(a.ctrl, kErrRange);
+        const uint8_t* blob = a.pool + (valid ? off : 0);
+        const int64_t qo = r * row_bytes + static_cast<int64_t>(rlh.seg0) * seg_bytes;
+        cg[b] = load_codes<BITS>(blob + qo);
+        cu[b] = load_codes<BITS>(blob + pl.q + qo);
+        const size_t si = static_cast<size_t>(r) * gpr + rlh.seg0 / 2;
+        sg[b] = load_raw<SB>(blob + 3 * pl.q, si);
+        su[b] = load_raw<SB>(blob + 3 * pl.q + pl.s, si);
+        bg[b] = load_raw<SB>(blob + 3 * pl.q + 3 * pl.s, si);
+        bu[b] = load_raw<SB>(blob + 3 * pl.q + 4 * pl.s, si);
       }
       for (int t = 0; t < T; ++t) {
         float v[1][kSegCodes];
@@ -380,8 +367,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
           seg_qdot_nt<BITS, 1>(cg[b], v, qg);
           seg_qdot_nt<BITS, 1>(cu[b], v, qu);
           float accg = 0.f, accu = 0.f;
-          accg += seg_value(sg[b], bg[b], qg[0], xs);
-          accu += seg_value(su[b], bu[b], qu[0], xs);
+          accg += seg_value(raw_value<SB>(sg[b]), raw_value<SB>(bg[b]), qg[0], xs);
+          accu += seg_value(raw_value<SB>(su[b]), raw_value<SB>(bu[b]), qu[0], xs);
           const float g = group_sum(accg, rlh.width);
           const float u = group_sum(accu, rlh.width);
           if ((lane % rlh.width) == 0)
@@ -391,12 +378,6 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
     }
   }
   if (timed_out && lane == 0) raise_error(a.ctrl, kErrTimeout);
-  // Block 0 retires the tag once every block's arrival word shows that it has
-  // read the epoch (by now they all have; the check makes it certain).
-  if (blockIdx.x == 0 && wave == 0) {
-    if (!wait_block_flags(a.arrive, a.nb, tag, lane, spins, a.spin_limit) && lane == 0) raise_error(a.ctrl, kErrTimeout);
-    if (lane == 0) __hip_atomic_store(a.ctrl + 1, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -406,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
 template <int BITS>
 struct DownTask {
   Seg<BITS> code;
-  float sc, bi;
+  uint32_t sc, bi;   // raw scale and bias bits (see load_raw)
   int j;        // distinct-expert index (U = shared), -1 if none
   int rloc;     // this lane's row within the block, -1 if outside
   bool valid;   // blob offset usable
@@ -418,7 +399,21 @@ struct LdsB {
   float* wts;        // [T][k]
   float* sig;        // [T]
   float* part;       // [(T k + T)][rb]
+  float* h;          // [(T k + T)][hs] staged activations, or nullptr when they do not fit
+  float* hsum;       // [(T k + T)][hs / 32] segment sums of the staged rows
 };
+
+// h rows are staged in LDS when they take at most this many bytes.  Each
+// 32-float segment sits at a stride of kSegPad floats, so the 16 lanes that
+// read the 16 segments of one row hit different LDS banks.
+constexpr size_t kHStageMax = 56 * 1024;
+constexpr int kSegPad = kSegCodes + 4;
+
+__host__ __device__ inline size_t h_stage_floats(int T, int k, int hs) {
+  return static_cast<size_t>(T) * (k + 1) * (hs / kSegCodes) * kSegPad;
+}
+
+__host__ __device__ inline bool h_staged(int T, int k, int hs) { return h_stage_floats(T, k, hs) * 4 <= kHStageMax; }
 
 __device__ inline LdsB carve_b(uint8_t* base, const FusedArgs& a) {
   LdsB s;
@@ -429,47 +424,45 @@ __device__ inline LdsB carve_b(uint8_t* base, const FusedArgs& a) {
   s.wts = reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * a.k * 4));
   s.sig = reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * 4));
   s.part = reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * (a.k + 1) * a.rb * 4));
+  const bool st = h_staged(a.T, a.k, a.hs);
+  s.h = st ? reinterpret_cast<float*>(take(h_stage_floats(a.T, a.k, a.hs) * 4)) : nullptr;
+  s.hsum = st ? reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * (a.k + 1) * (a.hs / kSegCodes) * 4)) : nullptr;
   return s;
 }
 
+// Requests one task's codes, scale and bias.  Straight-line code with
+// selects only: a dead task (past ntask) or a row past the end reads a valid
+// row of the shared blob or of blob 0, and an unusable blob reads blob 0;
+// all are masked at use.  Without branches the compiler keeps every task's
+// loads of a wave in flight together instead of draining them in between.
 template <int BITS, int SB>
 __device__ __forceinline__ void load_down_task(DownTask<BITS>& d, int task, int ntask, int np, int U, int row_lo,
                                                const FusedArgs& a, const LdsB& s, const RowLanes& rli,
                                                const RowLanes& rls) {
-  d.j = -1;
-  d.rloc = -1;
-  d.valid = false;
-  d.sc = 0.f;
-  d.bi = 0.f;
-#pragma unroll
-  for (int i = 0; i < BITS / 4; ++i) d.code.w[i] = u32x4{0, 0, 0, 0};
-  if (task >= ntask) return;
-  const int j = task / np, p = task % np;
+  const bool live = task < ntask;
+  const int tk = live ? task : 0;
+  const int j = tk / np, p = tk % np;
   const bool is_sh = j == U;
-  const RowLanes& rl = is_sh ? rls : rli;
+  const int rpp = is_sh ? rls.rpp : rli.rpp;
+  const int sub_row = is_sh ? rls.sub_row : rli.sub_row;
+  const int seg0 = is_sh ? rls.seg0 : rli.seg0;
   const int inter = is_sh ? a.SI : a.I;
   const Planes pl = planes_of(a.H, inter, BITS, SB);
-  const uint8_t* blob = a.shared;
-  bool valid = true;
-  if (!is_sh) {
-    const int64_t off = s.uoff[j];
-    valid = slot_ok(off, pl.blob, a.pool_bytes);
-    blob = a.pool + (valid ? off : 0);
-  }
-  d.j = j;
+  const int64_t off = s.uoff[is_sh ? 0 : j];
+  const bool valid = is_sh || slot_ok(off, pl.blob, a.pool_bytes);
+  const uint8_t* blob = is_sh ? a.shared : a.pool + (valid ? off : 0);
+  const int rloc = p * rpp + sub_row;
+  const int r0 = row_lo + rloc;
+  const bool in = rloc < a.rb && r0 < a.H;
+  const int r = in ? r0 : row_lo;
+  const int64_t row_bytes = static_cast<int64_t>(inter) * BITS / 8;
+  d.code = load_codes<BITS>(blob + 2 * pl.q + r * row_bytes + static_cast<int64_t>(seg0) * (kSegCodes * BITS / 8));
+  const size_t si = static_cast<size_t>(r) * (inter / 64) + seg0 / 2;
+  d.sc = load_raw<SB>(blob + 3 * pl.q + 2 * pl.s, si);
+  d.bi = load_raw<SB>(blob + 3 * pl.q + 5 * pl.s, si);
+  d.j = live ? j : -1;
+  d.rloc = live && in ? rloc : -1;
   d.valid = valid;
-  const int rloc = p * rl.rpp + rl.sub_row;
-  const int r = row_lo + rloc;
-  if (rloc < a.rb && r < a.H) {
-    d.rloc = rloc;
-    if (valid) {
-      const int64_t row_bytes = static_cast<int64_t>(inter) * BITS / 8;
-      d.code = load_codes<BITS>(blob + 2 * pl.q + r * row_bytes + static_cast<int64_t>(rl.seg0) * (kSegCodes * BITS / 8));
-      const size_t si = static_cast<size_t>(r) * (inter / 64) + rl.seg0 / 2;
-      d.sc = load_scalar<SB>(blob + 3 * pl.q + 2 * pl.s, si);
-      d.bi = load_scalar<SB>(blob + 3 * pl.q + 5 * pl.s, si);
-    }
-  }
 }
 
 template <int BITS, int SB, int OUT>
@@ -480,11 +473,27 @@ __global__ __launch_bounds__(kThreads) void k_decode_b(FusedArgs a) {
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int T = a.T, k = a.k;
+  // Retire launch A's tag: every block of A has finished, so none can still
+  // read the epoch word.
+  if (blockIdx.x == 0 && tid == 0)
+    __hip_atomic_store(a.ctrl + 1, __hip_atomic_load(a.ctrl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the routing record, all of it requested at once (bounded by umax, not by U)
   const int U = *a.ucount;
-  for (int i = tid; i < U; i += kThreads) s.uoff[i] = a.uoff[i];
-  for (int i = tid; i < U * T; i += kThreads) s.pidx[i] = a.pidx[i];
-  for (int i = tid; i < T * k; i += kThreads) s.wts[i] = a.wts[i];
-  for (int i = tid; i < T; i += kThreads) s.sig[i] = a.sig[i];
+  {
+    // one round trip per round: every array's element requested before any store
+    const int n = a.umax * T > T * k ? a.umax * T : T * k;
+    for (int i = tid; i < n; i += kThreads) {
+      const int64_t uo = a.uoff[i < a.umax ? i : 0];
+      const int32_t pi = a.pidx[i < a.umax * T ? i : 0];
+      const float wt = a.wts[i < T * k ? i : 0];
+      const float sg = a.sig[i < T ? i : 0];
+      if (i < a.umax) s.uoff[i] = uo;
+      if (i < a.umax * T) s.pidx[i] = pi;
+      if (i < T * k) s.wts[i] = wt;
+      if (i < T) s.sig[i] = sg;
+    }
+  }
   __syncthreads();
 
   const RowLanes rli = row_lanes(a.I, lane);
@@ -496,39 +505,52 @@ __global__ __launch_bounds__(kThreads) void k_decode_b(FusedArgs a) {
   const int ntask = nd * np;
   DownTask<BITS> dt[kMaxDownPerWave];
   float hv[kMaxDownPerWave][1][kSegCodes];
-  int t0[kMaxDownPerWave];
   for (int base = 0; base < ntask; base += kWaves * kMaxDownPerWave) {
-    // codes of this round's tasks and the h segment of each task's first pair,
-    // all requested before any compute
+    // codes of this round's tasks, all requested before any compute
 #pragma unroll
-    for (int q = 0; q < kMaxDownPerWave; ++q) {
+    for (int q = 0; q < kMaxDownPerWave; ++q)
       load_down_task<BITS, SB>(dt[q], base + wave + q * kWaves, ntask, np, U, row_lo, a, s, rli, rls);
-      t0[q] = -1;
-      if (dt[q].j >= 0) {
-        const bool is_sh = dt[q].j == U;
-        int t = 0;
-        if (!is_sh)
-          while (t < T && s.pidx[dt[q].j * T + t] < 0) ++t;
-        t0[q] = t;
-        const size_t pair = is_sh ? static_cast<size_t>(T) * k : static_cast<size_t>(t) * k + s.pidx[dt[q].j * T + t];
-        load_f32_seg(a.h + pair * a.hs, (is_sh ? rls : rli).seg0, hv[q][0]);
+    if (s.h && base == 0) {
+      // all h rows into LDS once, while the codes above are in flight
+      const float4* src = reinterpret_cast<const float4*>(a.h);
+      lds_u32x4* dst = (lds_u32x4*)(s.h);
+      const int n4 = T * (k + 1) * a.hs / 4;             // 8 float4 per segment
+      for (int i = tid; i < n4; i += kThreads) {
+        const float4 v = src[i];
+        dst[(i >> 3) * (kSegPad / 4) + (i & 7)] = u32x4{__float_as_uint(v.x), __float_as_uint(v.y),
+                                                          __float_as_uint(v.z), __float_as_uint(v.w)};
       }
+      __syncthreads();
+      // segment sums once per block, in the order seg_sum uses
+      const int nseg = a.hs / kSegCodes;
+      for (int i = tid; i < T * (k + 1) * nseg; i += kThreads) {
+        float v[kSegCodes];
+        load_lds_seg(s.h + static_cast<size_t>(i) * kSegPad, 0, v);
+        ((lds_f32*)(s.hsum))[i] = seg_sum(v);
+      }
+      __syncthreads();
     }
 #pragma unroll
     for (int q = 0; q < kMaxDownPerWave; ++q) {
       if (dt[q].j < 0) continue;
       const bool is_sh = dt[q].j == U;
       const RowLanes& rl = is_sh ? rls : rli;
-      for (int t = t0[q]; t < T; ++t) {
+      for (int t = 0; t < T; ++t) {
         const int i = is_sh ? k : s.pidx[dt[q].j * T + t];
         if (i < 0) continue;
         const size_t pair = is_sh ? static_cast<size_t>(T) * k + t : static_cast<size_t>(t) * k + i;
-        if (t != t0[q]) load_f32_seg(a.h + pair * a.hs, rl.seg0, hv[q][0]);
-        const float hs = seg_sum(hv[q][0]);
+        float hs;
+        if (s.h) {
+          load_lds_seg(s.h + (pair * (a.hs / kSegCodes) + rl.seg0) * kSegPad, 0, hv[q][0]);
+          hs = ((const lds_f32*)(s.hsum))[pair * (a.hs / kSegCodes) + rl.seg0];
+        } else {
+          load_f32_seg(a.h + pair * a.hs, rl.seg0, hv[q][0]);
+          hs = seg_sum(hv[q][0]);
+        }
         float qv[1];
         seg_qdot_nt<BITS, 1>(dt[q].code, hv[q], qv);
         float acc = 0.f;
-        acc += seg_value(dt[q].sc, dt[q].bi, qv[0], hs);
+        acc += seg_value(raw_value<SB>(dt[q].sc), raw_value<SB>(dt[q].bi), qv[0], hs);
         const float v = group_sum(acc, rl.width);
         if ((lane % rl.width) == 0 && dt[q].rloc >= 0) s.part[pair * a.rb + dt[q].rloc] = dt[q].valid ? v : 0.f;
       }
@@ -567,7 +589,7 @@ size_t lds_bytes_a(int T, int H, int E, int k, int umax, int act_sz) {
   return o;
 }
 
-size_t lds_bytes_b(int T, int k, int umax, int rb) {
+size_t lds_bytes_b(int T, int k, int umax, int rb, int hs) {
   size_t o = 0;
   auto take = [&](size_t n) { o += (n + 15) / 16 * 16; };
   take(static_cast<size_t>(umax) * 8);
@@ -575,6 +597,10 @@ size_t lds_bytes_b(int T, int k, int umax, int rb) {
   take(static_cast<size_t>(T) * k * 4);
   take(static_cast<size_t>(T) * 4);
   take(static_cast<size_t>(T) * (k + 1) * rb * 4);
+  if (h_staged(T, k, hs)) {
+    take(h_stage_floats(T, k, hs) * 4);
+    take(static_cast<size_t>(T) * (k + 1) * (hs / kSegCodes) * 4);
+  }
   return o;
 }
 
@@ -643,7 +669,7 @@ int fused_plan(const moe_desc& d, int T, FusedPlan* plan) {
       plan->nb_b = cus * 2;
       plan->rb_b = (d.hidden + plan->nb_b - 1) / plan->nb_b;
       plan->nb_b = (d.hidden + plan->rb_b - 1) / plan->rb_b;
-      plan->lds_b = lds_bytes_b(T, d.top_k, umax, plan->rb_b);
+      plan->lds_b = lds_bytes_b(T, d.top_k, umax, plan->rb_b, d.inter > d.shared_inter ? d.inter : d.shared_inter);
       return MOE_OK;
     }
   }
@@ -670,8 +696,6 @@ int launch_decode_fused(const Call& c, const FusedPlan& plan) {
   a.uoff = reinterpret_cast<int64_t*>(c.ws + c.L.f_uoff);
   a.pidx = reinterpret_cast<int32_t*>(c.ws + c.L.f_pidx);
   a.ctrl = reinterpret_cast<uint32_t*>(c.ws + c.L.ctrl);
-  a.flag_r = reinterpret_cast<uint32_t*>(c.ws + c.L.f_arrive);
-  a.arrive = a.flag_r + kFusedReplicas * kFusedMaxBlocks;
   a.pool_bytes = d.pool_bytes;
   a.shared_stride = d.shared_stride;
   a.T = c.T;

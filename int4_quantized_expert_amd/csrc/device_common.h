@@ -52,6 +52,27 @@ __device__ __forceinline__ float load_scalar(const void* base, size_t idx) {
   }
 }
 
+// Raw bits of one scale/bias value (float32 bits, or bf16 bits in the low
+// half), converted only where used: a conversion right after the load would
+// make the compiler wait for it there, serialising loads meant to overlap.
+template <int DT>
+__device__ __forceinline__ uint32_t load_raw(const void* base, size_t idx) {
+  if constexpr (DT == kF32) {
+    return static_cast<const uint32_t*>(base)[idx];
+  } else {
+    return static_cast<const uint16_t*>(base)[idx];
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float raw_value(uint32_t raw) {
+  if constexpr (DT == kF32) {
+    return __uint_as_float(raw);
+  } else {
+    return __uint_as_float(raw << 16);
+  }
+}
+
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *static_cast<const u32x4*>(p);
 }
@@ -62,29 +83,47 @@ __device__ __forceinline__ u32x4 load16_stream(const void* p) {
 
 // 32 activation values of one segment -> float registers.
 template <int ACT>
-__device__ __forceinline__ void load_act_seg(const void* row, int seg, float (&v)[kSegCodes]) {
+using ActRaw = u32x4[ACT == kF32 ? 8 : 4];
+
+// The raw 16-byte words of one 32-value activation segment; act_raw_f32
+// converts them.  Split so that callers can request several segments before
+// waiting for any.
+template <int ACT>
+__device__ __forceinline__ void load_act_raw(const void* row, int seg, ActRaw<ACT>& w) {
+  const u32x4* p = ACT == kF32
+                       ? reinterpret_cast<const u32x4*>(static_cast<const float*>(row) + seg * kSegCodes)
+                       : reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(row) + seg * kSegCodes);
+#pragma unroll
+  for (int i = 0; i < (ACT == kF32 ? 8 : 4); ++i) w[i] = p[i];
+}
+
+template <int ACT>
+__device__ __forceinline__ void act_raw_f32(const ActRaw<ACT>& w, float (&v)[kSegCodes]) {
   if constexpr (ACT == kF32) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(row) + seg * kSegCodes);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      u32x4 w = p[i];
-      v[4 * i + 0] = __uint_as_float(w[0]);
-      v[4 * i + 1] = __uint_as_float(w[1]);
-      v[4 * i + 2] = __uint_as_float(w[2]);
-      v[4 * i + 3] = __uint_as_float(w[3]);
+      v[4 * i + 0] = __uint_as_float(w[i][0]);
+      v[4 * i + 1] = __uint_as_float(w[i][1]);
+      v[4 * i + 2] = __uint_as_float(w[i][2]);
+      v[4 * i + 3] = __uint_as_float(w[i][3]);
     }
   } else {
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(row) + seg * kSegCodes);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      u32x4 w = p[i];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        v[8 * i + 2 * j + 0] = __uint_as_float(w[j] << 16);
-        v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+        v[8 * i + 2 * j + 0] = __uint_as_float(w[i][j] << 16);
+        v[8 * i + 2 * j + 1] = __uint_as_float(w[i][j] & 0xffff0000u);
       }
     }
   }
+}
+
+template <int ACT>
+__device__ __forceinline__ void load_act_seg(const void* row, int seg, float (&v)[kSegCodes]) {
+  ActRaw<ACT> w;
+  load_act_raw<ACT>(row, seg, w);
+  act_raw_f32<ACT>(w, v);
 }
 
 // 32 float32 values (e.g. an h segment) from global memory.
@@ -93,6 +132,23 @@ __device__ __forceinline__ void load_f32_seg(const float* row, int seg, float (&
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     u32x4 w = p[i];
+    v[4 * i + 0] = __uint_as_float(w[0]);
+    v[4 * i + 1] = __uint_as_float(w[1]);
+    v[4 * i + 2] = __uint_as_float(w[2]);
+    v[4 * i + 3] = __uint_as_float(w[3]);
+  }
+}
+
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+// 32 floats of one segment from LDS (p points into shared memory; the cast
+// makes the compiler use LDS instructions rather than generic ones).
+__device__ __forceinline__ void load_lds_seg(const float* p, int seg, float (&v)[kSegCodes]) {
+  const lds_u32x4* q = reinterpret_cast<const lds_u32x4*>((const lds_f32*)(p) + seg * kSegCodes);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const u32x4 w = q[i];
     v[4 * i + 0] = __uint_as_float(w[0]);
     v[4 * i + 1] = __uint_as_float(w[1]);
     v[4 * i + 2] = __uint_as_float(w[2]);
@@ -218,8 +274,11 @@ __device__ __forceinline__ void seg_qdot_nt(const Seg<BITS>& s_in, const float (
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t w = s.w[0][k];
-      const uint32_t lo = w & 0x0f0f0f0fu;
-      const uint32_t hi = (w >> 4) & 0x0f0f0f0fu;
+      uint32_t lo = w & 0x0f0f0f0fu;
+      uint32_t hi = (w >> 4) & 0x0f0f0f0fu;
+      // opaque masked words: the byte conversions below then map to single
+      // v_cvt_f32_ubyte{0..3} instead of a bit-field extract plus a conversion
+      asm volatile("" : "+v"(lo), "+v"(hi));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float qe = static_cast<float>((lo >> (8 * j)) & 0xffu);

@@ -27,8 +27,6 @@ struct FusedArgs {
   int64_t* uoff;        // [umax] their blob offsets
   int32_t* pidx;        // [umax, T] rank of expert u for token t, or -1
   uint32_t* ctrl;       // [0] error flags, [1] epoch
-  uint32_t* flag_r;     // [kFusedReplicas][kFusedMaxBlocks] "phase R stores done" tags
-  uint32_t* arrive;     // [nb] per-block "epoch read" tags
   int64_t pool_bytes;
   int64_t shared_stride;
   int T, H, E, k, I, SI, hs;

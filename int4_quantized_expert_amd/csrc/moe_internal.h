@@ -30,7 +30,6 @@ struct WsLayout {
   size_t f_lg;       // two-launch path: [kFusedReplicas][T, E] tagged logits (uint64)
   size_t f_uoff;     // two-launch path: [min(T k, E)] int64 blob offsets of the distinct experts
   size_t f_pidx;     // two-launch path: [min(T k, E), T] int32 rank of expert u for token t
-  size_t f_arrive;   // two-launch path: [kFusedReplicas + 1][kFusedMaxBlocks] uint32 flags, then arrival tags
   size_t p_x16;      // prefill: [T, H] float16 activations in MFMA k order
   size_t p_meta;     // prefill: int32 [0] number of expert tiles
   size_t p_tstart;   // prefill: [min(T k, E) + 2] int32 first tile of each distinct expert, then of the shared one
@@ -54,7 +53,6 @@ inline WsLayout ws_layout(const moe_desc& d, int32_t T) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes > 0 ? bytes : 1); return at; };
   L.ctrl = take(256);
-  L.f_arrive = take((kFusedReplicas + 1) * kFusedMaxBlocks * 4);
   L.logits = take(static_cast<size_t>(T) * d.n_experts * 4);
   L.ids = take(Tk * 4);
   L.wts = take(Tk * 4);
