@@ -65,7 +65,6 @@ struct LdsA {
   float* lg;         // [T][E] logits
   int32_t* ids;      // [T][k]
   float* vals;       // [T][k] chosen logits, then weights
-  float* ev;         // [kWaves][64] exp values for the ordered sum
   int64_t* slot;     // [E]
   int32_t* umap;     // [E] expert -> distinct index
   int32_t* uniq;     // [umax]
@@ -82,7 +81,6 @@ __device__ inline LdsA carve_a(uint8_t* base, const FusedArgs& a) {
   s.lg = reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * a.E * 4));
   s.ids = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.T) * a.k * 4));
   s.vals = reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * a.k * 4));
-  s.ev = reinterpret_cast<float*>(take(kWaves * 64 * 4));
   s.slot = reinterpret_cast<int64_t*>(take(static_cast<size_t>(a.E) * 8));
   s.umap = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.E) * 4));
   s.uniq = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.umax) * 4));
@@ -100,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
   const LdsA s = carve_a(lds_raw, a);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform: lets the compiler use scalar math
   const int T = a.T, H = a.H, E = a.E, k = a.k;
   uint32_t spins = 0;
   bool timed_out = false;
@@ -111,6 +109,53 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
     const uint32_t ep = __hip_atomic_load(a.ctrl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s.misc[1] = static_cast<int32_t>(ep + 1u);
   }
+  // ---- phase R setup: router rows on the first blocks (block-major,
+  // kRouterRowsPerWave row groups per wave, so only a few blocks produce
+  // logits); shared gate/up rows on the waves of the other blocks (wave-major,
+  // spread over the machine).  The first task's weights are requested before
+  // the x / slot-table copy below, so the two memory round trips overlap.
+  const size_t xrow = static_cast<size_t>(H) * a.act_sz;
+  const int nwaves = a.nb * kWaves;
+  const RowLanes rlh = row_lanes(H, lane);
+  const int router_tasks = (E + rlh.rpp - 1) / rlh.rpp;
+  const int router_waves = (router_tasks + kRouterRowsPerWave - 1) / kRouterRowsPerWave;
+  const int router_blocks = min(a.nb, (router_waves + kWaves - 1) / kWaves);
+  const int sh_tasks = (a.SI + rlh.rpp - 1) / rlh.rpp;
+  const int bwave = blockIdx.x * kWaves + wave;
+  const int r_task0 = bwave * kRouterRowsPerWave;
+  ActRaw<ACT> rw[kRouterRowsPerWave];
+  int ee[kRouterRowsPerWave];
+  auto load_router_rows = [&](int task) {
+#pragma unroll
+    for (int j = 0; j < kRouterRowsPerWave; ++j) {
+      const int e = (task + j) * rlh.rpp + rlh.sub_row;
+      ee[j] = task + j < router_tasks && e < E ? e : -1;
+      load_act_raw<ACT>(static_cast<const uint8_t*>(a.router) + static_cast<size_t>(ee[j] < 0 ? 0 : e) * xrow,
+                        rlh.seg0, rw[j]);
+    }
+  };
+  if (r_task0 < router_tasks) load_router_rows(r_task0);
+  const Planes pls = planes_of(H, a.SI, BITS, SB);
+  const int64_t sh_row_bytes = static_cast<int64_t>(H) * BITS / 8;
+  const int gpr = H / 64;
+  const int sh_blocks = a.nb > router_blocks ? a.nb - router_blocks : a.nb;
+  const int sh_b = a.nb > router_blocks ? static_cast<int>(blockIdx.x) - router_blocks : static_cast<int>(blockIdx.x);
+  const int s_task0 = sh_b >= 0 ? wave * sh_blocks + sh_b : sh_tasks;
+  Seg<BITS> scg, scu;
+  uint32_t ssg = 0, ssu = 0, sbg = 0, sbu = 0;
+  auto load_shared_row = [&](int task) {
+    const int rr0 = task * rlh.rpp + rlh.sub_row;
+    const int rr = rr0 < a.SI ? rr0 : 0;   // loads stay unconditional; the store is masked
+    const int64_t qo = rr * sh_row_bytes + static_cast<int64_t>(rlh.seg0) * (kSegCodes * BITS / 8);
+    scg = load_codes<BITS>(a.shared + qo);
+    scu = load_codes<BITS>(a.shared + pls.q + qo);
+    const size_t si = static_cast<size_t>(rr) * gpr + rlh.seg0 / 2;
+    ssg = load_raw<SB>(a.shared + 3 * pls.q, si);
+    ssu = load_raw<SB>(a.shared + 3 * pls.q + pls.s, si);
+    sbg = load_raw<SB>(a.shared + 3 * pls.q + 3 * pls.s, si);
+    sbu = load_raw<SB>(a.shared + 3 * pls.q + 4 * pls.s, si);
+  };
+  if (s_task0 < sh_tasks) load_shared_row(s_task0);
   {
     // x and the slot table into LDS; each round requests its elements of both
     // before storing any, so the copy costs one memory round trip per round
@@ -137,30 +182,11 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
   }
   __syncthreads();
   const uint32_t tag = static_cast<uint32_t>(s.misc[1]);
-  const size_t xrow = static_cast<size_t>(H) * a.act_sz;
-
-  // ---- phase R: router rows on the first blocks (block-major, kRouterRowsPerWave
-  // row groups per wave, so only a few blocks produce logits); shared gate/up
-  // rows on the waves of the other blocks (wave-major, spread over the machine)
   const int gwave = wave * a.nb + blockIdx.x;
-  const int nwaves = a.nb * kWaves;
-  const RowLanes rlh = row_lanes(H, lane);
-  const int router_tasks = (E + rlh.rpp - 1) / rlh.rpp;
-  const int router_waves = (router_tasks + kRouterRowsPerWave - 1) / kRouterRowsPerWave;
-  const int router_blocks = min(a.nb, (router_waves + kWaves - 1) / kWaves);
-  const int sh_tasks = (a.SI + rlh.rpp - 1) / rlh.rpp;
-  const int bwave = blockIdx.x * kWaves + wave;
-  for (int task = bwave * kRouterRowsPerWave; task < router_tasks; task += nwaves * kRouterRowsPerWave) {
-    // both rows requested before either is used (a dead row re-reads row 0)
-    ActRaw<ACT> rw[kRouterRowsPerWave];
-    int ee[kRouterRowsPerWave];
-#pragma unroll
-    for (int j = 0; j < kRouterRowsPerWave; ++j) {
-      const int e = (task + j) * rlh.rpp + rlh.sub_row;
-      ee[j] = task + j < router_tasks && e < E ? e : -1;
-      load_act_raw<ACT>(static_cast<const uint8_t*>(a.router) + static_cast<size_t>(ee[j] < 0 ? 0 : e) * xrow,
-                        rlh.seg0, rw[j]);
-    }
+
+  // ---- phase R
+  for (int task = r_task0; task < router_tasks; task += nwaves * kRouterRowsPerWave) {
+    if (task != r_task0) load_router_rows(task);
 #pragma unroll
     for (int j = 0; j < kRouterRowsPerWave; ++j) {
       if (task + j >= router_tasks) break;
@@ -182,40 +208,23 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
       }
     }
   }
-  {
-    const Planes pl = planes_of(H, a.SI, BITS, SB);
-    const int64_t row_bytes = static_cast<int64_t>(H) * BITS / 8;
-    const int seg_bytes = kSegCodes * BITS / 8;
-    const int gpr = H / 64;
-    // waves of blocks past the router blocks (all waves if there are none)
-    const int sh_blocks = a.nb > router_blocks ? a.nb - router_blocks : a.nb;
-    const int sh_b = a.nb > router_blocks ? static_cast<int>(blockIdx.x) - router_blocks : static_cast<int>(blockIdx.x);
-    for (int task = sh_b >= 0 ? wave * sh_blocks + sh_b : sh_tasks; task < sh_tasks; task += sh_blocks * kWaves) {
-      const int rr0 = task * rlh.rpp + rlh.sub_row;
-      const bool ok = rr0 < a.SI;
-      const int rr = ok ? rr0 : 0;   // loads stay unconditional; the store is masked
-      const int64_t qo = rr * row_bytes + static_cast<int64_t>(rlh.seg0) * seg_bytes;
-      const Seg<BITS> cg = load_codes<BITS>(a.shared + qo);
-      const Seg<BITS> cu = load_codes<BITS>(a.shared + pl.q + qo);
-      const size_t si = static_cast<size_t>(rr) * gpr + rlh.seg0 / 2;
-      const uint32_t sg = load_raw<SB>(a.shared + 3 * pl.q, si);
-      const uint32_t su = load_raw<SB>(a.shared + 3 * pl.q + pl.s, si);
-      const uint32_t bg = load_raw<SB>(a.shared + 3 * pl.q + 3 * pl.s, si);
-      const uint32_t bu = load_raw<SB>(a.shared + 3 * pl.q + 4 * pl.s, si);
-      for (int t = 0; t < T; ++t) {
-        float v[1][kSegCodes];
-        load_act_seg<ACT>(s.x + t * xrow, rlh.seg0, v[0]);
-        const float xs = seg_sum(v[0]);
-        float qg[1], qu[1];
-        seg_qdot_nt<BITS, 1>(cg, v, qg);
-        seg_qdot_nt<BITS, 1>(cu, v, qu);
-        float accg = 0.f, accu = 0.f;
-        accg += seg_value(raw_value<SB>(sg), raw_value<SB>(bg), qg[0], xs);
-        accu += seg_value(raw_value<SB>(su), raw_value<SB>(bu), qu[0], xs);
-        const float g = group_sum(accg, rlh.width);
-        const float u = group_sum(accu, rlh.width);
-        if (ok && (lane % rlh.width) == 0) a.h[(static_cast<size_t>(T) * k + t) * a.hs + rr] = silu(g) * u;
-      }
+  for (int task = s_task0; task < sh_tasks; task += sh_blocks * kWaves) {
+    if (task != s_task0) load_shared_row(task);
+    const int rr = task * rlh.rpp + rlh.sub_row;
+    const bool ok = rr < a.SI;
+    for (int t = 0; t < T; ++t) {
+      float v[1][kSegCodes];
+      load_act_seg<ACT>(s.x + t * xrow, rlh.seg0, v[0]);
+      const float xs = seg_sum(v[0]);
+      float qg[1], qu[1];
+      seg_qdot_nt<BITS, 1>(scg, v, qg);
+      seg_qdot_nt<BITS, 1>(scu, v, qu);
+      float accg = 0.f, accu = 0.f;
+      accg += seg_value(raw_value<SB>(ssg), raw_value<SB>(sbg), qg[0], xs);
+      accu += seg_value(raw_value<SB>(ssu), raw_value<SB>(sbu), qu[0], xs);
+      const float g = group_sum(accg, rlh.width);
+      const float u = group_sum(accu, rlh.width);
+      if (ok && (lane % rlh.width) == 0) a.h[(static_cast<size_t>(T) * k + t) * a.hs + rr] = silu(g) * u;
     }
   }
   // sigmoid(g . x_t) on block 0 (lane covers segments L, L + 64, ... as in the staged path)
@@ -251,8 +260,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
     __builtin_amdgcn_s_sleep(2);
   }
   for (int t = wave; t < T; t += kWaves)
-    topk_wave(s.lg + static_cast<size_t>(t) * E, E, k, lane, s.cand + wave * kCandMax, s.ev + wave * 64,
-              s.ids + t * k, s.vals + t * k);
+    topk_wave(s.lg + static_cast<size_t>(t) * E, E, k, lane, s.cand + wave * kCandMax, s.ids + t * k,
+              s.vals + t * k);
   if (T == 1) {
     // one token: its k experts are distinct; order them by id with a rank count
     if (wave == 0) {
@@ -430,38 +439,122 @@ __device__ inline LdsB carve_b(uint8_t* base, const FusedArgs& a) {
   return s;
 }
 
+// Per-launch constants of the down tasks, computed once per wave: plane
+// offsets and row sizes of the routed and the shared blobs, and this lane's
+// byte offsets within a row.
+struct DownCtx {
+  int64_t q_r, s_r, q_s, s_s;       // code / scale plane bytes (routed, shared)
+  int64_t blob_r;                   // routed blob bytes
+  int64_t rowb_r, rowb_s;           // code bytes per row
+  int gpr_r, gpr_s;                 // scale groups per row
+  int np;                           // row passes per expert
+};
+
+template <int BITS, int SB>
+__device__ __forceinline__ DownCtx down_ctx(const FusedArgs& a, const RowLanes& rli, const RowLanes& rls) {
+  DownCtx c;
+  const Planes pr = planes_of(a.H, a.I, BITS, SB), ps = planes_of(a.H, a.SI, BITS, SB);
+  c.q_r = pr.q;
+  c.s_r = pr.s;
+  c.q_s = ps.q;
+  c.s_s = ps.s;
+  c.blob_r = pr.blob;
+  c.rowb_r = static_cast<int64_t>(a.I) * BITS / 8;
+  c.rowb_s = static_cast<int64_t>(a.SI) * BITS / 8;
+  c.gpr_r = a.I / 64;
+  c.gpr_s = a.SI / 64;
+  const int rpp_min = rli.rpp < rls.rpp ? rli.rpp : rls.rpp;
+  c.np = (a.rb + rpp_min - 1) / rpp_min;
+  return c;
+}
+
 // Requests one task's codes, scale and bias.  Straight-line code with
 // selects only: a dead task (past ntask) or a row past the end reads a valid
 // row of the shared blob or of blob 0, and an unusable blob reads blob 0;
 // all are masked at use.  Without branches the compiler keeps every task's
 // loads of a wave in flight together instead of draining them in between.
 template <int BITS, int SB>
-__device__ __forceinline__ void load_down_task(DownTask<BITS>& d, int task, int ntask, int np, int U, int row_lo,
-                                               const FusedArgs& a, const LdsB& s, const RowLanes& rli,
+__device__ __forceinline__ void load_down_task(DownTask<BITS>& d, int task, int ntask, const DownCtx& c, int U,
+                                               int row_lo, const FusedArgs& a, const LdsB& s, const RowLanes& rli,
                                                const RowLanes& rls) {
   const bool live = task < ntask;
   const int tk = live ? task : 0;
-  const int j = tk / np, p = tk % np;
+  const int j = c.np == 1 ? tk : tk / c.np;
+  const int p = c.np == 1 ? 0 : tk - j * c.np;
   const bool is_sh = j == U;
   const int rpp = is_sh ? rls.rpp : rli.rpp;
   const int sub_row = is_sh ? rls.sub_row : rli.sub_row;
   const int seg0 = is_sh ? rls.seg0 : rli.seg0;
-  const int inter = is_sh ? a.SI : a.I;
-  const Planes pl = planes_of(a.H, inter, BITS, SB);
   const int64_t off = s.uoff[is_sh ? 0 : j];
-  const bool valid = is_sh || slot_ok(off, pl.blob, a.pool_bytes);
+  const bool valid = is_sh || slot_ok(off, c.blob_r, a.pool_bytes);
   const uint8_t* blob = is_sh ? a.shared : a.pool + (valid ? off : 0);
+  const int64_t q = is_sh ? c.q_s : c.q_r;
+  const int64_t sp = is_sh ? c.s_s : c.s_r;
   const int rloc = p * rpp + sub_row;
   const int r0 = row_lo + rloc;
   const bool in = rloc < a.rb && r0 < a.H;
   const int r = in ? r0 : row_lo;
-  const int64_t row_bytes = static_cast<int64_t>(inter) * BITS / 8;
-  d.code = load_codes<BITS>(blob + 2 * pl.q + r * row_bytes + static_cast<int64_t>(seg0) * (kSegCodes * BITS / 8));
-  const size_t si = static_cast<size_t>(r) * (inter / 64) + seg0 / 2;
-  d.sc = load_raw<SB>(blob + 3 * pl.q + 2 * pl.s, si);
-  d.bi = load_raw<SB>(blob + 3 * pl.q + 5 * pl.s, si);
+  d.code = load_codes<BITS>(blob + 2 * q + r * (is_sh ? c.rowb_s : c.rowb_r) + seg0 * (kSegCodes * BITS / 8));
+  const int si = r * (is_sh ? c.gpr_s : c.gpr_r) + seg0 / 2;
+  d.sc = load_raw<SB>(blob + 3 * q + 2 * sp, si);
+  d.bi = load_raw<SB>(blob + 3 * q + 5 * sp, si);
   d.j = live ? j : -1;
   d.rloc = live && in ? rloc : -1;
+  d.valid = valid;
+}
+
+// This lane's byte offsets inside a routed and inside the shared blob for the
+// single-pass layout (every task = rpp rows of one expert, np == 1): the code
+// word, the scale and the bias of its segment of its row.
+struct LaneOffsets {
+  int64_t code_r, sc_r, bi_r, code_s, sc_s, bi_s;
+  int rloc_r, rloc_s;   // row within the block, -1 if past the block or H
+};
+
+template <int BITS, int SB>
+__device__ __forceinline__ LaneOffsets lane_offsets(const FusedArgs& a, const DownCtx& c, const RowLanes& rli,
+                                                    const RowLanes& rls, int row_lo) {
+  LaneOffsets o;
+  const int sbsz = SB == kF32 ? 4 : 2;
+  const int r0r = row_lo + rli.sub_row, r0s = row_lo + rls.sub_row;
+  const bool inr = rli.sub_row < a.rb && r0r < a.H, ins = rls.sub_row < a.rb && r0s < a.H;
+  const int rr = inr ? r0r : row_lo, rs = ins ? r0s : row_lo;
+  o.code_r = 2 * c.q_r + rr * c.rowb_r + rli.seg0 * (kSegCodes * BITS / 8);
+  o.sc_r = 3 * c.q_r + 2 * c.s_r + static_cast<int64_t>(rr * c.gpr_r + rli.seg0 / 2) * sbsz;
+  o.bi_r = o.sc_r + 3 * c.s_r;
+  o.code_s = 2 * c.q_s + rs * c.rowb_s + rls.seg0 * (kSegCodes * BITS / 8);
+  o.sc_s = 3 * c.q_s + 2 * c.s_s + static_cast<int64_t>(rs * c.gpr_s + rls.seg0 / 2) * sbsz;
+  o.bi_s = o.sc_s + 3 * c.s_s;
+  o.rloc_r = inr ? rli.sub_row : -1;
+  o.rloc_s = ins ? rls.sub_row : -1;
+  return o;
+}
+
+template <int SB>
+__device__ __forceinline__ uint32_t load_raw_at(const uint8_t* p) {
+  if constexpr (SB == kF32) return *reinterpret_cast<const uint32_t*>(p);
+  else return *reinterpret_cast<const uint16_t*>(p);
+}
+
+// load_down_task for np == 1: the expert index is the task index, the blob
+// base is wave-uniform (scalar) and the lane offsets are precomputed.
+template <int BITS, int SB>
+__device__ __forceinline__ void load_down_task_1(DownTask<BITS>& d, int task, int ntask, const DownCtx& c, int U,
+                                                 const FusedArgs& a, const LdsB& s, const LaneOffsets& o) {
+  const bool live = task < ntask;
+  const int j = live ? task : U;            // a dead task re-reads the shared blob
+  const bool is_sh = j == U;
+  const int64_t off = is_sh ? 0 : s.uoff[j];
+  const bool valid = is_sh || slot_ok(off, c.blob_r, a.pool_bytes);
+  const uint64_t bits = reinterpret_cast<uint64_t>(is_sh ? a.shared : a.pool + (valid ? off : 0));
+  const uint8_t* blob = reinterpret_cast<const uint8_t*>(
+      (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(bits >> 32))) << 32) |
+      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(bits))));
+  d.code = load_codes<BITS>(blob + (is_sh ? o.code_s : o.code_r));
+  d.sc = load_raw_at<SB>(blob + (is_sh ? o.sc_s : o.sc_r));
+  d.bi = load_raw_at<SB>(blob + (is_sh ? o.bi_s : o.bi_r));
+  d.j = live ? j : -1;
+  d.rloc = live ? (is_sh ? o.rloc_s : o.rloc_r) : -1;
   d.valid = valid;
 }
 
@@ -471,7 +564,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_b(FusedArgs a) {
   const LdsB s = carve_b(lds_raw, a);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform: lets the compiler use scalar math
   const int T = a.T, k = a.k;
   // Retire launch A's tag: every block of A has finished, so none can still
   // read the epoch word.
@@ -499,17 +592,22 @@ __global__ __launch_bounds__(kThreads) void k_decode_b(FusedArgs a) {
   const RowLanes rli = row_lanes(a.I, lane);
   const RowLanes rls = row_lanes(a.SI, lane);
   const int row_lo = blockIdx.x * a.rb;
-  const int nd = U + 1;
-  const int rpp_min = rli.rpp < rls.rpp ? rli.rpp : rls.rpp;
-  const int np = (a.rb + rpp_min - 1) / rpp_min;
-  const int ntask = nd * np;
+  const DownCtx dc = down_ctx<BITS, SB>(a, rli, rls);
+  const int ntask = (U + 1) * dc.np;
+  const LaneOffsets lo = lane_offsets<BITS, SB>(a, dc, rli, rls, row_lo);
   DownTask<BITS> dt[kMaxDownPerWave];
   float hv[kMaxDownPerWave][1][kSegCodes];
   for (int base = 0; base < ntask; base += kWaves * kMaxDownPerWave) {
     // codes of this round's tasks, all requested before any compute
+    if (dc.np == 1) {
 #pragma unroll
-    for (int q = 0; q < kMaxDownPerWave; ++q)
-      load_down_task<BITS, SB>(dt[q], base + wave + q * kWaves, ntask, np, U, row_lo, a, s, rli, rls);
+      for (int q = 0; q < kMaxDownPerWave; ++q)
+        load_down_task_1<BITS, SB>(dt[q], base + wave + q * kWaves, ntask, dc, U, a, s, lo);
+    } else {
+#pragma unroll
+      for (int q = 0; q < kMaxDownPerWave; ++q)
+        load_down_task<BITS, SB>(dt[q], base + wave + q * kWaves, ntask, dc, U, row_lo, a, s, rli, rls);
+    }
     if (s.h && base == 0) {
       // all h rows into LDS once, while the codes above are in flight
       const float4* src = reinterpret_cast<const float4*>(a.h);
@@ -579,7 +677,6 @@ size_t lds_bytes_a(int T, int H, int E, int k, int umax, int act_sz) {
   take(static_cast<size_t>(T) * E * 4);
   take(static_cast<size_t>(T) * k * 4);
   take(static_cast<size_t>(T) * k * 4);
-  take(kWaves * 64 * 4);
   take(static_cast<size_t>(E) * 8);
   take(static_cast<size_t>(E) * 4);
   take(static_cast<size_t>(umax) * 4);

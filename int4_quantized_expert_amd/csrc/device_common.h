@@ -233,19 +233,22 @@ struct RowLanes {
   int seg0;     // this lane's first segment
 };
 
+// cols is a power of two >= 64 (the descriptor checks enforce it), so the
+// divisions reduce to shifts and masks.
 __device__ __forceinline__ RowLanes row_lanes(int cols, int lane) {
   RowLanes r;
-  r.spr = cols / kSegCodes;
+  const int sh = __builtin_ctz(static_cast<unsigned>(cols)) - 5;   // log2(cols / kSegCodes)
+  r.spr = 1 << sh;
   if (r.spr >= kWave) {
     r.rpp = 1;
     r.width = kWave;
     r.sub_row = 0;
     r.seg0 = lane;
   } else {
-    r.rpp = kWave / r.spr;
+    r.rpp = kWave >> sh;
     r.width = r.spr;
-    r.sub_row = lane / r.spr;
-    r.seg0 = lane % r.spr;
+    r.sub_row = lane >> sh;
+    r.seg0 = lane & (r.spr - 1);
   }
   return r;
 }

@@ -44,40 +44,49 @@ __device__ __forceinline__ void wave_sync_lds() {
 //  3. If more than kCandMax candidates qualify, k rounds of a wave arg-max
 //     finish the job.
 // Output: ids[0..k) and vals[0..k) = renormalised weights p_i, formed with the
-// same operations and order as the staged kernel.
-__device__ __forceinline__ void topk_wave(const float* lg, int E, int k, int lane, uint64_t* cand, float* ev,
-                                          int32_t* ids, float* vals) {
-  const int nj = (E + kWave - 1) / kWave;   // <= 16
-  uint32_t key[16];
+// same operations and order as the staged kernel.  lg, cand, ids and vals
+// must be in LDS.  NJ = logits per lane (E <= 64 NJ); the code is straight-
+// line over NJ so that every load and ballot is issued without waiting.
+template <int NJ>
+__device__ __forceinline__ void topk_wave_n(const float* lg_, int E, int k, int lane, uint64_t* cand_, int32_t* ids_,
+                                            float* vals_) {
+  const lds_f32* lg = (const lds_f32*)(lg_);
+  typedef __attribute__((address_space(3))) uint64_t lds_u64;
+  typedef __attribute__((address_space(3))) int32_t lds_i32;
+  lds_u64* cand = (lds_u64*)(cand_);
+  lds_i32* ids = (lds_i32*)(ids_);
+  lds_f32* vals = (lds_f32*)(vals_);
+  float raw[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + j * kWave;
+    raw[j] = lg[e < E ? e : 0];
+  }
+  uint32_t key[NJ];
   uint32_t lm = 0;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     const int e = lane + j * kWave;
-    uint32_t kv = 0u;
-    if (j < nj) {
-      kv = order_key(lg[e < E ? e : 0]);
-      kv = e < E ? (kv > 1u ? kv : 1u) : 0u;   // every real entry ranks above "no entry"
-    }
-    key[j] = kv;
-    lm = kv > lm ? kv : lm;
+    const uint32_t kv = order_key(raw[j]);
+    key[j] = e < E ? (kv > 1u ? kv : 1u) : 0u;   // every real entry ranks above "no entry"
+    lm = key[j] > lm ? key[j] : lm;
   }
   uint32_t theta = 0;
   for (int b = 31; b >= 16; --b) {
     const uint32_t c = theta | (1u << b);
     if (__popcll(__ballot(lm >= c)) >= static_cast<unsigned>(k)) theta = c;
   }
+  uint64_t m[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) m[j] = __ballot(key[j] != 0u && key[j] >= theta);
   int cnt = 0;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    if (j < nj) {
-      const bool in = key[j] != 0u && key[j] >= theta;
-      const uint64_t m = __ballot(in);
-      const int pos = cnt + __popcll(m & lane_mask_lt(lane));
-      const int id = lane + j * kWave;
-      const uint64_t w = (static_cast<uint64_t>(key[j]) << 32) | static_cast<uint32_t>(~id);
-      if (in && pos < kCandMax) cand[pos] = w;
-      cnt += __popcll(m);
-    }
+  for (int j = 0; j < NJ; ++j) {
+    const bool in = (m[j] >> lane) & 1ull;
+    const int pos = cnt + __popcll(m[j] & lane_mask_lt(lane));
+    const int id = lane + j * kWave;
+    if (in && pos < kCandMax) cand[pos] = (static_cast<uint64_t>(key[j]) << 32) | static_cast<uint32_t>(~id);
+    cnt += __popcll(m[j]);
   }
   if (cnt <= kCandMax) {
     wave_sync_lds();
@@ -86,7 +95,8 @@ __device__ __forceinline__ void topk_wave(const float* lg, int E, int k, int lan
     const uint64_t mine = cand[lane];
     int rank = 0;
     const int cnt8 = (cnt + 7) & ~7;
-    const u32x4* c4 = reinterpret_cast<const u32x4*>(cand);
+    typedef __attribute__((address_space(3))) u32x4 lds_v4;
+    const lds_v4* c4 = (const lds_v4*)(cand);
     for (int d0 = 0; d0 < cnt8; d0 += 8) {
       u32x4 q[4];
 #pragma unroll
@@ -111,14 +121,14 @@ __device__ __forceinline__ void topk_wave(const float* lg, int E, int k, int lan
       uint32_t bk = 0;
       int bid = 0x7fffffff;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         const int e = lane + j * kWave;
         if (!((taken >> j) & 1u) && e < E && (key[j] > bk || (key[j] == bk && e < bid))) { bk = key[j]; bid = e; }
       }
 #pragma unroll
-      for (int m = kWave / 2; m > 0; m >>= 1) {
-        const uint32_t ok = __shfl_xor(bk, m, kWave);
-        const int oid = __shfl_xor(bid, m, kWave);
+      for (int mm = kWave / 2; mm > 0; mm >>= 1) {
+        const uint32_t ok = __shfl_xor(bk, mm, kWave);
+        const int oid = __shfl_xor(bid, mm, kWave);
         if (ok > bk || (ok == bk && oid < bid)) { bk = ok; bid = oid; }
       }
       if ((bid & (kWave - 1)) == lane) taken |= 1u << (bid / kWave);
@@ -129,12 +139,17 @@ __device__ __forceinline__ void topk_wave(const float* lg, int E, int k, int lan
   // p_i = exp(l_i - l_0) / sum_j exp(l_j - l_0), the sum in rank order from 0
   const float top = vals[0];
   const float ex = lane < k ? expf(vals[lane] - top) : 0.f;
-  ev[lane] = ex;
-  wave_sync_lds();
   float sum = 0.f;
-  for (int i = 0; i < k; ++i) sum += ev[i];
-  wave_sync_lds();
+  for (int i = 0; i < k; ++i) sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), i));
   if (lane < k) vals[lane] = ex / sum;
+}
+
+__device__ __forceinline__ void topk_wave(const float* lg, int E, int k, int lane, uint64_t* cand, int32_t* ids,
+                                          float* vals) {
+  if (E <= 8 * kWave)
+    topk_wave_n<8>(lg, E, k, lane, cand, ids, vals);
+  else
+    topk_wave_n<16>(lg, E, k, lane, cand, ids, vals);
 }
 
 }  // namespace moe
