@@ -48,7 +48,6 @@ constexpr int kChunk = kPrefillChunk;   // pairs per tile (4 MFMA column blocks)
 constexpr int kGuRows = 128;            // gate/up rows (each) per block: 4 waves x 32
 constexpr int kDnRows = 256;            // down rows per block: 4 waves x 64
 constexpr int kSlice = 256;             // k staged in LDS per step
-constexpr int kRowBytes = kSlice * 2 + 16;   // one token's float16 slice + bank padding
 constexpr int kDispThreads = 1024;
 
 __device__ __forceinline__ uint32_t h2_bits(h2v v) { return __builtin_bit_cast(uint32_t, v); }
@@ -83,14 +82,25 @@ __device__ __forceinline__ u32x4 permute8(u32x4 v) {
   return o;
 }
 
+// (w & mask) | magic in one v_and_or_b32.  gfx9 VOP3 instructions read at
+// most one scalar or literal operand, so the compiler splits the expression
+// into two instructions when both constants are literals; here the mask is a
+// scalar and the magic number comes from a vector register.
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic_v) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(w), "s"(mask), "v"(magic_v));
+  return d;
+}
+
 // Dequantize 8 int4 codes (one word, low nibble first) into an A operand.
-__device__ __forceinline__ h8v dq_int4(uint32_t w, h2v s, h2v b) {
+// magic_v holds 0x64006400 (float16 1024 in both halves).
+__device__ __forceinline__ h8v dq_int4(uint32_t w, h2v s, h2v b, uint32_t magic_v) {
   const uint32_t hi = w >> 8;
   const h2v m1024 = {-1024.0f16, -1024.0f16}, r16 = {0.0625f16, 0.0625f16}, m64 = {-64.0f16, -64.0f16};
-  const h2v q0 = bits_h2((w & 0x000F000Fu) | 0x64006400u) + m1024;                          // (q0, q4)
-  const h2v q1 = __builtin_elementwise_fma(bits_h2((w & 0x00F000F0u) | 0x64006400u), r16, m64);   // (q1, q5)
-  const h2v q2 = bits_h2((hi & 0x000F000Fu) | 0x64006400u) + m1024;                         // (q2, q6)
-  const h2v q3 = __builtin_elementwise_fma(bits_h2((hi & 0x00F000F0u) | 0x64006400u), r16, m64);  // (q3, q7)
+  const h2v q0 = bits_h2(and_or(w, 0x000F000Fu, magic_v)) + m1024;                          // (q0, q4)
+  const h2v q1 = __builtin_elementwise_fma(bits_h2(and_or(w, 0x00F000F0u, magic_v)), r16, m64);   // (q1, q5)
+  const h2v q2 = bits_h2(and_or(hi, 0x000F000Fu, magic_v)) + m1024;                         // (q2, q6)
+  const h2v q3 = __builtin_elementwise_fma(bits_h2(and_or(hi, 0x00F000F0u, magic_v)), r16, m64);  // (q3, q7)
   u32x4 o;
   o[0] = h2_bits(__builtin_elementwise_fma(q0, s, b));
   o[1] = h2_bits(__builtin_elementwise_fma(q1, s, b));
@@ -100,24 +110,18 @@ __device__ __forceinline__ h8v dq_int4(uint32_t w, h2v s, h2v b) {
 }
 
 // Dequantize 8 int8 codes (two words, low byte first) into an A operand.
-__device__ __forceinline__ h8v dq_int8(uint32_t w0, uint32_t w1, h2v s, h2v b) {
+__device__ __forceinline__ h8v dq_int8(uint32_t w0, uint32_t w1, h2v s, h2v b, uint32_t magic_v) {
   const h2v m1024 = {-1024.0f16, -1024.0f16};
-  const h2v q0 = bits_h2((w0 & 0x00FF00FFu) | 0x64006400u) + m1024;          // (q0, q2)
-  const h2v q1 = bits_h2(((w0 >> 8) & 0x00FF00FFu) | 0x64006400u) + m1024;   // (q1, q3)
-  const h2v q2 = bits_h2((w1 & 0x00FF00FFu) | 0x64006400u) + m1024;          // (q4, q6)
-  const h2v q3 = bits_h2(((w1 >> 8) & 0x00FF00FFu) | 0x64006400u) + m1024;   // (q5, q7)
+  const h2v q0 = bits_h2(and_or(w0, 0x00FF00FFu, magic_v)) + m1024;          // (q0, q2)
+  const h2v q1 = bits_h2(and_or(w0 >> 8, 0x00FF00FFu, magic_v)) + m1024;     // (q1, q3)
+  const h2v q2 = bits_h2(and_or(w1, 0x00FF00FFu, magic_v)) + m1024;          // (q4, q6)
+  const h2v q3 = bits_h2(and_or(w1 >> 8, 0x00FF00FFu, magic_v)) + m1024;     // (q5, q7)
   u32x4 o;
   o[0] = h2_bits(__builtin_elementwise_fma(q0, s, b));
   o[1] = h2_bits(__builtin_elementwise_fma(q1, s, b));
   o[2] = h2_bits(__builtin_elementwise_fma(q2, s, b));
   o[3] = h2_bits(__builtin_elementwise_fma(q3, s, b));
   return __builtin_bit_cast(h8v, o);
-}
-
-template <int SB>
-__device__ __forceinline__ h2v load_h2(const uint8_t* base, size_t idx) {
-  const _Float16 v = static_cast<_Float16>(load_scalar<SB>(base, idx));
-  return h2v{v, v};
 }
 
 __device__ __forceinline__ f4v mfma16(h8v a, h8v b, f4v c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
@@ -355,6 +359,26 @@ struct Tile {
   bool ok;
 };
 
+// The hardware hands consecutive blocks of a grid to the 8 XCDs in turn, and
+// each XCD has its own L2.  Blocks are renumbered so that XCD x runs a
+// contiguous range of (tile, row block) pairs in order: the row blocks of one
+// tile then run on one XCD at about the same time and read the tile's
+// activations through the same L2.  The grid is a multiple of kXcds blocks
+// with at least meta[0] * n_rt of them; the spare ones return at once.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ bool block_map(const PfArgs& a, int* ti, int* rb) {
+  const int nb = a.meta[0] * a.n_rt;
+  const int per = (nb + kXcds - 1) / kXcds;
+  const int idx = blockIdx.x / kXcds;
+  if (idx >= per) return false;
+  const int logical = (blockIdx.x % kXcds) * per + idx;
+  if (logical >= nb) return false;
+  *ti = logical / a.n_rt;
+  *rb = logical % a.n_rt;
+  return true;
+}
+
 // Uniform per block: which expert and which pairs this tile covers.
 template <int BITS, int SB>
 __device__ __forceinline__ bool tile_of(const PfArgs& a, int ti, Tile* tl) {
@@ -389,14 +413,183 @@ __device__ __forceinline__ void tile_pairs(const PfArgs& a, const Tile& tl, int 
   }
 }
 
+// Weights are read through a buffer descriptor over the tile's blob: each load
+// takes this lane's byte offset (its row, its k quarter) and a wave-uniform
+// offset (matrix plane, 16-row block, k step) in a scalar register, so the
+// per-block addressing costs no vector registers.  Offsets past the blob read
+// zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t blob_rsrc(const uint8_t* blob, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blob), 0,
+                                           static_cast<int>(bytes < 0x7fffffff ? bytes : 0x7fffffff), 0x00020000);
+}
+
+constexpr int kNonTemporal = 2;   // buffer-load cache policy: streamed once
+
+// This lane's weights of one 128-k step for one 16-row MFMA block: its 32
+// codes (int4: one 16-byte word, int8: two) and a scale and a bias word.  A
+// 128-k step spans two 64-groups; lane quarter q uses group q / 2.  float32
+// scales: the word is that group's value.  bf16 scales: the word holds both
+// groups (low half first) and the lane picks its half with v_perm when it
+// converts (sb_value); the four lanes of a row then load one shared word.
+template <int BITS>
+struct StepW {
+  u32x4 c[BITS / 4];
+  uint32_t s, b;
+};
+
+// Where one 16-row block's planes start (wave-uniform byte offsets in the
+// blob) and where this lane's row starts inside them.
+struct BlockOffsets {
+  int code, scale, bias;   // uniform
+};
+struct LaneOffsets {
+  int code, sb;            // per lane: row and k quarter (row only for bf16 scales)
+  uint32_t sel;            // bf16 scales: v_perm selector of this lane's group half
+};
+
+template <int BITS, int SB>
+__device__ __forceinline__ LaneOffsets lane_offsets(int lrow, int rbytes, int sbrow, int q) {
+  LaneOffsets lo;
+  lo.code = lrow * rbytes + 32 * q * BITS / 8;
+  lo.sb = lrow * sbrow + (SB == kF32 ? (q >> 1) * 4 : 0);
+  lo.sel = (q >> 1) ? 0x03020c0cu : 0x01000c0cu;   // bf16 bits -> top half of a float32, low half zero
+  return lo;
+}
+
+// Float value of a scale or bias word for this lane.
+template <int SB>
+__device__ __forceinline__ float sb_value(uint32_t word, uint32_t sel) {
+  if constexpr (SB == kF32) return __uint_as_float(word);
+  else return __uint_as_float(__builtin_amdgcn_perm(0u, word, sel));
+}
+
+template <int BITS, int SB>
+__device__ __forceinline__ void load_step(StepW<BITS>& w, __amdgpu_buffer_rsrc_t rs, LaneOffsets lo, BlockOffsets bo,
+                                          int kb) {
+  constexpr int sbsz = SB == kF32 ? 4 : 2;
+#pragma unroll
+  for (int i = 0; i < BITS / 4; ++i)
+    w.c[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo.code,
+                                                                             bo.code + kb * BITS / 8 + 16 * i,
+                                                                             kNonTemporal));
+  w.s = __builtin_amdgcn_raw_buffer_load_b32(rs, lo.sb, bo.scale + (kb / 64) * sbsz, 0);
+  w.b = __builtin_amdgcn_raw_buffer_load_b32(rs, lo.sb, bo.bias + (kb / 64) * sbsz, 0);
+}
+
+// Both 128-k steps of a 256-k slice (int4): the codes are one 128-byte line
+// per row, and bf16 scales of the slice's four groups are one 8-byte word.
+template <int SB>
+__device__ __forceinline__ void load_slice4(StepW<4>& w0, StepW<4>& w1, __amdgpu_buffer_rsrc_t rs, LaneOffsets lo,
+                                            BlockOffsets bo, int kb) {
+  w0.c[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo.code, bo.code + kb / 2, kNonTemporal));
+  w1.c[0] = __builtin_bit_cast(u32x4,
+                               __builtin_amdgcn_raw_buffer_load_b128(rs, lo.code, bo.code + kb / 2 + 64, kNonTemporal));
+  if constexpr (SB == kF32) {
+    w0.s = __builtin_amdgcn_raw_buffer_load_b32(rs, lo.sb, bo.scale + (kb / 64) * 4, 0);
+    w1.s = __builtin_amdgcn_raw_buffer_load_b32(rs, lo.sb, bo.scale + (kb / 64 + 2) * 4, 0);
+    w0.b = __builtin_amdgcn_raw_buffer_load_b32(rs, lo.sb, bo.bias + (kb / 64) * 4, 0);
+    w1.b = __builtin_amdgcn_raw_buffer_load_b32(rs, lo.sb, bo.bias + (kb / 64 + 2) * 4, 0);
+  } else {
+    const auto sv = __builtin_amdgcn_raw_buffer_load_b64(rs, lo.sb, bo.scale + (kb / 64) * 2, 0);
+    const auto bv = __builtin_amdgcn_raw_buffer_load_b64(rs, lo.sb, bo.bias + (kb / 64) * 2, 0);
+    w0.s = sv[0];
+    w1.s = sv[1];
+    w0.b = bv[0];
+    w1.b = bv[1];
+  }
+}
+
+__device__ __forceinline__ h2v splat_h2(float v) {
+  const _Float16 h = static_cast<_Float16>(v);
+  return h2v{h, h};
+}
+
+// A operand of MFMA k-step j.
+template <int BITS>
+__device__ __forceinline__ h8v step_operand(const StepW<BITS>& w, int j, h2v s, h2v b, uint32_t magic_v) {
+  if constexpr (BITS == 4) {
+    return dq_int4(w.c[0][j], s, b, magic_v);
+  } else {
+    const u32x4& cw = w.c[j >> 1];
+    return dq_int8(cw[(2 * j) & 3], cw[(2 * j + 1) & 3], s, b, magic_v);
+  }
+}
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+// Calls f(IntC<nt>) for the tile's number of 16-column MFMA blocks, so that
+// every loop over column blocks has a compile-time trip count.
+template <typename F>
+__device__ __forceinline__ void with_nt(int nt, F&& f) {
+  switch (nt) {
+    case 1: f(IntC<1>{}); break;
+    case 2: f(IntC<2>{}); break;
+    case 3: f(IntC<3>{}); break;
+    default: f(IntC<4>{}); break;
+  }
+}
+
+// Activation staging shared by both expert kernels.  One staged 256-k slice is
+// chunk-major in LDS: [32 chunks in MFMA k order][64 columns][16 bytes], so the
+// B operand of one MFMA (16 columns, one chunk per lane quarter) is four runs
+// of 256 contiguous bytes.  The rows are copied global -> LDS by the gfx950
+// direct loads (global_load_lds_dwordx4: lane l's 16 bytes land at the
+// wave-uniform LDS address + 16 l), so they never pass through registers.
+// Lane l copies column (pair) l, wave w chunks 8 w .. 8 w + 7.  Lanes past
+// the tile's pairs copy column 0 again: MFMA columns are independent, and
+// those columns are never written out.
+constexpr int kChunkBytes = kChunk * 16;              // one chunk of all 64 columns
+constexpr int kStageBytes = (kSlice / 8) * kChunkBytes;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// src: this lane's column at the wave's first chunk of slice 0 (bytes).
+__device__ __forceinline__ void stage_slice(const uint8_t* src, int ks, uint8_t* stage, int w) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_global_load_lds(src + ks * 2 + 16 * i, (lds_void*)(stage + (8 * w + i) * kChunkBytes), 16, 0, 0);
+}
+
+// The direct copies of a stage must have landed, for every wave, before any
+// wave reads it: wait for all of this wave's memory operations, then barrier.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+__device__ __forceinline__ h8v stage_b(const uint8_t* stage, int S, int j, int ct, int r, int q) {
+  return *reinterpret_cast<const h8v*>(stage + (16 * S + 4 * j + q) * kChunkBytes + (16 * ct + r) * 16);
+}
+
+// Natural k (0..7) that MFMA slot s of an 8-group stands for; see permute8.
+template <int BITS>
+__device__ __forceinline__ int slot_k(int s) {
+  if constexpr (BITS == 4) return (s >> 1) + 4 * (s & 1);
+  else return (s & 4) + ((s >> 1) & 1) + 2 * (s & 1);
+}
+
 // Gate/up: block = (tile, 128-row block); wave w owns rows 32 w .. +31 of gate
-// and of up (two 16-row MFMA blocks each) for up to 64 pairs (4 column blocks).
+// and of up (two 16-row MFMA blocks each) for the tile's pairs (up to 4 column
+// blocks).  h leaves in the down kernel's operand order: inside each 16-row
+// block, MFMA row 4 q + i computes natural row 8 (q / 2) + slot_k(4 (q % 2) +
+// i), so lane quarter q's four results are four consecutive slots of 8-group
+// 2 b + q / 2, stored at chunk position chunk_of of that group.
+// Software-pipelined over 256-k slices: while a slice is multiplied, the next
+// slice's weights (registers) and activations (direct copies into the other
+// LDS stage) are in flight; one barrier per slice.  Rows (I or SI) are
+// multiples of 256, so every wave of a block has rows.
 template <int BITS, int SB>
 __global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
-  __shared__ __align__(16) uint8_t xs[kChunk * kRowBytes];
+  __shared__ __align__(16) uint8_t xs0[kStageBytes];
+  __shared__ __align__(16) uint8_t xs1[kStageBytes];
   __shared__ int s_pair[kChunk], s_tok[kChunk];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  const int ti = blockIdx.x / a.n_rt, rb = blockIdx.x % a.n_rt;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  int ti, rb;
+  if (!block_map(a, &ti, &rb)) return;
   Tile tl;
   if (!tile_of<BITS, SB>(a, ti, &tl)) return;
   const int rows = tl.rows_or_k;
@@ -406,119 +599,166 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
     return;
   }
   tile_pairs(a, tl, tid, s_pair, s_tok);
-  const int n = tl.n, NT = (n + 15) / 16;
+  const int n = tl.n;
   const Planes P = planes_of(a.H, rows, BITS, SB);
+  const __amdgpu_buffer_rsrc_t rs = blob_rsrc(tl.blob, P.blob);
   const int r = lane & 15, q = lane >> 4;
-  const int row0 = rb * kGuRows + w * 32 + r;   // this lane's A row in MFMA block 0; block 1 is +16
-  const bool w_on = rb * kGuRows + w * 32 < rows;
-  const size_t rbytes = static_cast<size_t>(a.H) * BITS / 8;
-  const int ng = a.H / 64;
-  const uint8_t* code[2] = {tl.blob, tl.blob + P.q};
-  const uint8_t* scl[2] = {tl.blob + 3 * P.q, tl.blob + 3 * P.q + P.s};
-  const uint8_t* bia[2] = {tl.blob + 3 * P.q + 3 * P.s, tl.blob + 3 * P.q + 4 * P.s};
-  f4v acc[2][2][4];
+  const uint32_t magic_v = __builtin_amdgcn_readfirstlane(0x64006400);   // kept in a vector register by and_or
+  constexpr int sbsz = SB == kF32 ? 4 : 2;
+  const int rbytes = a.H * BITS / 8;
+  const int sbrow = (a.H / 64) * sbsz;
+  const int wrow = rb * kGuRows + w * 32;                       // first row of the wave (uniform)
+  const int lrow = 8 * (r >> 3) + slot_k<BITS>(r & 7);          // this lane's row inside a 16-row block
+  const LaneOffsets lo = lane_offsets<BITS, SB>(lrow, rbytes, sbrow, q);
+  BlockOffsets bo[2][2];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr)
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) acc[m][rr][ct] = f4v{0.f, 0.f, 0.f, 0.f};
-  __syncthreads();   // s_tok ready
-  const int st_c = tid >> 2, st_part = tid & 3;   // staging: token, quarter of the slice
-  for (int ks = 0; ks < a.H; ks += kSlice) {
-    // stage 64 tokens x 256 k of float16 x (already in MFMA order)
-    {
-      u32x4 v[8];
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      if (st_c < n) {
-        const u32x4* src = a.x16 + static_cast<size_t>(s_tok[st_c]) * (a.H / 8) + ks / 8 + st_part * 8;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = src[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = zero;
-      }
-      __syncthreads();   // the previous slice has been consumed
-      u32x4* dst = reinterpret_cast<u32x4*>(xs + st_c * kRowBytes) + st_part * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dst[i] = v[i];
-      __syncthreads();
+    for (int rr = 0; rr < 2; ++rr) {
+      const int row = wrow + 16 * rr;
+      bo[m][rr] = {static_cast<int>(m * P.q) + row * rbytes, static_cast<int>(3 * P.q + m * P.s) + row * sbrow,
+                   static_cast<int>(3 * P.q + (3 + m) * P.s) + row * sbrow};
     }
-    if (!w_on) continue;
+  __syncthreads();   // s_tok ready
+  const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(a.x16) +
+                        static_cast<size_t>(s_tok[lane < n ? lane : 0]) * a.H * 2 + w * 8 * 16;
+  auto load_w = [&](StepW<BITS> (&dst)[2][2], int kb) {
 #pragma unroll
-    for (int S = 0; S < 2; ++S) {
-      const int kb = ks + 128 * S;
-      const int g = kb / 64 + (q >> 1);
-      h8v B[4][4];
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+      for (int rr = 0; rr < 2; ++rr) load_step<BITS, SB>(dst[m][rr], rs, lo, bo[m][rr], kb);
+  };
+  auto load_w2 = [&](StepW<BITS> (&d0)[2][2], StepW<BITS> (&d1)[2][2], int kb) {
+    if constexpr (BITS == 4) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          B[ct][j] = ct < NT ? *reinterpret_cast<const h8v*>(xs + (16 * ct + r) * kRowBytes + (16 * S + 4 * j + q) * 16)
-                             : h8v{};
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
+        for (int rr = 0; rr < 2; ++rr) load_slice4<SB>(d0[m][rr], d1[m][rr], rs, lo, bo[m][rr], kb);
+    }
+  };
+  with_nt((n + 15) / 16, [&](auto ntc) {
+    constexpr int NT = decltype(ntc)::value;
+    f4v acc[2][2][NT];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) acc[m][rr][ct] = f4v{0.f, 0.f, 0.f, 0.f};
+    // One 128-k step S (0 or 1) of the slice staged in `stage`.
+    auto mult = [&](int S, const uint8_t* stage, const StepW<BITS> (&wv)[2][2]) {
+      h2v sc[2][2], bc[2][2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) {
-          const int row = row0 + 16 * rr;
-          const uint8_t* cp = code[m] + row * rbytes + static_cast<size_t>(kb + 32 * q) * BITS / 8;
-          const h2v s = load_h2<SB>(scl[m], static_cast<size_t>(row) * ng + g);
-          const h2v b = load_h2<SB>(bia[m], static_cast<size_t>(row) * ng + g);
-          u32x4 c0 = load16_stream(cp), c1 = c0;
-          if constexpr (BITS == 8) c1 = load16_stream(cp + 16);
+          sc[m][rr] = splat_h2(sb_value<SB>(wv[m][rr].s, lo.sel));
+          bc[m][rr] = splat_h2(sb_value<SB>(wv[m][rr].b, lo.sel));
+        }
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            h8v A;
-            if constexpr (BITS == 4) {
-              A = dq_int4(c0[j], s, b);
-            } else {
-              const u32x4& cw = j < 2 ? c0 : c1;
-              A = dq_int8(cw[(2 * j) & 3], cw[(2 * j + 1) & 3], s, b);
-            }
+      for (int j = 0; j < 4; ++j) {
+        h8v B[NT];
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
-              if (ct < NT) acc[m][rr][ct] = mfma16(A, B[ct][j], acc[m][rr][ct]);
+        for (int ct = 0; ct < NT; ++ct) B[ct] = stage_b(stage, S, j, ct, r, q);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int rr = 0; rr < 2; ++rr) {
+            const h8v A = step_operand<BITS>(wv[m][rr], j, sc[m][rr], bc[m][rr], magic_v);
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) acc[m][rr][ct] = mfma16(A, B[ct], acc[m][rr][ct]);
           }
+      }
+    };
+    if constexpr (BITS == 4) {
+      // int4: a 128-k step is half of each row's 128-byte line; both steps of
+      // the next slice are requested together so that lines are fetched whole.
+      // The two register sets alternate roles from slice to slice.
+      StepW<BITS> wa[2][2], wa2[2][2], wb[2][2], wb2[2][2];
+      const int nsl = a.H / kSlice;
+      auto slice = [&](int sl, const uint8_t* cur, uint8_t* nxt, const StepW<BITS> (&c1)[2][2],
+                       const StepW<BITS> (&c2)[2][2], StepW<BITS> (&n1)[2][2], StepW<BITS> (&n2)[2][2]) {
+        const bool more = sl + 1 < nsl;
+        if (more) {
+          stage_slice(xsrc, (sl + 1) * kSlice, nxt, w);
+          load_w2(n1, n2, (sl + 1) * kSlice);
+        }
+        mult(0, cur, c1);
+        mult(1, cur, c2);
+        stage_barrier();
+      };
+      stage_slice(xsrc, 0, xs0, w);
+      load_w2(wa, wa2, 0);
+      stage_barrier();
+      for (int sl = 0; sl < nsl; sl += 2) {
+        slice(sl, xs0, xs1, wa, wa2, wb, wb2);
+        if (sl + 1 < nsl) slice(sl + 1, xs1, xs0, wb, wb2, wa, wa2);
+      }
+    } else {
+      // int8: one 128-k step already covers whole lines; prefetch one step
+      // ahead, alternating two register sets.  The number of steps is even.
+      StepW<BITS> wa[2][2], wb[2][2];
+      const int nst = a.H / 128;
+      auto step = [&](int st, int S, const uint8_t* cur, uint8_t* nxt, const StepW<BITS> (&cw)[2][2],
+                      StepW<BITS> (&nw)[2][2]) {
+        if (S == 0 && st + 2 < nst) stage_slice(xsrc, (st + 2) * 128, nxt, w);
+        if (st + 1 < nst) load_w(nw, (st + 1) * 128);
+        mult(S, cur, cw);
+        if (S == 1) stage_barrier();
+      };
+      stage_slice(xsrc, 0, xs0, w);
+      load_w(wa, 0);
+      stage_barrier();
+      for (int st = 0; st < nst; st += 4) {
+        step(st, 0, xs0, xs1, wa, wb);
+        step(st + 1, 1, xs0, xs1, wb, wa);
+        if (st + 2 < nst) {
+          step(st + 2, 0, xs1, xs0, wa, wb);
+          step(st + 3, 1, xs1, xs0, wb, wa);
         }
       }
     }
-  }
-  if (!w_on) return;
-  // h = silu(gate) * up, float16, rows 4 q .. 4 q + 3 of each 16-row block
+    // h = silu(gate) * up, float16, four consecutive slots per lane
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const int c = 16 * ct + r;
-    if (ct < NT && c < n) {
-      _Float16* hr = a.h + static_cast<size_t>(s_pair[c]) * a.hs;
+    for (int ct = 0; ct < NT; ++ct) {
+      const int c = 16 * ct + r;
+      if (c < n) {
+        _Float16* hr = a.h + static_cast<size_t>(s_pair[c]) * a.hs;
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        const int rw = rb * kGuRows + w * 32 + 16 * rr + 4 * q;
-        uint32_t o[2];
+        for (int rr = 0; rr < 2; ++rr) {
+          const int g8 = (wrow + 16 * rr) / 8 + (q >> 1);
+          uint32_t o[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const _Float16 h0 = static_cast<_Float16>(silu(acc[0][rr][ct][2 * i]) * acc[1][rr][ct][2 * i]);
-          const _Float16 h1 = static_cast<_Float16>(silu(acc[0][rr][ct][2 * i + 1]) * acc[1][rr][ct][2 * i + 1]);
-          o[i] = h2_bits(h2v{h0, h1});
+          for (int i = 0; i < 2; ++i) {
+            const _Float16 h0 = static_cast<_Float16>(silu(acc[0][rr][ct][2 * i]) * acc[1][rr][ct][2 * i]);
+            const _Float16 h1 = static_cast<_Float16>(silu(acc[0][rr][ct][2 * i + 1]) * acc[1][rr][ct][2 * i + 1]);
+            o[i] = h2_bits(h2v{h0, h1});
+          }
+          *reinterpret_cast<uint2*>(hr + 8 * chunk_of(g8) + 4 * (q & 1)) = make_uint2(o[0], o[1]);
         }
-        *reinterpret_cast<uint2*>(hr + rw) = make_uint2(o[0], o[1]);
       }
     }
-  }
+  });
 }
 
 // Down: block = (tile, 256-row block of H); wave w owns rows 64 w .. +63 (four
-// 16-row MFMA blocks) for up to 64 pairs.  Writes fp32 partial rows; a tile of
-// an unusable blob writes zeros, so that expert contributes nothing.
+// 16-row MFMA blocks) for the tile's pairs.  h rows arrive in operand order
+// and are staged like x.  Writes fp32 partial rows; a tile of an unusable blob
+// writes zeros, so that expert contributes nothing.  Pipelined over 256-k
+// slices like the gate/up kernel.
 template <int BITS, int SB>
 __global__ __launch_bounds__(kThreads, 2) void k_pf_down(PfArgs a) {
-  __shared__ __align__(16) uint8_t hsm[kChunk * kRowBytes];
+  __shared__ __align__(16) uint8_t hs0[kStageBytes];
+  __shared__ __align__(16) uint8_t hs1[kStageBytes];
   __shared__ int s_pair[kChunk], s_tok[kChunk];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  const int ti = blockIdx.x / a.n_rt, rb = blockIdx.x % a.n_rt;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  int ti, rb;
+  if (!block_map(a, &ti, &rb)) return;
   Tile tl;
   if (!tile_of<BITS, SB>(a, ti, &tl)) return;
   const int K = tl.rows_or_k;
-  const int n = tl.n, NT = (n + 15) / 16;
+  const int n = tl.n;
   tile_pairs(a, tl, tid, s_pair, s_tok);
   __syncthreads();
   const int r = lane & 15, q = lane >> 4;
@@ -532,83 +772,114 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_down(PfArgs a) {
     return;
   }
   const Planes P = planes_of(a.H, K, BITS, SB);   // down is [H, K]
-  const uint8_t* code = tl.blob + 2 * P.q;
-  const uint8_t* scl = tl.blob + 3 * P.q + 2 * P.s;
-  const uint8_t* bia = tl.blob + 3 * P.q + 5 * P.s;
-  const size_t rbytes = static_cast<size_t>(K) * BITS / 8;
-  const int ng = K / 64;
-  const int row0 = rb * kDnRows + w * 64 + r;
-  f4v acc[4][4];
+  const __amdgpu_buffer_rsrc_t rs = blob_rsrc(tl.blob, P.blob);
+  const uint32_t magic_v = __builtin_amdgcn_readfirstlane(0x64006400);
+  constexpr int sbsz = SB == kF32 ? 4 : 2;
+  const int rbytes = K * BITS / 8;
+  const int sbrow = (K / 64) * sbsz;
+  const int wrow = rb * kDnRows + w * 64;
+  const LaneOffsets lo = lane_offsets<BITS, SB>(r, rbytes, sbrow, q);
+  BlockOffsets bo[4];
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr)
+  for (int rr = 0; rr < 4; ++rr) {
+    const int row = wrow + 16 * rr;
+    bo[rr] = {static_cast<int>(2 * P.q) + row * rbytes, static_cast<int>(3 * P.q + 2 * P.s) + row * sbrow,
+              static_cast<int>(3 * P.q + 5 * P.s) + row * sbrow};
+  }
+  const uint8_t* hsrc = reinterpret_cast<const uint8_t*>(a.h) +
+                        static_cast<size_t>(s_pair[lane < n ? lane : 0]) * a.hs * 2 + w * 8 * 16;
+  auto load_w = [&](StepW<BITS> (&dst)[4], int kb) {
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[rr][ct] = f4v{0.f, 0.f, 0.f, 0.f};
-  const int st_c = tid >> 2, st_part = tid & 3;
-  for (int ks = 0; ks < K; ks += kSlice) {
-    {
-      // stage 64 pairs x 256 k of h, permuting each 8 values into slot order
-      u32x4 v[8];
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      if (st_c < n) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(a.h + static_cast<size_t>(s_pair[st_c]) * a.hs + ks) + st_part * 8;
+    for (int rr = 0; rr < 4; ++rr) load_step<BITS, SB>(dst[rr], rs, lo, bo[rr], kb);
+  };
+  auto load_w2 = [&](StepW<BITS> (&d0)[4], StepW<BITS> (&d1)[4], int kb) {
+    if constexpr (BITS == 4) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = src[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = zero;
-      }
-      __syncthreads();
-      u32x4* dst = reinterpret_cast<u32x4*>(hsm + st_c * kRowBytes);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dst[chunk_of(st_part * 8 + i)] = permute8<BITS>(v[i]);
-      __syncthreads();
+      for (int rr = 0; rr < 4; ++rr) load_slice4<SB>(d0[rr], d1[rr], rs, lo, bo[rr], kb);
     }
+  };
+  with_nt((n + 15) / 16, [&](auto ntc) {
+    constexpr int NT = decltype(ntc)::value;
+    f4v acc[4][NT];
 #pragma unroll
-    for (int S = 0; S < 2; ++S) {
-      const int kb = ks + 128 * S;
-      const int g = kb / 64 + (q >> 1);
-      h8v B[4][4];
+    for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          B[ct][j] = ct < NT ? *reinterpret_cast<const h8v*>(hsm + (16 * ct + r) * kRowBytes + (16 * S + 4 * j + q) * 16)
-                             : h8v{};
+      for (int ct = 0; ct < NT; ++ct) acc[rr][ct] = f4v{0.f, 0.f, 0.f, 0.f};
+    auto mult = [&](int S, const uint8_t* stage, const StepW<BITS> (&wv)[4]) {
+      h2v sc[4], bc[4];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int row = row0 + 16 * rr;
-        const uint8_t* cp = code + row * rbytes + static_cast<size_t>(kb + 32 * q) * BITS / 8;
-        const h2v s = load_h2<SB>(scl, static_cast<size_t>(row) * ng + g);
-        const h2v b = load_h2<SB>(bia, static_cast<size_t>(row) * ng + g);
-        u32x4 c0 = load16_stream(cp), c1 = c0;
-        if constexpr (BITS == 8) c1 = load16_stream(cp + 16);
+        sc[rr] = splat_h2(sb_value<SB>(wv[rr].s, lo.sel));
+        bc[rr] = splat_h2(sb_value<SB>(wv[rr].b, lo.sel));
+      }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          h8v A;
-          if constexpr (BITS == 4) {
-            A = dq_int4(c0[j], s, b);
-          } else {
-            const u32x4& cw = j < 2 ? c0 : c1;
-            A = dq_int8(cw[(2 * j) & 3], cw[(2 * j + 1) & 3], s, b);
-          }
+      for (int j = 0; j < 4; ++j) {
+        h8v B[NT];
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
-            if (ct < NT) acc[rr][ct] = mfma16(A, B[ct][j], acc[rr][ct]);
+        for (int ct = 0; ct < NT; ++ct) B[ct] = stage_b(stage, S, j, ct, r, q);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const h8v A = step_operand<BITS>(wv[rr], j, sc[rr], bc[rr], magic_v);
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) acc[rr][ct] = mfma16(A, B[ct], acc[rr][ct]);
+        }
+      }
+    };
+    if constexpr (BITS == 4) {
+      StepW<BITS> wa[4], wa2[4], wb[4], wb2[4];
+      const int nsl = K / kSlice;
+      auto slice = [&](int sl, const uint8_t* cur, uint8_t* nxt, const StepW<BITS> (&c1)[4],
+                       const StepW<BITS> (&c2)[4], StepW<BITS> (&n1)[4], StepW<BITS> (&n2)[4]) {
+        const bool more = sl + 1 < nsl;
+        if (more) {
+          stage_slice(hsrc, (sl + 1) * kSlice, nxt, w);
+          load_w2(n1, n2, (sl + 1) * kSlice);
+        }
+        mult(0, cur, c1);
+        mult(1, cur, c2);
+        stage_barrier();
+      };
+      stage_slice(hsrc, 0, hs0, w);
+      load_w2(wa, wa2, 0);
+      stage_barrier();
+      for (int sl = 0; sl < nsl; sl += 2) {
+        slice(sl, hs0, hs1, wa, wa2, wb, wb2);
+        if (sl + 1 < nsl) slice(sl + 1, hs1, hs0, wb, wb2, wa, wa2);
+      }
+    } else {
+      StepW<BITS> wa[4], wb[4];
+      const int nst = K / 128;
+      auto step = [&](int st, int S, const uint8_t* cur, uint8_t* nxt, const StepW<BITS> (&cw)[4],
+                      StepW<BITS> (&nw)[4]) {
+        if (S == 0 && st + 2 < nst) stage_slice(hsrc, (st + 2) * 128, nxt, w);
+        if (st + 1 < nst) load_w(nw, (st + 1) * 128);
+        mult(S, cur, cw);
+        if (S == 1) stage_barrier();
+      };
+      stage_slice(hsrc, 0, hs0, w);
+      load_w(wa, 0);
+      stage_barrier();
+      for (int st = 0; st < nst; st += 4) {
+        step(st, 0, hs0, hs1, wa, wb);
+        step(st + 1, 1, hs0, hs1, wb, wa);
+        if (st + 2 < nst) {
+          step(st + 2, 0, hs1, hs0, wa, wb);
+          step(st + 3, 1, hs1, hs0, wb, wa);
         }
       }
     }
-  }
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const int c = 16 * ct + r;
-    if (ct < NT && c < n) {
-      float* pr = a.partial + static_cast<size_t>(s_pair[c]) * a.H + rb * kDnRows + w * 64 + 4 * q;
+    for (int ct = 0; ct < NT; ++ct) {
+      const int c = 16 * ct + r;
+      if (c < n) {
+        float* pr = a.partial + static_cast<size_t>(s_pair[c]) * a.H + wrow + 4 * q;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        *reinterpret_cast<float4*>(pr + 16 * rr) =
-            make_float4(acc[rr][ct][0], acc[rr][ct][1], acc[rr][ct][2], acc[rr][ct][3]);
+        for (int rr = 0; rr < 4; ++rr)
+          *reinterpret_cast<float4*>(pr + 16 * rr) =
+              make_float4(acc[rr][ct][0], acc[rr][ct][1], acc[rr][ct][2], acc[rr][ct][3]);
+      }
     }
-  }
+  });
 }
 
 }  // namespace
@@ -617,8 +888,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_down(PfArgs a) {
 // Launchers.
 
 bool prefill_supported(const moe_desc& d, int T) {
+  // weight offsets inside a blob are 32-bit buffer offsets
+  const int wide = d.inter > d.shared_inter ? d.inter : d.shared_inter;
+  const bool blob_fits = planes_of(d.hidden, wide, d.bits, d.sb_dtype).blob < (int64_t{1} << 31);
   return T >= kPrefillMinT && d.act_dtype == kBF16 && d.hidden % kSlice == 0 && d.inter % kSlice == 0 &&
-         d.shared_inter % kSlice == 0 && d.n_experts <= 1024;
+         d.shared_inter % kSlice == 0 && d.n_experts <= 1024 && blob_fits;
 }
 
 static int last_error() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP; }
@@ -635,16 +909,21 @@ int launch_prefill_router(const Call& c, int32_t* ids2, float* wts2) {
   return launch_topk(c, logits, ids, wts, ids2, wts2);
 }
 
+// Blocks for up to max_tiles tiles of n_rt row blocks, rounded up to a
+// multiple of the XCD count (see block_map).
+static unsigned xcd_grid(int max_tiles, int n_rt) {
+  const unsigned nb = static_cast<unsigned>(max_tiles) * n_rt;
+  return (nb + kXcds - 1) / kXcds * kXcds;
+}
+
 template <int BITS, int SB>
 static void launch_tiles(const PfArgs& base, const Call& c) {
   const moe_desc& d = c.d;
   PfArgs a = base;
   a.n_rt = (d.inter > d.shared_inter ? d.inter : d.shared_inter) / kGuRows;
-  launch_kernel(k_pf_gateup<BITS, SB>, dim3(static_cast<unsigned>(c.L.max_tiles) * a.n_rt), dim3(kThreads), 0,
-                c.stream, a);
+  launch_kernel(k_pf_gateup<BITS, SB>, dim3(xcd_grid(c.L.max_tiles, a.n_rt)), dim3(kThreads), 0, c.stream, a);
   a.n_rt = d.hidden / kDnRows;
-  launch_kernel(k_pf_down<BITS, SB>, dim3(static_cast<unsigned>(c.L.max_tiles) * a.n_rt), dim3(kThreads), 0,
-                c.stream, a);
+  launch_kernel(k_pf_down<BITS, SB>, dim3(xcd_grid(c.L.max_tiles, a.n_rt)), dim3(kThreads), 0, c.stream, a);
 }
 
 int launch_prefill_experts(const Call& c) {
