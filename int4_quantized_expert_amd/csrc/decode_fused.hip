@@ -50,6 +50,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxDownPerWave = 4;    // down tasks per wave per round in launch B
 constexpr int kRouterRowsPerWave = 2; // router row groups per wave in phase R
+constexpr int kRowCost = 2;           // phase-G cost of a row's loads, in per-token dots
 
 __device__ __forceinline__ void store_tagged(uint64_t* p, float v, uint32_t tag) {
   __hip_atomic_store(p, (static_cast<uint64_t>(tag) << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
@@ -69,6 +70,7 @@ struct LdsA {
   int32_t* umap;     // [E] expert -> distinct index
   int32_t* uniq;     // [umax]
   int32_t* pidx;     // [umax][T] rank i of the expert for token t, or -1
+  int32_t* ucost;    // [umax + 1] phase-G work before distinct expert u (T > 1)
   uint64_t* cand;    // [kWaves][kCandMax] packed candidates
   int32_t* misc;     // [0] U, [1] tag
 };
@@ -85,6 +87,7 @@ __device__ inline LdsA carve_a(uint8_t* base, const FusedArgs& a) {
   s.umap = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.E) * 4));
   s.uniq = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.umax) * 4));
   s.pidx = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.umax) * a.T * 4));
+  s.ucost = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.umax + 1) * 4));
   s.cand = reinterpret_cast<uint64_t*>(take(kWaves * kCandMax * 8));
   s.misc = reinterpret_cast<int32_t*>(take(16 * 4));
   return s;
@@ -100,6 +103,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform: lets the compiler use scalar math
   const int T = a.T, H = a.H, E = a.E, k = a.k;
+  // bf16 activations with int4 codes take the v_dot2 segment dot
+  constexpr bool kDot2 = ACT == kBF16 && BITS == 4;
   uint32_t spins = 0;
   bool timed_out = false;
 
@@ -212,19 +217,34 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
     if (task != s_task0) load_shared_row(task);
     const int rr = task * rlh.rpp + rlh.sub_row;
     const bool ok = rr < a.SI;
-    for (int t = 0; t < T; ++t) {
-      float v[1][kSegCodes];
-      load_act_seg<ACT>(s.x + t * xrow, rlh.seg0, v[0]);
-      const float xs = seg_sum(v[0]);
-      float qg[1], qu[1];
-      seg_qdot_nt<BITS, 1>(scg, v, qg);
-      seg_qdot_nt<BITS, 1>(scu, v, qu);
-      float accg = 0.f, accu = 0.f;
-      accg += seg_value(raw_value<SB>(ssg), raw_value<SB>(sbg), qg[0], xs);
-      accu += seg_value(raw_value<SB>(ssu), raw_value<SB>(sbu), qu[0], xs);
-      const float g = group_sum(accg, rlh.width);
-      const float u = group_sum(accu, rlh.width);
-      if (ok && (lane % rlh.width) == 0) a.h[(static_cast<size_t>(T) * k + t) * a.hs + rr] = silu(g) * u;
+    if constexpr (kDot2) {
+      const QPairs pg = qpairs_bf16(scg), pu = qpairs_bf16(scu);
+      for (int t = 0; t < T; ++t) {
+        ActRaw<kBF16> xr;
+        load_lds_act_bf16(s.x + t * xrow, rlh.seg0, xr);
+        const float xs = xsum_bf16(xr);
+        float accg = 0.f, accu = 0.f;
+        accg += seg_value_d2(raw_value<SB>(ssg), raw_value<SB>(sbg), dot2_seg(pg, xr), xs);
+        accu += seg_value_d2(raw_value<SB>(ssu), raw_value<SB>(sbu), dot2_seg(pu, xr), xs);
+        const float g = group_sum(accg, rlh.width);
+        const float u = group_sum(accu, rlh.width);
+        if (ok && (lane % rlh.width) == 0) a.h[(static_cast<size_t>(T) * k + t) * a.hs + rr] = silu(g) * u;
+      }
+    } else {
+      for (int t = 0; t < T; ++t) {
+        float v[1][kSegCodes];
+        load_act_seg<ACT>(s.x + t * xrow, rlh.seg0, v[0]);
+        const float xs = seg_sum(v[0]);
+        float qg[1], qu[1];
+        seg_qdot_nt<BITS, 1>(scg, v, qg);
+        seg_qdot_nt<BITS, 1>(scu, v, qu);
+        float accg = 0.f, accu = 0.f;
+        accg += seg_value(raw_value<SB>(ssg), raw_value<SB>(sbg), qg[0], xs);
+        accu += seg_value(raw_value<SB>(ssu), raw_value<SB>(sbu), qu[0], xs);
+        const float g = group_sum(accg, rlh.width);
+        const float u = group_sum(accu, rlh.width);
+        if (ok && (lane % rlh.width) == 0) a.h[(static_cast<size_t>(T) * k + t) * a.hs + rr] = silu(g) * u;
+      }
     }
   }
   // sigmoid(g . x_t) on block 0 (lane covers segments L, L + 64, ... as in the staged path)
@@ -303,6 +323,29 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
     __syncthreads();
     for (int p = tid; p < T * k; p += kThreads) s.pidx[s.umap[s.ids[p]] * T + p / k] = p % k;
     __syncthreads();
+    // phase-G work per distinct expert: a row's loads plus one dot per token
+    // that uses it; prefix sums so that every wave takes an equal share
+    if (wave == 0) {
+      int carry = 0;
+      for (int u0 = 0; u0 < Ud; u0 += kWave) {
+        const int u = u0 + lane;
+        int c = 0;
+        if (u < Ud) {
+          c = kRowCost;
+          for (int t = 0; t < T; ++t) c += s.pidx[u * T + t] >= 0 ? 1 : 0;
+        }
+        int incl = c;
+#pragma unroll
+        for (int m = 1; m < kWave; m <<= 1) {
+          const int o = __shfl_up(incl, m, kWave);
+          if (lane >= m) incl += o;
+        }
+        if (u < Ud) s.ucost[u + 1] = carry + incl;
+        carry += __shfl(incl, kWave - 1, kWave);
+      }
+      if (lane == 0) s.ucost[0] = 0;
+    }
+    __syncthreads();
   }
   const int U = s.misc[0];
   if (blockIdx.x == 0) {
@@ -328,9 +371,45 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
     const int gpr = H / 64;
     const int groups_per_expert = a.I / rlh.rpp;
     const int total = U * groups_per_expert;
-    const int per_wave = (total + nwaves - 1) / nwaves;
-    const int g_lo = gwave * per_wave;
-    const int g_hi = min(total, g_lo + per_wave);
+    int g_lo, g_hi;
+    if (T == 1) {
+      // every unit costs the same
+      const int per_wave = (total + nwaves - 1) / nwaves;
+      g_lo = min(total, gwave * per_wave);
+      g_hi = min(total, g_lo + per_wave);
+    } else {
+      // equal shares of the work: unit (u, group) costs ucost[u + 1] - ucost[u]
+      // over groups_per_expert; a share starts at the first unit that starts
+      // at or after its cost position
+      const int64_t W = static_cast<int64_t>(s.ucost[U]) * groups_per_expert;
+      auto unit_at = [&](int64_t x) {
+        if (x >= W) return total;
+        int lo = 0, hi = U - 1;   // last u with ucost[u] * gpe <= x
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (static_cast<int64_t>(s.ucost[mid]) * groups_per_expert <= x) lo = mid;
+          else hi = mid - 1;
+        }
+        const int64_t c = s.ucost[lo + 1] - s.ucost[lo];   // cost of one unit of expert lo
+        const int64_t i = (x - static_cast<int64_t>(s.ucost[lo]) * groups_per_expert + c - 1) / c;
+        return lo * groups_per_expert + static_cast<int>(i);
+      };
+      g_lo = unit_at(W * gwave / nwaves);
+      g_hi = unit_at(W * (gwave + 1) / nwaves);
+    }
+    // per-token segment sums of x (the lane's segment is the same in every row)
+    float xsv[kFusedMaxT];
+    if constexpr (kDot2) {
+#pragma unroll
+      for (int t = 0; t < kFusedMaxT; ++t) {
+        xsv[t] = 0.f;
+        if (t < T) {
+          ActRaw<kBF16> xr;
+          load_lds_act_bf16(s.x + t * xrow, rlh.seg0, xr);
+          xsv[t] = xsum_bf16(xr);
+        }
+      }
+    }
     constexpr int kBatch = 4;
     for (int g0 = g_lo; g0 < g_hi; g0 += kBatch) {
       // every row of the batch is requested before any is used: no branches on
@@ -363,25 +442,49 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
         bg[b] = load_raw<SB>(blob + 3 * pl.q + 3 * pl.s, si);
         bu[b] = load_raw<SB>(blob + 3 * pl.q + 4 * pl.s, si);
       }
-      for (int t = 0; t < T; ++t) {
-        float v[1][kSegCodes];
-        load_act_seg<ACT>(s.x + t * xrow, rlh.seg0, v[0]);
-        const float xs = seg_sum(v[0]);
+      if constexpr (kDot2) {
+        // rows outer: each row's codes become bf16 pairs once for all its tokens
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
           if (uu[b] < 0) continue;
-          const int i = s.pidx[uu[b] * T + t];
-          if (i < 0) continue;                      // token t does not use this expert
-          float qg[1], qu[1];
-          seg_qdot_nt<BITS, 1>(cg[b], v, qg);
-          seg_qdot_nt<BITS, 1>(cu[b], v, qu);
-          float accg = 0.f, accu = 0.f;
-          accg += seg_value(raw_value<SB>(sg[b]), raw_value<SB>(bg[b]), qg[0], xs);
-          accu += seg_value(raw_value<SB>(su[b]), raw_value<SB>(bu[b]), qu[0], xs);
-          const float g = group_sum(accg, rlh.width);
-          const float u = group_sum(accu, rlh.width);
-          if ((lane % rlh.width) == 0)
-            a.h[(static_cast<size_t>(t) * k + i) * a.hs + rr[b]] = vv[b] ? silu(g) * u : 0.f;
+          const QPairs pg = qpairs_bf16(cg[b]), pu = qpairs_bf16(cu[b]);
+#pragma unroll
+          for (int t = 0; t < kFusedMaxT; ++t) {
+            if (t >= T) break;
+            const int i = s.pidx[uu[b] * T + t];
+            if (i < 0) continue;                    // token t does not use this expert
+            ActRaw<kBF16> xr;
+            load_lds_act_bf16(s.x + t * xrow, rlh.seg0, xr);
+            float accg = 0.f, accu = 0.f;
+            accg += seg_value_d2(raw_value<SB>(sg[b]), raw_value<SB>(bg[b]), dot2_seg(pg, xr), xsv[t]);
+            accu += seg_value_d2(raw_value<SB>(su[b]), raw_value<SB>(bu[b]), dot2_seg(pu, xr), xsv[t]);
+            const float g = group_sum(accg, rlh.width);
+            const float u = group_sum(accu, rlh.width);
+            if ((lane % rlh.width) == 0)
+              a.h[(static_cast<size_t>(t) * k + i) * a.hs + rr[b]] = vv[b] ? silu(g) * u : 0.f;
+          }
+        }
+      } else {
+        for (int t = 0; t < T; ++t) {
+          float v[1][kSegCodes];
+          load_act_seg<ACT>(s.x + t * xrow, rlh.seg0, v[0]);
+          const float xs = seg_sum(v[0]);
+#pragma unroll
+          for (int b = 0; b < kBatch; ++b) {
+            if (uu[b] < 0) continue;
+            const int i = s.pidx[uu[b] * T + t];
+            if (i < 0) continue;                      // token t does not use this expert
+            float qg[1], qu[1];
+            seg_qdot_nt<BITS, 1>(cg[b], v, qg);
+            seg_qdot_nt<BITS, 1>(cu[b], v, qu);
+            float accg = 0.f, accu = 0.f;
+            accg += seg_value(raw_value<SB>(sg[b]), raw_value<SB>(bg[b]), qg[0], xs);
+            accu += seg_value(raw_value<SB>(su[b]), raw_value<SB>(bu[b]), qu[0], xs);
+            const float g = group_sum(accg, rlh.width);
+            const float u = group_sum(accu, rlh.width);
+            if ((lane % rlh.width) == 0)
+              a.h[(static_cast<size_t>(t) * k + i) * a.hs + rr[b]] = vv[b] ? silu(g) * u : 0.f;
+          }
         }
       }
     }
@@ -390,26 +493,29 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Launch B: down projection of this block's output rows for every (token,
-// expert) pair and the shared expert, then the ordered combine.
+// Launch B: one block per (slice of rb output rows, token): the slice's down
+// rows of the token's k experts and of the shared expert, then the ordered
+// combine.  A block's partial sums are all its own, and the token's k + 1 h
+// rows (a few tens of KB) are staged in LDS once, so the work does not grow
+// per block with T.  Blocks are numbered so that the tokens of one slice run
+// on one XCD and share the slice's weight rows through its L2.
 // One task = `rpp` rows of one expert's Wd (lane: one segment of one row).
 template <int BITS>
 struct DownTask {
   Seg<BITS> code;
   uint32_t sc, bi;   // raw scale and bias bits (see load_raw)
-  int j;        // distinct-expert index (U = shared), -1 if none
+  int i;        // pair rank of the expert for the token (k = shared), -1 if none
   int rloc;     // this lane's row within the block, -1 if outside
   bool valid;   // blob offset usable
 };
 
 struct LdsB {
-  int64_t* uoff;     // [umax] blob offsets of the distinct experts
-  int32_t* pidx;     // [umax][T]
-  float* wts;        // [T][k]
-  float* sig;        // [T]
-  float* part;       // [(T k + T)][rb]
-  float* h;          // [(T k + T)][hs] staged activations, or nullptr when they do not fit
-  float* hsum;       // [(T k + T)][hs / 32] segment sums of the staged rows
+  int64_t* poff;     // [k] blob offsets of the token's experts, by rank
+  float* wts;        // [k] the token's combine weights
+  float* sig;        // [1] its shared-expert gate
+  float* part;       // [k + 1][rb]
+  float* h;          // [k + 1][hs / 32][kSegPad] staged activations, or nullptr when they do not fit
+  float* hsum;       // [k + 1][hs / 32] segment sums of the staged rows
 };
 
 // h rows are staged in LDS when they take at most this many bytes.  Each
@@ -417,25 +523,25 @@ struct LdsB {
 // read the 16 segments of one row hit different LDS banks.
 constexpr size_t kHStageMax = 56 * 1024;
 constexpr int kSegPad = kSegCodes + 4;
+constexpr int kXcds = 8;
 
-__host__ __device__ inline size_t h_stage_floats(int T, int k, int hs) {
-  return static_cast<size_t>(T) * (k + 1) * (hs / kSegCodes) * kSegPad;
+__host__ __device__ inline size_t h_stage_floats(int k, int hs) {
+  return static_cast<size_t>(k + 1) * (hs / kSegCodes) * kSegPad;
 }
 
-__host__ __device__ inline bool h_staged(int T, int k, int hs) { return h_stage_floats(T, k, hs) * 4 <= kHStageMax; }
+__host__ __device__ inline bool h_staged(int k, int hs) { return h_stage_floats(k, hs) * 4 <= kHStageMax; }
 
 __device__ inline LdsB carve_b(uint8_t* base, const FusedArgs& a) {
   LdsB s;
   size_t o = 0;
   auto take = [&](size_t n) { uint8_t* p = base + o; o += (n + 15) / 16 * 16; return p; };
-  s.uoff = reinterpret_cast<int64_t*>(take(static_cast<size_t>(a.umax) * 8));
-  s.pidx = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.umax) * a.T * 4));
-  s.wts = reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * a.k * 4));
-  s.sig = reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * 4));
-  s.part = reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * (a.k + 1) * a.rb * 4));
-  const bool st = h_staged(a.T, a.k, a.hs);
-  s.h = st ? reinterpret_cast<float*>(take(h_stage_floats(a.T, a.k, a.hs) * 4)) : nullptr;
-  s.hsum = st ? reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * (a.k + 1) * (a.hs / kSegCodes) * 4)) : nullptr;
+  s.poff = reinterpret_cast<int64_t*>(take(static_cast<size_t>(a.k) * 8));
+  s.wts = reinterpret_cast<float*>(take(static_cast<size_t>(a.k) * 4));
+  s.sig = reinterpret_cast<float*>(take(4));
+  s.part = reinterpret_cast<float*>(take(static_cast<size_t>(a.k + 1) * a.rb * 4));
+  const bool st = h_staged(a.k, a.hs);
+  s.h = st ? reinterpret_cast<float*>(take(h_stage_floats(a.k, a.hs) * 4)) : nullptr;
+  s.hsum = st ? reinterpret_cast<float*>(take(static_cast<size_t>(a.k + 1) * (a.hs / kSegCodes) * 4)) : nullptr;
   return s;
 }
 
@@ -474,18 +580,19 @@ __device__ __forceinline__ DownCtx down_ctx(const FusedArgs& a, const RowLanes& 
 // all are masked at use.  Without branches the compiler keeps every task's
 // loads of a wave in flight together instead of draining them in between.
 template <int BITS, int SB>
-__device__ __forceinline__ void load_down_task(DownTask<BITS>& d, int task, int ntask, const DownCtx& c, int U,
-                                               int row_lo, const FusedArgs& a, const LdsB& s, const RowLanes& rli,
+__device__ __forceinline__ void load_down_task(DownTask<BITS>& d, int task, int ntask, const DownCtx& c, int row_lo,
+                                               const FusedArgs& a, const LdsB& s, const RowLanes& rli,
                                                const RowLanes& rls) {
+  const int k = a.k;
   const bool live = task < ntask;
   const int tk = live ? task : 0;
-  const int j = c.np == 1 ? tk : tk / c.np;
-  const int p = c.np == 1 ? 0 : tk - j * c.np;
-  const bool is_sh = j == U;
+  const int i = c.np == 1 ? tk : tk / c.np;
+  const int p = c.np == 1 ? 0 : tk - i * c.np;
+  const bool is_sh = i == k;
   const int rpp = is_sh ? rls.rpp : rli.rpp;
   const int sub_row = is_sh ? rls.sub_row : rli.sub_row;
   const int seg0 = is_sh ? rls.seg0 : rli.seg0;
-  const int64_t off = s.uoff[is_sh ? 0 : j];
+  const int64_t off = s.poff[is_sh ? 0 : i];
   const bool valid = is_sh || slot_ok(off, c.blob_r, a.pool_bytes);
   const uint8_t* blob = is_sh ? a.shared : a.pool + (valid ? off : 0);
   const int64_t q = is_sh ? c.q_s : c.q_r;
@@ -498,7 +605,7 @@ __device__ __forceinline__ void load_down_task(DownTask<BITS>& d, int task, int 
   const int si = r * (is_sh ? c.gpr_s : c.gpr_r) + seg0 / 2;
   d.sc = load_raw<SB>(blob + 3 * q + 2 * sp, si);
   d.bi = load_raw<SB>(blob + 3 * q + 5 * sp, si);
-  d.j = live ? j : -1;
+  d.i = live ? i : -1;
   d.rloc = live && in ? rloc : -1;
   d.valid = valid;
 }
@@ -536,15 +643,16 @@ __device__ __forceinline__ uint32_t load_raw_at(const uint8_t* p) {
   else return *reinterpret_cast<const uint16_t*>(p);
 }
 
-// load_down_task for np == 1: the expert index is the task index, the blob
-// base is wave-uniform (scalar) and the lane offsets are precomputed.
+// load_down_task for np == 1: the pair rank is the task index, the blob base
+// is wave-uniform (scalar) and the lane offsets are precomputed.
 template <int BITS, int SB>
-__device__ __forceinline__ void load_down_task_1(DownTask<BITS>& d, int task, int ntask, const DownCtx& c, int U,
+__device__ __forceinline__ void load_down_task_1(DownTask<BITS>& d, int task, int ntask, const DownCtx& c,
                                                  const FusedArgs& a, const LdsB& s, const LaneOffsets& o) {
+  const int k = a.k;
   const bool live = task < ntask;
-  const int j = live ? task : U;            // a dead task re-reads the shared blob
-  const bool is_sh = j == U;
-  const int64_t off = is_sh ? 0 : s.uoff[j];
+  const int i = live ? task : k;            // a dead task re-reads the shared blob
+  const bool is_sh = i == k;
+  const int64_t off = is_sh ? 0 : s.poff[i];
   const bool valid = is_sh || slot_ok(off, c.blob_r, a.pool_bytes);
   const uint64_t bits = reinterpret_cast<uint64_t>(is_sh ? a.shared : a.pool + (valid ? off : 0));
   const uint8_t* blob = reinterpret_cast<const uint8_t*>(
@@ -553,7 +661,7 @@ __device__ __forceinline__ void load_down_task_1(DownTask<BITS>& d, int task, in
   d.code = load_codes<BITS>(blob + (is_sh ? o.code_s : o.code_r));
   d.sc = load_raw_at<SB>(blob + (is_sh ? o.sc_s : o.sc_r));
   d.bi = load_raw_at<SB>(blob + (is_sh ? o.bi_s : o.bi_r));
-  d.j = live ? j : -1;
+  d.i = live ? i : -1;
   d.rloc = live ? (is_sh ? o.rloc_s : o.rloc_r) : -1;
   d.valid = valid;
 }
@@ -571,30 +679,47 @@ __global__ __launch_bounds__(kThreads) void k_decode_b(FusedArgs a) {
   if (blockIdx.x == 0 && tid == 0)
     __hip_atomic_store(a.ctrl + 1, __hip_atomic_load(a.ctrl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u,
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // the routing record, all of it requested at once (bounded by umax, not by U)
-  const int U = *a.ucount;
+  // (slice, token) of this block: XCD x (blocks x, x + 8, ...) runs a
+  // contiguous range of them, token-minor
+  int slice, t;
   {
-    // one round trip per round: every array's element requested before any store
-    const int n = a.umax * T > T * k ? a.umax * T : T * k;
-    for (int i = tid; i < n; i += kThreads) {
-      const int64_t uo = a.uoff[i < a.umax ? i : 0];
-      const int32_t pi = a.pidx[i < a.umax * T ? i : 0];
-      const float wt = a.wts[i < T * k ? i : 0];
-      const float sg = a.sig[i < T ? i : 0];
-      if (i < a.umax) s.uoff[i] = uo;
-      if (i < a.umax * T) s.pidx[i] = pi;
-      if (i < T * k) s.wts[i] = wt;
-      if (i < T) s.sig[i] = sg;
+    const int nb = a.nslice * T;
+    const int per = (nb + kXcds - 1) / kXcds;
+    const int idx = blockIdx.x / kXcds;
+    if (idx >= per) return;
+    const int logical = (blockIdx.x % kXcds) * per + idx;
+    if (logical >= nb) return;
+    slice = logical / T;
+    t = logical - slice * T;
+  }
+  // the token's routing: blob offsets by rank, weights, gate; every element
+  // requested before any is stored (a rank that no distinct expert claims
+  // keeps offset -1, which slot_ok rejects)
+  if (tid < k) s.poff[tid] = -1;
+  __syncthreads();
+  {
+    const int U = *a.ucount;
+    for (int u0 = 0; u0 < a.umax || u0 < k; u0 += kThreads) {
+      const int u = u0 + tid;
+      const int32_t i = a.pidx[(u < a.umax ? u : 0) * T + t];
+      const int64_t off = a.uoff[u < a.umax ? u : 0];
+      const float wt = a.wts[t * k + (u < k ? u : 0)];
+      const float sg = a.sig[t];
+      if (u < a.umax && u < U && i >= 0 && i < k) s.poff[i] = off;
+      if (u < k) s.wts[u] = wt;
+      if (u == 0) s.sig[0] = sg;
     }
   }
   __syncthreads();
 
   const RowLanes rli = row_lanes(a.I, lane);
   const RowLanes rls = row_lanes(a.SI, lane);
-  const int row_lo = blockIdx.x * a.rb;
+  const int row_lo = slice * a.rb;
   const DownCtx dc = down_ctx<BITS, SB>(a, rli, rls);
-  const int ntask = (U + 1) * dc.np;
+  const int ntask = (k + 1) * dc.np;
+  const int nseg = a.hs / kSegCodes;
   const LaneOffsets lo = lane_offsets<BITS, SB>(a, dc, rli, rls, row_lo);
+  auto h_row = [&](int i) { return i < k ? static_cast<size_t>(t) * k + i : static_cast<size_t>(T) * k + t; };
   DownTask<BITS> dt[kMaxDownPerWave];
   float hv[kMaxDownPerWave][1][kSegCodes];
   for (int base = 0; base < ntask; base += kWaves * kMaxDownPerWave) {
@@ -602,66 +727,60 @@ __global__ __launch_bounds__(kThreads) void k_decode_b(FusedArgs a) {
     if (dc.np == 1) {
 #pragma unroll
       for (int q = 0; q < kMaxDownPerWave; ++q)
-        load_down_task_1<BITS, SB>(dt[q], base + wave + q * kWaves, ntask, dc, U, a, s, lo);
+        load_down_task_1<BITS, SB>(dt[q], base + wave + q * kWaves, ntask, dc, a, s, lo);
     } else {
 #pragma unroll
       for (int q = 0; q < kMaxDownPerWave; ++q)
-        load_down_task<BITS, SB>(dt[q], base + wave + q * kWaves, ntask, dc, U, row_lo, a, s, rli, rls);
+        load_down_task<BITS, SB>(dt[q], base + wave + q * kWaves, ntask, dc, row_lo, a, s, rli, rls);
     }
     if (s.h && base == 0) {
-      // all h rows into LDS once, while the codes above are in flight
-      const float4* src = reinterpret_cast<const float4*>(a.h);
+      // the token's k + 1 h rows into LDS once, while the codes above are in flight
+      const int r4 = a.hs / 4;                            // float4 per row
+      const int n4 = (k + 1) * r4;
       lds_u32x4* dst = (lds_u32x4*)(s.h);
-      const int n4 = T * (k + 1) * a.hs / 4;             // 8 float4 per segment
-      for (int i = tid; i < n4; i += kThreads) {
-        const float4 v = src[i];
-        dst[(i >> 3) * (kSegPad / 4) + (i & 7)] = u32x4{__float_as_uint(v.x), __float_as_uint(v.y),
+      for (int j = tid; j < n4; j += kThreads) {
+        const int i = j / r4;
+        const float4 v = reinterpret_cast<const float4*>(a.h + h_row(i) * a.hs)[j - i * r4];
+        dst[(j >> 3) * (kSegPad / 4) + (j & 7)] = u32x4{__float_as_uint(v.x), __float_as_uint(v.y),
                                                           __float_as_uint(v.z), __float_as_uint(v.w)};
       }
       __syncthreads();
       // segment sums once per block, in the order seg_sum uses
-      const int nseg = a.hs / kSegCodes;
-      for (int i = tid; i < T * (k + 1) * nseg; i += kThreads) {
+      for (int j = tid; j < (k + 1) * nseg; j += kThreads) {
         float v[kSegCodes];
-        load_lds_seg(s.h + static_cast<size_t>(i) * kSegPad, 0, v);
-        ((lds_f32*)(s.hsum))[i] = seg_sum(v);
+        load_lds_seg(s.h + static_cast<size_t>(j) * kSegPad, 0, v);
+        ((lds_f32*)(s.hsum))[j] = seg_sum(v);
       }
       __syncthreads();
     }
 #pragma unroll
     for (int q = 0; q < kMaxDownPerWave; ++q) {
-      if (dt[q].j < 0) continue;
-      const bool is_sh = dt[q].j == U;
-      const RowLanes& rl = is_sh ? rls : rli;
-      for (int t = 0; t < T; ++t) {
-        const int i = is_sh ? k : s.pidx[dt[q].j * T + t];
-        if (i < 0) continue;
-        const size_t pair = is_sh ? static_cast<size_t>(T) * k + t : static_cast<size_t>(t) * k + i;
-        float hs;
-        if (s.h) {
-          load_lds_seg(s.h + (pair * (a.hs / kSegCodes) + rl.seg0) * kSegPad, 0, hv[q][0]);
-          hs = ((const lds_f32*)(s.hsum))[pair * (a.hs / kSegCodes) + rl.seg0];
-        } else {
-          load_f32_seg(a.h + pair * a.hs, rl.seg0, hv[q][0]);
-          hs = seg_sum(hv[q][0]);
-        }
-        float qv[1];
-        seg_qdot_nt<BITS, 1>(dt[q].code, hv[q], qv);
-        float acc = 0.f;
-        acc += seg_value(raw_value<SB>(dt[q].sc), raw_value<SB>(dt[q].bi), qv[0], hs);
-        const float v = group_sum(acc, rl.width);
-        if ((lane % rl.width) == 0 && dt[q].rloc >= 0) s.part[pair * a.rb + dt[q].rloc] = dt[q].valid ? v : 0.f;
+      if (dt[q].i < 0) continue;
+      const int i = dt[q].i;
+      const RowLanes& rl = i == k ? rls : rli;
+      float hs;
+      if (s.h) {
+        load_lds_seg(s.h + (static_cast<size_t>(i) * nseg + rl.seg0) * kSegPad, 0, hv[q][0]);
+        hs = ((const lds_f32*)(s.hsum))[i * nseg + rl.seg0];
+      } else {
+        load_f32_seg(a.h + h_row(i) * a.hs, rl.seg0, hv[q][0]);
+        hs = seg_sum(hv[q][0]);
       }
+      float qv[1];
+      seg_qdot_nt<BITS, 1>(dt[q].code, hv[q], qv);
+      float acc = 0.f;
+      acc += seg_value(raw_value<SB>(dt[q].sc), raw_value<SB>(dt[q].bi), qv[0], hs);
+      const float v = group_sum(acc, rl.width);
+      if ((lane % rl.width) == 0 && dt[q].rloc >= 0) s.part[i * a.rb + dt[q].rloc] = dt[q].valid ? v : 0.f;
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < T * a.rb; idx += kThreads) {
-    const int t = idx / a.rb, rloc = idx % a.rb;
+  for (int rloc = tid; rloc < a.rb; rloc += kThreads) {
     const int n = row_lo + rloc;
     if (n >= a.H) continue;
     float acc = 0.f;
-    for (int i = 0; i < k; ++i) acc = fmaf(s.wts[t * k + i], s.part[(static_cast<size_t>(t) * k + i) * a.rb + rloc], acc);
-    acc = fmaf(s.sig[t], s.part[(static_cast<size_t>(T) * k + t) * a.rb + rloc], acc);
+    for (int i = 0; i < k; ++i) acc = fmaf(s.wts[i], s.part[i * a.rb + rloc], acc);
+    acc = fmaf(s.sig[0], s.part[k * a.rb + rloc], acc);
     if constexpr (OUT == kF32) {
       static_cast<float*>(a.out)[static_cast<size_t>(t) * a.H + n] = acc;
     } else {
@@ -681,22 +800,22 @@ size_t lds_bytes_a(int T, int H, int E, int k, int umax, int act_sz) {
   take(static_cast<size_t>(E) * 4);
   take(static_cast<size_t>(umax) * 4);
   take(static_cast<size_t>(umax) * T * 4);
+  take(static_cast<size_t>(umax + 1) * 4);
   take(kWaves * kCandMax * 8);
   take(16 * 4);
   return o;
 }
 
-size_t lds_bytes_b(int T, int k, int umax, int rb, int hs) {
+size_t lds_bytes_b(int k, int rb, int hs) {
   size_t o = 0;
   auto take = [&](size_t n) { o += (n + 15) / 16 * 16; };
-  take(static_cast<size_t>(umax) * 8);
-  take(static_cast<size_t>(umax) * T * 4);
-  take(static_cast<size_t>(T) * k * 4);
-  take(static_cast<size_t>(T) * 4);
-  take(static_cast<size_t>(T) * (k + 1) * rb * 4);
-  if (h_staged(T, k, hs)) {
-    take(h_stage_floats(T, k, hs) * 4);
-    take(static_cast<size_t>(T) * (k + 1) * (hs / kSegCodes) * 4);
+  take(static_cast<size_t>(k) * 8);
+  take(static_cast<size_t>(k) * 4);
+  take(4);
+  take(static_cast<size_t>(k + 1) * rb * 4);
+  if (h_staged(k, hs)) {
+    take(h_stage_floats(k, hs) * 4);
+    take(static_cast<size_t>(k + 1) * (hs / kSegCodes) * 4);
   }
   return o;
 }
@@ -762,11 +881,13 @@ int fused_plan(const moe_desc& d, int T, FusedPlan* plan) {
       plan->nb = nb;
       plan->lds = lds;
       plan->umax = umax;
-      // launch B: a few output rows per block, two blocks per CU
-      plan->nb_b = cus * 2;
-      plan->rb_b = (d.hidden + plan->nb_b - 1) / plan->nb_b;
-      plan->nb_b = (d.hidden + plan->rb_b - 1) / plan->rb_b;
-      plan->lds_b = lds_bytes_b(T, d.top_k, umax, plan->rb_b, d.inter > d.shared_inter ? d.inter : d.shared_inter);
+      // launch B: one block per (slice, token); slices of a few output rows,
+      // wider as T grows, so that the grid stays at two to four blocks per CU
+      const int rb1 = (d.hidden + cus * 2 - 1) / (cus * 2);
+      plan->rb_b = rb1 * ((T + 1) / 2);
+      plan->nslice = (d.hidden + plan->rb_b - 1) / plan->rb_b;
+      plan->nb_b = (plan->nslice * T + kXcds - 1) / kXcds * kXcds;
+      plan->lds_b = lds_bytes_b(d.top_k, plan->rb_b, d.inter > d.shared_inter ? d.inter : d.shared_inter);
       return MOE_OK;
     }
   }
@@ -804,6 +925,7 @@ int launch_decode_fused(const Call& c, const FusedPlan& plan) {
   a.hs = c.L.hstride;
   a.nb = plan.nb;
   a.rb = plan.rb_b;
+  a.nslice = plan.nslice;
   a.umax = plan.umax;
   a.act_sz = d.act_dtype == kF32 ? 4 : 2;
   a.spin_limit = 1u << 20;

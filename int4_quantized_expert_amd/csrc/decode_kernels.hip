@@ -296,6 +296,48 @@ __global__ __launch_bounds__(256) void k_gateup(GateUpArgs a) {
     n_tok = a.ustart[u + 1] - first;
   }
   const size_t act_sz = ACT == kF32 ? 4 : 2;
+  if constexpr (ACT == kBF16 && BITS == 4) {
+    // v_dot2 segment dots (same arithmetic as the two-launch decode kernel)
+    for (int c = 0; c < n_tok; ++c) {
+      int tok, hrow;
+      if (shared) {
+        tok = c;
+        hrow = a.T * a.k + c;
+      } else {
+        const int pair = a.plist[first + c];
+        tok = pair / a.k;
+        hrow = pair;
+      }
+      float accg[kMaxPass], accu[kMaxPass];
+#pragma unroll
+      for (int p = 0; p < kMaxPass; ++p) { accg[p] = 0.f; accu[p] = 0.f; }
+#pragma unroll
+      for (int n = 0; n < NSL; ++n) {
+        const int seg = rl.seg0 + n * kWave;
+        ActRaw<kBF16> xr;
+        load_act_raw<kBF16>(static_cast<const uint8_t*>(a.x) + static_cast<size_t>(tok) * a.H * act_sz, seg, xr);
+        const float xs = xsum_bf16(xr);
+#pragma unroll
+        for (int p = 0; p < kMaxPass; ++p) {
+          if (p < npass) {
+            accg[p] += seg_value_d2(sg[p][n], bg[p][n], dot2_seg(qpairs_bf16(cg[p][n]), xr), xs);
+            accu[p] += seg_value_d2(su[p][n], bu[p][n], dot2_seg(qpairs_bf16(cu[p][n]), xr), xs);
+          }
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < kMaxPass; ++p) {
+        if (p < npass) {
+          const int r = row0 + p * rl.rpp + rl.sub_row;
+          const float g = group_sum(accg[p], rl.width);
+          const float v = group_sum(accu[p], rl.width);
+          if (r < rows && (lane % rl.width) == 0)
+            a.h[static_cast<size_t>(hrow) * a.hstride + r] = valid ? silu(g) * v : 0.f;
+        }
+      }
+    }
+    return;
+  }
   for (int c0 = 0; c0 < n_tok; c0 += TOKC) {
     float xv[TOKC][kSegCodes];
     float xs[TOKC][NSL];

@@ -317,6 +317,80 @@ __device__ __forceinline__ void seg_qdot_nt(const Seg<BITS>& s_in, const float (
   for (int t = 0; t < NT; ++t) out[t] = a0[t] + a1[t];
 }
 
+// bf16 activations with int4 codes: the segment dot on v_dot2_f32_bf16.
+// Each code q becomes the bf16 value 128 + q (exact: 128 + q < 256 needs 8
+// significant bits), pairs (q_2j, q_2j+1) side by side as the raw activation
+// words hold (x_2j, x_2j+1).  One instruction then adds two products, both
+// exact in float32, and  D = sum (128 + q) x,  so  sum q x = D - 128 sum x.
+struct QPairs {
+  uint32_t p[16];
+};
+
+__device__ __forceinline__ QPairs qpairs_bf16(const Seg<4>& s_in) {
+  constexpr uint32_t kHi = 0x43434343u;   // 0x43 is the high byte of bf16 128.0
+  QPairs o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t w = s_in.w[0][k];
+    asm volatile("" : "+v"(w));           // keep the conversion where the caller uses it
+    const uint32_t lo = w & 0x0f0f0f0fu;          // bytes: q0 q2 q4 q6
+    const uint32_t hi = (w >> 4) & 0x0f0f0f0fu;   // bytes: q1 q3 q5 q7
+    const uint32_t t0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // q0 q1 q2 q3
+    const uint32_t t1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);   // q4 q5 q6 q7
+    o.p[4 * k + 0] = __builtin_amdgcn_perm(kHi, t0, 0x04010400u);     // (128 + q0, 128 + q1)
+    o.p[4 * k + 1] = __builtin_amdgcn_perm(kHi, t0, 0x04030402u);     // (128 + q2, 128 + q3)
+    o.p[4 * k + 2] = __builtin_amdgcn_perm(kHi, t1, 0x04010400u);
+    o.p[4 * k + 3] = __builtin_amdgcn_perm(kHi, t1, 0x04030402u);
+  }
+  return o;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// D = sum over the segment of (128 + q) x, two chains of eight.
+__device__ __forceinline__ float dot2_seg(const QPairs& q, const ActRaw<kBF16>& x) {
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a0 = dot2_bf16(q.p[4 * i + 0], x[i][0], a0);
+    a1 = dot2_bf16(q.p[4 * i + 1], x[i][1], a1);
+    a0 = dot2_bf16(q.p[4 * i + 2], x[i][2], a0);
+    a1 = dot2_bf16(q.p[4 * i + 3], x[i][3], a1);
+  }
+  return a0 + a1;
+}
+
+// sum x of a raw bf16 segment, on the same instruction (pairs times (1, 1)).
+__device__ __forceinline__ float xsum_bf16(const ActRaw<kBF16>& x) {
+  constexpr uint32_t kOnes = 0x3f803f80u;
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a0 = dot2_bf16(kOnes, x[i][0], a0);
+    a1 = dot2_bf16(kOnes, x[i][1], a1);
+    a0 = dot2_bf16(kOnes, x[i][2], a0);
+    a1 = dot2_bf16(kOnes, x[i][3], a1);
+  }
+  return a0 + a1;
+}
+
+// One segment's affine contribution s sum q x + b sum x from D and sum x.
+__device__ __forceinline__ float seg_value_d2(float s, float b, float d, float xs) {
+  return seg_value(s, b, d - 128.f * xs, xs);
+}
+
+// Raw bf16 segment of an activation row held in LDS.
+__device__ __forceinline__ void load_lds_act_bf16(const uint8_t* row, int seg, ActRaw<kBF16>& w) {
+  const lds_u32x4* p = reinterpret_cast<const lds_u32x4*>((const __attribute__((address_space(3))) uint8_t*)(row) +
+                                                          seg * kSegCodes * 2);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = p[i];
+}
+
 // Blob plane offsets (see include/moe_layer.h): Q bytes of codes and S bytes
 // of scales per matrix, all three matrices the same size.
 struct Planes {

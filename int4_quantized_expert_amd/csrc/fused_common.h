@@ -32,6 +32,7 @@ struct FusedArgs {
   int T, H, E, k, I, SI, hs;
   int nb;               // launch A blocks (all resident)
   int rb;               // launch B output rows per block
+  int nslice;           // launch B row slices (blocks: nslice * T)
   int umax;             // min(T k, E)
   int act_sz;
   uint32_t spin_limit;
@@ -43,6 +44,7 @@ struct FusedPlan {
   int umax;
   int nb_b;     // launch B grid
   int rb_b;     // launch B rows per block
+  int nslice;   // launch B row slices
   size_t lds_b; // launch B dynamic LDS
 };
 
