@@ -52,6 +52,11 @@ constexpr int kMaxDownPerWave = 4;    // down tasks per wave per round in launch
 constexpr int kRouterRowsPerWave = 2; // router row groups per wave in phase R
 constexpr int kRowCost = 2;           // phase-G cost of a row's loads, in per-token dots
 
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
 __device__ __forceinline__ void store_tagged(uint64_t* p, float v, uint32_t tag) {
   __hip_atomic_store(p, (static_cast<uint64_t>(tag) << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
@@ -59,6 +64,13 @@ __device__ __forceinline__ void store_tagged(uint64_t* p, float v, uint32_t tag)
 
 __device__ __forceinline__ uint64_t load_tagged(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The logits area also holds, after top-k, one float per (wave, token, lane)
+// for phase G.
+__host__ __device__ inline size_t lg_floats(int T, int E) {
+  const size_t lg = static_cast<size_t>(T) * E, xs = static_cast<size_t>(kWaves) * T * kWave;
+  return lg > xs ? lg : xs;
 }
 
 struct LdsA {
@@ -71,6 +83,7 @@ struct LdsA {
   int32_t* uniq;     // [umax]
   int32_t* pidx;     // [umax][T] rank i of the expert for token t, or -1
   int32_t* ucost;    // [umax + 1] phase-G work before distinct expert u (T > 1)
+  uint64_t* uranks;  // [umax] byte t: 1 + rank of expert u for token t, 0 if unused
   uint64_t* cand;    // [kWaves][kCandMax] packed candidates
   int32_t* misc;     // [0] U, [1] tag
 };
@@ -80,7 +93,7 @@ __device__ inline LdsA carve_a(uint8_t* base, const FusedArgs& a) {
   size_t o = 0;
   auto take = [&](size_t n) { uint8_t* p = base + o; o += (n + 15) / 16 * 16; return p; };
   s.x = take(static_cast<size_t>(a.T) * a.H * a.act_sz);
-  s.lg = reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * a.E * 4));
+  s.lg = reinterpret_cast<float*>(take(lg_floats(a.T, a.E) * 4));
   s.ids = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.T) * a.k * 4));
   s.vals = reinterpret_cast<float*>(take(static_cast<size_t>(a.T) * a.k * 4));
   s.slot = reinterpret_cast<int64_t*>(take(static_cast<size_t>(a.E) * 8));
@@ -88,6 +101,7 @@ __device__ inline LdsA carve_a(uint8_t* base, const FusedArgs& a) {
   s.uniq = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.umax) * 4));
   s.pidx = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.umax) * a.T * 4));
   s.ucost = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.umax + 1) * 4));
+  s.uranks = reinterpret_cast<uint64_t*>(take(static_cast<size_t>(a.umax) * 8));
   s.cand = reinterpret_cast<uint64_t*>(take(kWaves * kCandMax * 8));
   s.misc = reinterpret_cast<int32_t*>(take(16 * 4));
   return s;
@@ -226,8 +240,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
         float accg = 0.f, accu = 0.f;
         accg += seg_value_d2(raw_value<SB>(ssg), raw_value<SB>(sbg), dot2_seg(pg, xr), xs);
         accu += seg_value_d2(raw_value<SB>(ssu), raw_value<SB>(sbu), dot2_seg(pu, xr), xs);
-        const float g = group_sum(accg, rlh.width);
-        const float u = group_sum(accu, rlh.width);
+        float g, u;
+        gu_sums(accg, accu, rlh.width, g, u);
         if (ok && (lane % rlh.width) == 0) a.h[(static_cast<size_t>(T) * k + t) * a.hs + rr] = silu(g) * u;
       }
     } else {
@@ -241,8 +255,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
         float accg = 0.f, accu = 0.f;
         accg += seg_value(raw_value<SB>(ssg), raw_value<SB>(sbg), qg[0], xs);
         accu += seg_value(raw_value<SB>(ssu), raw_value<SB>(sbu), qu[0], xs);
-        const float g = group_sum(accg, rlh.width);
-        const float u = group_sum(accu, rlh.width);
+        float g, u;
+        gu_sums(accg, accu, rlh.width, g, u);
         if (ok && (lane % rlh.width) == 0) a.h[(static_cast<size_t>(T) * k + t) * a.hs + rr] = silu(g) * u;
       }
     }
@@ -292,6 +306,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
       if (lane < k) {
         s.uniq[r] = e;
         s.pidx[r] = lane;
+        s.uranks[r] = static_cast<uint64_t>(lane + 1);
       }
       if (lane == 0) s.misc[0] = k;
     }
@@ -332,7 +347,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
         int c = 0;
         if (u < Ud) {
           c = kRowCost;
-          for (int t = 0; t < T; ++t) c += s.pidx[u * T + t] >= 0 ? 1 : 0;
+          uint64_t rk = 0;
+          for (int t = 0; t < T; ++t) {
+            const int i = s.pidx[u * T + t];
+            c += i >= 0 ? 1 : 0;
+            rk |= static_cast<uint64_t>(i + 1) << (8 * t);
+          }
+          s.uranks[u] = rk;
         }
         int incl = c;
 #pragma unroll
@@ -397,28 +418,30 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
       g_lo = unit_at(W * gwave / nwaves);
       g_hi = unit_at(W * (gwave + 1) / nwaves);
     }
-    // per-token segment sums of x (the lane's segment is the same in every row)
-    float xsv[kFusedMaxT];
+    // per-token segment sums of x (the lane's segment is the same in every
+    // row), once per wave, in a wave-private table in the logits area, which
+    // nothing reads after top-k
+    lds_f32* const xs_tab = (lds_f32*)(s.lg) + wave * T * kWave;
     if constexpr (kDot2) {
-#pragma unroll
-      for (int t = 0; t < kFusedMaxT; ++t) {
-        xsv[t] = 0.f;
-        if (t < T) {
-          ActRaw<kBF16> xr;
-          load_lds_act_bf16(s.x + t * xrow, rlh.seg0, xr);
-          xsv[t] = xsum_bf16(xr);
-        }
+      for (int t = 0; t < T; ++t) {
+        ActRaw<kBF16> xr;
+        load_lds_act_bf16(s.x + t * xrow, rlh.seg0, xr);
+        xs_tab[t * kWave + lane] = xsum_bf16(xr);
       }
     }
+    // Rows go in batches of kBatch; the next batch's loads are requested
+    // before the current batch is computed (two register sets, alternating).
     constexpr int kBatch = 4;
-    for (int g0 = g_lo; g0 < g_hi; g0 += kBatch) {
-      // every row of the batch is requested before any is used: no branches on
-      // the loads (a row past the end repeats the first one, an unusable blob
-      // reads blob 0; both are masked at the store) and raw scale bits
+    struct Batch {
       Seg<BITS> cg[kBatch], cu[kBatch];
       uint32_t sg[kBatch], su[kBatch], bg[kBatch], bu[kBatch];
       int uu[kBatch], rr[kBatch];
       bool vv[kBatch];
+    };
+    // every row of a batch is requested before any is used: no branches on
+    // the loads (a row past the end repeats the first one, an unusable blob
+    // reads blob 0; both are masked at the store) and raw scale bits
+    auto load_batch = [&](Batch& B, int g0) {
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
         const int g = g0 + b;
@@ -428,40 +451,51 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
         const int r = (gc % groups_per_expert) * rlh.rpp + rlh.sub_row;
         const int64_t off = s.slot[s.uniq[u]];
         const bool valid = slot_ok(off, pl.blob, a.pool_bytes);
-        uu[b] = live ? u : -1;
-        rr[b] = r;
-        vv[b] = valid;
+        B.uu[b] = live ? u : -1;
+        B.rr[b] = r;
+        B.vv[b] = valid;
         if (live && !valid && lane == 0) raise_error(a.ctrl, kErrRange);
         const uint8_t* blob = a.pool + (valid ? off : 0);
         const int64_t qo = r * row_bytes + static_cast<int64_t>(rlh.seg0) * seg_bytes;
-        cg[b] = load_codes<BITS>(blob + qo);
-        cu[b] = load_codes<BITS>(blob + pl.q + qo);
+        B.cg[b] = load_codes<BITS>(blob + qo);
+        B.cu[b] = load_codes<BITS>(blob + pl.q + qo);
         const size_t si = static_cast<size_t>(r) * gpr + rlh.seg0 / 2;
-        sg[b] = load_raw<SB>(blob + 3 * pl.q, si);
-        su[b] = load_raw<SB>(blob + 3 * pl.q + pl.s, si);
-        bg[b] = load_raw<SB>(blob + 3 * pl.q + 3 * pl.s, si);
-        bu[b] = load_raw<SB>(blob + 3 * pl.q + 4 * pl.s, si);
+        B.sg[b] = load_raw<SB>(blob + 3 * pl.q, si);
+        B.su[b] = load_raw<SB>(blob + 3 * pl.q + pl.s, si);
+        B.bg[b] = load_raw<SB>(blob + 3 * pl.q + 3 * pl.s, si);
+        B.bu[b] = load_raw<SB>(blob + 3 * pl.q + 4 * pl.s, si);
       }
+    };
+    auto compute_batch = [&](const Batch& B, auto wtag) {
+      // row sums: width known at compile time for full-wave rows
+      constexpr int W = decltype(wtag)::value;
       if constexpr (kDot2) {
-        // rows outer: each row's codes become bf16 pairs once for all its tokens
+        // rows outer: each row's codes become bf16 pairs once for all its
+        // tokens; the tokens that use the row come from its packed ranks
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
-          if (uu[b] < 0) continue;
-          const QPairs pg = qpairs_bf16(cg[b]), pu = qpairs_bf16(cu[b]);
-#pragma unroll
-          for (int t = 0; t < kFusedMaxT; ++t) {
-            if (t >= T) break;
-            const int i = s.pidx[uu[b] * T + t];
-            if (i < 0) continue;                    // token t does not use this expert
+          if (B.uu[b] < 0) continue;
+          const uint64_t rkv = s.uranks[B.uu[b]];
+          uint64_t rk = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rkv >> 32))) << 32) |
+                        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rkv)));
+          const QPairs pg = qpairs_bf16(B.cg[b]), pu = qpairs_bf16(B.cu[b]);
+          const float sgv = raw_value<SB>(B.sg[b]), bgv = raw_value<SB>(B.bg[b]);
+          const float suv = raw_value<SB>(B.su[b]), buv = raw_value<SB>(B.bu[b]);
+          while (rk != 0) {
+            const int sh = __builtin_ctzll(rk) & ~7;
+            const int t = sh >> 3;
+            const int i = static_cast<int>((rk >> sh) & 0xffu) - 1;
+            rk &= ~(0xffull << sh);
             ActRaw<kBF16> xr;
             load_lds_act_bf16(s.x + t * xrow, rlh.seg0, xr);
+            const float xs = xs_tab[t * kWave + lane];
             float accg = 0.f, accu = 0.f;
-            accg += seg_value_d2(raw_value<SB>(sg[b]), raw_value<SB>(bg[b]), dot2_seg(pg, xr), xsv[t]);
-            accu += seg_value_d2(raw_value<SB>(su[b]), raw_value<SB>(bu[b]), dot2_seg(pu, xr), xsv[t]);
-            const float g = group_sum(accg, rlh.width);
-            const float u = group_sum(accu, rlh.width);
+            accg += seg_value_d2(sgv, bgv, dot2_seg(pg, xr), xs);
+            accu += seg_value_d2(suv, buv, dot2_seg(pu, xr), xs);
+            float g, u;
+            gu_sums_w<W>(accg, accu, rlh.width, g, u);
             if ((lane % rlh.width) == 0)
-              a.h[(static_cast<size_t>(t) * k + i) * a.hs + rr[b]] = vv[b] ? silu(g) * u : 0.f;
+              a.h[(static_cast<size_t>(t) * k + i) * a.hs + B.rr[b]] = B.vv[b] ? silu(g) * u : 0.f;
           }
         }
       } else {
@@ -471,22 +505,37 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
           const float xs = seg_sum(v[0]);
 #pragma unroll
           for (int b = 0; b < kBatch; ++b) {
-            if (uu[b] < 0) continue;
-            const int i = s.pidx[uu[b] * T + t];
+            if (B.uu[b] < 0) continue;
+            const int i = s.pidx[B.uu[b] * T + t];
             if (i < 0) continue;                      // token t does not use this expert
             float qg[1], qu[1];
-            seg_qdot_nt<BITS, 1>(cg[b], v, qg);
-            seg_qdot_nt<BITS, 1>(cu[b], v, qu);
+            seg_qdot_nt<BITS, 1>(B.cg[b], v, qg);
+            seg_qdot_nt<BITS, 1>(B.cu[b], v, qu);
             float accg = 0.f, accu = 0.f;
-            accg += seg_value(raw_value<SB>(sg[b]), raw_value<SB>(bg[b]), qg[0], xs);
-            accu += seg_value(raw_value<SB>(su[b]), raw_value<SB>(bu[b]), qu[0], xs);
-            const float g = group_sum(accg, rlh.width);
-            const float u = group_sum(accu, rlh.width);
+            accg += seg_value(raw_value<SB>(B.sg[b]), raw_value<SB>(B.bg[b]), qg[0], xs);
+            accu += seg_value(raw_value<SB>(B.su[b]), raw_value<SB>(B.bu[b]), qu[0], xs);
+            float g, u;
+            gu_sums_w<W>(accg, accu, rlh.width, g, u);
             if ((lane % rlh.width) == 0)
-              a.h[(static_cast<size_t>(t) * k + i) * a.hs + rr[b]] = vv[b] ? silu(g) * u : 0.f;
+              a.h[(static_cast<size_t>(t) * k + i) * a.hs + B.rr[b]] = B.vv[b] ? silu(g) * u : 0.f;
           }
         }
       }
+    };
+    auto run = [&](auto wtag) {
+      Batch b0, b1;
+      load_batch(b0, g_lo);
+      for (int g0 = g_lo; g0 < g_hi; g0 += 2 * kBatch) {
+        if (g0 + kBatch < g_hi) load_batch(b1, g0 + kBatch);
+        compute_batch(b0, wtag);
+        if (g0 + kBatch >= g_hi) break;
+        if (g0 + 2 * kBatch < g_hi) load_batch(b0, g0 + 2 * kBatch);
+        compute_batch(b1, wtag);
+      }
+    };
+    if (g_lo < g_hi) {
+      if (rlh.width == kWave) run(IntC<kWave>{});
+      else run(IntC<0>{});
     }
   }
   if (timed_out && lane == 0) raise_error(a.ctrl, kErrTimeout);
@@ -793,7 +842,7 @@ size_t lds_bytes_a(int T, int H, int E, int k, int umax, int act_sz) {
   size_t o = 0;
   auto take = [&](size_t n) { o += (n + 15) / 16 * 16; };
   take(static_cast<size_t>(T) * H * act_sz);
-  take(static_cast<size_t>(T) * E * 4);
+  take(lg_floats(T, E) * 4);
   take(static_cast<size_t>(T) * k * 4);
   take(static_cast<size_t>(T) * k * 4);
   take(static_cast<size_t>(E) * 8);
@@ -801,6 +850,7 @@ size_t lds_bytes_a(int T, int H, int E, int k, int umax, int act_sz) {
   take(static_cast<size_t>(umax) * 4);
   take(static_cast<size_t>(umax) * T * 4);
   take(static_cast<size_t>(umax + 1) * 4);
+  take(static_cast<size_t>(umax) * 8);
   take(kWaves * kCandMax * 8);
   take(16 * 4);
   return o;

@@ -329,8 +329,8 @@ __global__ __launch_bounds__(256) void k_gateup(GateUpArgs a) {
       for (int p = 0; p < kMaxPass; ++p) {
         if (p < npass) {
           const int r = row0 + p * rl.rpp + rl.sub_row;
-          const float g = group_sum(accg[p], rl.width);
-          const float v = group_sum(accu[p], rl.width);
+          float g, v;
+          gu_sums(accg[p], accu[p], rl.width, g, v);
           if (r < rows && (lane % rl.width) == 0)
             a.h[static_cast<size_t>(hrow) * a.hstride + r] = valid ? silu(g) * v : 0.f;
         }
@@ -385,8 +385,8 @@ __global__ __launch_bounds__(256) void k_gateup(GateUpArgs a) {
         const int r = row0 + p * rl.rpp + rl.sub_row;
 #pragma unroll
         for (int t = 0; t < TOKC; ++t) {
-          const float g = group_sum(accg[p][t], rl.width);
-          const float v = group_sum(accu[p][t], rl.width);
+          float g, v;
+          gu_sums(accg[p][t], accu[p][t], rl.width, g, v);
           if (c0 + t < n_tok && r < rows && (lane % rl.width) == 0) {
             a.h[static_cast<size_t>(hrow[t]) * a.hstride + r] = valid ? silu(g) * v : 0.f;
           }

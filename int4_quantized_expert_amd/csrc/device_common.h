@@ -187,22 +187,77 @@ __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
+// v + v of lane l ^ D for D = 16 or 32, on gfx950's v_permlane16/32_swap: with
+// both operands holding v, the swap leaves the two addends of every lane in
+// the two results (no LDS round trip, unlike a bpermute).
+template <int D>
+__device__ __forceinline__ float swap_sum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if constexpr (D == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+}
+
 // Sum over aligned groups of `width` lanes (power of two <= 64).  Each step
 // adds the value of a partner lane that adds ours back (mirror within 16,
 // mirror within 8, reversal within 4, swap of neighbours; then xor 16, 32),
 // so every lane of a group ends with the bitwise same total.  The first four
-// steps are DPP moves, which cost a few cycles instead of an LDS round trip.
+// steps are DPP moves and the last two lane swaps, so no step takes an LDS
+// round trip.
 __device__ __forceinline__ float group_sum(float v, int width) {
   if (width >= 16) v += dpp_f32<0x140>(v);   // row_mirror
   if (width >= 8) v += dpp_f32<0x141>(v);    // row_half_mirror
   if (width >= 4) v += dpp_f32<0x1B>(v);     // quad_perm [3, 2, 1, 0]
   if (width >= 2) v += dpp_f32<0xB1>(v);     // quad_perm [1, 0, 3, 2]
-  if (width >= 32) v += __shfl_xor(v, 16, kWave);
-  if (width >= 64) v += __shfl_xor(v, 32, kWave);
+  if (width >= 32) v = swap_sum<16>(v);
+  if (width >= 64) v = swap_sum<32>(v);
   return v;
 }
 
-__device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
+// group_sum for a width known at compile time: the same steps in the same
+// order, without the run-time tests.
+template <int W>
+__device__ __forceinline__ float group_sum_w(float v) {
+  if constexpr (W >= 16) v += dpp_f32<0x140>(v);
+  if constexpr (W >= 8) v += dpp_f32<0x141>(v);
+  if constexpr (W >= 4) v += dpp_f32<0x1B>(v);
+  if constexpr (W >= 2) v += dpp_f32<0xB1>(v);
+  if constexpr (W >= 32) v = swap_sum<16>(v);
+  if constexpr (W >= 64) v = swap_sum<32>(v);
+  return v;
+}
+
+// Gate and up row sums of one row at once.  Full-wave rows (width 64): one
+// lane swap leaves gate pairs in lanes 0-31 and up pairs in lanes 32-63, the
+// rest of the reduction runs within each half, and lanes 0 and 32 hand the
+// totals to the whole wave.  Narrower rows: two group_sums.  Every lane ends
+// with its row's totals.
+template <int W>
+__device__ __forceinline__ void gu_sums_w(float accg, float accu, int width, float& g, float& u) {
+  if (W == kWave || (W == 0 && width == kWave)) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(accg), __float_as_uint(accu), false, false);
+    const float v = group_sum_w<32>(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+    g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));   // the builtin takes int: move bits
+    u = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  } else if constexpr (W == 0) {
+    g = group_sum(accg, width);
+    u = group_sum(accu, width);
+  } else {
+    g = group_sum_w<W>(accg);
+    u = group_sum_w<W>(accu);
+  }
+}
+
+__device__ __forceinline__ void gu_sums(float accg, float accu, int width, float& g, float& u) {
+  gu_sums_w<0>(accg, accu, width, g, u);
+}
+
+// silu(a) = a / (1 + e^-a) on the hardware exp and reciprocal (about one ulp each).
+__device__ __forceinline__ float silu(float a) { return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
 
 __device__ __forceinline__ float sigmoid(float a) { return 1.0f / (1.0f + expf(-a)); }
 
