@@ -108,440 +108,6 @@ __device__ inline LdsA carve_a(uint8_t* base, const FusedArgs& a) {
 }
 
 // ---------------------------------------------------------------------------
-// Launch A: phases R, K, G.
-template <int BITS, int SB, int ACT>
-__global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
-  extern __shared__ __align__(16) uint8_t lds_raw[];
-  const LdsA s = carve_a(lds_raw, a);
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform: lets the compiler use scalar math
-  const int T = a.T, H = a.H, E = a.E, k = a.k;
-  // bf16 activations with int4 codes take the v_dot2 segment dot
-  constexpr bool kDot2 = ACT == kBF16 && BITS == 4;
-  uint32_t spins = 0;
-  bool timed_out = false;
-
-  // This call's tag: the epoch word plus one.  Launch B advances the word, so
-  // it cannot change while any block of this launch still has to read it.
-  if (tid == 0) {
-    const uint32_t ep = __hip_atomic_load(a.ctrl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s.misc[1] = static_cast<int32_t>(ep + 1u);
-  }
-  // ---- phase R setup: router rows on the first blocks (block-major,
-  // kRouterRowsPerWave row groups per wave, so only a few blocks produce
-  // logits); shared gate/up rows on the waves of the other blocks (wave-major,
-  // spread over the machine).  The first task's weights are requested before
-  // the x / slot-table copy below, so the two memory round trips overlap.
-  const size_t xrow = static_cast<size_t>(H) * a.act_sz;
-  const int nwaves = a.nb * kWaves;
-  const RowLanes rlh = row_lanes(H, lane);
-  const int router_tasks = (E + rlh.rpp - 1) / rlh.rpp;
-  const int router_waves = (router_tasks + kRouterRowsPerWave - 1) / kRouterRowsPerWave;
-  const int router_blocks = min(a.nb, (router_waves + kWaves - 1) / kWaves);
-  const int sh_tasks = (a.SI + rlh.rpp - 1) / rlh.rpp;
-  const int bwave = blockIdx.x * kWaves + wave;
-  const int r_task0 = bwave * kRouterRowsPerWave;
-  ActRaw<ACT> rw[kRouterRowsPerWave];
-  int ee[kRouterRowsPerWave];
-  auto load_router_rows = [&](int task) {
-#pragma unroll
-    for (int j = 0; j < kRouterRowsPerWave; ++j) {
-      const int e = (task + j) * rlh.rpp + rlh.sub_row;
-      ee[j] = task + j < router_tasks && e < E ? e : -1;
-      load_act_raw<ACT>(static_cast<const uint8_t*>(a.router) + static_cast<size_t>(ee[j] < 0 ? 0 : e) * xrow,
-                        rlh.seg0, rw[j]);
-    }
-  };
-  if (r_task0 < router_tasks) load_router_rows(r_task0);
-  const Planes pls = planes_of(H, a.SI, BITS, SB);
-  const int64_t sh_row_bytes = static_cast<int64_t>(H) * BITS / 8;
-  const int gpr = H / 64;
-  const int sh_blocks = a.nb > router_blocks ? a.nb - router_blocks : a.nb;
-  const int sh_b = a.nb > router_blocks ? static_cast<int>(blockIdx.x) - router_blocks : static_cast<int>(blockIdx.x);
-  const int s_task0 = sh_b >= 0 ? wave * sh_blocks + sh_b : sh_tasks;
-  Seg<BITS> scg, scu;
-  uint32_t ssg = 0, ssu = 0, sbg = 0, sbu = 0;
-  auto load_shared_row = [&](int task) {
-    const int rr0 = task * rlh.rpp + rlh.sub_row;
-    const int rr = rr0 < a.SI ? rr0 : 0;   // loads stay unconditional; the store is masked
-    const int64_t qo = rr * sh_row_bytes + static_cast<int64_t>(rlh.seg0) * (kSegCodes * BITS / 8);
-    scg = load_codes<BITS>(a.shared + qo);
-    scu = load_codes<BITS>(a.shared + pls.q + qo);
-    const size_t si = static_cast<size_t>(rr) * gpr + rlh.seg0 / 2;
-    ssg = load_raw<SB>(a.shared + 3 * pls.q, si);
-    ssu = load_raw<SB>(a.shared + 3 * pls.q + pls.s, si);
-    sbg = load_raw<SB>(a.shared + 3 * pls.q + 3 * pls.s, si);
-    sbu = load_raw<SB>(a.shared + 3 * pls.q + 4 * pls.s, si);
-  };
-  if (s_task0 < sh_tasks) load_shared_row(s_task0);
-  {
-    // x and the slot table into LDS; each round requests its elements of both
-    // before storing any, so the copy costs one memory round trip per round
-    const int n16 = T * H * a.act_sz / 16;
-    const u32x4* src = static_cast<const u32x4*>(a.x);
-    u32x4* dst = reinterpret_cast<u32x4*>(s.x);
-    const int n = n16 > E ? n16 : E;
-    for (int i0 = 0; i0 < n; i0 += 2 * kThreads) {
-      u32x4 xv[2];
-      int64_t sv[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int i = i0 + u * kThreads + tid;
-        xv[u] = src[i < n16 ? i : 0];
-        sv[u] = a.slot_table[i < E ? i : 0];
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int i = i0 + u * kThreads + tid;
-        if (i < n16) dst[i] = xv[u];
-        if (i < E) s.slot[i] = sv[u];
-      }
-    }
-  }
-  __syncthreads();
-  const uint32_t tag = static_cast<uint32_t>(s.misc[1]);
-  const int gwave = wave * a.nb + blockIdx.x;
-
-  // ---- phase R
-  for (int task = r_task0; task < router_tasks; task += nwaves * kRouterRowsPerWave) {
-    if (task != r_task0) load_router_rows(task);
-#pragma unroll
-    for (int j = 0; j < kRouterRowsPerWave; ++j) {
-      if (task + j >= router_tasks) break;
-      const bool active = ee[j] >= 0;
-      float r[kSegCodes];
-      act_raw_f32<ACT>(rw[j], r);
-      for (int t = 0; t < T; ++t) {
-        float acc = 0.f;
-        if (active) {
-          float v[kSegCodes];
-          load_act_seg<ACT>(s.x + t * xrow, rlh.seg0, v);
-#pragma unroll
-          for (int c = 0; c < kSegCodes; ++c) acc = fmaf(v[c], r[c], acc);
-        }
-        acc = group_sum(acc, rlh.width);
-        if (active)   // every lane of the row holds the sum: each stores some of the copies
-          for (int rep = lane % rlh.width; rep < kFusedReplicas; rep += rlh.width)
-            store_tagged(a.lg + (static_cast<size_t>(rep) * T + t) * E + ee[j], acc, tag);
-      }
-    }
-  }
-  for (int task = s_task0; task < sh_tasks; task += sh_blocks * kWaves) {
-    if (task != s_task0) load_shared_row(task);
-    const int rr = task * rlh.rpp + rlh.sub_row;
-    const bool ok = rr < a.SI;
-    if constexpr (kDot2) {
-      const QPairs pg = qpairs_bf16(scg), pu = qpairs_bf16(scu);
-      for (int t = 0; t < T; ++t) {
-        ActRaw<kBF16> xr;
-        load_lds_act_bf16(s.x + t * xrow, rlh.seg0, xr);
-        const float xs = xsum_bf16(xr);
-        float accg = 0.f, accu = 0.f;
-        accg += seg_value_d2(raw_value<SB>(ssg), raw_value<SB>(sbg), dot2_seg(pg, xr), xs);
-        accu += seg_value_d2(raw_value<SB>(ssu), raw_value<SB>(sbu), dot2_seg(pu, xr), xs);
-        float g, u;
-        gu_sums(accg, accu, rlh.width, g, u);
-        if (ok && (lane % rlh.width) == 0) a.h[(static_cast<size_t>(T) * k + t) * a.hs + rr] = silu(g) * u;
-      }
-    } else {
-      for (int t = 0; t < T; ++t) {
-        float v[1][kSegCodes];
-        load_act_seg<ACT>(s.x + t * xrow, rlh.seg0, v[0]);
-        const float xs = seg_sum(v[0]);
-        float qg[1], qu[1];
-        seg_qdot_nt<BITS, 1>(scg, v, qg);
-        seg_qdot_nt<BITS, 1>(scu, v, qu);
-        float accg = 0.f, accu = 0.f;
-        accg += seg_value(raw_value<SB>(ssg), raw_value<SB>(sbg), qg[0], xs);
-        accu += seg_value(raw_value<SB>(ssu), raw_value<SB>(sbu), qu[0], xs);
-        float g, u;
-        gu_sums(accg, accu, rlh.width, g, u);
-        if (ok && (lane % rlh.width) == 0) a.h[(static_cast<size_t>(T) * k + t) * a.hs + rr] = silu(g) * u;
-      }
-    }
-  }
-  // sigmoid(g . x_t) on block 0 (lane covers segments L, L + 64, ... as in the staged path)
-  if (blockIdx.x == 0 && wave == kWaves - 1) {
-    const uint8_t* gvec = a.shared + a.shared_stride;
-    const int nseg = H / kSegCodes;
-    for (int t = 0; t < T; ++t) {
-      float acc = 0.f;
-      if (lane < nseg) {
-        float xv[kSegCodes], gv[kSegCodes];
-        load_act_seg<ACT>(s.x + t * xrow, lane, xv);
-        load_act_seg<ACT>(gvec, lane, gv);
-#pragma unroll
-        for (int c = 0; c < kSegCodes; ++c) acc = fmaf(xv[c], gv[c], acc);
-      }
-      acc = group_sum(acc, kWave);
-      if (lane == 0) a.sig[t] = sigmoid(acc);
-    }
-  }
-
-  // ---- phase K: gather all logits (each word checked against this call's
-  // tag, re-read until every one has arrived), top-k, dispatch
-  const int rep = blockIdx.x % kFusedReplicas;
-  for (;;) {
-    int missing = 0;
-    for (int i = tid; i < T * E; i += kThreads) {
-      const uint64_t w = load_tagged(a.lg + static_cast<size_t>(rep) * T * E + i);
-      if (static_cast<uint32_t>(w >> 32) != tag) missing = 1;
-      else s.lg[i] = __uint_as_float(static_cast<uint32_t>(w));
-    }
-    if (!__syncthreads_or(missing)) break;
-    if (++spins > a.spin_limit) { timed_out = true; break; }
-    __builtin_amdgcn_s_sleep(2);
-  }
-  for (int t = wave; t < T; t += kWaves)
-    topk_wave(s.lg + static_cast<size_t>(t) * E, E, k, lane, s.cand + wave * kCandMax, s.ids + t * k,
-              s.vals + t * k);
-  if (T == 1) {
-    // one token: its k experts are distinct; order them by id with a rank count
-    if (wave == 0) {
-      int e = lane < k ? s.ids[lane] : 0x7fffffff;
-      e = e >= 0 && e < E ? e : 0;
-      int r = 0;
-      for (int j = 0; j < k; ++j) r += s.ids[j] < e ? 1 : 0;
-      if (lane < k) {
-        s.uniq[r] = e;
-        s.pidx[r] = lane;
-        s.uranks[r] = static_cast<uint64_t>(lane + 1);
-      }
-      if (lane == 0) s.misc[0] = k;
-    }
-    __syncthreads();
-  } else {
-    for (int e = tid; e < E; e += kThreads) s.umap[e] = -1;
-    __syncthreads();
-    for (int p = tid; p < T * k; p += kThreads) {
-      const int e = s.ids[p];
-      s.ids[p] = e >= 0 && e < E ? e : 0;           // ids come from [0, E) by construction
-      s.umap[s.ids[p]] = 0;                         // mark
-    }
-    __syncthreads();
-    if (wave == 0) {
-      int base = 0;
-      for (int c0 = 0; c0 < E; c0 += kWave) {
-        const int e = c0 + lane;
-        const bool used = e < E && s.umap[e] == 0;
-        const uint64_t m = __ballot(used);
-        const int pos = base + __popcll(m & lane_mask_lt(lane));
-        if (used) { s.uniq[pos] = e; s.umap[e] = pos; }
-        base += __popcll(m);
-      }
-      if (lane == 0) s.misc[0] = base;
-    }
-    __syncthreads();
-    const int Ud = s.misc[0];
-    for (int i = tid; i < Ud * T; i += kThreads) s.pidx[i] = -1;
-    __syncthreads();
-    for (int p = tid; p < T * k; p += kThreads) s.pidx[s.umap[s.ids[p]] * T + p / k] = p % k;
-    __syncthreads();
-    // phase-G work per distinct expert: a row's loads plus one dot per token
-    // that uses it; prefix sums so that every wave takes an equal share
-    if (wave == 0) {
-      int carry = 0;
-      for (int u0 = 0; u0 < Ud; u0 += kWave) {
-        const int u = u0 + lane;
-        int c = 0;
-        if (u < Ud) {
-          c = kRowCost;
-          uint64_t rk = 0;
-          for (int t = 0; t < T; ++t) {
-            const int i = s.pidx[u * T + t];
-            c += i >= 0 ? 1 : 0;
-            rk |= static_cast<uint64_t>(i + 1) << (8 * t);
-          }
-          s.uranks[u] = rk;
-        }
-        int incl = c;
-#pragma unroll
-        for (int m = 1; m < kWave; m <<= 1) {
-          const int o = __shfl_up(incl, m, kWave);
-          if (lane >= m) incl += o;
-        }
-        if (u < Ud) s.ucost[u + 1] = carry + incl;
-        carry += __shfl(incl, kWave - 1, kWave);
-      }
-      if (lane == 0) s.ucost[0] = 0;
-    }
-    __syncthreads();
-  }
-  const int U = s.misc[0];
-  if (blockIdx.x == 0) {
-    // routing record for launch B (and the optional outputs)
-    for (int p = tid; p < T * k; p += kThreads) {
-      a.wts[p] = s.vals[p];
-      if (a.ids_out) a.ids_out[p] = s.ids[p];
-      if (a.wts_out) a.wts_out[p] = s.vals[p];
-    }
-    for (int i = tid; i < U * T; i += kThreads) a.pidx[i] = s.pidx[i];
-    for (int i = tid; i < U; i += kThreads) {
-      a.uniq[i] = s.uniq[i];
-      a.uoff[i] = s.slot[s.uniq[i]];
-    }
-    if (tid == 0) *a.ucount = U;
-  }
-
-  // ---- phase G: routed gate/up rows, flattened over (expert, row group)
-  {
-    const Planes pl = planes_of(H, a.I, BITS, SB);
-    const int64_t row_bytes = static_cast<int64_t>(H) * BITS / 8;
-    const int seg_bytes = kSegCodes * BITS / 8;
-    const int gpr = H / 64;
-    const int groups_per_expert = a.I / rlh.rpp;
-    const int total = U * groups_per_expert;
-    int g_lo, g_hi;
-    if (T == 1) {
-      // every unit costs the same
-      const int per_wave = (total + nwaves - 1) / nwaves;
-      g_lo = min(total, gwave * per_wave);
-      g_hi = min(total, g_lo + per_wave);
-    } else {
-      // equal shares of the work: unit (u, group) costs ucost[u + 1] - ucost[u]
-      // over groups_per_expert; a share starts at the first unit that starts
-      // at or after its cost position
-      const int64_t W = static_cast<int64_t>(s.ucost[U]) * groups_per_expert;
-      auto unit_at = [&](int64_t x) {
-        if (x >= W) return total;
-        int lo = 0, hi = U - 1;   // last u with ucost[u] * gpe <= x
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (static_cast<int64_t>(s.ucost[mid]) * groups_per_expert <= x) lo = mid;
-          else hi = mid - 1;
-        }
-        const int64_t c = s.ucost[lo + 1] - s.ucost[lo];   // cost of one unit of expert lo
-        const int64_t i = (x - static_cast<int64_t>(s.ucost[lo]) * groups_per_expert + c - 1) / c;
-        return lo * groups_per_expert + static_cast<int>(i);
-      };
-      g_lo = unit_at(W * gwave / nwaves);
-      g_hi = unit_at(W * (gwave + 1) / nwaves);
-    }
-    // per-token segment sums of x (the lane's segment is the same in every
-    // row), once per wave, in a wave-private table in the logits area, which
-    // nothing reads after top-k
-    lds_f32* const xs_tab = (lds_f32*)(s.lg) + wave * T * kWave;
-    if constexpr (kDot2) {
-      for (int t = 0; t < T; ++t) {
-        ActRaw<kBF16> xr;
-        load_lds_act_bf16(s.x + t * xrow, rlh.seg0, xr);
-        xs_tab[t * kWave + lane] = xsum_bf16(xr);
-      }
-    }
-    // Rows go in batches of kBatch; the next batch's loads are requested
-    // before the current batch is computed (two register sets, alternating).
-    constexpr int kBatch = 4;
-    struct Batch {
-      Seg<BITS> cg[kBatch], cu[kBatch];
-      uint32_t sg[kBatch], su[kBatch], bg[kBatch], bu[kBatch];
-      int uu[kBatch], rr[kBatch];
-      bool vv[kBatch];
-    };
-    // every row of a batch is requested before any is used: no branches on
-    // the loads (a row past the end repeats the first one, an unusable blob
-    // reads blob 0; both are masked at the store) and raw scale bits
-    auto load_batch = [&](Batch& B, int g0) {
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        const int g = g0 + b;
-        const bool live = g < g_hi;
-        const int gc = live ? g : g_lo;
-        const int u = gc / groups_per_expert;
-        const int r = (gc % groups_per_expert) * rlh.rpp + rlh.sub_row;
-        const int64_t off = s.slot[s.uniq[u]];
-        const bool valid = slot_ok(off, pl.blob, a.pool_bytes);
-        B.uu[b] = live ? u : -1;
-        B.rr[b] = r;
-        B.vv[b] = valid;
-        if (live && !valid && lane == 0) raise_error(a.ctrl, kErrRange);
-        const uint8_t* blob = a.pool + (valid ? off : 0);
-        const int64_t qo = r * row_bytes + static_cast<int64_t>(rlh.seg0) * seg_bytes;
-        B.cg[b] = load_codes<BITS>(blob + qo);
-        B.cu[b] = load_codes<BITS>(blob + pl.q + qo);
-        const size_t si = static_cast<size_t>(r) * gpr + rlh.seg0 / 2;
-        B.sg[b] = load_raw<SB>(blob + 3 * pl.q, si);
-        B.su[b] = load_raw<SB>(blob + 3 * pl.q + pl.s, si);
-        B.bg[b] = load_raw<SB>(blob + 3 * pl.q + 3 * pl.s, si);
-        B.bu[b] = load_raw<SB>(blob + 3 * pl.q + 4 * pl.s, si);
-      }
-    };
-    auto compute_batch = [&](const Batch& B, auto wtag) {
-      // row sums: width known at compile time for full-wave rows
-      constexpr int W = decltype(wtag)::value;
-      if constexpr (kDot2) {
-        // rows outer: each row's codes become bf16 pairs once for all its
-        // tokens; the tokens that use the row come from its packed ranks
-#pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-          if (B.uu[b] < 0) continue;
-          const uint64_t rkv = s.uranks[B.uu[b]];
-          uint64_t rk = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rkv >> 32))) << 32) |
-                        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rkv)));
-          const QPairs pg = qpairs_bf16(B.cg[b]), pu = qpairs_bf16(B.cu[b]);
-          const float sgv = raw_value<SB>(B.sg[b]), bgv = raw_value<SB>(B.bg[b]);
-          const float suv = raw_value<SB>(B.su[b]), buv = raw_value<SB>(B.bu[b]);
-          while (rk != 0) {
-            const int sh = __builtin_ctzll(rk) & ~7;
-            const int t = sh >> 3;
-            const int i = static_cast<int>((rk >> sh) & 0xffu) - 1;
-            rk &= ~(0xffull << sh);
-            ActRaw<kBF16> xr;
-            load_lds_act_bf16(s.x + t * xrow, rlh.seg0, xr);
-            const float xs = xs_tab[t * kWave + lane];
-            float accg = 0.f, accu = 0.f;
-            accg += seg_value_d2(sgv, bgv, dot2_seg(pg, xr), xs);
-            accu += seg_value_d2(suv, buv, dot2_seg(pu, xr), xs);
-            float g, u;
-            gu_sums_w<W>(accg, accu, rlh.width, g, u);
-            if ((lane % rlh.width) == 0)
-              a.h[(static_cast<size_t>(t) * k + i) * a.hs + B.rr[b]] = B.vv[b] ? silu(g) * u : 0.f;
-          }
-        }
-      } else {
-        for (int t = 0; t < T; ++t) {
-          float v[1][kSegCodes];
-          load_act_seg<ACT>(s.x + t * xrow, rlh.seg0, v[0]);
-          const float xs = seg_sum(v[0]);
-#pragma unroll
-          for (int b = 0; b < kBatch; ++b) {
-            if (B.uu[b] < 0) continue;
-            const int i = s.pidx[B.uu[b] * T + t];
-            if (i < 0) continue;                      // token t does not use this expert
-            float qg[1], qu[1];
-            seg_qdot_nt<BITS, 1>(B.cg[b], v, qg);
-            seg_qdot_nt<BITS, 1>(B.cu[b], v, qu);
-            float accg = 0.f, accu = 0.f;
-            accg += seg_value(raw_value<SB>(B.sg[b]), raw_value<SB>(B.bg[b]), qg[0], xs);
-            accu += seg_value(raw_value<SB>(B.su[b]), raw_value<SB>(B.bu[b]), qu[0], xs);
-            float g, u;
-            gu_sums_w<W>(accg, accu, rlh.width, g, u);
-            if ((lane % rlh.width) == 0)
-              a.h[(static_cast<size_t>(t) * k + i) * a.hs + B.rr[b]] = B.vv[b] ? silu(g) * u : 0.f;
-          }
-        }
-      }
-    };
-    auto run = [&](auto wtag) {
-      Batch b0, b1;
-      load_batch(b0, g_lo);
-      for (int g0 = g_lo; g0 < g_hi; g0 += 2 * kBatch) {
-        if (g0 + kBatch < g_hi) load_batch(b1, g0 + kBatch);
-        compute_batch(b0, wtag);
-        if (g0 + kBatch >= g_hi) break;
-        if (g0 + 2 * kBatch < g_hi) load_batch(b0, g0 + 2 * kBatch);
-        compute_batch(b1, wtag);
-      }
-    };
-    if (g_lo < g_hi) {
-      if (rlh.width == kWave) run(IntC<kWave>{});
-      else run(IntC<0>{});
-    }
-  }
-  if (timed_out && lane == 0) raise_error(a.ctrl, kErrTimeout);
-}
-
-// ---------------------------------------------------------------------------
 // Launch B: one block per (slice of rb output rows, token): the slice's down
 // rows of the token's k experts and of the shared expert, then the ordered
 // combine.  A block's partial sums are all its own, and the token's k + 1 h
@@ -686,144 +252,145 @@ __device__ __forceinline__ LaneOffsets lane_offsets(const FusedArgs& a, const Do
   return o;
 }
 
-template <int SB>
-__device__ __forceinline__ uint32_t load_raw_at(const uint8_t* p) {
-  if constexpr (SB == kF32) return *reinterpret_cast<const uint32_t*>(p);
-  else return *reinterpret_cast<const uint16_t*>(p);
-}
-
 // load_down_task for np == 1: the pair rank is the task index, the blob base
-// is wave-uniform (scalar) and the lane offsets are precomputed.
+// is wave-uniform (scalar), the lane offsets are precomputed and the blob
+// offset `off` (s.poff[i], read by the caller before any task's loads) is
+// given.
 template <int BITS, int SB>
 __device__ __forceinline__ void load_down_task_1(DownTask<BITS>& d, int task, int ntask, const DownCtx& c,
-                                                 const FusedArgs& a, const LdsB& s, const LaneOffsets& o) {
+                                                 const FusedArgs& a, int64_t off, const LaneOffsets& o) {
   const int k = a.k;
   const bool live = task < ntask;
   const int i = live ? task : k;            // a dead task re-reads the shared blob
   const bool is_sh = i == k;
-  const int64_t off = is_sh ? 0 : s.poff[i];
   const bool valid = is_sh || slot_ok(off, c.blob_r, a.pool_bytes);
   const uint64_t bits = reinterpret_cast<uint64_t>(is_sh ? a.shared : a.pool + (valid ? off : 0));
-  const uint8_t* blob = reinterpret_cast<const uint8_t*>(
-      (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(bits >> 32))) << 32) |
-      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(bits))));
-  d.code = load_codes<BITS>(blob + (is_sh ? o.code_s : o.code_r));
-  d.sc = load_raw_at<SB>(blob + (is_sh ? o.sc_s : o.sc_r));
-  d.bi = load_raw_at<SB>(blob + (is_sh ? o.bi_s : o.bi_r));
+  const uint64_t blob = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(bits >> 32))) << 32) |
+                        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(bits)));
+  d.code = load_codes_g<BITS>(blob + (is_sh ? o.code_s : o.code_r));
+  d.sc = load_raw_g<SB>(blob + (is_sh ? o.sc_s : o.sc_r));
+  d.bi = load_raw_g<SB>(blob + (is_sh ? o.bi_s : o.bi_r));
   d.i = live ? i : -1;
   d.rloc = live ? (is_sh ? o.rloc_s : o.rloc_r) : -1;
   d.valid = valid;
 }
 
-template <int BITS, int SB, int OUT>
-__global__ __launch_bounds__(kThreads) void k_decode_b(FusedArgs a) {
-  extern __shared__ __align__(16) uint8_t lds_raw[];
-  const LdsB s = carve_b(lds_raw, a);
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform: lets the compiler use scalar math
-  const int T = a.T, k = a.k;
-  // Retire launch A's tag: every block of A has finished, so none can still
-  // read the epoch word.
-  if (blockIdx.x == 0 && tid == 0)
-    __hip_atomic_store(a.ctrl + 1, __hip_atomic_load(a.ctrl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u,
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // (slice, token) of this block: XCD x (blocks x, x + 8, ...) runs a
-  // contiguous range of them, token-minor
-  int slice, t;
-  {
-    const int nb = a.nslice * T;
-    const int per = (nb + kXcds - 1) / kXcds;
-    const int idx = blockIdx.x / kXcds;
-    if (idx >= per) return;
-    const int logical = (blockIdx.x % kXcds) * per + idx;
-    if (logical >= nb) return;
-    slice = logical / T;
-    t = logical - slice * T;
-  }
-  // the token's routing: blob offsets by rank, weights, gate; every element
-  // requested before any is stored (a rank that no distinct expert claims
-  // keeps offset -1, which slot_ok rejects)
-  if (tid < k) s.poff[tid] = -1;
-  __syncthreads();
-  {
-    const int U = *a.ucount;
-    for (int u0 = 0; u0 < a.umax || u0 < k; u0 += kThreads) {
-      const int u = u0 + tid;
-      const int32_t i = a.pidx[(u < a.umax ? u : 0) * T + t];
-      const int64_t off = a.uoff[u < a.umax ? u : 0];
-      const float wt = a.wts[t * k + (u < k ? u : 0)];
-      const float sg = a.sig[t];
-      if (u < a.umax && u < U && i >= 0 && i < k) s.poff[i] = off;
-      if (u < k) s.wts[u] = wt;
-      if (u == 0) s.sig[0] = sg;
-    }
-  }
-  __syncthreads();
+// (slice, token) unit of this block: XCD x (blocks x, x + 8, ...) runs a
+// contiguous range of units, token-minor, so the tokens of one slice read
+// the slice's weight rows through one L2.  False for a block without a unit.
+__device__ __forceinline__ bool unit_of(int nunits, int T, int* slice, int* t) {
+  const int per = (nunits + kXcds - 1) / kXcds;
+  const int idx = blockIdx.x / kXcds;
+  if (idx >= per) return false;
+  const int logical = (blockIdx.x % kXcds) * per + idx;
+  if (logical >= nunits) return false;
+  *slice = logical / T;
+  *t = logical - *slice * T;
+  return true;
+}
 
-  const RowLanes rli = row_lanes(a.I, lane);
-  const RowLanes rls = row_lanes(a.SI, lane);
-  const int row_lo = slice * a.rb;
-  const DownCtx dc = down_ctx<BITS, SB>(a, rli, rls);
-  const int ntask = (k + 1) * dc.np;
-  const int nseg = a.hs / kSegCodes;
-  const LaneOffsets lo = lane_offsets<BITS, SB>(a, dc, rli, rls, row_lo);
-  auto h_row = [&](int i) { return i < k ? static_cast<size_t>(t) * k + i : static_cast<size_t>(T) * k + t; };
-  DownTask<BITS> dt[kMaxDownPerWave];
-  float hv[kMaxDownPerWave][1][kSegCodes];
-  for (int base = 0; base < ntask; base += kWaves * kMaxDownPerWave) {
-    // codes of this round's tasks, all requested before any compute
-    if (dc.np == 1) {
-#pragma unroll
-      for (int q = 0; q < kMaxDownPerWave; ++q)
-        load_down_task_1<BITS, SB>(dt[q], base + wave + q * kWaves, ntask, dc, a, s, lo);
-    } else {
-#pragma unroll
-      for (int q = 0; q < kMaxDownPerWave; ++q)
-        load_down_task<BITS, SB>(dt[q], base + wave + q * kWaves, ntask, dc, row_lo, a, s, rli, rls);
-    }
-    if (s.h && base == 0) {
-      // the token's k + 1 h rows into LDS once, while the codes above are in flight
-      const int r4 = a.hs / 4;                            // float4 per row
-      const int n4 = (k + 1) * r4;
-      lds_u32x4* dst = (lds_u32x4*)(s.h);
-      for (int j = tid; j < n4; j += kThreads) {
-        const int i = j / r4;
-        const float4 v = reinterpret_cast<const float4*>(a.h + h_row(i) * a.hs)[j - i * r4];
-        dst[(j >> 3) * (kSegPad / 4) + (j & 7)] = u32x4{__float_as_uint(v.x), __float_as_uint(v.y),
-                                                          __float_as_uint(v.z), __float_as_uint(v.w)};
-      }
-      __syncthreads();
-      // segment sums once per block, in the order seg_sum uses
-      for (int j = tid; j < (k + 1) * nseg; j += kThreads) {
-        float v[kSegCodes];
-        load_lds_seg(s.h + static_cast<size_t>(j) * kSegPad, 0, v);
-        ((lds_f32*)(s.hsum))[j] = seg_sum(v);
-      }
-      __syncthreads();
-    }
+// Per-unit constants of a block's down tasks (kept as separate locals by the
+// callers: bundled in one struct, selects between its fields become loads
+// through a selected address and the struct lands in scratch memory).
+#define DOWN_SETUP(BITS, SB, a, slice, lane)                                  \
+  const RowLanes rli = row_lanes((a).I, lane);                                \
+  const RowLanes rls = row_lanes((a).SI, lane);                               \
+  const int row_lo = (slice) * (a).rb;                                        \
+  const DownCtx dc = down_ctx<BITS, SB>(a, rli, rls);                         \
+  const int ntask = ((a).k + 1) * dc.np;                                      \
+  const LaneOffsets lo = lane_offsets<BITS, SB>(a, dc, rli, rls, row_lo)
+
+// Requests the loads of the round of tasks starting at `base` (this wave's
+// kMaxDownPerWave of them); every blob offset is read before any load.
+template <int BITS, int SB>
+__device__ __forceinline__ void issue_down_round(DownTask<BITS> (&dt)[kMaxDownPerWave], int base, int ntask,
+                                                 const DownCtx& dc, const LaneOffsets& lo, const RowLanes& rli,
+                                                 const RowLanes& rls, int row_lo, const FusedArgs& a, const LdsB& s,
+                                                 int wave) {
+  if (dc.np == 1) {
+    int64_t offs[kMaxDownPerWave];
 #pragma unroll
     for (int q = 0; q < kMaxDownPerWave; ++q) {
-      if (dt[q].i < 0) continue;
-      const int i = dt[q].i;
-      const RowLanes& rl = i == k ? rls : rli;
-      float hs;
-      if (s.h) {
-        load_lds_seg(s.h + (static_cast<size_t>(i) * nseg + rl.seg0) * kSegPad, 0, hv[q][0]);
-        hs = ((const lds_f32*)(s.hsum))[i * nseg + rl.seg0];
-      } else {
-        load_f32_seg(a.h + h_row(i) * a.hs, rl.seg0, hv[q][0]);
-        hs = seg_sum(hv[q][0]);
-      }
-      float qv[1];
-      seg_qdot_nt<BITS, 1>(dt[q].code, hv[q], qv);
-      float acc = 0.f;
-      acc += seg_value(raw_value<SB>(dt[q].sc), raw_value<SB>(dt[q].bi), qv[0], hs);
-      const float v = group_sum(acc, rl.width);
-      if ((lane % rl.width) == 0 && dt[q].rloc >= 0) s.part[i * a.rb + dt[q].rloc] = dt[q].valid ? v : 0.f;
+      const int i = base + wave + q * kWaves;
+      offs[q] = s.poff[i < a.k ? i : 0];
     }
+#pragma unroll
+    for (int q = 0; q < kMaxDownPerWave; ++q)
+      load_down_task_1<BITS, SB>(dt[q], base + wave + q * kWaves, ntask, dc, a, offs[q], lo);
+  } else {
+#pragma unroll
+    for (int q = 0; q < kMaxDownPerWave; ++q)
+      load_down_task<BITS, SB>(dt[q], base + wave + q * kWaves, ntask, dc, row_lo, a, s, rli, rls);
+  }
+}
+
+__device__ __forceinline__ size_t h_row_of(int T, int k, int t, int i) {
+  return i < k ? static_cast<size_t>(t) * k + i : static_cast<size_t>(T) * k + t;
+}
+
+// One round: each task's row segment dot with the token's h row, reduced over
+// the row's lanes, into s.part.
+template <int BITS, int SB>
+__device__ __forceinline__ void compute_down_round(const DownTask<BITS> (&dt)[kMaxDownPerWave], const RowLanes& rli,
+                                                   const RowLanes& rls, const FusedArgs& a, const LdsB& s, int T, int t,
+                                                   int lane) {
+  const int k = a.k, nseg = a.hs / kSegCodes;
+#pragma unroll
+  for (int q = 0; q < kMaxDownPerWave; ++q) {
+    if (dt[q].i < 0) continue;
+    const int i = dt[q].i;
+    const bool is_sh = i == k;
+    const int seg0 = is_sh ? rls.seg0 : rli.seg0;
+    const int width = is_sh ? rls.width : rli.width;
+    float hv[1][kSegCodes];
+    float hs;
+    if (s.h) {
+      load_lds_seg(s.h + (static_cast<size_t>(i) * nseg + seg0) * kSegPad, 0, hv[0]);
+      hs = ((const lds_f32*)(s.hsum))[i * nseg + seg0];
+    } else {
+      load_f32_seg(a.h + h_row_of(T, k, t, i) * a.hs, seg0, hv[0]);
+      hs = seg_sum(hv[0]);
+    }
+    float qv[1];
+    seg_qdot_nt<BITS, 1>(dt[q].code, hv, qv);
+    float acc = 0.f;
+    acc += seg_value(raw_value<SB>(dt[q].sc), raw_value<SB>(dt[q].bi), qv[0], hs);
+    const float v = group_sum(acc, width);
+    if ((lane % width) == 0 && dt[q].rloc >= 0) s.part[i * a.rb + dt[q].rloc] = dt[q].valid ? v : 0.f;
+  }
+}
+
+// Segment sums of the staged h rows, in the order seg_sum uses.
+__device__ __forceinline__ void h_segment_sums(const FusedArgs& a, const LdsB& s, int tid) {
+  for (int j = tid; j < (a.k + 1) * (a.hs / kSegCodes); j += kThreads) {
+    float v[kSegCodes];
+    load_lds_seg(s.h + static_cast<size_t>(j) * kSegPad, 0, v);
+    ((lds_f32*)(s.hsum))[j] = seg_sum(v);
+  }
+}
+
+// The token's k + 1 h rows from the plain h buffer into s.h.
+__device__ __forceinline__ void stage_h_plain(const FusedArgs& a, const LdsB& s, int T, int t, int tid) {
+  const int k = a.k;
+  const int r4 = a.hs / 4;                            // float4 per row
+  const int n4 = (k + 1) * r4;
+  lds_u32x4* dst = (lds_u32x4*)(s.h);
+  for (int j = tid; j < n4; j += kThreads) {
+    const int i = j / r4;
+    const float4 v = reinterpret_cast<const float4*>(a.h + h_row_of(T, k, t, i) * a.hs)[j - i * r4];
+    dst[(j >> 3) * (kSegPad / 4) + (j & 7)] = u32x4{__float_as_uint(v.x), __float_as_uint(v.y),
+                                                      __float_as_uint(v.z), __float_as_uint(v.w)};
   }
   __syncthreads();
+  h_segment_sums(a, s, tid);
+  __syncthreads();
+}
+
+// Ordered combine of the unit's rows: sum over ranks of weight * partial,
+// then the gated shared expert.
+template <int OUT>
+__device__ __forceinline__ void combine_unit(const FusedArgs& a, const LdsB& s, int row_lo, int t, int tid) {
+  const int k = a.k;
   for (int rloc = tid; rloc < a.rb; rloc += kThreads) {
     const int n = row_lo + rloc;
     if (n >= a.H) continue;
@@ -836,6 +403,499 @@ __global__ __launch_bounds__(kThreads) void k_decode_b(FusedArgs a) {
       static_cast<uint16_t*>(a.out)[static_cast<size_t>(t) * a.H + n] = f32_to_bf16(acc);
     }
   }
+}
+
+// sigmoid(g . x) for one token on one wave (lane covers segments L, L + 64,
+// ... as in the staged path).
+template <int ACT>
+__device__ __forceinline__ float shared_gate(const uint8_t* xrow, const uint8_t* gvec, int H, int lane) {
+  const int nseg = H / kSegCodes;
+  float acc = 0.f;
+  if (lane < nseg) {
+    float xv[kSegCodes], gv[kSegCodes];
+    load_act_seg<ACT>(xrow, lane, xv);
+    load_act_seg<ACT>(gvec, lane, gv);
+#pragma unroll
+    for (int c = 0; c < kSegCodes; ++c) acc = fmaf(xv[c], gv[c], acc);
+  }
+  acc = group_sum(acc, kWave);
+  return sigmoid(acc);
+}
+
+// ---------------------------------------------------------------------------
+// Launch A: phases R, K, G.
+template <int BITS, int SB, int ACT>
+__global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
+  extern __shared__ __align__(16) uint8_t lds_raw[];
+  const LdsA s = carve_a(lds_raw, a);
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform: lets the compiler use scalar math
+  const int T = a.T, H = a.H, E = a.E, k = a.k;
+  // bf16 activations with int4 codes take the v_dot2 segment dot
+  constexpr bool kDot2 = ACT == kBF16 && BITS == 4;
+  uint32_t spins = 0;
+  bool timed_out = false;
+
+  // This call's tag: this block's epoch counter plus one.  Every block's
+  // counter holds the same value at the start of a call; launch B advances
+  // them all, after every block of this launch has read its own.
+  if (tid == 0) s.misc[1] = static_cast<int32_t>(a.epochs[blockIdx.x] + 1u);
+  // ---- phase R setup: router rows on the first blocks (block-major,
+  // kRouterRowsPerWave row groups per wave, so only a few blocks produce
+  // logits); shared gate/up rows on the waves of the other blocks (wave-major,
+  // spread over the machine).  The first task's weights are requested before
+  // the x / slot-table copy below, so the two memory round trips overlap.
+  const size_t xrow = static_cast<size_t>(H) * a.act_sz;
+  const int nwaves = a.nb * kWaves;
+  const RowLanes rlh = row_lanes(H, lane);
+  const int router_tasks = (E + rlh.rpp - 1) / rlh.rpp;
+  const int router_waves = (router_tasks + kRouterRowsPerWave - 1) / kRouterRowsPerWave;
+  const int router_blocks = min(a.nb, (router_waves + kWaves - 1) / kWaves);
+  const int sh_tasks = (a.SI + rlh.rpp - 1) / rlh.rpp;
+  const int bwave = blockIdx.x * kWaves + wave;
+  const int r_task0 = bwave * kRouterRowsPerWave;
+  ActRaw<ACT> rw[kRouterRowsPerWave];
+  int ee[kRouterRowsPerWave];
+  auto load_router_rows = [&](int task) {
+#pragma unroll
+    for (int j = 0; j < kRouterRowsPerWave; ++j) {
+      const int e = (task + j) * rlh.rpp + rlh.sub_row;
+      ee[j] = task + j < router_tasks && e < E ? e : -1;
+      load_act_raw<ACT>(static_cast<const uint8_t*>(a.router) + static_cast<size_t>(ee[j] < 0 ? 0 : e) * xrow,
+                        rlh.seg0, rw[j]);
+    }
+  };
+  if (r_task0 < router_tasks) load_router_rows(r_task0);
+  const Planes pls = planes_of(H, a.SI, BITS, SB);
+  const int64_t sh_row_bytes = static_cast<int64_t>(H) * BITS / 8;
+  const int gpr = H / 64;
+  const int sh_blocks = a.nb > router_blocks ? a.nb - router_blocks : a.nb;
+  const int sh_b = a.nb > router_blocks ? static_cast<int>(blockIdx.x) - router_blocks : static_cast<int>(blockIdx.x);
+  const int s_task0 = sh_b >= 0 ? wave * sh_blocks + sh_b : sh_tasks;
+  Seg<BITS> scg, scu;
+  uint32_t ssg = 0, ssu = 0, sbg = 0, sbu = 0;
+  auto load_shared_row = [&](int task) {
+    const int rr0 = task * rlh.rpp + rlh.sub_row;
+    const int rr = rr0 < a.SI ? rr0 : 0;   // loads stay unconditional; the store is masked
+    const int64_t qo = rr * sh_row_bytes + static_cast<int64_t>(rlh.seg0) * (kSegCodes * BITS / 8);
+    scg = load_codes<BITS>(a.shared + qo);
+    scu = load_codes<BITS>(a.shared + pls.q + qo);
+    const size_t si = static_cast<size_t>(rr) * gpr + rlh.seg0 / 2;
+    ssg = load_raw<SB>(a.shared + 3 * pls.q, si);
+    ssu = load_raw<SB>(a.shared + 3 * pls.q + pls.s, si);
+    sbg = load_raw<SB>(a.shared + 3 * pls.q + 3 * pls.s, si);
+    sbu = load_raw<SB>(a.shared + 3 * pls.q + 4 * pls.s, si);
+  };
+  if (s_task0 < sh_tasks) load_shared_row(s_task0);
+  {
+    // x and the slot table into LDS; each round requests its elements of both
+    // before storing any, so the copy costs one memory round trip per round
+    const int n16 = T * H * a.act_sz / 16;
+    const u32x4* src = static_cast<const u32x4*>(a.x);
+    u32x4* dst = reinterpret_cast<u32x4*>(s.x);
+    const int n = n16 > E ? n16 : E;
+    for (int i0 = 0; i0 < n; i0 += 2 * kThreads) {
+      u32x4 xv[2];
+      int64_t sv[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = i0 + u * kThreads + tid;
+        xv[u] = src[i < n16 ? i : 0];
+        sv[u] = a.slot_table[i < E ? i : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = i0 + u * kThreads + tid;
+        if (i < n16) dst[i] = xv[u];
+        if (i < E) s.slot[i] = sv[u];
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t tag = static_cast<uint32_t>(s.misc[1]);
+  const int gwave = wave * a.nb + blockIdx.x;
+  auto put_h = [&](size_t row, int r, float v) { a.h[row * a.hs + r] = v; };
+
+  // ---- phase R
+  for (int task = r_task0; task < router_tasks; task += nwaves * kRouterRowsPerWave) {
+    if (task != r_task0) load_router_rows(task);
+#pragma unroll
+    for (int j = 0; j < kRouterRowsPerWave; ++j) {
+      if (task + j >= router_tasks) break;
+      const bool active = ee[j] >= 0;
+      float r[kSegCodes];
+      act_raw_f32<ACT>(rw[j], r);
+      for (int t = 0; t < T; ++t) {
+        float acc = 0.f;
+        if (active) {
+          float v[kSegCodes];
+          load_act_seg<ACT>(s.x + t * xrow, rlh.seg0, v);
+#pragma unroll
+          for (int c = 0; c < kSegCodes; ++c) acc = fmaf(v[c], r[c], acc);
+        }
+        acc = group_sum(acc, rlh.width);
+        if (active)   // every lane of the row holds the sum: each stores some of the copies
+          for (int rep = lane % rlh.width; rep < kFusedReplicas; rep += rlh.width)
+            store_tagged(a.lg + (static_cast<size_t>(rep) * T + t) * E + ee[j], acc, tag);
+      }
+    }
+  }
+  for (int task = s_task0; task < sh_tasks; task += sh_blocks * kWaves) {
+    if (task != s_task0) load_shared_row(task);
+    const int rr = task * rlh.rpp + rlh.sub_row;
+    const bool ok = rr < a.SI;
+    if constexpr (kDot2) {
+      const QPairs pg = qpairs_bf16(scg), pu = qpairs_bf16(scu);
+      for (int t = 0; t < T; ++t) {
+        ActRaw<kBF16> xr;
+        load_lds_act_bf16(s.x + t * xrow, rlh.seg0, xr);
+        const float xs = xsum_bf16(xr);
+        float accg = 0.f, accu = 0.f;
+        accg += seg_value_d2(raw_value<SB>(ssg), raw_value<SB>(sbg), dot2_seg(pg, xr), xs);
+        accu += seg_value_d2(raw_value<SB>(ssu), raw_value<SB>(sbu), dot2_seg(pu, xr), xs);
+        float g, u;
+        gu_sums(accg, accu, rlh.width, g, u);
+        if (ok && (lane % rlh.width) == 0) put_h(static_cast<size_t>(T) * k + t, rr, silu(g) * u);
+      }
+    } else {
+      for (int t = 0; t < T; ++t) {
+        float v[1][kSegCodes];
+        load_act_seg<ACT>(s.x + t * xrow, rlh.seg0, v[0]);
+        const float xs = seg_sum(v[0]);
+        float qg[1], qu[1];
+        seg_qdot_nt<BITS, 1>(scg, v, qg);
+        seg_qdot_nt<BITS, 1>(scu, v, qu);
+        float accg = 0.f, accu = 0.f;
+        accg += seg_value(raw_value<SB>(ssg), raw_value<SB>(sbg), qg[0], xs);
+        accu += seg_value(raw_value<SB>(ssu), raw_value<SB>(sbu), qu[0], xs);
+        float g, u;
+        gu_sums(accg, accu, rlh.width, g, u);
+        if (ok && (lane % rlh.width) == 0) put_h(static_cast<size_t>(T) * k + t, rr, silu(g) * u);
+      }
+    }
+  }
+  // sigmoid(g . x_t) for launch B on block 0
+  if (blockIdx.x == 0 && wave == kWaves - 1) {
+    for (int t = 0; t < T; ++t) {
+      const float g = shared_gate<ACT>(s.x + t * xrow, a.shared + a.shared_stride, H, lane);
+      if (lane == 0) a.sig[t] = g;
+    }
+  }
+
+  // ---- phase K: gather all logits (each word checked against this call's
+  // tag, re-read until every one has arrived), top-k, dispatch
+  const int rep = blockIdx.x % kFusedReplicas;
+  for (;;) {
+    int missing = 0;
+    for (int i = tid; i < T * E; i += kThreads) {
+      const uint64_t w = load_tagged(a.lg + static_cast<size_t>(rep) * T * E + i);
+      if (static_cast<uint32_t>(w >> 32) != tag) missing = 1;
+      else s.lg[i] = __uint_as_float(static_cast<uint32_t>(w));
+    }
+    if (!__syncthreads_or(missing)) break;
+    if (++spins > a.spin_limit) { timed_out = true; break; }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  for (int t = wave; t < T; t += kWaves)
+    topk_wave(s.lg + static_cast<size_t>(t) * E, E, k, lane, s.cand + wave * kCandMax, s.ids + t * k,
+              s.vals + t * k);
+  if (T == 1) {
+    // one token: its k experts are distinct; order them by id with a rank count
+    if (wave == 0) {
+      int e = lane < k ? s.ids[lane] : 0x7fffffff;
+      e = e >= 0 && e < E ? e : 0;
+      int r = 0;
+      for (int j = 0; j < k; ++j) r += s.ids[j] < e ? 1 : 0;
+      if (lane < k) {
+        s.uniq[r] = e;
+        s.pidx[r] = lane;
+        s.uranks[r] = static_cast<uint64_t>(lane + 1);
+      }
+      if (lane == 0) s.misc[0] = k;
+    }
+    __syncthreads();
+  } else {
+    for (int e = tid; e < E; e += kThreads) s.umap[e] = -1;
+    __syncthreads();
+    for (int p = tid; p < T * k; p += kThreads) {
+      const int e = s.ids[p];
+      s.ids[p] = e >= 0 && e < E ? e : 0;           // ids come from [0, E) by construction
+      s.umap[s.ids[p]] = 0;                         // mark
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int base = 0;
+      for (int c0 = 0; c0 < E; c0 += kWave) {
+        const int e = c0 + lane;
+        const bool used = e < E && s.umap[e] == 0;
+        const uint64_t m = __ballot(used);
+        const int pos = base + __popcll(m & lane_mask_lt(lane));
+        if (used) { s.uniq[pos] = e; s.umap[e] = pos; }
+        base += __popcll(m);
+      }
+      if (lane == 0) s.misc[0] = base;
+    }
+    __syncthreads();
+    const int Ud = s.misc[0];
+    for (int i = tid; i < Ud * T; i += kThreads) s.pidx[i] = -1;
+    __syncthreads();
+    for (int p = tid; p < T * k; p += kThreads) s.pidx[s.umap[s.ids[p]] * T + p / k] = p % k;
+    __syncthreads();
+    // phase-G work per distinct expert: a row's loads plus one dot per token
+    // that uses it; prefix sums so that every wave takes an equal share
+    if (wave == 0) {
+      int carry = 0;
+      for (int u0 = 0; u0 < Ud; u0 += kWave) {
+        const int u = u0 + lane;
+        int c = 0;
+        if (u < Ud) {
+          c = kRowCost;
+          uint64_t rk = 0;
+          for (int t = 0; t < T; ++t) {
+            const int i = s.pidx[u * T + t];
+            c += i >= 0 ? 1 : 0;
+            rk |= static_cast<uint64_t>(i + 1) << (8 * t);
+          }
+          s.uranks[u] = rk;
+        }
+        int incl = c;
+#pragma unroll
+        for (int m = 1; m < kWave; m <<= 1) {
+          const int o = __shfl_up(incl, m, kWave);
+          if (lane >= m) incl += o;
+        }
+        if (u < Ud) s.ucost[u + 1] = carry + incl;
+        carry += __shfl(incl, kWave - 1, kWave);
+      }
+      if (lane == 0) s.ucost[0] = 0;
+    }
+    __syncthreads();
+  }
+  const int U = s.misc[0];
+  if (blockIdx.x == 0) {
+    // routing record for launch B (and the optional outputs)
+    for (int p = tid; p < T * k; p += kThreads) {
+      a.wts[p] = s.vals[p];
+      if (a.ids_out) a.ids_out[p] = s.ids[p];
+      if (a.wts_out) a.wts_out[p] = s.vals[p];
+    }
+    for (int i = tid; i < U * T; i += kThreads) a.pidx[i] = s.pidx[i];
+    for (int i = tid; i < U; i += kThreads) {
+      a.uniq[i] = s.uniq[i];
+      a.uoff[i] = s.slot[s.uniq[i]];
+    }
+    if (tid == 0) *a.ucount = U;
+  }
+  // ---- phase G: routed gate/up rows, flattened over (expert, row group)
+  {
+    const Planes pl = planes_of(H, a.I, BITS, SB);
+    const int64_t row_bytes = static_cast<int64_t>(H) * BITS / 8;
+    const int seg_bytes = kSegCodes * BITS / 8;
+    const int gpr = H / 64;
+    const int groups_per_expert = a.I / rlh.rpp;
+    const int total = U * groups_per_expert;
+    int g_lo, g_hi;
+    if (T == 1) {
+      // every unit costs the same
+      const int per_wave = (total + nwaves - 1) / nwaves;
+      g_lo = min(total, gwave * per_wave);
+      g_hi = min(total, g_lo + per_wave);
+    } else {
+      // equal shares of the work: unit (u, group) costs ucost[u + 1] - ucost[u]
+      // over groups_per_expert; a share starts at the first unit that starts
+      // at or after its cost position
+      const int64_t W = static_cast<int64_t>(s.ucost[U]) * groups_per_expert;
+      auto unit_at = [&](int64_t x) {
+        if (x >= W) return total;
+        int lo = 0, hi = U - 1;   // last u with ucost[u] * gpe <= x
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (static_cast<int64_t>(s.ucost[mid]) * groups_per_expert <= x) lo = mid;
+          else hi = mid - 1;
+        }
+        const int64_t c = s.ucost[lo + 1] - s.ucost[lo];   // cost of one unit of expert lo
+        const int64_t i = (x - static_cast<int64_t>(s.ucost[lo]) * groups_per_expert + c - 1) / c;
+        return lo * groups_per_expert + static_cast<int>(i);
+      };
+      g_lo = unit_at(W * gwave / nwaves);
+      g_hi = unit_at(W * (gwave + 1) / nwaves);
+    }
+    // per-token segment sums of x (the lane's segment is the same in every
+    // row), once per wave, in a wave-private table in the logits area, which
+    // nothing reads after top-k
+    lds_f32* const xs_tab = (lds_f32*)(s.lg) + wave * T * kWave;
+    if constexpr (kDot2) {
+      for (int t = 0; t < T; ++t) {
+        ActRaw<kBF16> xr;
+        load_lds_act_bf16(s.x + t * xrow, rlh.seg0, xr);
+        xs_tab[t * kWave + lane] = xsum_bf16(xr);
+      }
+    }
+    // Rows go in batches of kBatch; the next batch's loads are requested
+    // before the current batch is computed (two register sets, alternating).
+    constexpr int kBatch = 4;
+    struct Batch {
+      Seg<BITS> cg[kBatch], cu[kBatch];
+      uint32_t sg[kBatch], su[kBatch], bg[kBatch], bu[kBatch];
+      int uu[kBatch], rr[kBatch];
+      bool vv[kBatch];
+    };
+    // every row of a batch is requested before any is used: no branches on
+    // the loads (a row past the end repeats the first one, an unusable blob
+    // reads blob 0; both are masked at the store) and raw scale bits
+    auto load_batch = [&](Batch& B, int g0) {
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int g = g0 + b;
+        const bool live = g < g_hi;
+        const int gc = live ? g : g_lo;
+        const int u = gc / groups_per_expert;
+        const int r = (gc % groups_per_expert) * rlh.rpp + rlh.sub_row;
+        const int64_t off = s.slot[s.uniq[u]];
+        const bool valid = slot_ok(off, pl.blob, a.pool_bytes);
+        B.uu[b] = live ? u : -1;
+        B.rr[b] = r;
+        B.vv[b] = valid;
+        if (live && !valid && lane == 0) raise_error(a.ctrl, kErrRange);
+        const uint8_t* blob = a.pool + (valid ? off : 0);
+        const int64_t qo = r * row_bytes + static_cast<int64_t>(rlh.seg0) * seg_bytes;
+        B.cg[b] = load_codes<BITS>(blob + qo);
+        B.cu[b] = load_codes<BITS>(blob + pl.q + qo);
+        const size_t si = static_cast<size_t>(r) * gpr + rlh.seg0 / 2;
+        B.sg[b] = load_raw<SB>(blob + 3 * pl.q, si);
+        B.su[b] = load_raw<SB>(blob + 3 * pl.q + pl.s, si);
+        B.bg[b] = load_raw<SB>(blob + 3 * pl.q + 3 * pl.s, si);
+        B.bu[b] = load_raw<SB>(blob + 3 * pl.q + 4 * pl.s, si);
+      }
+    };
+    auto compute_batch = [&](const Batch& B, auto wtag) {
+      // row sums: width known at compile time for full-wave rows
+      constexpr int W = decltype(wtag)::value;
+      if constexpr (kDot2) {
+        // rows outer: each row's codes become bf16 pairs once for all its
+        // tokens; the tokens that use the row come from its packed ranks
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+          if (B.uu[b] < 0) continue;
+          const uint64_t rkv = s.uranks[B.uu[b]];
+          uint64_t rk = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rkv >> 32))) << 32) |
+                        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rkv)));
+          const QPairs pg = qpairs_bf16(B.cg[b]), pu = qpairs_bf16(B.cu[b]);
+          const float sgv = raw_value<SB>(B.sg[b]), bgv = raw_value<SB>(B.bg[b]);
+          const float suv = raw_value<SB>(B.su[b]), buv = raw_value<SB>(B.bu[b]);
+          while (rk != 0) {
+            const int sh = __builtin_ctzll(rk) & ~7;
+            const int t = sh >> 3;
+            const int i = static_cast<int>((rk >> sh) & 0xffu) - 1;
+            rk &= ~(0xffull << sh);
+            ActRaw<kBF16> xr;
+            load_lds_act_bf16(s.x + t * xrow, rlh.seg0, xr);
+            const float xs = xs_tab[t * kWave + lane];
+            float accg = 0.f, accu = 0.f;
+            accg += seg_value_d2(sgv, bgv, dot2_seg(pg, xr), xs);
+            accu += seg_value_d2(suv, buv, dot2_seg(pu, xr), xs);
+            float g, u;
+            gu_sums_w<W>(accg, accu, rlh.width, g, u);
+            if ((lane % rlh.width) == 0)
+              put_h(static_cast<size_t>(t) * k + i, B.rr[b], B.vv[b] ? silu(g) * u : 0.f);
+          }
+        }
+      } else {
+        for (int t = 0; t < T; ++t) {
+          float v[1][kSegCodes];
+          load_act_seg<ACT>(s.x + t * xrow, rlh.seg0, v[0]);
+          const float xs = seg_sum(v[0]);
+#pragma unroll
+          for (int b = 0; b < kBatch; ++b) {
+            if (B.uu[b] < 0) continue;
+            const int i = s.pidx[B.uu[b] * T + t];
+            if (i < 0) continue;                      // token t does not use this expert
+            float qg[1], qu[1];
+            seg_qdot_nt<BITS, 1>(B.cg[b], v, qg);
+            seg_qdot_nt<BITS, 1>(B.cu[b], v, qu);
+            float accg = 0.f, accu = 0.f;
+            accg += seg_value(raw_value<SB>(B.sg[b]), raw_value<SB>(B.bg[b]), qg[0], xs);
+            accu += seg_value(raw_value<SB>(B.su[b]), raw_value<SB>(B.bu[b]), qu[0], xs);
+            float g, u;
+            gu_sums_w<W>(accg, accu, rlh.width, g, u);
+            if ((lane % rlh.width) == 0)
+              put_h(static_cast<size_t>(t) * k + i, B.rr[b], B.vv[b] ? silu(g) * u : 0.f);
+          }
+        }
+      }
+    };
+    auto run = [&](auto wtag) {
+      Batch b0, b1;
+      load_batch(b0, g_lo);
+      for (int g0 = g_lo; g0 < g_hi; g0 += 2 * kBatch) {
+        if (g0 + kBatch < g_hi) load_batch(b1, g0 + kBatch);
+        compute_batch(b0, wtag);
+        if (g0 + kBatch >= g_hi) break;
+        if (g0 + 2 * kBatch < g_hi) load_batch(b0, g0 + 2 * kBatch);
+        compute_batch(b1, wtag);
+      }
+    };
+    if (g_lo < g_hi) {
+      if (rlh.width == kWave) run(IntC<kWave>{});
+      else run(IntC<0>{});
+    }
+  }
+  if (timed_out && lane == 0) raise_error(a.ctrl, kErrTimeout);
+}
+
+// ---------------------------------------------------------------------------
+// Launch B: one block per (slice of rb output rows, token): the slice's down
+// rows of the token's k experts and of the shared expert, then the ordered
+// combine.  A block's partial sums are all its own, and the token's k + 1 h
+// rows are staged in LDS once.
+template <int BITS, int SB, int OUT>
+__global__ __launch_bounds__(kThreads) void k_decode_b(FusedArgs a) {
+  extern __shared__ __align__(16) uint8_t lds_raw[];
+  const LdsB s = carve_b(lds_raw, a);
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform: lets the compiler use scalar math
+  const int T = a.T, k = a.k;
+  // Retire launch A's tag: every block of A has finished, so none can still
+  // read its epoch counter; each thread advances its own counters.
+  if (blockIdx.x == 0)
+    for (int j = tid; j < kFusedMaxBlocks; j += kThreads) a.epochs[j] = a.epochs[j] + 1u;
+  int slice, t;
+  if (!unit_of(a.nslice * T, T, &slice, &t)) return;
+  // the token's routing: blob offsets by rank, weights, gate; every element
+  // requested before any is stored (a rank that no distinct expert claims
+  // keeps offset -1, which slot_ok rejects)
+  if (tid < k) s.poff[tid] = -1;
+  __syncthreads();
+  {
+    const int U = *a.ucount;
+    const int n = a.umax > k ? a.umax : k;
+    for (int u0 = 0; u0 < n; u0 += kThreads) {
+      const int u = u0 + tid;
+      const int uc = u < a.umax ? u : 0;
+      const int32_t i = __builtin_nontemporal_load(a.pidx + uc * T + t);
+      const int64_t off = __builtin_nontemporal_load(a.uoff + uc);
+      const float wt = __builtin_nontemporal_load(a.wts + t * k + (u < k ? u : 0));
+      const float sg = __builtin_nontemporal_load(a.sig + t);
+      const bool claim = u < a.umax && u < U && i >= 0 && i < k;
+      if (claim) s.poff[i] = off;
+      if (u < k) s.wts[u] = wt;
+      if (u == 0) s.sig[0] = sg;
+    }
+  }
+  __syncthreads();
+  DOWN_SETUP(BITS, SB, a, slice, lane);
+  DownTask<BITS> dt[kMaxDownPerWave];
+  for (int base = 0; base < ntask; base += kWaves * kMaxDownPerWave) {
+    // codes of this round's tasks, all requested before any compute
+    issue_down_round<BITS, SB>(dt, base, ntask, dc, lo, rli, rls, row_lo, a, s, wave);
+    // the token's h rows into LDS once, while the codes above are in flight
+    if (s.h && base == 0) stage_h_plain(a, s, T, t, tid);
+    compute_down_round<BITS, SB>(dt, rli, rls, a, s, T, t, lane);
+  }
+  __syncthreads();
+  combine_unit<OUT>(a, s, row_lo, t, tid);
 }
 
 size_t lds_bytes_a(int T, int H, int E, int k, int umax, int act_sz) {
@@ -875,9 +935,7 @@ size_t lds_bytes_b(int k, int rb, int hs) {
 template <int BITS, int SB, int ACT, int OUT>
 static int launch_variant(const FusedArgs& a, const FusedPlan& p, hipStream_t stream) {
   launch_kernel(k_decode_a<BITS, SB, ACT>, dim3(p.nb), dim3(kThreads), p.lds, stream, a);
-  FusedArgs b = a;
-  b.rb = p.rb_b;
-  launch_kernel(k_decode_b<BITS, SB, OUT>, dim3(p.nb_b), dim3(kThreads), p.lds_b, stream, b);
+  launch_kernel(k_decode_b<BITS, SB, OUT>, dim3(p.nb_b), dim3(kThreads), p.lds_b, stream, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
@@ -919,6 +977,7 @@ int fused_plan(const moe_desc& d, int T, FusedPlan* plan) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MOE_ENODEV;
   const int act_sz = d.act_dtype == kF32 ? 4 : 2;
   const int umax = T * d.top_k < d.n_experts ? T * d.top_k : d.n_experts;
+  const int hs = d.inter > d.shared_inter ? d.inter : d.shared_inter;
   const size_t lds = lds_bytes_a(T, d.hidden, d.n_experts, d.top_k, umax, act_sz);
   if (lds > 64 * 1024) return MOE_EINVAL;
   // launch A: two resident blocks per CU when they fit, else one
@@ -937,7 +996,7 @@ int fused_plan(const moe_desc& d, int T, FusedPlan* plan) {
       plan->rb_b = rb1 * ((T + 1) / 2);
       plan->nslice = (d.hidden + plan->rb_b - 1) / plan->rb_b;
       plan->nb_b = (plan->nslice * T + kXcds - 1) / kXcds * kXcds;
-      plan->lds_b = lds_bytes_b(d.top_k, plan->rb_b, d.inter > d.shared_inter ? d.inter : d.shared_inter);
+      plan->lds_b = lds_bytes_b(d.top_k, plan->rb_b, hs);
       return MOE_OK;
     }
   }
@@ -976,6 +1035,7 @@ int launch_decode_fused(const Call& c, const FusedPlan& plan) {
   a.nb = plan.nb;
   a.rb = plan.rb_b;
   a.nslice = plan.nslice;
+  a.epochs = reinterpret_cast<uint32_t*>(c.ws + c.L.f_epoch);
   a.umax = plan.umax;
   a.act_sz = d.act_dtype == kF32 ? 4 : 2;
   a.spin_limit = 1u << 20;

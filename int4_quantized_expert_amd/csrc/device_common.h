@@ -177,6 +177,27 @@ __device__ __forceinline__ Seg<BITS> load_codes(const uint8_t* p) {
   return s;
 }
 
+// The same loads through an address known to be global memory (a pointer
+// rebuilt from integers, e.g. after readfirstlane, is otherwise generic and
+// compiles to FLAT loads, which also count against the LDS wait counter).
+typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) const uint32_t g_u32;
+typedef __attribute__((address_space(1))) const uint16_t g_u16;
+
+template <int BITS>
+__device__ __forceinline__ Seg<BITS> load_codes_g(uint64_t addr) {
+  Seg<BITS> s;
+#pragma unroll
+  for (int i = 0; i < BITS / 4; ++i) s.w[i] = __builtin_nontemporal_load(reinterpret_cast<g_u32x4*>(addr + 16 * i));
+  return s;
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t load_raw_g(uint64_t addr) {
+  if constexpr (DT == kF32) return *reinterpret_cast<g_u32*>(addr);
+  else return *reinterpret_cast<g_u16*>(addr);
+}
+
 __device__ __forceinline__ float seg_value(float s, float b, float qx, float xs) {
   return fmaf(s, qx, b * xs);
 }

@@ -26,7 +26,8 @@ struct FusedArgs {
   int32_t* uniq;        // [umax] distinct experts, ascending id
   int64_t* uoff;        // [umax] their blob offsets
   int32_t* pidx;        // [umax, T] rank of expert u for token t, or -1
-  uint32_t* ctrl;       // [0] error flags, [1] epoch
+  uint32_t* ctrl;       // [0] error flags
+  uint32_t* epochs;     // [kFusedMaxBlocks] per-block call counters (tag = counter + 1)
   int64_t pool_bytes;
   int64_t shared_stride;
   int T, H, E, k, I, SI, hs;

@@ -14,9 +14,13 @@ namespace moe {
 constexpr int kFusedMaxBlocks = 2048;
 
 // Byte layout of the caller's workspace for calls with up to T_max tokens.
-// Every region starts on a 256-byte boundary.
+// Every region starts on a 256-byte boundary.  The control words and the
+// two-launch decode's tagged logits come first and have the same offsets for
+// every T (sized for kFusedMaxT tokens), so that calls with different token
+// counts on one workspace agree on the epoch counters and never read another
+// region's bytes as a tagged word.
 struct WsLayout {
-  size_t ctrl;       // uint32 control words: [0] error flags, [1] fused-path epoch
+  size_t ctrl;       // uint32 control words: [0] error flags, then the epoch counters
   size_t logits;     // [T, E] float32 router logits
   size_t ids;        // [T, k] int32 chosen experts
   size_t wts;        // [T, k] float32 renormalised weights
@@ -27,9 +31,10 @@ struct WsLayout {
   size_t plist;      // [T k] int32 pair indices (t * k + i) grouped by expert
   size_t h;          // [T k + T, max(I, SI)] float32 SwiGLU activations
   size_t partial;    // [T k + T, H] float32 per-pair down projections
-  size_t f_lg;       // two-launch path: [kFusedReplicas][T, E] tagged logits (uint64)
+  size_t f_lg;       // two-launch path: [kFusedReplicas][Tf, E] tagged logits (uint64), Tf = kFusedMaxT
   size_t f_uoff;     // two-launch path: [min(T k, E)] int64 blob offsets of the distinct experts
   size_t f_pidx;     // two-launch path: [min(T k, E), T] int32 rank of expert u for token t
+  size_t f_epoch;    // two-launch path: [kFusedMaxBlocks] uint32 per-block call counters (inside ctrl)
   size_t p_x16;      // prefill: [T, H] float16 activations in MFMA k order
   size_t p_meta;     // prefill: int32 [0] number of expert tiles
   size_t p_tstart;   // prefill: [min(T k, E) + 2] int32 first tile of each distinct expert, then of the shared one
@@ -52,7 +57,10 @@ inline WsLayout ws_layout(const moe_desc& d, int32_t T) {
   const int32_t hs = d.inter > d.shared_inter ? d.inter : d.shared_inter;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes > 0 ? bytes : 1); return at; };
-  L.ctrl = take(256);
+  L.ctrl = take(256 + static_cast<size_t>(kFusedMaxBlocks) * 4);
+  L.f_epoch = L.ctrl + 256;
+  const size_t Tf = kFusedMaxT;
+  L.f_lg = take(static_cast<size_t>(kFusedReplicas) * Tf * d.n_experts * 8);
   L.logits = take(static_cast<size_t>(T) * d.n_experts * 4);
   L.ids = take(Tk * 4);
   L.wts = take(Tk * 4);
@@ -63,7 +71,6 @@ inline WsLayout ws_layout(const moe_desc& d, int32_t T) {
   L.plist = take(Tk * 4);
   L.h = take((Tk + T) * static_cast<size_t>(hs) * 4);
   L.partial = take((Tk + T) * static_cast<size_t>(d.hidden) * 4);
-  L.f_lg = take(static_cast<size_t>(kFusedReplicas) * T * d.n_experts * 8);
   L.f_uoff = take(static_cast<size_t>(umax) * 8);
   L.f_pidx = take(static_cast<size_t>(umax) * T * 4);
   const size_t chunks = (Tk + kPrefillChunk - 1) / kPrefillChunk + (static_cast<size_t>(T) + kPrefillChunk - 1) / kPrefillChunk;
