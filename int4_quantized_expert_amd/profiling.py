@@ -10,9 +10,11 @@ The summary is a small markdown file with one JSON block.  It carries a digest
 of the kernel sources, so a reader can tell whether the counters still describe
 the code as it stands (bench.py reports `traffic` only when they do).
 
-    python -m int4_quantized_expert_amd.profiling --fetch F.csv --write W.csv \\
+    python -m int4_quantized_expert_amd.profiling traffic --fetch F.csv --write W.csv \\
         --copy-bytes 268435456 --workload 80b_stack_decode --tokens 1 --out profiles/X.md \\
-        --command "the rocprofv3 command line"
+        --command "the rocprofv3 command lines"
+    python -m int4_quantized_expert_amd.profiling kernels --stats S.csv --title "..." \\
+        --out profiles/Y.md --command "the rocprofv3 command line"
 """
 
 from __future__ import annotations
@@ -45,9 +47,9 @@ def source_digest() -> str:
 
 def short_name(kernel: str) -> str:
     """`void moe::(anonymous namespace)::k_decode_a<4, 1, 1>(moe::FusedArgs)` -> `k_decode_a<4, 1, 1>`."""
-    name = kernel.split("(moe::")[0].split("(anonymous namespace)::")[-1]
-    name = re.sub(r"^void ", "", name).strip()
-    return name.split("(")[0] if "<" not in name else name
+    name = re.sub(r"^void ", "", kernel.replace("(anonymous namespace)::", "")).strip()
+    m = re.match(r"[\w:]*?(\w+(?:<[^()]*>)?)\s*(?:\(|$)", name)
+    return m.group(1) if m else name
 
 
 def read_counter(path: str) -> dict[str, list[float]]:
@@ -120,17 +122,53 @@ def load_traffic(profiles_dir: str, workload: str, tokens: int) -> dict | None:
     return None
 
 
+def kernel_stats(stats_csv: str) -> list[dict]:
+    """Rows of a rocprofv3 --stats kernel summary (durations in microseconds)."""
+    rows = []
+    with open(stats_csv) as fh:
+        for r in csv.DictReader(fh):
+            rows.append({"kernel": short_name(r["Name"]), "calls": int(r["Calls"]),
+                         "avg_us": float(r["AverageNs"]) / 1e3, "min_us": float(r["MinNs"]) / 1e3,
+                         "max_us": float(r["MaxNs"]) / 1e3, "share": float(r["Percentage"])})
+    return rows
+
+
+def write_kernel_summary(out: str, rows: list[dict], title: str, command: str, notes: str) -> None:
+    lines = [f"# {title}\n\n",
+             "Command (from the repository root; rocprofv3 run from /tmp with TMPDIR=/tmp):\n\n",
+             "```\n" + command.strip() + "\n```\n\n"]
+    if notes:
+        lines.append(notes.strip() + "\n\n")
+    lines += ["| Kernel | Calls | Avg us | Min us | Max us | Share |\n", "|---|---|---|---|---|---|\n"]
+    for r in rows:
+        lines.append(f"| {r['kernel']} | {r['calls']} | {r['avg_us']:.2f} | {r['min_us']:.2f} | {r['max_us']:.2f} | "
+                     f"{r['share']:.1f}% |\n")
+    with open(out, "w") as fh:
+        fh.writelines(lines)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
-    ap.add_argument("--copy-bytes", type=int, default=256 << 20)
-    ap.add_argument("--workload", required=True)
-    ap.add_argument("--tokens", type=int, required=True)
-    ap.add_argument("--out", required=True)
-    ap.add_argument("--command", required=True)
+    sub = ap.add_subparsers(dest="what")
+    t = sub.add_parser("traffic", help="FETCH_SIZE / WRITE_SIZE passes -> bytes per launch")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-bytes", type=int, default=256 << 20)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--tokens", type=int, required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--command", required=True)
+    k = sub.add_parser("kernels", help="rocprofv3 --stats kernel summary -> markdown table")
+    k.add_argument("--stats", required=True)
+    k.add_argument("--title", required=True)
+    k.add_argument("--out", required=True)
+    k.add_argument("--command", required=True)
+    k.add_argument("--notes", default="")
     a = ap.parse_args()
-    write_summary(a.out, traffic_table(a.fetch, a.write, a.copy_bytes), a.workload, a.tokens, a.command)
+    if a.what == "kernels":
+        write_kernel_summary(a.out, kernel_stats(a.stats), a.title, a.command, a.notes)
+    else:
+        write_summary(a.out, traffic_table(a.fetch, a.write, a.copy_bytes), a.workload, a.tokens, a.command)
 
 
 if __name__ == "__main__":
