@@ -49,7 +49,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxDownPerWave = 4;    // down tasks per wave per round in launch B
-constexpr int kRouterRowsPerWave = 2; // router row groups per wave in phase R
+constexpr int kRouterRowsPerWave = 1; // router row groups per wave in phase R
 constexpr int kRowCost = 2;           // phase-G cost of a row's loads, in per-token dots
 
 template <int V>
