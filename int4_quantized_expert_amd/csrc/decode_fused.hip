@@ -46,8 +46,10 @@ namespace moe {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;             // launch B blocks
 constexpr int kWaves = kThreads / kWave;
+constexpr int kThreadsA = 512;            // launch A blocks: one per CU (fewer blocks start sooner)
+constexpr int kWavesA = kThreadsA / kWave;
 constexpr int kMaxDownPerWave = 4;    // down tasks per wave per round in launch B
 constexpr int kRouterRowsPerWave = 1; // router row groups per wave in phase R
 constexpr int kRowCost = 2;           // phase-G cost of a row's loads, in per-token dots
@@ -69,7 +71,7 @@ __device__ __forceinline__ uint64_t load_tagged(const uint64_t* p) {
 // The logits area also holds, after top-k, one float per (wave, token, lane)
 // for phase G.
 __host__ __device__ inline size_t lg_floats(int T, int E) {
-  const size_t lg = static_cast<size_t>(T) * E, xs = static_cast<size_t>(kWaves) * T * kWave;
+  const size_t lg = static_cast<size_t>(T) * E, xs = static_cast<size_t>(kWavesA) * T * kWave;
   return lg > xs ? lg : xs;
 }
 
@@ -84,7 +86,7 @@ struct LdsA {
   int32_t* pidx;     // [umax][T] rank i of the expert for token t, or -1
   int32_t* ucost;    // [umax + 1] phase-G work before distinct expert u (T > 1)
   uint64_t* uranks;  // [umax] byte t: 1 + rank of expert u for token t, 0 if unused
-  uint64_t* cand;    // [kWaves][kCandMax] packed candidates
+  uint64_t* cand;    // [kWavesA][kCandMax] packed candidates
   int32_t* misc;     // [0] U, [1] tag
 };
 
@@ -102,7 +104,7 @@ __device__ inline LdsA carve_a(uint8_t* base, const FusedArgs& a) {
   s.pidx = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.umax) * a.T * 4));
   s.ucost = reinterpret_cast<int32_t*>(take(static_cast<size_t>(a.umax + 1) * 4));
   s.uranks = reinterpret_cast<uint64_t*>(take(static_cast<size_t>(a.umax) * 8));
-  s.cand = reinterpret_cast<uint64_t*>(take(kWaves * kCandMax * 8));
+  s.cand = reinterpret_cast<uint64_t*>(take(kWavesA * kCandMax * 8));
   s.misc = reinterpret_cast<int32_t*>(take(16 * 4));
   return s;
 }
@@ -425,7 +427,7 @@ __device__ __forceinline__ float shared_gate(const uint8_t* xrow, const uint8_t*
 // ---------------------------------------------------------------------------
 // Launch A: phases R, K, G.
 template <int BITS, int SB, int ACT>
-__global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
+__global__ __launch_bounds__(kThreadsA) void k_decode_a(FusedArgs a) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   const LdsA s = carve_a(lds_raw, a);
   const int tid = threadIdx.x;
@@ -447,13 +449,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
   // spread over the machine).  The first task's weights are requested before
   // the x / slot-table copy below, so the two memory round trips overlap.
   const size_t xrow = static_cast<size_t>(H) * a.act_sz;
-  const int nwaves = a.nb * kWaves;
+  const int nwaves = a.nb * kWavesA;
   const RowLanes rlh = row_lanes(H, lane);
   const int router_tasks = (E + rlh.rpp - 1) / rlh.rpp;
   const int router_waves = (router_tasks + kRouterRowsPerWave - 1) / kRouterRowsPerWave;
-  const int router_blocks = min(a.nb, (router_waves + kWaves - 1) / kWaves);
+  const int router_blocks = min(a.nb, (router_waves + kWavesA - 1) / kWavesA);
   const int sh_tasks = (a.SI + rlh.rpp - 1) / rlh.rpp;
-  const int bwave = blockIdx.x * kWaves + wave;
+  const int bwave = blockIdx.x * kWavesA + wave;
   const int r_task0 = bwave * kRouterRowsPerWave;
   ActRaw<ACT> rw[kRouterRowsPerWave];
   int ee[kRouterRowsPerWave];
@@ -495,18 +497,18 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
     const u32x4* src = static_cast<const u32x4*>(a.x);
     u32x4* dst = reinterpret_cast<u32x4*>(s.x);
     const int n = n16 > E ? n16 : E;
-    for (int i0 = 0; i0 < n; i0 += 2 * kThreads) {
+    for (int i0 = 0; i0 < n; i0 += 2 * kThreadsA) {
       u32x4 xv[2];
       int64_t sv[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int i = i0 + u * kThreads + tid;
+        const int i = i0 + u * kThreadsA + tid;
         xv[u] = src[i < n16 ? i : 0];
         sv[u] = a.slot_table[i < E ? i : 0];
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int i = i0 + u * kThreads + tid;
+        const int i = i0 + u * kThreadsA + tid;
         if (i < n16) dst[i] = xv[u];
         if (i < E) s.slot[i] = sv[u];
       }
@@ -541,7 +543,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
       }
     }
   }
-  for (int task = s_task0; task < sh_tasks; task += sh_blocks * kWaves) {
+  for (int task = s_task0; task < sh_tasks; task += sh_blocks * kWavesA) {
     if (task != s_task0) load_shared_row(task);
     const int rr = task * rlh.rpp + rlh.sub_row;
     const bool ok = rr < a.SI;
@@ -576,7 +578,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
     }
   }
   // sigmoid(g . x_t) for launch B on block 0
-  if (blockIdx.x == 0 && wave == kWaves - 1) {
+  if (blockIdx.x == 0 && wave == kWavesA - 1) {
     for (int t = 0; t < T; ++t) {
       const float g = shared_gate<ACT>(s.x + t * xrow, a.shared + a.shared_stride, H, lane);
       if (lane == 0) a.sig[t] = g;
@@ -588,7 +590,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
   const int rep = blockIdx.x % kFusedReplicas;
   for (;;) {
     int missing = 0;
-    for (int i = tid; i < T * E; i += kThreads) {
+    for (int i = tid; i < T * E; i += kThreadsA) {
       const uint64_t w = load_tagged(a.lg + static_cast<size_t>(rep) * T * E + i);
       if (static_cast<uint32_t>(w >> 32) != tag) missing = 1;
       else s.lg[i] = __uint_as_float(static_cast<uint32_t>(w));
@@ -597,7 +599,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
     if (++spins > a.spin_limit) { timed_out = true; break; }
     __builtin_amdgcn_s_sleep(2);
   }
-  for (int t = wave; t < T; t += kWaves)
+  for (int t = wave; t < T; t += kWavesA)
     topk_wave(s.lg + static_cast<size_t>(t) * E, E, k, lane, s.cand + wave * kCandMax, s.ids + t * k,
               s.vals + t * k);
   if (T == 1) {
@@ -616,9 +618,9 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
     }
     __syncthreads();
   } else {
-    for (int e = tid; e < E; e += kThreads) s.umap[e] = -1;
+    for (int e = tid; e < E; e += kThreadsA) s.umap[e] = -1;
     __syncthreads();
-    for (int p = tid; p < T * k; p += kThreads) {
+    for (int p = tid; p < T * k; p += kThreadsA) {
       const int e = s.ids[p];
       s.ids[p] = e >= 0 && e < E ? e : 0;           // ids come from [0, E) by construction
       s.umap[s.ids[p]] = 0;                         // mark
@@ -638,9 +640,9 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
     }
     __syncthreads();
     const int Ud = s.misc[0];
-    for (int i = tid; i < Ud * T; i += kThreads) s.pidx[i] = -1;
+    for (int i = tid; i < Ud * T; i += kThreadsA) s.pidx[i] = -1;
     __syncthreads();
-    for (int p = tid; p < T * k; p += kThreads) s.pidx[s.umap[s.ids[p]] * T + p / k] = p % k;
+    for (int p = tid; p < T * k; p += kThreadsA) s.pidx[s.umap[s.ids[p]] * T + p / k] = p % k;
     __syncthreads();
     // phase-G work per distinct expert: a row's loads plus one dot per token
     // that uses it; prefix sums so that every wave takes an equal share
@@ -675,13 +677,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_a(FusedArgs a) {
   const int U = s.misc[0];
   if (blockIdx.x == 0) {
     // routing record for launch B (and the optional outputs)
-    for (int p = tid; p < T * k; p += kThreads) {
+    for (int p = tid; p < T * k; p += kThreadsA) {
       a.wts[p] = s.vals[p];
       if (a.ids_out) a.ids_out[p] = s.ids[p];
       if (a.wts_out) a.wts_out[p] = s.vals[p];
     }
-    for (int i = tid; i < U * T; i += kThreads) a.pidx[i] = s.pidx[i];
-    for (int i = tid; i < U; i += kThreads) {
+    for (int i = tid; i < U * T; i += kThreadsA) a.pidx[i] = s.pidx[i];
+    for (int i = tid; i < U; i += kThreadsA) {
       a.uniq[i] = s.uniq[i];
       a.uoff[i] = s.slot[s.uniq[i]];
     }
@@ -911,7 +913,7 @@ size_t lds_bytes_a(int T, int H, int E, int k, int umax, int act_sz) {
   take(static_cast<size_t>(umax) * T * 4);
   take(static_cast<size_t>(umax + 1) * 4);
   take(static_cast<size_t>(umax) * 8);
-  take(kWaves * kCandMax * 8);
+  take(kWavesA * kCandMax * 8);
   take(16 * 4);
   return o;
 }
@@ -934,14 +936,14 @@ size_t lds_bytes_b(int k, int rb, int hs) {
 
 template <int BITS, int SB, int ACT, int OUT>
 static int launch_variant(const FusedArgs& a, const FusedPlan& p, hipStream_t stream) {
-  launch_kernel(k_decode_a<BITS, SB, ACT>, dim3(p.nb), dim3(kThreads), p.lds, stream, a);
+  launch_kernel(k_decode_a<BITS, SB, ACT>, dim3(p.nb), dim3(kThreadsA), p.lds, stream, a);
   launch_kernel(k_decode_b<BITS, SB, OUT>, dim3(p.nb_b), dim3(kThreads), p.lds_b, stream, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 template <int BITS, int SB, int ACT, int OUT>
 static int occupancy_variant(size_t lds, int* blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_decode_a<BITS, SB, ACT>, kThreads, lds) == hipSuccess
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_decode_a<BITS, SB, ACT>, kThreadsA, lds) == hipSuccess
              ? MOE_OK
              : MOE_EHIP;
 }
@@ -980,8 +982,8 @@ int fused_plan(const moe_desc& d, int T, FusedPlan* plan) {
   const int hs = d.inter > d.shared_inter ? d.inter : d.shared_inter;
   const size_t lds = lds_bytes_a(T, d.hidden, d.n_experts, d.top_k, umax, act_sz);
   if (lds > 64 * 1024) return MOE_EINVAL;
-  // launch A: two resident blocks per CU when they fit, else one
-  for (int per_cu = 2; per_cu >= 1; --per_cu) {
+  // launch A: one resident block per CU
+  for (int per_cu = 1; per_cu >= 1; --per_cu) {
     const int nb = cus * per_cu;
     if (nb > kFusedMaxBlocks) continue;
     int fit = 0;
