@@ -46,7 +46,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kThreads = 256;             // launch B blocks
+constexpr int kThreads = 512;             // launch B blocks
 constexpr int kWaves = kThreads / kWave;
 constexpr int kThreadsA = 512;            // launch A blocks: one per CU (fewer blocks start sooner)
 constexpr int kWavesA = kThreadsA / kWave;
@@ -993,8 +993,8 @@ int fused_plan(const moe_desc& d, int T, FusedPlan* plan) {
       plan->lds = lds;
       plan->umax = umax;
       // launch B: one block per (slice, token); slices of a few output rows,
-      // wider as T grows, so that the grid stays at two to four blocks per CU
-      const int rb1 = (d.hidden + cus * 2 - 1) / (cus * 2);
+      // wider as T grows, so that the grid stays at one to two blocks per CU
+      const int rb1 = (d.hidden + cus - 1) / cus;
       plan->rb_b = rb1 * ((T + 1) / 2);
       plan->nslice = (d.hidden + plan->rb_b - 1) / plan->rb_b;
       plan->nb_b = (plan->nslice * T + kXcds - 1) / kXcds * kXcds;
