@@ -377,11 +377,22 @@ __device__ __forceinline__ void stage_h_plain(const FusedArgs& a, const LdsB& s,
   const int r4 = a.hs / 4;                            // float4 per row
   const int n4 = (k + 1) * r4;
   lds_u32x4* dst = (lds_u32x4*)(s.h);
-  for (int j = tid; j < n4; j += kThreads) {
-    const int i = j / r4;
-    const float4 v = reinterpret_cast<const float4*>(a.h + h_row_of(T, k, t, i) * a.hs)[j - i * r4];
-    dst[(j >> 3) * (kSegPad / 4) + (j & 7)] = u32x4{__float_as_uint(v.x), __float_as_uint(v.y),
-                                                      __float_as_uint(v.z), __float_as_uint(v.w)};
+  // each thread's loads of a pass are all requested before any is stored
+  constexpr int kPer = 4;
+  for (int j0 = 0; j0 < n4; j0 += kPer * kThreads) {
+    u32x4 v[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int j = j0 + q * kThreads + tid;
+      const int jc = j < n4 ? j : 0;
+      const int i = jc / r4;
+      v[q] = reinterpret_cast<const u32x4*>(a.h + h_row_of(T, k, t, i) * a.hs)[jc - i * r4];
+    }
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int j = j0 + q * kThreads + tid;
+      if (j < n4) dst[(j >> 3) * (kSegPad / 4) + (j & 7)] = v[q];
+    }
   }
   __syncthreads();
   h_segment_sums(a, s, tid);
