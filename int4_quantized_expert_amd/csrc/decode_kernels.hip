@@ -521,20 +521,50 @@ template <int OUT>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ partial, const int32_t* __restrict__ ids,
                                                  const float* __restrict__ wts, const float* __restrict__ gate,
                                                  void* __restrict__ out, int T, int k, int H, int E) {
+  // one thread per 4 consecutive outputs of one token; the partial rows of a
+  // group of pairs are all requested before any is used, and an unusable
+  // expert id only masks its term (same order of operations as before)
+  constexpr int kGroup = 4;
+  const int h4 = H / 4;
   const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= static_cast<size_t>(T) * H) return;
-  const int t = static_cast<int>(idx / H);
-  const int n = static_cast<int>(idx % H);
-  float acc = 0.f;
-  for (int i = 0; i < k; ++i) {
-    const int e = ids[t * k + i];
-    if (e >= 0 && e < E) acc = fmaf(wts[t * k + i], partial[(static_cast<size_t>(t) * k + i) * H + n], acc);
+  if (idx >= static_cast<size_t>(T) * h4) return;
+  const int t = static_cast<int>(idx / h4);
+  const int n4 = static_cast<int>(idx % h4);
+  const float4 sh = reinterpret_cast<const float4*>(partial + (static_cast<size_t>(T) * k + t) * H)[n4];
+  const float g = gate[t];
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i0 = 0; i0 < k; i0 += kGroup) {
+    float4 p[kGroup];
+    float w[kGroup];
+    bool ok[kGroup];
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const int i = i0 + j < k ? i0 + j : i0;
+      const int e = ids[t * k + i];
+      ok[j] = i0 + j < k && e >= 0 && e < E;
+      w[j] = wts[t * k + i];
+      p[j] = reinterpret_cast<const float4*>(partial + (static_cast<size_t>(t) * k + i) * H)[n4];
+    }
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      if (ok[j]) {
+        acc.x = fmaf(w[j], p[j].x, acc.x);
+        acc.y = fmaf(w[j], p[j].y, acc.y);
+        acc.z = fmaf(w[j], p[j].z, acc.z);
+        acc.w = fmaf(w[j], p[j].w, acc.w);
+      }
+    }
   }
-  acc = fmaf(gate[t], partial[(static_cast<size_t>(T) * k + t) * H + n], acc);
+  acc.x = fmaf(g, sh.x, acc.x);
+  acc.y = fmaf(g, sh.y, acc.y);
+  acc.z = fmaf(g, sh.z, acc.z);
+  acc.w = fmaf(g, sh.w, acc.w);
   if constexpr (OUT == kF32) {
-    static_cast<float*>(out)[idx] = acc;
+    reinterpret_cast<float4*>(out)[idx] = acc;
   } else {
-    static_cast<uint16_t*>(out)[idx] = f32_to_bf16(acc);
+    const uint32_t lo = f32_to_bf16(acc.x) | (static_cast<uint32_t>(f32_to_bf16(acc.y)) << 16);
+    const uint32_t hi = f32_to_bf16(acc.z) | (static_cast<uint32_t>(f32_to_bf16(acc.w)) << 16);
+    reinterpret_cast<uint2*>(out)[idx] = make_uint2(lo, hi);
   }
 }
 
@@ -687,7 +717,7 @@ int launch_experts(const Call& c) {
 
 int launch_combine(const Call& c, const float* partial, const float* gate) {
   const moe_desc& d = c.d;
-  const size_t n = static_cast<size_t>(c.T) * d.hidden;
+  const size_t n = static_cast<size_t>(c.T) * d.hidden / 4;   // one thread per 4 outputs (H % 64 == 0)
   const dim3 grid(static_cast<unsigned>((n + 255) / 256)), block(256);
   if (d.out_dtype == kF32)
     launch_kernel(k_combine<kF32>, grid, block, 0, c.stream, partial, c.ids, c.wts, gate, c.out, c.T, d.top_k,
