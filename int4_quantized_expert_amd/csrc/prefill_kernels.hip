@@ -127,57 +127,6 @@ __device__ __forceinline__ h8v dq_int8(uint32_t w0, uint32_t w1, h2v s, h2v b, u
 __device__ __forceinline__ f4v mfma16(h8v a, h8v b, f4v c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
 // ---------------------------------------------------------------------------
-// Router logits [T, E] = x [T, H] . R [E, H]^T, bf16 operands, fp32 sums.
-// Block: 64 experts x 64 tokens; wave w owns experts 16 w .. +15.
-__global__ __launch_bounds__(kThreads) void k_pf_router(const uint16_t* __restrict__ x, const uint16_t* __restrict__ R,
-                                                       float* __restrict__ logits, int T, int H, int E) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  const int r = lane & 15, q = lane >> 4;
-  const int e = blockIdx.x * 64 + w * 16 + r;
-  const bool e_ok = e < E;
-  const uint16_t* ra = R + static_cast<size_t>(e_ok ? e : 0) * H;
-  const int t0 = blockIdx.y * 64;
-  const uint16_t* xa[4];
-  bool t_ok[4];
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const int t = t0 + 16 * ct + r;
-    t_ok[ct] = t < T;
-    xa[ct] = x + static_cast<size_t>(t_ok[ct] ? t : 0) * H;
-  }
-  f4v acc[4];
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) acc[ct] = f4v{0.f, 0.f, 0.f, 0.f};
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (int k0 = 0; k0 < H; k0 += 128) {
-    const int kk = k0 + 32 * q;
-    u32x4 a[4], b[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) a[j] = e_ok ? load16(ra + kk + 8 * j) : zero;
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[ct][j] = t_ok[ct] ? load16(xa[ct] + kk + 8 * j) : zero;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8v, a[j]), __builtin_bit_cast(b8v, b[ct][j]),
-                                                          acc[ct], 0, 0, 0);
-  }
-  const int e0 = blockIdx.x * 64 + w * 16 + 4 * q;
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const int t = t0 + 16 * ct + r;
-    if (t < T) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (e0 + i < E) logits[static_cast<size_t>(t) * E + e0 + i] = acc[ct][i];
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Shared-expert gate sigmoid(g . x_t), one wave per token, fp32.
 __global__ __launch_bounds__(kThreads) void k_pf_gate(const void* __restrict__ x, const void* __restrict__ gvec,
                                                      float* __restrict__ gate, int T, int H) {
@@ -564,6 +513,112 @@ __device__ __forceinline__ h8v stage_b(const uint8_t* stage, int S, int j, int c
   return *reinterpret_cast<const h8v*>(stage + (16 * S + 4 * j + q) * kChunkBytes + (16 * ct + r) * 16);
 }
 
+// Row-pair staging: one direct-load instruction brings two rows' 256-k
+// slices (2 x 512 bytes, whole cache lines) into a 1 KB block of LDS; lane L
+// copies chunk (L % 32) ^ (row & 7) of row 2 i + L / 32, so chunk c of a row
+// sits at position 32 (row % 2) + (c ^ (row & 7)) of its block.  Sixteen
+// lanes reading one chunk of sixteen consecutive rows then spread over all
+// banks.  A 64-row slice is 32 blocks, 8 per wave.
+__device__ __forceinline__ int pair_pos(int row, int chunk) {
+  return (row >> 1) * kChunkBytes + (32 * (row & 1) + (chunk ^ (row & 7))) * 16;
+}
+
+// row_src: this lane's row (row 2 i + lane / 32 of each of the wave's blocks
+// i = 8 w .. 8 w + 7, i.e. row 16 w + 2 j + lane / 32 for j < 8) at chunk
+// (lane % 32) ^ (row & 7) of slice 0, given for each j.
+struct PairRows {
+  const uint8_t* src[8];
+};
+
+__device__ __forceinline__ void stage_pairs(const PairRows& pr, int ks, uint8_t* stage, int w) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    __builtin_amdgcn_global_load_lds(pr.src[j] + ks * 2, (lds_void*)(stage + (8 * w + j) * kChunkBytes), 16, 0, 0);
+}
+
+// Router logits [T, E] = x [T, H] . R [E, H]^T: bf16 operands (exact
+// products), fp32 sums, on v_mfma_f32_16x16x32_bf16.  Block: 64 experts x 64
+// tokens; wave w owns experts 16 w .. +15 for the 64 tokens (four column
+// blocks).  Both operands are staged a 256-k slice at a time into LDS with
+// row-pair direct loads (natural k order for both), two stages, one barrier
+// per slice.  Blocks are renumbered so that
+// XCD x runs a contiguous range of (token block, expert block) pairs,
+// token-major: an XCD's blocks share their token tiles and the router matrix
+// through its L2.
+__global__ __launch_bounds__(kThreads) void k_pf_router(const uint16_t* __restrict__ x, const uint16_t* __restrict__ R,
+                                                       float* __restrict__ logits, int T, int H, int E) {
+  __shared__ __align__(16) uint8_t rs0[kStageBytes];
+  __shared__ __align__(16) uint8_t rs1[kStageBytes];
+  __shared__ __align__(16) uint8_t xs0[kStageBytes];
+  __shared__ __align__(16) uint8_t xs1[kStageBytes];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int neb = (E + 63) / 64, nb = neb * ((T + 63) / 64);
+  const int per = (nb + kXcds - 1) / kXcds;
+  const int idx = blockIdx.x / kXcds;
+  if (idx >= per) return;
+  const int logical = (blockIdx.x % kXcds) * per + idx;
+  if (logical >= nb) return;
+  const int tb = logical / neb, eb = logical % neb;
+  const int r = lane & 15, q = lane >> 4;
+  // this lane's rows and chunks for the row-pair direct loads, clamped into
+  // range (the sums of a clamped row are never stored)
+  PairRows rsrc, xsrc;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = 16 * w + 2 * j + (lane >> 5);              // row of the tile
+    const int chunk = (lane & 31) ^ (row & 7);
+    const int e_row = min(eb * 64 + row, E - 1), t_row = min(tb * 64 + row, T - 1);
+    rsrc.src[j] = reinterpret_cast<const uint8_t*>(R + static_cast<size_t>(e_row) * H) + chunk * 16;
+    xsrc.src[j] = reinterpret_cast<const uint8_t*>(x + static_cast<size_t>(t_row) * H) + chunk * 16;
+  }
+  f4v acc[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) acc[ct] = f4v{0.f, 0.f, 0.f, 0.f};
+  auto mult = [&](const uint8_t* rst, const uint8_t* xst) {
+#pragma unroll
+    for (int st = 0; st < kSlice / 32; ++st) {
+      const b8v A = *reinterpret_cast<const b8v*>(rst + pair_pos(16 * w + r, 4 * st + q));
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const b8v B = *reinterpret_cast<const b8v*>(xst + pair_pos(16 * ct + r, 4 * st + q));
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[ct], 0, 0, 0);
+      }
+    }
+  };
+  const int nsl = H / kSlice;
+  stage_pairs(rsrc, 0, rs0, w);
+  stage_pairs(xsrc, 0, xs0, w);
+  stage_barrier();
+  for (int sl = 0; sl < nsl; sl += 2) {
+    if (sl + 1 < nsl) {
+      stage_pairs(rsrc, (sl + 1) * kSlice, rs1, w);
+      stage_pairs(xsrc, (sl + 1) * kSlice, xs1, w);
+    }
+    mult(rs0, xs0);
+    stage_barrier();
+    if (sl + 1 < nsl) {
+      if (sl + 2 < nsl) {
+        stage_pairs(rsrc, (sl + 2) * kSlice, rs0, w);
+        stage_pairs(xsrc, (sl + 2) * kSlice, xs0, w);
+      }
+      mult(rs1, xs1);
+      stage_barrier();
+    }
+  }
+  // D row 4 q + i (expert), column r (token) of each column block
+  const int e0 = eb * 64 + w * 16 + 4 * q;
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const int t = tb * 64 + 16 * ct + r;
+    if (t < T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (e0 + i < E) logits[static_cast<size_t>(t) * E + e0 + i] = acc[ct][i];
+    }
+  }
+}
+
 // Natural k (0..7) that MFMA slot s of an 8-group stands for; see permute8.
 template <int BITS>
 __device__ __forceinline__ int slot_k(int s) {
@@ -902,7 +957,8 @@ int launch_prefill_router(const Call& c, int32_t* ids2, float* wts2) {
   float* logits = reinterpret_cast<float*>(c.ws + c.L.logits);
   int32_t* ids = reinterpret_cast<int32_t*>(c.ws + c.L.ids);
   float* wts = reinterpret_cast<float*>(c.ws + c.L.wts);
-  const dim3 grid((d.n_experts + 63) / 64, (c.T + 63) / 64);
+  const int nb = ((d.n_experts + 63) / 64) * ((c.T + 63) / 64);
+  const dim3 grid(static_cast<unsigned>((nb + kXcds - 1) / kXcds * kXcds));
   launch_kernel(k_pf_router, grid, dim3(kThreads), 0, c.stream, static_cast<const uint16_t*>(c.x),
                 static_cast<const uint16_t*>(c.router_w), logits, c.T, d.hidden, d.n_experts);
   if (last_error()) return MOE_EHIP;
