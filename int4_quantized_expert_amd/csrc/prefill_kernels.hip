@@ -448,6 +448,15 @@ __device__ __forceinline__ void load_slice4(StepW<4>& w0, StepW<4>& w1, __amdgpu
   }
 }
 
+// The codes alone of both 128-k steps of a 256-k slice (int4; the scales come
+// through LDS).
+__device__ __forceinline__ void load_codes4(StepW<4>& w0, StepW<4>& w1, __amdgpu_buffer_rsrc_t rs, LaneOffsets lo,
+                                            BlockOffsets bo, int kb) {
+  w0.c[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo.code, bo.code + kb / 2, kNonTemporal));
+  w1.c[0] = __builtin_bit_cast(u32x4,
+                               __builtin_amdgcn_raw_buffer_load_b128(rs, lo.code, bo.code + kb / 2 + 64, kNonTemporal));
+}
+
 __device__ __forceinline__ h2v splat_h2(float v) {
   const _Float16 h = static_cast<_Float16>(v);
   return h2v{h, h};
@@ -492,6 +501,16 @@ __device__ __forceinline__ void with_nt(int nt, F&& f) {
 // those columns are never written out.
 constexpr int kChunkBytes = kChunk * 16;              // one chunk of all 64 columns
 constexpr int kStageBytes = (kSlice / 8) * kChunkBytes;
+
+// int4 codes with bf16 scales: the scale and bias words of a slice are copied
+// into LDS with the slice's activations (direct 4-byte loads), instead of
+// being held in registers one slice ahead.  Per wave and slice: [m][scale,
+// bias][32 rows][2 words] for gate/up (word S holds the two groups of 128-k
+// step S), [scale, bias][64 rows][2 words] for down: 1 KB per wave.
+constexpr int kSbWave = 1024;
+constexpr int kSbStage = 4 * kSbWave;
+template <int BITS, int SB>
+constexpr bool kLdsSb = BITS == 4 && SB == kBF16;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -638,8 +657,9 @@ __device__ __forceinline__ int slot_k(int s) {
 // multiples of 256, so every wave of a block has rows.
 template <int BITS, int SB>
 __global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
-  __shared__ __align__(16) uint8_t xs0[kStageBytes];
-  __shared__ __align__(16) uint8_t xs1[kStageBytes];
+  constexpr bool kLsb = kLdsSb<BITS, SB>;
+  __shared__ __align__(16) uint8_t xs0[kStageBytes + (kLsb ? kSbStage : 0)];
+  __shared__ __align__(16) uint8_t xs1[kStageBytes + (kLsb ? kSbStage : 0)];
   __shared__ int s_pair[kChunk], s_tok[kChunk];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -684,11 +704,31 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
       for (int rr = 0; rr < 2; ++rr) load_step<BITS, SB>(dst[m][rr], rs, lo, bo[m][rr], kb);
   };
   auto load_w2 = [&](StepW<BITS> (&d0)[2][2], StepW<BITS> (&d1)[2][2], int kb) {
-    if constexpr (BITS == 4) {
+    if constexpr (kLsb) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) load_codes4(d0[m][rr], d1[m][rr], rs, lo, bo[m][rr], kb);
+    } else if constexpr (BITS == 4) {
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) load_slice4<SB>(d0[m][rr], d1[m][rr], rs, lo, bo[m][rr], kb);
+    }
+  };
+  // the wave's 32 rows' scale and bias words of the slice at kb: lane l
+  // copies word l % 2 of row l / 2 of one plane
+  const uint32_t sb_lane = static_cast<uint32_t>((lane >> 1) * sbrow + 4 * (lane & 1));
+  auto stage_sb = [&](int kb, uint8_t* stage) {
+    if constexpr (kLsb) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const int soff = static_cast<int>(3 * P.q + (sb ? 3 + m : m) * P.s) + wrow * sbrow + (kb / 64) * 2;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (lds_void*)(stage + kStageBytes + w * kSbWave + (2 * m + sb) * 256), 4, sb_lane, soff, 0, 0);
+        }
     }
   };
   with_nt((n + 15) / 16, [&](auto ntc) {
@@ -707,8 +747,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) {
-          sc[m][rr] = splat_h2(sb_value<SB>(wv[m][rr].s, lo.sel));
-          bc[m][rr] = splat_h2(sb_value<SB>(wv[m][rr].b, lo.sel));
+          if constexpr (kLsb) {
+            const uint8_t* sw = stage + kStageBytes + w * kSbWave + 2 * m * 256 + (16 * rr + lrow) * 8 + 4 * S;
+            sc[m][rr] = splat_h2(sb_value<SB>(*reinterpret_cast<const uint32_t*>(sw), lo.sel));
+            bc[m][rr] = splat_h2(sb_value<SB>(*reinterpret_cast<const uint32_t*>(sw + 256), lo.sel));
+          } else {
+            sc[m][rr] = splat_h2(sb_value<SB>(wv[m][rr].s, lo.sel));
+            bc[m][rr] = splat_h2(sb_value<SB>(wv[m][rr].b, lo.sel));
+          }
         }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -736,6 +782,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
         const bool more = sl + 1 < nsl;
         if (more) {
           stage_slice(xsrc, (sl + 1) * kSlice, nxt, w);
+          stage_sb((sl + 1) * kSlice, nxt);
           load_w2(n1, n2, (sl + 1) * kSlice);
         }
         mult(0, cur, c1);
@@ -743,6 +790,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
         stage_barrier();
       };
       stage_slice(xsrc, 0, xs0, w);
+      stage_sb(0, xs0);
       load_w2(wa, wa2, 0);
       stage_barrier();
       for (int sl = 0; sl < nsl; sl += 2) {
