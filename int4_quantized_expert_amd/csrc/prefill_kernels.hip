@@ -532,6 +532,7 @@ __device__ __forceinline__ h8v stage_b(const uint8_t* stage, int S, int j, int c
   return *reinterpret_cast<const h8v*>(stage + (16 * S + 4 * j + q) * kChunkBytes + (16 * ct + r) * 16);
 }
 
+
 // Row-pair staging: one direct-load instruction brings two rows' 256-k
 // slices (2 x 512 bytes, whole cache lines) into a 1 KB block of LDS; lane L
 // copies chunk (L % 32) ^ (row & 7) of row 2 i + L / 32, so chunk c of a row
@@ -553,6 +554,55 @@ __device__ __forceinline__ void stage_pairs(const PairRows& pr, int ks, uint8_t*
 #pragma unroll
   for (int j = 0; j < 8; ++j)
     __builtin_amdgcn_global_load_lds(pr.src[j] + ks * 2, (lds_void*)(stage + (8 * w + j) * kChunkBytes), 16, 0, 0);
+}
+
+// Row-pair staging of the activation rows of a tile (layout of pair_pos):
+// this lane's byte offsets, one per block it copies, from a buffer
+// descriptor over the whole activation array (under 2^31 bytes); the k
+// offset of the slice is a scalar.
+struct PairOffs {
+  uint32_t off[8];
+};
+
+template <typename RowStart>
+__device__ __forceinline__ PairOffs pair_offsets(int w, int lane, RowStart row_start) {
+  PairOffs po;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = 16 * w + 2 * j + (lane >> 5);
+    po.off[j] = row_start(row) + 16u * static_cast<uint32_t>((lane & 31) ^ (row & 7));
+  }
+  return po;
+}
+
+__device__ __forceinline__ void stage_pairs(__amdgpu_buffer_rsrc_t src, const PairOffs& po, int ks, uint8_t* stage,
+                                            int w) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)(stage + (8 * w + j) * kChunkBytes), 16, po.off[j], ks * 2,
+                                             0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t act_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+// B operand reads of a row-pair staged slice: lane (r, q) reads chunk
+// 16 S + 4 j + q of row 16 ct + r.  Rows 16 ct + r share r & 7 and the xor
+// only touches a chunk's low three bits, so every read is one of two per-lane
+// bases (by j % 2) plus a constant.
+struct PairRead {
+  int even, odd;
+};
+
+__device__ __forceinline__ PairRead pair_read(int r, int q) {
+  const int row_part = (r >> 1) * kChunkBytes + 32 * (r & 1) * 16;
+  return {row_part + (q ^ (r & 7)) * 16, row_part + ((4 + q) ^ (r & 7)) * 16};
+}
+
+__device__ __forceinline__ h8v stage_b_pair(const uint8_t* stage, const PairRead& pr, int S, int j, int ct) {
+  return *reinterpret_cast<const h8v*>(stage + ((j & 1) ? pr.odd : pr.even) + ct * 8 * kChunkBytes + S * 256 +
+                                       (j >> 1) * 128);
 }
 
 // Router logits [T, E] = x [T, H] . R [E, H]^T: bf16 operands (exact
@@ -697,6 +747,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
   __syncthreads();   // s_tok ready
   const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(a.x16) +
                         static_cast<size_t>(s_tok[lane < n ? lane : 0]) * a.H * 2 + w * 8 * 16;
+  // int4 with bf16 scales: activations staged as row pairs (whole lines per
+  // direct load)
+  const __amdgpu_buffer_rsrc_t xrs = act_rsrc(a.x16, static_cast<int64_t>(a.T) * a.H * 2);
+  PairOffs xo;
+  if constexpr (kLsb)
+    xo = pair_offsets(w, lane, [&](int row) {
+      return static_cast<uint32_t>(s_tok[row < n ? row : 0]) * static_cast<uint32_t>(a.H * 2);
+    });
+  const PairRead prd = pair_read(r, q);
+  auto stage_x = [&](int ks, uint8_t* stage) {
+    if constexpr (kLsb) stage_pairs(xrs, xo, ks, stage, w);
+    else stage_slice(xsrc, ks, stage, w);
+  };
   auto load_w = [&](StepW<BITS> (&dst)[2][2], int kb) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -760,7 +823,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
       for (int j = 0; j < 4; ++j) {
         h8v B[NT];
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) B[ct] = stage_b(stage, S, j, ct, r, q);
+        for (int ct = 0; ct < NT; ++ct)
+          B[ct] = kLsb ? stage_b_pair(stage, prd, S, j, ct) : stage_b(stage, S, j, ct, r, q);
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -781,7 +845,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
                        const StepW<BITS> (&c2)[2][2], StepW<BITS> (&n1)[2][2], StepW<BITS> (&n2)[2][2]) {
         const bool more = sl + 1 < nsl;
         if (more) {
-          stage_slice(xsrc, (sl + 1) * kSlice, nxt, w);
+          stage_x((sl + 1) * kSlice, nxt);
           stage_sb((sl + 1) * kSlice, nxt);
           load_w2(n1, n2, (sl + 1) * kSlice);
         }
@@ -789,7 +853,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
         mult(1, cur, c2);
         stage_barrier();
       };
-      stage_slice(xsrc, 0, xs0, w);
+      stage_x(0, xs0);
       stage_sb(0, xs0);
       load_w2(wa, wa2, 0);
       stage_barrier();
@@ -994,8 +1058,10 @@ bool prefill_supported(const moe_desc& d, int T) {
   // weight offsets inside a blob are 32-bit buffer offsets
   const int wide = d.inter > d.shared_inter ? d.inter : d.shared_inter;
   const bool blob_fits = planes_of(d.hidden, wide, d.bits, d.sb_dtype).blob < (int64_t{1} << 31);
+  // activations read through 32-bit buffer offsets
+  const bool act_fits = static_cast<int64_t>(T) * d.hidden * 2 < (int64_t{1} << 31);
   return T >= kPrefillMinT && d.act_dtype == kBF16 && d.hidden % kSlice == 0 && d.inter % kSlice == 0 &&
-         d.shared_inter % kSlice == 0 && d.n_experts <= 1024 && blob_fits;
+         d.shared_inter % kSlice == 0 && d.n_experts <= 1024 && blob_fits && act_fits;
 }
 
 static int last_error() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP; }
