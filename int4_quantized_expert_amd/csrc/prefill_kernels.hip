@@ -46,7 +46,8 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kChunk = kPrefillChunk;   // pairs per tile (4 MFMA column blocks)
 constexpr int kGuRows = 128;            // gate/up rows (each) per block: 4 waves x 32
-constexpr int kDnRows = 256;            // down rows per block: 4 waves x 64
+constexpr int kDnRows = 256;            // down rows per row block: 4 waves x 64
+constexpr int kDownGroup = 2;           // row blocks per down block (int4, bf16 scales)
 constexpr int kSlice = 256;             // k staged in LDS per step
 constexpr int kDispThreads = 1024;
 
@@ -296,7 +297,8 @@ struct PfArgs {
   uint32_t* flags;
   int64_t pool_bytes;
   int T, k, H, E, I, SI, hs;
-  int n_rt;                // row blocks per tile in this launch
+  int n_rt;                // blocks per tile in this launch
+  int n_g;                 // down: 256-row blocks per block
 };
 
 struct Tile {
@@ -908,15 +910,21 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
   });
 }
 
-// Down: block = (tile, 256-row block of H); wave w owns rows 64 w .. +63 (four
-// 16-row MFMA blocks) for the tile's pairs.  h rows arrive in operand order
-// and are staged like x.  Writes fp32 partial rows; a tile of an unusable blob
-// writes zeros, so that expert contributes nothing.  Pipelined over 256-k
-// slices like the gate/up kernel.
+// Down: block = (tile, n_g consecutive 256-row blocks of H); wave w owns
+// rows 64 w .. +63 (four 16-row MFMA blocks) of each row block for the tile's
+// pairs.  h rows arrive in operand order and are staged like x.  Writes fp32
+// partial rows; a tile of an unusable blob writes zeros, so that expert
+// contributes nothing.
+// int4 with bf16 scales: the block walks its row blocks one 256-k slice
+// ("step") at a time with the next step's codes in registers and its scales
+// and h slice in the other LDS stage; with K <= 512 the h tile stays
+// resident after the first two steps.  Other formats: one row block per
+// block, pipelined over slices like the gate/up kernel.
 template <int BITS, int SB>
 __global__ __launch_bounds__(kThreads, 2) void k_pf_down(PfArgs a) {
-  __shared__ __align__(16) uint8_t hs0[kStageBytes];
-  __shared__ __align__(16) uint8_t hs1[kStageBytes];
+  constexpr bool kLsb = kLdsSb<BITS, SB>;
+  __shared__ __align__(16) uint8_t hs0[kStageBytes + (kLsb ? kSbStage : 0)];
+  __shared__ __align__(16) uint8_t hs1[kStageBytes + (kLsb ? kSbStage : 0)];
   __shared__ int s_pair[kChunk], s_tok[kChunk];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -926,14 +934,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_down(PfArgs a) {
   if (!tile_of<BITS, SB>(a, ti, &tl)) return;
   const int K = tl.rows_or_k;
   const int n = tl.n;
+  const int G = a.n_g;
   tile_pairs(a, tl, tid, s_pair, s_tok);
   __syncthreads();
   const int r = lane & 15, q = lane >> 4;
   if (!tl.ok) {
     // zero this block's output rows of the tile's pairs
-    for (int i = tid; i < n * (kDnRows / 4); i += kThreads) {
-      const int c = i / (kDnRows / 4), col = (i % (kDnRows / 4)) * 4;
-      *reinterpret_cast<float4*>(a.partial + static_cast<size_t>(s_pair[c]) * a.H + rb * kDnRows + col) =
+    const int span = G * kDnRows;
+    for (int i = tid; i < n * (span / 4); i += kThreads) {
+      const int c = i / (span / 4), col = (i % (span / 4)) * 4;
+      *reinterpret_cast<float4*>(a.partial + static_cast<size_t>(s_pair[c]) * a.H + rb * span + col) =
           make_float4(0.f, 0.f, 0.f, 0.f);
     }
     return;
@@ -944,7 +954,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_down(PfArgs a) {
   constexpr int sbsz = SB == kF32 ? 4 : 2;
   const int rbytes = K * BITS / 8;
   const int sbrow = (K / 64) * sbsz;
-  const int wrow = rb * kDnRows + w * 64;
+  const int wrow = rb * G * kDnRows + w * 64;   // the wave's first row in the first row block
   const LaneOffsets lo = lane_offsets<BITS, SB>(r, rbytes, sbrow, q);
   BlockOffsets bo[4];
 #pragma unroll
@@ -955,6 +965,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_down(PfArgs a) {
   }
   const uint8_t* hsrc = reinterpret_cast<const uint8_t*>(a.h) +
                         static_cast<size_t>(s_pair[lane < n ? lane : 0]) * a.hs * 2 + w * 8 * 16;
+  const __amdgpu_buffer_rsrc_t hrs =
+      act_rsrc(a.h, (static_cast<int64_t>(a.T) * a.k + a.T) * a.hs * 2);
+  PairOffs ho;
+  if constexpr (kLsb)
+    ho = pair_offsets(w, lane, [&](int row) {
+      return static_cast<uint32_t>(s_pair[row < n ? row : 0]) * static_cast<uint32_t>(a.hs * 2);
+    });
+  const PairRead prd = pair_read(r, q);
   auto load_w = [&](StepW<BITS> (&dst)[4], int kb) {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) load_step<BITS, SB>(dst[rr], rs, lo, bo[rr], kb);
@@ -972,18 +990,27 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_down(PfArgs a) {
     for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) acc[rr][ct] = f4v{0.f, 0.f, 0.f, 0.f};
+    // One 128-k step S of the slice in `stage`; scale words from registers or,
+    // with kLsb, from the stage's scale area.
     auto mult = [&](int S, const uint8_t* stage, const StepW<BITS> (&wv)[4]) {
       h2v sc[4], bc[4];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        sc[rr] = splat_h2(sb_value<SB>(wv[rr].s, lo.sel));
-        bc[rr] = splat_h2(sb_value<SB>(wv[rr].b, lo.sel));
+        if constexpr (kLsb) {
+          const uint8_t* sw = stage + kStageBytes + w * kSbWave + (16 * rr + r) * 8 + 4 * S;
+          sc[rr] = splat_h2(sb_value<SB>(*reinterpret_cast<const uint32_t*>(sw), lo.sel));
+          bc[rr] = splat_h2(sb_value<SB>(*reinterpret_cast<const uint32_t*>(sw + 512), lo.sel));
+        } else {
+          sc[rr] = splat_h2(sb_value<SB>(wv[rr].s, lo.sel));
+          bc[rr] = splat_h2(sb_value<SB>(wv[rr].b, lo.sel));
+        }
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         h8v B[NT];
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) B[ct] = stage_b(stage, S, j, ct, r, q);
+        for (int ct = 0; ct < NT; ++ct)
+          B[ct] = kLsb ? stage_b_pair(stage, prd, S, j, ct) : stage_b(stage, S, j, ct, r, q);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const h8v A = step_operand<BITS>(wv[rr], j, sc[rr], bc[rr], magic_v);
@@ -992,7 +1019,70 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_down(PfArgs a) {
         }
       }
     };
-    if constexpr (BITS == 4) {
+    // partial rows of the row block whose first wave row is row0
+    auto store = [&](int row0) {
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
+        const int c = 16 * ct + r;
+        if (c < n) {
+          float* pr = a.partial + static_cast<size_t>(s_pair[c]) * a.H + row0 + 4 * q;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            *reinterpret_cast<float4*>(pr + 16 * rr) =
+                make_float4(acc[rr][ct][0], acc[rr][ct][1], acc[rr][ct][2], acc[rr][ct][3]);
+        }
+      }
+    };
+    if constexpr (kLsb) {
+      const int nsl = K / kSlice;
+      const int nsteps = G * nsl;
+      // step st: row block st / nsl (rows from wrow + that * kDnRows), slice st % nsl
+      const uint32_t sb_lane = static_cast<uint32_t>((lane >> 1) * sbrow + 4 * (lane & 1));
+      auto stage_step = [&](int st, uint8_t* stage) {
+        const int g = st / nsl, ks = (st % nsl) * kSlice;
+        if (nsl > 2 || st < 2) stage_pairs(hrs, ho, ks, stage, w);   // else the stage already holds it
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int soff = static_cast<int>(3 * P.q + (sb ? 5 : 2) * P.s) +
+                             (wrow + g * kDnRows + 32 * half) * sbrow + (ks / 64) * 2;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (lds_void*)(stage + kStageBytes + w * kSbWave + sb * 512 + half * 256), 4, sb_lane, soff, 0, 0);
+          }
+      };
+      auto load_codes = [&](StepW<BITS> (&d0)[4], StepW<BITS> (&d1)[4], int st) {
+        const int g = st / nsl, ks = (st % nsl) * kSlice;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          load_codes4(d0[rr], d1[rr], rs, lo, BlockOffsets{bo[rr].code + g * kDnRows * rbytes, 0, 0}, ks);
+      };
+      StepW<BITS> wa[4], wa2[4], wb[4], wb2[4];
+      auto step = [&](int st, const uint8_t* cur, uint8_t* nxt, const StepW<BITS> (&c1)[4],
+                      const StepW<BITS> (&c2)[4], StepW<BITS> (&n1)[4], StepW<BITS> (&n2)[4]) {
+        if (st + 1 < nsteps) {
+          stage_step(st + 1, nxt);
+          load_codes(n1, n2, st + 1);
+        }
+        mult(0, cur, c1);
+        mult(1, cur, c2);
+        if (st % nsl == nsl - 1) {
+          store(wrow + (st / nsl) * kDnRows);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) acc[rr][ct] = f4v{0.f, 0.f, 0.f, 0.f};
+        }
+        stage_barrier();
+      };
+      stage_step(0, hs0);
+      load_codes(wa, wa2, 0);
+      stage_barrier();
+      for (int st = 0; st < nsteps; st += 2) {
+        step(st, hs0, hs1, wa, wa2, wb, wb2);
+        if (st + 1 < nsteps) step(st + 1, hs1, hs0, wb, wb2, wa, wa2);
+      }
+    } else if constexpr (BITS == 4) {
       StepW<BITS> wa[4], wa2[4], wb[4], wb2[4];
       const int nsl = K / kSlice;
       auto slice = [&](int sl, const uint8_t* cur, uint8_t* nxt, const StepW<BITS> (&c1)[4],
@@ -1013,6 +1103,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_down(PfArgs a) {
         slice(sl, hs0, hs1, wa, wa2, wb, wb2);
         if (sl + 1 < nsl) slice(sl + 1, hs1, hs0, wb, wb2, wa, wa2);
       }
+      store(wrow);
     } else {
       StepW<BITS> wa[4], wb[4];
       const int nst = K / 128;
@@ -1034,17 +1125,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_down(PfArgs a) {
           step(st + 3, 1, hs1, hs0, wb, wa);
         }
       }
-    }
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      const int c = 16 * ct + r;
-      if (c < n) {
-        float* pr = a.partial + static_cast<size_t>(s_pair[c]) * a.H + wrow + 4 * q;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          *reinterpret_cast<float4*>(pr + 16 * rr) =
-              make_float4(acc[rr][ct][0], acc[rr][ct][1], acc[rr][ct][2], acc[rr][ct][3]);
-      }
+      store(wrow);
     }
   });
 }
@@ -1059,7 +1140,8 @@ bool prefill_supported(const moe_desc& d, int T) {
   const int wide = d.inter > d.shared_inter ? d.inter : d.shared_inter;
   const bool blob_fits = planes_of(d.hidden, wide, d.bits, d.sb_dtype).blob < (int64_t{1} << 31);
   // activations read through 32-bit buffer offsets
-  const bool act_fits = static_cast<int64_t>(T) * d.hidden * 2 < (int64_t{1} << 31);
+  const int64_t h_bytes = (static_cast<int64_t>(T) * d.top_k + T) * wide * 2;
+  const bool act_fits = static_cast<int64_t>(T) * d.hidden * 2 < (int64_t{1} << 31) && h_bytes < (int64_t{1} << 31);
   return T >= kPrefillMinT && d.act_dtype == kBF16 && d.hidden % kSlice == 0 && d.inter % kSlice == 0 &&
          d.shared_inter % kSlice == 0 && d.n_experts <= 1024 && blob_fits && act_fits;
 }
@@ -1092,7 +1174,8 @@ static void launch_tiles(const PfArgs& base, const Call& c) {
   PfArgs a = base;
   a.n_rt = (d.inter > d.shared_inter ? d.inter : d.shared_inter) / kGuRows;
   launch_kernel(k_pf_gateup<BITS, SB>, dim3(xcd_grid(c.L.max_tiles, a.n_rt)), dim3(kThreads), 0, c.stream, a);
-  a.n_rt = d.hidden / kDnRows;
+  a.n_g = kLdsSb<BITS, SB> && (d.hidden / kDnRows) % kDownGroup == 0 ? kDownGroup : 1;
+  a.n_rt = d.hidden / (kDnRows * a.n_g);
   launch_kernel(k_pf_down<BITS, SB>, dim3(xcd_grid(c.L.max_tiles, a.n_rt)), dim3(kThreads), 0, c.stream, a);
 }
 
@@ -1127,6 +1210,7 @@ int launch_prefill_experts(const Call& c) {
   a.SI = d.shared_inter;
   a.hs = L.hstride;
   a.n_rt = 1;
+  a.n_g = 1;
 
   const void* gvec = c.shared + d.shared_stride;
   launch_kernel(k_pf_gate, dim3((c.T + 3) / 4), dim3(kThreads), 0, c.stream, c.x, gvec, gate, c.T, d.hidden);
