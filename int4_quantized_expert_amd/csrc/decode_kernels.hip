@@ -10,6 +10,7 @@
 
 #include "device_common.h"
 #include "moe_internal.h"
+#include "topk_wave.h"
 
 namespace moe {
 
@@ -51,58 +52,46 @@ __global__ __launch_bounds__(256) void k_router_logits(const void* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Top-k per token (one wave per token): k rounds of a wave arg-max over
-// (logit descending, id ascending), then p_i = exp(l_i - l_0) / sum_j exp(l_j - l_0)
-// with the sum taken in rank order.
-constexpr int kTopkPerLane = 16;   // E <= 1024
+// Top-k per token, one wave per token (topk_wave: a threshold from the lane
+// maxima, then the candidates above it ranked exactly by (logit descending,
+// id ascending)), then p_i = exp(l_i - l_0) / sum_j exp(l_j - l_0) with the
+// sum taken in rank order.  The token's logits row is copied to LDS first,
+// all loads of a lane issued together.
+constexpr int kTopkWaves = 4;
+constexpr int kTopkMaxE = 1024;
 
-__device__ __forceinline__ bool better(float v, int id, float bv, int bid) {
-  return v > bv || (v == bv && id < bid);
-}
-
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
-                                              int32_t* __restrict__ ids, float* __restrict__ wts,
-                                              int32_t* __restrict__ ids2, float* __restrict__ wts2) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int t = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
-  if (t >= T) return;
-  float v[kTopkPerLane];
-  uint32_t taken = 0;
+__global__ __launch_bounds__(kTopkWaves * kWave) void k_topk(const float* __restrict__ logits, int T, int E, int k,
+                                                           int32_t* __restrict__ ids, float* __restrict__ wts,
+                                                           int32_t* __restrict__ ids2, float* __restrict__ wts2) {
+  __shared__ float s_lg[kTopkWaves][kTopkMaxE];
+  __shared__ uint64_t s_cand[kTopkWaves][kCandMax];
+  __shared__ int32_t s_ids[kTopkWaves][kWave];
+  __shared__ float s_vals[kTopkWaves][kWave];
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  const int t = blockIdx.x * kTopkWaves + wv;
+  if (t >= T) return;   // the waves of a block never synchronise with each other
+  const float* row = logits + static_cast<size_t>(t) * E;
+  float v[kTopkMaxE / kWave];
 #pragma unroll
-  for (int j = 0; j < kTopkPerLane; ++j) {
+  for (int j = 0; j < kTopkMaxE / kWave; ++j) {
     const int e = lane + j * kWave;
-    v[j] = e < E ? logits[static_cast<size_t>(t) * E + e] : -INFINITY;
+    v[j] = row[e < E ? e : 0];
   }
-  float my_v = 0.f;
-  int my_id = -1;
-  float top = 0.f;
-  for (int i = 0; i < k; ++i) {
-    float bv = -INFINITY;
-    int bid = 0x7fffffff;
 #pragma unroll
-    for (int j = 0; j < kTopkPerLane; ++j) {
-      const int e = lane + j * kWave;
-      if (e < E && !((taken >> j) & 1u) && better(v[j], e, bv, bid)) { bv = v[j]; bid = e; }
-    }
-#pragma unroll
-    for (int m = kWave / 2; m > 0; m >>= 1) {
-      const float ov = __shfl_xor(bv, m, kWave);
-      const int oid = __shfl_xor(bid, m, kWave);
-      if (better(ov, oid, bv, bid)) { bv = ov; bid = oid; }
-    }
-    if ((bid & (kWave - 1)) == lane) taken |= 1u << (bid / kWave);
-    if (lane == i) { my_v = bv; my_id = bid; }
-    if (i == 0) top = bv;
+  for (int j = 0; j < kTopkMaxE / kWave; ++j) {
+    const int e = lane + j * kWave;
+    if (e < E) s_lg[wv][e] = v[j];
   }
-  const float ex = lane < k ? expf(my_v - top) : 0.f;
-  float sum = 0.f;
-  for (int i = 0; i < k; ++i) sum += __shfl(ex, i, kWave);
+  wave_sync_lds();
+  topk_wave(s_lg[wv], E, k, lane, s_cand[wv], s_ids[wv], s_vals[wv]);
+  wave_sync_lds();
   if (lane < k) {
-    const float p = ex / sum;
     const size_t o = static_cast<size_t>(t) * k + lane;
-    ids[o] = my_id;
+    const int id = s_ids[wv][lane];
+    const float p = s_vals[wv][lane];
+    ids[o] = id;
     wts[o] = p;
-    if (ids2) ids2[o] = my_id;
+    if (ids2) ids2[o] = id;
     if (wts2) wts2[o] = p;
   }
 }
@@ -610,8 +599,8 @@ int launch_router_topk(const Call& c, int32_t* ids2, float* wts2) {
 }
 
 int launch_topk(const Call& c, const float* logits, int32_t* ids, float* wts, int32_t* ids2, float* wts2) {
-  launch_kernel(k_topk, dim3((c.T + 3) / 4), dim3(256), 0, c.stream, logits, c.T, c.d.n_experts, c.d.top_k, ids,
-                wts, ids2, wts2);
+  launch_kernel(k_topk, dim3((c.T + kTopkWaves - 1) / kTopkWaves), dim3(kTopkWaves * kWave), 0, c.stream, logits,
+                c.T, c.d.n_experts, c.d.top_k, ids, wts, ids2, wts2);
   return last_launch_error();
 }
 

@@ -39,6 +39,8 @@ struct WsLayout {
   size_t p_meta;     // prefill: int32 [0] number of expert tiles
   size_t p_tstart;   // prefill: [min(T k, E) + 2] int32 first tile of each distinct expert, then of the shared one
   size_t p_tile;     // prefill: [max tiles] int32 distinct-expert rank of each tile (the shared expert is rank U)
+  size_t p_estart;   // prefill: [E] int32 start of each expert's pair list
+  size_t p_erank;    // prefill: [T k] int32 place of each pair in its expert's list (-1: unusable id)
   size_t total;
   int32_t umax;      // min(T k, E)
   int32_t hstride;   // max(I, SI)
@@ -79,6 +81,8 @@ inline WsLayout ws_layout(const moe_desc& d, int32_t T) {
   L.p_meta = take(16);
   L.p_tstart = take((static_cast<size_t>(umax) + 2) * 4);
   L.p_tile = take(static_cast<size_t>(L.max_tiles) * 4);
+  L.p_estart = take(static_cast<size_t>(d.n_experts) * 4);
+  L.p_erank = take(Tk * 4);
   L.total = o;
   L.umax = umax;
   L.hstride = hs;

@@ -8,11 +8,12 @@
 //
 //   k_pf_router    logits = x R^T on v_mfma_f32_16x16x32_bf16 (exact bf16
 //                  products, fp32 accumulation)
-//   k_pf_gate      sigmoid(g . x) per token, fp32
 //   (k_topk)       the staged path's per-token top-k and renormalisation
-//   k_pf_dispatch  stable counting sort of the (token, rank) pairs by expert
+//   k_pf_gate      sigmoid(g . x) per token, fp32
+//   k_pf_dispatch  each pair's place in its expert's list, the list starts
 //                  and a table of tiles of up to 64 pairs of one expert
-//   k_pf_xprep     x to float16, stored in the k order the MFMA operands use
+//   k_pf_xprep     x to float16, stored in the k order the MFMA operands use;
+//                  also writes the pair lists
 //   k_pf_gateup    per tile: h = silu(Wg x) * (Wu x), h in float16
 //   k_pf_down      per tile: partial = Wd h, fp32 per (pair, output row)
 //   (k_combine)    the staged path's ordered combine with the shared expert
@@ -50,6 +51,7 @@ constexpr int kDnRows = 256;            // down rows per row block: 4 waves x 64
 constexpr int kDownGroup = 2;           // row blocks per down block (int4, bf16 scales)
 constexpr int kSlice = 256;             // k staged in LDS per step
 constexpr int kDispThreads = 1024;
+constexpr int kDispBatch = 8;           // dispatch: id loads in flight per lane
 
 __device__ __forceinline__ uint32_t h2_bits(h2v v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ h2v bits_h2(uint32_t v) { return __builtin_bit_cast(h2v, v); }
@@ -148,46 +150,47 @@ __global__ __launch_bounds__(kThreads) void k_pf_gate(const void* __restrict__ x
 }
 
 // ---------------------------------------------------------------------------
-// Stable counting sort of the T k (token, rank) pairs by expert.
-//
-// Waves w < nsl each own a contiguous slice of pairs.  Pass 1 counts per
-// (slice, expert); a scan turns the counts into each slice's first position
-// in each expert's list; pass 2 walks every slice in order, 64 pairs at a
-// time, and places each pair after the earlier pairs of its expert (found by
-// matching the expert id bit by bit across the wave), so lists keep token
-// order.  Also writes the distinct experts (ascending id), their list starts,
-// and the tile table: expert rank u gets ceil(n_u / 64) tiles, then the shared
-// expert ceil(T / 64) tiles of consecutive tokens.
+// Pair lists by expert, pass 1 (one block).  Each pair takes the next place in
+// its expert's list with an LDS atomic increment (places follow the order the
+// increments land in; no value depends on it, since every pair's columns and
+// output rows are its own).  A scan of the counts gives each expert's list
+// start; the distinct experts (ascending id), their list starts and the tile
+// table follow: expert rank u gets ceil(n_u / 64) tiles, then the shared
+// expert ceil(T / 64) tiles of consecutive tokens.  Pass 2 (in k_pf_xprep,
+// spread over the grid) writes every pair at its expert's start plus its
+// place.
 __global__ __launch_bounds__(kDispThreads) void k_pf_dispatch(const int32_t* __restrict__ ids, int T, int k, int E,
-                                                             int nsl, int32_t* __restrict__ ucount,
-                                                             int32_t* __restrict__ uniq, int32_t* __restrict__ ustart,
-                                                             int32_t* __restrict__ plist, int32_t* __restrict__ tstart,
+                                                             int32_t* __restrict__ erank, int32_t* __restrict__ estart,
+                                                             int32_t* __restrict__ ucount, int32_t* __restrict__ uniq,
+                                                             int32_t* __restrict__ ustart, int32_t* __restrict__ tstart,
                                                              int32_t* __restrict__ tile_u, int32_t* __restrict__ meta,
                                                              uint32_t* __restrict__ flags) {
-  extern __shared__ int32_t cnt[];   // [nsl][E]
+  __shared__ int cnt[kDispThreads];
   __shared__ int ws_c[kDispThreads / kWave], ws_u[kDispThreads / kWave], ws_t[kDispThreads / kWave];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const int np = T * k;
-  const int per = (np + nsl - 1) / nsl;
-  for (int i = tid; i < nsl * E; i += kDispThreads) cnt[i] = 0;
+  cnt[tid] = 0;
   __syncthreads();
-  const int p_lo = w * per, p_hi = min(np, p_lo + per);
-  if (w < nsl) {
-    for (int p = p_lo + lane; p < p_hi; p += kWave) {
-      const int e = ids[p];
-      if (e >= 0 && e < E) atomicAdd(&cnt[w * E + e], 1);
-      else raise_error(flags, kErrRange);
+  // kDispBatch pairs per thread in flight: all loads before any use
+  for (int b0 = 0; b0 < np; b0 += kDispBatch * kDispThreads) {
+    int ev[kDispBatch];
+#pragma unroll
+    for (int v = 0; v < kDispBatch; ++v) {
+      const int p = b0 + v * kDispThreads + tid;
+      ev[v] = ids[p < np ? p : 0];
+    }
+#pragma unroll
+    for (int v = 0; v < kDispBatch; ++v) {
+      const int p = b0 + v * kDispThreads + tid;
+      if (p >= np) continue;
+      const int e = ev[v];
+      const bool ok = e >= 0 && e < E;
+      if (!ok) raise_error(flags, kErrRange);
+      erank[p] = ok ? atomicAdd(&cnt[e], 1) : -1;
     }
   }
   __syncthreads();
-  int c = 0;
-  if (tid < E) {
-    for (int s = 0; s < nsl; ++s) {
-      const int v = cnt[s * E + tid];
-      cnt[s * E + tid] = c;
-      c += v;
-    }
-  }
+  const int c = tid < E ? cnt[tid] : 0;
   const int u = c > 0 ? 1 : 0;
   const int nt = (c + kChunk - 1) / kChunk;
   int ic = c, iu = u, it = nt;
@@ -212,14 +215,12 @@ __global__ __launch_bounds__(kDispThreads) void k_pf_dispatch(const int32_t* __r
   const int start = (w > 0 ? ws_c[w - 1] : 0) + ic - c;
   const int rank = (w > 0 ? ws_u[w - 1] : 0) + iu - u;
   const int tile0 = (w > 0 ? ws_t[w - 1] : 0) + it - nt;
-  if (tid < E) {
-    for (int s = 0; s < nsl; ++s) cnt[s * E + tid] += start;
-    if (u) {
-      uniq[rank] = tid;
-      ustart[rank] = start;
-      tstart[rank] = tile0;
-      for (int i = 0; i < nt; ++i) tile_u[tile0 + i] = rank;
-    }
+  if (tid < E) estart[tid] = start;
+  if (tid < E && u) {
+    uniq[rank] = tid;
+    ustart[rank] = start;
+    tstart[rank] = tile0;
+    for (int i = 0; i < nt; ++i) tile_u[tile0 + i] = rank;
   }
   if (tid == kDispThreads - 1) {
     const int U = ws_u[kDispThreads / kWave - 1];
@@ -232,37 +233,22 @@ __global__ __launch_bounds__(kDispThreads) void k_pf_dispatch(const int32_t* __r
     for (int i = 0; i < shared_tiles; ++i) tile_u[routed + i] = U;
     meta[0] = routed + shared_tiles;
   }
-  __syncthreads();
-  if (w < nsl) {
-    for (int base = p_lo; base < p_hi; base += kWave) {
-      const int p = base + lane;
-      const int e = p < p_hi ? ids[p] : -1;
-      const bool ok = e >= 0 && e < E;
-      uint64_t m = __ballot(ok);
-      for (int b = 0; (1 << b) < E; ++b) {
-        const bool bit = (e >> b) & 1;
-        const uint64_t bb = __ballot(bit);
-        m &= bit ? bb : ~bb;
-      }
-      const int before = __popcll(m & lane_mask_lt(lane));
-      int pos = 0;
-      if (ok) pos = cnt[w * E + e] + before;
-      wave_sync_lds();
-      if (ok) {
-        plist[pos] = p;
-        if (before == __popcll(m) - 1) cnt[w * E + e] = pos + 1;   // last of its group moves the cursor
-      }
-      wave_sync_lds();
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
 // x [T, H] bf16 -> float16 in MFMA k order, one thread per 8 values.
+// The grid also writes the pair lists (pass 2 of the dispatch).
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void k_pf_xprep(const uint16_t* __restrict__ x, u32x4* __restrict__ x16, int T,
-                                                      int H) {
+                                                      int H, const int32_t* __restrict__ ids,
+                                                      const int32_t* __restrict__ erank,
+                                                      const int32_t* __restrict__ estart, int np,
+                                                      int32_t* __restrict__ plist) {
   const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (size_t p = i; p < static_cast<size_t>(np); p += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const int r = erank[p];
+    if (r >= 0) plist[estart[ids[p]] + r] = static_cast<int32_t>(p);
+  }
   const int g_row = H / 8;
   if (i >= static_cast<size_t>(T) * g_row) return;
   const size_t t = i / g_row;
@@ -1213,19 +1199,24 @@ int launch_prefill_experts(const Call& c) {
   a.n_g = 1;
 
   const void* gvec = c.shared + d.shared_stride;
+  int32_t* estart = reinterpret_cast<int32_t*>(ws + L.p_estart);
+  int32_t* erank = reinterpret_cast<int32_t*>(ws + L.p_erank);
   launch_kernel(k_pf_gate, dim3((c.T + 3) / 4), dim3(kThreads), 0, c.stream, c.x, gvec, gate, c.T, d.hidden);
-  const int nsl_cap = (60 * 1024) / (4 * d.n_experts);
-  const int nsl = nsl_cap < kDispThreads / kWave ? nsl_cap : kDispThreads / kWave;
-  launch_kernel(k_pf_dispatch, dim3(1), dim3(kDispThreads), static_cast<uint32_t>(nsl * d.n_experts * 4), c.stream,
-                c.ids, c.T, d.top_k, d.n_experts, nsl, const_cast<int32_t*>(a.ucount), const_cast<int32_t*>(a.uniq),
-                const_cast<int32_t*>(a.ustart), const_cast<int32_t*>(a.plist), const_cast<int32_t*>(a.tstart),
-                const_cast<int32_t*>(a.tile_u), const_cast<int32_t*>(a.meta), flags);
+  launch_kernel(k_pf_dispatch, dim3(1), dim3(kDispThreads), 0, c.stream, c.ids, c.T, d.top_k, d.n_experts, erank,
+                estart, const_cast<int32_t*>(a.ucount), const_cast<int32_t*>(a.uniq), const_cast<int32_t*>(a.ustart),
+                const_cast<int32_t*>(a.tstart), const_cast<int32_t*>(a.tile_u), const_cast<int32_t*>(a.meta), flags);
   const size_t nchunk = static_cast<size_t>(c.T) * d.hidden / 8;
   const dim3 xgrid(static_cast<unsigned>((nchunk + kThreads - 1) / kThreads));
   u32x4* x16 = reinterpret_cast<u32x4*>(ws + L.p_x16);
   const uint16_t* x = static_cast<const uint16_t*>(c.x);
-  if (d.bits == 4) launch_kernel(k_pf_xprep<4>, xgrid, dim3(kThreads), 0, c.stream, x, x16, c.T, d.hidden);
-  else launch_kernel(k_pf_xprep<8>, xgrid, dim3(kThreads), 0, c.stream, x, x16, c.T, d.hidden);
+  const int np = c.T * d.top_k;
+  int32_t* plist = const_cast<int32_t*>(a.plist);
+  if (d.bits == 4)
+    launch_kernel(k_pf_xprep<4>, xgrid, dim3(kThreads), 0, c.stream, x, x16, c.T, d.hidden, c.ids,
+                  static_cast<const int32_t*>(erank), static_cast<const int32_t*>(estart), np, plist);
+  else
+    launch_kernel(k_pf_xprep<8>, xgrid, dim3(kThreads), 0, c.stream, x, x16, c.T, d.hidden, c.ids,
+                  static_cast<const int32_t*>(erank), static_cast<const int32_t*>(estart), np, plist);
   if (d.bits == 4 && d.sb_dtype == kBF16) launch_tiles<4, kBF16>(a, c);
   else if (d.bits == 4) launch_tiles<4, kF32>(a, c);
   else if (d.sb_dtype == kBF16) launch_tiles<8, kBF16>(a, c);
