@@ -563,16 +563,48 @@ __device__ __forceinline__ PairOffs pair_offsets(int w, int lane, RowStart row_s
   return po;
 }
 
-__device__ __forceinline__ void stage_pairs(__amdgpu_buffer_rsrc_t src, const PairOffs& po, int ks, uint8_t* stage,
-                                            int w) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)(stage + (8 * w + j) * kChunkBytes), 16, po.off[j], ks * 2,
-                                             0, 0);
+// Direct (global -> LDS) buffer loads written as inline assembly.  Issued
+// through the compiler's intrinsic, a direct load into one LDS stage makes
+// the compiler wait for it before LDS reads it cannot prove to be of the other
+// stage, which serialises the pipeline; the assembly form is invisible to it,
+// and the kernels wait for their direct loads themselves (stage_barrier)
+// before any wave reads a stage.  M0 (the LDS base of the copy) is saved and
+// restored around the load, and one wait state separates its write from the
+// load.  The descriptor is the plain four-word form over [base, base + bytes).
+__device__ __forceinline__ u32x4 raw_rsrc(const void* base, int64_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const auto uni = [](uint32_t v) { return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(v)); };
+  return u32x4{uni(static_cast<uint32_t>(b)), uni(static_cast<uint32_t>(b >> 32) & 0xffffu),
+               uni(static_cast<uint32_t>(bytes)), 0x00020000u};
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t act_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+template <int BYTES>
+__device__ __forceinline__ void lds_load(u32x4 rs, uint8_t* lds, uint32_t voff, int soff) {
+  static_assert(BYTES == 4 || BYTES == 16, "4- or 16-byte direct loads");
+  const uint32_t la = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)lds)));
+  const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(soff));
+  uint32_t saved;
+  if constexpr (BYTES == 16)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(la), "v"(voff), "s"(rs), "s"(so)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(la), "v"(voff), "s"(rs), "s"(so)
+        : "memory");
+}
+
+__device__ __forceinline__ void stage_pairs(u32x4 src, const PairOffs& po, int ks, uint8_t* stage, int w) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) lds_load<16>(src, stage + (8 * w + j) * kChunkBytes, po.off[j], ks * 2);
 }
 
 // B operand reads of a row-pair staged slice: lane (r, q) reads chunk
@@ -737,7 +769,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
                         static_cast<size_t>(s_tok[lane < n ? lane : 0]) * a.H * 2 + w * 8 * 16;
   // int4 with bf16 scales: activations staged as row pairs (whole lines per
   // direct load)
-  const __amdgpu_buffer_rsrc_t xrs = act_rsrc(a.x16, static_cast<int64_t>(a.T) * a.H * 2);
+  const u32x4 xrs = raw_rsrc(a.x16, static_cast<int64_t>(a.T) * a.H * 2);
+  const u32x4 rsa = raw_rsrc(tl.blob, P.blob);
   PairOffs xo;
   if constexpr (kLsb)
     xo = pair_offsets(w, lane, [&](int row) {
@@ -777,8 +810,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
           const int soff = static_cast<int>(3 * P.q + (sb ? 3 + m : m) * P.s) + wrow * sbrow + (kb / 64) * 2;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rs, (lds_void*)(stage + kStageBytes + w * kSbWave + (2 * m + sb) * 256), 4, sb_lane, soff, 0, 0);
+          lds_load<4>(rsa, stage + kStageBytes + w * kSbWave + (2 * m + sb) * 256, sb_lane, soff);
         }
     }
   };
@@ -799,9 +831,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) {
           if constexpr (kLsb) {
-            const uint8_t* sw = stage + kStageBytes + w * kSbWave + 2 * m * 256 + (16 * rr + lrow) * 8 + 4 * S;
-            sc[m][rr] = splat_h2(sb_value<SB>(*reinterpret_cast<const uint32_t*>(sw), lo.sel));
-            bc[m][rr] = splat_h2(sb_value<SB>(*reinterpret_cast<const uint32_t*>(sw + 256), lo.sel));
+            const uint8_t* sw = stage + kStageBytes + w * kSbWave + 2 * m * 256 + (16 * rr + lrow) * 8;
+            const uint2 sv = *reinterpret_cast<const uint2*>(sw), bv = *reinterpret_cast<const uint2*>(sw + 256);
+            sc[m][rr] = splat_h2(sb_value<SB>(S ? sv.y : sv.x, lo.sel));
+            bc[m][rr] = splat_h2(sb_value<SB>(S ? bv.y : bv.x, lo.sel));
           } else {
             sc[m][rr] = splat_h2(sb_value<SB>(wv[m][rr].s, lo.sel));
             bc[m][rr] = splat_h2(sb_value<SB>(wv[m][rr].b, lo.sel));
@@ -951,8 +984,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_down(PfArgs a) {
   }
   const uint8_t* hsrc = reinterpret_cast<const uint8_t*>(a.h) +
                         static_cast<size_t>(s_pair[lane < n ? lane : 0]) * a.hs * 2 + w * 8 * 16;
-  const __amdgpu_buffer_rsrc_t hrs =
-      act_rsrc(a.h, (static_cast<int64_t>(a.T) * a.k + a.T) * a.hs * 2);
+  const u32x4 hrs = raw_rsrc(a.h, (static_cast<int64_t>(a.T) * a.k + a.T) * a.hs * 2);
+  const u32x4 rsa = raw_rsrc(tl.blob, P.blob);
   PairOffs ho;
   if constexpr (kLsb)
     ho = pair_offsets(w, lane, [&](int row) {
@@ -983,9 +1016,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_down(PfArgs a) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         if constexpr (kLsb) {
-          const uint8_t* sw = stage + kStageBytes + w * kSbWave + (16 * rr + r) * 8 + 4 * S;
-          sc[rr] = splat_h2(sb_value<SB>(*reinterpret_cast<const uint32_t*>(sw), lo.sel));
-          bc[rr] = splat_h2(sb_value<SB>(*reinterpret_cast<const uint32_t*>(sw + 512), lo.sel));
+          const uint8_t* sw = stage + kStageBytes + w * kSbWave + (16 * rr + r) * 8;
+          const uint2 sv = *reinterpret_cast<const uint2*>(sw), bv = *reinterpret_cast<const uint2*>(sw + 512);
+          sc[rr] = splat_h2(sb_value<SB>(S ? sv.y : sv.x, lo.sel));
+          bc[rr] = splat_h2(sb_value<SB>(S ? bv.y : bv.x, lo.sel));
         } else {
           sc[rr] = splat_h2(sb_value<SB>(wv[rr].s, lo.sel));
           bc[rr] = splat_h2(sb_value<SB>(wv[rr].b, lo.sel));
@@ -1033,8 +1067,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_down(PfArgs a) {
           for (int half = 0; half < 2; ++half) {
             const int soff = static_cast<int>(3 * P.q + (sb ? 5 : 2) * P.s) +
                              (wrow + g * kDnRows + 32 * half) * sbrow + (ks / 64) * 2;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs, (lds_void*)(stage + kStageBytes + w * kSbWave + sb * 512 + half * 256), 4, sb_lane, soff, 0, 0);
+            lds_load<4>(rsa, stage + kStageBytes + w * kSbWave + sb * 512 + half * 256, sb_lane, soff);
           }
       };
       auto load_codes = [&](StepW<BITS> (&d0)[4], StepW<BITS> (&d1)[4], int st) {
