@@ -134,3 +134,36 @@ def test_prefill_bad_slot_reports_erange_and_drops_the_expert():
     with pytest.raises(M.MoeError) as ei:
         run(upload(data, pool=dl.pool, slots=slots), 32)
     assert ei.value.code == -5
+
+
+def test_prefill_bad_expert_id_reports_erange_and_drops_only_that_pair():
+    """An id outside [0, E) handed to the split API is reported (MOE_ERANGE) and
+    its pair contributes nothing: the output equals the call with that pair's
+    weight set to zero, bit for bit, for every token."""
+    geo = synth.Geometry(256, 16, 2, 256, 256, 4, "bf16", "bf16")
+    data = make_layer(geo, 21, 0, 48, n_cand=128, margin_scale=PF)
+    dl = upload(data)
+    T, k, H, E = data.T, dl.desc.top_k, dl.desc.hidden, dl.desc.n_experts
+    ids = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    wts = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    ws = torch.zeros(M.workspace_bytes(dl.desc, T), dtype=torch.uint8, device=DEV)
+    M.workspace_init(ws)
+    M.router_topk(dl.desc, T, dl.x, dl.R, ids, wts, ws)
+    torch.cuda.synchronize()
+    bad_ids = ids.clone()
+    bad_ids[3, 1] = E + 7
+    out_bad = torch.empty(T, H, dtype=torch.float32, device=DEV)
+    M.experts_forward(dl.desc, T, dl.x, bad_ids, wts, dl.slots, dl.pool, dl.shared, out_bad, ws)
+    torch.cuda.synchronize()
+    with pytest.raises(M.MoeError) as ei:
+        M.status_check(ws)
+    assert ei.value.code == -5
+    zero_w = wts.clone()
+    zero_w[3, 1] = 0.0
+    ws2 = torch.zeros_like(ws)
+    M.workspace_init(ws2)
+    out_zero = torch.empty(T, H, dtype=torch.float32, device=DEV)
+    M.experts_forward(dl.desc, T, dl.x, ids, zero_w, dl.slots, dl.pool, dl.shared, out_zero, ws2)
+    torch.cuda.synchronize()
+    M.status_check(ws2)
+    assert torch.equal(out_bad, out_zero)
