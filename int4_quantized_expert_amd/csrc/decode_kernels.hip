@@ -506,8 +506,22 @@ __global__ __launch_bounds__(256) void k_down(DownArgs a) {
 // Combine: y[t, n] = sum_{i<k} p[t,i] partial[t k + i, n] (i ascending, FMA
 // chain) then + sigmoid(g.x_t) partial_shared[t, n].  Pairs whose id is out of
 // range contribute nothing.
-template <int OUT>
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ partial, const int32_t* __restrict__ ids,
+// Four consecutive partial values as floats: fp32 rows (staged path) or
+// float16 rows (prefill path).
+__device__ __forceinline__ float4 load_part4(const float* p, size_t row, int H, int n4) {
+  return reinterpret_cast<const float4*>(p + row * H)[n4];
+}
+
+__device__ __forceinline__ float4 load_part4(const _Float16* p, size_t row, int H, int n4) {
+  const uint2 v = reinterpret_cast<const uint2*>(p + row * H)[n4];
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 a = __builtin_bit_cast(h2, v.x), b = __builtin_bit_cast(h2, v.y);
+  return make_float4(static_cast<float>(a[0]), static_cast<float>(a[1]), static_cast<float>(b[0]),
+                     static_cast<float>(b[1]));
+}
+
+template <int OUT, typename PT>
+__global__ __launch_bounds__(256) void k_combine(const PT* __restrict__ partial, const int32_t* __restrict__ ids,
                                                  const float* __restrict__ wts, const float* __restrict__ gate,
                                                  void* __restrict__ out, int T, int k, int H, int E) {
   // one thread per 4 consecutive outputs of one token; the partial rows of a
@@ -519,7 +533,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ parti
   if (idx >= static_cast<size_t>(T) * h4) return;
   const int t = static_cast<int>(idx / h4);
   const int n4 = static_cast<int>(idx % h4);
-  const float4 sh = reinterpret_cast<const float4*>(partial + (static_cast<size_t>(T) * k + t) * H)[n4];
+  const float4 sh = load_part4(partial, static_cast<size_t>(T) * k + t, H, n4);
   const float g = gate[t];
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int i0 = 0; i0 < k; i0 += kGroup) {
@@ -532,7 +546,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ parti
       const int e = ids[t * k + i];
       ok[j] = i0 + j < k && e >= 0 && e < E;
       w[j] = wts[t * k + i];
-      p[j] = reinterpret_cast<const float4*>(partial + (static_cast<size_t>(t) * k + i) * H)[n4];
+      p[j] = load_part4(partial, static_cast<size_t>(t) * k + i, H, n4);
     }
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) {
@@ -704,17 +718,24 @@ int launch_experts(const Call& c) {
   return launch_combine(c, partial, gate);
 }
 
-int launch_combine(const Call& c, const float* partial, const float* gate) {
+template <typename PT>
+static int launch_combine_t(const Call& c, const PT* partial, const float* gate) {
   const moe_desc& d = c.d;
   const size_t n = static_cast<size_t>(c.T) * d.hidden / 4;   // one thread per 4 outputs (H % 64 == 0)
   const dim3 grid(static_cast<unsigned>((n + 255) / 256)), block(256);
   if (d.out_dtype == kF32)
-    launch_kernel(k_combine<kF32>, grid, block, 0, c.stream, partial, c.ids, c.wts, gate, c.out, c.T, d.top_k,
+    launch_kernel(k_combine<kF32, PT>, grid, block, 0, c.stream, partial, c.ids, c.wts, gate, c.out, c.T, d.top_k,
                   d.hidden, d.n_experts);
   else
-    launch_kernel(k_combine<kBF16>, grid, block, 0, c.stream, partial, c.ids, c.wts, gate, c.out, c.T, d.top_k,
-                  d.hidden, d.n_experts);
+    launch_kernel(k_combine<kBF16, PT>, grid, block, 0, c.stream, partial, c.ids, c.wts, gate, c.out, c.T,
+                  d.top_k, d.hidden, d.n_experts);
   return last_launch_error();
+}
+
+int launch_combine(const Call& c, const float* partial, const float* gate) { return launch_combine_t(c, partial, gate); }
+
+int launch_combine(const Call& c, const _Float16* partial, const float* gate) {
+  return launch_combine_t(c, partial, gate);
 }
 
 }  // namespace moe

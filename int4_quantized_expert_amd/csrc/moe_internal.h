@@ -30,7 +30,7 @@ struct WsLayout {
   size_t ustart;     // [min(T k, E) + 1] int32 start of each expert's pair list
   size_t plist;      // [T k] int32 pair indices (t * k + i) grouped by expert
   size_t h;          // [T k + T, max(I, SI)] float32 SwiGLU activations
-  size_t partial;    // [T k + T, H] float32 per-pair down projections
+  size_t partial;    // [T k + T, H] per-pair down projections: float32 (decode), float16 (prefill)
   size_t f_lg;       // two-launch path: [kFusedReplicas][Tf, E] tagged logits (uint64), Tf = kFusedMaxT
   size_t f_uoff;     // two-launch path: [min(T k, E)] int64 blob offsets of the distinct experts
   size_t f_pidx;     // two-launch path: [min(T k, E), T] int32 rank of expert u for token t
@@ -130,7 +130,8 @@ int launch_experts(const Call& c);
 // Pieces of the staged path the prefill path shares: per-token top-k of given
 // logits, and the ordered combine of per-pair partial rows.
 int launch_topk(const Call& c, const float* logits, int32_t* ids, float* wts, int32_t* ids2, float* wts2);
-int launch_combine(const Call& c, const float* partial, const float* gate);
+int launch_combine(const Call& c, const float* partial, const float* gate);      // fp32 partial rows
+int launch_combine(const Call& c, const _Float16* partial, const float* gate);   // float16 partial rows
 int launch_ws_init(uint8_t* ws, size_t bytes, hipStream_t stream);
 
 // Prefill path (many tokens): MFMA router and grouped expert GEMMs.

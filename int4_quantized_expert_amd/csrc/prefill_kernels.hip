@@ -15,7 +15,8 @@
 //   k_pf_xprep     x to float16, stored in the k order the MFMA operands use;
 //                  also writes the pair lists
 //   k_pf_gateup    per tile: h = silu(Wg x) * (Wu x), h in float16
-//   k_pf_down      per tile: partial = Wd h, fp32 per (pair, output row)
+//   k_pf_down      per tile: partial = Wd h, fp32 sums stored as float16 per
+//                  (pair, output row)
 //   (k_combine)    the staged path's ordered combine with the shared expert
 //
 // Expert weights are dequantized straight into MFMA A operands: each int4/int8
@@ -279,7 +280,7 @@ struct PfArgs {
   const int32_t* tile_u;
   const int32_t* meta;
   _Float16* h;             // [T k + T, hs] natural k order
-  float* partial;          // [T k + T, H]
+  _Float16* partial;       // [T k + T, H]
   uint32_t* flags;
   int64_t pool_bytes;
   int T, k, H, E, I, SI, hs;
@@ -931,9 +932,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
 
 // Down: block = (tile, n_g consecutive 256-row blocks of H); wave w owns
 // rows 64 w .. +63 (four 16-row MFMA blocks) of each row block for the tile's
-// pairs.  h rows arrive in operand order and are staged like x.  Writes fp32
-// partial rows; a tile of an unusable blob writes zeros, so that expert
-// contributes nothing.
+// pairs.  h rows arrive in operand order and are staged like x.  Writes the
+// fp32 sums rounded to float16 partial rows (half the bytes written here and
+// read back by the combine; like x and h, values must stay inside the float16
+// range); a tile of an unusable blob writes zeros, so that expert contributes
+// nothing.
 // int4 with bf16 scales: the block walks its row blocks one 256-k slice
 // ("step") at a time with the next step's codes in registers and its scales
 // and h slice in the other LDS stage; with K <= 512 the h tile stays
@@ -962,8 +965,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_down(PfArgs a) {
     const int span = G * kDnRows;
     for (int i = tid; i < n * (span / 4); i += kThreads) {
       const int c = i / (span / 4), col = (i % (span / 4)) * 4;
-      *reinterpret_cast<float4*>(a.partial + static_cast<size_t>(s_pair[c]) * a.H + rb * span + col) =
-          make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<uint2*>(a.partial + static_cast<size_t>(s_pair[c]) * a.H + rb * span + col) =
+          make_uint2(0u, 0u);
     }
     return;
   }
@@ -1045,11 +1048,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_down(PfArgs a) {
       for (int ct = 0; ct < NT; ++ct) {
         const int c = 16 * ct + r;
         if (c < n) {
-          float* pr = a.partial + static_cast<size_t>(s_pair[c]) * a.H + row0 + 4 * q;
+          _Float16* pr = a.partial + static_cast<size_t>(s_pair[c]) * a.H + row0 + 4 * q;
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            *reinterpret_cast<float4*>(pr + 16 * rr) =
-                make_float4(acc[rr][ct][0], acc[rr][ct][1], acc[rr][ct][2], acc[rr][ct][3]);
+          for (int rr = 0; rr < 4; ++rr) {
+            const h2v lo = {static_cast<_Float16>(acc[rr][ct][0]), static_cast<_Float16>(acc[rr][ct][1])};
+            const h2v hi = {static_cast<_Float16>(acc[rr][ct][2]), static_cast<_Float16>(acc[rr][ct][3])};
+            *reinterpret_cast<uint2*>(pr + 16 * rr) = make_uint2(h2_bits(lo), h2_bits(hi));
+          }
         }
       }
     };
@@ -1204,7 +1209,7 @@ int launch_prefill_experts(const Call& c) {
   const WsLayout& L = c.L;
   uint32_t* flags = reinterpret_cast<uint32_t*>(ws + L.ctrl);
   float* gate = reinterpret_cast<float*>(ws + L.gate);
-  float* partial = reinterpret_cast<float*>(ws + L.partial);
+  _Float16* partial = reinterpret_cast<_Float16*>(ws + L.partial);
   PfArgs a;
   a.x16 = reinterpret_cast<const u32x4*>(ws + L.p_x16);
   a.slot_table = c.slot_table;
