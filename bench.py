@@ -319,6 +319,9 @@ def kernel_work(desc, geo, T, n_kernels, uniq, prefill, out_bytes):
             ("k_combine", out, None),
         ]
         return table[:n_kernels]
+    if n_kernels == 1:
+        return [("k_decode_a (one launch: router, top-k, gate/up, down, ordered combine)",
+                 router + gvec + 3 * p_s + 3 * p_r * uniq + out, None)]
     if n_kernels == 2:
         return [("k_decode_a (router, shared gate/up, top-k, dispatch, routed gate/up)",
                  router + gvec + 2 * p_s + 2 * p_r * uniq, None),

@@ -399,6 +399,36 @@ __device__ __forceinline__ void stage_h_plain(const FusedArgs& a, const LdsB& s,
   __syncthreads();
 }
 
+// Single launch (T = 1): the token's k + 1 h rows into s.h with loads that
+// bypass this XCD's L2 (scope-of-device, the level the writers' stores were
+// acknowledged at), and the shared-expert gate likewise.
+__device__ __forceinline__ void stage_h_device(const FusedArgs& a, const LdsB& s, int tid) {
+  const int k = a.k;
+  const int r4 = a.hs / 4;
+  const int n4 = (k + 1) * r4;
+  const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(a.h, 0, (k + 1) * a.hs * 4, 0x00020000);
+  constexpr int kScDevice = 16;   // cache policy: scope device (sc1)
+  lds_u32x4* dst = (lds_u32x4*)(s.h);
+  constexpr int kPer = 4;
+  for (int j0 = 0; j0 < n4; j0 += kPer * kThreads) {
+    u32x4 v[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int j = j0 + q * kThreads + tid;
+      v[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hr, (j < n4 ? j : 0) * 16, 0, kScDevice));
+    }
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int j = j0 + q * kThreads + tid;
+      if (j < n4) dst[(j >> 3) * (kSegPad / 4) + (j & 7)] = v[q];
+    }
+  }
+  if (tid == 0) s.sig[0] = __hip_atomic_load(a.sig, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  h_segment_sums(a, s, tid);
+  __syncthreads();
+}
+
 // Ordered combine of the unit's rows: sum over ranks of weight * partial,
 // then the gated shared expert.
 template <int OUT>
@@ -436,8 +466,16 @@ __device__ __forceinline__ float shared_gate(const uint8_t* xrow, const uint8_t*
 }
 
 // ---------------------------------------------------------------------------
-// Launch A: phases R, K, G.
-template <int BITS, int SB, int ACT>
+// Launch A: phases R, K, G.  With ONE (T = 1 only) the same blocks then run
+// launch B's work as well, with no second launch: h and the shared-expert
+// gate are written with scope-of-device stores, every block raises a tagged
+// completion flag once its stores are acknowledged, and after every block's
+// flag is seen a block requests the codes of its down unit, stages h with
+// scope-of-device loads, finishes its down rows and the ordered combine, and
+// advances the epoch counters itself.  (Requesting the down codes before
+// phase G instead made the waves wait for them there, about 2 us, and was no
+// faster overall.)
+template <int BITS, int SB, int ACT, int OUT = kF32, bool ONE = false>
 __global__ __launch_bounds__(kThreadsA) void k_decode_a(FusedArgs a) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   const LdsA s = carve_a(lds_raw, a);
@@ -528,7 +566,10 @@ __global__ __launch_bounds__(kThreadsA) void k_decode_a(FusedArgs a) {
   __syncthreads();
   const uint32_t tag = static_cast<uint32_t>(s.misc[1]);
   const int gwave = wave * a.nb + blockIdx.x;
-  auto put_h = [&](size_t row, int r, float v) { a.h[row * a.hs + r] = v; };
+  auto put_h = [&](size_t row, int r, float v) {
+    if constexpr (ONE) __hip_atomic_store(a.h + row * a.hs + r, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else a.h[row * a.hs + r] = v;
+  };
 
   // ---- phase R
   for (int task = r_task0; task < router_tasks; task += nwaves * kRouterRowsPerWave) {
@@ -592,7 +633,10 @@ __global__ __launch_bounds__(kThreadsA) void k_decode_a(FusedArgs a) {
   if (blockIdx.x == 0 && wave == kWavesA - 1) {
     for (int t = 0; t < T; ++t) {
       const float g = shared_gate<ACT>(s.x + t * xrow, a.shared + a.shared_stride, H, lane);
-      if (lane == 0) a.sig[t] = g;
+      if (lane == 0) {
+        if constexpr (ONE) __hip_atomic_store(a.sig + t, g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else a.sig[t] = g;
+      }
     }
   }
 
@@ -699,6 +743,18 @@ __global__ __launch_bounds__(kThreadsA) void k_decode_a(FusedArgs a) {
       a.uoff[i] = s.slot[s.uniq[i]];
     }
     if (tid == 0) *a.ucount = U;
+  }
+  // ---- single launch: the routing of this block's down unit
+  int slice = 0, ut = 0;
+  bool has_unit = false;
+  LdsB sb{};
+  if constexpr (ONE) {
+    sb = carve_b(lds_raw + a.lds_b_off, a);
+    if (tid < k) {
+      sb.poff[tid] = s.slot[s.ids[tid]];
+      sb.wts[tid] = s.vals[tid];
+    }
+    has_unit = unit_of(a.nslice, 1, &slice, &ut);
   }
   // ---- phase G: routed gate/up rows, flattened over (expert, row group)
   {
@@ -854,6 +910,42 @@ __global__ __launch_bounds__(kThreadsA) void k_decode_a(FusedArgs a) {
       else run(IntC<0>{});
     }
   }
+  if constexpr (ONE) {
+    // this block's h and gate stores are acknowledged (scope device), then its
+    // flag goes out in every replica; wait for every block's flag
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid < kFusedReplicas)
+      __hip_atomic_store(a.gflags + tid * kFusedMaxBlocks + blockIdx.x, tag, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t* fl = a.gflags + (blockIdx.x % kFusedReplicas) * kFusedMaxBlocks;
+    uint32_t fspins = 0;
+    bool flags_out = false;
+    for (;;) {
+      int missing = 0;
+      for (int j = tid; j < a.nb; j += kThreadsA)
+        if (__hip_atomic_load(fl + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag) missing = 1;
+      if (!__syncthreads_or(missing)) break;
+      if (++fspins > a.spin_limit) { flags_out = true; break; }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (flags_out) timed_out = true;
+    if (has_unit && !flags_out) {
+      // the down codes are requested first, then h is staged while they arrive
+      DOWN_SETUP(BITS, SB, a, slice, lane);
+      DownTask<BITS> dt[kMaxDownPerWave];
+      issue_down_round<BITS, SB>(dt, 0, ntask, dc, lo, rli, rls, row_lo, a, sb, wave);
+      stage_h_device(a, sb, tid);
+      compute_down_round<BITS, SB>(dt, rli, rls, a, sb, 1, 0, lane);
+      __syncthreads();
+      combine_unit<OUT>(a, sb, row_lo, 0, tid);
+    }
+    // every block has read its epoch counter (at its start, before its flag):
+    // advance them, the ones past the grid by block 0
+    if (tid == 0) a.epochs[blockIdx.x] = a.epochs[blockIdx.x] + 1u;
+    if (blockIdx.x == 0)
+      for (int j = a.nb + tid; j < kFusedMaxBlocks; j += kThreadsA) a.epochs[j] = a.epochs[j] + 1u;
+  }
   if (timed_out && lane == 0) raise_error(a.ctrl, kErrTimeout);
 }
 
@@ -947,16 +1039,25 @@ size_t lds_bytes_b(int k, int rb, int hs) {
 
 template <int BITS, int SB, int ACT, int OUT>
 static int launch_variant(const FusedArgs& a, const FusedPlan& p, hipStream_t stream) {
-  launch_kernel(k_decode_a<BITS, SB, ACT>, dim3(p.nb), dim3(kThreadsA), p.lds, stream, a);
-  launch_kernel(k_decode_b<BITS, SB, OUT>, dim3(p.nb_b), dim3(kThreads), p.lds_b, stream, a);
+  if (BITS == 4 && p.one) {
+    // int4 only (the int8 variant would not fit its registers)
+    if constexpr (BITS == 4)
+      launch_kernel(k_decode_a<BITS, SB, ACT, OUT, true>, dim3(p.nb), dim3(kThreadsA), p.lds_one, stream, a);
+  } else {
+    launch_kernel(k_decode_a<BITS, SB, ACT>, dim3(p.nb), dim3(kThreadsA), p.lds, stream, a);
+    launch_kernel(k_decode_b<BITS, SB, OUT>, dim3(p.nb_b), dim3(kThreads), p.lds_b, stream, a);
+  }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 template <int BITS, int SB, int ACT, int OUT>
-static int occupancy_variant(size_t lds, int* blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_decode_a<BITS, SB, ACT>, kThreadsA, lds) == hipSuccess
-             ? MOE_OK
-             : MOE_EHIP;
+static int occupancy_variant(size_t lds, int* blocks, bool one) {
+  hipError_t e = hipErrorInvalidValue;
+  if constexpr (BITS == 4) {
+    if (one) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_decode_a<BITS, SB, ACT, OUT, true>, kThreadsA, lds);
+  }
+  if (!one) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_decode_a<BITS, SB, ACT>, kThreadsA, lds);
+  return e == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 #define FUSED_DISPATCH(FN, ...)                                                            \
@@ -971,7 +1072,9 @@ static int occupancy_variant(size_t lds, int* blocks) {
     return MOE_EINVAL;                                                                     \
   } while (0)
 
-static int fused_occupancy(const moe_desc& d, size_t lds, int* blocks) { FUSED_DISPATCH(occupancy_variant, lds, blocks); }
+static int fused_occupancy(const moe_desc& d, size_t lds, int* blocks, bool one) {
+  FUSED_DISPATCH(occupancy_variant, lds, blocks, one);
+}
 
 static int fused_launch(const moe_desc& d, const FusedArgs& a, const FusedPlan& p, hipStream_t s) {
   FUSED_DISPATCH(launch_variant, a, p, s);
@@ -981,6 +1084,12 @@ bool fused_supported(const moe_desc& d, int T) {
   if (T < 1 || T > kFusedMaxT) return false;
   const int s = d.sb_dtype, a = d.act_dtype;
   return (s == kBF16 && a == kBF16) || (s == kF32 && a == kF32 && d.out_dtype == kF32);
+}
+
+// Rows per wave pass of row_lanes (host side).
+static int row_lanes_rpp(int cols) {
+  const int spr = cols / kSegCodes;
+  return spr >= kWave ? 1 : kWave / spr;
 }
 
 int fused_plan(const moe_desc& d, int T, FusedPlan* plan) {
@@ -998,7 +1107,7 @@ int fused_plan(const moe_desc& d, int T, FusedPlan* plan) {
     const int nb = cus * per_cu;
     if (nb > kFusedMaxBlocks) continue;
     int fit = 0;
-    if (fused_occupancy(d, lds, &fit) != MOE_OK) return MOE_EHIP;
+    if (fused_occupancy(d, lds, &fit, false) != MOE_OK) return MOE_EHIP;
     if (fit >= per_cu) {
       plan->nb = nb;
       plan->lds = lds;
@@ -1010,6 +1119,20 @@ int fused_plan(const moe_desc& d, int T, FusedPlan* plan) {
       plan->nslice = (d.hidden + plan->rb_b - 1) / plan->rb_b;
       plan->nb_b = (plan->nslice * T + kXcds - 1) / kXcds * kXcds;
       plan->lds_b = lds_bytes_b(d.top_k, plan->rb_b, hs);
+      // T = 1 in one launch: every down unit on its own block of launch A, the
+      // h rows staged in LDS, one round of down tasks per wave, and a resident
+      // block per CU with both phases' LDS
+      plan->one = false;
+      plan->lds_one = (lds + 15) / 16 * 16 + plan->lds_b;
+      if (T == 1 && d.bits == 4 && plan->nslice <= nb && h_staged(d.top_k, hs) && plan->lds_one <= 64 * 1024) {
+        const int rpp_i = row_lanes_rpp(d.inter), rpp_s = row_lanes_rpp(d.shared_inter);
+        const int rpp_min = rpp_i < rpp_s ? rpp_i : rpp_s;
+        const int ntask = (d.top_k + 1) * ((plan->rb_b + rpp_min - 1) / rpp_min);
+        int fit1 = 0;
+        if (ntask <= kWaves * kMaxDownPerWave && fused_occupancy(d, plan->lds_one, &fit1, true) == MOE_OK &&
+            fit1 >= 1)
+          plan->one = true;
+      }
       return MOE_OK;
     }
   }
@@ -1049,6 +1172,8 @@ int launch_decode_fused(const Call& c, const FusedPlan& plan) {
   a.rb = plan.rb_b;
   a.nslice = plan.nslice;
   a.epochs = reinterpret_cast<uint32_t*>(c.ws + c.L.f_epoch);
+  a.gflags = reinterpret_cast<uint32_t*>(c.ws + c.L.f_gflag);
+  a.lds_b_off = (plan.lds + 15) / 16 * 16;
   a.umax = plan.umax;
   a.act_sz = d.act_dtype == kF32 ? 4 : 2;
   a.spin_limit = 1u << 20;

@@ -28,6 +28,8 @@ struct FusedArgs {
   int32_t* pidx;        // [umax, T] rank of expert u for token t, or -1
   uint32_t* ctrl;       // [0] error flags
   uint32_t* epochs;     // [kFusedMaxBlocks] per-block call counters (tag = counter + 1)
+  uint32_t* gflags;     // [kFusedReplicas][kFusedMaxBlocks] single launch: tag of each block whose h is written
+  size_t lds_b_off;     // single launch: where the down-phase LDS starts
   int64_t pool_bytes;
   int64_t shared_stride;
   int T, H, E, k, I, SI, hs;
@@ -47,6 +49,8 @@ struct FusedPlan {
   int rb_b;     // launch B rows per block
   int nslice;   // launch B row slices
   size_t lds_b; // launch B dynamic LDS
+  bool one;     // T = 1 in a single launch (the down phase runs in launch A's blocks)
+  size_t lds_one;
 };
 
 }  // namespace moe

@@ -35,6 +35,7 @@ struct WsLayout {
   size_t f_uoff;     // two-launch path: [min(T k, E)] int64 blob offsets of the distinct experts
   size_t f_pidx;     // two-launch path: [min(T k, E), T] int32 rank of expert u for token t
   size_t f_epoch;    // two-launch path: [kFusedMaxBlocks] uint32 per-block call counters (inside ctrl)
+  size_t f_gflag;    // single-launch decode: [kFusedReplicas][kFusedMaxBlocks] uint32 completion tags
   size_t p_x16;      // prefill: [T, H] float16 activations in MFMA k order
   size_t p_meta;     // prefill: int32 [0] number of expert tiles
   size_t p_tstart;   // prefill: [min(T k, E) + 2] int32 first tile of each distinct expert, then of the shared one
@@ -63,6 +64,7 @@ inline WsLayout ws_layout(const moe_desc& d, int32_t T) {
   L.f_epoch = L.ctrl + 256;
   const size_t Tf = kFusedMaxT;
   L.f_lg = take(static_cast<size_t>(kFusedReplicas) * Tf * d.n_experts * 8);
+  L.f_gflag = take(static_cast<size_t>(kFusedReplicas) * kFusedMaxBlocks * 4);
   L.logits = take(static_cast<size_t>(T) * d.n_experts * 4);
   L.ids = take(Tk * 4);
   L.wts = take(Tk * 4);

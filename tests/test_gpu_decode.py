@@ -218,7 +218,7 @@ def test_launch_event_hook_times_each_kernel():
     data = make_layer(synth.PRESETS["80b"], 4, 9, 1, routing="zipf", n_cand=32)
     dl = upload(data, "f32")
     ref = run(dl, 1)
-    for staged, kernels in ((False, 2), (True, 6)):
+    for staged, kernels in ((False, 1), (True, 6)):   # T = 1 runs in one launch
         timer = M.LaunchTimer(16)
         timer.arm()
         got = run(dl, 1, staged=staged)
