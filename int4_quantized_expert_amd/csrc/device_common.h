@@ -142,6 +142,46 @@ __device__ __forceinline__ void load_f32_seg(const float* row, int seg, float (&
 typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
+// Direct (global -> LDS) buffer loads written as inline assembly.  Issued
+// through the compiler's intrinsic, a direct load into one LDS stage makes
+// the compiler wait for it before LDS reads it cannot prove to be of the other
+// stage, which serialises the pipeline; the assembly form is invisible to it,
+// and the kernels wait for their direct loads themselves (s_waitcnt 0, then a
+// barrier) before any wave reads the copied bytes.  M0 (the LDS base of the copy) is saved and
+// restored around the load, and one wait state separates its write from the
+// load.  The descriptor is the plain four-word form over [base, base + bytes).
+__device__ __forceinline__ u32x4 raw_rsrc(const void* base, int64_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const auto uni = [](uint32_t v) { return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(v)); };
+  return u32x4{uni(static_cast<uint32_t>(b)), uni(static_cast<uint32_t>(b >> 32) & 0xffffu),
+               uni(static_cast<uint32_t>(bytes)), 0x00020000u};
+}
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+template <int BYTES>
+__device__ __forceinline__ void lds_load(u32x4 rs, uint8_t* lds, uint32_t voff, int soff) {
+  static_assert(BYTES == 4 || BYTES == 16, "4- or 16-byte direct loads");
+  const uint32_t la = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)lds)));
+  const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(soff));
+  uint32_t saved;
+  if constexpr (BYTES == 16)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(la), "v"(voff), "s"(rs), "s"(so)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(la), "v"(voff), "s"(rs), "s"(so)
+        : "memory");
+}
+
+
 // 32 floats of one segment from LDS (p points into shared memory; the cast
 // makes the compiler use LDS instructions rather than generic ones).
 __device__ __forceinline__ void load_lds_seg(const float* p, int seg, float (&v)[kSegCodes]) {
