@@ -326,6 +326,85 @@ __device__ __forceinline__ void issue_down_round(DownTask<BITS> (&dt)[kMaxDownPe
   }
 }
 
+// Single launch: a block's down operands are copied into LDS by direct loads
+// issued right after the block raises its flag, so that they arrive while it
+// waits for every other block's.  Per wave, d_slots slots of
+// [64 lanes x 16 code bytes][64 scale words][64 bias words]; lane l's code
+// chunk sits at 16 l and its scale and bias words at 4 l.
+constexpr int kDownSlotBytes = kWave * 16 + 2 * kWave * 4;
+
+__device__ __forceinline__ uint8_t* down_slot(uint8_t* lds_raw, const FusedArgs& a, int wave, int q) {
+  return lds_raw + a.lds_d_off + static_cast<size_t>(wave * a.d_slots + q) * kDownSlotBytes;
+}
+
+// Issues the direct loads of this wave's tasks and fills their rank, row and
+// validity as load_down_task does; sc and bi hold, until read_down, the shift
+// that selects a 2-byte value within its aligned word.  The blob of pair
+// rank i < k is at slot[ids[i]] (the token's experts and the slot table, in
+// LDS); a dead task (past ntask or past d_slots) gets rank -1 and no loads.
+template <int BITS, int SB>
+__device__ __forceinline__ void prefetch_down(DownTask<BITS> (&dt)[kMaxDownPerWave], uint8_t* lds_raw, int ntask,
+                                              const DownCtx& c, int row_lo, const FusedArgs& a, const int64_t* slot,
+                                              const int32_t* ids, const RowLanes& rli, const RowLanes& rls, int wave) {
+  static_assert(BITS == 4, "one 16-byte code chunk per lane");
+  const int k = a.k;
+  const int sbsz = SB == kF32 ? 4 : 2;
+#pragma unroll
+  for (int q = 0; q < kMaxDownPerWave; ++q) {
+    const int task = wave + q * kWaves;
+    dt[q].i = -1;
+    if (q >= a.d_slots || task >= ntask) continue;
+    const int i = c.np == 1 ? task : task / c.np;
+    const int p = c.np == 1 ? 0 : task - i * c.np;
+    const bool is_sh = i == k;
+    const int rpp = is_sh ? rls.rpp : rli.rpp;
+    const int sub_row = is_sh ? rls.sub_row : rli.sub_row;
+    const int seg0 = is_sh ? rls.seg0 : rli.seg0;
+    const int64_t q_b = is_sh ? c.q_s : c.q_r;
+    const int64_t s_b = is_sh ? c.s_s : c.s_r;
+    const int64_t off = is_sh ? 0 : slot[ids[i]];
+    const bool valid = is_sh || slot_ok(off, c.blob_r, a.pool_bytes);
+    const uint8_t* blob = is_sh ? a.shared : a.pool + (valid ? off : 0);
+    const int rloc = p * rpp + sub_row;
+    const int r0 = row_lo + rloc;
+    const bool in = rloc < a.rb && r0 < a.H;
+    const int r = in ? r0 : row_lo;
+    const uint32_t code = static_cast<uint32_t>(2 * q_b + r * (is_sh ? c.rowb_s : c.rowb_r) + seg0 * (kSegCodes * BITS / 8));
+    const int64_t si = static_cast<int64_t>(r) * (is_sh ? c.gpr_s : c.gpr_r) + seg0 / 2;
+    const uint32_t sc = static_cast<uint32_t>(3 * q_b + 2 * s_b + si * sbsz);
+    const uint32_t bi = static_cast<uint32_t>(3 * q_b + 5 * s_b + si * sbsz);
+    // the blob's data; an unusable blob reads zeros
+    const u32x4 rs = raw_rsrc(blob, valid ? 3 * q_b + 6 * s_b : 0);
+    uint8_t* sl = down_slot(lds_raw, a, wave, q);
+    lds_load<16>(rs, sl, code, 0);
+    lds_load<4>(rs, sl + kWave * 16, sc & ~3u, 0);
+    lds_load<4>(rs, sl + kWave * 20, bi & ~3u, 0);
+    dt[q].i = i;
+    dt[q].rloc = in ? rloc : -1;
+    dt[q].valid = valid;
+    dt[q].sc = 8 * (sc & 2u);
+    dt[q].bi = 8 * (bi & 2u);
+  }
+}
+
+// The operands of prefetch_down's tasks, read back from LDS once the wave
+// has waited for its direct loads.
+template <int BITS, int SB>
+__device__ __forceinline__ void read_down(DownTask<BITS> (&dt)[kMaxDownPerWave], uint8_t* lds_raw,
+                                          const FusedArgs& a, int wave, int lane) {
+  typedef __attribute__((address_space(3))) const uint32_t lds_w;
+#pragma unroll
+  for (int q = 0; q < kMaxDownPerWave; ++q) {
+    if (dt[q].i < 0) continue;
+    const lds_u8* sl = (const lds_u8*)(down_slot(lds_raw, a, wave, q));
+    dt[q].code.w[0] = *(const lds_u32x4*)(sl + 16 * lane);
+    const uint32_t sw = *(lds_w*)(sl + kWave * 16 + 4 * lane);
+    const uint32_t bw = *(lds_w*)(sl + kWave * 20 + 4 * lane);
+    dt[q].sc = SB == kF32 ? sw : sw >> dt[q].sc;
+    dt[q].bi = SB == kF32 ? bw : bw >> dt[q].bi;
+  }
+}
+
 __device__ __forceinline__ size_t h_row_of(int T, int k, int t, int i) {
   return i < k ? static_cast<size_t>(t) * k + i : static_cast<size_t>(T) * k + t;
 }
@@ -918,6 +997,13 @@ __global__ __launch_bounds__(kThreadsA) void k_decode_a(FusedArgs a) {
     if (tid < kFusedReplicas)
       __hip_atomic_store(a.gflags + tid * kFusedMaxBlocks + blockIdx.x, tag, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
+    // this block's down operands travel to LDS during the wait
+    DownTask<BITS> dt[kMaxDownPerWave];
+    if (has_unit) {
+      DOWN_SETUP(BITS, SB, a, slice, lane);
+      (void)lo;
+      prefetch_down<BITS, SB>(dt, lds_raw, ntask, dc, row_lo, a, s.slot, s.ids, rli, rls, wave);
+    }
     const uint32_t* fl = a.gflags + (blockIdx.x % kFusedReplicas) * kFusedMaxBlocks;
     uint32_t fspins = 0;
     bool flags_out = false;
@@ -929,13 +1015,19 @@ __global__ __launch_bounds__(kThreadsA) void k_decode_a(FusedArgs a) {
       if (++fspins > a.spin_limit) { flags_out = true; break; }
       __builtin_amdgcn_s_sleep(2);
     }
-    if (flags_out) timed_out = true;
+    if (flags_out) {
+      timed_out = true;
+      __builtin_amdgcn_s_waitcnt(0);   // no direct load outlives the block
+    }
     if (has_unit && !flags_out) {
-      // the down codes are requested first, then h is staged while they arrive
-      DOWN_SETUP(BITS, SB, a, slice, lane);
-      DownTask<BITS> dt[kMaxDownPerWave];
-      issue_down_round<BITS, SB>(dt, 0, ntask, dc, lo, rli, rls, row_lo, a, sb, wave);
+      // stage h (its loads wait for the direct ones too: one counter, in
+      // order), then the down rows from LDS
+      const RowLanes rli = row_lanes(a.I, lane);
+      const RowLanes rls = row_lanes(a.SI, lane);
+      const int row_lo = slice * a.rb;
       stage_h_device(a, sb, tid);
+      __builtin_amdgcn_s_waitcnt(0);
+      read_down<BITS, SB>(dt, lds_raw, a, wave, lane);
       compute_down_round<BITS, SB>(dt, rli, rls, a, sb, 1, 0, lane);
       __syncthreads();
       combine_unit<OUT>(a, sb, row_lo, 0, tid);
@@ -1054,7 +1146,13 @@ template <int BITS, int SB, int ACT, int OUT>
 static int occupancy_variant(size_t lds, int* blocks, bool one) {
   hipError_t e = hipErrorInvalidValue;
   if constexpr (BITS == 4) {
-    if (one) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_decode_a<BITS, SB, ACT, OUT, true>, kThreadsA, lds);
+    if (one) {
+      // the single launch may take more than the default 64 KB of dynamic LDS
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_decode_a<BITS, SB, ACT, OUT, true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_decode_a<BITS, SB, ACT, OUT, true>, kThreadsA, lds);
+    }
   }
   if (!one) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_decode_a<BITS, SB, ACT>, kThreadsA, lds);
   return e == hipSuccess ? MOE_OK : MOE_EHIP;
@@ -1122,16 +1220,22 @@ int fused_plan(const moe_desc& d, int T, FusedPlan* plan) {
       // T = 1 in one launch: every down unit on its own block of launch A, the
       // h rows staged in LDS, one round of down tasks per wave, and a resident
       // block per CU with both phases' LDS
+      // (plus the prefetched down operands; blob offsets fit 32 bits)
       plan->one = false;
-      plan->lds_one = (lds + 15) / 16 * 16 + plan->lds_b;
-      if (T == 1 && d.bits == 4 && plan->nslice <= nb && h_staged(d.top_k, hs) && plan->lds_one <= 64 * 1024) {
-        const int rpp_i = row_lanes_rpp(d.inter), rpp_s = row_lanes_rpp(d.shared_inter);
-        const int rpp_min = rpp_i < rpp_s ? rpp_i : rpp_s;
-        const int ntask = (d.top_k + 1) * ((plan->rb_b + rpp_min - 1) / rpp_min);
+      const int rpp_i = row_lanes_rpp(d.inter), rpp_s = row_lanes_rpp(d.shared_inter);
+      const int rpp_min = rpp_i < rpp_s ? rpp_i : rpp_s;
+      const int ntask = (d.top_k + 1) * ((plan->rb_b + rpp_min - 1) / rpp_min);
+      plan->d_slots = (ntask + kWaves - 1) / kWaves;
+      plan->lds_one = (lds + 15) / 16 * 16 + (plan->lds_b + 15) / 16 * 16 +
+                      static_cast<size_t>(kWaves) * plan->d_slots * kDownSlotBytes;
+      int lds_max = 0;
+      if (hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+        return MOE_ENODEV;
+      const int64_t ext = planes_of(d.hidden, hs, d.bits, d.sb_dtype).blob;
+      if (T == 1 && d.bits == 4 && plan->nslice <= nb && h_staged(d.top_k, hs) &&
+          plan->lds_one <= static_cast<size_t>(lds_max) && ntask <= kWaves * kMaxDownPerWave && ext < (1ll << 31)) {
         int fit1 = 0;
-        if (ntask <= kWaves * kMaxDownPerWave && fused_occupancy(d, plan->lds_one, &fit1, true) == MOE_OK &&
-            fit1 >= 1)
-          plan->one = true;
+        if (fused_occupancy(d, plan->lds_one, &fit1, true) == MOE_OK && fit1 >= 1) plan->one = true;
       }
       return MOE_OK;
     }
@@ -1174,6 +1278,8 @@ int launch_decode_fused(const Call& c, const FusedPlan& plan) {
   a.epochs = reinterpret_cast<uint32_t*>(c.ws + c.L.f_epoch);
   a.gflags = reinterpret_cast<uint32_t*>(c.ws + c.L.f_gflag);
   a.lds_b_off = (plan.lds + 15) / 16 * 16;
+  a.lds_d_off = a.lds_b_off + (plan.lds_b + 15) / 16 * 16;
+  a.d_slots = plan.d_slots;
   a.umax = plan.umax;
   a.act_sz = d.act_dtype == kF32 ? 4 : 2;
   a.spin_limit = 1u << 20;

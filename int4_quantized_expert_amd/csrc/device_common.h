@@ -147,9 +147,11 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 // the compiler wait for it before LDS reads it cannot prove to be of the other
 // stage, which serialises the pipeline; the assembly form is invisible to it,
 // and the kernels wait for their direct loads themselves (s_waitcnt 0, then a
-// barrier) before any wave reads the copied bytes.  M0 (the LDS base of the copy) is saved and
-// restored around the load, and one wait state separates its write from the
-// load.  The descriptor is the plain four-word form over [base, base + bytes).
+// barrier when other waves read the copied bytes).  Lane l's bytes land at
+// lds + BYTES * l.  M0 (the LDS base of the copy) is saved and restored around
+// the load, and one wait state separates its write from the load.  The
+// descriptor is the plain four-word form over [base, base + bytes); a load
+// past its end reads zeros.
 __device__ __forceinline__ u32x4 raw_rsrc(const void* base, int64_t bytes) {
   const uint64_t b = reinterpret_cast<uint64_t>(base);
   const auto uni = [](uint32_t v) { return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(v)); };

@@ -30,6 +30,8 @@ struct FusedArgs {
   uint32_t* epochs;     // [kFusedMaxBlocks] per-block call counters (tag = counter + 1)
   uint32_t* gflags;     // [kFusedReplicas][kFusedMaxBlocks] single launch: tag of each block whose h is written
   size_t lds_b_off;     // single launch: where the down-phase LDS starts
+  size_t lds_d_off;     // single launch: where the prefetched down operands start
+  int d_slots;          // single launch: down task slots per wave
   int64_t pool_bytes;
   int64_t shared_stride;
   int T, H, E, k, I, SI, hs;
@@ -51,6 +53,7 @@ struct FusedPlan {
   size_t lds_b; // launch B dynamic LDS
   bool one;     // T = 1 in a single launch (the down phase runs in launch A's blocks)
   size_t lds_one;
+  int d_slots;  // single launch: down task slots per wave (operands prefetched into LDS)
 };
 
 }  // namespace moe
