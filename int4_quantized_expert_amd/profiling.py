@@ -45,8 +45,38 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
+def _unmangle(name: str) -> str | None:
+    """`_ZN3moe12_GLOBAL__N_19k_combineILi1EDF16_EEv...` -> `k_combine<1, _Float16>`.
+
+    rocprofv3 leaves some template kernels mangled; only the forms the library
+    uses are read (integer, bool, float and _Float16 template arguments).
+    """
+    m = re.match(r"_ZN3moe(?:12_GLOBAL__N_1)?(\d+)", name)
+    if not m:
+        return None
+    n = int(m.group(1))
+    ident, rest = name[m.end():m.end() + n], name[m.end() + n:]
+    if not rest.startswith("I"):
+        return ident
+    args, pos = [], 1
+    while pos < len(rest) and rest[pos] != "E":
+        t = re.match(r"L[ib](-?\d+)E|DF16_|f", rest[pos:])
+        if not t:
+            return ident
+        args.append(t.group(1) if t.group(1) is not None else ("_Float16" if t.group(0) == "DF16_" else "float"))
+        pos += t.end()
+    return f"{ident}<{', '.join(args)}>"
+
+
+def is_library_kernel(name: str) -> bool:
+    return name.startswith(("void moe::", "moe::", "_ZN3moe"))
+
+
 def short_name(kernel: str) -> str:
     """`void moe::(anonymous namespace)::k_decode_a<4, 1, 1>(moe::FusedArgs)` -> `k_decode_a<4, 1, 1>`."""
+    un = _unmangle(kernel)
+    if un is not None:
+        return un
     name = re.sub(r"^void ", "", kernel.replace("(anonymous namespace)::", "")).strip()
     m = re.match(r"[\w:]*?(\w+(?:<[^()]*>)?)\s*(?:\(|$)", name)
     return m.group(1) if m else name
@@ -68,7 +98,7 @@ def traffic_table(fetch_csv: str, write_csv: str, copy_bytes: int) -> dict:
     f_scale, w_scale = max(f[COPY_KERNEL]) / kib, max(w[COPY_KERNEL]) / kib
     rows = {}
     for name in f:
-        if not (name.startswith("void moe::") or name.startswith("moe::")) or name not in w:
+        if not is_library_kernel(name) or name not in w:
             continue
         fk = sum(f[name]) / len(f[name])
         wk = sum(w[name]) / len(w[name])

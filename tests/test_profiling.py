@@ -35,3 +35,14 @@ def test_traffic_scaled_by_copy_and_keyed_by_digest(tmp_path):
     text = (out / "x.md").read_text().replace(P.source_digest(), "0" * 64)
     (out / "x.md").write_text(text)
     assert P.load_traffic(str(out), "wl", 1) is None, "a summary of other sources must not be used"
+
+
+def test_kernel_names_demangled_or_shortened():
+    # rocprofv3 prints some template kernels mangled, others demangled
+    assert P.short_name("_ZN3moe12_GLOBAL__N_19k_combineILi1EDF16_EEvPKT0_PKiPKfS8_Pviiii") == "k_combine<1, _Float16>"
+    assert P.short_name("_ZN3moe12_GLOBAL__N_19k_combineILi0EfEEvPKT0_PKiPKfS8_Pviiii") == "k_combine<0, float>"
+    assert P.short_name("void moe::(anonymous namespace)::k_decode_a<4, 1, 1, 0, true>(moe::FusedArgs)") == \
+        "k_decode_a<4, 1, 1, 0, true>"
+    assert P.short_name("moe::(anonymous namespace)::k_topk(float const*, int, int, int*, float*)") == "k_topk"
+    assert P.is_library_kernel("_ZN3moe12_GLOBAL__N_19k_combineILi1EDF16_EEvPKT0_PKiPKfS8_Pviiii")
+    assert not P.is_library_kernel(P.COPY_KERNEL)
