@@ -70,6 +70,8 @@ extern "C" {
 #define MOE_ETIMEOUT (-7) /* the fused decode kernel's bounded wait expired: some
                              of its blocks never became resident (the GPU was
                              shared with other work); the output is invalid    */
+#define MOE_EIO (-8)      /* expert store: a file could not be opened, read or
+                             written, or it is not a store of the stated shape */
 
 /* Storage dtypes. */
 #define MOE_F32 0
@@ -282,7 +284,69 @@ int moe_cache_slot_of(const moe_cache* cache, int32_t layer, int32_t id);
 
 void moe_cache_destroy(moe_cache* cache);
 
-/* Text of the last moe_cache_* error on this thread. */
+/* ------------------------------------------------------------------------
+ * Expert store: the slow tier as one container file on disk.
+ *
+ * The pages repack the routed experts into fixed-stride blobs in one
+ * container, so that fetching an expert is one positioned read at an offset
+ * computed from its (layer, id), without mapping the file into memory
+ * (linlog.top article, core design 2, fixed-stride reads; Swiftlet README
+ * translation, "How it works"; kerneldigest.dev article, inference flow, the
+ * cache-miss step).  File layout (little-endian):
+ *   bytes [0, 4096): header = 8-byte magic "MOEBLOB1", int32 n_layers,
+ *     int32 n_experts, int64 stride, int64 blob_bytes, zeros to 4096;
+ *   blob (layer, id) at 4096 + (layer * n_experts + id) * stride, stride
+ *     bytes, laid out as a pool blob (moe_blob_bytes() <= stride).
+ * stride is a positive multiple of 4096, so every blob is page-aligned in the
+ * file (positioned reads with O_DIRECT need that).  Errors of the moe_store_*
+ * calls are reported by moe_cache_last_error().
+ */
+typedef struct moe_store moe_store;
+
+#define MOE_STORE_DIRECT 1   /* moe_store_open: read with O_DIRECT, past the
+                                page cache (not every file system allows it) */
+
+/* Creates (or truncates) the file, writes the header and sizes the file;
+ * the blobs read as zeros until written.  NULL on error. */
+moe_store* moe_store_create(const char* path, int32_t n_layers, int32_t n_experts, int64_t stride,
+                            int64_t blob_bytes);
+
+/* Opens a store read-only; flags = 0 or MOE_STORE_DIRECT.  NULL on error
+ * (bad magic or shape, file shorter than its header says: MOE_EIO). */
+moe_store* moe_store_open(const char* path, int32_t flags);
+
+int moe_store_info(const moe_store* store, int32_t* n_layers, int32_t* n_experts, int64_t* stride,
+                   int64_t* blob_bytes);
+
+/* One positioned read of blob (layer, id): stride bytes into dst_host.
+ * A MOE_STORE_DIRECT store reads into its own page-aligned buffer and copies
+ * out (direct transfers into HIP pinned memory fail).  Blocking.  MOE_EINVAL
+ * or MOE_EIO.  One thread per store. */
+int moe_store_read(moe_store* store, int32_t layer, int32_t id, void* dst_host);
+
+/* Writes stride bytes from src_host as blob (layer, id) of a store made by
+ * moe_store_create.  Blocking. */
+int moe_store_write(moe_store* store, int32_t layer, int32_t id, const void* src_host);
+
+/* Closes the file.  A cache made on the store must be destroyed first. */
+void moe_store_close(moe_store* store);
+
+/* A cache whose misses come from a store instead of a pinned host copy of
+ * every blob: the geometry (stride, n_layers, n_experts) is the store's.
+ * Each miss in moe_cache_acquire is one moe_store_read into the next of
+ * n_staging (1..64) pinned staging buffers (staging_pinned, caller-owned,
+ * n_staging * stride bytes from hipHostMalloc), then the same
+ * hipMemcpyAsync into the slot on the
+ * copy stream.  A staging buffer is read into again only after the copy out
+ * of it has finished: acquire then waits on the host (hipEventSynchronize),
+ * which may include compute that the copy stream was told to wait for.
+ * Keep the staging memory until the copy stream has finished the last
+ * acquire's copies.  After MOE_EIO from acquire the cache must be destroyed,
+ * as after MOE_EHIP.  NULL on bad arguments. */
+moe_cache* moe_cache_create_from_store(int32_t n_slots, void* pool_base, moe_store* store, void* staging_pinned,
+                                       int32_t n_staging);
+
+/* Text of the last moe_cache_* or moe_store_* error on this thread. */
 const char* moe_cache_last_error(void);
 
 #ifdef __cplusplus

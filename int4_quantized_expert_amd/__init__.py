@@ -9,7 +9,9 @@ if the library is missing, every call raises.
 from ._lib import (  # noqa: F401
     MOE_BF16,
     MOE_F32,
+    STORE_DIRECT,
     ExpertCache,
+    ExpertStore,
     LaunchTimer,
     MoeDesc,
     MoeError,

@@ -95,6 +95,21 @@ def lib() -> ctypes.CDLL:
         L.moe_cache_destroy.restype = None
         L.moe_cache_last_error.argtypes = []
         L.moe_cache_last_error.restype = ctypes.c_char_p
+        L.moe_cache_create_from_store.argtypes = [i32, vp, vp, vp, i32]
+        L.moe_cache_create_from_store.restype = vp
+        L.moe_store_create.argtypes = [ctypes.c_char_p, i32, i32, i64, i64]
+        L.moe_store_create.restype = vp
+        L.moe_store_open.argtypes = [ctypes.c_char_p, i32]
+        L.moe_store_open.restype = vp
+        L.moe_store_info.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i64),
+                                     ctypes.POINTER(i64)]
+        L.moe_store_info.restype = ctypes.c_int
+        L.moe_store_read.argtypes = [vp, i32, i32, vp]
+        L.moe_store_read.restype = ctypes.c_int
+        L.moe_store_write.argtypes = [vp, i32, i32, vp]
+        L.moe_store_write.restype = ctypes.c_int
+        L.moe_store_close.argtypes = [vp]
+        L.moe_store_close.restype = None
         L.moe_set_launch_events.argtypes = [ctypes.POINTER(vp), i32, ctypes.POINTER(i32)]
         L.moe_set_launch_events.restype = ctypes.c_int
         L.moe_last_error.argtypes = []
@@ -248,19 +263,86 @@ def _stream_handle(st) -> int | None:
     return st.cuda_stream
 
 
+STORE_DIRECT = 1
+
+
+class ExpertStore:
+    """One container file of fixed-stride expert blobs (moe_store_*).
+
+    ExpertStore.create(path, ...) makes a writable store; ExpertStore(path)
+    opens one read-only (direct=True asks for O_DIRECT reads).  Blobs are
+    numpy uint8 arrays (or raw host addresses) of `stride` bytes.
+    """
+
+    def __init__(self, path: str, direct: bool = False, _handle=None):
+        if _handle is None:
+            _handle = lib().moe_store_open(os.fsencode(path), STORE_DIRECT if direct else 0)
+            if not _handle:
+                raise MoeError(-8, lib().moe_cache_last_error().decode())
+        self._h = _handle
+        nl, ne, st, bb = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+        self._check(lib().moe_store_info(self._h, ctypes.byref(nl), ctypes.byref(ne), ctypes.byref(st),
+                                         ctypes.byref(bb)))
+        self.n_layers, self.n_experts, self.stride, self.blob_bytes = nl.value, ne.value, st.value, bb.value
+
+    @classmethod
+    def create(cls, path: str, n_layers: int, n_experts: int, stride: int, blob_bytes: int) -> "ExpertStore":
+        h = lib().moe_store_create(os.fsencode(path), n_layers, n_experts, stride, blob_bytes)
+        if not h:
+            raise MoeError(-8, lib().moe_cache_last_error().decode())
+        return cls(path, _handle=h)
+
+    def _check(self, rc: int) -> None:
+        if rc != 0:
+            raise MoeError(rc, lib().moe_cache_last_error().decode())
+
+    def _host_ptr(self, buf) -> int:
+        if isinstance(buf, int):
+            return buf
+        assert buf.nbytes >= self.stride and buf.flags["C_CONTIGUOUS"]
+        return buf.ctypes.data
+
+    def read(self, layer: int, expert: int, dst) -> None:
+        self._check(lib().moe_store_read(self._h, layer, expert, self._host_ptr(dst)))
+
+    def write(self, layer: int, expert: int, src) -> None:
+        self._check(lib().moe_store_write(self._h, layer, expert, self._host_ptr(src)))
+
+    def close(self) -> None:
+        if self._h:
+            lib().moe_store_close(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 class ExpertCache:
     """HBM slot pool caching expert blobs of a pinned host store (moe_cache_*).
 
     pool / host may be torch tensors or raw addresses; both None gives the
     policy-only planning mode (no device work).  ids and slot tables are numpy
-    arrays on the host.
+    arrays on the host.  ExpertCache.from_store reads misses from an
+    ExpertStore through pinned staging buffers instead.
     """
 
-    def __init__(self, n_slots: int, stride: int, pool, host, n_layers: int, n_experts: int):
+    def __init__(self, n_slots: int, stride: int, pool, host, n_layers: int, n_experts: int, _handle=None):
         self.n_experts = n_experts
-        self._h = lib().moe_cache_create(n_slots, stride, _ptr(pool), _ptr(host), n_layers, n_experts)
+        self._h = _handle or lib().moe_cache_create(n_slots, stride, _ptr(pool), _ptr(host), n_layers, n_experts)
         if not self._h:
             raise MoeError(-1, "moe_cache_create rejected its arguments")
+
+    @classmethod
+    def from_store(cls, n_slots: int, pool, store: "ExpertStore", staging, n_staging: int) -> "ExpertCache":
+        h = lib().moe_cache_create_from_store(n_slots, _ptr(pool), store._h, _ptr(staging), n_staging)
+        if not h:
+            raise MoeError(-1, lib().moe_cache_last_error().decode())
+        c = cls(n_slots, store.stride, None, None, store.n_layers, store.n_experts, _handle=h)
+        c._store = store          # the store must outlive the cache
+        return c
 
     def _check(self, rc: int) -> None:
         if rc != 0:

@@ -15,13 +15,11 @@ from gpu_util import DEV
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("T", [64, 8])
-def test_partial_residency_bitwise_equals_resident(T):
+def _resident_reference(T, L, seed):
+    """Inputs of an L-layer 35B int8 run and its fully resident outputs."""
     geo = synth.PRESETS["35b_int8"]
-    L, E, k, H = 4, geo.n_experts, geo.top_k, geo.hidden
+    E, k, H = geo.n_experts, geo.top_k, geo.hidden
     stride = geo.blob_stride
-    n_slots = (L * E * 2) // 5 if T >= 64 else 96    # 40% of the experts; fewer for small calls
-    seed = 31
     cur = torch.cuda.current_stream()
     pool = torch.empty(L * E * stride, dtype=torch.uint8, device=DEV)
     for l in range(L):
@@ -38,32 +36,39 @@ def test_partial_residency_bitwise_equals_resident(T):
     ws = torch.zeros(M.workspace_bytes(desc, T), dtype=torch.uint8, device=DEV)
     M.workspace_init(ws)
     slots_res = torch.arange(E, dtype=torch.int64, device=DEV) * stride
-
-    def x_ptr(l, s):
-        return x_d.data_ptr() + (l * 2 * T + s * T) * H * 2
-
-    def args(l):
-        return r_d.data_ptr() + l * E * H * 2, shared.data_ptr() + l * geo.shared_bytes
-
-    # resident reference
+    ctx = dict(geo=geo, L=L, T=T, pool=pool, shared=shared, x_d=x_d, r_d=r_d, ws=ws)
     ref = {}
     for s in range(2):
         for l in range(L):
             out = torch.empty(T, H, dtype=torch.float32, device=DEV)
-            R, sh = args(l)
-            M.layer_forward(desc, T, x_ptr(l, s), R, slots_res, pool.data_ptr() + l * E * stride, sh, out, ws)
+            R, sh = _layer_args(ctx, l)
+            M.layer_forward(desc, T, _x_ptr(ctx, l, s), R, slots_res, pool.data_ptr() + l * E * stride, sh, out, ws)
             ref[(s, l)] = out
     torch.cuda.synchronize()
     M.status_check(ws)
+    ctx["ref"] = ref
+    return ctx
 
-    # partial: pinned host store, slot pool of 40% of the experts
-    host = torch.empty(L * E * stride, dtype=torch.uint8, pin_memory=True)
-    host.copy_(pool)
-    torch.cuda.synchronize()
-    slot_pool = torch.empty(n_slots * stride, dtype=torch.uint8, device=DEV)
+
+def _x_ptr(ctx, l, s):
+    T, H = ctx["T"], ctx["geo"].hidden
+    return ctx["x_d"].data_ptr() + (l * 2 * T + s * T) * H * 2
+
+
+def _layer_args(ctx, l):
+    geo = ctx["geo"]
+    E, H = geo.n_experts, geo.hidden
+    return ctx["r_d"].data_ptr() + l * E * H * 2, ctx["shared"].data_ptr() + l * geo.shared_bytes
+
+
+def _run_partial(ctx, cache, n_slots, slot_pool):
+    """Every (step, layer) call through the cache; each output must equal the
+    resident one bit for bit.  Returns (hits, misses, evictions, distinct)."""
+    geo, L, T, ws = ctx["geo"], ctx["L"], ctx["T"], ctx["ws"]
+    E, k, H = geo.n_experts, geo.top_k, geo.hidden
+    cur = torch.cuda.current_stream()
     desc_p = M.desc_for(H, E, k, geo.inter, geo.shared_inter, geo.bits, geo.act, geo.sb, "f32",
-                        pool_bytes=n_slots * stride)
-    cache = M.ExpertCache(n_slots, stride, slot_pool, host, L, E)
+                        pool_bytes=n_slots * geo.blob_stride)
     copy_stream = torch.cuda.Stream()
     ready = torch.cuda.Event()
     done = [torch.cuda.Event() for _ in range(L)]
@@ -75,21 +80,74 @@ def test_partial_residency_bitwise_equals_resident(T):
     # layer-major for small calls, so a layer's hot experts are reused before eviction
     order = [(s, l) for s in range(2) for l in range(L)] if T >= 64 else [(s, l) for l in range(L) for s in range(2)]
     for s, l in order:
-        R, sh = args(l)
-        M.router_topk(desc_p, T, x_ptr(l, s), R, ids, wts, ws)
+        R, sh = _layer_args(ctx, l)
+        M.router_topk(desc_p, T, _x_ptr(ctx, l, s), R, ids, wts, ws)
         ids_h = ids.cpu().numpy()
         distinct += len(np.unique(ids_h))
         cache.acquire(l, ids_h, table_h, copy_stream, ready)
         cur.wait_event(ready)
         table_d.copy_(torch.from_numpy(table_h))
         out = torch.empty(T, H, dtype=torch.float32, device=DEV)
-        M.experts_forward(desc_p, T, x_ptr(l, s), ids, wts, table_d, slot_pool, sh, out, ws)
+        M.experts_forward(desc_p, T, _x_ptr(ctx, l, s), ids, wts, table_d, slot_pool, sh, out, ws)
         done[l].record(cur)
         cache.release(l, done[l])
         torch.cuda.synchronize()
         M.status_check(ws)
-        assert torch.equal(out, ref[(s, l)]), f"step {s} layer {l} differs from the resident run"
-    hits, misses, evictions = cache.stats()
+        assert torch.equal(out, ctx["ref"][(s, l)]), f"step {s} layer {l} differs from the resident run"
+    return (*cache.stats(), distinct)
+
+
+@pytest.mark.parametrize("T", [64, 8])
+def test_partial_residency_bitwise_equals_resident(T):
+    L, seed = 4, 31
+    ctx = _resident_reference(T, L, seed)
+    geo = ctx["geo"]
+    E, stride = geo.n_experts, geo.blob_stride
+    n_slots = (L * E * 2) // 5 if T >= 64 else 96    # 40% of the experts; fewer for small calls
+    # partial: pinned host store, slot pool of 40% of the experts
+    host = torch.empty(L * E * stride, dtype=torch.uint8, pin_memory=True)
+    host.copy_(ctx["pool"])
+    torch.cuda.synchronize()
+    slot_pool = torch.empty(n_slots * stride, dtype=torch.uint8, device=DEV)
+    cache = M.ExpertCache(n_slots, stride, slot_pool, host, L, E)
+    hits, misses, evictions, distinct = _run_partial(ctx, cache, n_slots, slot_pool)
     assert hits + misses == distinct
     assert misses > 0 and evictions > 0 and hits > 0
     cache.close()
+
+
+@pytest.mark.parametrize("direct", [False, True])
+def test_partial_residency_from_file_store_bitwise_equals_resident(tmp_path, direct):
+    """The same run with misses read from a container file of fixed-stride
+    blobs (one positioned read per blob into pinned staging, then the copy):
+    linlog.top article, core design 2; the output still equals the resident
+    run bit for bit."""
+    L, T, seed = 2, 64, 37
+    ctx = _resident_reference(T, L, seed)
+    geo = ctx["geo"]
+    E, stride = geo.n_experts, geo.blob_stride
+    path = str(tmp_path / "experts.store")
+    store_w = M.ExpertStore.create(path, L, E, stride, geo.blob_bytes(geo.inter))
+    host = ctx["pool"].cpu().numpy()
+    for l in range(L):
+        for e in range(E):
+            store_w.write(l, e, host[(l * E + e) * stride:(l * E + e + 1) * stride])
+    store_w.close()
+    del host
+    try:
+        store = M.ExpertStore(path, direct=direct)
+    except M.MoeError as err:
+        if direct:
+            pytest.skip(f"this file system refuses O_DIRECT: {err}")
+        raise
+    assert (store.n_layers, store.n_experts, store.stride) == (L, E, stride)
+    n_slots = (L * E * 2) // 5
+    n_staging = 4
+    staging = torch.empty(n_staging * stride, dtype=torch.uint8, pin_memory=True)
+    slot_pool = torch.empty(n_slots * stride, dtype=torch.uint8, device=DEV)
+    cache = M.ExpertCache.from_store(n_slots, slot_pool, store, staging, n_staging)
+    hits, misses, evictions, distinct = _run_partial(ctx, cache, n_slots, slot_pool)
+    assert hits + misses == distinct
+    assert misses > n_staging and evictions > 0 and hits > 0
+    cache.close()
+    store.close()
