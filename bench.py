@@ -468,8 +468,9 @@ def kernel_work(desc, geo, T, n_kernels, uniq, prefill, out_bytes):
 
 
 def cpu_baseline(geo, args, x_host, r_host, shared_host, n_layers, XS, T, shared_bytes, NX):
-    """The oracle (float64, unmodified) on a bounded sample: one token of the
-    first timed batch per layer, until the time budget is spent."""
+    """The oracle (float64, unmodified) on a bounded sample: the tokens of the
+    timed batches in order, each through every layer, until the time budget
+    is spent."""
     import synth
     from oracle import moe_oracle as O
     try:
@@ -482,20 +483,24 @@ def cpu_baseline(geo, args, x_host, r_host, shared_host, n_layers, XS, T, shared
     stride = geo.blob_stride
     pool = np.zeros(geo.n_experts * stride, dtype=np.uint8)
     slots = np.arange(geo.n_experts, dtype=np.int64) * stride
-    s = args.warmup % XS
-    spent, done = 0.0, 0
-    for l in range(n_layers):
-        x1 = x_host[l % NX, s * T: s * T + 1]
-        xs = O.decode_dense(x1, geo.act).reshape(1, -1)
-        rs = O.decode_dense(r_host[l], geo.act).reshape(geo.n_experts, -1)
-        for e in O.select_topk(O.router_logits(xs, rs)[0], geo.top_k):
-            e = int(e)
-            synth.fill_blob(geo, geo.inter, synth.blob_key(args.seed, l, e), pool[e * stride:(e + 1) * stride])
-        sh = shared_host[l * shared_bytes:(l + 1) * shared_bytes]
-        t0 = time.perf_counter()
-        O.moe_layer(shape, 1, x1, r_host[l], slots, pool, sh)
-        spent += time.perf_counter() - t0
-        done += 1
+    q0 = (args.warmup % XS) * T          # first token of the first timed batch
+    spent, done, tokens = 0.0, 0, 0
+    for q in range(q0, XS * T):
+        for l in range(n_layers):
+            x1 = x_host[l % NX, q: q + 1]
+            xs = O.decode_dense(x1, geo.act).reshape(1, -1)
+            rs = O.decode_dense(r_host[l], geo.act).reshape(geo.n_experts, -1)
+            for e in O.select_topk(O.router_logits(xs, rs)[0], geo.top_k):
+                e = int(e)
+                synth.fill_blob(geo, geo.inter, synth.blob_key(args.seed, l, e), pool[e * stride:(e + 1) * stride])
+            sh = shared_host[l * shared_bytes:(l + 1) * shared_bytes]
+            t0 = time.perf_counter()
+            O.moe_layer(shape, 1, x1, r_host[l], slots, pool, sh)
+            spent += time.perf_counter() - t0
+            done += 1
+            if spent >= args.cpu_seconds:
+                break
+        tokens += 1
         if spent >= args.cpu_seconds:
             break
     return {
@@ -503,8 +508,8 @@ def cpu_baseline(geo, args, x_host, r_host, shared_host, n_layers, XS, T, shared
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{done} layer-tokens (token 0 of the first timed batch, layers 0..{done - 1}), "
-                  f"{spent:.1f} s of float64 numpy",
+        "sample": f"{done} layer-tokens ({tokens} token(s) of the timed batches from the first, each through "
+                  f"layers in order, the last pass possibly partial), {spent:.1f} s of float64 numpy",
     }
 
 
