@@ -119,3 +119,18 @@ def test_fresh_store_reads_zeros_until_written(tmp_path):
     s.read(1, 2, buf)
     assert np.array_equal(buf, one)
     s.close()
+
+
+def test_cache_from_store_rejects_bad_arguments_before_any_device_call(tmp_path):
+    path = tmp_path / "c.store"
+    _make(path, _blobs())
+    s = M.ExpertStore(str(path))
+    L_ = M.lib()
+    fake = 1 << 20          # never dereferenced: validation fails first
+    assert not L_.moe_cache_create_from_store(8, None, s._h, fake, 4)        # no pool
+    assert not L_.moe_cache_create_from_store(8, fake, None, fake, 4)        # no store
+    assert not L_.moe_cache_create_from_store(8, fake, s._h, None, 4)        # no staging
+    assert not L_.moe_cache_create_from_store(8, fake, s._h, fake, 0)        # no staging buffers
+    assert not L_.moe_cache_create_from_store(8, fake, s._h, fake, 65)       # too many
+    assert "staging" in L_.moe_cache_last_error().decode()
+    s.close()
