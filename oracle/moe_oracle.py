@@ -313,3 +313,34 @@ def summation_bound(x_row: np.ndarray, router: np.ndarray, exact_products: bool)
     u = 2.0 ** -24
     gamma = m * u / (1.0 - m * u)
     return gamma * (np.abs(x_row) @ np.abs(router).T)
+
+
+# ---------------------------------------------------------------- layer stack
+
+def bf16_round_bits(f32: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16, ties to even (NaN stays a
+    quiet NaN); returns the 16-bit patterns.  Written from the definition:
+    keep the top 16 bits, and add one unit of the kept part when the dropped
+    16 bits exceed half a unit, or equal it and the kept part is odd."""
+    u = np.ascontiguousarray(f32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    hi, lo = u >> 16, u & 0xFFFF
+    up = (lo > 0x8000) | ((lo == 0x8000) & ((hi & 1) == 1))
+    out = (hi + up.astype(np.uint64)) & 0xFFFF
+    nan = ((u & 0x7F800000) == 0x7F800000) & ((u & 0x007FFFFF) != 0)
+    out = np.where(nan, hi | 0x40, out)
+    return out.astype(np.uint16)
+
+
+def residual_next(x_raw: np.ndarray, y: np.ndarray, act_dtype: str) -> np.ndarray:
+    """Input of the next layer in a stack: x + y, with y the layer's output.
+    Reading (the pages run the whole layer stack per token but print no
+    formula; plain residual chaining): the sum is taken in float32, the
+    precision of the stored result, and rounded to nearest even for bf16
+    activations, so that both paths take the same rounding decision.
+    x_raw holds the stored activations (uint16 bf16 patterns or float32)."""
+    x32 = decode_dense(x_raw, act_dtype).astype(np.float32)
+    s = x32 + np.asarray(y, dtype=np.float32)
+    if act_dtype == "bf16":
+        return bf16_round_bits(s)
+    return s.astype(np.float32)
+
