@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chain", action="store_true",
+                    help="decode workloads: feed each layer x + y of the layer before (moe_residual_add), "
+                         "layer 0 taking the step's tokens")
     ap.add_argument("--store-path", default="/tmp/moe_35b_int8.store",
                     help="35b_int8_store: container file written (or rewritten) before timing")
     ap.add_argument("--buffered", action="store_true",
@@ -147,12 +150,25 @@ def main():
     act_sz = 2 if geo.act == "bf16" else 4
     r_bytes = E * H * act_sz
 
+    chain = None
+    if args.chain:
+        assert not prefill, "--chain is for the decode workloads"
+        chain = torch.empty(n_layers * T * H * act_sz, dtype=torch.uint8, device=dev)
+
+    def x_in(l, s):
+        xs = s % XS
+        if chain is not None and l > 0:
+            return chain.data_ptr() + l * T * H * act_sz
+        return x.data_ptr() + ((l % NX) * XS * T + xs * T) * H * act_sz
+
     def layer_call(l, s, strm):
         xs = s % XS
-        M.layer_forward(desc, T, x.data_ptr() + ((l % NX) * XS * T + xs * T) * H * act_sz,
-                        routers.data_ptr() + l * r_bytes,
+        M.layer_forward(desc, T, x_in(l, s), routers.data_ptr() + l * r_bytes,
                         slots, pool.data_ptr() + l * E * stride, shared.data_ptr() + l * shared_bytes,
                         out[l], ws, ids[l, xs], None, stream=strm)
+        if chain is not None and l + 1 < n_layers:
+            M.residual_add(T, H, geo.act, x_in(l, s), out[l], chain.data_ptr() + (l + 1) * T * H * act_sz,
+                           stream=strm)
 
     def step(s, strm):
         for l in range(n_layers):
@@ -266,6 +282,7 @@ def main():
             "experts": E, "top_k": k, "inter": geo.inter, "shared_inter": geo.shared_inter,
             "bits": geo.bits, "group": 64, "scale_dtype": geo.sb, "act_dtype": geo.act, "out_dtype": out_dt,
             "routing": routing, "pool_gb": round(pool.numel() / 1e9, 2), "graphs": not args.eager,
+            "chained": bool(args.chain),
         },
         "hbm": {
             "algorithmic_bytes_per_layer": round(bytes_per_layer),

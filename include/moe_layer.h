@@ -215,6 +215,19 @@ int moe_set_launch_events(void* const* events, int32_t capacity, int32_t* n_reco
  */
 int moe_status_check(void* workspace, void* stream);
 
+/* The step after the layer in a stack of layers: x_next = x + y for the
+ * layer input x [T, H] (act_dtype: MOE_BF16 or MOE_F32) and the layer output
+ * y [T, H] (fp32), the sum taken in fp32 and, for bf16, rounded to nearest
+ * even into bf16.  The pages run token after token through the whole layer
+ * stack on the device, and report the decode loop as bound by dispatch rather
+ * than by expert reads (Swiftlet README translation, "Status"; linlog.top
+ * article, section "Capability limits"); chaining each layer's output into
+ * the next layer's input is the plain reading of that loop.  x_next may be x
+ * (in place).  Device pointers, caller-owned; asynchronous on `stream`.
+ * MOE_EINVAL on bad sizes, dtype or NULL pointers. */
+int moe_residual_add(int32_t T, int32_t H, int32_t act_dtype, const void* x, const float* y, void* x_next,
+                     void* stream);
+
 /* Text of the last error on this thread ("" if none). */
 const char* moe_last_error(void);
 

@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     layer_forward_staged,
     last_error,
     lib,
+    residual_add,
     router_topk,
     status_check,
     workspace_bytes,

@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.moe_router_topk.restype = ctypes.c_int
         L.moe_experts_forward.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_experts_forward.restype = ctypes.c_int
+        L.moe_residual_add.argtypes = [i32, i32, i32, vp, vp, vp, vp]
+        L.moe_residual_add.restype = ctypes.c_int
         L.moe_status_check.argtypes = [vp, vp]
         L.moe_status_check.restype = ctypes.c_int
         L.moe_cache_create.argtypes = [i32, i64, vp, vp, i32, i32]
@@ -209,6 +211,12 @@ def experts_forward(d: MoeDesc, T: int, x, topk_ids, topk_w, slot_table, pool, s
     _check(lib().moe_experts_forward(ctypes.byref(d), T, _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(slot_table),
                                      _ptr(pool), _ptr(shared_w), _ptr(out), _ptr(ws), _nbytes(ws),
                                      _stream(stream, ws)))
+
+
+def residual_add(T: int, H: int, act: str, x, y, x_next, stream=None) -> None:
+    """x_next = x + y (fp32 sum; rounded to bf16 when act == "bf16"); device tensors or addresses."""
+    _check(lib().moe_residual_add(T, H, MOE_BF16 if act == "bf16" else MOE_F32, _ptr(x), _ptr(y), _ptr(x_next),
+                                  _stream(stream, x if hasattr(x, "device") else None)))
 
 
 def status_check(ws, stream=None) -> None:

@@ -268,6 +268,17 @@ int moe_layer_forward_staged(const moe_desc* d, int32_t T, const void* x, const 
                        topk_w, stream, false);
 }
 
+int moe_residual_add(int32_t T, int32_t H, int32_t act_dtype, const void* x, const float* y, void* x_next,
+                     void* stream) {
+  if (T < 0 || H < 1 || static_cast<int64_t>(T) * H >= (int64_t(1) << 31))
+    return fail(MOE_EINVAL, "T must be >= 0 and H >= 1, with T * H < 2^31");
+  if (act_dtype != MOE_F32 && act_dtype != MOE_BF16) return fail(MOE_EINVAL, "act_dtype must be MOE_F32 or MOE_BF16");
+  if (!x || !y || !x_next) return fail(MOE_EINVAL, "NULL x, y or x_next");
+  if (T == 0) return ok();
+  return finish(moe::launch_residual(act_dtype, x, y, x_next,
+                                     static_cast<int64_t>(T) * H, static_cast<hipStream_t>(stream)));
+}
+
 int moe_status_check(void* workspace, void* stream) {
   if (!workspace || !aligned(workspace, 256)) return fail(MOE_EINVAL, "workspace is NULL or not 256-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -586,6 +586,31 @@ static int last_launch_error() {
   return e == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
+// x_next = x + y per element: the sum in fp32, rounded to nearest even when
+// the activations are bf16.  Each element is read and written by one thread,
+// so x_next may be x.
+template <int ACT>
+__global__ __launch_bounds__(256) void k_residual(const void* __restrict__ x, const float* __restrict__ y,
+                                                 void* x_next, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  if constexpr (ACT == kBF16) {
+    const float xv = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(x)[i]) << 16);
+    static_cast<uint16_t*>(x_next)[i] = f32_to_bf16(xv + y[i]);
+  } else {
+    static_cast<float*>(x_next)[i] = static_cast<const float*>(x)[i] + y[i];
+  }
+}
+
+int launch_residual(int act_dtype, const void* x, const float* y, void* x_next, int64_t n, hipStream_t stream) {
+  const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
+  if (act_dtype == kBF16)
+    hipLaunchKernelGGL(k_residual<kBF16>, dim3(blocks), dim3(256), 0, stream, x, y, x_next, n);
+  else
+    hipLaunchKernelGGL(k_residual<kF32>, dim3(blocks), dim3(256), 0, stream, x, y, x_next, n);
+  return last_launch_error();
+}
+
 int launch_ws_init(uint8_t* ws, size_t bytes, hipStream_t stream) {
   const size_t n = bytes / 4;
   const size_t blocks = (n + 255) / 256;

@@ -135,6 +135,7 @@ int launch_topk(const Call& c, const float* logits, int32_t* ids, float* wts, in
 int launch_combine(const Call& c, const float* partial, const float* gate);      // fp32 partial rows
 int launch_combine(const Call& c, const _Float16* partial, const float* gate);   // float16 partial rows
 int launch_ws_init(uint8_t* ws, size_t bytes, hipStream_t stream);
+int launch_residual(int act_dtype, const void* x, const float* y, void* x_next, int64_t n, hipStream_t stream);
 
 // Prefill path (many tokens): MFMA router and grouped expert GEMMs.
 bool prefill_supported(const moe_desc& d, int T);
