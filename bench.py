@@ -64,7 +64,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chain", action="store_true",
-                    help="decode workloads: feed each layer x + y of the layer before (moe_residual_add), "
+                    help="decode workloads: feed each layer x + y of the layer before (moe_layer_forward_chain), "
                          "layer 0 taking the step's tokens")
     ap.add_argument("--store-path", default="/tmp/moe_35b_int8.store",
                     help="35b_int8_store: container file written (or rewritten) before timing")
@@ -163,12 +163,13 @@ def main():
 
     def layer_call(l, s, strm):
         xs = s % XS
-        M.layer_forward(desc, T, x_in(l, s), routers.data_ptr() + l * r_bytes,
-                        slots, pool.data_ptr() + l * E * stride, shared.data_ptr() + l * shared_bytes,
-                        out[l], ws, ids[l, xs], None, stream=strm)
+        args_l = (desc, T, x_in(l, s), routers.data_ptr() + l * r_bytes, slots, pool.data_ptr() + l * E * stride,
+                  shared.data_ptr() + l * shared_bytes, out[l])
         if chain is not None and l + 1 < n_layers:
-            M.residual_add(T, H, geo.act, x_in(l, s), out[l], chain.data_ptr() + (l + 1) * T * H * act_sz,
-                           stream=strm)
+            M.layer_forward_chain(*args_l, chain.data_ptr() + (l + 1) * T * H * act_sz, ws, ids[l, xs], None,
+                                  stream=strm)
+        else:
+            M.layer_forward(*args_l, ws, ids[l, xs], None, stream=strm)
 
     def step(s, strm):
         for l in range(n_layers):

@@ -228,6 +228,17 @@ int moe_status_check(void* workspace, void* stream);
 int moe_residual_add(int32_t T, int32_t H, int32_t act_dtype, const void* x, const float* y, void* x_next,
                      void* stream);
 
+/* moe_layer_forward, then the stack step into x_next [T, H] (the activation
+ * dtype): the same bits as moe_layer_forward followed by moe_residual_add on
+ * its output, for the same passages.  The fused decode path writes x_next in
+ * its ordered combine, without a launch of its own; the other paths launch
+ * the step after the layer.  Needs out_dtype MOE_F32; x_next 16-byte aligned
+ * and not x.  MOE_EINVAL otherwise. */
+int moe_layer_forward_chain(const moe_desc* desc, int32_t T, const void* x, const void* router_w,
+                            const int64_t* slot_table, const void* pool_base, const void* shared_w, void* out,
+                            void* x_next, void* workspace, size_t ws_bytes, int32_t* topk_ids, float* topk_w,
+                            void* stream);
+
 /* Text of the last error on this thread ("" if none). */
 const char* moe_last_error(void);
 

@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     desc_for,
     experts_forward,
     layer_forward,
+    layer_forward_chain,
     layer_forward_staged,
     last_error,
     lib,

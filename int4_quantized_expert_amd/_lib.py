@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.moe_router_topk.restype = ctypes.c_int
         L.moe_experts_forward.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_experts_forward.restype = ctypes.c_int
+        L.moe_layer_forward_chain.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+        L.moe_layer_forward_chain.restype = ctypes.c_int
         L.moe_residual_add.argtypes = [i32, i32, i32, vp, vp, vp, vp]
         L.moe_residual_add.restype = ctypes.c_int
         L.moe_status_check.argtypes = [vp, vp]
@@ -191,6 +193,14 @@ def layer_forward(d: MoeDesc, T: int, x, router_w, slot_table, pool, shared_w, o
     _check(lib().moe_layer_forward(ctypes.byref(d), T, _ptr(x), _ptr(router_w), _ptr(slot_table), _ptr(pool),
                                    _ptr(shared_w), _ptr(out), _ptr(ws), _nbytes(ws), _ptr(topk_ids),
                                    _ptr(topk_w), _stream(stream, ws)))
+
+
+def layer_forward_chain(d: MoeDesc, T: int, x, router_w, slot_table, pool, shared_w, out, x_next, ws,
+                        topk_ids=None, topk_w=None, stream=None) -> None:
+    """layer_forward, then x_next = x + out (moe_layer_forward_chain)."""
+    _check(lib().moe_layer_forward_chain(ctypes.byref(d), T, _ptr(x), _ptr(router_w), _ptr(slot_table), _ptr(pool),
+                                         _ptr(shared_w), _ptr(out), _ptr(x_next), _ptr(ws), _nbytes(ws),
+                                         _ptr(topk_ids), _ptr(topk_w), _stream(stream, ws)))
 
 
 def layer_forward_staged(d: MoeDesc, T: int, x, router_w, slot_table, pool, shared_w, out, ws,

@@ -214,7 +214,7 @@ int moe_experts_forward(const moe_desc* d, int32_t T, const void* x, const int32
 static int layer_forward(const moe_desc* d, int32_t T, const void* x, const void* router_w,
                          const int64_t* slot_table, const void* pool_base, const void* shared_w, void* out,
                          void* workspace, size_t ws_bytes, int32_t* topk_ids, float* topk_w, void* stream,
-                         bool allow_fused) {
+                         bool allow_fused, void* x_next = nullptr) {
   MarkScope marks;
   int rc;
   if ((rc = check_desc(d)) || (rc = check_T(T))) return rc;
@@ -223,6 +223,8 @@ static int layer_forward(const moe_desc* d, int32_t T, const void* x, const void
   if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(out, 16) || !aligned(slot_table, 8) ||
       !aligned(pool_base, 256) || !aligned(shared_w, 256))
     return fail(MOE_EINVAL, "misaligned pointer (x/router_w/out 16, slot_table 8, pool_base/shared_w 256)");
+  if (x_next && (d->out_dtype != MOE_F32 || !aligned(x_next, 16) || x_next == x))
+    return fail(MOE_EINVAL, "x_next needs fp32 output, 16-byte alignment and a buffer other than x");
   moe::WsLayout L;
   if ((rc = check_ws(*d, T, workspace, ws_bytes, &L))) return rc;
   if (T == 0) return ok();
@@ -230,6 +232,7 @@ static int layer_forward(const moe_desc* d, int32_t T, const void* x, const void
   c.d = *d;
   c.T = T;
   c.x = x;
+  c.x_next = x_next;
   c.router_w = router_w;
   c.slot_table = slot_table;
   c.pool = static_cast<const uint8_t*>(pool_base);
@@ -246,12 +249,27 @@ static int layer_forward(const moe_desc* d, int32_t T, const void* x, const void
     moe::FusedPlan plan;
     if (cached_plan(*d, T, &plan) == MOE_OK) return finish(moe::launch_decode_fused(c, plan));
   }
+  // the other paths take the stack step as a kernel of its own
+  const auto step = [&](int r) {
+    if (r != MOE_OK || !x_next) return r;
+    return moe::launch_residual(d->act_dtype, x, static_cast<const float*>(out), x_next,
+                                static_cast<int64_t>(T) * d->hidden, c.stream);
+  };
   if (allow_fused && moe::prefill_supported(*d, T)) {
     if ((rc = moe::launch_prefill_router(c, topk_ids, topk_w))) return finish(rc);
-    return finish(moe::launch_prefill_experts(c));
+    return finish(step(moe::launch_prefill_experts(c)));
   }
   if ((rc = moe::launch_router_topk(c, topk_ids, topk_w))) return finish(rc);
-  return finish(moe::launch_experts(c));
+  return finish(step(moe::launch_experts(c)));
+}
+
+int moe_layer_forward_chain(const moe_desc* d, int32_t T, const void* x, const void* router_w,
+                            const int64_t* slot_table, const void* pool_base, const void* shared_w, void* out,
+                            void* x_next, void* workspace, size_t ws_bytes, int32_t* topk_ids, float* topk_w,
+                            void* stream) {
+  if (!x_next) return fail(MOE_EINVAL, "NULL x_next");
+  return layer_forward(d, T, x, router_w, slot_table, pool_base, shared_w, out, workspace, ws_bytes, topk_ids,
+                       topk_w, stream, true, x_next);
 }
 
 int moe_layer_forward(const moe_desc* d, int32_t T, const void* x, const void* router_w, const int64_t* slot_table,

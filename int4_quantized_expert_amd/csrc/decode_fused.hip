@@ -520,7 +520,17 @@ __device__ __forceinline__ void combine_unit(const FusedArgs& a, const LdsB& s, 
     for (int i = 0; i < k; ++i) acc = fmaf(s.wts[i], s.part[i * a.rb + rloc], acc);
     acc = fmaf(s.sig[0], s.part[k * a.rb + rloc], acc);
     if constexpr (OUT == kF32) {
-      static_cast<float*>(a.out)[static_cast<size_t>(t) * a.H + n] = acc;
+      const size_t j = static_cast<size_t>(t) * a.H + n;
+      static_cast<float*>(a.out)[j] = acc;
+      if (a.x_next) {
+        // the stack step, as moe_residual_add takes it: fp32 sum, nearest-even bf16
+        if (a.act_sz == 2) {
+          const float xv = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.x)[j]) << 16);
+          static_cast<uint16_t*>(a.x_next)[j] = f32_to_bf16(xv + acc);
+        } else {
+          static_cast<float*>(a.x_next)[j] = static_cast<const float*>(a.x)[j] + acc;
+        }
+      }
     } else {
       static_cast<uint16_t*>(a.out)[static_cast<size_t>(t) * a.H + n] = f32_to_bf16(acc);
     }
@@ -1252,6 +1262,7 @@ int launch_decode_fused(const Call& c, const FusedPlan& plan) {
   a.pool = c.pool;
   a.shared = c.shared;
   a.out = c.out;
+  a.x_next = c.x_next;
   a.ids_out = c.ids_out;
   a.wts_out = c.wts_out;
   a.lg = reinterpret_cast<uint64_t*>(c.ws + c.L.f_lg);

@@ -16,6 +16,7 @@ struct FusedArgs {
   const uint8_t* pool;
   const uint8_t* shared;
   void* out;
+  void* x_next;         // optional [T, H] activations: x + out (stack step), out fp32
   int32_t* ids_out;     // optional [T, k]
   float* wts_out;       // optional [T, k]
   uint64_t* lg;         // [kFusedReplicas][T, E] tagged logits

@@ -101,6 +101,7 @@ struct Call {
   const uint8_t* pool;
   const uint8_t* shared;
   void* out;
+  void* x_next;           // optional: x + out into the next layer's input (fp32 out only)
   uint8_t* ws;
   WsLayout L;
   const int32_t* ids;     // routing used by the expert kernels

@@ -44,7 +44,17 @@ def test_layer_stack_chained_parity(name, T, tol):
             compared += tokens.size
         x_next = torch.empty_like(x)
         M.residual_add(T, H, geo.act, x, y, x_next)
+        # the chained entry point: the same output and the same next input
+        y2 = torch.full_like(y, float("nan"))
+        x_next2 = torch.empty_like(x)
+        ws = torch.zeros(M.workspace_bytes(dl.desc, T), dtype=torch.uint8, device=DEV)
+        M.workspace_init(ws)
+        M.layer_forward_chain(dl.desc, T, x, dl.R, dl.slots, dl.pool, dl.shared, y2, x_next2, ws)
         torch.cuda.synchronize()
+        M.status_check(ws)
+        assert torch.equal(y2, y), f"layer {l}: chained output differs"
+        assert torch.equal(x_next2, x_next), f"layer {l}: chained next input differs"
+
         want = O.residual_next(x_host, y.cpu().numpy(), geo.act)
         got = x_next.cpu().numpy().view(xdt).reshape(T, H)
         assert np.array_equal(got.view(np.uint8), np.ascontiguousarray(want).view(np.uint8)), f"layer {l} step"
