@@ -137,11 +137,13 @@ def main():
                      else synth.router_normal(geo, args.seed, l))
     x = torch.from_numpy(x_host.view(np.uint8)).to(dev)
     routers = torch.from_numpy(r_host.view(np.uint8)).to(dev)
-    slots = torch.arange(E, dtype=torch.int64, device=dev) * stride
+    # one pool base for the whole stack: layer l's expert e at byte offset (l E + e) stride,
+    # so the slot offsets of the deeper layers exceed 2^32 (up to 4.3e10 on the 80B stack)
+    slots = (torch.arange(n_layers * E, dtype=torch.int64, device=dev) * stride).reshape(n_layers, E)
     out = torch.empty(n_layers, T, H, dtype=torch.float32 if out_dt == "f32" else torch.bfloat16, device=dev)
     ids = torch.full((n_layers, XS, T, k), -1, dtype=torch.int32, device=dev)
     desc = M.desc_for(H, E, k, geo.inter, geo.shared_inter, geo.bits, geo.act, geo.sb, out_dt,
-                      pool_bytes=E * stride)
+                      pool_bytes=pool.numel())
     ws = torch.zeros(M.workspace_bytes(desc, T), dtype=torch.uint8, device=dev)
     M.workspace_init(ws)
     torch.cuda.synchronize()
@@ -163,7 +165,7 @@ def main():
 
     def layer_call(l, s, strm):
         xs = s % XS
-        args_l = (desc, T, x_in(l, s), routers.data_ptr() + l * r_bytes, slots, pool.data_ptr() + l * E * stride,
+        args_l = (desc, T, x_in(l, s), routers.data_ptr() + l * r_bytes, slots[l], pool.data_ptr(),
                   shared.data_ptr() + l * shared_bytes, out[l])
         if chain is not None and l + 1 < n_layers:
             M.layer_forward_chain(*args_l, chain.data_ptr() + (l + 1) * T * H * act_sz, ws, ids[l, xs], None,
@@ -282,7 +284,8 @@ def main():
             "workload": args.workload, "layers": n_layers, "tokens_per_call": T, "hidden": H,
             "experts": E, "top_k": k, "inter": geo.inter, "shared_inter": geo.shared_inter,
             "bits": geo.bits, "group": 64, "scale_dtype": geo.sb, "act_dtype": geo.act, "out_dtype": out_dt,
-            "routing": routing, "pool_gb": round(pool.numel() / 1e9, 2), "graphs": not args.eager,
+            "routing": routing, "pool_gb": round(pool.numel() / 1e9, 2), "pool_bases": 1,
+            "max_slot_offset": int(slots.max().item()), "graphs": not args.eager,
             "chained": bool(args.chain),
         },
         "hbm": {
@@ -488,14 +491,35 @@ def kernel_work(desc, geo, T, n_kernels, uniq, prefill, out_bytes):
 def cpu_baseline(geo, args, x_host, r_host, shared_host, n_layers, XS, T, shared_bytes, NX):
     """The oracle (float64, unmodified) on a bounded sample: the tokens of the
     timed batches in order, each through every layer, until the time budget
-    is spent."""
+    is spent.  BLAS threads are set explicitly to the cores this process may
+    run on; a second, shorter pass with one thread gives the 1-thread figure."""
+    from threadpoolctl import threadpool_limits
+
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
+        main_leg = _oracle_sample(geo, args, x_host, r_host, shared_host, n_layers, XS, T, shared_bytes, NX,
+                                  args.cpu_seconds)
+    with threadpool_limits(limits=1):
+        one = _oracle_sample(geo, args, x_host, r_host, shared_host, n_layers, XS, T, shared_bytes, NX,
+                             max(2.0, args.cpu_seconds / 3))
+    done, spent, tokens = main_leg
+    done1, spent1, _ = one
+    return {
+        "value": round(done / spent, 3),
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{done} layer-tokens ({tokens} token(s) of the timed batches from the first, each through "
+                  f"layers in order, the last pass possibly partial), {spent:.1f} s of float64 numpy with "
+                  f"BLAS threads set to {cores}",
+        "one_thread": {"value": round(done1 / spent1, 3), "unit": "tokens/s", "cores": 1,
+                       "sample": f"{done1} layer-tokens, {spent1:.1f} s"},
+    }
+
+
+def _oracle_sample(geo, args, x_host, r_host, shared_host, n_layers, XS, T, shared_bytes, NX, budget):
     import synth
     from oracle import moe_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
     shape = O.LayerShape(geo.hidden, geo.n_experts, geo.top_k, geo.inter, geo.shared_inter, geo.bits,
                          geo.act, geo.sb)
     stride = geo.blob_stride
@@ -516,19 +540,12 @@ def cpu_baseline(geo, args, x_host, r_host, shared_host, n_layers, XS, T, shared
             O.moe_layer(shape, 1, x1, r_host[l], slots, pool, sh)
             spent += time.perf_counter() - t0
             done += 1
-            if spent >= args.cpu_seconds:
+            if spent >= budget:
                 break
         tokens += 1
-        if spent >= args.cpu_seconds:
+        if spent >= budget:
             break
-    return {
-        "value": round(done / spent, 3),
-        "unit": "tokens/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": f"{done} layer-tokens ({tokens} token(s) of the timed batches from the first, each through "
-                  f"layers in order, the last pass possibly partial), {spent:.1f} s of float64 numpy",
-    }
+    return done, spent, tokens
 
 
 if __name__ == "__main__":

@@ -25,6 +25,7 @@ ERRORS = {
     -5: "MOE_ERANGE",
     -6: "MOE_ENOSPC",
     -7: "MOE_ETIMEOUT",
+    -8: "MOE_EIO",
 }
 
 

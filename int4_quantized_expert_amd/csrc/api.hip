@@ -57,6 +57,12 @@ bool pow2_in(int32_t v, int32_t lo, int32_t hi) { return v >= lo && v <= hi && (
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// True if the byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && pa < pb + nb && pb < pa + na;
+}
+
 int64_t blob_bytes_raw(const moe_desc& d, int32_t inter) {
   const int64_t q = static_cast<int64_t>(d.hidden) * inter * d.bits / 8;
   const int64_t s = static_cast<int64_t>(d.hidden) * (inter / 64) * (d.sb_dtype == MOE_F32 ? 4 : 2);
@@ -223,8 +229,15 @@ static int layer_forward(const moe_desc* d, int32_t T, const void* x, const void
   if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(out, 16) || !aligned(slot_table, 8) ||
       !aligned(pool_base, 256) || !aligned(shared_w, 256))
     return fail(MOE_EINVAL, "misaligned pointer (x/router_w/out 16, slot_table 8, pool_base/shared_w 256)");
-  if (x_next && (d->out_dtype != MOE_F32 || !aligned(x_next, 16) || x_next == x))
-    return fail(MOE_EINVAL, "x_next needs fp32 output, 16-byte alignment and a buffer other than x");
+  if (x_next) {
+    if (d->out_dtype != MOE_F32 || !aligned(x_next, 16))
+      return fail(MOE_EINVAL, "x_next needs fp32 output and 16-byte alignment");
+    // the fused combine writes out and x_next element by element while other
+    // blocks still read x: x_next must share no byte with x or with out
+    const size_t act = d->act_dtype == MOE_F32 ? 4 : 2, n = static_cast<size_t>(T) * d->hidden;
+    if (overlaps(x_next, n * act, x, n * act) || overlaps(x_next, n * act, out, n * 4))
+      return fail(MOE_EINVAL, "x_next overlaps x or out");
+  }
   moe::WsLayout L;
   if ((rc = check_ws(*d, T, workspace, ws_bytes, &L))) return rc;
   if (T == 0) return ok();
@@ -292,6 +305,13 @@ int moe_residual_add(int32_t T, int32_t H, int32_t act_dtype, const void* x, con
     return fail(MOE_EINVAL, "T must be >= 0 and H >= 1, with T * H < 2^31");
   if (act_dtype != MOE_F32 && act_dtype != MOE_BF16) return fail(MOE_EINVAL, "act_dtype must be MOE_F32 or MOE_BF16");
   if (!x || !y || !x_next) return fail(MOE_EINVAL, "NULL x, y or x_next");
+  {
+    // each element is read and then written by one thread: x_next may be x
+    // exactly, but no other overlap with x or y is race-free
+    const size_t n = static_cast<size_t>(T) * H, act = act_dtype == MOE_F32 ? 4 : 2;
+    if ((x_next != x && overlaps(x_next, n * act, x, n * act)) || overlaps(x_next, n * act, y, n * 4))
+      return fail(MOE_EINVAL, "x_next overlaps y, or overlaps x other than exactly in place");
+  }
   if (T == 0) return ok();
   return finish(moe::launch_residual(act_dtype, x, y, x_next,
                                      static_cast<int64_t>(T) * H, static_cast<hipStream_t>(stream)));

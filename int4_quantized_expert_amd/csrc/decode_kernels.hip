@@ -590,8 +590,9 @@ static int last_launch_error() {
 // the activations are bf16.  Each element is read and written by one thread,
 // so x_next may be x.
 template <int ACT>
-__global__ __launch_bounds__(256) void k_residual(const void* __restrict__ x, const float* __restrict__ y,
-                                                 void* x_next, int64_t n) {
+// x_next may be x (the in-place step): no pointer here is restrict-qualified,
+// and each element is read before it is written by the same thread.
+__global__ __launch_bounds__(256) void k_residual(const void* x, const float* y, void* x_next, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= n) return;
   if constexpr (ACT == kBF16) {

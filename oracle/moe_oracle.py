@@ -50,7 +50,6 @@ are float32 or bfloat16.  All arithmetic here is float64 on the stored values.
 
 from __future__ import annotations
 
-import math
 from dataclasses import dataclass
 
 import numpy as np
@@ -290,12 +289,39 @@ def moe_layer_dense(shape: LayerShape, T: int, x, router_w, slot_table, pool, sh
     return y
 
 
-def topk_margin(logits_row: np.ndarray, k: int) -> float:
-    """Gap between the k-th and (k+1)-th largest logit (inf when k == E)."""
-    if k >= logits_row.shape[0]:
-        return math.inf
-    srt = np.sort(logits_row)[::-1]
-    return float(srt[k - 1] - srt[k])
+def moe_layer_by_expert(shape: LayerShape, T: int, x, router_w, slot_table, pool, shared_w):
+    """Third formulation, for many tokens: the routed sum taken expert by expert.
+
+    y_t = sum_{e in S_t} p_{t,e} E_e(x_t) + sigmoid(g . x_t) E_shared(x_t) is the
+    masked dense sum of moe_layer_dense with its zero terms skipped: every
+    expert that some token chose is parsed once, applied to all the tokens
+    that chose it (one float64 matrix product per matrix), and its weighted
+    output added to those tokens' rows.  Routing (R2) is the same
+    select_topk / renormalised_weights as the other formulations.  The
+    additions into a row run in ascending expert id rather than rank order,
+    which changes float64 rounding only.
+
+    Returns (y [T, H] float64, topk_ids [T, k] int32, topk_w [T, k] float64).
+    """
+    H, k = shape.hidden, shape.top_k
+    xs, rw, gvec = load_inputs(shape, T, x, router_w, shared_w)
+    logits = router_logits(xs, rw)
+    ids = np.stack([select_topk(logits[t], k) for t in range(T)]) if T else np.zeros((0, k), np.int32)
+    w = np.stack([renormalised_weights(logits[t, ids[t]]) for t in range(T)]) if T else np.zeros((0, k))
+    y = np.zeros((T, H))
+    for e in np.unique(ids):
+        tok, rank = np.nonzero(ids == e)
+        wg, wu, wd = parse_blob(expert_blob(shape, pool, slot_table, int(e)), H, shape.inter, shape.bits,
+                                shape.sb_dtype)
+        xe = xs[tok].T                                      # [H, n]
+        h = silu(wg @ xe) * (wu @ xe)                       # [I, n]
+        y[tok] += (wd @ h).T * w[tok, rank][:, None]
+    sh = np.ascontiguousarray(shared_w).view(np.uint8)
+    wg, wu, wd = parse_blob(sh[: blob_bytes(H, shape.shared_inter, shape.bits, shape.sb_dtype)], H,
+                            shape.shared_inter, shape.bits, shape.sb_dtype)
+    xa = xs.T
+    y += (wd @ (silu(wg @ xa) * (wu @ xa))).T * sigmoid(xs @ gvec)[:, None]
+    return y, ids, w
 
 
 def summation_bound(x_row: np.ndarray, router: np.ndarray, exact_products: bool) -> np.ndarray:

@@ -168,6 +168,38 @@ def oracle_run(data: LayerData, tokens=None):
                        tokens=tokens)
 
 
+def oracle_run_all(data: LayerData):
+    """Every token of the batch through the oracle's expert-major formulation
+    (each chosen blob parsed once for all the tokens that chose it): fast
+    enough for thousands of tokens.  Returns (y, ids, w)."""
+    return O.moe_layer_by_expert(oracle_shape(data.geo), data.T, data.x, data.R, data.slots, data.pool,
+                                 data.shared)
+
+
+def relocate(dl: DeviceLayer, data: LayerData, seed: int = 0):
+    """The same blobs in one pool of more than 4 GiB at a permuted placement:
+    every odd expert above byte offset 2^32 (offsets that do not fit 32 bits),
+    every even one below it.  Returns (big pool, slot table), ready for
+    upload(data, pool=..., slots=...)."""
+    g = data.geo
+    stride = g.blob_stride
+    E = g.n_experts
+    n_lo, n_hi = (E + 1) // 2, E // 2
+    base = (1 << 32) + 3 * 256
+    big = torch.zeros(base + (n_hi + 1) * stride, dtype=torch.uint8, device=DEV)
+    rng = np.random.default_rng(seed)
+    lo_perm, hi_perm = rng.permutation(n_lo + 1)[:n_lo], rng.permutation(n_hi + 1)[:n_hi]
+    slots = np.empty(E, dtype=np.int64)
+    src = np.asarray(data.slots, dtype=np.int64)
+    for e in range(E):
+        off = base + int(hi_perm[e // 2]) * stride if e % 2 else int(lo_perm[e // 2]) * stride
+        slots[e] = off
+        big[off: off + stride] = dl.pool[int(src[e]): int(src[e]) + stride]
+    torch.cuda.synchronize()
+    assert slots.max() > (1 << 32) and slots.min() < (1 << 32)
+    return big, slots
+
+
 def bf16_half_ulp(v: np.ndarray) -> np.ndarray:
     a = np.abs(v)
     e = np.floor(np.log2(np.where(a > 0, a, 1e-38)))

@@ -120,3 +120,37 @@ def test_launch_event_hook_argument_checks():
     assert L.moe_layer_forward(ctypes.byref(d), -1, None, None, None, None, None, None, None, 0, None, None,
                                None) == -1
     assert n.value == 7, "a consumed setting must not be written again"
+
+
+def test_chain_rejects_x_next_overlapping_x_or_out():
+    """x_next must share no byte with x or out (the fused combine writes them
+    element by element while other blocks still read x)."""
+    d = good_desc()
+    T, H = 2, 2048
+    buf = ctypes.create_string_buffer(1 << 20)
+    p = ctypes.addressof(buf) // 256 * 256 + 256
+    x, out, ws = p, p + 65536, p + 131072
+    L = M.lib()
+    need = M.workspace_bytes(d, T)
+
+    def chain(x_next):
+        return L.moe_layer_forward_chain(ctypes.byref(d), T, x, p, p, p, p, out, x_next, ws, need, None, None,
+                                         None)
+    assert chain(x) == -1                          # in place
+    assert chain(x + 16) == -1                     # x at an offset
+    assert chain(x - T * H * 2 + 16) == -1         # ends inside x
+    assert chain(out) == -1                        # x_next == out
+    assert chain(out + T * H * 4 - 16) == -1       # starts inside out
+    assert "overlaps" in M.last_error()
+
+
+def test_residual_add_rejects_partial_overlap():
+    T, H = 2, 256
+    buf = ctypes.create_string_buffer(1 << 16)
+    p = ctypes.addressof(buf) // 256 * 256 + 256
+    x, y = p, p + 8192
+    L = M.lib()
+    assert L.moe_residual_add(T, H, M.MOE_BF16, x, y, x + 2, None) == -1     # shifted in-place
+    assert L.moe_residual_add(T, H, M.MOE_BF16, x, y, y + 4, None) == -1     # into y
+    assert L.moe_residual_add(T, H, M.MOE_F32, x, y, y - 4, None) == -1      # ends inside y
+    assert L.moe_residual_add(0, H, M.MOE_BF16, x, y, x, None) == 0          # exact in place is fine

@@ -314,6 +314,27 @@ def test_routed_loop_matches_dense_masked(preset, E, k, bits):
     assert np.max(np.abs(y - yd)) <= 1e-12 * np.max(np.abs(y))
 
 
+@pytest.mark.parametrize("E,k,bits,sb,T", [(16, 2, 4, "f32", 6), (12, 3, 8, "bf16", 9), (16, 16, 4, "bf16", 3)])
+def test_expert_major_matches_token_loop_and_dense(E, k, bits, sb, T):
+    """The expert-by-expert formulation (used for whole-batch checks of many
+    tokens) agrees with the per-token loop and the dense masked sum."""
+    base = synth.PRESETS["tiny"]
+    g = synth.Geometry(base.hidden, E, k, base.inter, 2 * base.shared_inter, bits, "f32", sb)
+    shape = O.LayerShape(g.hidden, E, k, g.inter, g.shared_inter, bits, "f32", sb)
+    pool, slots = synth.make_pool(g, 31, 1)
+    slots = slots[::-1].copy()                      # a permuted placement
+    shared = synth.make_shared(g, 31, 1)
+    x = synth.tokens(g, 31, 1, T)
+    R = synth.router_normal(g, 31, 1)
+    y, ids, w, _ = O.moe_layer(shape, T, x, R, slots, pool, shared)
+    yb, idb, wb = O.moe_layer_by_expert(shape, T, x, R, slots, pool, shared)
+    yd = O.moe_layer_dense(shape, T, x, R, slots, pool, shared)
+    np.testing.assert_array_equal(ids, idb)
+    np.testing.assert_allclose(wb, w, rtol=0, atol=1e-15)
+    assert np.max(np.abs(yb - y)) <= 1e-12 * np.max(np.abs(y))
+    assert np.max(np.abs(yb - yd)) <= 1e-12 * np.max(np.abs(y))
+
+
 def test_gemv_core_against_scalar_loop():
     """Dequantized matvec vs a scalar loop over the packed words (64 x 64)."""
     rng = np.random.default_rng(8)
@@ -374,6 +395,33 @@ def test_summation_bound_holds_float32():
     pair = prod.sum(axis=1, dtype=np.float32)
     assert np.all(np.abs(seq - exact) <= bound)
     assert np.all(np.abs(pair - exact) <= bound)
+
+
+def test_summation_bound_fixed_values_and_attained():
+    """Hand-worked values of the bound, and a sum whose float32 error reaches it.
+
+    x = (1, -2, 0.5), rows (1, 1, 1) and (2, 0, -4): sum |x_h R_eh| = 3.5 and 4.
+    With exact products n - 1 = 2 additions, so the bound is gamma_2 times
+    that, gamma_m = m 2^-24 / (1 - m 2^-24); with rounded products, gamma_3.
+    Summing (1, 2^-24, 2^-24) left to right in float32 rounds both additions
+    back to 1 (ties to even), an error of exactly 2^-23, while the bound is
+    gamma_2 (1 + 2^-23) = 2^-23 (1 + 2^-23) / (1 - 2^-23): a bound one
+    notch smaller (gamma_1, or u / 2 per addition) would not cover it."""
+    u = 2.0 ** -24
+    g2, g3 = 2 * u / (1 - 2 * u), 3 * u / (1 - 3 * u)
+    x = np.array([1.0, -2.0, 0.5])
+    R = np.array([[1.0, 1.0, 1.0], [2.0, 0.0, -4.0]])
+    assert np.array_equal(O.summation_bound(x, R, True), np.array([g2 * 3.5, g2 * 4.0]))
+    assert np.array_equal(O.summation_bound(x, R, False), np.array([g3 * 3.5, g3 * 4.0]))
+    terms = np.array([1.0, u, u])
+    s = np.float32(0.0)
+    for v in terms.astype(np.float32):
+        s = np.float32(s + v)
+    err = abs(float(s) - terms.sum())
+    assert err == 2.0 ** -23
+    bound = float(O.summation_bound(np.ones(3), terms[None, :], True)[0])
+    assert err <= bound < err * (1 + 2.0 ** -21)
+    assert err > (u / (1 - u)) * terms.sum()        # gamma_1 would be too small
 
 
 def test_splitmix64_published_outputs():
