@@ -70,6 +70,9 @@ def parse():
                     help="35b_int8_store: container file written (or rewritten) before timing")
     ap.add_argument("--buffered", action="store_true",
                     help="35b_int8_store: read through the page cache instead of O_DIRECT")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="80b_stack_decode at T = 1: skip the extra figures (chained, uniform routing, T = 8, "
+                         "prefill) reported on the same line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first fill and copy a 256 MiB buffer once: the known-size reference that scales "
                          "HBM byte counters read by a profiler")
@@ -98,18 +101,8 @@ def main():
 
     if args.workload == "35b_int8_store":
         return store_stream(args, torch, M, synth, sgpu)
-    preset, n_layers, T_fixed, routing, out_dt = WORKLOADS[args.workload]
-    geo = synth.PRESETS[preset]
-    T = T_fixed or args.tokens
-    prefill = T_fixed is not None
-    K, W = args.steps, args.warmup
-    S = K + W
-    XS = 1 if prefill else S          # distinct token batches per layer
-    H, E, k = geo.hidden, geo.n_experts, geo.top_k
-    stride = geo.blob_stride
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream(dev)
     if args.copy_probe:
         src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -117,15 +110,81 @@ def main():
         dst.copy_(src)           # reads and writes COPY_PROBE_BYTES
         torch.cuda.synchronize()
         del src, dst
+    ctx = Context(args, torch, M, synth, sgpu)
+    head = measure(ctx, args.workload, args.tokens, args.chain, None, args.steps, args.warmup)
+    result = head["line"]
+    if not args.no_extras and args.workload == "80b_stack_decode" and args.tokens == 1 and not args.chain:
+        # further figures on the same line: the chained stack, near-uniform routing (fewer blobs served
+        # again from the 256 MB last-level cache than under Zipf routing), T = 8 and the T = 2048 prefill
+        extra = {}
+        ke, we = min(args.steps, 16), 2
+        for name, wl, T, chain, routing, kk in (("chained_t1", "80b_stack_decode", 1, True, None, ke),
+                                                ("uniform_t1", "80b_stack_decode", 1, False, "normal", ke),
+                                                ("t8", "80b_stack_decode", 8, False, None, ke),
+                                                ("prefill_t2048", "80b_prefill", 2048, False, None, 2)):
+            r = measure(ctx, wl, T, chain, routing, kk, we)["line"]
+            extra[name] = {key: r[key] for key in ("value", "unit", "ms_per_step", "steps", "hbm", "roofline",
+                                                   "kernels")}
+            extra[name]["config"] = {key: r["config"][key] for key in ("workload", "tokens_per_call", "routing",
+                                                                       "chained", "out_dtype")}
+        result["extra"] = extra
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(head["geo"], args, head["x_host"], head["r_host"], head["shared_host"],
+                                              head["n_layers"], head["XS"], head["T"], head["geo"].shared_bytes,
+                                              head["NX"])
+    print(json.dumps(result), flush=True)
+
+
+class Context:
+    """Device state shared by the measured configurations: the 43.5 GB pool of
+    the 80B stack (or the 35B one) and the per-layer shared-expert buffers."""
+
+    def __init__(self, args, torch, M, synth, sgpu):
+        self.args, self.torch, self.M, self.synth, self.sgpu = args, torch, M, synth, sgpu
+        self.dev = torch.device("cuda:0")
+        self.pools = {}
+
+    def pool(self, preset, n_layers):
+        key = (preset, n_layers)
+        if key not in self.pools:
+            torch, synth, geo = self.torch, self.synth, self.synth.PRESETS[preset]
+            E, stride = geo.n_experts, geo.blob_stride
+            stream = torch.cuda.current_stream(self.dev)
+            self.pools.clear()
+            torch.cuda.empty_cache()
+            t0 = time.time()
+            pool = torch.empty(n_layers * E * stride, dtype=torch.uint8, device=self.dev)
+            for l in range(n_layers):
+                self.sgpu.fill_blobs(geo, pool.data_ptr() + l * E * stride, E, self.args.seed, l, 0,
+                                     stream=stream.cuda_stream)
+            shared_host = np.concatenate([synth.make_shared(geo, self.args.seed, l) for l in range(n_layers)])
+            shared = torch.from_numpy(shared_host).to(self.dev)
+            torch.cuda.synchronize()
+            log(f"pool filled in {time.time() - t0:.1f}s: {pool.numel() / 1e9:.2f} GB, {n_layers} layers")
+            self.pools[key] = (pool, shared, shared_host)
+        return self.pools[key]
+
+
+def measure(ctx, workload, T_arg, chain_on, routing_over, K, W):
+    """Times K steps (after W warm-up steps) of one workload configuration and
+    returns the JSON line plus what the CPU baseline needs."""
+    args, torch, M, synth = ctx.args, ctx.torch, ctx.M, ctx.synth
+    preset, n_layers, T_fixed, routing, out_dt = WORKLOADS[workload]
+    routing = routing_over or routing
+    geo = synth.PRESETS[preset]
+    T = T_fixed or T_arg
+    prefill = T_fixed is not None
+    S = K + W
+    XS = 1 if prefill else S          # distinct token batches per layer
+    H, E, k = geo.hidden, geo.n_experts, geo.top_k
+    stride = geo.blob_stride
+    dev = ctx.dev
+    stream = torch.cuda.current_stream(dev)
+    pool, shared, shared_host = ctx.pool(preset, n_layers)
+    shared_bytes = geo.shared_bytes
 
     # ---------------------------------------------------------------- inputs
     t0 = time.time()
-    pool = torch.empty(n_layers * E * stride, dtype=torch.uint8, device=dev)
-    for l in range(n_layers):
-        sgpu.fill_blobs(geo, pool.data_ptr() + l * E * stride, E, args.seed, l, 0, stream=stream.cuda_stream)
-    shared_bytes = geo.shared_bytes
-    shared_host = np.concatenate([synth.make_shared(geo, args.seed, l) for l in range(n_layers)])
-    shared = torch.from_numpy(shared_host).to(dev)
     # prefill: 8 distinct 2048-token batches cycle over the layers (each layer has its own router)
     NX = min(n_layers, 8) if prefill else n_layers
     x_host = np.empty((NX, XS * T, H), dtype=np.uint16)
@@ -141,41 +200,50 @@ def main():
     # so the slot offsets of the deeper layers exceed 2^32 (up to 4.3e10 on the 80B stack)
     slots = (torch.arange(n_layers * E, dtype=torch.int64, device=dev) * stride).reshape(n_layers, E)
     out = torch.empty(n_layers, T, H, dtype=torch.float32 if out_dt == "f32" else torch.bfloat16, device=dev)
-    ids = torch.full((n_layers, XS, T, k), -1, dtype=torch.int32, device=dev)
+    ids = torch.full((XS, n_layers, T, k), -1, dtype=torch.int32, device=dev)
     desc = M.desc_for(H, E, k, geo.inter, geo.shared_inter, geo.bits, geo.act, geo.sb, out_dt,
                       pool_bytes=pool.numel())
     ws = torch.zeros(M.workspace_bytes(desc, T), dtype=torch.uint8, device=dev)
     M.workspace_init(ws)
     torch.cuda.synchronize()
-    log(f"inputs ready in {time.time() - t0:.1f}s: pool {pool.numel() / 1e9:.2f} GB, {n_layers} layers, T={T}")
+    log(f"{workload} T={T} routing={routing} chain={chain_on}: inputs ready in {time.time() - t0:.1f}s")
 
     act_sz = 2 if geo.act == "bf16" else 4
     r_bytes = E * H * act_sz
-
+    xb = T * H * act_sz
+    ob = T * H * out.element_size()
     chain = None
-    if args.chain:
+    if chain_on:
         assert not prefill, "--chain is for the decode workloads"
-        chain = torch.empty(n_layers * T * H * act_sz, dtype=torch.uint8, device=dev)
+        chain = torch.empty(n_layers * xb, dtype=torch.uint8, device=dev)
+    # T = 1: one moe_stack_forward call per step, which runs all layers in one launch
+    use_stack = not prefill and T == 1
 
     def x_in(l, s):
-        xs = s % XS
         if chain is not None and l > 0:
-            return chain.data_ptr() + l * T * H * act_sz
-        return x.data_ptr() + ((l % NX) * XS * T + xs * T) * H * act_sz
+            return chain.data_ptr() + (l - 1) * xb
+        return x.data_ptr() + ((l % NX) * XS * T + (s % XS) * T) * H * act_sz
 
     def layer_call(l, s, strm):
         xs = s % XS
         args_l = (desc, T, x_in(l, s), routers.data_ptr() + l * r_bytes, slots[l], pool.data_ptr(),
                   shared.data_ptr() + l * shared_bytes, out[l])
-        if chain is not None and l + 1 < n_layers:
-            M.layer_forward_chain(*args_l, chain.data_ptr() + (l + 1) * T * H * act_sz, ws, ids[l, xs], None,
-                                  stream=strm)
+        if chain is not None:
+            M.layer_forward_chain(*args_l, chain.data_ptr() + l * xb, ws, ids[xs, l], None, stream=strm)
         else:
-            M.layer_forward(*args_l, ws, ids[l, xs], None, stream=strm)
+            M.layer_forward(*args_l, ws, ids[xs, l], None, stream=strm)
+
+    def stack_call(s, strm):
+        M.stack_forward(desc, n_layers, T, x.data_ptr() + (s % XS) * xb, XS * xb, routers, r_bytes, slots, E * 8,
+                        pool, shared, shared_bytes, out, ob, ws, x_chain=chain,
+                        chain_stride=xb if chain is not None else 0, topk_ids=ids[s % XS], stream=strm)
 
     def step(s, strm):
-        for l in range(n_layers):
-            layer_call(l, s, strm)
+        if use_stack:
+            stack_call(s, strm)
+        else:
+            for l in range(n_layers):
+                layer_call(l, s, strm)
 
     # ---------------------------------------------------------------- timed run
     graphs = []
@@ -212,13 +280,14 @@ def main():
     layer_tokens = K * n_layers * T
     value = layer_tokens / (total_ms * 1e-3)
     log(f"timed {K} steps: {total_ms:.2f} ms (wall {wall * 1e3:.2f} ms), {ms_per_step * 1e3 / n_layers:.2f} us/layer")
+    del graphs
 
     # algorithmic bytes from the realised routing (distinct experts per layer call)
     ids_h = ids.cpu().numpy()
     steps_timed = [s % XS for s in range(W, S)]
-    per_ls = np.array([[len(np.unique(ids_h[l, xs])) for xs in steps_timed] for l in range(n_layers)])
+    per_ls = np.array([[len(np.unique(ids_h[xs, l])) for xs in steps_timed] for l in range(n_layers)])
     blob = M.blob_bytes(desc, False)
-    fixed = M.blob_bytes(desc, True) + r_bytes + H * act_sz + T * H * act_sz + T * H * out.element_size()
+    fixed = M.blob_bytes(desc, True) + r_bytes + H * act_sz + xb + ob
     bytes_total = float(per_ls.sum() * blob + fixed * per_ls.size)
     bytes_per_layer = bytes_total / per_ls.size
     stack_gbs = bytes_total / (total_ms * 1e-3) / 1e9
@@ -227,14 +296,20 @@ def main():
     # The library attaches a start/end event pair to each kernel dispatch of one call
     # (moe_set_launch_events); the runtime stamps them with that dispatch's execution.
     n_inst = min(8 if not prefill else 2, K)
-    timers = [M.LaunchTimer(16) for _ in range(n_inst * n_layers)]
-    torch.cuda.synchronize()
-    i = 0
+    calls = []          # (step, layer or None for a whole-stack call)
     for s in range(W, W + n_inst):
-        for l in range(n_layers):
-            timers[i].arm()
+        if use_stack:
+            calls.append((s, None))
+        else:
+            calls += [(s, l) for l in range(n_layers)]
+    timers = [M.LaunchTimer(16) for _ in calls]
+    torch.cuda.synchronize()
+    for tm, (s, l) in zip(timers, calls):
+        tm.arm()
+        if l is None:
+            stack_call(s, stream.cuda_stream)
+        else:
             layer_call(l, s, stream.cuda_stream)
-            i += 1
     torch.cuda.synchronize()
     M.status_check(ws)
     n_k = {t.n_recorded // 2 for t in timers}
@@ -242,9 +317,11 @@ def main():
         raise RuntimeError(f"calls launched differing kernel counts: {sorted(n_k)}")
     n_k = n_k.pop()
     durs = np.array([t.kernel_us() for t in timers])                       # [calls, kernels] us
-    uniq_inst = np.array([per_ls[l, s - W] for s in range(W, W + n_inst) for l in range(n_layers)],
-                         dtype=np.float64)
-    kernels = kernel_work(desc, geo, T, n_k, uniq_inst, prefill, out.element_size())
+    if use_stack:
+        uniq_inst = [per_ls[:, s - W].astype(np.float64) for s, _ in calls]   # per call: one value per layer
+    else:
+        uniq_inst = [np.array([per_ls[l, s - W]], dtype=np.float64) for s, l in calls]
+    kernels = kernel_work(desc, geo, T, n_k, uniq_inst, prefill, out.element_size(), use_stack, n_layers)
     table = []
     for j, (name, nbytes, flops) in enumerate(kernels):
         us = float(durs[:, j].mean())
@@ -259,7 +336,7 @@ def main():
     dom = max(range(n_k), key=lambda j: durs[:, j].mean())
     achieved = table[dom]["gbs"]
     traffic = None
-    counters = load_traffic(os.path.join(ROOT, "profiles"), args.workload, T)
+    counters = load_traffic(os.path.join(ROOT, "profiles"), workload, T)
     if counters is not None:
         stem = table[dom]["kernel"].split(" ")[0]
         hits = [r for kname, r in counters["kernels"].items() if kname.split("<")[0] == stem]
@@ -281,12 +358,12 @@ def main():
         "dtype": "f32" if not prefill else "f16",
         "data": "synthetic",
         "config": {
-            "workload": args.workload, "layers": n_layers, "tokens_per_call": T, "hidden": H,
+            "workload": workload, "layers": n_layers, "tokens_per_call": T, "hidden": H,
             "experts": E, "top_k": k, "inter": geo.inter, "shared_inter": geo.shared_inter,
             "bits": geo.bits, "group": 64, "scale_dtype": geo.sb, "act_dtype": geo.act, "out_dtype": out_dt,
             "routing": routing, "pool_gb": round(pool.numel() / 1e9, 2), "pool_bases": 1,
             "max_slot_offset": int(slots.max().item()), "graphs": not args.eager,
-            "chained": bool(args.chain),
+            "chained": bool(chain_on), "launch": "one per step (all layers)" if use_stack else "per layer",
         },
         "hbm": {
             "algorithmic_bytes_per_layer": round(bytes_per_layer),
@@ -311,12 +388,11 @@ def main():
     if "tflops" in table[dom]:
         result["roofline"]["mfma"] = {"achieved": table[dom]["tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
                                       "unit": "TFLOP/s", "frac": table[dom]["mfma_frac"]}
-
-    # ---------------------------------------------------------------- CPU oracle baseline
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(geo, args, x_host, r_host, shared_host, n_layers, XS, T,
-                                              shared_bytes, NX)
-    print(json.dumps(result), flush=True)
+    out_info = {"line": result, "geo": geo, "x_host": x_host, "r_host": r_host, "shared_host": shared_host,
+                "n_layers": n_layers, "XS": XS, "T": T, "NX": NX}
+    del x, routers, out, ws, chain
+    torch.cuda.synchronize()
+    return out_info
 
 
 def store_stream(args, torch, M, synth, sgpu):
@@ -447,11 +523,10 @@ def store_stream(args, torch, M, synth, sgpu):
     print(json.dumps(line), flush=True)
 
 
-def kernel_work(desc, geo, T, n_kernels, uniq, prefill, out_bytes):
-    """(name, algorithmic HBM bytes, MFMA flops) of each kernel of one layer call, per call
-    (arrays over calls).  A plane is one matrix of a blob: its codes, scales and biases.
-    Workspace traffic (logits, h, partial rows) is not counted.
-    """
+def kernel_work(desc, geo, T, n_kernels, uniq, prefill, out_bytes, stack=False, n_layers=1):
+    """(name, algorithmic HBM bytes, MFMA flops) of each kernel of one call, per call (lists over calls;
+    uniq[c] holds the distinct experts of each layer of call c).  A plane is one matrix of a blob: its
+    codes, scales and biases.  Workspace traffic (logits, h, partial rows, exchanged words) is not counted."""
     H, E, I, SI, k = desc.hidden, desc.n_experts, desc.inter, desc.shared_inter, desc.top_k
     sb = 4 if geo.sb == "f32" else 2
     act = 4 if geo.act == "f32" else 2
@@ -463,28 +538,33 @@ def kernel_work(desc, geo, T, n_kernels, uniq, prefill, out_bytes):
     router = E * H * act + T * H * act
     gvec = H * act
     out = T * H * out_bytes
+    u = np.array([float(np.sum(v)) for v in uniq])     # distinct experts summed over a call's layers
+    nl = np.array([float(len(v)) for v in uniq])       # layers per call
     if prefill:
         pairs = T * k
         table = [
-            ("k_pf_router", router, 2.0 * T * E * H),
+            ("k_pf_router", router * nl, 2.0 * T * E * H * nl),
             ("k_topk", None, None),
-            ("k_pf_gate", gvec + T * H * act, None),
+            ("k_pf_gate", (gvec + T * H * act) * nl, None),
             ("k_pf_dispatch", None, None),
-            ("k_pf_xprep", T * H * act, None),
-            ("k_pf_gateup", 2 * p_s + 2 * p_r * uniq, 4.0 * (pairs * I + T * SI) * H),
-            ("k_pf_down", p_s + p_r * uniq, 2.0 * (pairs * I + T * SI) * H),
-            ("k_combine", out, None),
+            ("k_pf_xprep", T * H * act * nl, None),
+            ("k_pf_gateup", 2 * p_s * nl + 2 * p_r * u, 4.0 * (pairs * I + T * SI) * H * nl),
+            ("k_pf_down", p_s * nl + p_r * u, 2.0 * (pairs * I + T * SI) * H * nl),
+            ("k_combine", out * nl, None),
         ]
         return table[:n_kernels]
+    if stack:
+        return [(f"k_decode_stack (one launch: {n_layers} layers of router, top-k, gate/up, down, ordered combine)",
+                 (router + gvec + 3 * p_s + out) * nl + 3 * p_r * u, None)]
     if n_kernels == 1:
         return [("k_decode_a (one launch: router, top-k, gate/up, down, ordered combine)",
-                 router + gvec + 3 * p_s + 3 * p_r * uniq + out, None)]
+                 (router + gvec + 3 * p_s + out) * nl + 3 * p_r * u, None)]
     if n_kernels == 2:
         return [("k_decode_a (router, shared gate/up, top-k, dispatch, routed gate/up)",
-                 router + gvec + 2 * p_s + 2 * p_r * uniq, None),
-                ("k_decode_b (down projections, ordered combine)", p_s + p_r * uniq + out, None)]
+                 (router + gvec + 2 * p_s) * nl + 2 * p_r * u, None),
+                ("k_decode_b (down projections, ordered combine)", (p_s + out) * nl + p_r * u, None)]
     names = ["k_router_logits", "k_topk", "k_dispatch", "k_gateup", "k_down", "k_combine"]
-    nb = [router, None, gvec + T * H * act, 2 * p_s + 2 * p_r * uniq, p_s + p_r * uniq, out]
+    nb = [router * nl, None, (gvec + T * H * act) * nl, 2 * p_s * nl + 2 * p_r * u, p_s * nl + p_r * u, out * nl]
     return [(n, b, None) for n, b in zip(names, nb)][:n_kernels]
 
 

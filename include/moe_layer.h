@@ -154,18 +154,27 @@ int moe_layer_forward(const moe_desc* d, int32_t T, const void* x, const void* r
                       float* topk_w, void* stream);
 
 /*
- * Which kernels run.  For 1 <= T <= 8 with bf16 activations and scales (or
- * float32 activations, scales and output) moe_layer_forward runs TWO launches
- * per layer.  The first grid (all blocks resident at once) computes router
- * logits, the shared expert's gate/up rows and the sigmoid gate, exchanges the
- * logits between blocks as tagged 64-bit words (no fences), then every block
- * takes top-k and dispatch redundantly and computes its share of the routed
- * gate/up rows.  The second launch does the down projections and the ordered
- * combine.  The first launch needs every block resident, i.e. the GPU's
- * compute units not taken by other work; a bounded wait that expires raises
- * MOE_ETIMEOUT in moe_status_check.  Larger T runs the staged path (six
- * launches).  moe_layer_forward_staged always runs the staged path; both paths
- * give bitwise identical results.
+ * Which kernels run.  moe_layer_forward picks by T and the descriptor:
+ *   - T = 1 on the 80B/35B layer shape (hidden 2048, intermediate sizes 512,
+ *     int4 codes, bf16 activations and scales, E <= 512, top_k <= 10): ONE
+ *     launch, the stack kernel of moe_stack_forward with one layer (router,
+ *     top-k, gate/up, down and the ordered combine; blocks exchange the
+ *     logits and h as tagged words).
+ *   - other T <= 8 with bf16 activations and scales (or float32 activations,
+ *     scales and output): the fused decode path.  T = 1 with int4 codes is
+ *     one launch; otherwise two (the first computes the router logits, the
+ *     shared expert's gate/up rows and the gate, exchanges the logits between
+ *     blocks as tagged words, takes top-k and dispatch redundantly in every
+ *     block and computes the routed gate/up rows; the second the down rows
+ *     and the combine).
+ *   - T >= 16 with bf16 activations and H, I, SI multiples of 256: the MFMA
+ *     prefill path.
+ *   - otherwise: the staged path (six launches).
+ * The single-launch kernels need every block of their grid resident, i.e.
+ * the GPU's compute units not taken by other work; a bounded wait that
+ * expires raises MOE_ETIMEOUT in moe_status_check.
+ * moe_layer_forward_staged always runs the staged path.  For T <= 8 the
+ * staged and the decode paths give bitwise identical results.
  */
 int moe_layer_forward_staged(const moe_desc* d, int32_t T, const void* x, const void* router_w,
                              const int64_t* slot_table, const void* pool_base, const void* shared_w,
@@ -238,6 +247,41 @@ int moe_layer_forward_chain(const moe_desc* desc, int32_t T, const void* x, cons
                             const int64_t* slot_table, const void* pool_base, const void* shared_w, void* out,
                             void* x_next, void* workspace, size_t ws_bytes, int32_t* topk_ids, float* topk_w,
                             void* stream);
+
+/*
+ * A stack of n_layers MoE layers with the same descriptor, run in order: the
+ * pages run every token through the whole layer stack on the GPU and report
+ * the decode loop as bound by dispatch rather than by expert reads (Swiftlet
+ * README translation, "How it works" and "Status"; linlog.top article,
+ * "Capability limits").  Layer l (0 <= l < n_layers) reads
+ *   input      x + l * x_stride, or, when x_chain is not NULL and l > 0,
+ *              x_chain + (l - 1) * chain_stride
+ *   router     router_w + l * router_stride
+ *   slot table (const uint8_t*) slot_table + l * slot_stride  (int64 [E])
+ *   shared     shared_w + l * shared_stride
+ * all in one pool (pool_base, desc->pool_bytes), and writes
+ *   out        out + l * out_stride
+ *   x_chain    x_chain + l * chain_stride = its input + its output (the stack
+ *              step of moe_residual_add), when x_chain is not NULL
+ *   topk_ids / topk_w  (optional) [n_layers][T][k].
+ * Strides are in bytes; each must hold one layer's data and keep the
+ * alignment that moe_layer_forward asks of its pointer (checked when
+ * n_layers > 1).  x_chain needs out_dtype MOE_F32 and may not overlap x or
+ * out.  The result equals n_layers calls of moe_layer_forward (or, with
+ * x_chain, moe_layer_forward_chain) bit for bit.  For T = 1 on the 80B/35B
+ * layer shape (hidden 2048, intermediate sizes 512, int4 codes, bf16
+ * activations and scales, E <= 512, top_k <= 10) the whole stack is ONE
+ * launch that keeps every block of the grid resident (the GPU's compute
+ * units must not be taken by other work; a bounded wait that expires raises
+ * MOE_ETIMEOUT in moe_status_check); otherwise the layers run as separate
+ * calls.  The timing hook (moe_set_launch_events) counts the whole stack as
+ * one call.  MOE_EINVAL, MOE_ENOMEM, MOE_EHIP as for moe_layer_forward.
+ */
+int moe_stack_forward(const moe_desc* d, int32_t n_layers, int32_t T, const void* x, int64_t x_stride,
+                      const void* router_w, int64_t router_stride, const int64_t* slot_table, int64_t slot_stride,
+                      const void* pool_base, const void* shared_w, int64_t shared_stride, void* out,
+                      int64_t out_stride, void* x_chain, int64_t chain_stride, int32_t* topk_ids, float* topk_w,
+                      void* workspace, size_t ws_bytes, void* stream);
 
 /* Text of the last error on this thread ("" if none). */
 const char* moe_last_error(void);

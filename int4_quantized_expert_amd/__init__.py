@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     lib,
     residual_add,
     router_topk,
+    stack_forward,
     status_check,
     workspace_bytes,
     workspace_init,

@@ -82,6 +82,9 @@ def lib() -> ctypes.CDLL:
         L.moe_experts_forward.restype = ctypes.c_int
         L.moe_layer_forward_chain.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
         L.moe_layer_forward_chain.restype = ctypes.c_int
+        L.moe_stack_forward.argtypes = [dp, i32, i32, vp, i64, vp, i64, vp, i64, vp, vp, i64, vp, i64, vp, i64,
+                                        vp, vp, vp, sz, vp]
+        L.moe_stack_forward.restype = ctypes.c_int
         L.moe_residual_add.argtypes = [i32, i32, i32, vp, vp, vp, vp]
         L.moe_residual_add.restype = ctypes.c_int
         L.moe_status_check.argtypes = [vp, vp]
@@ -222,6 +225,18 @@ def experts_forward(d: MoeDesc, T: int, x, topk_ids, topk_w, slot_table, pool, s
     _check(lib().moe_experts_forward(ctypes.byref(d), T, _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(slot_table),
                                      _ptr(pool), _ptr(shared_w), _ptr(out), _ptr(ws), _nbytes(ws),
                                      _stream(stream, ws)))
+
+
+def stack_forward(d: MoeDesc, n_layers: int, T: int, x, x_stride: int, router_w, router_stride: int, slot_table,
+                  slot_stride: int, pool, shared_w, shared_stride: int, out, out_stride: int, ws,
+                  x_chain=None, chain_stride: int = 0, topk_ids=None, topk_w=None, stream=None) -> None:
+    """n_layers layers in order (moe_stack_forward); strides in bytes; layer l's data at base + l * stride.
+    With x_chain, layer l > 0 reads x_chain + (l - 1) * chain_stride and layer l writes its input + output
+    at x_chain + l * chain_stride."""
+    _check(lib().moe_stack_forward(ctypes.byref(d), n_layers, T, _ptr(x), x_stride, _ptr(router_w), router_stride,
+                                   _ptr(slot_table), slot_stride, _ptr(pool), _ptr(shared_w), shared_stride,
+                                   _ptr(out), out_stride, _ptr(x_chain), chain_stride, _ptr(topk_ids),
+                                   _ptr(topk_w), _ptr(ws), _nbytes(ws), _stream(stream, ws)))
 
 
 def residual_add(T: int, H: int, act: str, x, y, x_next, stream=None) -> None:

@@ -126,6 +126,24 @@ int cached_plan(const moe_desc& d, int T, moe::FusedPlan* plan) {
   return rc;
 }
 
+// Stack-kernel plans, cached per (device, E, k, output dtype).
+int cached_stack_plan(const moe_desc& d, moe::StackPlan* plan) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int, int>, std::pair<int, moe::StackPlan>> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ENODEV;
+  const auto key = std::make_tuple(dev, d.n_experts, d.top_k, d.out_dtype);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it == cache.end()) {
+    moe::StackPlan p{};
+    const int rc = moe::stack_plan(d, &p);
+    it = cache.emplace(key, std::make_pair(rc, p)).first;
+  }
+  *plan = it->second.second;
+  return it->second.first;
+}
+
 int finish(int rc) {
   if (rc != MOE_OK) {
     hipError_t e = hipGetLastError();
@@ -258,6 +276,27 @@ static int layer_forward(const moe_desc* d, int32_t T, const void* x, const void
   c.ids_out = topk_ids;
   c.wts_out = topk_w;
   c.stream = static_cast<hipStream_t>(stream);
+  if (allow_fused && T == 1 && moe::stack_supported(*d)) {
+    moe::StackPlan sp;
+    if (cached_stack_plan(*d, &sp) == MOE_OK) {
+      moe::StackCall sc{};
+      sc.d = *d;
+      sc.n_layers = 1;
+      sc.x = x;
+      sc.router_w = router_w;
+      sc.slot_table = slot_table;
+      sc.pool = c.pool;
+      sc.shared = c.shared;
+      sc.out = out;
+      sc.x_chain = x_next;
+      sc.ids_out = topk_ids;
+      sc.wts_out = topk_w;
+      sc.ws = c.ws;
+      sc.L = L;
+      sc.stream = c.stream;
+      return finish(moe::launch_decode_stack(sc, sp));
+    }
+  }
   if (allow_fused && moe::fused_supported(*d, T)) {
     moe::FusedPlan plan;
     if (cached_plan(*d, T, &plan) == MOE_OK) return finish(moe::launch_decode_fused(c, plan));
@@ -274,6 +313,87 @@ static int layer_forward(const moe_desc* d, int32_t T, const void* x, const void
   }
   if ((rc = moe::launch_router_topk(c, topk_ids, topk_w))) return finish(rc);
   return finish(step(moe::launch_experts(c)));
+}
+
+int moe_stack_forward(const moe_desc* d, int32_t n_layers, int32_t T, const void* x, int64_t x_stride,
+                      const void* router_w, int64_t router_stride, const int64_t* slot_table, int64_t slot_stride,
+                      const void* pool_base, const void* shared_w, int64_t shared_stride, void* out,
+                      int64_t out_stride, void* x_chain, int64_t chain_stride, int32_t* topk_ids, float* topk_w,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  MarkScope marks;
+  int rc;
+  if ((rc = check_desc(d)) || (rc = check_T(T))) return rc;
+  if (n_layers < 0 || n_layers > 4096) return fail(MOE_EINVAL, "n_layers=%d must be in [0, 4096]", n_layers);
+  if (!x || !router_w || !slot_table || !pool_base || !shared_w || !out)
+    return fail(MOE_EINVAL, "NULL input or output pointer");
+  const size_t act = d->act_dtype == MOE_F32 ? 4 : 2, outsz = d->out_dtype == MOE_F32 ? 4 : 2;
+  const int64_t xb = static_cast<int64_t>(T) * d->hidden * act, ob = static_cast<int64_t>(T) * d->hidden * outsz;
+  const int64_t rbytes = static_cast<int64_t>(d->n_experts) * d->hidden * act;
+  if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(out, 16) || !aligned(slot_table, 8) ||
+      !aligned(pool_base, 256) || !aligned(shared_w, 256) || (x_chain && !aligned(x_chain, 16)))
+    return fail(MOE_EINVAL, "misaligned pointer (x/router_w/out/x_chain 16, slot_table 8, pool_base/shared_w 256)");
+  if (n_layers > 1 &&
+      ((!x_chain && (x_stride < xb || x_stride % 16)) || router_stride < rbytes || router_stride % 16 ||
+       slot_stride < static_cast<int64_t>(d->n_experts) * 8 || slot_stride % 8 || shared_stride < d->shared_stride ||
+       shared_stride % 256 || out_stride < ob || out_stride % 16 || (x_chain && (chain_stride < xb || chain_stride % 16))))
+    return fail(MOE_EINVAL, "a per-layer stride is smaller than one layer's data or misaligned");
+  if (x_chain) {
+    if (d->out_dtype != MOE_F32) return fail(MOE_EINVAL, "x_chain needs fp32 output");
+    const int64_t span = (n_layers - 1) * chain_stride + xb;
+    if (overlaps(x_chain, span, x, xb) || overlaps(x_chain, span, out, (n_layers - 1) * out_stride + ob))
+      return fail(MOE_EINVAL, "x_chain overlaps x or out");
+  }
+  moe::WsLayout L;
+  if ((rc = check_ws(*d, T, workspace, ws_bytes, &L))) return rc;
+  if (T == 0 || n_layers == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (T == 1 && moe::stack_supported(*d)) {
+    moe::StackPlan sp;
+    if (cached_stack_plan(*d, &sp) == MOE_OK) {
+      moe::StackCall sc{};
+      sc.d = *d;
+      sc.n_layers = n_layers;
+      sc.x = x;
+      sc.x_stride = x_stride;
+      sc.router_w = router_w;
+      sc.router_stride = router_stride;
+      sc.slot_table = slot_table;
+      sc.slot_stride = slot_stride;
+      sc.pool = static_cast<const uint8_t*>(pool_base);
+      sc.shared = static_cast<const uint8_t*>(shared_w);
+      sc.shared_stride = shared_stride;
+      sc.out = out;
+      sc.out_stride = out_stride;
+      sc.x_chain = x_chain;
+      sc.chain_stride = chain_stride;
+      sc.ids_out = topk_ids;
+      sc.wts_out = topk_w;
+      sc.ws = static_cast<uint8_t*>(workspace);
+      sc.L = L;
+      sc.stream = st;
+      return finish(moe::launch_decode_stack(sc, sp));
+    }
+  }
+  // any other shape or T: the layers one call after another
+  const size_t k = static_cast<size_t>(T) * d->top_k;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const uint8_t* xl = (x_chain && l > 0) ? static_cast<const uint8_t*>(x_chain) + (l - 1) * chain_stride
+                                           : static_cast<const uint8_t*>(x) + l * x_stride;
+    const uint8_t* rl = static_cast<const uint8_t*>(router_w) + l * router_stride;
+    const int64_t* sl = reinterpret_cast<const int64_t*>(reinterpret_cast<const uint8_t*>(slot_table) + l * slot_stride);
+    const uint8_t* shl = static_cast<const uint8_t*>(shared_w) + l * shared_stride;
+    uint8_t* ol = static_cast<uint8_t*>(out) + l * out_stride;
+    int32_t* il = topk_ids ? topk_ids + l * k : nullptr;
+    float* wl = topk_w ? topk_w + l * k : nullptr;
+    if (x_chain)
+      rc = moe_layer_forward_chain(d, T, xl, rl, sl, pool_base, shl, ol,
+                                   static_cast<uint8_t*>(x_chain) + l * chain_stride, workspace, ws_bytes, il, wl,
+                                   stream);
+    else
+      rc = moe_layer_forward(d, T, xl, rl, sl, pool_base, shl, ol, workspace, ws_bytes, il, wl, stream);
+    if (rc != MOE_OK) return rc;
+  }
+  return ok();
 }
 
 int moe_layer_forward_chain(const moe_desc* d, int32_t T, const void* x, const void* router_w,

@@ -36,6 +36,9 @@ struct WsLayout {
   size_t f_pidx;     // two-launch path: [min(T k, E), T] int32 rank of expert u for token t
   size_t f_epoch;    // two-launch path: [kFusedMaxBlocks] uint32 per-block call counters (inside ctrl)
   size_t f_gflag;    // single-launch decode: [kFusedReplicas][kFusedMaxBlocks] uint32 completion tags
+  size_t s_lg;       // stack decode: tagged logits (replicated)
+  size_t s_h;        // stack decode: tagged h rows and gate (replicated)
+  size_t s_x;        // stack decode: tagged next-layer input (replicated)
   size_t p_x16;      // prefill: [T, H] float16 activations in MFMA k order
   size_t p_meta;     // prefill: int32 [0] number of expert tiles
   size_t p_tstart;   // prefill: [min(T k, E) + 2] int32 first tile of each distinct expert, then of the shared one
@@ -53,6 +56,13 @@ constexpr int kPrefillMinT = 16;    // fewest tokens that take the prefill path
 
 inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
+// Stack decode (T = 1, one persistent launch for one or more layers): the
+// shapes it is built for and the sizes of its exchange buffers.
+bool stack_supported(const moe_desc& d);
+size_t stack_ws_lg(const moe_desc& d);
+size_t stack_ws_h(const moe_desc& d);
+size_t stack_ws_x();
+
 inline WsLayout ws_layout(const moe_desc& d, int32_t T) {
   WsLayout L{};
   const size_t Tk = static_cast<size_t>(T) * d.top_k;
@@ -65,6 +75,11 @@ inline WsLayout ws_layout(const moe_desc& d, int32_t T) {
   const size_t Tf = kFusedMaxT;
   L.f_lg = take(static_cast<size_t>(kFusedReplicas) * Tf * d.n_experts * 8);
   L.f_gflag = take(static_cast<size_t>(kFusedReplicas) * kFusedMaxBlocks * 4);
+  // the stack decode's exchange words; their offsets do not depend on T either
+  const bool st = stack_supported(d);
+  L.s_lg = take(st ? stack_ws_lg(d) : 0);
+  L.s_h = take(st ? stack_ws_h(d) : 0);
+  L.s_x = take(st ? stack_ws_x() : 0);
   L.logits = take(static_cast<size_t>(T) * d.n_experts * 4);
   L.ids = take(Tk * 4);
   L.wts = take(Tk * 4);
@@ -142,6 +157,42 @@ int launch_residual(int act_dtype, const void* x, const float* y, void* x_next, 
 bool prefill_supported(const moe_desc& d, int T);
 int launch_prefill_router(const Call& c, int32_t* ids_dst, float* wts_dst);
 int launch_prefill_experts(const Call& c);
+
+// Stack decode: layer l reads x + l x_stride (or, when x_chain is set and
+// l > 0, x_chain + (l - 1) chain_stride), router_w + l router_stride,
+// slot_table + l slot_stride (bytes), shared + l shared_stride, and writes
+// out + l out_stride and, when x_chain is set, x_chain + l chain_stride =
+// its input + its output.
+struct StackCall {
+  moe_desc d;
+  int32_t n_layers;
+  const void* x;
+  int64_t x_stride;
+  const void* router_w;
+  int64_t router_stride;
+  const int64_t* slot_table;
+  int64_t slot_stride;
+  const uint8_t* pool;
+  const uint8_t* shared;
+  int64_t shared_stride;
+  void* out;
+  int64_t out_stride;
+  void* x_chain;
+  int64_t chain_stride;
+  int32_t* ids_out;       // optional [n_layers][k]
+  float* wts_out;
+  uint8_t* ws;
+  WsLayout L;
+  hipStream_t stream;
+};
+
+struct StackPlan {
+  int nb, rb, rpb, spb, gpb;
+  size_t lds;
+};
+
+int stack_plan(const moe_desc& d, StackPlan* plan);
+int launch_decode_stack(const StackCall& c, const StackPlan& plan);
 
 // Two-launch decode (T <= kFusedMaxT).
 bool fused_supported(const moe_desc& d, int T);

@@ -36,7 +36,7 @@ CASES = [
                          ids=[f"{c[0]}-T{c[1]}{'-staged' if c[4] else ''}" for c in CASES])
 def test_offsets_beyond_4gib_bitwise(preset, T, routing, out, staged, tokens):
     margin = 2.0 if T >= 16 else 1.0
-    data = make_layer(synth.PRESETS[preset], 41, T, T, routing=routing, n_cand=max(96, 4 * T),
+    data = make_layer(synth.PRESETS[preset], 41, T, T, routing=routing, n_cand=max(96, 16 * T),
                       margin_scale=margin, oracle_tokens=tokens)
     dl = upload(data, out)
     y0, i0, w0 = run(dl, T, staged=staged)
