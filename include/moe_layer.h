@@ -182,6 +182,22 @@ int moe_layer_forward_staged(const moe_desc* d, int32_t T, const void* x, const 
                              float* topk_w, void* stream);
 
 /*
+ * The same layer on scalar kernels: one GPU thread per output value (a
+ * router logit, a token's routing and gate, one element of h, one element of
+ * a down row, one output element), with no cross-lane operations.  The pages
+ * check their fast GPU kernels against scalar ones that give identical output
+ * (Swiftlet README translation, "Correctness"; linlog.top article,
+ * "Correctness guarantees").  These kernels state the order in which the fast
+ * kernels associate every sum and follow it, so for any T their results
+ * equal moe_layer_forward_staged bit for bit (and, for T <= 8, the fast decode
+ * paths of moe_layer_forward).  Slow by design: a check, not a production
+ * path.  Same arguments, workspace and errors as moe_layer_forward.
+ */
+int moe_layer_forward_scalar(const moe_desc* d, int32_t T, const void* x, const void* router_w,
+                             const int64_t* slot_table, const void* pool_base, const void* shared_w, void* out,
+                             void* workspace, size_t ws_bytes, int32_t* topk_ids, float* topk_w, void* stream);
+
+/*
  * First half of moe_layer_forward: router logits, top-k and renormalised
  * weights into topk_ids [T, k] / topk_w [T, k] (both required).
  */

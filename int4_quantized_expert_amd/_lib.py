@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_forward.restype = ctypes.c_int
         L.moe_layer_forward_staged.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
         L.moe_layer_forward_staged.restype = ctypes.c_int
+        L.moe_layer_forward_scalar.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+        L.moe_layer_forward_scalar.restype = ctypes.c_int
         L.moe_router_topk.argtypes = [dp, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moe_router_topk.restype = ctypes.c_int
         L.moe_experts_forward.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -213,6 +215,14 @@ def layer_forward_staged(d: MoeDesc, T: int, x, router_w, slot_table, pool, shar
     _check(lib().moe_layer_forward_staged(ctypes.byref(d), T, _ptr(x), _ptr(router_w), _ptr(slot_table),
                                           _ptr(pool), _ptr(shared_w), _ptr(out), _ptr(ws), _nbytes(ws),
                                           _ptr(topk_ids), _ptr(topk_w), _stream(stream, ws)))
+
+
+def layer_forward_scalar(d: MoeDesc, T: int, x, router_w, slot_table, pool, shared_w, out, ws,
+                         topk_ids=None, topk_w=None, stream=None) -> None:
+    """The layer on the scalar kernels (one thread per output value): the fast kernels' order of sums."""
+    _check(lib().moe_layer_forward_scalar(ctypes.byref(d), T, _ptr(x), _ptr(router_w), _ptr(slot_table), _ptr(pool),
+                                          _ptr(shared_w), _ptr(out), _ptr(ws), _nbytes(ws), _ptr(topk_ids),
+                                          _ptr(topk_w), _stream(stream, ws)))
 
 
 def router_topk(d: MoeDesc, T: int, x, router_w, topk_ids, topk_w, ws, stream=None) -> None:

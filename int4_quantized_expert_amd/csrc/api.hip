@@ -419,6 +419,37 @@ int moe_layer_forward_staged(const moe_desc* d, int32_t T, const void* x, const 
                        topk_w, stream, false);
 }
 
+int moe_layer_forward_scalar(const moe_desc* d, int32_t T, const void* x, const void* router_w,
+                             const int64_t* slot_table, const void* pool_base, const void* shared_w, void* out,
+                             void* workspace, size_t ws_bytes, int32_t* topk_ids, float* topk_w, void* stream) {
+  MarkScope marks;
+  int rc;
+  if ((rc = check_desc(d)) || (rc = check_T(T))) return rc;
+  if (!x || !router_w || !slot_table || !pool_base || !shared_w || !out)
+    return fail(MOE_EINVAL, "NULL input or output pointer");
+  if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(out, 16) || !aligned(slot_table, 8) ||
+      !aligned(pool_base, 256) || !aligned(shared_w, 256))
+    return fail(MOE_EINVAL, "misaligned pointer (x/router_w/out 16, slot_table 8, pool_base/shared_w 256)");
+  moe::WsLayout L;
+  if ((rc = check_ws(*d, T, workspace, ws_bytes, &L))) return rc;
+  if (T == 0) return ok();
+  moe::Call c{};
+  c.d = *d;
+  c.T = T;
+  c.x = x;
+  c.router_w = router_w;
+  c.slot_table = slot_table;
+  c.pool = static_cast<const uint8_t*>(pool_base);
+  c.shared = static_cast<const uint8_t*>(shared_w);
+  c.out = out;
+  c.ws = static_cast<uint8_t*>(workspace);
+  c.L = L;
+  c.ids_out = topk_ids;
+  c.wts_out = topk_w;
+  c.stream = static_cast<hipStream_t>(stream);
+  return finish(moe::launch_scalar(c));
+}
+
 int moe_residual_add(int32_t T, int32_t H, int32_t act_dtype, const void* x, const float* y, void* x_next,
                      void* stream) {
   if (T < 0 || H < 1 || static_cast<int64_t>(T) * H >= (int64_t(1) << 31))

@@ -61,8 +61,14 @@ constexpr int64_t kBlob = 3 * kQ + 6 * kS;
 constexpr int kRowQ = kH / 2;              // code bytes of a gate/up row
 constexpr int kDRowQ = kI / 2;             // code bytes of a down row
 constexpr int kDRowSB = (kI / 64) * 2;     // scale (or bias) bytes of a down row
-constexpr int kLgRep = 16, kHRep = 8, kXRep = 16;
-constexpr int kMaxK = 16, kMaxRpb = 4, kMaxSpb = 4, kMaxRb = 16, kMaxG = 4, kMaxE = 512;
+constexpr int kLgRep = 8, kHRep = 4, kXRep = 8;   // copies of the exchanged words
+constexpr int kFlagRep = 16;                        // copies of the per-block flags
+constexpr int kMaxNb = 512;                         // blocks whose flags one wave polls
+constexpr int kMaxK = 10, kMaxRpb = 4, kMaxSpb = 4, kMaxRb = 16, kMaxG = 4, kMaxE = 512;
+constexpr int kMaxHn = (kMaxK + 1) * kI + 1;        // exchanged h words: k routed rows, shared row, gate
+constexpr int kRdWaves = 6;                         // waves that read exchanged words (0..5)
+constexpr int kRdThr = kRdWaves * kWave;
+constexpr int kFlLg = 0, kFlH = 1, kFlX = 2;        // flag kinds
 
 // Bytes of LDS per region, rounded so that 256-byte direct-load rounds that
 // run past a region's end land in its own padding.
@@ -88,6 +94,8 @@ constexpr int kMCnt = kNW;            // [kNW] per-wave candidate counts
 constexpr int kMIds = 2 * kNW;        // [kMaxK] chosen experts by rank
 constexpr int kMVals = kMIds + kMaxK; // [kMaxK] chosen logits, then weights
 constexpr int kMSig = kMVals + kMaxK; // sigmoid(g . x)
+constexpr int kMOk = kMSig + 1;       // result of the last flag wait
+constexpr int kMRd = kMOk + 1;        // [kRdWaves] results of the reading waves
 constexpr int kMOff = 64;             // [kMaxK] int64 blob offsets by rank (8-byte aligned)
 constexpr int kMWords = kMOff + 2 * kMaxK;
 
@@ -128,10 +136,6 @@ __device__ __forceinline__ void store_tag(uint64_t* p, uint32_t bits, uint32_t t
   __hip_atomic_store(p, (static_cast<uint64_t>(tag) << 32) | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ uint64_t load_tag(const uint64_t* p) {
-  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Maximum over the wave (every lane gets it).
@@ -165,9 +169,10 @@ struct StackArgs {
   int64_t xc_stride;
   int32_t* ids_out;          // optional [L][k]
   float* wts_out;            // optional [L][k]
-  uint64_t* lg;              // [kLgRep][E] tagged logits
-  uint64_t* hx;              // [kHRep][hn] tagged h rows (ranks 0..k-1, shared), then the gate
+  uint64_t* lg;              // [kLgRep][kMaxE] tagged logits
+  uint64_t* hx;              // [kHRep][kMaxHn] tagged h rows (ranks 0..k-1, shared), then the gate
   uint64_t* xx;              // [kXRep][kH / 2] tagged next-layer input (two bf16 per word)
+  uint32_t* flags;           // [3][kFlagRep][kMaxNb] per-block exchange flags
   uint32_t* ctrl;            // [0] error flags
   uint32_t* epochs;          // per-block call counters
   int L, E, k, nb, rpb, spb, rb, gpb, hn;
@@ -263,17 +268,89 @@ __device__ __forceinline__ void issue_down(const StackArgs& a, const SLds& S, ui
   }
 }
 
-// Bounded poll: re-reads (through `load`) the words a thread still misses
-// until the whole block has them.  Returns false on expiry.
-template <typename F>
-__device__ __forceinline__ bool poll_block(F&& pass, uint32_t spin_limit, bool dead) {
-  if (dead) return false;
+// Exchanges.  A producer block stores its words (value bits and the layer's
+// tag), then, once every wave of the block has issued them (the caller's
+// barrier), raises its flag: the tag in every copy of the block's flag word.
+// A reader polls the flags of all blocks with one wave (1 KB per try), then
+// reads the words once; a flag may be seen before the words it follows, so a
+// word with an older tag is read again.  Polling the flags instead of the
+// words keeps the traffic of waiting blocks small while the other blocks
+// still stream their operands.  Every wait is bounded.
+__device__ __forceinline__ void raise_flag(const StackArgs& a, int kind, uint32_t tag, int wave, int lane) {
+  if (wave == 0 && lane < kFlagRep)
+    __hip_atomic_store(a.flags + (kind * kFlagRep + lane) * kMaxNb + blockIdx.x, tag, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// True once every block's flag of `kind` carries `tag`; false on expiry (or
+// when an earlier wait expired).
+__device__ __forceinline__ bool wait_flags(const StackArgs& a, int kind, uint32_t tag, bool dead, lds_w32* misc,
+                                           int wave, int lane) {
+  if (wave == 0) {
+    bool ok = !dead;
+    if (ok) {
+      const uint32_t* r = a.flags + (kind * kFlagRep + blockIdx.x % kFlagRep) * kMaxNb;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(r), 0, kMaxNb * 4, 0x00020000);
+      for (uint32_t spins = 0;; ++spins) {
+        bool all = true;
+        for (int j = lane * 4; j < a.nb; j += kWave * 4) {   // scope of device (sc1)
+          const u32x4 f = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, j * 4, 0, 16));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) all = all && (j + q >= a.nb || f[q] == tag);
+        }
+        if (__ballot(!all) == 0) break;
+        if (spins >= a.spin_limit) { ok = false; break; }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    if (lane == 0) misc[kMOk] = ok ? 1u : 0u;
+  }
+  __syncthreads();
+  return misc[kMOk] != 0u;
+}
+
+// The n tagged words at `src` (thread t of the first nthr takes words
+// t + q nthr, q < PER), read until each carries `tag`; put(i, bits) stores
+// word i's value.  Run by the reading waves only, under a branch on the wave
+// index, with no barrier inside: the copy waves, whose direct loads are still
+// in flight, must never execute the wait that follows these loads.  False on
+// expiry.
+template <int PER, typename F>
+__device__ __forceinline__ bool read_tagged(const uint64_t* src, int n, int nthr, uint32_t tag, uint32_t limit,
+                                            F&& put) {
+  const int tid = threadIdx.x;
+  uint32_t need = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q)
+    if (tid + q * nthr < n) need |= 1u << q;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t*>(src), 0, n * 8, 0x00020000);
   for (uint32_t spins = 0;; ++spins) {
-    const int missing = pass();
-    if (!__syncthreads_or(missing)) return true;
-    if (spins >= spin_limit) return false;
+    uint64_t w[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q)   // scope of device (sc1): past this XCD's L2, where the writers' stores went
+      w[q] = (need >> q) & 1u
+                 ? __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rs, (tid + q * nthr) * 8, 0, 16))
+                 : 0ull;
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+      if (((need >> q) & 1u) && static_cast<uint32_t>(w[q] >> 32) == tag) {
+        put(tid + q * nthr, static_cast<uint32_t>(w[q]));
+        need &= ~(1u << q);
+      }
+    if (__ballot(need != 0u) == 0) return true;
+    if (spins >= limit) return false;
     __builtin_amdgcn_s_sleep(1);
   }
+}
+
+// After a barrier: true if every reading wave's read succeeded.
+__device__ __forceinline__ bool reads_ok(const lds_w32* misc) {
+  bool ok = true;
+#pragma unroll
+  for (int w = 0; w < kRdWaves; ++w) ok = ok && misc[kMRd + w] != 0u;
+  return ok;
 }
 
 template <int OUT>
@@ -321,7 +398,7 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
 #pragma unroll
         for (int c = 0; c < kSegCodes; ++c) acc = fmaf(v[c], r[c], acc);
         acc = group_sum(acc, kWave);
-        if (lane < kLgRep) store_tag(a.lg + static_cast<size_t>(lane) * E + e, __float_as_uint(acc), tag);
+        if (lane < kLgRep) store_tag(a.lg + static_cast<size_t>(lane) * kMaxE + e, __float_as_uint(acc), tag);
       } else {
         const int u = j - a.rpb;
         const int r = b * a.spb + u;
@@ -341,7 +418,7 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
         float g, uu;
         gu_sums_w<kWave>(accg, accu, kWave, g, uu);
         const float h = silu(g) * uu;
-        if (lane < kHRep) store_tag(a.hx + static_cast<size_t>(lane) * a.hn + k * kI + r, __float_as_uint(h), tag);
+        if (lane < kHRep) store_tag(a.hx + static_cast<size_t>(lane) * kMaxHn + k * kI + r, __float_as_uint(h), tag);
       }
     }
     if (b == 0 && wave == kNW - 1) {
@@ -358,24 +435,22 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
       }
       acc = group_sum(acc, kWave);
       const float sgm = sigmoid(acc);
-      if (lane < kHRep) store_tag(a.hx + static_cast<size_t>(lane) * a.hn + (k + 1) * kI, __float_as_uint(sgm), tag);
+      if (lane < kHRep) store_tag(a.hx + static_cast<size_t>(lane) * kMaxHn + (k + 1) * kI, __float_as_uint(sgm), tag);
     }
 
     // ------------------------------------------------------------------ K
+    __syncthreads();                 // every wave's logit stores are issued
+    raise_flag(a, kFlLg, tag, wave, lane);
     {
-      const uint64_t* src = a.lg + static_cast<size_t>(b % kLgRep) * E;
-      bool have = tid >= E;
-      const bool ok = poll_block([&]() {
-        if (!have) {
-          const uint64_t w = load_tag(src + tid);
-          if (static_cast<uint32_t>(w >> 32) == tag) {
-            lg[tid] = __uint_as_float(static_cast<uint32_t>(w));
-            have = true;
-          }
-        }
-        return have ? 0 : 1;
-      }, a.spin_limit, dead);
-      dead = dead || !ok;
+      bool ok = wait_flags(a, kFlLg, tag, dead, misc, wave, lane);
+      if (ok && wave < kRdWaves) {
+        const bool r = read_tagged<(kMaxE + kRdThr - 1) / kRdThr>(
+            a.lg + static_cast<size_t>(b % kLgRep) * kMaxE, E, kRdThr, tag, a.spin_limit,
+            [&](int i, uint32_t bits) { ((lds_f32*)(lg))[i] = __uint_as_float(bits); });
+        if (lane == 0) misc[kMRd + wave] = r ? 1u : 0u;
+      }
+      __syncthreads();
+      dead = dead || !(ok && reads_ok(misc));
     }
     // top-k over the block: each wave bounds its share of the keys from below
     // (its j-th largest, j * waves-with-keys >= k), so that every key at or
@@ -403,16 +478,38 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
       for (int w = 0; w < nwd; ++w) theta = min(theta, misc[kMTheta + w]);
       const bool cand = tid < E && key >= theta;
       const uint64_t cm = __ballot(cand);
-      lds_w64* cl = (lds_w64*)(lds + S.cand);
-      const uint64_t mine = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~tid);
-      if (cand) cl[wave * kWave + __popcll(cm & lane_mask_lt(lane))] = mine;
       if (lane == 0) misc[kMCnt + wave] = static_cast<uint32_t>(__popcll(cm));
       __syncthreads();
+      // one contiguous list of the candidates (in id order), padded with
+      // zeros to a multiple of 8 (a zero word never outranks a candidate)
+      int base = 0, total = 0;
+      for (int w = 0; w < kNW; ++w) {
+        const int c = static_cast<int>(misc[kMCnt + w]);
+        base += w < wave ? c : 0;
+        total += c;
+      }
+      lds_w64* cl = (lds_w64*)(lds + S.cand);
+      const uint64_t mine = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~tid);
+      if (cand) cl[base + __popcll(cm & lane_mask_lt(lane))] = mine;
+      const int total8 = (total + 7) & ~7;
+      if (tid >= total && tid < total8) cl[tid] = 0ull;
+      __syncthreads();
       if (cand) {
+        // rank = number of candidates that order before this one; eight per
+        // round, every read of a round requested before any compare
         int rank = 0;
-        for (int w = 0; w < nwd; ++w) {
-          const int n = static_cast<int>(misc[kMCnt + w]);
-          for (int j = 0; j < n; ++j) rank += cl[w * kWave + j] > mine ? 1 : 0;
+        const lds_u32x4* c4 = (const lds_u32x4*)(cl);
+        for (int d0 = 0; d0 < total8; d0 += 8) {
+          u32x4 q[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) q[i] = c4[d0 / 2 + i];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint64_t w0 = (static_cast<uint64_t>(q[i][1]) << 32) | q[i][0];
+            const uint64_t w1 = (static_cast<uint64_t>(q[i][3]) << 32) | q[i][2];
+            rank += (w0 > mine) ? 1 : 0;
+            rank += (w1 > mine) ? 1 : 0;
+          }
         }
         if (rank < k) {
           misc[kMIds + rank] = static_cast<uint32_t>(tid);
@@ -490,53 +587,40 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
           gu_sums_w<kWave>(accg, accu, kWave, g, uu);
           const float h = vv[j] ? silu(g) * uu : 0.f;
           if (lane < kHRep)
-            store_tag(a.hx + static_cast<size_t>(lane) * a.hn + ii[j] * kI + rr[j], __float_as_uint(h), tag);
+            store_tag(a.hx + static_cast<size_t>(lane) * kMaxHn + ii[j] * kI + rr[j], __float_as_uint(h), tag);
         }
       } else if (wave == kWaveDown) {
         issue_down(a, S, lds, lane);
+      } else if (wave == kWaveStatic && l + 1 < a.L) {
+        // the next layer's static operands: into the other copy, free since
+        // the layer before this one ended
+        issue_static(a, S, lds, p ^ 1, l + 1, lane);
       }
     }
 
     // ------------------------------------------------------------------ H
-    // the next layer's static operands travel during the wait
-    if (wave == kWaveStatic && l + 1 < a.L) issue_static(a, S, lds, p ^ 1, l + 1, lane);
+    __syncthreads();                 // every wave's h stores are issued
+    raise_flag(a, kFlH, tag, wave, lane);
     if (wave == kWaveDown) wait_vm0();
     {
       float* hs = reinterpret_cast<float*>(lds + S.hs);
-      const uint64_t* src = a.hx + static_cast<size_t>(b % kHRep) * a.hn;
-      const int nh = a.hn;
-      constexpr int kPoll = kGW * kWave;
-      constexpr int kPer = 16;                     // words per polling thread (hn <= 16 * 384)
-      uint32_t need = 0;
-      if (wave < kGW)
-        for (int q = 0; q < kPer; ++q)
-          if (tid + q * kPoll < nh) need |= 1u << q;
-      const __amdgpu_buffer_rsrc_t hr =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t*>(src), 0, nh * 8, 0x00020000);
-      const bool ok = poll_block([&]() {
-        if (need) {
-          uint64_t w[kPer];
-#pragma unroll
-          for (int q = 0; q < kPer; ++q)   // scope of device (sc1): past this XCD's L2, where the writers' stores went
-            w[q] = (need >> q) & 1u ? __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(hr, tid * 8, q * kPoll * 8, 16)) : 0ull;
-#pragma unroll
-          for (int q = 0; q < kPer; ++q) {
-            if (((need >> q) & 1u) && static_cast<uint32_t>(w[q] >> 32) == tag) {
-              const int i = tid + q * kPoll;
-              const float v = __uint_as_float(static_cast<uint32_t>(w[q]));
+      const int nh = (k + 1) * kI + 1;
+      // waves 0..5 read (wave 6 still has the static copies in flight)
+      bool ok = wait_flags(a, kFlH, tag, dead, misc, wave, lane);
+      if (ok && wave < kRdWaves) {
+        const bool r = read_tagged<(kMaxHn + kRdThr - 1) / kRdThr>(
+            a.hx + static_cast<size_t>(b % kHRep) * kMaxHn, nh, kRdThr, tag, a.spin_limit, [&](int i, uint32_t bits) {
               if (i < (k + 1) * kI) {
                 const int row = i / kI, c = i % kI;
-                ((lds_f32*)(hs))[(row * kSegI + c / kSegCodes) * kPad + c % kSegCodes] = v;
+                ((lds_f32*)(hs))[(row * kSegI + c / kSegCodes) * kPad + c % kSegCodes] = __uint_as_float(bits);
               } else {
-                misc[kMSig] = __float_as_uint(v);
+                misc[kMSig] = bits;
               }
-              need &= ~(1u << q);
-            }
-          }
-        }
-        return need ? 1 : 0;
-      }, a.spin_limit, dead);
-      dead = dead || !ok;
+            });
+        if (lane == 0) misc[kMRd + wave] = r ? 1u : 0u;
+      }
+      __syncthreads();
+      dead = dead || !(ok && reads_ok(misc));
       // segment sums of the staged rows, in the order seg_sum uses
       float* hsum = reinterpret_cast<float*>(lds + S.hsum);
       for (int j = tid; j < (k + 1) * kSegI; j += kThr) {
@@ -614,25 +698,18 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
         const uint32_t bits = static_cast<uint32_t>(xn[2 * w]) | (static_cast<uint32_t>(xn[2 * w + 1]) << 16);
         store_tag(a.xx + static_cast<size_t>(rep) * (kH / 2) + row_lo / 2 + w, bits, ntag);
       }
-      uint8_t* Pn = lds + (p ^ 1) * S.p_bytes;
-      const uint64_t* src = a.xx + static_cast<size_t>(b % kXRep) * (kH / 2);
-      uint32_t need = 0;
-      for (int q = 0; q < (kH / 2) / kThr; ++q) need |= 1u << q;
-      const bool ok = poll_block([&]() {
-        if (need) {
-          uint64_t w[(kH / 2) / kThr];
-#pragma unroll
-          for (int q = 0; q < (kH / 2) / kThr; ++q) w[q] = (need >> q) & 1u ? load_tag(src + tid + q * kThr) : 0ull;
-#pragma unroll
-          for (int q = 0; q < (kH / 2) / kThr; ++q)
-            if (((need >> q) & 1u) && static_cast<uint32_t>(w[q] >> 32) == ntag) {
-              ((lds_w32*)(Pn + S.p_x))[tid + q * kThr] = static_cast<uint32_t>(w[q]);
-              need &= ~(1u << q);
-            }
-        }
-        return need ? 1 : 0;
-      }, a.spin_limit, dead);
-      dead = dead || !ok;
+      __syncthreads();               // every x store is issued
+      raise_flag(a, kFlX, ntag, wave, lane);
+      lds_w32* xd = (lds_w32*)(lds + (p ^ 1) * S.p_bytes + S.p_x);
+      bool ok = wait_flags(a, kFlX, ntag, dead, misc, wave, lane);
+      if (ok && wave < kRdWaves) {
+        const bool r = read_tagged<(kH / 2 + kRdThr - 1) / kRdThr>(
+            a.xx + static_cast<size_t>(b % kXRep) * (kH / 2), kH / 2, kRdThr, ntag, a.spin_limit,
+            [&](int i, uint32_t bits) { xd[i] = bits; });
+        if (lane == 0) misc[kMRd + wave] = r ? 1u : 0u;
+      }
+      __syncthreads();
+      dead = dead || !(ok && reads_ok(misc));
     }
     if (wave == kWaveStatic) wait_vm0();
     __syncthreads();
@@ -654,9 +731,10 @@ bool stack_supported(const moe_desc& d) {
          d.sb_dtype == kBF16 && d.n_experts <= kMaxE && d.top_k <= kMaxK;
 }
 
-size_t stack_ws_lg(const moe_desc& d) { return static_cast<size_t>(kLgRep) * d.n_experts * 8; }
-size_t stack_ws_h(const moe_desc& d) { return static_cast<size_t>(kHRep) * ((d.top_k + 1) * kI + 1) * 8; }
+size_t stack_ws_lg() { return static_cast<size_t>(kLgRep) * kMaxE * 8; }
+size_t stack_ws_h() { return static_cast<size_t>(kHRep) * kMaxHn * 8; }
 size_t stack_ws_x() { return static_cast<size_t>(kXRep) * (kH / 2) * 8; }
+size_t stack_ws_flags() { return static_cast<size_t>(3) * kFlagRep * kMaxNb * 4; }
 
 // Grid and LDS of the stack kernel on the current device: one block per CU,
 // each CU's share of rows an exact multiple of a down pass.
@@ -667,13 +745,12 @@ int stack_plan(const moe_desc& d, StackPlan* plan) {
   if (hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
     return MOE_ENODEV;
   const int nb = cus;
-  if (nb < 1 || nb > kFusedMaxBlocks || kH % nb) return MOE_EINVAL;
+  if (nb < 1 || nb > kMaxNb || kH % nb) return MOE_EINVAL;
   const int rb = kH / nb;
   const int rpb = (d.n_experts + nb - 1) / nb, spb = (kI + nb - 1) / nb;
   const int gpb = (d.top_k * kI + nb - 1) / nb;
   if (rb % kRpp || rb > kMaxRb || rpb > kMaxRpb || spb > kMaxSpb || gpb > kGW * kMaxG || rpb + spb > kNW - 1)
     return MOE_EINVAL;
-  if ((d.top_k + 1) * kI + 1 > 16 * kGW * kWave) return MOE_EINVAL;
   const SLds S = stack_lds(d.n_experts, d.top_k, rpb, spb, rb);
   if (S.total > static_cast<uint32_t>(lds_max)) return MOE_EINVAL;
   const void* fn = d.out_dtype == kF32 ? reinterpret_cast<const void*>(k_decode_stack<kF32>)
@@ -718,6 +795,7 @@ int launch_decode_stack(const StackCall& c, const StackPlan& plan) {
   a.lg = reinterpret_cast<uint64_t*>(c.ws + c.L.s_lg);
   a.hx = reinterpret_cast<uint64_t*>(c.ws + c.L.s_h);
   a.xx = reinterpret_cast<uint64_t*>(c.ws + c.L.s_x);
+  a.flags = reinterpret_cast<uint32_t*>(c.ws + c.L.s_flags);
   a.ctrl = reinterpret_cast<uint32_t*>(c.ws + c.L.ctrl);
   a.epochs = reinterpret_cast<uint32_t*>(c.ws + c.L.f_epoch);
   a.L = c.n_layers;

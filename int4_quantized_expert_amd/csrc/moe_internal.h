@@ -12,6 +12,7 @@
 namespace moe {
 
 constexpr int kFusedMaxBlocks = 2048;
+constexpr int kMaxExperts = 1024;   // largest n_experts a descriptor may have
 
 // Byte layout of the caller's workspace for calls with up to T_max tokens.
 // Every region starts on a 256-byte boundary.  The control words and the
@@ -39,6 +40,7 @@ struct WsLayout {
   size_t s_lg;       // stack decode: tagged logits (replicated)
   size_t s_h;        // stack decode: tagged h rows and gate (replicated)
   size_t s_x;        // stack decode: tagged next-layer input (replicated)
+  size_t s_flags;    // stack decode: per-block exchange flags (three kinds, replicated)
   size_t p_x16;      // prefill: [T, H] float16 activations in MFMA k order
   size_t p_meta;     // prefill: int32 [0] number of expert tiles
   size_t p_tstart;   // prefill: [min(T k, E) + 2] int32 first tile of each distinct expert, then of the shared one
@@ -59,9 +61,10 @@ inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 // Stack decode (T = 1, one persistent launch for one or more layers): the
 // shapes it is built for and the sizes of its exchange buffers.
 bool stack_supported(const moe_desc& d);
-size_t stack_ws_lg(const moe_desc& d);
-size_t stack_ws_h(const moe_desc& d);
+size_t stack_ws_lg();
+size_t stack_ws_h();
 size_t stack_ws_x();
+size_t stack_ws_flags();
 
 inline WsLayout ws_layout(const moe_desc& d, int32_t T) {
   WsLayout L{};
@@ -71,15 +74,19 @@ inline WsLayout ws_layout(const moe_desc& d, int32_t T) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes > 0 ? bytes : 1); return at; };
   L.ctrl = take(256 + static_cast<size_t>(kFusedMaxBlocks) * 4);
+  // the stack decode's exchange words and flags: fixed offsets and sizes for
+  // every descriptor and T, so that only its own tagged words (with older
+  // tags) are ever found there
+  L.s_lg = take(stack_ws_lg());
+  L.s_h = take(stack_ws_h());
+  L.s_x = take(stack_ws_x());
+  L.s_flags = take(stack_ws_flags());
   L.f_epoch = L.ctrl + 256;
   const size_t Tf = kFusedMaxT;
-  L.f_lg = take(static_cast<size_t>(kFusedReplicas) * Tf * d.n_experts * 8);
+  // sized for the largest E: words of other regions (plain data of calls with
+  // another descriptor) never land where tagged words are looked for
+  L.f_lg = take(static_cast<size_t>(kFusedReplicas) * Tf * kMaxExperts * 8);
   L.f_gflag = take(static_cast<size_t>(kFusedReplicas) * kFusedMaxBlocks * 4);
-  // the stack decode's exchange words; their offsets do not depend on T either
-  const bool st = stack_supported(d);
-  L.s_lg = take(st ? stack_ws_lg(d) : 0);
-  L.s_h = take(st ? stack_ws_h(d) : 0);
-  L.s_x = take(st ? stack_ws_x() : 0);
   L.logits = take(static_cast<size_t>(T) * d.n_experts * 4);
   L.ids = take(Tk * 4);
   L.wts = take(Tk * 4);
@@ -151,6 +158,8 @@ int launch_topk(const Call& c, const float* logits, int32_t* ids, float* wts, in
 int launch_combine(const Call& c, const float* partial, const float* gate);      // fp32 partial rows
 int launch_combine(const Call& c, const _Float16* partial, const float* gate);   // float16 partial rows
 int launch_ws_init(uint8_t* ws, size_t bytes, hipStream_t stream);
+// Scalar path: one thread per output value, the fast kernels' order of sums.
+int launch_scalar(const Call& c);
 int launch_residual(int act_dtype, const void* x, const float* y, void* x_next, int64_t n, hipStream_t stream);
 
 // Prefill path (many tokens): MFMA router and grouped expert GEMMs.

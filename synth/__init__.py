@@ -220,10 +220,13 @@ def make_shared(geo: Geometry, seed: int, layer: int) -> np.ndarray:
 
 # --------------------------------------------------------- dense activations
 
-def tokens(geo: Geometry, seed: int, layer: int, T: int, stream_id: int = 0) -> np.ndarray:
-    """x [T, H] ~ N(0, 1), raw activation storage."""
+def tokens(geo: Geometry, seed: int, layer: int, T: int, stream_id: int = 0, std: float = 1.0) -> np.ndarray:
+    """x [T, H] ~ N(0, std^2), raw activation storage."""
     rng = np.random.Generator(np.random.PCG64([seed, layer, 0x70C5, stream_id]))
-    return to_act(rng.standard_normal((T, geo.hidden), dtype=np.float32), geo.act)
+    x = rng.standard_normal((T, geo.hidden), dtype=np.float32)
+    if std != 1.0:
+        x = (x * np.float32(std)).astype(np.float32)
+    return to_act(x, geo.act)
 
 
 def router_normal(geo: Geometry, seed: int, layer: int, std: float = 0.05) -> np.ndarray:
