@@ -299,6 +299,30 @@ int moe_stack_forward(const moe_desc* d, int32_t n_layers, int32_t T, const void
                       int64_t out_stride, void* x_chain, int64_t chain_stride, int32_t* topk_ids, float* topk_w,
                       void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * moe_layer_forward without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The workspace is a fixed array of
+ * 16 MiB inside the library, one per GPU (each GPU the library runs on
+ * holds it until the process ends); it is cleared by a fill kernel on
+ * `stream` at the first call on each device, and every call leaves it ready
+ * for the next.  Calls that would need more than 16 MiB of workspace
+ * (moe_workspace_bytes(d, T) > 16 MiB, e.g. the 80B layer shape beyond
+ * about T = 64) return MOE_ENOMEM.  The call makes no device allocation
+ * (no hipMalloc / hipFree), and returns after enqueueing like
+ * moe_layer_forward, with the same results bit for bit.
+ *   status  optional (NULL or 4-byte aligned device pointer): after the
+ *           layer, receives this GPU's device error flags (bit 0: a pair
+ *           skipped for a bad slot offset or id, MOE_ERANGE; bit 1: a
+ *           bounded wait expired, MOE_ETIMEOUT), which are then cleared.
+ *           With NULL they accumulate unreported.
+ * All calls on one GPU share its array: calls that may overlap on one GPU
+ * (several streams, several host threads) race and must not be made.
+ */
+int moe_layer_forward_noalloc(const moe_desc* d, int32_t T, const void* x, const void* router_w,
+                              const int64_t* slot_table, const void* pool_base, const void* shared_w, void* out,
+                              int32_t* topk_ids, float* topk_w, uint32_t* status, void* stream);
+
 /* Text of the last error on this thread ("" if none). */
 const char* moe_last_error(void);
 

@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     experts_forward,
     layer_forward,
     layer_forward_chain,
+    layer_forward_noalloc,
     layer_forward_scalar,
     layer_forward_staged,
     last_error,

@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.moe_stack_forward.argtypes = [dp, i32, i32, vp, i64, vp, i64, vp, i64, vp, vp, i64, vp, i64, vp, i64,
                                         vp, vp, vp, sz, vp]
         L.moe_stack_forward.restype = ctypes.c_int
+        L.moe_layer_forward_noalloc.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_layer_forward_noalloc.restype = ctypes.c_int
         L.moe_residual_add.argtypes = [i32, i32, i32, vp, vp, vp, vp]
         L.moe_residual_add.restype = ctypes.c_int
         L.moe_status_check.argtypes = [vp, vp]
@@ -199,6 +201,15 @@ def layer_forward(d: MoeDesc, T: int, x, router_w, slot_table, pool, shared_w, o
     _check(lib().moe_layer_forward(ctypes.byref(d), T, _ptr(x), _ptr(router_w), _ptr(slot_table), _ptr(pool),
                                    _ptr(shared_w), _ptr(out), _ptr(ws), _nbytes(ws), _ptr(topk_ids),
                                    _ptr(topk_w), _stream(stream, ws)))
+
+
+def layer_forward_noalloc(d: MoeDesc, T: int, x, router_w, slot_table, pool, shared_w, out, topk_ids=None,
+                          topk_w=None, status=None, stream=None) -> None:
+    """layer_forward on the library's own fixed scratch (moe_layer_forward_noalloc): no workspace argument,
+    no device allocation.  status: optional 4-byte device tensor that receives the device error flags."""
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(d), T, _ptr(x), _ptr(router_w), _ptr(slot_table), _ptr(pool),
+                                           _ptr(shared_w), _ptr(out), _ptr(topk_ids), _ptr(topk_w), _ptr(status),
+                                           _stream(stream, out)))
 
 
 def layer_forward_chain(d: MoeDesc, T: int, x, router_w, slot_table, pool, shared_w, out, x_next, ws,

@@ -152,6 +152,48 @@ int finish(int rc) {
   return ok();
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of the no-allocation entry point: one file-scope device array per
+// GPU (each GPU the library runs on holds its own copy until the process
+// ends), used as the workspace.  Host code never passes `scratch` itself to a
+// kernel (in host code the name is a host-side stand-in, not a device
+// address): set-up looks up each device's address once with
+// hipGetSymbolAddress, with that device current, and keeps it.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  void* ptr = nullptr;   // device address of this GPU's copy
+  bool ready = false;    // cleared once (the first call on the device)
+};
+ScratchSlot g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// This device's scratch address, cleared on `stream` at its first use; the
+// clear is a fill kernel (no memset), so it may be captured in a graph.
+int scratch_for_current_device(hipStream_t stream, uint8_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_ENODEV, "no current device");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ENODEV, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchSlot& sl = g_scratch[dev];
+  if (!sl.ptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_EHIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    sl.ptr = p;
+  }
+  if (!sl.ready) {
+    if (moe::launch_ws_init(static_cast<uint8_t*>(sl.ptr), kScratchBytes, stream) != MOE_OK)
+      return fail(MOE_EHIP, "clearing the scratch failed: %s", hipGetErrorString(hipGetLastError()));
+    sl.ready = true;
+  }
+  *out = static_cast<uint8_t*>(sl.ptr);
+  return MOE_OK;
+}
+
 }  // namespace
 
 namespace moe {
@@ -417,6 +459,34 @@ int moe_layer_forward_staged(const moe_desc* d, int32_t T, const void* x, const 
                              void* workspace, size_t ws_bytes, int32_t* topk_ids, float* topk_w, void* stream) {
   return layer_forward(d, T, x, router_w, slot_table, pool_base, shared_w, out, workspace, ws_bytes, topk_ids,
                        topk_w, stream, false);
+}
+
+int moe_layer_forward_noalloc(const moe_desc* d, int32_t T, const void* x, const void* router_w,
+                              const int64_t* slot_table, const void* pool_base, const void* shared_w, void* out,
+                              int32_t* topk_ids, float* topk_w, uint32_t* status, void* stream) {
+  int rc;
+  if ((rc = check_desc(d)) || (rc = check_T(T))) return rc;
+  const size_t need = moe::ws_layout(*d, T).total;
+  if (need > kScratchBytes)
+    return fail(MOE_ENOMEM, "T=%d needs %zu bytes of workspace; the no-allocation entry point has %zu", T, need,
+                kScratchBytes);
+  if (status && !aligned(status, 4)) return fail(MOE_EINVAL, "status must be 4-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* ws = nullptr;
+  if (T > 0 && (rc = scratch_for_current_device(st, &ws))) return rc;
+  if (T == 0) {
+    // the argument checks of moe_layer_forward, nothing enqueued: any
+    // 256-aligned workspace address passes them, and none is touched
+    static __align__(256) uint8_t no_ws[256];
+    return layer_forward(d, T, x, router_w, slot_table, pool_base, shared_w, out, no_ws, need, topk_ids, topk_w,
+                         stream, true);
+  }
+  if ((rc = layer_forward(d, T, x, router_w, slot_table, pool_base, shared_w, out, ws, kScratchBytes, topk_ids,
+                          topk_w, stream, true)))
+    return rc;
+  if (status) return finish(moe::launch_take_flags(reinterpret_cast<uint32_t*>(ws + moe::ws_layout(*d, T).ctrl),
+                                                   status, st));
+  return MOE_OK;
 }
 
 int moe_layer_forward_scalar(const moe_desc* d, int32_t T, const void* x, const void* router_w,

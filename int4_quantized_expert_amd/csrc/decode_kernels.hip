@@ -576,6 +576,14 @@ __global__ void k_fill_u32(uint32_t* p, size_t n, uint32_t v) {
   if (i < n) p[i] = v;
 }
 
+// The device error flags into *status, then cleared (one thread).
+__global__ void k_take_flags(uint32_t* flags, uint32_t* status) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    *status = *flags;
+    *flags = 0u;
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -609,6 +617,11 @@ int launch_residual(int act_dtype, const void* x, const float* y, void* x_next, 
     hipLaunchKernelGGL(k_residual<kBF16>, dim3(blocks), dim3(256), 0, stream, x, y, x_next, n);
   else
     hipLaunchKernelGGL(k_residual<kF32>, dim3(blocks), dim3(256), 0, stream, x, y, x_next, n);
+  return last_launch_error();
+}
+
+int launch_take_flags(uint32_t* flags, uint32_t* status, hipStream_t stream) {
+  hipLaunchKernelGGL(k_take_flags, dim3(1), dim3(64), 0, stream, flags, status);
   return last_launch_error();
 }
 

@@ -160,6 +160,7 @@ int launch_combine(const Call& c, const _Float16* partial, const float* gate);  
 int launch_ws_init(uint8_t* ws, size_t bytes, hipStream_t stream);
 // Scalar path: one thread per output value, the fast kernels' order of sums.
 int launch_scalar(const Call& c);
+int launch_take_flags(uint32_t* flags, uint32_t* status, hipStream_t stream);
 int launch_residual(int act_dtype, const void* x, const float* y, void* x_next, int64_t n, hipStream_t stream);
 
 // Prefill path (many tokens): MFMA router and grouped expert GEMMs.
