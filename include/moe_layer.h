@@ -377,7 +377,10 @@ moe_cache* moe_cache_create(int32_t n_slots, int64_t stride, void* pool_base, co
 /* ids_host: n expert ids (duplicates allowed).  Returns MOE_OK, MOE_EINVAL
  * (bad argument or id outside [0, n_experts)), MOE_ENOSPC (more distinct
  * experts than slots, or too few slots free of unreleased acquires) or
- * MOE_EHIP; after MOE_EHIP the cache must be destroyed. */
+ * MOE_EHIP (a copy could not be issued).  After MOE_EHIP (or MOE_EIO from a
+ * store read) no expert this call missed is left resident, the hits it held
+ * are released, and copies issued before the failure still order later
+ * ones; the cache stays usable if the device does. */
 int moe_cache_acquire(moe_cache* cache, int32_t layer, const int32_t* ids_host, int32_t n,
                       int64_t* slot_table_host, void* copy_stream, void* ready);
 
@@ -386,6 +389,25 @@ int moe_cache_acquire(moe_cache* cache, int32_t layer, const int32_t* ids_host, 
 int moe_cache_release(moe_cache* cache, int32_t layer, void* compute_done);
 
 void moe_cache_stats(const moe_cache* cache, int64_t* hits, int64_t* misses, int64_t* evictions);
+
+/* Policy flags (moe_cache_set_policy).  MOE_CACHE_KEEP_COUNTS: a blob's use
+ * count survives its eviction, so a frequently used expert that a burst of
+ * others pushed out comes back with its count and is not the next victim
+ * (with the flag clear, counts restart at eviction).  Either way the policy
+ * changes only which blobs stay resident, never the outputs. */
+#define MOE_CACHE_KEEP_COUNTS 1
+
+/* Sets the policy flags of a cache (0 or MOE_CACHE_KEEP_COUNTS) for its later
+ * acquires.  MOE_EINVAL on a NULL cache or unknown flags. */
+int moe_cache_set_policy(moe_cache* cache, int32_t flags);
+
+/* Failure injection, for tests of the error path: the copy that is the
+ * nth_copy-th (0 = the next) to be issued from now on fails as a failed
+ * hipMemcpyAsync would (MOE_EHIP from moe_cache_acquire); -1 disarms.  In
+ * planning mode the copies that would be issued are counted.  After a failed
+ * acquire no expert that call missed is left resident, the hits it held are
+ * released, and the cache stays usable. */
+int moe_cache_inject_fault(moe_cache* cache, int32_t nth_copy);
 
 /* Slot index holding (layer, id), or -1. */
 int moe_cache_slot_of(const moe_cache* cache, int32_t layer, int32_t id);
@@ -449,8 +471,8 @@ void moe_store_close(moe_store* store);
  * of it has finished: acquire then waits on the host (hipEventSynchronize),
  * which may include compute that the copy stream was told to wait for.
  * Keep the staging memory until the copy stream has finished the last
- * acquire's copies.  After MOE_EIO from acquire the cache must be destroyed,
- * as after MOE_EHIP.  NULL on bad arguments. */
+ * acquire's copies.  A failed read (MOE_EIO from acquire) is rolled back like
+ * a failed copy.  NULL on bad arguments. */
 moe_cache* moe_cache_create_from_store(int32_t n_slots, void* pool_base, moe_store* store, void* staging_pinned,
                                        int32_t n_staging);
 

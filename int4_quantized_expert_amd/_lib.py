@@ -101,6 +101,10 @@ def lib() -> ctypes.CDLL:
         L.moe_cache_release.restype = ctypes.c_int
         L.moe_cache_stats.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
         L.moe_cache_stats.restype = None
+        L.moe_cache_set_policy.argtypes = [vp, i32]
+        L.moe_cache_set_policy.restype = ctypes.c_int
+        L.moe_cache_inject_fault.argtypes = [vp, i32]
+        L.moe_cache_inject_fault.restype = ctypes.c_int
         L.moe_cache_slot_of.argtypes = [vp, i32, i32]
         L.moe_cache_slot_of.restype = ctypes.c_int
         L.moe_cache_destroy.argtypes = [vp]
@@ -319,6 +323,7 @@ def _stream_handle(st) -> int | None:
 
 
 STORE_DIRECT = 1
+CACHE_KEEP_COUNTS = 1
 
 
 class ExpertStore:
@@ -418,6 +423,13 @@ class ExpertCache:
         h, m, e = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
         lib().moe_cache_stats(self._h, ctypes.byref(h), ctypes.byref(m), ctypes.byref(e))
         return h.value, m.value, e.value
+
+    def set_policy(self, keep_counts: bool) -> None:
+        self._check(lib().moe_cache_set_policy(self._h, CACHE_KEEP_COUNTS if keep_counts else 0))
+
+    def inject_fault(self, nth_copy: int) -> None:
+        """The nth copy issued from now on fails (MOE_EHIP from acquire); -1 disarms."""
+        self._check(lib().moe_cache_inject_fault(self._h, nth_copy))
 
     def slot_of(self, layer: int, expert: int) -> int:
         return lib().moe_cache_slot_of(self._h, layer, expert)

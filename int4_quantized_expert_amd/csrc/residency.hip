@@ -91,6 +91,9 @@ struct moe_cache {
   hipEvent_t last_copies = nullptr;    // recorded after the latest acquire's copies
   hipStream_t last_stream = nullptr;
   bool any_copies = false;
+  bool keep_counts = false;            // MOE_CACHE_KEEP_COUNTS: uses survive eviction
+  std::vector<int64_t> count;          // [layer * E + id] uses so far (kept across evictions)
+  int64_t fault_at = -1;               // copies until an injected failure (-1: none)
 
   Key key(int32_t s) const {
     const Slot& x = slots[s];
@@ -173,6 +176,17 @@ int store_read(moe_store* s, int32_t layer, int32_t id, void* dst, uint8_t* boun
 
 namespace {
 
+// True if the copy about to be issued is the one an injected fault targets
+// (moe_cache_inject_fault); the fault then disarms.
+bool take_fault(moe_cache* c) {
+  if (c->fault_at < 0) return false;
+  if (c->fault_at-- == 0) {
+    c->fault_at = -1;
+    return true;
+  }
+  return false;
+}
+
 struct MissJob {
   int32_t e, s;
   hipEvent_t reader;   // compute_done of the slot's last reader, or null
@@ -192,6 +206,7 @@ int copy_from_host(moe_cache* c, int32_t layer, const std::vector<MissJob>& jobs
   for (const MissJob& j : jobs) {
     if (wait_reader(cs, j, &waited) != MOE_OK) return MOE_EHIP;
     const uint8_t* src = c->host + (static_cast<size_t>(layer) * c->n_experts + j.e) * c->stride;
+    if (take_fault(c)) return cache_fail(MOE_EHIP, "injected copy failure");
     if (hipMemcpyAsync(c->pool + static_cast<size_t>(j.s) * c->stride, src, c->stride, hipMemcpyHostToDevice, cs) !=
         hipSuccess)
       return cache_fail(MOE_EHIP, "hipMemcpyAsync failed");
@@ -229,6 +244,7 @@ int copy_from_store(moe_cache* c, int32_t layer, const std::vector<MissJob>& job
     for (int i = 0; i < m; ++i) {
       const MissJob& j = jobs[b + i];
       if (wait_reader(cs, j, &waited) != MOE_OK) return MOE_EHIP;
+      if (take_fault(c)) return cache_fail(MOE_EHIP, "injected copy failure");
       if (hipMemcpyAsync(c->pool + static_cast<size_t>(j.s) * c->stride,
                          c->staging + static_cast<size_t>(stage[i]) * c->stride, c->stride, hipMemcpyHostToDevice,
                          cs) != hipSuccess)
@@ -386,6 +402,7 @@ moe_cache* moe_cache_create(int32_t n_slots, int64_t stride, void* pool_base, co
   c->planning = pool_base == nullptr;
   c->slots.resize(n_slots);
   c->where.assign(static_cast<size_t>(n_layers) * n_experts, -1);
+  c->count.assign(static_cast<size_t>(n_layers) * n_experts, 0);
   c->pending.resize(n_layers);
   for (int32_t s = 0; s < n_slots; ++s) c->evictable.insert(c->key(s));
   if (!c->planning && hipEventCreateWithFlags(&c->last_copies, hipEventDisableTiming) != hipSuccess) {
@@ -470,14 +487,19 @@ int moe_cache_acquire(moe_cache* c, int32_t layer, const int32_t* ids_host, int3
     return cache_fail(MOE_EHIP, "hipStreamWaitEvent failed");
   std::vector<int32_t> held;
   held.reserve(distinct);
+  const int64_t hits0 = c->hits, misses0 = c->misses;
+  std::vector<std::pair<int32_t, Slot>> hit_before;   // for the rollback of a failed call
   // hits first: they are held, so no miss of this call can evict them
   for (int32_t e = 0; e < E; ++e) {
     if (!need[e]) continue;
-    const int32_t s = c->where[static_cast<size_t>(layer) * E + e];
+    const size_t le = static_cast<size_t>(layer) * E + e;
+    const int32_t s = c->where[le];
     if (s < 0) continue;
+    hit_before.emplace_back(s, c->slots[s]);
     c->hold(s);
     Slot& x = c->slots[s];
-    x.uses += 1;
+    c->count[le] += 1;
+    x.uses = c->keep_counts ? c->count[le] : x.uses + 1;
     x.last = now;
     held.push_back(s);
     slot_table_host[e] = static_cast<int64_t>(s) * c->stride;
@@ -486,7 +508,8 @@ int moe_cache_acquire(moe_cache* c, int32_t layer, const int32_t* ids_host, int3
   // the policy first (slot of every miss), then the copies
   std::vector<MissJob> jobs;
   for (int32_t e = 0; e < E; ++e) {
-    if (!need[e] || c->where[static_cast<size_t>(layer) * E + e] >= 0) continue;
+    const size_t le = static_cast<size_t>(layer) * E + e;
+    if (!need[e] || c->where[le] >= 0) continue;
     const int32_t s = std::get<5>(*c->evictable.begin());
     c->hold(s);
     Slot& x = c->slots[s];
@@ -495,20 +518,58 @@ int moe_cache_acquire(moe_cache* c, int32_t layer, const int32_t* ids_host, int3
       ++c->evictions;
     }
     jobs.push_back({e, s, x.reader});
+    c->count[le] += 1;
     x.layer = layer;
     x.id = e;
-    x.uses = 1;
+    x.uses = c->keep_counts ? c->count[le] : 1;
     x.last = now;
     x.reader = nullptr;
-    c->where[static_cast<size_t>(layer) * E + e] = s;
+    c->where[le] = s;
     held.push_back(s);
     slot_table_host[e] = static_cast<int64_t>(s) * c->stride;
     ++c->misses;
   }
-  if (!c->planning && !jobs.empty()) {
-    const int rc = c->store ? copy_from_store(c, layer, jobs, cs) : copy_from_host(c, layer, jobs, cs);
-    if (rc != MOE_OK) return rc;
-    c->any_copies = true;
+  int rc = MOE_OK;
+  if (c->planning) {
+    for (size_t j = 0; j < jobs.size() && rc == MOE_OK; ++j)
+      if (take_fault(c)) rc = cache_fail(MOE_EHIP, "injected copy failure");
+  } else if (!jobs.empty()) {
+    rc = c->store ? copy_from_store(c, layer, jobs, cs) : copy_from_host(c, layer, jobs, cs);
+    // copies issued before a failure still run: later copies of this cache
+    // stay behind them (issue order), whatever stream they use
+    if (hipEventRecord(c->last_copies, cs) == hipSuccess) {
+      c->any_copies = true;
+      c->last_stream = cs;
+    } else if (rc == MOE_OK) {
+      rc = cache_fail(MOE_EHIP, "hipEventRecord failed");
+    }
+  }
+  if (rc != MOE_OK) {
+    // nothing of this call stays resident: the slots its misses took become
+    // empty (keeping the event of their last reader, whom a later copy into
+    // them must still wait for), and its holds are dropped
+    for (const MissJob& j : jobs) {
+      Slot& x = c->slots[j.s];
+      c->where[static_cast<size_t>(layer) * E + j.e] = -1;
+      c->count[static_cast<size_t>(layer) * E + j.e] -= 1;
+      x.layer = -1;
+      x.id = -1;
+      x.uses = 0;
+      x.last = -1;
+      x.reader = j.reader;
+    }
+    for (int32_t e = 0; e < E; ++e)
+      if (need[e] && c->where[static_cast<size_t>(layer) * E + e] >= 0)
+        c->count[static_cast<size_t>(layer) * E + e] -= 1;
+    for (const auto& hb : hit_before) {
+      // back to the uses and last use the hit found (its hold is dropped below)
+      c->slots[hb.first].uses = hb.second.uses;
+      c->slots[hb.first].last = hb.second.last;
+    }
+    for (int32_t s : held) c->unhold(s);
+    c->hits = hits0;
+    c->misses = misses0;
+    return rc;
   }
   c->pending[layer].push_back(std::move(held));
   if (!c->planning) {
@@ -517,6 +578,18 @@ int moe_cache_acquire(moe_cache* c, int32_t layer, const int32_t* ids_host, int3
       return cache_fail(MOE_EHIP, "hipEventRecord failed");
     c->last_stream = cs;
   }
+  return MOE_OK;
+}
+
+int moe_cache_set_policy(moe_cache* c, int32_t flags) {
+  if (!c || (flags & ~MOE_CACHE_KEEP_COUNTS)) return cache_fail(MOE_EINVAL, "bad cache or policy flags");
+  c->keep_counts = (flags & MOE_CACHE_KEEP_COUNTS) != 0;
+  return MOE_OK;
+}
+
+int moe_cache_inject_fault(moe_cache* c, int32_t nth_copy) {
+  if (!c || nth_copy < -1) return cache_fail(MOE_EINVAL, "bad cache or copy index");
+  c->fault_at = nth_copy;
   return MOE_OK;
 }
 
