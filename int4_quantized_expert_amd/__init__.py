@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     STORE_DIRECT,
     ExpertCache,
     ExpertStore,
+    GdnDesc,
     LaunchTimer,
     MoeDesc,
     MoeError,
@@ -19,6 +20,8 @@ from ._lib import (  # noqa: F401
     clear_launch_events,
     desc_for,
     experts_forward,
+    gdn_desc,
+    gdn_forward,
     layer_forward,
     layer_forward_chain,
     layer_forward_noalloc,

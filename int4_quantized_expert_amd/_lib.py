@@ -53,6 +53,20 @@ class MoeDesc(ctypes.Structure):
     ]
 
 
+class GdnDesc(ctypes.Structure):
+    """Descriptor of the gated-delta-rule recurrence (gdn_recurrence.h)."""
+    _fields_ = [
+        ("n_k_heads", ctypes.c_int32),
+        ("n_v_heads", ctypes.c_int32),
+        ("d_k", ctypes.c_int32),
+        ("d_v", ctypes.c_int32),
+        ("act_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("eps", ctypes.c_float),
+    ]
+
+
 _lib = None
 
 
@@ -128,6 +142,8 @@ def lib() -> ctypes.CDLL:
         L.moe_store_close.restype = None
         L.moe_set_launch_events.argtypes = [ctypes.POINTER(vp), i32, ctypes.POINTER(i32)]
         L.moe_set_launch_events.restype = ctypes.c_int
+        L.gdn_recurrence_forward.argtypes = [ctypes.POINTER(GdnDesc), i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.gdn_recurrence_forward.restype = ctypes.c_int
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -238,6 +254,19 @@ def layer_forward_scalar(d: MoeDesc, T: int, x, router_w, slot_table, pool, shar
     _check(lib().moe_layer_forward_scalar(ctypes.byref(d), T, _ptr(x), _ptr(router_w), _ptr(slot_table), _ptr(pool),
                                           _ptr(shared_w), _ptr(out), _ptr(ws), _nbytes(ws), _ptr(topk_ids),
                                           _ptr(topk_w), _stream(stream, ws)))
+
+
+def gdn_desc(n_k_heads, n_v_heads, d_k, d_v, act="bf16", out="f32", scale=None, eps=1e-6) -> GdnDesc:
+    """Descriptor for the gated delta rule; scale defaults to 1/sqrt(d_k)."""
+    dt = {"f32": MOE_F32, "bf16": MOE_BF16}
+    return GdnDesc(n_k_heads, n_v_heads, d_k, d_v, dt[act], dt[out],
+                   float(d_k ** -0.5 if scale is None else scale), float(eps))
+
+
+def gdn_forward(d: GdnDesc, B: int, T: int, q, k, v, alpha, beta, state, out, stream=None) -> None:
+    """Advance B sequences by T tokens of the gated delta rule; state is updated in place."""
+    _check(lib().gdn_recurrence_forward(ctypes.byref(d), B, T, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                        _ptr(state), _ptr(out), _stream(stream, state)))
 
 
 def router_topk(d: MoeDesc, T: int, x, router_w, topk_ids, topk_w, ws, stream=None) -> None:

@@ -197,6 +197,12 @@ int scratch_for_current_device(hipStream_t stream, uint8_t** out) {
 }  // namespace
 
 namespace moe {
+// The thread's error text for entry points defined in other files.
+int api_fail(int code, const char* msg) { return fail(code, "%s", msg); }
+int api_ok() { return ok(); }
+}  // namespace moe
+
+namespace moe {
 bool next_launch_events(hipEvent_t* start, hipEvent_t* stop) {
   if (g_marks.used + 2 > g_marks.cap) return false;
   *start = g_marks.ev[g_marks.used];

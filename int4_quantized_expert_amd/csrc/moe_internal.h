@@ -12,6 +12,11 @@
 namespace moe {
 
 constexpr int kFusedMaxBlocks = 2048;
+
+// Sets the calling thread's moe_last_error() text and returns `code`;
+// api_ok() clears it and returns MOE_OK.
+int api_fail(int code, const char* msg);
+int api_ok();
 constexpr int kMaxExperts = 1024;   // largest n_experts a descriptor may have
 
 // Byte layout of the caller's workspace for calls with up to T_max tokens.

@@ -1,5 +1,5 @@
 """C ABI checks that need no GPU: the library loads, exports every entry point
-declared in include/moe_layer.h, and rejects bad arguments on the host before
+declared under include/, and rejects bad arguments on the host before
 any device call."""
 
 import ctypes
@@ -20,13 +20,13 @@ def declared_functions():
         if f.endswith(".h"):
             text = open(os.path.join(inc, f)).read()
             text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-            names += re.findall(r"^[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", text, flags=re.M)
+            names += re.findall(r"^[A-Za-z_][\w\s\*]*?\b((?:moe|gdn)_\w+)\s*\(", text, flags=re.M)
     return sorted(set(names))
 
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert "moe_layer_forward" in names and len(names) >= 8
+    assert "moe_layer_forward" in names and "gdn_recurrence_forward" in names and len(names) >= 8
     lib = M.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
@@ -154,3 +154,52 @@ def test_residual_add_rejects_partial_overlap():
     assert L.moe_residual_add(T, H, M.MOE_BF16, x, y, y + 4, None) == -1     # into y
     assert L.moe_residual_add(T, H, M.MOE_F32, x, y, y - 4, None) == -1      # ends inside y
     assert L.moe_residual_add(0, H, M.MOE_BF16, x, y, x, None) == 0          # exact in place is fine
+
+
+def _gdn_args():
+    """Host buffers standing in for device pointers: every call below is
+    rejected (or is a no-op) before any device work, so they are never read."""
+    buf = ctypes.create_string_buffer(1 << 20)
+    base = ctypes.addressof(buf) // 256 * 256 + 256
+    B, T, nk, nv, dk, dv = 2, 3, 2, 4, 128, 64
+    q = base
+    k = q + B * T * nk * dk * 2
+    v = k + B * T * nk * dk * 2
+    al = v + B * T * nv * dv * 2
+    be = al + B * T * nv * 4 + 64
+    st = (be + B * T * nv * 4 + 255) // 256 * 256
+    out = st + B * nv * dv * dk * 4
+    return buf, dict(B=B, T=T, q=q, k=k, v=v, al=al, be=be, st=st, out=out)
+
+
+def _gdn_call(d, a, **over):
+    a = {**a, **over}
+    return M.lib().gdn_recurrence_forward(ctypes.byref(d), a["B"], a["T"], a["q"], a["k"], a["v"], a["al"], a["be"],
+                                          a["st"], a["out"], None)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("n_k_heads", 0), ("n_v_heads", 3), ("n_v_heads", 2048), ("d_k", 96), ("d_k", 256), ("d_v", 8), ("d_v", 72),
+    ("d_v", 272), ("act_dtype", 5), ("out_dtype", -1), ("scale", float("inf")), ("eps", -1.0), ("eps", float("nan")),
+])
+def test_gdn_bad_descriptor_rejected(field, value):
+    keep, a = _gdn_args()
+    d = M.gdn_desc(2, 4, 128, 64)
+    setattr(d, field, value)
+    assert _gdn_call(d, a) == -1
+    assert M.last_error()
+
+
+def test_gdn_pointer_and_size_checks():
+    keep, a = _gdn_args()
+    d = M.gdn_desc(2, 4, 128, 64, act="bf16", out="f32")
+    assert _gdn_call(d, a, q=None) == -1
+    assert _gdn_call(d, a, st=a["st"] + 8) == -1            # state not 16-byte aligned
+    assert _gdn_call(d, a, al=a["al"] + 2) == -1            # alpha not 4-byte aligned
+    assert _gdn_call(d, a, B=-1) == -1
+    assert _gdn_call(d, a, T=(1 << 20) + 1) == -1
+    assert _gdn_call(d, a, out=a["st"] + 256) == -1         # out inside the state
+    assert _gdn_call(d, a, st=a["v"]) == -1                 # state over v
+    assert _gdn_call(d, a, out=a["q"]) == -1                # out over q
+    assert _gdn_call(d, a, B=0) == 0                        # nothing to do: no device call
+    assert _gdn_call(d, a, T=0) == 0
