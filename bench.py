@@ -13,6 +13,9 @@ Workloads (synthetic, seeded; pools filled in place by the device generator):
   80b_prefill  the 80B layer shape at T = 2048 tokens per call with near-uniform
       routing (about 40 tokens per expert, every expert used), bf16 output; one
       step = all 48 layers once.
+  80b_gdn_decode  the gated-delta-rule recurrence of the 36 DeltaNet layers
+      (16 q/k heads, 32 value heads, 128 x 128 fp32 state per head): one token
+      of --sequences sequences through every layer's recurrence.
 
 Steps are captured as HIP graphs and replayed (--eager launches directly).
 Prints one JSON line: layer-tokens/s as `value`; the roofline of the dominant
@@ -35,7 +38,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from int4_quantized_expert_amd.profiling import load_traffic  # noqa: E402
+from int4_quantized_expert_amd.profiling import load_traffic, traffic_of  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0     # dense fp16/bf16 MFMA peak of MI355X
@@ -58,7 +61,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=64, help="timed steps (each through every layer)")
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--tokens", type=int, default=1, help="tokens per call for the decode workloads")
-    ap.add_argument("--workload", default="80b_stack_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="80b_stack_decode", choices=sorted(WORKLOADS) + ["80b_gdn_decode"])
+    ap.add_argument("--sequences", type=int, default=64, help="80b_gdn_decode: sequences per call")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
@@ -111,6 +115,14 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     ctx = Context(args, torch, M, synth, sgpu)
+    if args.workload == "80b_gdn_decode":
+        r = measure_gdn(ctx, args.sequences, args.steps, args.warmup)
+        line = {"metric": "gated-delta-rule decode tokens/s + achieved HBM GB/s (% of 8 TB/s)",
+                "value": r["value"], "unit": r["unit"], "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                "dtype": "f32", "data": "synthetic", "config": r["config"], "roofline": r["roofline"]}
+        print(json.dumps(line), flush=True)
+        return
     head = measure(ctx, args.workload, args.tokens, args.chain, None, args.steps, args.warmup)
     result = head["line"]
     if not args.no_extras and args.workload == "80b_stack_decode" and args.tokens == 1 and not args.chain:
@@ -127,6 +139,10 @@ def main():
                                                    "kernels")}
             extra[name]["config"] = {key: r["config"][key] for key in ("workload", "tokens_per_call", "routing",
                                                                        "chained", "out_dtype")}
+        # the gated-delta-rule recurrence of the 36 DeltaNet layers: one
+        # sequence, and a batch of 64 sequences
+        for B in (1, 64):
+            extra[f"gdn_decode_b{B}"] = measure_gdn(ctx, B, ke, we)
         result["extra"] = extra
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(head["geo"], args, head["x_host"], head["r_host"], head["shared_host"],
@@ -338,13 +354,7 @@ def measure(ctx, workload, T_arg, chain_on, routing_over, K, W):
         table.append(row)
     dom = max(range(n_k), key=lambda j: durs[:, j].mean())
     achieved = table[dom]["gbs"]
-    traffic = None
-    counters = load_traffic(os.path.join(ROOT, "profiles"), workload, T)
-    if counters is not None:
-        stem = table[dom]["kernel"].split(" ")[0]
-        hits = [r for kname, r in counters["kernels"].items() if kname.split("<")[0] == stem]
-        if len(hits) == 1:
-            traffic = hits[0]["traffic_bytes"]
+    traffic = traffic_of(load_traffic(os.path.join(ROOT, "profiles"), workload, T), table[dom]["kernel"])
     unit_us = float(durs.sum(axis=1).mean())
 
     result = {
@@ -396,6 +406,75 @@ def measure(ctx, workload, T_arg, chain_on, routing_over, K, W):
     del x, routers, out, ws, chain
     torch.cuda.synchronize()
     return out_info
+
+
+GDN_LAYERS = 36      # three quarters of the 48 layers
+
+
+def measure_gdn(ctx, B, K, W):
+    """One token of B sequences through the gated-delta-rule recurrence of 36
+    layers (80B-shaped: 16 q/k heads, 32 value heads, 128 x 128 fp32 state per
+    head), one gdn_recurrence_forward call per layer, captured in a HIP graph.
+    Returns the figure with the roofline of the recurrence kernel."""
+    torch, M = ctx.torch, ctx.M
+    from synth.gdn import GDN_PRESETS, gdn_inputs
+    p = GDN_PRESETS["80b"]
+    nk, nv, dk, dv = p["n_k_heads"], p["n_v_heads"], p["d_k"], p["d_v"]
+    desc = M.gdn_desc(nk, nv, dk, dv, act="bf16", out="bf16")
+    q, k, v, al, be, st = gdn_inputs(nk, nv, dk, dv, B, 1, ctx.args.seed, "bf16")
+    put = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(ctx.dev)
+    qd, kd, vd, ad, bd = put(q), put(k), put(v), put(al), put(be)
+    st1 = put(st)
+    states = torch.empty((GDN_LAYERS,) + tuple(st1.shape), dtype=torch.float32, device=ctx.dev)
+    states.copy_(st1.unsqueeze(0).expand_as(states))
+    out = torch.empty((GDN_LAYERS, B, 1, nv, dv), dtype=torch.bfloat16, device=ctx.dev)
+    stream = torch.cuda.Stream(ctx.dev)
+
+    def step():
+        for l in range(GDN_LAYERS):
+            M.gdn_forward(desc, B, 1, qd, kd, vd, ad, bd, states[l], out[l], stream=stream)
+
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if not ctx.args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+    run = graph.replay if graph is not None else step
+    with torch.cuda.stream(stream):
+        for _ in range(W):
+            run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(K):
+            run()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    per_launch_us = ms * 1e3 / GDN_LAYERS
+    nbytes = (2 * B * nv * dv * dk * 4          # state read and written
+              + 2 * B * nk * dk * 2 + B * nv * dv * 2   # q, k, v (bf16)
+              + 2 * B * nv * 4 + B * nv * dv * 2)       # alpha, beta, out (bf16)
+    gbs = nbytes / (per_launch_us * 1e-6) / 1e9
+    log(f"gdn B={B}: {ms:.4f} ms per step of {GDN_LAYERS} layers, {per_launch_us:.2f} us per launch, {gbs:.0f} GB/s")
+    del states, out
+    return {
+        "value": round(B / (ms * 1e-3), 1), "unit": "tokens/s (36 recurrences each)", "ms_per_step": round(ms, 4),
+        "steps": K,
+        "config": {"workload": "80b_gdn_decode", "sequences": B, "layers": GDN_LAYERS, "q_k_heads": nk,
+                   "v_heads": nv, "d_k": dk, "d_v": dv, "state_dtype": "f32", "act_dtype": "bf16",
+                   "out_dtype": "bf16", "graphs": graph is not None},
+        "roofline": {"kernel": "k_gdn_recurrence", "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_of(load_traffic(os.path.join(ROOT, "profiles"), "80b_gdn_decode", B),
+                                           "k_gdn_recurrence"),
+                     "avg_us": round(per_launch_us, 3), "bytes_per_launch": nbytes,
+                     "timing": "graph of 36 back-to-back launches on one stream / 36"},
+    }
 
 
 def store_stream(args, torch, M, synth, sgpu):

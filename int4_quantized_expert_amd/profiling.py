@@ -33,9 +33,10 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
 def source_digest() -> str:
-    """sha256 over the kernel sources, the public header and the build flags."""
+    """sha256 over the kernel sources, the public headers and the build flags."""
     h = hashlib.sha256()
-    files = [os.path.join(PKG, "build.py"), os.path.join(ROOT, "include", "moe_layer.h")]
+    inc = os.path.join(ROOT, "include")
+    files = [os.path.join(PKG, "build.py")] + [os.path.join(inc, f) for f in sorted(os.listdir(inc)) if f.endswith(".h")]
     csrc = os.path.join(PKG, "csrc")
     files += [os.path.join(csrc, f) for f in sorted(os.listdir(csrc)) if f.endswith((".hip", ".h"))]
     for f in files:
@@ -150,6 +151,20 @@ def load_traffic(profiles_dir: str, workload: str, tokens: int) -> dict | None:
         if blob.get("workload") == workload and blob.get("tokens") == tokens and blob.get("source_digest") == digest:
             return blob
     return None
+
+
+def traffic_of(blob: dict | None, kernel: str) -> int | None:
+    """Bytes per launch of `kernel` (a short name, or its stem before any
+    template arguments or description) in a counter table, if exactly one
+    entry matches."""
+    if blob is None:
+        return None
+    rows = blob["kernels"]
+    if kernel in rows:
+        return rows[kernel]["traffic_bytes"]
+    stem = kernel.split(" ")[0].split("<")[0]
+    hits = [r for name, r in rows.items() if name.split("<")[0] == stem]
+    return hits[0]["traffic_bytes"] if len(hits) == 1 else None
 
 
 def kernel_stats(stats_csv: str) -> list[dict]:
