@@ -151,3 +151,78 @@ def test_partial_residency_from_file_store_bitwise_equals_resident(tmp_path, dir
     assert misses > n_staging and evictions > 0 and hits > 0
     cache.close()
     store.close()
+
+
+@pytest.mark.parametrize("keep_counts", [False, True])
+def test_eviction_while_the_reader_is_in_flight(keep_counts):
+    """Hazard ordering with no host wait on the compute: call i + 1's router
+    runs on its own stream and its acquire evicts slots that call i's experts
+    (held back on the compute stream behind a long matmul) have not read yet.
+    The copies must wait for call i's compute_done event; every output must
+    still equal the fully resident run bit for bit (explicit hazard
+    management: Swiftlet README translation, "Relation to TurboFieldfare").
+    Separate workspaces for the router and the experts; a pinned slot table
+    per call, since the compute stream copies it after the host moved on."""
+    L, T, seed = 4, 64, 43
+    ctx = _resident_reference(T, L, seed)
+    geo = ctx["geo"]
+    E, k, H, stride = geo.n_experts, geo.top_k, geo.hidden, geo.blob_stride
+    n_slots = 200
+    host = torch.empty(L * E * stride, dtype=torch.uint8, pin_memory=True)
+    host.copy_(ctx["pool"])
+    torch.cuda.synchronize()
+    slot_pool = torch.empty(n_slots * stride, dtype=torch.uint8, device=DEV)
+    cache = M.ExpertCache(n_slots, stride, slot_pool, host, L, E)
+    cache.set_policy(keep_counts)
+    desc_p = M.desc_for(H, E, k, geo.inter, geo.shared_inter, geo.bits, geo.act, geo.sb, "f32",
+                        pool_bytes=n_slots * stride)
+    ws_r = torch.zeros(M.workspace_bytes(desc_p, T), dtype=torch.uint8, device=DEV)
+    ws_c = torch.zeros_like(ws_r)
+    M.workspace_init(ws_r)
+    M.workspace_init(ws_c)
+    s_route, s_comp, s_copy = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    a = torch.randn(3072, 3072, device=DEV)
+    torch.cuda.synchronize()
+    # both steps of a layer back to back (hits), then the next layer (evictions)
+    order = [(s, l) for rep in range(2) for l in range(L) for s in range(2)]
+    calls, in_flight_evictions = [], 0
+    for i, (s, l) in enumerate(order):
+        R, sh = _layer_args(ctx, l)
+        c = dict(s=s, l=l, ids=torch.empty(T, k, dtype=torch.int32, device=DEV),
+                 wts=torch.empty(T, k, dtype=torch.float32, device=DEV),
+                 ids_h=torch.empty(T, k, dtype=torch.int32, pin_memory=True),
+                 table_h=torch.zeros(E, dtype=torch.int64, pin_memory=True),
+                 table_d=torch.empty(E, dtype=torch.int64, device=DEV),
+                 out=torch.full((T, H), float("nan"), dtype=torch.float32, device=DEV),
+                 routed=torch.cuda.Event(), ready=torch.cuda.Event(), done=torch.cuda.Event())
+        with torch.cuda.stream(s_route):
+            M.router_topk(desc_p, T, _x_ptr(ctx, l, s), R, c["ids"], c["wts"], ws_r, stream=s_route)
+            c["ids_h"].copy_(c["ids"], non_blocking=True)
+            c["routed"].record(s_route)
+        c["routed"].synchronize()                     # the host waits for the router only
+        cache.acquire(l, c["ids_h"].numpy(), c["table_h"].numpy(), s_copy, c["ready"])
+        if calls:
+            p = calls[-1]
+            if not p["done"].query():
+                used = np.unique(p["ids_h"].numpy())
+                in_flight_evictions += sum(cache.slot_of(p["l"], int(e)) * stride != int(p["table_h"][e])
+                                           for e in used)
+        with torch.cuda.stream(s_comp):
+            s_comp.wait_event(c["routed"])
+            s_comp.wait_event(c["ready"])
+            torch.mm(a, a)                            # keeps this call's readers pending for a while
+            c["table_d"].copy_(c["table_h"], non_blocking=True)
+            M.experts_forward(desc_p, T, _x_ptr(ctx, l, s), c["ids"], c["wts"], c["table_d"], slot_pool, sh,
+                              c["out"], ws_c, stream=s_comp)
+            c["done"].record(s_comp)
+        cache.release(l, c["done"])
+        calls.append(c)
+    torch.cuda.synchronize()
+    M.status_check(ws_r)
+    M.status_check(ws_c)
+    for i, c in enumerate(calls):
+        assert torch.equal(c["out"], ctx["ref"][(c["s"], c["l"])]), f"call {i} (step {c['s']}, layer {c['l']})"
+    hits, misses, evictions = cache.stats()
+    assert evictions > 0 and hits > 0
+    assert in_flight_evictions > 0, "no slot was evicted while its reader was pending: the test did not test"
+    cache.close()
