@@ -52,6 +52,8 @@ WORKLOADS = {
     "80b_prefill": ("80b", 48, 2048, "normal", "bf16"),
     # experts streamed from a container file through a 40% HBM slot pool (not the headline metric)
     "35b_int8_store": ("35b_int8", 4, 64, "zipf", "f32"),
+    # partial residency at full scale: 40 layers, 4,096 slots (40%), misses from pinned host memory
+    "35b_int8_partial": ("35b_int8", 40, 64, "zipf", "f32"),
 }
 
 
@@ -105,6 +107,8 @@ def main():
 
     if args.workload == "35b_int8_store":
         return store_stream(args, torch, M, synth, sgpu)
+    if args.workload == "35b_int8_partial":
+        return partial_residency(args, torch, M, synth, sgpu)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.copy_probe:
@@ -475,6 +479,178 @@ def measure_gdn(ctx, B, K, W):
                      "avg_us": round(per_launch_us, 3), "bytes_per_launch": nbytes,
                      "timing": "graph of 36 back-to-back launches on one stream / 36"},
     }
+
+
+def host_ram_gb():
+    try:
+        with open("/proc/meminfo") as fh:
+            for line in fh:
+                if line.startswith("MemTotal:"):
+                    return round(int(line.split()[1]) / 1e6, 1)
+    except OSError:
+        pass
+    return None
+
+
+def partial_residency(args, torch, M, synth, sgpu):
+    """The 35B int8 layer over 40 layers with an HBM slot pool of 40% of the
+    experts (4,096 slots of 3,342,336 B): misses copied from a 34.2 GB pinned
+    host store on a copy stream, the router of each call on its own stream,
+    the experts on a compute stream, no host wait on the compute (the cache
+    orders every slot overwrite after the last reader's event).  Timed for
+    both eviction policies (use counts restarting at eviction, and kept), next
+    to the same calls on the fully resident pool; sampled layers' outputs are
+    compared with the resident run bit for bit."""
+    preset, n_layers, T, _, out_dt = WORKLOADS[args.workload]
+    geo = synth.PRESETS[preset]
+    K, W = args.steps, args.warmup
+    H, E, k = geo.hidden, geo.n_experts, geo.top_k
+    stride = geo.blob_stride
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cur = torch.cuda.current_stream(dev)
+    t0 = time.time()
+    total = n_layers * E * stride
+    pool = torch.empty(total, dtype=torch.uint8, device=dev)
+    for l in range(n_layers):
+        sgpu.fill_blobs(geo, pool.data_ptr() + l * E * stride, E, args.seed, l, 0, stream=cur.cuda_stream)
+    host = torch.empty(total, dtype=torch.uint8, pin_memory=True)
+    host.copy_(pool)
+    torch.cuda.synchronize()
+    log(f"pool and pinned host store ready in {time.time() - t0:.1f}s: {total / 1e9:.2f} GB each")
+    shared = torch.from_numpy(np.concatenate([synth.make_shared(geo, args.seed, l) for l in range(n_layers)])).to(dev)
+    S = K + W
+    xs = np.stack([synth.tokens(geo, args.seed, l, S * T) for l in range(n_layers)])
+    rs = np.stack([synth.router_zipf(geo, args.seed, l, xs[l]) for l in range(n_layers)])
+    x = torch.from_numpy(xs.view(np.uint8)).to(dev)
+    routers = torch.from_numpy(rs.view(np.uint8)).to(dev)
+    n_slots = (n_layers * E * 2) // 5
+    slot_pool = torch.empty(n_slots * stride, dtype=torch.uint8, device=dev)
+    desc_p = M.desc_for(H, E, k, geo.inter, geo.shared_inter, geo.bits, geo.act, geo.sb, out_dt,
+                        pool_bytes=n_slots * stride)
+    desc_r = M.desc_for(H, E, k, geo.inter, geo.shared_inter, geo.bits, geo.act, geo.sb, out_dt, pool_bytes=total)
+    ws_r = torch.zeros(M.workspace_bytes(desc_p, T), dtype=torch.uint8, device=dev)
+    ws_c = torch.zeros_like(ws_r)
+    M.workspace_init(ws_r)
+    M.workspace_init(ws_c)
+    s_route, s_comp, s_copy = torch.cuda.Stream(dev), torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    sampled = {0, n_layers // 3, 2 * n_layers // 3, n_layers - 1}
+
+    def xp(l, s):
+        return x.data_ptr() + (l * S * T + s * T) * H * 2
+
+    def rp(l):
+        return routers.data_ptr() + l * E * H * 2
+
+    def sp(l):
+        return shared.data_ptr() + l * geo.shared_bytes
+
+    # the fully resident run: timed, and the sampled layers' outputs kept
+    ref = {}
+    out_r = torch.empty(T, H, dtype=torch.float32, device=dev)
+    res_slots = torch.arange(n_layers * E, dtype=torch.int64, device=dev).reshape(n_layers, E) * stride
+
+    def step_resident(s, keep):
+        for l in range(n_layers):
+            M.layer_forward(desc_r, T, xp(l, s), rp(l), res_slots[l], pool, sp(l), out_r, ws_c)
+            if keep and l in sampled:
+                ref[(s, l)] = out_r.clone()
+
+    for s in range(W):
+        step_resident(s, False)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for s in range(W, S):
+        step_resident(s, True)
+    torch.cuda.synchronize()
+    dt_res = time.perf_counter() - t1
+    M.status_check(ws_c)
+
+    NR = 8      # ring of per-call buffers; an entry is reused after its call's compute_done
+    ring = [dict(ids=torch.empty(T, k, dtype=torch.int32, device=dev),
+                 wts=torch.empty(T, k, dtype=torch.float32, device=dev),
+                 ids_h=torch.empty(T, k, dtype=torch.int32, pin_memory=True),
+                 table_h=torch.zeros(E, dtype=torch.int64, pin_memory=True),
+                 table_d=torch.empty(E, dtype=torch.int64, device=dev),
+                 out=torch.empty(T, H, dtype=torch.float32, device=dev),
+                 routed=torch.cuda.Event(), ready=torch.cuda.Event(), done=torch.cuda.Event(), used=False)
+            for _ in range(NR)]
+
+    def run_policy(keep_counts):
+        cache = M.ExpertCache(n_slots, stride, slot_pool, host, n_layers, E)
+        cache.set_policy(keep_counts)
+        n_call, checked, equal = 0, 0, 0
+        pending = []
+
+        def call(s, l, timed):
+            nonlocal n_call
+            c = ring[n_call % NR]
+            n_call += 1
+            if c["used"]:
+                c["done"].synchronize()
+            c["used"] = True
+            with torch.cuda.stream(s_route):
+                M.router_topk(desc_p, T, xp(l, s), rp(l), c["ids"], c["wts"], ws_r, stream=s_route)
+                c["ids_h"].copy_(c["ids"], non_blocking=True)
+                c["routed"].record(s_route)
+            c["routed"].synchronize()
+            cache.acquire(l, c["ids_h"].numpy(), c["table_h"].numpy(), s_copy, c["ready"])
+            with torch.cuda.stream(s_comp):
+                s_comp.wait_event(c["routed"])
+                s_comp.wait_event(c["ready"])
+                c["table_d"].copy_(c["table_h"], non_blocking=True)
+                M.experts_forward(desc_p, T, xp(l, s), c["ids"], c["wts"], c["table_d"], slot_pool, sp(l), c["out"],
+                                  ws_c, stream=s_comp)
+                if timed and l in sampled:
+                    pending.append(((s, l), c["out"].clone()))
+                c["done"].record(s_comp)
+            cache.release(l, c["done"])
+
+        for s in range(W):
+            for l in range(n_layers):
+                call(s, l, False)
+        torch.cuda.synchronize()
+        h0, m0, e0 = cache.stats()
+        t = time.perf_counter()
+        for s in range(W, S):
+            for l in range(n_layers):
+                call(s, l, True)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t
+        h1, m1, e1 = cache.stats()
+        M.status_check(ws_r)
+        M.status_check(ws_c)
+        for key, o in pending:
+            checked += 1
+            equal += int(torch.equal(o, ref[key]))
+        cache.close()
+        hits, misses = h1 - h0, m1 - m0
+        log(f"partial residency keep_counts={keep_counts}: {dt / K * 1e3:.1f} ms/step, hit rate "
+            f"{hits / max(1, hits + misses):.3f}, {equal}/{checked} sampled calls bitwise equal")
+        return {"value": round(K * n_layers * T / dt, 1), "ms_per_step": round(dt / K * 1e3, 3),
+                "hits": hits, "misses": misses, "evictions": e1 - e0,
+                "hit_rate": round(hits / max(1, hits + misses), 4),
+                "miss_gbs": round(misses * stride / dt / 1e9, 2),
+                "sampled_calls": checked, "sampled_bitwise_equal": equal}
+
+    kept = run_policy(True)      # the cache's default policy: the headline figure
+    lfu = run_policy(False)
+    line = {
+        "metric": "MoE-layer tokens/s with partial residency (35B int8, 40 layers, 40% of experts in HBM)",
+        "value": kept["value"], "unit": "layer-tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": kept["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u8 codes, f32 accumulate", "data": "synthetic",
+        "config": {"workload": args.workload, "layers": n_layers, "tokens_per_call": T, "experts": E,
+                   "top_k": k, "slots": n_slots, "slot_bytes": stride, "pinned_host_store_bytes": total,
+                   "host_ram_gb": host_ram_gb(), "routing": "zipf",
+                   "sampled_layers": sorted(sampled)},
+        "policy_counts_kept": kept,
+        "policy_counts_restart": lfu,
+        "resident": {"value": round(K * n_layers * T / dt_res, 1), "ms_per_step": round(dt_res / K * 1e3, 3)},
+        "timing": "host wall clock around K steps of 40 calls, synchronized on both sides; per call the host waits "
+                  "for the router's ids only",
+    }
+    print(json.dumps(line), flush=True)
 
 
 def store_stream(args, torch, M, synth, sgpu):

@@ -353,8 +353,10 @@ const char* moe_last_error(void);
  *
  * Policy: a miss takes an empty slot (lowest first), else evicts the resident
  * blob with the fewest uses, ties to the oldest last use, then the lower
- * (layer, id).  Uses count once per acquire that needs the blob and restart
- * when it is evicted.  Blobs the current call needs are never evicted by it,
+ * (layer, id).  Uses count once per acquire that needs the blob, over the
+ * cache's whole life (an evicted blob keeps its count; moe_cache_set_policy
+ * can make counts restart at eviction instead).  Blobs the current call
+ * needs are never evicted by it,
  * nor are blobs of acquires not yet released.
  * Ordering (no host waits): a victim slot is overwritten only after the
  * compute_done event of the last released call that read it (if that event
@@ -390,11 +392,13 @@ int moe_cache_release(moe_cache* cache, int32_t layer, void* compute_done);
 
 void moe_cache_stats(const moe_cache* cache, int64_t* hits, int64_t* misses, int64_t* evictions);
 
-/* Policy flags (moe_cache_set_policy).  MOE_CACHE_KEEP_COUNTS: a blob's use
- * count survives its eviction, so a frequently used expert that a burst of
- * others pushed out comes back with its count and is not the next victim
- * (with the flag clear, counts restart at eviction).  Either way the policy
- * changes only which blobs stay resident, never the outputs. */
+/* Policy flags (moe_cache_set_policy).  MOE_CACHE_KEEP_COUNTS (set when a
+ * cache is created): a blob's use count survives its eviction, so a
+ * frequently used expert that a burst of others pushed out comes back with
+ * its count and is not the next victim.  With the flag clear, counts restart
+ * at eviction, and a cycle of blobs longer than the pool degenerates to
+ * least-recently-used order.  Either way the policy changes only which blobs
+ * stay resident, never the outputs. */
 #define MOE_CACHE_KEEP_COUNTS 1
 
 /* Sets the policy flags of a cache (0 or MOE_CACHE_KEEP_COUNTS) for its later

@@ -91,7 +91,7 @@ struct moe_cache {
   hipEvent_t last_copies = nullptr;    // recorded after the latest acquire's copies
   hipStream_t last_stream = nullptr;
   bool any_copies = false;
-  bool keep_counts = false;            // MOE_CACHE_KEEP_COUNTS: uses survive eviction
+  bool keep_counts = true;             // MOE_CACHE_KEEP_COUNTS (the default): uses survive eviction
   std::vector<int64_t> count;          // [layer * E + id] uses so far (kept across evictions)
   int64_t fault_at = -1;               // copies until an injected failure (-1: none)
 
