@@ -82,16 +82,14 @@ struct SLds {
   uint32_t hs;         // staged h [(k + 1) * kSegI][kPad] floats
   uint32_t hsum;       // [(k + 1) * kSegI] segment sums
   uint32_t lg;         // [kMaxE] logits
-  uint32_t cand;       // [kNW][kWave] packed top-k candidates
+  uint32_t cand;       // [kWave] packed top-k candidates (wave 0)
   uint32_t misc;       // see below
   uint32_t part;       // [(k + 1) * rb] partial down sums
   uint32_t total;
 };
 
 // misc words (32-bit each)
-constexpr int kMTheta = 0;            // [kNW] per-wave key bounds
-constexpr int kMCnt = kNW;            // [kNW] per-wave candidate counts
-constexpr int kMIds = 2 * kNW;        // [kMaxK] chosen experts by rank
+constexpr int kMIds = 0;              // [kMaxK] chosen experts by rank
 constexpr int kMVals = kMIds + kMaxK; // [kMaxK] chosen logits, then weights
 constexpr int kMSig = kMVals + kMaxK; // sigmoid(g . x)
 constexpr int kMOk = kMSig + 1;       // result of the last flag wait
@@ -137,19 +135,6 @@ __device__ __forceinline__ void store_tag(uint64_t* p, uint32_t bits, uint32_t t
 }
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Maximum over the wave (every lane gets it).
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
-  v = mx(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x140, 0xf, 0xf, false)));
-  v = mx(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xf, 0xf, false)));
-  v = mx(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x1B, 0xf, 0xf, false)));
-  v = mx(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xf, 0xf, false)));
-  auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  v = mx(r16[0], r16[1]);
-  auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return mx(r32[0], r32[1]);
-}
 
 struct StackArgs {
   const uint8_t* x;          // layer l's input at x + l * x_stride (layer 0 only when chained)
@@ -452,91 +437,24 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
       __syncthreads();
       dead = dead || !(ok && reads_ok(misc));
     }
-    // top-k over the block: each wave bounds its share of the keys from below
-    // (its j-th largest, j * waves-with-keys >= k), so that every key at or
-    // above the smallest bound is a candidate and at least k of them qualify;
-    // the candidates, packed as (key << 32 | ~id), are then ranked exactly
-    {
-      const int nwd = (E + kWave - 1) / kWave;
-      const int jr = (k + nwd - 1) / nwd;
-      uint32_t key = 0;
-      if (tid < E) {
-        const uint32_t kv = order_key(lg[tid]);
-        key = kv > 1u ? kv : 1u;
-      }
-      if (wave < nwd) {
-        uint32_t kk = key, th = 0;
-        for (int r = 0; r < jr; ++r) {
-          th = wave_max_u32(kk);
-          const uint64_t m = __ballot(kk == th && kk != 0u);
-          if (m != 0 && lane == __builtin_ctzll(m)) kk = 0;
-        }
-        if (lane == 0) misc[kMTheta + wave] = th;
-      }
-      __syncthreads();
-      uint32_t theta = 0xffffffffu;
-      for (int w = 0; w < nwd; ++w) theta = min(theta, misc[kMTheta + w]);
-      const bool cand = tid < E && key >= theta;
-      const uint64_t cm = __ballot(cand);
-      if (lane == 0) misc[kMCnt + wave] = static_cast<uint32_t>(__popcll(cm));
-      __syncthreads();
-      // one contiguous list of the candidates (in id order), padded with
-      // zeros to a multiple of 8 (a zero word never outranks a candidate)
-      int base = 0, total = 0;
-      for (int w = 0; w < kNW; ++w) {
-        const int c = static_cast<int>(misc[kMCnt + w]);
-        base += w < wave ? c : 0;
-        total += c;
-      }
-      lds_w64* cl = (lds_w64*)(lds + S.cand);
-      const uint64_t mine = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~tid);
-      if (cand) cl[base + __popcll(cm & lane_mask_lt(lane))] = mine;
-      const int total8 = (total + 7) & ~7;
-      if (tid >= total && tid < total8) cl[tid] = 0ull;
-      __syncthreads();
-      if (cand) {
-        // rank = number of candidates that order before this one; eight per
-        // round, every read of a round requested before any compare
-        int rank = 0;
-        const lds_u32x4* c4 = (const lds_u32x4*)(cl);
-        for (int d0 = 0; d0 < total8; d0 += 8) {
-          u32x4 q[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) q[i] = c4[d0 / 2 + i];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint64_t w0 = (static_cast<uint64_t>(q[i][1]) << 32) | q[i][0];
-            const uint64_t w1 = (static_cast<uint64_t>(q[i][3]) << 32) | q[i][2];
-            rank += (w0 > mine) ? 1 : 0;
-            rank += (w1 > mine) ? 1 : 0;
-          }
-        }
-        if (rank < k) {
-          misc[kMIds + rank] = static_cast<uint32_t>(tid);
-          misc[kMVals + rank] = __float_as_uint(lg[tid]);
+    // top-k on wave 0 (the staged kernels' wave top-k: a bound from the lane
+    // maxima, the candidates above it ranked exactly, the weights in rank
+    // order), then the chosen experts' blob offsets; one barrier for all
+    if (wave == 0) {
+      topk_wave_n<8>(lg, E, k, lane, reinterpret_cast<uint64_t*>(lds + S.cand),
+                     reinterpret_cast<int32_t*>(reinterpret_cast<uint32_t*>(lds + S.misc) + kMIds),
+                     reinterpret_cast<float*>(reinterpret_cast<uint32_t*>(lds + S.misc) + kMVals));
+      const lds_i64* slot = (const lds_i64*)(P + S.p_slot);
+      if (lane < k) {
+        const int e = static_cast<int>(misc[kMIds + lane]);
+        ((lds_i64*)(misc + kMOff))[lane] = slot[e];
+        if (b == 0) {
+          if (a.ids_out) a.ids_out[static_cast<size_t>(l) * k + lane] = e;
+          if (a.wts_out) a.wts_out[static_cast<size_t>(l) * k + lane] = __uint_as_float(misc[kMVals + lane]);
         }
       }
-      __syncthreads();
-      if (wave == 0) {
-        // p_i = exp(l_i - l_0) / sum_j exp(l_j - l_0), the sum in rank order
-        const float top = __uint_as_float(misc[kMVals]);
-        const float ex = lane < k ? expf(__uint_as_float(misc[kMVals + (lane < k ? lane : 0)]) - top) : 0.f;
-        float sum = 0.f;
-        for (int i = 0; i < k; ++i)
-          sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), i));
-        const lds_i64* slot = (const lds_i64*)(P + S.p_slot);
-        if (lane < k) {
-          const int e = static_cast<int>(misc[kMIds + lane]);
-          misc[kMVals + lane] = __float_as_uint(ex / sum);
-          ((lds_i64*)(misc + kMOff))[lane] = slot[e];
-          if (b == 0) {
-            if (a.ids_out) a.ids_out[static_cast<size_t>(l) * k + lane] = e;
-            if (a.wts_out) a.wts_out[static_cast<size_t>(l) * k + lane] = ex / sum;
-          }
-        }
-      }
-      __syncthreads();
     }
+    __syncthreads();
 
     // ------------------------------------------------------------------ G
     {
