@@ -9,9 +9,12 @@
 //
 // Organisation.  The work is bound by HBM: every token reads and writes the
 // whole state (64 KB per 128 x 128 head) and does 4 flops per element.  So:
-//   - a block owns 16 P rows of one head's state and holds them in registers
-//     for all T tokens of the call (one read and one write of the state per
-//     call, whatever T);
+//   - a block owns 16 rows of one head's state (P = 1 pass; the kernel takes
+//     more passes as a template argument, measured slower) and holds them in
+//     registers for all T tokens of the call (one read and one write of the
+//     state per call, whatever T), read and written with non-temporal
+//     accesses (the state is streamed once per call and should not displace
+//     the caches' other lines);
 //   - 16 lanes share a row, each with 4-column chunks at 64 m + 4 j
 //     (m < d_k / 64), so that a wave's 16-byte loads cover 256 contiguous
 //     bytes of each of its 4 rows;
@@ -19,8 +22,6 @@
 //     permutations that give every lane the same bits;
 //   - the next token's q, k, v, alpha and beta are requested before the
 //     current token's arithmetic, so their latency hides behind it;
-//   - P (1, 2 or 4 row passes per block) is chosen on the host so that small
-//     batches still spread over every compute unit.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -36,6 +37,8 @@ namespace {
 constexpr int kGThr = 256;                        // 4 waves
 constexpr int kRowLanes = 16;                     // lanes per state row
 constexpr int kRowsPerPass = kGThr / kRowLanes;   // 16 rows per block pass
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct GdnArgs {
   const void* q;
@@ -144,9 +147,9 @@ __global__ __launch_bounds__(kGThr) void k_gdn_recurrence(GdnArgs a) {
   for (int p = 0; p < P; ++p) {
 #pragma unroll
     for (int m = 0; m < NC; ++m) {
-      const float4 w = *reinterpret_cast<const float4*>(st + static_cast<int64_t>(row_lane0 + p * kRowsPerPass) * DK +
-                                                        64 * m + 4 * j);
-      S[p][m][0] = w.x; S[p][m][1] = w.y; S[p][m][2] = w.z; S[p][m][3] = w.w;
+      const f32x4 w = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4*>(st + static_cast<int64_t>(row_lane0 + p * kRowsPerPass) * DK + 64 * m + 4 * j));
+      S[p][m][0] = w[0]; S[p][m][1] = w[1]; S[p][m][2] = w[2]; S[p][m][3] = w[3];
     }
   }
 
@@ -215,8 +218,9 @@ __global__ __launch_bounds__(kGThr) void k_gdn_recurrence(GdnArgs a) {
   for (int p = 0; p < P; ++p) {
 #pragma unroll
     for (int m = 0; m < NC; ++m) {
-      *reinterpret_cast<float4*>(st + static_cast<int64_t>(row_lane0 + p * kRowsPerPass) * DK + 64 * m + 4 * j) =
-          make_float4(S[p][m][0], S[p][m][1], S[p][m][2], S[p][m][3]);
+      const f32x4 w = {S[p][m][0], S[p][m][1], S[p][m][2], S[p][m][3]};
+      __builtin_nontemporal_store(
+          w, reinterpret_cast<f32x4*>(st + static_cast<int64_t>(row_lane0 + p * kRowsPerPass) * DK + 64 * m + 4 * j));
     }
   }
 }
@@ -229,11 +233,8 @@ hipError_t launch_p(const GdnArgs& a, int64_t blocks, hipStream_t s) {
 
 template <int DK, int ACT, int OUT>
 hipError_t launch_dk(const GdnArgs& a, int P, int64_t blocks, hipStream_t s) {
-  switch (P) {
-    case 4: return launch_p<DK, 4, ACT, OUT>(a, blocks, s);
-    case 2: return launch_p<DK, 2, ACT, OUT>(a, blocks, s);
-    default: return launch_p<DK, 1, ACT, OUT>(a, blocks, s);
-  }
+  (void)P;
+  return launch_p<DK, 1, ACT, OUT>(a, blocks, s);
 }
 
 template <int ACT, int OUT>
@@ -289,13 +290,11 @@ extern "C" int gdn_recurrence_forward(const gdn_desc* d, int32_t B, int32_t T, c
   }
   if (overlaps(state, n_s, out, n_o)) return bad("state and out overlap");
 
-  // rows per block: the most passes that still leave 1024 blocks, else one
+  // one pass of 16 rows per block (measured fastest at every batch size:
+  // the most blocks, the most loads in flight)
   const int64_t heads = static_cast<int64_t>(B) * d->n_v_heads;
-  int P = 1;
-  for (int c : {4, 2}) {
-    if (d->d_v % (kRowsPerPass * c) == 0 && heads * (d->d_v / (kRowsPerPass * c)) >= 1024) { P = c; break; }
-  }
-  const int64_t blocks = heads * (d->d_v / (kRowsPerPass * P));
+  const int P = 1;
+  const int64_t blocks = heads * (d->d_v / kRowsPerPass);
   if (blocks > 0x7fffffffLL) return bad("B * n_v_heads * d_v = %lld rows is too many for one launch", heads * d->d_v);
 
   GdnArgs a;

@@ -144,8 +144,7 @@ def test_matches_oracle_within_derived_bound(name, kw):
 @pytest.mark.parametrize("B", [1, 8, 64])
 def test_decode_step_at_the_benchmark_sizes(B):
     """One token for B sequences of the 80B-shaped layer (B = 1: a single
-    stream; B = 64: the batched figure), every element against the oracle.
-    The three sizes take 1, 2 and 4 row passes per block."""
+    stream; B = 64: the batched figure), every element against the oracle."""
     check(Case(**GDN_PRESETS["80b"], B=B, T=1, seed=10 + B))
 
 
