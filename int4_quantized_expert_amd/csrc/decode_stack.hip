@@ -1,29 +1,44 @@
 // Persistent decode of a stack of MoE layers, one token per layer (gfx950).
 //
-// One launch runs L layers in order on a grid of one resident 512-thread
-// block per CU.  Per layer:
-//   R  router rows, the shared expert's gate/up rows and sigmoid(g . x), from
-//      operands already in LDS (copied there while the previous layer ran)
-//   K  every block gathers the E logits and takes top-k and the renormalised
-//      weights itself, all eight waves at once
-//   G  the routed gate/up rows, an equal share per block, every load of a
-//      wave requested at once; meanwhile one wave copies the block's down
-//      operands (its output rows of each chosen expert) into LDS
-//   H  every block gathers h (k routed rows, the shared row, the gate)
-//   D  down rows from LDS, ordered combine, output (and, in a chain, the next
-//      layer's input x + y, exchanged like h)
-// Blocks exchange data only through tagged 64-bit words: the value's bits
-// and a per-layer tag, written with relaxed device-scope stores and read with
-// device-scope loads until every word a block needs carries the tag.  Words
-// are written in several replicas, each read by a fraction of the blocks.
-// Every wait is bounded; on expiry the kernel raises kErrTimeout and skips
-// all later waits.
+// One launch runs L layers in order on a grid of 256 resident 512-thread
+// blocks (one per CU).  The blocks form eight groups of 32 (block b is in
+// group b % 8; the dispatcher sends block b to XCD b % 8, so a group is one
+// XCD).  Each layer's work is split into units: the k routed experts (rank i)
+// and the shared expert's down projection (unit k).  Group g takes units g
+// and g + 8, so each unit's expert lives in one group:
+//   R  every block: two router rows and two of the shared expert's gate/up
+//      rows from LDS (copied there while the previous layer ran); block 0
+//      also sigma(g . x)
+//   K  grid-wide: every block reads the E logits and takes top-k and the
+//      renormalised weights itself (one wave)
+//   G  per group: the 512 gate/up row pairs of each routed unit of the group,
+//      16 per block, every load of a wave requested at once; meanwhile one
+//      wave copies the block's 64 down rows of each unit into LDS
+//   H  per group: the 32 blocks of a group gather their units' h (512 values
+//      each; the shared expert's h comes from R)
+//   D  per group: the block's 64 down rows of each unit, the row sums stored
+//      per unit as tagged words
+// The ordered combine (ranks ascending, then sigma times the shared unit)
+// reads every unit's row sums, so it waits for all groups: unchained, block b
+// finishes rows 8b..8b+7 of layer l while the next layer's top-k runs (the
+// last layer after one more grid-wide wait); chained, every group finishes
+// all rows after a grid-wide wait and exchanges the next input within the
+// group.
+//
+// Blocks exchange data only through tagged 64-bit words: the value's bits and
+// the layer's tag, written with relaxed device-scope stores and read with
+// device-scope loads until every word a block needs carries the tag.  The
+// logits are read that way directly; the other exchanges first wait for
+// per-block flags (the tag, raised once a block's words are issued: 256 of
+// them in one of 16 replicas grid-wide, 32 in a group) and then read the
+// words once, reading again any word that is still old.  Every wait is
+// bounded; on expiry the kernel raises kErrTimeout and skips all later waits,
+// so the grid always drains.  Regions written before a grid-wide wait and
+// read after another block's (the logits, the shared h, the row sums)
+// alternate between two copies by layer parity.
 //
 // Work inside a layer needs every block resident at once (checked with the
-// occupancy query when the plan is made).  Across layers, one exchange per
-// layer (h) orders everything: a block writes a layer's words only after it
-// has read every block's h of the layer before, so a buffer is never
-// overwritten while another block may still read it.
+// occupancy query when the plan is made).
 //
 // The arithmetic of every row (segment FMA chains, v_dot2 on exact bf16
 // codes, the symmetric lane reductions, the combine order) is that of the
@@ -49,9 +64,18 @@ constexpr int kH = 2048;                   // hidden size this kernel is built f
 constexpr int kI = 512;                    // routed and shared intermediate size
 constexpr int kThr = 512;
 constexpr int kNW = kThr / kWave;          // 8 waves per block
-constexpr int kGW = 6;                     // waves 0..5 take the phase-G rows
+constexpr int kNG = 8;                     // block groups (block b in group b % 8)
+constexpr int kNM = 32;                    // blocks per group
+constexpr int kNB = kNG * kNM;             // blocks in the grid
+constexpr int kUPG = 2;                    // units of one group per layer, at most
+constexpr int kHPM = kI / kNM;             // gate/up row pairs of a unit per block (16)
+constexpr int kDPM = kH / kNM;             // down rows of a unit per block (64)
+constexpr int kFR = kH / kNB;              // output rows a block finishes, unchained (8)
+constexpr int kGW = 6;                     // waves 0..5 take the gate/up pairs
+constexpr int kMaxG = (kUPG * kHPM + kGW - 1) / kGW;   // pairs per wave, at most (6)
 constexpr int kWaveStatic = 6;             // copies the next layer's static operands
-constexpr int kWaveDown = 7;               // copies the routed down operands
+constexpr int kWaveDown = 7;               // copies the down operands
+constexpr int kWaveFin = 1;                // finishes the previous layer's rows (unchained)
 constexpr int kSegI = kI / kSegCodes;      // 16 segments per down row
 constexpr int kRpp = kWave / kSegI;        // 4 down rows per wave pass
 constexpr int kPad = kSegCodes + 4;        // staged h: floats per segment (bank spread)
@@ -61,14 +85,24 @@ constexpr int64_t kBlob = 3 * kQ + 6 * kS;
 constexpr int kRowQ = kH / 2;              // code bytes of a gate/up row
 constexpr int kDRowQ = kI / 2;             // code bytes of a down row
 constexpr int kDRowSB = (kI / 64) * 2;     // scale (or bias) bytes of a down row
-constexpr int kLgRep = 8, kHRep = 4, kXRep = 8;   // copies of the exchanged words
-constexpr int kFlagRep = 16;                        // copies of the per-block flags
-constexpr int kMaxNb = 512;                         // blocks whose flags one wave polls
-constexpr int kMaxK = 10, kMaxRpb = 4, kMaxSpb = 4, kMaxRb = 16, kMaxG = 4, kMaxE = 512;
-constexpr int kMaxHn = (kMaxK + 1) * kI + 1;        // exchanged h words: k routed rows, shared row, gate
-constexpr int kRdWaves = 6;                         // waves that read exchanged words (0..5)
+constexpr uint32_t kDRowB = kDRowQ + 2 * kDRowSB;   // LDS bytes of one staged down row
+constexpr int kLgRep = 8;                  // copies of the exchanged logits
+constexpr int kFlagRep = 16;               // copies of the grid-wide flags
+constexpr int kMaxK = 10, kMaxRpb = 2, kSpb = kI / kNB, kMaxE = kNB * kMaxRpb;
+constexpr int kTopC = 16;                  // top-k candidates each wave keeps
+constexpr int kRdWaves = 6;                // waves that read exchanged words (0..5)
 constexpr int kRdThr = kRdWaves * kWave;
-constexpr int kFlLg = 0, kFlH = 1, kFlX = 2;        // flag kinds
+constexpr int kSigW = (kMaxK + 1) * kH;    // sigma's word in a row-sum copy
+constexpr int kPartW = kSigW + 64;         // words of one row-sum copy
+constexpr int kFlP = 1, kFlH = 2, kFlX = 3;   // flag kinds (H, X: per group; kind 0 is unused)
+static_assert(kSpb == 2 && kMaxG * kGW >= kUPG * kHPM && kMaxK + 1 <= kUPG * kNG, "grid shape");
+
+// Exchange regions (word offsets into the one tagged-word buffer).
+constexpr size_t kXLg = 0;                                      // [2][kLgRep][kMaxE] logits
+constexpr size_t kXSh = kXLg + size_t(2) * kLgRep * kMaxE;      // [2][kI] shared h
+constexpr size_t kXHx = kXSh + size_t(2) * kI;                  // [kNG][kUPG][kI] h of each group's routed units
+constexpr size_t kXPart = kXHx + size_t(kNG) * kUPG * kI;       // [2][kPartW] row sums by unit, then sigma
+constexpr size_t kXWords = kXPart + size_t(2) * kPartW;
 
 // Bytes of LDS per region, rounded so that 256-byte direct-load rounds that
 // run past a region's end land in its own padding.
@@ -76,50 +110,45 @@ __host__ __device__ constexpr uint32_t r256(uint32_t n) { return (n + 255u) / 25
 
 struct SLds {
   // static operands of one layer (two copies, by layer parity)
-  uint32_t p_x, p_rr, p_suq, p_susb, p_sdq, p_sdsb, p_slot, p_gv, p_bytes;
-  uint32_t p[2];
-  uint32_t d, d_per;   // routed down operands: [k][d_per] = codes [rb][256], scales [rb][8], biases [rb][8]
-  uint32_t hs;         // staged h [(k + 1) * kSegI][kPad] floats
-  uint32_t hsum;       // [(k + 1) * kSegI] segment sums
-  uint32_t lg;         // [kMaxE] logits
-  uint32_t cand;       // [kWave] packed top-k candidates (wave 0)
-  uint32_t misc;       // see below
-  uint32_t part;       // [(k + 1) * rb] partial down sums
+  uint32_t p_x, p_rr, p_suq, p_susb, p_slot, p_gv, p_bytes;
+  uint32_t d;      // [kUPG][kDPM rows]: codes [64][256 B], scales [64][16 B], biases [64][16 B]
+  uint32_t hs;     // [kUPG][kSegI][kPad] floats: h of the group's units, one after the other
+  uint32_t lg;     // [kMaxE] logits
+  uint32_t cand;   // [8 waves][16] top-k candidates
+  uint32_t misc;   // see below
+  uint32_t fin;    // [kMaxK + 1][kDPM] row sums being combined, then sigma
+  uint32_t xn;     // [kDPM] bf16 next-layer input rows (chained)
   uint32_t total;
 };
 
 // misc words (32-bit each)
-constexpr int kMIds = 0;              // [kMaxK] chosen experts by rank
-constexpr int kMVals = kMIds + kMaxK; // [kMaxK] chosen logits, then weights
-constexpr int kMSig = kMVals + kMaxK; // sigmoid(g . x)
-constexpr int kMOk = kMSig + 1;       // result of the last flag wait
-constexpr int kMRd = kMOk + 1;        // [kRdWaves] results of the reading waves
-constexpr int kMOff = 64;             // [kMaxK] int64 blob offsets by rank (8-byte aligned)
+constexpr int kMIds = 0;               // [kMaxK] chosen experts by rank
+constexpr int kMVals = 16;             // [2][kMaxK] chosen logits, then weights, by layer parity
+constexpr int kMSig = kMVals + 2 * kMaxK;   // sigmoid(g . x) of this layer (block 0)
+constexpr int kMOk = kMSig + 1;        // result of the last flag wait
+constexpr int kMFin = kMOk + 1;        // result of the finishing wave's reads
+constexpr int kMRd = kMFin + 1;        // [kRdWaves] results of the reading waves
+constexpr int kMOff = 64;              // [kMaxK] int64 blob offsets by rank (8-byte aligned)
 constexpr int kMWords = kMOff + 2 * kMaxK;
 
-__host__ __device__ inline SLds stack_lds(int E, int k, int rpb, int spb, int rb) {
+__host__ __device__ inline SLds stack_lds(int E, int rpb) {
   SLds s{};
   uint32_t o = 0;
   s.p_x = o;    o += r256(kH * 2);
   s.p_rr = o;   o += r256(static_cast<uint32_t>(rpb) * kH * 2);
-  s.p_suq = o;  o += r256(static_cast<uint32_t>(spb) * 2 * kRowQ);
-  s.p_susb = o; o += r256(static_cast<uint32_t>(spb) * 4 * (kH / 64) * 2);
-  s.p_sdq = o;  o += r256(static_cast<uint32_t>(rb) * kDRowQ);
-  s.p_sdsb = o; o += r256(static_cast<uint32_t>(rb) * 2 * kDRowSB);
+  s.p_suq = o;  o += r256(kSpb * 2 * kRowQ);
+  s.p_susb = o; o += r256(kSpb * 4 * (kH / 64) * 2);
   s.p_slot = o; o += r256(static_cast<uint32_t>(E) * 8);
   s.p_gv = o;   o += r256(kH * 2);
   s.p_bytes = o;
-  s.p[0] = 0;
-  s.p[1] = s.p_bytes;
   uint32_t t = 2 * s.p_bytes;
-  s.d_per = r256(static_cast<uint32_t>(rb) * (kDRowQ + 2 * kDRowSB));
-  s.d = t;      t += static_cast<uint32_t>(k) * s.d_per;
-  s.hs = t;     t += static_cast<uint32_t>(k + 1) * kSegI * kPad * 4;
-  s.hsum = t;   t += r256(static_cast<uint32_t>(k + 1) * kSegI * 4);
+  s.d = t;      t += kUPG * kDPM * kDRowB;
+  s.hs = t;     t += kUPG * kSegI * kPad * 4;
   s.lg = t;     t += kMaxE * 4;
-  s.cand = t;   t += kNW * kWave * 8;
+  s.cand = t;   t += kNW * kTopC * 8;
   s.misc = t;   t += r256(kMWords * 4);
-  s.part = t;   t += r256(static_cast<uint32_t>(k + 1) * rb * 4 + static_cast<uint32_t>(rb) * 2);
+  s.fin = t;    t += r256(((kMaxK + 1) * kDPM + 1) * 4);
+  s.xn = t;     t += r256(kDPM * 2);
   s.total = t;
   return s;
 }
@@ -133,6 +162,15 @@ typedef __attribute__((address_space(3))) uint16_t lds_w16;
 __device__ __forceinline__ void store_tag(uint64_t* p, uint32_t bits, uint32_t tag) {
   __hip_atomic_store(p, (static_cast<uint64_t>(tag) << 32) | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// One tagged word, read past this XCD's L2 (device scope).
+__device__ __forceinline__ uint64_t load_tag(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Tags only grow within a call and from call to call, so "at least" is a
+// signed difference (safe across wrap-around).
+__device__ __forceinline__ bool tag_ge(uint32_t f, uint32_t tag) { return static_cast<int32_t>(f - tag) >= 0; }
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -154,14 +192,12 @@ struct StackArgs {
   int64_t xc_stride;
   int32_t* ids_out;          // optional [L][k]
   float* wts_out;            // optional [L][k]
-  uint64_t* lg;              // [kLgRep][kMaxE] tagged logits
-  uint64_t* hx;              // [kHRep][kMaxHn] tagged h rows (ranks 0..k-1, shared), then the gate
-  uint64_t* xx;              // [kXRep][kH / 2] tagged next-layer input (two bf16 per word)
-  uint32_t* flags;           // [3][kFlagRep][kMaxNb] per-block exchange flags
+  uint64_t* xw;              // tagged words, regions at kX*
+  uint64_t* xx;              // [kNG][kH / 2] tagged next-layer input of each group (two bf16 per word)
+  uint32_t* flags;           // [4 kinds][kFlagRep][kNB] exchange flags
   uint32_t* ctrl;            // [0] error flags
   uint32_t* epochs;          // per-block call counters
-  int L, E, k, nb, rpb, spb, rb, gpb, hn;
-  int out_bf16;
+  int L, E, k, rpb;
   uint32_t spin_limit;
 };
 
@@ -175,18 +211,31 @@ __device__ __forceinline__ void copy_lds(u32x4 rs, uint8_t* dst, uint32_t src, u
     lds_load<W>(rs, dst + j, src + j + static_cast<uint32_t>(lane) * W, 0);
 }
 
+// n down rows from row r0 of the blob behind `rs` into LDS at D: codes
+// [n][256 B], then scales [n][16 B] and biases [n][16 B] (4-byte direct loads,
+// 256 bytes a round: n * 32 bytes is a whole number of rounds).
+__device__ __forceinline__ void copy_down_rows(u32x4 rs, uint8_t* D, int r0, int n, int lane) {
+  copy_lds<16>(rs, D, static_cast<uint32_t>(2 * kQ + r0 * kDRowQ), n * kDRowQ, lane);
+  const uint32_t per = static_cast<uint32_t>(n) * kDRowSB;
+  for (uint32_t j = 0; j < 2 * per; j += kWave * 4) {
+    const uint32_t q = j + static_cast<uint32_t>(lane) * 4;
+    const uint32_t plane = q / per, within = q - plane * per;
+    const uint32_t poff = static_cast<uint32_t>(3 * kQ + (plane == 0 ? 2 : 5) * kS);
+    lds_load<4>(rs, D + n * kDRowQ + j, poff + static_cast<uint32_t>(r0) * kDRowSB + within, 0);
+  }
+}
+
 // The static operands of layer l (those that do not depend on its routing)
-// into LDS copy `p`: its slot table, this block's router rows, shared
-// gate/up rows and shared down rows, the gate vector (block 0) and, unless
-// the input comes from the chain, x.  Issued by one wave; that wave waits for
-// them (s_waitcnt vmcnt(0)) before the barrier that precedes their use.
+// into LDS copy `p`: its slot table, this block's router rows and shared
+// gate/up rows, the gate vector (block 0) and, unless the input comes from
+// the chain, x.  Direct-to-LDS loads: cheap to request, slow to
+// land (few in flight per CU), so one wave requests them a layer ahead and
+// waits for them (s_waitcnt vmcnt(0)) only at the end of the layer.
 __device__ __forceinline__ void issue_static(const StackArgs& a, const SLds& S, uint8_t* lds, int p, int l,
                                              int lane) {
   uint8_t* P = lds + p * S.p_bytes;
   const int b = blockIdx.x;
-  // slot table
   copy_lds<16>(raw_rsrc(a.slots + l * a.s_stride, int64_t(a.E) * 8), P + S.p_slot, 0, a.E * 8, lane);
-  // router rows
   {
     const u32x4 rs = raw_rsrc(a.router + l * a.r_stride, int64_t(a.E) * kH * 2);
     for (int j = 0; j < a.rpb; ++j) {
@@ -196,17 +245,16 @@ __device__ __forceinline__ void issue_static(const StackArgs& a, const SLds& S, 
   }
   const uint8_t* sh = a.shared + l * a.sh_stride;
   const u32x4 rsh = raw_rsrc(sh, kBlob);
-  // shared gate/up rows r = b * spb + j: gate codes then up codes per unit
-  for (int j = 0; j < a.spb; ++j) {
-    const int r = b * a.spb + j;
-    if (r >= kI) continue;
+  // shared gate/up rows r = b * kSpb + j: gate codes then up codes per unit
+  for (int j = 0; j < kSpb; ++j) {
+    const int r = b * kSpb + j;
     copy_lds<16>(rsh, P + S.p_suq + (2 * j) * kRowQ, static_cast<uint32_t>(r) * kRowQ, kRowQ, lane);
     copy_lds<16>(rsh, P + S.p_suq + (2 * j + 1) * kRowQ, static_cast<uint32_t>(kQ + r * kRowQ), kRowQ, lane);
   }
-  // their scales and biases: [gate s, up s, gate b, up b][spb rows][32 groups] bf16
+  // their scales and biases: [gate s, up s, gate b, up b][kSpb rows][32 groups] bf16
   {
-    const uint32_t per = static_cast<uint32_t>(a.spb) * (kH / 64) * 2;   // bytes per plane
-    const uint32_t base = static_cast<uint32_t>(b * a.spb) * (kH / 64) * 2;
+    constexpr uint32_t per = kSpb * (kH / 64) * 2;   // bytes per plane
+    const uint32_t base = static_cast<uint32_t>(b * kSpb) * (kH / 64) * 2;
     for (uint32_t j = 0; j < 4 * per; j += kWave * 4) {
       const uint32_t q = j + static_cast<uint32_t>(lane) * 4;
       const uint32_t plane = q / per, within = q - plane * per;
@@ -214,75 +262,73 @@ __device__ __forceinline__ void issue_static(const StackArgs& a, const SLds& S, 
       lds_load<4>(rsh, P + S.p_susb + j, poff + base + within, 0);
     }
   }
-  // shared down rows [row_lo, row_lo + rb): codes, then [scales | biases]
-  {
-    const int row_lo = b * a.rb;
-    copy_lds<16>(rsh, P + S.p_sdq, static_cast<uint32_t>(2 * kQ + row_lo * kDRowQ), a.rb * kDRowQ, lane);
-    const uint32_t per = static_cast<uint32_t>(a.rb) * kDRowSB;
-    for (uint32_t j = 0; j < 2 * per; j += kWave * 4) {
-      const uint32_t q = j + static_cast<uint32_t>(lane) * 4;
-      const uint32_t plane = q / per, within = q - plane * per;
-      const uint32_t poff = static_cast<uint32_t>(3 * kQ + (plane == 0 ? 2 : 5) * kS);
-      lds_load<4>(rsh, P + S.p_sdsb + j, poff + static_cast<uint32_t>(row_lo) * kDRowSB + within, 0);
-    }
-  }
   if (b == 0) copy_lds<16>(raw_rsrc(sh + a.gv_off, kH * 2), P + S.p_gv, 0, kH * 2, lane);
   if (l == 0 || a.x_chain == nullptr)
     copy_lds<16>(raw_rsrc(a.x + l * a.x_stride, kH * 2), P + S.p_x, 0, kH * 2, lane);
 }
 
-// The routed down operands of this block's rows: for rank i, rows
-// [row_lo, row_lo + rb) of expert ids[i]'s down matrix (codes, scales,
-// biases).  An unusable blob offset reads zeros.
-__device__ __forceinline__ void issue_down(const StackArgs& a, const SLds& S, uint8_t* lds, int lane) {
-  const lds_i64* roff = (const lds_i64*)(reinterpret_cast<lds_w32*>((lds_w32*)(lds + S.misc)) + kMOff);
-  const int row_lo = blockIdx.x * a.rb;
-  const uint32_t per = static_cast<uint32_t>(a.rb) * kDRowSB;
-  for (int i = 0; i < a.k; ++i) {
-    const int64_t off = roff[i];
-    const bool ok = slot_ok(off, kBlob, a.pool_bytes);
-    const u32x4 rs = raw_rsrc(a.pool + (ok ? off : 0), ok ? kBlob : 0);
-    uint8_t* D = lds + S.d + i * S.d_per;
-    copy_lds<16>(rs, D, static_cast<uint32_t>(2 * kQ + row_lo * kDRowQ), a.rb * kDRowQ, lane);
-    for (uint32_t j = 0; j < 2 * per; j += kWave * 4) {
-      const uint32_t q = j + static_cast<uint32_t>(lane) * 4;
-      const uint32_t plane = q / per, within = q - plane * per;
-      const uint32_t poff = static_cast<uint32_t>(3 * kQ + (plane == 0 ? 2 : 5) * kS);
-      lds_load<4>(rs, D + a.rb * kDRowQ + j, poff + static_cast<uint32_t>(row_lo) * kDRowSB + within, 0);
-    }
+// Blob of unit u (a routed rank below k, else the shared expert) and whether
+// its offset is usable; an unusable blob reads zeros.
+__device__ __forceinline__ const uint8_t* unit_blob(const StackArgs& a, const lds_w32* misc, int u, int l, bool& ok) {
+  if (u >= a.k) {
+    ok = true;
+    return a.shared + l * a.sh_stride;
+  }
+  const int64_t off0 = ((const lds_i64*)(misc + kMOff))[u];
+  const int64_t off = (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(off0 >> 32))) << 32) |
+                      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(off0)));
+  ok = slot_ok(off, kBlob, a.pool_bytes);
+  return a.pool + (ok ? off : 0);
+}
+
+// The down rows [64 m, 64 m + 64) of each unit of the group (codes, scales,
+// biases) into LDS.
+__device__ __forceinline__ void issue_down(const StackArgs& a, const SLds& S, uint8_t* lds, const lds_w32* misc,
+                                           int grp, int mem, int nu, int l, int lane) {
+  for (int s = 0; s < nu; ++s) {
+    bool ok;
+    const uint8_t* blob = unit_blob(a, misc, grp + kNG * s, l, ok);
+    copy_down_rows(raw_rsrc(blob, ok ? kBlob : 0), lds + S.d + s * kDPM * kDRowB, mem * kDPM, kDPM, lane);
   }
 }
 
-// Exchanges.  A producer block stores its words (value bits and the layer's
-// tag), then, once every wave of the block has issued them (the caller's
-// barrier), raises its flag: the tag in every copy of the block's flag word.
-// A reader polls the flags of all blocks with one wave (1 KB per try), then
-// reads the words once; a flag may be seen before the words it follows, so a
-// word with an older tag is read again.  Polling the flags instead of the
-// words keeps the traffic of waiting blocks small while the other blocks
-// still stream their operands.  Every wait is bounded.
+// Flags.  Grid-wide kinds: a block writes its tag into every replica; a
+// reader's wave 0 polls the 256 flags of replica b % 16 (1 KB per try).  Group
+// kinds: one copy, block (g, m) at 32 g + m, so a group's flags (or four
+// groups' flags) are contiguous.  A wait ends when every flag is at least the
+// tag, so a block already a layer ahead never holds it up.
 __device__ __forceinline__ void raise_flag(const StackArgs& a, int kind, uint32_t tag, int wave, int lane) {
   if (wave == 0 && lane < kFlagRep)
-    __hip_atomic_store(a.flags + (kind * kFlagRep + lane) * kMaxNb + blockIdx.x, tag, __ATOMIC_RELAXED,
+    __hip_atomic_store(a.flags + (kind * kFlagRep + lane) * kNB + blockIdx.x, tag, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// True once every block's flag of `kind` carries `tag`; false on expiry (or
-// when an earlier wait expired).
-__device__ __forceinline__ bool wait_flags(const StackArgs& a, int kind, uint32_t tag, bool dead, lds_w32* misc,
-                                           int wave, int lane) {
+__device__ __forceinline__ void raise_group_flag(const StackArgs& a, int kind, uint32_t tag, int grp, int mem,
+                                                 int wave, int lane) {
+  if (wave == 0 && lane == 0)
+    __hip_atomic_store(a.flags + kind * kFlagRep * kNB + grp * kNM + mem, tag, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// True once every flag of the set carries at least `tag`; false on expiry (or
+// when an earlier wait expired).  Grid-wide kinds (g0 < 0) poll all 256 flags
+// of the block's replica; group kinds the n flags from group g0 on.
+__device__ __forceinline__ bool wait_flags(const StackArgs& a, int kind, uint32_t tag, int g0, int n, bool dead,
+                                           lds_w32* misc, int wave, int lane) {
   if (wave == 0) {
     bool ok = !dead;
     if (ok) {
-      const uint32_t* r = a.flags + (kind * kFlagRep + blockIdx.x % kFlagRep) * kMaxNb;
+      const uint32_t* r = g0 >= 0 ? a.flags + kind * kFlagRep * kNB + g0 * kNM
+                                  : a.flags + (kind * kFlagRep + blockIdx.x % kFlagRep) * kNB;
+      if (g0 < 0) n = kNB;
       const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(r), 0, kMaxNb * 4, 0x00020000);
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(r), 0, n * 4, 0x00020000);
       for (uint32_t spins = 0;; ++spins) {
         bool all = true;
-        for (int j = lane * 4; j < a.nb; j += kWave * 4) {   // scope of device (sc1)
-          const u32x4 f = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, j * 4, 0, 16));
+        if (lane * 4 < n) {   // scope of device (sc1)
+          const u32x4 f = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, 0, 16));
 #pragma unroll
-          for (int q = 0; q < 4; ++q) all = all && (j + q >= a.nb || f[q] == tag);
+          for (int q = 0; q < 4; ++q) all = all && tag_ge(f[q], tag);
         }
         if (__ballot(!all) == 0) break;
         if (spins >= a.spin_limit) { ok = false; break; }
@@ -295,29 +341,23 @@ __device__ __forceinline__ bool wait_flags(const StackArgs& a, int kind, uint32_
   return misc[kMOk] != 0u;
 }
 
-// The n tagged words at `src` (thread t of the first nthr takes words
-// t + q nthr, q < PER), read until each carries `tag`; put(i, bits) stores
-// word i's value.  Run by the reading waves only, under a branch on the wave
-// index, with no barrier inside: the copy waves, whose direct loads are still
-// in flight, must never execute the wait that follows these loads.  False on
+// Tagged words read by nthr threads: word i (reader rt takes i = rt + q nthr,
+// q < PER) at addr(i), read until it carries `tag`; put(i, bits) stores its
+// value.  Run by the reading waves only, under a branch on the wave index,
+// with no barrier inside: the copy waves, whose direct loads are still in
+// flight, must never execute the wait that follows these loads.  False on
 // expiry.
-template <int PER, typename F>
-__device__ __forceinline__ bool read_tagged(const uint64_t* src, int n, int nthr, uint32_t tag, uint32_t limit,
-                                            F&& put) {
-  const int tid = threadIdx.x;
+template <int PER, typename A, typename F>
+__device__ __forceinline__ bool read_tagged(int rt, int n, int nthr, uint32_t tag, uint32_t limit, A&& addr, F&& put) {
+  const int tid = rt;
   uint32_t need = 0;
 #pragma unroll
   for (int q = 0; q < PER; ++q)
     if (tid + q * nthr < n) need |= 1u << q;
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t*>(src), 0, n * 8, 0x00020000);
   for (uint32_t spins = 0;; ++spins) {
     uint64_t w[PER];
 #pragma unroll
-    for (int q = 0; q < PER; ++q)   // scope of device (sc1): past this XCD's L2, where the writers' stores went
-      w[q] = (need >> q) & 1u
-                 ? __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rs, (tid + q * nthr) * 8, 0, 16))
-                 : 0ull;
+    for (int q = 0; q < PER; ++q) w[q] = (need >> q) & 1u ? load_tag(addr(tid + q * nthr)) : 0ull;
 #pragma unroll
     for (int q = 0; q < PER; ++q)
       if (((need >> q) & 1u) && static_cast<uint32_t>(w[q] >> 32) == tag) {
@@ -338,21 +378,147 @@ __device__ __forceinline__ bool reads_ok(const lds_w32* misc) {
   return ok;
 }
 
+// Block-wide top-k.  Keys are (order key of the logit << 32 | ~id), so a
+// larger key is a larger logit, then a lower id (ties to the lower id); an
+// absent entry is 0 and every real one is at least 1 << 32.
+//
+// The value of lane (lane ^ S) within the wave.
+template <int S>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int lane) {
+  if constexpr (S == 1) {
+    return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xf, 0xf, false);   // quad_perm [1, 0, 3, 2]
+  } else if constexpr (S == 2) {
+    return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xf, 0xf, false);   // quad_perm [2, 3, 0, 1]
+  } else if constexpr (S == 4) {
+    return __builtin_amdgcn_ds_swizzle(v, 0x1F | (4 << 10));     // bit mode, xor 4
+  } else if constexpr (S == 8) {
+    return __builtin_amdgcn_mov_dpp(v, 0x128, 0xf, 0xf, false);  // row_ror:8 (xor 8 within a row)
+  } else if constexpr (S == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
+
+// One compare-exchange step of a bitonic sort of the wave's 64 keys into
+// descending lane order: blocks of SIZE lanes, partner at distance S.
+template <int SIZE, int S>
+__device__ __forceinline__ void bitonic_step(uint64_t& key, int lane) {
+  const uint32_t plo = lane_xor<S>(static_cast<uint32_t>(key), lane);
+  const uint32_t phi = lane_xor<S>(static_cast<uint32_t>(key >> 32), lane);
+  const uint64_t pk = (static_cast<uint64_t>(phi) << 32) | plo;
+  const bool desc = (lane & SIZE) == 0;        // this block's direction (all of them for SIZE = 64)
+  const bool lower = (lane & S) == 0;
+  if ((pk > key) == (lower == desc)) key = pk;   // the lower lane keeps the larger key in a descending block
+}
+
+template <int SIZE>
+__device__ __forceinline__ void bitonic_merge(uint64_t& key, int lane) {
+  if constexpr (SIZE >= 64) bitonic_step<SIZE, 32>(key, lane);
+  if constexpr (SIZE >= 32) bitonic_step<SIZE, 16>(key, lane);
+  if constexpr (SIZE >= 16) bitonic_step<SIZE, 8>(key, lane);
+  if constexpr (SIZE >= 8) bitonic_step<SIZE, 4>(key, lane);
+  if constexpr (SIZE >= 4) bitonic_step<SIZE, 2>(key, lane);
+  bitonic_step<SIZE, 1>(key, lane);
+}
+
+__device__ __forceinline__ uint64_t bitonic_sort64(uint64_t key, int lane) {
+  bitonic_merge<2>(key, lane);
+  bitonic_merge<4>(key, lane);
+  bitonic_merge<8>(key, lane);
+  bitonic_merge<16>(key, lane);
+  bitonic_merge<32>(key, lane);
+  bitonic_merge<64>(key, lane);
+  return key;
+}
+
+// Unchained: one wave finishes rows [8 b, 8 b + 8) of layer lf, the ordered
+// combine of the row sums of every unit (tag `tg`) with the weights of that
+// layer.  False if a word never arrived.
+template <int OUT>
+__device__ __forceinline__ bool finish_rows(const StackArgs& a, const SLds& S, uint8_t* lds, int lf, uint32_t tg,
+                                            int lane) {
+  const lds_w32* misc = (const lds_w32*)(lds + S.misc);
+  lds_f32* fin = (lds_f32*)(lds + S.fin);
+  const uint64_t* part = a.xw + kXPart + static_cast<size_t>(lf & 1) * kPartW;
+  const int k = a.k, row0 = blockIdx.x * kFR;
+  const int n = (k + 1) * kFR + 1;   // row sums of every unit, then sigma
+  uint32_t need = 0;
+  for (int q = 0; q < 2; ++q)
+    if (lane + q * kWave < n) need |= 1u << q;
+  for (uint32_t spins = 0;; ++spins) {
+    uint64_t w[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int i = lane + q * kWave;
+      const size_t at = i < n - 1 ? static_cast<size_t>(i / kFR) * kH + row0 + i % kFR : static_cast<size_t>(kSigW);
+      w[q] = (need >> q) & 1u ? load_tag(part + at) : 0ull;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (((need >> q) & 1u) && static_cast<uint32_t>(w[q] >> 32) == tg) {
+        fin[lane + q * kWave] = __uint_as_float(static_cast<uint32_t>(w[q]));
+        need &= ~(1u << q);
+      }
+    if (__ballot(need != 0u) == 0) break;
+    if (spins >= a.spin_limit) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  wave_sync_lds();
+  if (lane < kFR) {
+    const lds_f32* vals = (const lds_f32*)(misc + kMVals + (lf & 1) * kMaxK);
+    float acc = 0.f;
+    for (int i = 0; i < k; ++i) acc = fmaf(vals[i], fin[i * kFR + lane], acc);
+    acc = fmaf(fin[n - 1], fin[k * kFR + lane], acc);
+    uint8_t* o = a.out + lf * a.out_stride;
+    if constexpr (OUT == kF32) reinterpret_cast<float*>(o)[row0 + lane] = acc;
+    else reinterpret_cast<uint16_t*>(o)[row0 + lane] = f32_to_bf16(acc);
+  }
+  return true;
+}
+
+// One pass of four down rows: LDS rows lr (this lane's row, lane / 16 of
+// the pass) of the nrow staged at Dq (codes, then scales, then biases), the
+// lane's segment lane % 16 against its h segment hv (sum hsv).  Every lane of
+// the row ends with the row's sum.
+__device__ __forceinline__ float down_row(const uint8_t* Dq, int nrow, int lr, int seg, const float (&hv)[1][kSegCodes],
+                                          float hsv) {
+  const lds_w16* sbw = (const lds_w16*)(Dq + nrow * kDRowQ);
+  Seg<4> code;
+  code.w[0] = *(const lds_u32x4*)((const lds_u8*)(Dq) + lr * kDRowQ + 16 * seg);
+  const int gi = lr * (kI / 64) + seg / 2;
+  const float sc = bf16_to_f32(sbw[gi]);
+  const float bi = bf16_to_f32(sbw[nrow * (kI / 64) + gi]);
+  float qv[1];
+  seg_qdot_nt<4, 1>(code, hv, qv);
+  float acc = 0.f;
+  acc += seg_value(sc, bi, qv[0], hsv);
+  return group_sum(acc, kSegI);
+}
+
 template <int OUT>
 __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
-  const SLds S = stack_lds(a.E, a.k, a.rpb, a.spb, a.rb);
+  const SLds S = stack_lds(a.E, a.rpb);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int b = blockIdx.x;
+  const int grp = b % kNG, mem = b / kNG;
   const int E = a.E, k = a.k;
   lds_w32* misc = (lds_w32*)(lds + S.misc);
   float* const lg = reinterpret_cast<float*>(lds + S.lg);
   const uint32_t epoch = a.epochs[b];
   bool dead = false;
-  bool bad = false;   // a routed blob offset was unusable (its pair contributes nothing)
+  bool bad = false;   // a routed blob offset was unusable (its unit contributes nothing)
+  // units of this group: g and g + 8 up to k (k is the shared expert); the
+  // routed ones (below k) come first
+  const int nu = (grp <= k ? 1 : 0) + (grp + kNG <= k ? 1 : 0);
+  const int nr = (grp < k ? 1 : 0) + (grp + kNG < k ? 1 : 0);
 
+  if (tid == 0) misc[kMFin] = 1u;
   if (wave == kWaveStatic) {
     issue_static(a, S, lds, 0, 0, lane);
     wait_vm0();
@@ -361,16 +527,19 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
 
   for (int l = 0; l < a.L; ++l) {
     const uint32_t tag = epoch + 1u + static_cast<uint32_t>(l);
-    const int p = l & 1;
-    uint8_t* P = lds + p * S.p_bytes;
+    const int p = l & 1;                                     // copy of the exchange regions
+    uint8_t* P = lds + p * S.p_bytes;                        // this layer's static operands
     const uint8_t* xl = P + S.p_x;                           // this layer's input (bf16)
+    uint64_t* const lgw = a.xw + kXLg + static_cast<size_t>(p) * kLgRep * kMaxE;
+    uint64_t* const shw = a.xw + kXSh + static_cast<size_t>(p) * kI;
+    uint64_t* const part = a.xw + kXPart + static_cast<size_t>(p) * kPartW;
 
     // ------------------------------------------------------------------ R
     // per lane: its 32-value segment of x (lane = segment for H = 2048)
     ActRaw<kBF16> xr;
     load_lds_act_bf16(xl, lane, xr);
     const float xs = xsum_bf16(xr);
-    for (int j = wave; j < a.rpb + a.spb; j += kNW) {
+    for (int j = wave; j < a.rpb + kSpb; j += kNW) {
       if (j < a.rpb) {
         const int e = b * a.rpb + j;
         if (e >= E) continue;
@@ -383,15 +552,14 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
 #pragma unroll
         for (int c = 0; c < kSegCodes; ++c) acc = fmaf(v[c], r[c], acc);
         acc = group_sum(acc, kWave);
-        if (lane < kLgRep) store_tag(a.lg + static_cast<size_t>(lane) * kMaxE + e, __float_as_uint(acc), tag);
+        if (lane < kLgRep) store_tag(lgw + static_cast<size_t>(lane) * kMaxE + e, __float_as_uint(acc), tag);
       } else {
         const int u = j - a.rpb;
-        const int r = b * a.spb + u;
-        if (r >= kI) continue;
+        const int r = b * kSpb + u;
         Seg<4> cg, cu;
         cg.w[0] = *(const lds_u32x4*)((const lds_u8*)(P + S.p_suq + (2 * u) * kRowQ) + 16 * lane);
         cu.w[0] = *(const lds_u32x4*)((const lds_u8*)(P + S.p_suq + (2 * u + 1) * kRowQ) + 16 * lane);
-        const uint32_t per = static_cast<uint32_t>(a.spb) * (kH / 64);   // bf16 values per plane
+        constexpr uint32_t per = kSpb * (kH / 64);   // bf16 values per plane
         const lds_w16* sb = (const lds_w16*)(P + S.p_susb);
         const int gi = u * (kH / 64) + lane / 2;
         const float sg = bf16_to_f32(sb[gi]), su = bf16_to_f32(sb[per + gi]);
@@ -403,11 +571,11 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
         float g, uu;
         gu_sums_w<kWave>(accg, accu, kWave, g, uu);
         const float h = silu(g) * uu;
-        if (lane < kHRep) store_tag(a.hx + static_cast<size_t>(lane) * kMaxHn + k * kI + r, __float_as_uint(h), tag);
+        if (lane == 0) store_tag(shw + r, __float_as_uint(h), tag);
       }
     }
     if (b == 0 && wave == kNW - 1) {
-      // sigmoid(g . x), as the staged path forms it
+      // sigmoid(g . x), as the staged path forms it; stored with the row sums
       float acc = 0.f;
       {
         float xv[kSegCodes], gv[kSegCodes];
@@ -419,218 +587,254 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
         for (int c = 0; c < kSegCodes; ++c) acc = fmaf(xv[c], gv[c], acc);
       }
       acc = group_sum(acc, kWave);
-      const float sgm = sigmoid(acc);
-      if (lane < kHRep) store_tag(a.hx + static_cast<size_t>(lane) * kMaxHn + (k + 1) * kI, __float_as_uint(sgm), tag);
+      if (lane == 0) misc[kMSig] = __float_as_uint(sigmoid(acc));
     }
 
     // ------------------------------------------------------------------ K
+    // The logits are read as words, without a flag wait: every block's R
+    // ends at about the same time and the memory is quiet here, so one
+    // round trip (then another for any word still old) beats waiting for a
+    // flag and then reading.
     __syncthreads();                 // every wave's logit stores are issued
-    raise_flag(a, kFlLg, tag, wave, lane);
     {
-      bool ok = wait_flags(a, kFlLg, tag, dead, misc, wave, lane);
+      const bool ok = !dead;
       if (ok && wave < kRdWaves) {
+        const uint64_t* src = lgw + static_cast<size_t>(b % kLgRep) * kMaxE;
         const bool r = read_tagged<(kMaxE + kRdThr - 1) / kRdThr>(
-            a.lg + static_cast<size_t>(b % kLgRep) * kMaxE, E, kRdThr, tag, a.spin_limit,
+            tid, E, kRdThr, tag, a.spin_limit, [&](int i) { return src + i; },
             [&](int i, uint32_t bits) { ((lds_f32*)(lg))[i] = __uint_as_float(bits); });
         if (lane == 0) misc[kMRd + wave] = r ? 1u : 0u;
       }
       __syncthreads();
       dead = dead || !(ok && reads_ok(misc));
     }
-    // top-k on wave 0 (the staged kernels' wave top-k: a bound from the lane
-    // maxima, the candidates above it ranked exactly, the weights in rank
-    // order), then the chosen experts' blob offsets; one barrier for all
+    // top-k on wave 0 (a bound from the lane maxima, the candidates above it
+    // ranked exactly, the weights in rank order), then the chosen experts'
+    // blob offsets; meanwhile wave 1 finishes the previous layer's rows
     if (wave == 0) {
       topk_wave_n<8>(lg, E, k, lane, reinterpret_cast<uint64_t*>(lds + S.cand),
                      reinterpret_cast<int32_t*>(reinterpret_cast<uint32_t*>(lds + S.misc) + kMIds),
-                     reinterpret_cast<float*>(reinterpret_cast<uint32_t*>(lds + S.misc) + kMVals));
+                     reinterpret_cast<float*>(reinterpret_cast<uint32_t*>(lds + S.misc) + kMVals + p * kMaxK));
       const lds_i64* slot = (const lds_i64*)(P + S.p_slot);
       if (lane < k) {
         const int e = static_cast<int>(misc[kMIds + lane]);
         ((lds_i64*)(misc + kMOff))[lane] = slot[e];
         if (b == 0) {
           if (a.ids_out) a.ids_out[static_cast<size_t>(l) * k + lane] = e;
-          if (a.wts_out) a.wts_out[static_cast<size_t>(l) * k + lane] = __uint_as_float(misc[kMVals + lane]);
+          if (a.wts_out) a.wts_out[static_cast<size_t>(l) * k + lane] = __uint_as_float(misc[kMVals + p * kMaxK + lane]);
         }
+      }
+    } else if (wave == kWaveFin) {
+      if (l > 0 && !a.x_chain && !dead) {
+        const bool r = finish_rows<OUT>(a, S, lds, l - 1, tag - 1u, lane);
+        if (lane == 0) misc[kMFin] = r ? 1u : 0u;
       }
     }
     __syncthreads();
+    dead = dead || misc[kMFin] == 0u;
 
     // ------------------------------------------------------------------ G
     {
-      const int g0 = b * a.gpb;
-      const int g1 = min(g0 + a.gpb, k * kI);
-      const lds_i64* roff = (const lds_i64*)(misc + kMOff);
+      // waves 0..5: the row pairs [16 m, 16 m + 16) of one routed unit each;
+      // with two routed units waves 0..2 take the first and 3..5 the second
+      // (pairs w % 3 + 3 i), with one every sixth pair from w.  One
+      // descriptor per wave, every load requested before any compute.
+      const int s = nr == 2 ? wave / 3 : 0;
+      const int q0 = mem * kHPM + (nr == 2 ? wave % 3 : wave);
+      const int qs = nr == 2 ? 3 : kGW;
+      const bool gw = wave < kGW && s < nr;
+      const int npw = gw ? (kHPM - (q0 - mem * kHPM) + qs - 1) / qs : 0;   // this wave's pairs
       Seg<4> cg[kMaxG], cu[kMaxG];
       uint32_t sg[kMaxG], su[kMaxG], bg[kMaxG], bu[kMaxG];
-      bool live[kMaxG], vv[kMaxG];
-      int ii[kMaxG], rr[kMaxG];
-      if (wave < kGW) {
+      bool vv = false;
+      if (gw) {
+        bool ok;
+        const uint8_t* blob = unit_blob(a, misc, grp + kNG * s, l, ok);
+        vv = ok;
+        if (!ok) bad = true;
+        // one descriptor over the blob (an unusable one reads zeros); the
+        // plane offsets go in the scalar offset, the lane's in the vector one
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blob), 0, ok ? static_cast<int>(kBlob) : 0, 0x00020000);
 #pragma unroll
         for (int j = 0; j < kMaxG; ++j) {
-          const int u0 = g0 + wave + kGW * j;
-          live[j] = u0 < g1;
-          const int u = live[j] ? u0 : g0;
-          ii[j] = u / kI;
-          rr[j] = u % kI;
-          const int64_t off0 = roff[ii[j]];
-          const int64_t off = (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(off0 >> 32))) << 32) |
-                              static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(off0)));
-          vv[j] = slot_ok(off, kBlob, a.pool_bytes);
-          if (live[j] && !vv[j]) bad = true;
-          // one descriptor over the blob (an unusable one reads zeros); the
-          // plane offsets go in the scalar offset, the lane's in the vector one
-          const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-              const_cast<uint8_t*>(a.pool + (vv[j] ? off : 0)), 0, vv[j] ? static_cast<int>(kBlob) : 0, 0x00020000);
-          const int qo = rr[j] * kRowQ + 16 * lane;
-          cg[j].w[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, qo, 0, 2));
-          cu[j].w[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, qo, kQ, 2));
-          const int si = (rr[j] * (kH / 64) + lane / 2) * 2;
-          sg[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, si, 3 * kQ, 0);
-          su[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, si, 3 * kQ + kS, 0);
-          bg[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, si, 3 * kQ + 3 * kS, 0);
-          bu[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, si, 3 * kQ + 4 * kS, 0);
+          cg[j].w[0] = u32x4{0u, 0u, 0u, 0u};
+          cu[j].w[0] = u32x4{0u, 0u, 0u, 0u};
+          sg[j] = su[j] = bg[j] = bu[j] = 0u;
+          if (j < npw) {
+            const int rr = q0 + qs * j;
+            const int qo = rr * kRowQ + 16 * lane;
+            cg[j].w[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, qo, 0, 2));
+            cu[j].w[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, qo, kQ, 2));
+            const int si = (rr * (kH / 64) + lane / 2) * 2;
+            sg[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, si, 3 * kQ, 0);
+            su[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, si, 3 * kQ + kS, 0);
+            bg[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, si, 3 * kQ + 3 * kS, 0);
+            bu[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, si, 3 * kQ + 4 * kS, 0);
+          }
         }
       }
       __syncthreads();   // the down copies start after every phase-G load is requested
-      if (wave < kGW) {
+      if (gw) {
+        uint64_t* const hx = a.xw + kXHx + (static_cast<size_t>(grp) * kUPG + s) * kI;
+        // two pairs at a time, with no branch between them
 #pragma unroll
-        for (int j = 0; j < kMaxG; ++j) {
-          if (!live[j]) continue;
-          const QPairs pg = qpairs_bf16(cg[j]), pu = qpairs_bf16(cu[j]);
-          float accg = 0.f, accu = 0.f;
-          accg += seg_value_d2(raw_value<kBF16>(sg[j]), raw_value<kBF16>(bg[j]), dot2_seg(pg, xr), xs);
-          accu += seg_value_d2(raw_value<kBF16>(su[j]), raw_value<kBF16>(bu[j]), dot2_seg(pu, xr), xs);
-          float g, uu;
-          gu_sums_w<kWave>(accg, accu, kWave, g, uu);
-          const float h = vv[j] ? silu(g) * uu : 0.f;
-          if (lane < kHRep)
-            store_tag(a.hx + static_cast<size_t>(lane) * kMaxHn + ii[j] * kI + rr[j], __float_as_uint(h), tag);
+        for (int j = 0; j < kMaxG; j += 2) {
+          if (j < npw) {
+            float g[2], uu[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const QPairs pg = qpairs_bf16(cg[j + t]), pu = qpairs_bf16(cu[j + t]);
+              float accg = 0.f, accu = 0.f;
+              accg += seg_value_d2(raw_value<kBF16>(sg[j + t]), raw_value<kBF16>(bg[j + t]), dot2_seg(pg, xr), xs);
+              accu += seg_value_d2(raw_value<kBF16>(su[j + t]), raw_value<kBF16>(bu[j + t]), dot2_seg(pu, xr), xs);
+              gu_sums_w<kWave>(accg, accu, kWave, g[t], uu[t]);
+            }
+            const float h0 = vv ? silu(g[0]) * uu[0] : 0.f;
+            const float h1 = vv ? silu(g[1]) * uu[1] : 0.f;
+            if (lane == 0) {
+              store_tag(hx + q0 + qs * j, __float_as_uint(h0), tag);
+              if (j + 1 < npw) store_tag(hx + q0 + qs * (j + 1), __float_as_uint(h1), tag);
+            }
+          }
         }
+      } else if (wave == kWaveStatic) {
+        // the next layer's static operands into the other copy, free since
+        // the layer before this one ended (waited for at the end of this one)
+        if (l + 1 < a.L) issue_static(a, S, lds, p ^ 1, l + 1, lane);
       } else if (wave == kWaveDown) {
-        issue_down(a, S, lds, lane);
-      } else if (wave == kWaveStatic && l + 1 < a.L) {
-        // the next layer's static operands: into the other copy, free since
-        // the layer before this one ended
-        issue_static(a, S, lds, p ^ 1, l + 1, lane);
+        issue_down(a, S, lds, misc, grp, mem, nu, l, lane);
       }
     }
 
     // ------------------------------------------------------------------ H
     __syncthreads();                 // every wave's h stores are issued
-    raise_flag(a, kFlH, tag, wave, lane);
+    raise_group_flag(a, kFlH, tag, grp, mem, wave, lane);
     if (wave == kWaveDown) wait_vm0();
     {
       float* hs = reinterpret_cast<float*>(lds + S.hs);
-      const int nh = (k + 1) * kI + 1;
-      // waves 0..5 read (wave 6 still has the static copies in flight)
-      bool ok = wait_flags(a, kFlH, tag, dead, misc, wave, lane);
+      // the group's flags; waves 0..5 read (wave 6 still has the static
+      // copies in flight) h of the group's units: routed ones from the group,
+      // the shared one from phase R
+      bool ok = wait_flags(a, kFlH, tag, grp, kNM, dead, misc, wave, lane);
       if (ok && wave < kRdWaves) {
-        const bool r = read_tagged<(kMaxHn + kRdThr - 1) / kRdThr>(
-            a.hx + static_cast<size_t>(b % kHRep) * kMaxHn, nh, kRdThr, tag, a.spin_limit, [&](int i, uint32_t bits) {
-              if (i < (k + 1) * kI) {
-                const int row = i / kI, c = i % kI;
-                ((lds_f32*)(hs))[(row * kSegI + c / kSegCodes) * kPad + c % kSegCodes] = __uint_as_float(bits);
-              } else {
-                misc[kMSig] = bits;
-              }
+        const uint64_t* hx = a.xw + kXHx + static_cast<size_t>(grp) * kUPG * kI;
+        const bool r = read_tagged<(kUPG * kI + kRdThr - 1) / kRdThr>(
+            tid, nu * kI, kRdThr, tag, a.spin_limit,
+            [&](int i) {
+              const int s = i / kI, c = i % kI;
+              return grp + kNG * s < k ? hx + static_cast<size_t>(s) * kI + c : shw + c;
+            },
+            [&](int i, uint32_t bits) {
+              const int s = i / kI, c = i % kI;
+              ((lds_f32*)(hs))[((s * kSegI) + c / kSegCodes) * kPad + c % kSegCodes] = __uint_as_float(bits);
             });
         if (lane == 0) misc[kMRd + wave] = r ? 1u : 0u;
       }
       __syncthreads();
       dead = dead || !(ok && reads_ok(misc));
-      // segment sums of the staged rows, in the order seg_sum uses
-      float* hsum = reinterpret_cast<float*>(lds + S.hsum);
-      for (int j = tid; j < (k + 1) * kSegI; j += kThr) {
-        float v[kSegCodes];
-        load_lds_seg(hs + static_cast<size_t>(j) * kPad, 0, v);
-        ((lds_f32*)(hsum))[j] = seg_sum(v);
-      }
-      __syncthreads();
     }
 
     // ------------------------------------------------------------------ D
-    {
-      const int row_lo = b * a.rb;
-      const int npass = a.rb / kRpp;
-      const int ntask = (k + 1) * npass;
+    if (nu > 0 && !dead) {
+      // wave w: unit w * nu / 8, rows [row0, row0 + 8 nu) of it, four per pass;
+      // lane: segment lane % 16 of row lane / 16 of the pass, its h segment
+      // and that segment's sum held in registers for every pass
+      const int s = wave * nu / kNW;
+      const int u = grp + kNG * s;
+      const int npass = 2 * nu;
+      const int row0 = (wave % (kNW / nu)) * npass * kRpp;
       const int sub = lane / kSegI, seg = lane % kSegI;
-      const lds_i64* roff = (const lds_i64*)(misc + kMOff);
+      bool valid = true;
+      if (u < k) (void)unit_blob(a, misc, u, l, valid);
       const float* hs = reinterpret_cast<const float*>(lds + S.hs);
-      const float* hsum = reinterpret_cast<const float*>(lds + S.hsum);
-      float* part = reinterpret_cast<float*>(lds + S.part);
-      for (int t = wave; t < ntask; t += kNW) {
-        const int i = t / npass, pp = t % npass;
-        const int rloc = pp * kRpp + sub;
-        const uint8_t* base = i < k ? lds + S.d + i * S.d_per : nullptr;
-        const uint8_t* q8 = i < k ? base : P + S.p_sdq;
-        const uint8_t* sb8 = i < k ? base + a.rb * kDRowQ : P + S.p_sdsb;
-        Seg<4> code;
-        code.w[0] = *(const lds_u32x4*)((const lds_u8*)(q8) + rloc * kDRowQ + 16 * seg);
-        const lds_w16* sbw = (const lds_w16*)(sb8);
-        const int gi = rloc * (kI / 64) + seg / 2;
-        const float sc = bf16_to_f32(sbw[gi]);
-        const float bi = bf16_to_f32(sbw[a.rb * (kI / 64) + gi]);
-        float hv[1][kSegCodes];
-        load_lds_seg(hs + (static_cast<size_t>(i) * kSegI + seg) * kPad, 0, hv[0]);
-        const float hsv = ((const lds_f32*)(hsum))[i * kSegI + seg];
-        float qv[1];
-        seg_qdot_nt<4, 1>(code, hv, qv);
-        float acc = 0.f;
-        acc += seg_value(sc, bi, qv[0], hsv);
-        const float v = group_sum(acc, kSegI);
-        const bool valid = i == k || slot_ok(roff[i], kBlob, a.pool_bytes);
-        if (seg == 0) ((lds_f32*)(part))[i * a.rb + rloc] = valid ? v : 0.f;
-      }
-      __syncthreads();
-      // ordered combine: ranks ascending, then the gated shared expert
-      const float sgm = __uint_as_float(misc[kMSig]);
-      if (tid < a.rb && row_lo + tid < kH) {
-        const int n = row_lo + tid;
-        float acc = 0.f;
-        for (int i = 0; i < k; ++i)
-          acc = fmaf(__uint_as_float(misc[kMVals + i]), ((const lds_f32*)(part))[i * a.rb + tid], acc);
-        acc = fmaf(sgm, ((const lds_f32*)(part))[k * a.rb + tid], acc);
-        uint8_t* o = a.out + l * a.out_stride;
-        if constexpr (OUT == kF32) reinterpret_cast<float*>(o)[n] = acc;
-        else reinterpret_cast<uint16_t*>(o)[n] = f32_to_bf16(acc);
-        if (a.x_chain) {
-          // the stack step x + y: fp32 sum, nearest-even bf16
-          const float xv = bf16_to_f32(((const lds_w16*)(xl))[n]);
-          const uint16_t xn = f32_to_bf16(xv + acc);
-          reinterpret_cast<uint16_t*>(a.x_chain + l * a.xc_stride)[n] = xn;
-          ((lds_w16*)(lds + S.part))[(k + 1) * a.rb * 2 + tid] = xn;   // staged for the tagged words
-        }
+      float hv[1][kSegCodes];
+      load_lds_seg(hs + (static_cast<size_t>(s) * kSegI + seg) * kPad, 0, hv[0]);
+      const float hsv = seg_sum(hv[0]);
+      const uint8_t* Dq = lds + S.d + s * kDPM * kDRowB;
+      for (int pp = 0; pp < npass; ++pp) {
+        const int rloc = row0 + pp * kRpp + sub;
+        const float v = down_row(Dq, kDPM, rloc, seg, hv, hsv);
+        if (seg == 0) store_tag(part + static_cast<size_t>(u) * kH + mem * kDPM + rloc, __float_as_uint(valid ? v : 0.f), tag);
       }
     }
+    if (b == 0 && tid == 0) store_tag(part + kSigW, misc[kMSig], tag);
 
-    // ------------------------------------------------------------------ next input
-    if (a.x_chain && l + 1 < a.L) {
-      __syncthreads();
-      const uint32_t ntag = tag + 1u;    // the next layer's tag marks its input
-      const int row_lo = b * a.rb;
-      const lds_w16* xn = (const lds_w16*)(lds + S.part) + (k + 1) * a.rb * 2;
-      const int nw = a.rb / 2;
-      if (tid < nw * kXRep) {
-        const int w = tid % nw, rep = tid / nw;
-        const uint32_t bits = static_cast<uint32_t>(xn[2 * w]) | (static_cast<uint32_t>(xn[2 * w + 1]) << 16);
-        store_tag(a.xx + static_cast<size_t>(rep) * (kH / 2) + row_lo / 2 + w, bits, ntag);
-      }
-      __syncthreads();               // every x store is issued
-      raise_flag(a, kFlX, ntag, wave, lane);
-      lds_w32* xd = (lds_w32*)(lds + (p ^ 1) * S.p_bytes + S.p_x);
-      bool ok = wait_flags(a, kFlX, ntag, dead, misc, wave, lane);
+    // ------------------------------------------------------------------ chained: the next input
+    if (a.x_chain) {
+      __syncthreads();               // every row-sum store is issued
+      raise_flag(a, kFlP, tag, wave, lane);
+      lds_f32* fin = (lds_f32*)(lds + S.fin);
+      bool ok = wait_flags(a, kFlP, tag, -1, kNB, dead, misc, wave, lane);
+      const int nf = (k + 1) * kDPM + 1;   // the rows [64 m, 64 m + 64) of every unit, then sigma
       if (ok && wave < kRdWaves) {
-        const bool r = read_tagged<(kH / 2 + kRdThr - 1) / kRdThr>(
-            a.xx + static_cast<size_t>(b % kXRep) * (kH / 2), kH / 2, kRdThr, ntag, a.spin_limit,
-            [&](int i, uint32_t bits) { xd[i] = bits; });
+        const bool r = read_tagged<((kMaxK + 1) * kDPM + 1 + kRdThr - 1) / kRdThr>(
+            tid, nf, kRdThr, tag, a.spin_limit,
+            [&](int i) {
+              return i < nf - 1 ? part + static_cast<size_t>(i / kDPM) * kH + mem * kDPM + i % kDPM : part + kSigW;
+            },
+            [&](int i, uint32_t bits) { fin[i] = __uint_as_float(bits); });
         if (lane == 0) misc[kMRd + wave] = r ? 1u : 0u;
       }
       __syncthreads();
       dead = dead || !(ok && reads_ok(misc));
+      if (tid < kDPM) {
+        // ordered combine: ranks ascending, then the gated shared expert; the
+        // stack step x + y in fp32, rounded to nearest even bf16
+        const int n = mem * kDPM + tid;
+        const lds_f32* vals = (const lds_f32*)(misc + kMVals + p * kMaxK);
+        float acc = 0.f;
+        for (int i = 0; i < k; ++i) acc = fmaf(vals[i], fin[i * kDPM + tid], acc);
+        acc = fmaf(fin[nf - 1], fin[k * kDPM + tid], acc);
+        const float xv = bf16_to_f32(((const lds_w16*)(xl))[n]);
+        const uint16_t xn = f32_to_bf16(xv + acc);
+        if (grp == 0) {
+          uint8_t* o = a.out + l * a.out_stride;
+          if constexpr (OUT == kF32) reinterpret_cast<float*>(o)[n] = acc;
+          else reinterpret_cast<uint16_t*>(o)[n] = f32_to_bf16(acc);
+          reinterpret_cast<uint16_t*>(a.x_chain + l * a.xc_stride)[n] = xn;
+        }
+        ((lds_w16*)(lds + S.xn))[tid] = xn;
+      }
+      if (l + 1 < a.L) {
+        __syncthreads();
+        const uint32_t ntag = tag + 1u;    // the next layer's tag marks its input
+        uint64_t* xg = a.xx + static_cast<size_t>(grp) * (kH / 2);
+        if (tid < kDPM / 2) {
+          const lds_w16* xs16 = (const lds_w16*)(lds + S.xn);
+          const uint32_t bits = static_cast<uint32_t>(xs16[2 * tid]) | (static_cast<uint32_t>(xs16[2 * tid + 1]) << 16);
+          store_tag(xg + mem * (kDPM / 2) + tid, bits, ntag);
+        }
+        __syncthreads();               // every x store is issued
+        raise_group_flag(a, kFlX, ntag, grp, mem, wave, lane);
+        lds_w32* xd = (lds_w32*)(lds + (p ^ 1) * S.p_bytes + S.p_x);
+        bool ok2 = wait_flags(a, kFlX, ntag, grp, kNM, dead, misc, wave, lane);
+        if (ok2 && wave < kRdWaves) {
+          const bool r = read_tagged<(kH / 2 + kRdThr - 1) / kRdThr>(
+              tid, kH / 2, kRdThr, ntag, a.spin_limit, [&](int i) { return xg + i; },
+              [&](int i, uint32_t bits) { xd[i] = bits; });
+          if (lane == 0) misc[kMRd + wave] = r ? 1u : 0u;
+        }
+        __syncthreads();
+        dead = dead || !(ok2 && reads_ok(misc));
+      }
     }
     if (wave == kWaveStatic) wait_vm0();
     __syncthreads();
+  }
+
+  // unchained: the last layer's rows, once every group's row sums are out
+  if (!a.x_chain && a.L > 0) {
+    const uint32_t tl = epoch + static_cast<uint32_t>(a.L);
+    raise_flag(a, kFlP, tl, wave, lane);
+    bool ok = wait_flags(a, kFlP, tl, -1, kNB, dead, misc, wave, lane);
+    if (wave == kWaveFin) {
+      bool r = true;
+      if (ok) r = finish_rows<OUT>(a, S, lds, a.L - 1, tl, lane);
+      if (lane == 0) misc[kMFin] = r ? 1u : 0u;
+    }
+    __syncthreads();
+    dead = dead || !ok || misc[kMFin] == 0u;
   }
 
   if (bad && lane == 0) raise_error(a.ctrl, kErrRange);
@@ -639,7 +843,7 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
   // the grid by block 0), so that all counters stay equal
   if (tid == 0) a.epochs[b] = epoch + static_cast<uint32_t>(a.L);
   if (b == 0)
-    for (int j = a.nb + tid; j < kFusedMaxBlocks; j += kThr) a.epochs[j] = a.epochs[j] + static_cast<uint32_t>(a.L);
+    for (int j = kNB + tid; j < kFusedMaxBlocks; j += kThr) a.epochs[j] = a.epochs[j] + static_cast<uint32_t>(a.L);
 }
 
 }  // namespace
@@ -649,27 +853,23 @@ bool stack_supported(const moe_desc& d) {
          d.sb_dtype == kBF16 && d.n_experts <= kMaxE && d.top_k <= kMaxK;
 }
 
-size_t stack_ws_lg() { return static_cast<size_t>(kLgRep) * kMaxE * 8; }
-size_t stack_ws_h() { return static_cast<size_t>(kHRep) * kMaxHn * 8; }
-size_t stack_ws_x() { return static_cast<size_t>(kXRep) * (kH / 2) * 8; }
-size_t stack_ws_flags() { return static_cast<size_t>(3) * kFlagRep * kMaxNb * 4; }
+size_t stack_ws_lg() { return kXWords * 8; }
+size_t stack_ws_h() { return 256; }
+size_t stack_ws_x() { return static_cast<size_t>(kNG) * (kH / 2) * 8; }
+size_t stack_ws_flags() { return static_cast<size_t>(4) * kFlagRep * kNB * 4; }
 
-// Grid and LDS of the stack kernel on the current device: one block per CU,
-// each CU's share of rows an exact multiple of a down pass.
+// Grid and LDS of the stack kernel on the current device: 256 blocks, one per
+// CU, all resident at once.
 int stack_plan(const moe_desc& d, StackPlan* plan) {
   int dev = 0, cus = 0, lds_max = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MOE_ENODEV;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MOE_ENODEV;
   if (hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
     return MOE_ENODEV;
-  const int nb = cus;
-  if (nb < 1 || nb > kMaxNb || kH % nb) return MOE_EINVAL;
-  const int rb = kH / nb;
-  const int rpb = (d.n_experts + nb - 1) / nb, spb = (kI + nb - 1) / nb;
-  const int gpb = (d.top_k * kI + nb - 1) / nb;
-  if (rb % kRpp || rb > kMaxRb || rpb > kMaxRpb || spb > kMaxSpb || gpb > kGW * kMaxG || rpb + spb > kNW - 1)
-    return MOE_EINVAL;
-  const SLds S = stack_lds(d.n_experts, d.top_k, rpb, spb, rb);
+  if (cus < kNB) return MOE_EINVAL;
+  const int rpb = (d.n_experts + kNB - 1) / kNB;
+  if (rpb > kMaxRpb || d.top_k < 1) return MOE_EINVAL;
+  const SLds S = stack_lds(d.n_experts, rpb);
   if (S.total > static_cast<uint32_t>(lds_max)) return MOE_EINVAL;
   const void* fn = d.out_dtype == kF32 ? reinterpret_cast<const void*>(k_decode_stack<kF32>)
                                        : reinterpret_cast<const void*>(k_decode_stack<kBF16>);
@@ -681,11 +881,11 @@ int stack_plan(const moe_desc& d, StackPlan* plan) {
                            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, k_decode_stack<kBF16>, kThr, S.total);
   if (e != hipSuccess) return MOE_EHIP;
   if (fit < 1) return MOE_EINVAL;
-  plan->nb = nb;
-  plan->rb = rb;
+  plan->nb = kNB;
+  plan->rb = kDPM;
   plan->rpb = rpb;
-  plan->spb = spb;
-  plan->gpb = gpb;
+  plan->spb = kSpb;
+  plan->gpb = kHPM;
   plan->lds = S.total;
   return MOE_OK;
 }
@@ -710,8 +910,7 @@ int launch_decode_stack(const StackCall& c, const StackPlan& plan) {
   a.xc_stride = c.chain_stride;
   a.ids_out = c.ids_out;
   a.wts_out = c.wts_out;
-  a.lg = reinterpret_cast<uint64_t*>(c.ws + c.L.s_lg);
-  a.hx = reinterpret_cast<uint64_t*>(c.ws + c.L.s_h);
+  a.xw = reinterpret_cast<uint64_t*>(c.ws + c.L.s_lg);
   a.xx = reinterpret_cast<uint64_t*>(c.ws + c.L.s_x);
   a.flags = reinterpret_cast<uint32_t*>(c.ws + c.L.s_flags);
   a.ctrl = reinterpret_cast<uint32_t*>(c.ws + c.L.ctrl);
@@ -719,13 +918,7 @@ int launch_decode_stack(const StackCall& c, const StackPlan& plan) {
   a.L = c.n_layers;
   a.E = d.n_experts;
   a.k = d.top_k;
-  a.nb = plan.nb;
   a.rpb = plan.rpb;
-  a.spb = plan.spb;
-  a.rb = plan.rb;
-  a.gpb = plan.gpb;
-  a.hn = (d.top_k + 1) * kI + 1;
-  a.out_bf16 = d.out_dtype == kBF16;
   a.spin_limit = 1u << 21;
   if (d.out_dtype == kF32)
     launch_kernel(k_decode_stack<kF32>, dim3(plan.nb), dim3(kThr), plan.lds, c.stream, a);
