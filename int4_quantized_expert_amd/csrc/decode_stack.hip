@@ -27,15 +27,15 @@
 //
 // Blocks exchange data only through tagged 64-bit words: the value's bits and
 // the layer's tag, written with relaxed device-scope stores and read with
-// device-scope loads until every word a block needs carries the tag.  The
-// logits are read that way directly; the other exchanges first wait for
-// per-block flags (the tag, raised once a block's words are issued: 256 of
-// them in one of 16 replicas grid-wide, 32 in a group) and then read the
-// words once, reading again any word that is still old.  Every wait is
-// bounded; on expiry the kernel raises kErrTimeout and skips all later waits,
-// so the grid always drains.  Regions written before a grid-wide wait and
-// read after another block's (the logits, the shared h, the row sums)
-// alternate between two copies by layer parity.
+// device-scope loads, each word read again (after a short sleep) until it
+// carries the tag; no flags.  Reading a block's word of layer l orders
+// everything that block did before writing it, and every block writes logit
+// words in phase R (E is a multiple of 256), so a block that has read the
+// logits of layer l + 1 knows every block has finished layer l's reads.
+// Regions written before that point and read after it (the logits, the
+// shared h, the row sums) alternate between two copies by layer parity.
+// Every wait is bounded; on expiry the kernel raises kErrTimeout and skips
+// all later waits, so the grid always drains.
 //
 // Work inside a layer needs every block resident at once (checked with the
 // occupancy query when the plan is made).
@@ -87,14 +87,12 @@ constexpr int kDRowQ = kI / 2;             // code bytes of a down row
 constexpr int kDRowSB = (kI / 64) * 2;     // scale (or bias) bytes of a down row
 constexpr uint32_t kDRowB = kDRowQ + 2 * kDRowSB;   // LDS bytes of one staged down row
 constexpr int kLgRep = 8;                  // copies of the exchanged logits
-constexpr int kFlagRep = 16;               // copies of the grid-wide flags
 constexpr int kMaxK = 10, kMaxRpb = 2, kSpb = kI / kNB, kMaxE = kNB * kMaxRpb;
 constexpr int kTopC = 16;                  // top-k candidates each wave keeps
 constexpr int kRdWaves = 6;                // waves that read exchanged words (0..5)
 constexpr int kRdThr = kRdWaves * kWave;
 constexpr int kSigW = (kMaxK + 1) * kH;    // sigma's word in a row-sum copy
 constexpr int kPartW = kSigW + 64;         // words of one row-sum copy
-constexpr int kFlP = 1, kFlH = 2, kFlX = 3;   // flag kinds (H, X: per group; kind 0 is unused)
 static_assert(kSpb == 2 && kMaxG * kGW >= kUPG * kHPM && kMaxK + 1 <= kUPG * kNG, "grid shape");
 
 // Exchange regions (word offsets into the one tagged-word buffer).
@@ -125,8 +123,7 @@ struct SLds {
 constexpr int kMIds = 0;               // [kMaxK] chosen experts by rank
 constexpr int kMVals = 16;             // [2][kMaxK] chosen logits, then weights, by layer parity
 constexpr int kMSig = kMVals + 2 * kMaxK;   // sigmoid(g . x) of this layer (block 0)
-constexpr int kMOk = kMSig + 1;        // result of the last flag wait
-constexpr int kMFin = kMOk + 1;        // result of the finishing wave's reads
+constexpr int kMFin = kMSig + 1;       // result of the finishing wave's reads
 constexpr int kMRd = kMFin + 1;        // [kRdWaves] results of the reading waves
 constexpr int kMOff = 64;              // [kMaxK] int64 blob offsets by rank (8-byte aligned)
 constexpr int kMWords = kMOff + 2 * kMaxK;
@@ -194,7 +191,6 @@ struct StackArgs {
   float* wts_out;            // optional [L][k]
   uint64_t* xw;              // tagged words, regions at kX*
   uint64_t* xx;              // [kNG][kH / 2] tagged next-layer input of each group (two bf16 per word)
-  uint32_t* flags;           // [4 kinds][kFlagRep][kNB] exchange flags
   uint32_t* ctrl;            // [0] error flags
   uint32_t* epochs;          // per-block call counters
   int L, E, k, rpb;
@@ -290,55 +286,6 @@ __device__ __forceinline__ void issue_down(const StackArgs& a, const SLds& S, ui
     const uint8_t* blob = unit_blob(a, misc, grp + kNG * s, l, ok);
     copy_down_rows(raw_rsrc(blob, ok ? kBlob : 0), lds + S.d + s * kDPM * kDRowB, mem * kDPM, kDPM, lane);
   }
-}
-
-// Flags.  Grid-wide kinds: a block writes its tag into every replica; a
-// reader's wave 0 polls the 256 flags of replica b % 16 (1 KB per try).  Group
-// kinds: one copy, block (g, m) at 32 g + m, so a group's flags (or four
-// groups' flags) are contiguous.  A wait ends when every flag is at least the
-// tag, so a block already a layer ahead never holds it up.
-__device__ __forceinline__ void raise_flag(const StackArgs& a, int kind, uint32_t tag, int wave, int lane) {
-  if (wave == 0 && lane < kFlagRep)
-    __hip_atomic_store(a.flags + (kind * kFlagRep + lane) * kNB + blockIdx.x, tag, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void raise_group_flag(const StackArgs& a, int kind, uint32_t tag, int grp, int mem,
-                                                 int wave, int lane) {
-  if (wave == 0 && lane == 0)
-    __hip_atomic_store(a.flags + kind * kFlagRep * kNB + grp * kNM + mem, tag, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// True once every flag of the set carries at least `tag`; false on expiry (or
-// when an earlier wait expired).  Grid-wide kinds (g0 < 0) poll all 256 flags
-// of the block's replica; group kinds the n flags from group g0 on.
-__device__ __forceinline__ bool wait_flags(const StackArgs& a, int kind, uint32_t tag, int g0, int n, bool dead,
-                                           lds_w32* misc, int wave, int lane) {
-  if (wave == 0) {
-    bool ok = !dead;
-    if (ok) {
-      const uint32_t* r = g0 >= 0 ? a.flags + kind * kFlagRep * kNB + g0 * kNM
-                                  : a.flags + (kind * kFlagRep + blockIdx.x % kFlagRep) * kNB;
-      if (g0 < 0) n = kNB;
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(r), 0, n * 4, 0x00020000);
-      for (uint32_t spins = 0;; ++spins) {
-        bool all = true;
-        if (lane * 4 < n) {   // scope of device (sc1)
-          const u32x4 f = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, 0, 16));
-#pragma unroll
-          for (int q = 0; q < 4; ++q) all = all && tag_ge(f[q], tag);
-        }
-        if (__ballot(!all) == 0) break;
-        if (spins >= a.spin_limit) { ok = false; break; }
-        __builtin_amdgcn_s_sleep(1);
-      }
-    }
-    if (lane == 0) misc[kMOk] = ok ? 1u : 0u;
-  }
-  __syncthreads();
-  return misc[kMOk] != 0u;
 }
 
 // Tagged words read by nthr threads: word i (reader rt takes i = rt + q nthr,
@@ -591,10 +538,7 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
     }
 
     // ------------------------------------------------------------------ K
-    // The logits are read as words, without a flag wait: every block's R
-    // ends at about the same time and the memory is quiet here, so one
-    // round trip (then another for any word still old) beats waiting for a
-    // flag and then reading.
+    // every block reads the E logits (replica b % 8) as they arrive
     __syncthreads();                 // every wave's logit stores are issued
     {
       const bool ok = !dead;
@@ -708,15 +652,14 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
     }
 
     // ------------------------------------------------------------------ H
-    __syncthreads();                 // every wave's h stores are issued
-    raise_group_flag(a, kFlH, tag, grp, mem, wave, lane);
+    __syncthreads();                 // every wave's h stores are issued, and every wave is here
     if (wave == kWaveDown) wait_vm0();
     {
       float* hs = reinterpret_cast<float*>(lds + S.hs);
-      // the group's flags; waves 0..5 read (wave 6 still has the static
-      // copies in flight) h of the group's units: routed ones from the group,
-      // the shared one from phase R
-      bool ok = wait_flags(a, kFlH, tag, grp, kNM, dead, misc, wave, lane);
+      // waves 0..5 read (wave 6 still has the static copies in flight) h of
+      // the group's units: routed ones from the group, the shared one from
+      // phase R
+      const bool ok = !dead;
       if (ok && wave < kRdWaves) {
         const uint64_t* hx = a.xw + kXHx + static_cast<size_t>(grp) * kUPG * kI;
         const bool r = read_tagged<(kUPG * kI + kRdThr - 1) / kRdThr>(
@@ -762,10 +705,9 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
 
     // ------------------------------------------------------------------ chained: the next input
     if (a.x_chain) {
-      __syncthreads();               // every row-sum store is issued
-      raise_flag(a, kFlP, tag, wave, lane);
+      __syncthreads();
       lds_f32* fin = (lds_f32*)(lds + S.fin);
-      bool ok = wait_flags(a, kFlP, tag, -1, kNB, dead, misc, wave, lane);
+      const bool ok = !dead;
       const int nf = (k + 1) * kDPM + 1;   // the rows [64 m, 64 m + 64) of every unit, then sigma
       if (ok && wave < kRdWaves) {
         const bool r = read_tagged<((kMaxK + 1) * kDPM + 1 + kRdThr - 1) / kRdThr>(
@@ -805,10 +747,8 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
           const uint32_t bits = static_cast<uint32_t>(xs16[2 * tid]) | (static_cast<uint32_t>(xs16[2 * tid + 1]) << 16);
           store_tag(xg + mem * (kDPM / 2) + tid, bits, ntag);
         }
-        __syncthreads();               // every x store is issued
-        raise_group_flag(a, kFlX, ntag, grp, mem, wave, lane);
         lds_w32* xd = (lds_w32*)(lds + (p ^ 1) * S.p_bytes + S.p_x);
-        bool ok2 = wait_flags(a, kFlX, ntag, grp, kNM, dead, misc, wave, lane);
+        const bool ok2 = !dead;
         if (ok2 && wave < kRdWaves) {
           const bool r = read_tagged<(kH / 2 + kRdThr - 1) / kRdThr>(
               tid, kH / 2, kRdThr, ntag, a.spin_limit, [&](int i) { return xg + i; },
@@ -826,15 +766,13 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
   // unchained: the last layer's rows, once every group's row sums are out
   if (!a.x_chain && a.L > 0) {
     const uint32_t tl = epoch + static_cast<uint32_t>(a.L);
-    raise_flag(a, kFlP, tl, wave, lane);
-    bool ok = wait_flags(a, kFlP, tl, -1, kNB, dead, misc, wave, lane);
     if (wave == kWaveFin) {
       bool r = true;
-      if (ok) r = finish_rows<OUT>(a, S, lds, a.L - 1, tl, lane);
+      if (!dead) r = finish_rows<OUT>(a, S, lds, a.L - 1, tl, lane);
       if (lane == 0) misc[kMFin] = r ? 1u : 0u;
     }
     __syncthreads();
-    dead = dead || !ok || misc[kMFin] == 0u;
+    dead = dead || misc[kMFin] == 0u;
   }
 
   if (bad && lane == 0) raise_error(a.ctrl, kErrRange);
@@ -849,14 +787,13 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
 }  // namespace
 
 bool stack_supported(const moe_desc& d) {
+  // every block must write at least one logit word (see the exchange notes)
   return d.hidden == kH && d.inter == kI && d.shared_inter == kI && d.bits == 4 && d.act_dtype == kBF16 &&
-         d.sb_dtype == kBF16 && d.n_experts <= kMaxE && d.top_k <= kMaxK;
+         d.sb_dtype == kBF16 && d.n_experts <= kMaxE && d.n_experts % kNB == 0 && d.top_k <= kMaxK;
 }
 
 size_t stack_ws_lg() { return kXWords * 8; }
-size_t stack_ws_h() { return 256; }
 size_t stack_ws_x() { return static_cast<size_t>(kNG) * (kH / 2) * 8; }
-size_t stack_ws_flags() { return static_cast<size_t>(4) * kFlagRep * kNB * 4; }
 
 // Grid and LDS of the stack kernel on the current device: 256 blocks, one per
 // CU, all resident at once.
@@ -912,7 +849,6 @@ int launch_decode_stack(const StackCall& c, const StackPlan& plan) {
   a.wts_out = c.wts_out;
   a.xw = reinterpret_cast<uint64_t*>(c.ws + c.L.s_lg);
   a.xx = reinterpret_cast<uint64_t*>(c.ws + c.L.s_x);
-  a.flags = reinterpret_cast<uint32_t*>(c.ws + c.L.s_flags);
   a.ctrl = reinterpret_cast<uint32_t*>(c.ws + c.L.ctrl);
   a.epochs = reinterpret_cast<uint32_t*>(c.ws + c.L.f_epoch);
   a.L = c.n_layers;

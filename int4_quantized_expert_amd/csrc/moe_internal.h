@@ -42,10 +42,8 @@ struct WsLayout {
   size_t f_pidx;     // two-launch path: [min(T k, E), T] int32 rank of expert u for token t
   size_t f_epoch;    // two-launch path: [kFusedMaxBlocks] uint32 per-block call counters (inside ctrl)
   size_t f_gflag;    // single-launch decode: [kFusedReplicas][kFusedMaxBlocks] uint32 completion tags
-  size_t s_lg;       // stack decode: tagged logits (replicated)
-  size_t s_h;        // stack decode: tagged h rows and gate (replicated)
-  size_t s_x;        // stack decode: tagged next-layer input (replicated)
-  size_t s_flags;    // stack decode: per-block exchange flags (three kinds, replicated)
+  size_t s_lg;       // stack decode: tagged words (logits, shared h, each group's h, row sums by unit)
+  size_t s_x;        // stack decode: tagged next-layer input of each group
   size_t p_x16;      // prefill: [T, H] float16 activations in MFMA k order
   size_t p_meta;     // prefill: int32 [0] number of expert tiles
   size_t p_tstart;   // prefill: [min(T k, E) + 2] int32 first tile of each distinct expert, then of the shared one
@@ -67,9 +65,7 @@ inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 // shapes it is built for and the sizes of its exchange buffers.
 bool stack_supported(const moe_desc& d);
 size_t stack_ws_lg();
-size_t stack_ws_h();
 size_t stack_ws_x();
-size_t stack_ws_flags();
 
 inline WsLayout ws_layout(const moe_desc& d, int32_t T) {
   WsLayout L{};
@@ -83,9 +79,7 @@ inline WsLayout ws_layout(const moe_desc& d, int32_t T) {
   // every descriptor and T, so that only its own tagged words (with older
   // tags) are ever found there
   L.s_lg = take(stack_ws_lg());
-  L.s_h = take(stack_ws_h());
   L.s_x = take(stack_ws_x());
-  L.s_flags = take(stack_ws_flags());
   L.f_epoch = L.ctrl + 256;
   const size_t Tf = kFusedMaxT;
   // sized for the largest E: words of other regions (plain data of calls with
