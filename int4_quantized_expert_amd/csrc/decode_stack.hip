@@ -3,27 +3,31 @@
 // One launch runs L layers in order on a grid of 256 resident 512-thread
 // blocks (one per CU).  The blocks form eight groups of 32 (block b is in
 // group b % 8; the dispatcher sends block b to XCD b % 8, so a group is one
-// XCD).  Each layer's work is split into units: the k routed experts (rank i)
-// and the shared expert's down projection (unit k).  Group g takes units g
-// and g + 8, so each unit's expert lives in one group:
-//   R  every block: two router rows and two of the shared expert's gate/up
-//      rows from LDS (copied there while the previous layer ran); block 0
-//      also sigma(g . x)
-//   K  grid-wide: every block reads the E logits and takes top-k and the
-//      renormalised weights itself (one wave)
-//   G  per group: the 512 gate/up row pairs of each routed unit of the group,
-//      16 per block, every load of a wave requested at once; meanwhile one
-//      wave copies the block's 64 down rows of each unit into LDS
-//   H  per group: the 32 blocks of a group gather their units' h (512 values
-//      each; the shared expert's h comes from R)
-//   D  per group: the block's 64 down rows of each unit, the row sums stored
-//      per unit as tagged words
+// XCD).  The work of a layer is divided so that every block has the same
+// share and most exchanges stay inside a group:
+//   * whole units: routed rank r < 8 lives in group r (its 512 gate/up row
+//     pairs, 16 per block, and its 2048 down rows, 64 per block);
+//   * split units: ranks 8 and 9 (k = 10) each live in four groups (0..3 and
+//     4..7): 4 row pairs and 16 down rows per block;
+//   * the shared expert: its gate/up rows in phase R on every block (two per
+//     block, from LDS), its down rows 8 per block.
+// Per layer:
+//   R  two router rows and two shared gate/up rows per block, from LDS
+//      (copied there while the previous layer ran); block 0 also sigma(g . x)
+//   K  every block reads the E logits and takes top-k and the renormalised
+//      weights itself (one wave)
+//   G  the block's gate/up row pairs of its whole and split unit, every load
+//      of a wave requested at once; meanwhile one wave copies the block's
+//      down rows of its three units into LDS and another the next layer's
+//      static operands
+//   H  h of the whole unit (from the group), the split unit (from its four
+//      groups) and the shared expert (from R)
+//   D  the block's 88 down rows, stored as row sums per unit
 // The ordered combine (ranks ascending, then sigma times the shared unit)
-// reads every unit's row sums, so it waits for all groups: unchained, block b
-// finishes rows 8b..8b+7 of layer l while the next layer's top-k runs (the
-// last layer after one more grid-wide wait); chained, every group finishes
-// all rows after a grid-wide wait and exchanges the next input within the
-// group.
+// reads every unit's row sums: unchained, block b finishes rows 8b..8b+7 of
+// layer l while the next layer's top-k runs (the last layer at the end);
+// chained, every group finishes all rows and exchanges the next input within
+// the group.
 //
 // Blocks exchange data only through tagged 64-bit words: the value's bits and
 // the layer's tag, written with relaxed device-scope stores and read with
@@ -67,12 +71,17 @@ constexpr int kNW = kThr / kWave;          // 8 waves per block
 constexpr int kNG = 8;                     // block groups (block b in group b % 8)
 constexpr int kNM = 32;                    // blocks per group
 constexpr int kNB = kNG * kNM;             // blocks in the grid
-constexpr int kUPG = 2;                    // units of one group per layer, at most
-constexpr int kHPM = kI / kNM;             // gate/up row pairs of a unit per block (16)
-constexpr int kDPM = kH / kNM;             // down rows of a unit per block (64)
-constexpr int kFR = kH / kNB;              // output rows a block finishes, unchained (8)
-constexpr int kGW = 6;                     // waves 0..5 take the gate/up pairs
-constexpr int kMaxG = (kUPG * kHPM + kGW - 1) / kGW;   // pairs per wave, at most (6)
+constexpr int kQuads = 2;                  // ranks 8 and 9: split units, over groups 0..3 and 4..7
+constexpr int kQG = kNG / kQuads;          // groups per split unit (4)
+constexpr int kHPM = kI / kNM;             // gate/up row pairs of a whole unit per block (16)
+constexpr int kDPM = kH / kNM;             // down rows of a whole unit per block (64)
+constexpr int kSHP = kI / (kQG * kNM);     // gate/up row pairs of a split unit per block (4)
+constexpr int kSDR = kH / (kQG * kNM);     // down rows of a split unit per block (16)
+constexpr int kFR = kH / kNB;              // shared down rows per block, and output rows a block
+                                           // finishes when unchained (8)
+constexpr int kWGW = 5;                    // waves 0..4 take the whole unit's pairs, wave 5 the split unit's
+constexpr int kGW = kWGW + 1;
+constexpr int kMaxG = (kHPM + kWGW - 1) / kWGW;        // pairs per wave, at most (4)
 constexpr int kWaveStatic = 6;             // copies the next layer's static operands
 constexpr int kWaveDown = 7;               // copies the down operands
 constexpr int kWaveFin = 1;                // finishes the previous layer's rows (unchained)
@@ -93,13 +102,14 @@ constexpr int kRdWaves = 6;                // waves that read exchanged words (0
 constexpr int kRdThr = kRdWaves * kWave;
 constexpr int kSigW = (kMaxK + 1) * kH;    // sigma's word in a row-sum copy
 constexpr int kPartW = kSigW + 64;         // words of one row-sum copy
-static_assert(kSpb == 2 && kMaxG * kGW >= kUPG * kHPM && kMaxK + 1 <= kUPG * kNG, "grid shape");
+static_assert(kSpb == 2 && kMaxG == kSHP && kMaxK <= kNG + kQuads && kFR == 8, "grid shape");
 
 // Exchange regions (word offsets into the one tagged-word buffer).
 constexpr size_t kXLg = 0;                                      // [2][kLgRep][kMaxE] logits
 constexpr size_t kXSh = kXLg + size_t(2) * kLgRep * kMaxE;      // [2][kI] shared h
-constexpr size_t kXHx = kXSh + size_t(2) * kI;                  // [kNG][kUPG][kI] h of each group's routed units
-constexpr size_t kXPart = kXHx + size_t(kNG) * kUPG * kI;       // [2][kPartW] row sums by unit, then sigma
+constexpr size_t kXHx = kXSh + size_t(2) * kI;                  // [kNG][kI] h of each group's whole unit
+constexpr size_t kXHq = kXHx + size_t(kNG) * kI;                // [kQuads][kI] h of the split units
+constexpr size_t kXPart = kXHq + size_t(kQuads) * kI;           // [2][kPartW] row sums by unit, then sigma
 constexpr size_t kXWords = kXPart + size_t(2) * kPartW;
 
 // Bytes of LDS per region, rounded so that 256-byte direct-load rounds that
@@ -109,8 +119,9 @@ __host__ __device__ constexpr uint32_t r256(uint32_t n) { return (n + 255u) / 25
 struct SLds {
   // static operands of one layer (two copies, by layer parity)
   uint32_t p_x, p_rr, p_suq, p_susb, p_slot, p_gv, p_bytes;
-  uint32_t d;      // [kUPG][kDPM rows]: codes [64][256 B], scales [64][16 B], biases [64][16 B]
-  uint32_t hs;     // [kUPG][kSegI][kPad] floats: h of the group's units, one after the other
+  uint32_t d[3];   // down rows of the whole, split and shared unit: codes [n][256 B], scales [n][16 B],
+                   // biases [n][16 B] (n = 64, 16, 8)
+  uint32_t hs;     // [3][kSegI][kPad] floats: h of the whole, split and shared unit
   uint32_t lg;     // [kMaxE] logits
   uint32_t cand;   // [8 waves][16] top-k candidates
   uint32_t misc;   // see below
@@ -139,8 +150,10 @@ __host__ __device__ inline SLds stack_lds(int E, int rpb) {
   s.p_gv = o;   o += r256(kH * 2);
   s.p_bytes = o;
   uint32_t t = 2 * s.p_bytes;
-  s.d = t;      t += kUPG * kDPM * kDRowB;
-  s.hs = t;     t += kUPG * kSegI * kPad * 4;
+  s.d[0] = t;   t += kDPM * kDRowB;
+  s.d[1] = t;   t += kSDR * kDRowB;
+  s.d[2] = t;   t += kFR * kDRowB;
+  s.hs = t;     t += 3 * kSegI * kPad * 4;
   s.lg = t;     t += kMaxE * 4;
   s.cand = t;   t += kNW * kTopC * 8;
   s.misc = t;   t += r256(kMWords * 4);
@@ -277,15 +290,21 @@ __device__ __forceinline__ const uint8_t* unit_blob(const StackArgs& a, const ld
   return a.pool + (ok ? off : 0);
 }
 
-// The down rows [64 m, 64 m + 64) of each unit of the group (codes, scales,
-// biases) into LDS.
+// The block's down rows of its whole unit (rows [64 m, + 64) of rank g), its
+// split unit (rows [512 (g % 4) + 16 m, + 16) of rank 8 + g / 4) and the shared
+// expert (rows [256 g + 8 m, + 8)), into LDS.
 __device__ __forceinline__ void issue_down(const StackArgs& a, const SLds& S, uint8_t* lds, const lds_w32* misc,
-                                           int grp, int mem, int nu, int l, int lane) {
-  for (int s = 0; s < nu; ++s) {
-    bool ok;
-    const uint8_t* blob = unit_blob(a, misc, grp + kNG * s, l, ok);
-    copy_down_rows(raw_rsrc(blob, ok ? kBlob : 0), lds + S.d + s * kDPM * kDRowB, mem * kDPM, kDPM, lane);
+                                           int grp, int mem, bool has_w, bool has_s, int l, int lane) {
+  bool ok;
+  if (has_w) {
+    const uint8_t* blob = unit_blob(a, misc, grp, l, ok);
+    copy_down_rows(raw_rsrc(blob, ok ? kBlob : 0), lds + S.d[0], mem * kDPM, kDPM, lane);
   }
+  if (has_s) {
+    const uint8_t* blob = unit_blob(a, misc, kNG + grp / kQG, l, ok);
+    copy_down_rows(raw_rsrc(blob, ok ? kBlob : 0), lds + S.d[1], (grp % kQG) * (kH / kQG) + mem * kSDR, kSDR, lane);
+  }
+  copy_down_rows(raw_rsrc(a.shared + l * a.sh_stride, kBlob), lds + S.d[2], grp * (kH / kNG) + mem * kFR, kFR, lane);
 }
 
 // Tagged words read by nthr threads: word i (reader rt takes i = rt + q nthr,
@@ -460,10 +479,11 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
   const uint32_t epoch = a.epochs[b];
   bool dead = false;
   bool bad = false;   // a routed blob offset was unusable (its unit contributes nothing)
-  // units of this group: g and g + 8 up to k (k is the shared expert); the
-  // routed ones (below k) come first
-  const int nu = (grp <= k ? 1 : 0) + (grp + kNG <= k ? 1 : 0);
-  const int nr = (grp < k ? 1 : 0) + (grp + kNG < k ? 1 : 0);
+  // this block's units: the whole unit (rank g), the split unit (rank
+  // 8 + g / 4, a quarter of it per group) and an eighth of the shared down
+  const bool has_w = grp < k;
+  const int ur_s = kNG + grp / kQG;
+  const bool has_s = ur_s < k;
 
   if (tid == 0) misc[kMFin] = 1u;
   if (wave == kWaveStatic) {
@@ -538,10 +558,9 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
     }
 
     // ------------------------------------------------------------------ K
-    // every block reads the E logits (replica b % 8) as they arrive
     __syncthreads();                 // every wave's logit stores are issued
     {
-      const bool ok = !dead;
+      bool ok = !dead;
       if (ok && wave < kRdWaves) {
         const uint64_t* src = lgw + static_cast<size_t>(b % kLgRep) * kMaxE;
         const bool r = read_tagged<(kMaxE + kRdThr - 1) / kRdThr>(
@@ -579,21 +598,20 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
 
     // ------------------------------------------------------------------ G
     {
-      // waves 0..5: the row pairs [16 m, 16 m + 16) of one routed unit each;
-      // with two routed units waves 0..2 take the first and 3..5 the second
-      // (pairs w % 3 + 3 i), with one every sixth pair from w.  One
-      // descriptor per wave, every load requested before any compute.
-      const int s = nr == 2 ? wave / 3 : 0;
-      const int q0 = mem * kHPM + (nr == 2 ? wave % 3 : wave);
-      const int qs = nr == 2 ? 3 : kGW;
-      const bool gw = wave < kGW && s < nr;
-      const int npw = gw ? (kHPM - (q0 - mem * kHPM) + qs - 1) / qs : 0;   // this wave's pairs
+      // waves 0..4: the whole unit's row pairs [16 m, 16 m + 16), every fifth
+      // from w; wave 5: the split unit's four pairs [128 (g % 4) + 4 m, + 4).
+      // One descriptor per wave, every load requested before any compute.
+      const bool split = wave == kWGW;
+      const bool gw = wave < kWGW ? has_w : (split && has_s);
+      const int q0 = split ? (grp % kQG) * (kI / kQG) + mem * kSHP : mem * kHPM + wave;
+      const int qs = split ? 1 : kWGW;
+      const int npw = !gw ? 0 : split ? kSHP : (kHPM - wave + kWGW - 1) / kWGW;   // this wave's pairs
       Seg<4> cg[kMaxG], cu[kMaxG];
       uint32_t sg[kMaxG], su[kMaxG], bg[kMaxG], bu[kMaxG];
       bool vv = false;
       if (gw) {
         bool ok;
-        const uint8_t* blob = unit_blob(a, misc, grp + kNG * s, l, ok);
+        const uint8_t* blob = unit_blob(a, misc, split ? ur_s : grp, l, ok);
         vv = ok;
         if (!ok) bad = true;
         // one descriptor over the blob (an unusable one reads zeros); the
@@ -620,7 +638,7 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
       }
       __syncthreads();   // the down copies start after every phase-G load is requested
       if (gw) {
-        uint64_t* const hx = a.xw + kXHx + (static_cast<size_t>(grp) * kUPG + s) * kI;
+        uint64_t* const hx = split ? a.xw + kXHq + static_cast<size_t>(grp / kQG) * kI : a.xw + kXHx + static_cast<size_t>(grp) * kI;
         // two pairs at a time, with no branch between them
 #pragma unroll
         for (int j = 0; j < kMaxG; j += 2) {
@@ -647,67 +665,68 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
         // the layer before this one ended (waited for at the end of this one)
         if (l + 1 < a.L) issue_static(a, S, lds, p ^ 1, l + 1, lane);
       } else if (wave == kWaveDown) {
-        issue_down(a, S, lds, misc, grp, mem, nu, l, lane);
+        issue_down(a, S, lds, misc, grp, mem, has_w, has_s, l, lane);
       }
     }
 
-    // ------------------------------------------------------------------ H
-    __syncthreads();                 // every wave's h stores are issued, and every wave is here
+    // ------------------------------------------------------------------ H, D
+    __syncthreads();                 // every wave's h stores are issued
     if (wave == kWaveDown) wait_vm0();
     {
       float* hs = reinterpret_cast<float*>(lds + S.hs);
       // waves 0..5 read (wave 6 still has the static copies in flight) h of
-      // the group's units: routed ones from the group, the shared one from
-      // phase R
-      const bool ok = !dead;
+      // the whole unit (slot 0), the split unit (slot 1) and the shared
+      // expert (slot 2), the present ones one after the other
+      const int n0 = has_w ? kI : 0, n1 = has_s ? kI : 0;
+      bool ok = !dead;
       if (ok && wave < kRdWaves) {
-        const uint64_t* hx = a.xw + kXHx + static_cast<size_t>(grp) * kUPG * kI;
-        const bool r = read_tagged<(kUPG * kI + kRdThr - 1) / kRdThr>(
-            tid, nu * kI, kRdThr, tag, a.spin_limit,
-            [&](int i) {
-              const int s = i / kI, c = i % kI;
-              return grp + kNG * s < k ? hx + static_cast<size_t>(s) * kI + c : shw + c;
-            },
+        const uint64_t* hw = a.xw + kXHx + static_cast<size_t>(grp) * kI;
+        const uint64_t* hq = a.xw + kXHq + static_cast<size_t>(grp / kQG) * kI;
+        const bool r = read_tagged<(3 * kI + kRdThr - 1) / kRdThr>(
+            tid, n0 + n1 + kI, kRdThr, tag, a.spin_limit,
+            [&](int i) { return i < n0 ? hw + i : i < n0 + n1 ? hq + (i - n0) : shw + (i - n0 - n1); },
             [&](int i, uint32_t bits) {
-              const int s = i / kI, c = i % kI;
-              ((lds_f32*)(hs))[((s * kSegI) + c / kSegCodes) * kPad + c % kSegCodes] = __uint_as_float(bits);
+              const int t = i < n0 ? 0 : i < n0 + n1 ? 1 : 2;
+              const int c = i < n0 ? i : i < n0 + n1 ? i - n0 : i - n0 - n1;
+              ((lds_f32*)(hs))[((t * kSegI) + c / kSegCodes) * kPad + c % kSegCodes] = __uint_as_float(bits);
             });
         if (lane == 0) misc[kMRd + wave] = r ? 1u : 0u;
       }
       __syncthreads();
       dead = dead || !(ok && reads_ok(misc));
     }
-
-    // ------------------------------------------------------------------ D
-    if (nu > 0 && !dead) {
-      // wave w: unit w * nu / 8, rows [row0, row0 + 8 nu) of it, four per pass;
-      // lane: segment lane % 16 of row lane / 16 of the pass, its h segment
-      // and that segment's sum held in registers for every pass
-      const int s = wave * nu / kNW;
-      const int u = grp + kNG * s;
-      const int npass = 2 * nu;
-      const int row0 = (wave % (kNW / nu)) * npass * kRpp;
+    if (!dead) {
+      // passes of four rows: 16 of the whole unit, 4 of the split unit, 2 of
+      // the shared expert (absent units take none); wave w takes passes w,
+      // w + 8, w + 16.  Lane: segment lane % 16 of row lane / 16 of the pass.
+      const int npw_ = has_w ? kDPM / kRpp : 0, nps = has_s ? kSDR / kRpp : 0;
+      const int npass = npw_ + nps + kFR / kRpp;
       const int sub = lane / kSegI, seg = lane % kSegI;
-      bool valid = true;
-      if (u < k) (void)unit_blob(a, misc, u, l, valid);
       const float* hs = reinterpret_cast<const float*>(lds + S.hs);
-      float hv[1][kSegCodes];
-      load_lds_seg(hs + (static_cast<size_t>(s) * kSegI + seg) * kPad, 0, hv[0]);
-      const float hsv = seg_sum(hv[0]);
-      const uint8_t* Dq = lds + S.d + s * kDPM * kDRowB;
-      for (int pp = 0; pp < npass; ++pp) {
-        const int rloc = row0 + pp * kRpp + sub;
-        const float v = down_row(Dq, kDPM, rloc, seg, hv, hsv);
-        if (seg == 0) store_tag(part + static_cast<size_t>(u) * kH + mem * kDPM + rloc, __float_as_uint(valid ? v : 0.f), tag);
+      for (int pp = wave; pp < npass; pp += kNW) {
+        const int t = pp < npw_ ? 0 : pp < npw_ + nps ? 1 : 2;                         // wave-uniform
+        const int lr = (pp - (t == 0 ? 0 : t == 1 ? npw_ : npw_ + nps)) * kRpp + sub;   // row in the unit's LDS rows
+        const int nrow = t == 0 ? kDPM : t == 1 ? kSDR : kFR;
+        const int u = t == 0 ? grp : t == 1 ? ur_s : k;
+        const int row = t == 0 ? mem * kDPM + lr
+                        : t == 1 ? (grp % kQG) * (kH / kQG) + mem * kSDR + lr
+                                 : grp * (kH / kNG) + mem * kFR + lr;
+        bool valid = true;
+        if (t < 2) (void)unit_blob(a, misc, u, l, valid);
+        float hv[1][kSegCodes];
+        load_lds_seg(hs + (static_cast<size_t>(t) * kSegI + seg) * kPad, 0, hv[0]);
+        const float hsv = seg_sum(hv[0]);
+        const float v = down_row(lds + (t == 0 ? S.d[0] : t == 1 ? S.d[1] : S.d[2]), nrow, lr, seg, hv, hsv);
+        if (seg == 0) store_tag(part + static_cast<size_t>(u) * kH + row, __float_as_uint(valid ? v : 0.f), tag);
       }
     }
     if (b == 0 && tid == 0) store_tag(part + kSigW, misc[kMSig], tag);
 
     // ------------------------------------------------------------------ chained: the next input
     if (a.x_chain) {
-      __syncthreads();
+      __syncthreads();               // every row-sum store is issued
       lds_f32* fin = (lds_f32*)(lds + S.fin);
-      const bool ok = !dead;
+      bool ok = !dead;
       const int nf = (k + 1) * kDPM + 1;   // the rows [64 m, 64 m + 64) of every unit, then sigma
       if (ok && wave < kRdWaves) {
         const bool r = read_tagged<((kMaxK + 1) * kDPM + 1 + kRdThr - 1) / kRdThr>(
@@ -747,8 +766,9 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
           const uint32_t bits = static_cast<uint32_t>(xs16[2 * tid]) | (static_cast<uint32_t>(xs16[2 * tid + 1]) << 16);
           store_tag(xg + mem * (kDPM / 2) + tid, bits, ntag);
         }
+        __syncthreads();               // every x store is issued
         lds_w32* xd = (lds_w32*)(lds + (p ^ 1) * S.p_bytes + S.p_x);
-        const bool ok2 = !dead;
+        bool ok2 = !dead;
         if (ok2 && wave < kRdWaves) {
           const bool r = read_tagged<(kH / 2 + kRdThr - 1) / kRdThr>(
               tid, kH / 2, kRdThr, ntag, a.spin_limit, [&](int i) { return xg + i; },
@@ -766,13 +786,14 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
   // unchained: the last layer's rows, once every group's row sums are out
   if (!a.x_chain && a.L > 0) {
     const uint32_t tl = epoch + static_cast<uint32_t>(a.L);
+    bool ok = !dead;
     if (wave == kWaveFin) {
       bool r = true;
-      if (!dead) r = finish_rows<OUT>(a, S, lds, a.L - 1, tl, lane);
+      if (ok) r = finish_rows<OUT>(a, S, lds, a.L - 1, tl, lane);
       if (lane == 0) misc[kMFin] = r ? 1u : 0u;
     }
     __syncthreads();
-    dead = dead || misc[kMFin] == 0u;
+    dead = dead || !ok || misc[kMFin] == 0u;
   }
 
   if (bad && lane == 0) raise_error(a.ctrl, kErrRange);
