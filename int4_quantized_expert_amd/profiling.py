@@ -15,6 +15,14 @@ the code as it stands (bench.py reports `traffic` only when they do).
         --command "the rocprofv3 command lines"
     python -m int4_quantized_expert_amd.profiling kernels --stats S.csv --title "..." \\
         --out profiles/Y.md --command "the rocprofv3 command line"
+    python -m int4_quantized_expert_amd.profiling counters --pmc A.csv B.csv --title "..." \\
+        --out profiles/Z.md --command "the rocprofv3 command lines"
+
+The `counters` form summarises SQ counter passes (any counters, any number of
+passes) per library kernel: the mean per dispatch of each counter, the kernel's
+register, LDS and scratch use as the profiler recorded them, and the shares of
+wave time that the SQ_WAIT_* and SQ_ACTIVE_INST_* counters give (all of them
+count in the same 4-cycle units, so their ratios to SQ_WAVE_CYCLES are shares).
 """
 
 from __future__ import annotations
@@ -192,6 +200,70 @@ def write_kernel_summary(out: str, rows: list[dict], title: str, command: str, n
         fh.writelines(lines)
 
 
+SHARES = (("SQ_WAIT_ANY", "waiting on anything"),
+          ("SQ_WAIT_INST_ANY", "waiting on an issued instruction's result (s_waitcnt)"),
+          ("SQ_ACTIVE_INST_VALU", "issuing VALU instructions"),
+          ("SQ_ACTIVE_INST_VMEM", "issuing vector memory instructions"),
+          ("SQ_ACTIVE_INST_LDS", "issuing LDS instructions"),
+          ("SQ_ACTIVE_INST_SCA", "issuing scalar instructions"),
+          ("SQ_WAIT_INST_LDS", "waiting on LDS results"))
+
+
+def counter_table(paths: list[str]) -> dict:
+    """Per library kernel: mean per dispatch of every counter in the passes,
+    and the launch resources the profiler recorded with them."""
+    vals: dict = defaultdict(lambda: defaultdict(list))
+    res: dict = {}
+    for path in paths:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"]
+                if not is_library_kernel(name):
+                    continue
+                k = short_name(name)
+                vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                res[k] = {f: int(float(r[f])) for f in ("Grid_Size", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size",
+                                                       "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count") if f in r}
+    out = {}
+    for k, per in vals.items():
+        means = {c: sum(v) / len(v) for c, v in per.items()}
+        row = {"dispatches": max(len(v) for v in per.values()), "resources": res[k],
+               "counters": {c: round(m, 1) for c, m in sorted(means.items())}, "shares": {}}
+        wc = means.get("SQ_WAVE_CYCLES")
+        if wc:
+            for c, _ in SHARES:
+                if c in means:
+                    row["shares"][c] = round(means[c] / wc, 4)
+        out[k] = row
+    return out
+
+
+def write_counter_summary(out: str, table: dict, title: str, command: str, notes: str) -> None:
+    lines = [f"# {title}\n\n",
+             "Commands (from the repository root; rocprofv3 run from /tmp with TMPDIR=/tmp):\n\n",
+             "```\n" + command.strip() + "\n```\n\n"]
+    if notes:
+        lines.append(notes.strip() + "\n\n")
+    for k, row in table.items():
+        r = row["resources"]
+        lines.append(f"## {k}\n\n{row['dispatches']} dispatches; grid {r.get('Grid_Size')} work-items in groups of "
+                     f"{r.get('Workgroup_Size')}; {r.get('VGPR_Count')} VGPRs + {r.get('Accum_VGPR_Count')} AGPRs, "
+                     f"{r.get('SGPR_Count')} SGPRs, {r.get('LDS_Block_Size')} B LDS and {r.get('Scratch_Size')} B "
+                     f"scratch per work-item as recorded.\n\n")
+        if row["shares"]:
+            lines += ["| Share of wave time | Counter / SQ_WAVE_CYCLES |\n", "|---|---|\n"]
+            for c, what in SHARES:
+                if c in row["shares"]:
+                    lines.append(f"| {what} | {row['shares'][c]:.3f} ({c}) |\n")
+            lines.append("\n")
+        lines += ["| Counter | Mean per dispatch |\n", "|---|---|\n"]
+        for c, v in row["counters"].items():
+            lines.append(f"| {c} | {v:.1f} |\n")
+        lines.append("\n")
+    with open(out, "w") as fh:
+        fh.writelines(lines)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="what")
@@ -209,8 +281,16 @@ def main():
     k.add_argument("--out", required=True)
     k.add_argument("--command", required=True)
     k.add_argument("--notes", default="")
+    c = sub.add_parser("counters", help="SQ counter passes -> per-kernel means and shares of wave time")
+    c.add_argument("--pmc", required=True, nargs="+")
+    c.add_argument("--title", required=True)
+    c.add_argument("--out", required=True)
+    c.add_argument("--command", required=True)
+    c.add_argument("--notes", default="")
     a = ap.parse_args()
-    if a.what == "kernels":
+    if a.what == "counters":
+        write_counter_summary(a.out, counter_table(a.pmc), a.title, a.command, a.notes)
+    elif a.what == "kernels":
         write_kernel_summary(a.out, kernel_stats(a.stats), a.title, a.command, a.notes)
     else:
         write_summary(a.out, traffic_table(a.fetch, a.write, a.copy_bytes), a.workload, a.tokens, a.command)

@@ -46,3 +46,20 @@ def test_kernel_names_demangled_or_shortened():
     assert P.short_name("moe::(anonymous namespace)::k_topk(float const*, int, int, int*, float*)") == "k_topk"
     assert P.is_library_kernel("_ZN3moe12_GLOBAL__N_19k_combineILi1EDF16_EEvPKT0_PKiPKfS8_Pviiii")
     assert not P.is_library_kernel(P.COPY_KERNEL)
+
+
+def test_counter_summary_means_and_shares(tmp_path):
+    ka = "void moe::(anonymous namespace)::k_decode_stack<0>(moe::StackArgs)"
+    p1, p2 = tmp_path / "a.csv", tmp_path / "b.csv"
+    _csv(p1, [(ka, "SQ_WAVE_CYCLES", 1000.0), (ka, "SQ_WAVE_CYCLES", 3000.0), (ka, "SQ_WAIT_ANY", 500.0),
+              (ka, "SQ_WAIT_ANY", 1500.0), (P.COPY_KERNEL, "SQ_WAVE_CYCLES", 7.0)])
+    _csv(p2, [(ka, "SQ_ACTIVE_INST_VALU", 400.0), (ka, "SQ_ACTIVE_INST_VALU", 400.0)])
+    t = P.counter_table([str(p1), str(p2)])
+    assert list(t) == ["k_decode_stack<0>"], "only library kernels are summarised"
+    r = t["k_decode_stack<0>"]
+    assert r["dispatches"] == 2
+    assert r["counters"]["SQ_WAVE_CYCLES"] == 2000.0 and r["counters"]["SQ_WAIT_ANY"] == 1000.0
+    assert r["shares"] == {"SQ_WAIT_ANY": 0.5, "SQ_ACTIVE_INST_VALU": 0.2}
+    P.write_counter_summary(str(tmp_path / "c.md"), t, "title", "cmd", "")
+    text = (tmp_path / "c.md").read_text()
+    assert "| waiting on anything | 0.500 (SQ_WAIT_ANY) |" in text
