@@ -239,8 +239,8 @@ def measure(ctx, workload, T_arg, chain_on, routing_over, K, W):
     if chain_on:
         assert not prefill, "--chain is for the decode workloads"
         chain = torch.empty(n_layers * xb, dtype=torch.uint8, device=dev)
-    # T = 1: one moe_stack_forward call per step, which runs all layers in one launch
-    use_stack = not prefill and T == 1
+    # one moe_stack_forward call per step, which runs all layers in one launch: T = 1, and T <= 8 unchained
+    use_stack = not prefill and (T == 1 or (T <= 8 and not chain_on))
 
     def x_in(l, s):
         if chain is not None and l > 0:
@@ -812,7 +812,8 @@ def kernel_work(desc, geo, T, n_kernels, uniq, prefill, out_bytes, stack=False, 
         ]
         return table[:n_kernels]
     if stack:
-        return [(f"k_decode_stack (one launch: {n_layers} layers of router, top-k, gate/up, down, ordered combine)",
+        name = "k_decode_stack" if T == 1 else "k_decode_stack_t"
+        return [(f"{name} (one launch: {n_layers} layers of router, top-k, gate/up, down, ordered combine)",
                  (router + gvec + 3 * p_s + out) * nl + 3 * p_r * u, None)]
     if n_kernels == 1:
         return [("k_decode_a (one launch: router, top-k, gate/up, down, ordered combine)",

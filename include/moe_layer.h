@@ -156,10 +156,10 @@ int moe_layer_forward(const moe_desc* d, int32_t T, const void* x, const void* r
 /*
  * Which kernels run.  moe_layer_forward picks by T and the descriptor:
  *   - T = 1 on the 80B/35B layer shape (hidden 2048, intermediate sizes 512,
- *     int4 codes, bf16 activations and scales, E <= 512, top_k <= 10): ONE
- *     launch, the stack kernel of moe_stack_forward with one layer (router,
- *     top-k, gate/up, down and the ordered combine; blocks exchange the
- *     logits and h as tagged words).
+ *     int4 codes, bf16 activations and scales, E a multiple of 256 up to
+ *     512, top_k <= 10): ONE launch, the stack kernel of moe_stack_forward
+ *     with one layer (router, top-k, gate/up, down and the ordered combine;
+ *     blocks exchange the logits and h as tagged words).
  *   - other T <= 8 with bf16 activations and scales (or float32 activations,
  *     scales and output): the fused decode path.  T = 1 with int4 codes is
  *     one launch; otherwise two (the first computes the router logits, the
@@ -284,12 +284,13 @@ int moe_layer_forward_chain(const moe_desc* desc, int32_t T, const void* x, cons
  * alignment that moe_layer_forward asks of its pointer (checked when
  * n_layers > 1).  x_chain needs out_dtype MOE_F32 and may not overlap x or
  * out.  The result equals n_layers calls of moe_layer_forward (or, with
- * x_chain, moe_layer_forward_chain) bit for bit.  For T = 1 on the 80B/35B
- * layer shape (hidden 2048, intermediate sizes 512, int4 codes, bf16
- * activations and scales, E <= 512, top_k <= 10) the whole stack is ONE
- * launch that keeps every block of the grid resident (the GPU's compute
+ * x_chain, moe_layer_forward_chain) bit for bit.  On the 80B/35B layer
+ * shape (hidden 2048, intermediate sizes 512, int4 codes, bf16 activations
+ * and scales, E a multiple of 256 up to 512, top_k <= 10) the whole stack is
+ * ONE launch for T = 1 (chained or not) and for 2 <= T <= 8 without x_chain;
+ * that launch keeps every block of the grid resident (the GPU's compute
  * units must not be taken by other work; a bounded wait that expires raises
- * MOE_ETIMEOUT in moe_status_check); otherwise the layers run as separate
+ * MOE_ETIMEOUT in moe_status_check).  Otherwise the layers run as separate
  * calls.  The timing hook (moe_set_launch_events) counts the whole stack as
  * one call.  MOE_EINVAL, MOE_ENOMEM, MOE_EHIP as for moe_layer_forward.
  */
@@ -308,7 +309,7 @@ int moe_stack_forward(const moe_desc* d, int32_t n_layers, int32_t T, const void
  * `stream` at the first call on each device, and every call leaves it ready
  * for the next.  Calls that would need more than 16 MiB of workspace
  * (moe_workspace_bytes(d, T) > 16 MiB, e.g. the 80B layer shape beyond
- * about T = 64) return MOE_ENOMEM.  The call makes no device allocation
+ * T = 96) return MOE_ENOMEM.  The call makes no device allocation
  * (no hipMalloc / hipFree), and returns after enqueueing like
  * moe_layer_forward, with the same results bit for bit.
  *   status  optional (NULL or 4-byte aligned device pointer): after the

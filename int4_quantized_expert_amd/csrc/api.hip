@@ -144,6 +144,24 @@ int cached_stack_plan(const moe_desc& d, moe::StackPlan* plan) {
   return it->second.first;
 }
 
+// Plans of the stack kernel for 2..8 tokens, cached per (device, E, k, output dtype).
+int cached_stack_t_plan(const moe_desc& d, moe::StackPlan* plan) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int, int>, std::pair<int, moe::StackPlan>> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ENODEV;
+  const auto key = std::make_tuple(dev, d.n_experts, d.top_k, d.out_dtype);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it == cache.end()) {
+    moe::StackPlan p{};
+    const int rc = moe::stack_t_plan(d, &p);
+    it = cache.emplace(key, std::make_pair(rc, p)).first;
+  }
+  *plan = it->second.second;
+  return it->second.first;
+}
+
 int finish(int rc) {
   if (rc != MOE_OK) {
     hipError_t e = hipGetLastError();
@@ -330,6 +348,7 @@ static int layer_forward(const moe_desc* d, int32_t T, const void* x, const void
       moe::StackCall sc{};
       sc.d = *d;
       sc.n_layers = 1;
+      sc.T = 1;
       sc.x = x;
       sc.router_w = router_w;
       sc.slot_table = slot_table;
@@ -401,6 +420,7 @@ int moe_stack_forward(const moe_desc* d, int32_t n_layers, int32_t T, const void
       moe::StackCall sc{};
       sc.d = *d;
       sc.n_layers = n_layers;
+      sc.T = 1;
       sc.x = x;
       sc.x_stride = x_stride;
       sc.router_w = router_w;
@@ -420,6 +440,32 @@ int moe_stack_forward(const moe_desc* d, int32_t n_layers, int32_t T, const void
       sc.L = L;
       sc.stream = st;
       return finish(moe::launch_decode_stack(sc, sp));
+    }
+  }
+  if (!x_chain && moe::stack_t_supported(*d, T)) {
+    moe::StackPlan sp;
+    if (cached_stack_t_plan(*d, &sp) == MOE_OK) {
+      moe::StackCall sc{};
+      sc.d = *d;
+      sc.n_layers = n_layers;
+      sc.T = T;
+      sc.x = x;
+      sc.x_stride = x_stride;
+      sc.router_w = router_w;
+      sc.router_stride = router_stride;
+      sc.slot_table = slot_table;
+      sc.slot_stride = slot_stride;
+      sc.pool = static_cast<const uint8_t*>(pool_base);
+      sc.shared = static_cast<const uint8_t*>(shared_w);
+      sc.shared_stride = shared_stride;
+      sc.out = out;
+      sc.out_stride = out_stride;
+      sc.ids_out = topk_ids;
+      sc.wts_out = topk_w;
+      sc.ws = static_cast<uint8_t*>(workspace);
+      sc.L = L;
+      sc.stream = st;
+      return finish(moe::launch_decode_stack_t(sc, sp));
     }
   }
   // any other shape or T: the layers one call after another

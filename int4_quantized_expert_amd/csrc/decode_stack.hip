@@ -58,6 +58,7 @@
 
 #include "device_common.h"
 #include "moe_internal.h"
+#include "stack_common.h"
 #include "topk_wave.h"
 
 namespace moe {
@@ -163,27 +164,6 @@ __host__ __device__ inline SLds stack_lds(int E, int rpb) {
   return s;
 }
 
-typedef __attribute__((address_space(3))) uint32_t lds_w32;
-typedef __attribute__((address_space(3))) int32_t lds_i32;
-typedef __attribute__((address_space(3))) uint64_t lds_w64;
-typedef __attribute__((address_space(3))) int64_t lds_i64;
-typedef __attribute__((address_space(3))) uint16_t lds_w16;
-
-__device__ __forceinline__ void store_tag(uint64_t* p, uint32_t bits, uint32_t tag) {
-  __hip_atomic_store(p, (static_cast<uint64_t>(tag) << 32) | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// One tagged word, read past this XCD's L2 (device scope).
-__device__ __forceinline__ uint64_t load_tag(const uint64_t* p) {
-  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Tags only grow within a call and from call to call, so "at least" is a
-// signed difference (safe across wrap-around).
-__device__ __forceinline__ bool tag_ge(uint32_t f, uint32_t tag) { return static_cast<int32_t>(f - tag) >= 0; }
-
-__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 struct StackArgs {
   const uint8_t* x;          // layer l's input at x + l * x_stride (layer 0 only when chained)
   int64_t x_stride;
@@ -209,16 +189,6 @@ struct StackArgs {
   int L, E, k, rpb;
   uint32_t spin_limit;
 };
-
-// Direct copies (global -> LDS, 16 or 4 bytes per lane) of `bytes` contiguous
-// bytes at byte `src` of the buffer `rs` into `dst`.  Lane l of round j copies
-// bytes [j W + l w, + w) (W = 64 w); a round that runs past `bytes` lands in
-// the region's padding.
-template <int W>
-__device__ __forceinline__ void copy_lds(u32x4 rs, uint8_t* dst, uint32_t src, uint32_t bytes, int lane) {
-  for (uint32_t j = 0; j < bytes; j += kWave * W)
-    lds_load<W>(rs, dst + j, src + j + static_cast<uint32_t>(lane) * W, 0);
-}
 
 // n down rows from row r0 of the blob behind `rs` into LDS at D: codes
 // [n][256 B], then scales [n][16 B] and biases [n][16 B] (4-byte direct loads,
@@ -305,35 +275,6 @@ __device__ __forceinline__ void issue_down(const StackArgs& a, const SLds& S, ui
     copy_down_rows(raw_rsrc(blob, ok ? kBlob : 0), lds + S.d[1], (grp % kQG) * (kH / kQG) + mem * kSDR, kSDR, lane);
   }
   copy_down_rows(raw_rsrc(a.shared + l * a.sh_stride, kBlob), lds + S.d[2], grp * (kH / kNG) + mem * kFR, kFR, lane);
-}
-
-// Tagged words read by nthr threads: word i (reader rt takes i = rt + q nthr,
-// q < PER) at addr(i), read until it carries `tag`; put(i, bits) stores its
-// value.  Run by the reading waves only, under a branch on the wave index,
-// with no barrier inside: the copy waves, whose direct loads are still in
-// flight, must never execute the wait that follows these loads.  False on
-// expiry.
-template <int PER, typename A, typename F>
-__device__ __forceinline__ bool read_tagged(int rt, int n, int nthr, uint32_t tag, uint32_t limit, A&& addr, F&& put) {
-  const int tid = rt;
-  uint32_t need = 0;
-#pragma unroll
-  for (int q = 0; q < PER; ++q)
-    if (tid + q * nthr < n) need |= 1u << q;
-  for (uint32_t spins = 0;; ++spins) {
-    uint64_t w[PER];
-#pragma unroll
-    for (int q = 0; q < PER; ++q) w[q] = (need >> q) & 1u ? load_tag(addr(tid + q * nthr)) : 0ull;
-#pragma unroll
-    for (int q = 0; q < PER; ++q)
-      if (((need >> q) & 1u) && static_cast<uint32_t>(w[q] >> 32) == tag) {
-        put(tid + q * nthr, static_cast<uint32_t>(w[q]));
-        need &= ~(1u << q);
-      }
-    if (__ballot(need != 0u) == 0) return true;
-    if (spins >= limit) return false;
-    __builtin_amdgcn_s_sleep(1);
-  }
 }
 
 // After a barrier: true if every reading wave's read succeeded.
@@ -813,7 +754,7 @@ bool stack_supported(const moe_desc& d) {
          d.sb_dtype == kBF16 && d.n_experts <= kMaxE && d.n_experts % kNB == 0 && d.top_k <= kMaxK;
 }
 
-size_t stack_ws_lg() { return kXWords * 8; }
+size_t stack_ws_lg() { return (kXWords > stack_t_ws_words() ? kXWords : stack_t_ws_words()) * 8; }
 size_t stack_ws_x() { return static_cast<size_t>(kNG) * (kH / 2) * 8; }
 
 // Grid and LDS of the stack kernel on the current device: 256 blocks, one per

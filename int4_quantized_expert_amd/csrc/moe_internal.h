@@ -42,7 +42,7 @@ struct WsLayout {
   size_t f_pidx;     // two-launch path: [min(T k, E), T] int32 rank of expert u for token t
   size_t f_epoch;    // two-launch path: [kFusedMaxBlocks] uint32 per-block call counters (inside ctrl)
   size_t f_gflag;    // single-launch decode: [kFusedReplicas][kFusedMaxBlocks] uint32 completion tags
-  size_t s_lg;       // stack decode: tagged words (logits, shared h, each group's h, row sums by unit)
+  size_t s_lg;       // stack decode (either kernel): tagged words (logits, h, row sums)
   size_t s_x;        // stack decode: tagged next-layer input of each group
   size_t p_x16;      // prefill: [T, H] float16 activations in MFMA k order
   size_t p_meta;     // prefill: int32 [0] number of expert tiles
@@ -175,6 +175,7 @@ int launch_prefill_experts(const Call& c);
 struct StackCall {
   moe_desc d;
   int32_t n_layers;
+  int32_t T;              // tokens per layer (1: k_decode_stack, 2..8: k_decode_stack_t)
   const void* x;
   int64_t x_stride;
   const void* router_w;
@@ -188,7 +189,7 @@ struct StackCall {
   int64_t out_stride;
   void* x_chain;
   int64_t chain_stride;
-  int32_t* ids_out;       // optional [n_layers][k]
+  int32_t* ids_out;       // optional [n_layers][T][k]
   float* wts_out;
   uint8_t* ws;
   WsLayout L;
@@ -202,6 +203,13 @@ struct StackPlan {
 
 int stack_plan(const moe_desc& d, StackPlan* plan);
 int launch_decode_stack(const StackCall& c, const StackPlan& plan);
+
+// Stack decode of 2..8 tokens per layer (unchained): the same shapes, its
+// exchange words in the same workspace region (tags grow across both kernels).
+bool stack_t_supported(const moe_desc& d, int T);
+size_t stack_t_ws_words();
+int stack_t_plan(const moe_desc& d, StackPlan* plan);
+int launch_decode_stack_t(const StackCall& c, const StackPlan& plan);
 
 // Two-launch decode (T <= kFusedMaxT).
 bool fused_supported(const moe_desc& d, int T);

@@ -194,3 +194,66 @@ def test_stack_repeat_calls_on_one_workspace():
         assert torch.equal(one[0], out[1, 0])
         outs.append(out)
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("preset,L,T,routing", [("80b", 3, 8, "zipf"), ("80b", 2, 8, "normal"), ("80b", 2, 2, "zipf"),
+                                                ("35b", 3, 5, "zipf")])
+def test_stack_multi_token_bitwise_and_oracle(preset, L, T, routing):
+    """2..8 tokens per layer: one persistent launch for the stack (unchained),
+    equal bit for bit to the staged kernels layer by layer, and to the oracle."""
+    st = Stack(synth.PRESETS[preset], L, T, 70 + T, routing=routing)
+    a = st.run_stack()
+    b = st.run_layers()
+    for p, q in zip(a[:3], b[:3]):
+        assert torch.equal(p, q)
+    for l, data in enumerate(st.layers):
+        y_ref, ids_ref, w_ref, _ = oracle_run(data)
+        check_routing(a[1][l], a[2][l], ids_ref, w_ref)
+        assert check_close(a[0][l], y_ref, data.geo.act) <= 2e-3
+
+
+def test_stack_multi_token_bad_slot_reports_erange_like_layer_calls():
+    st = Stack(synth.PRESETS["35b"], 3, 4, 80)
+    _, ids, _, _ = st.run_stack()
+    slots = st.slots.clone()
+    slots[2, int(ids[2, 1, 0].item())] = st.pool.numel() + 256        # layer 2, token 1's top expert: past the pool
+    L, T, H = st.L, st.T, st.geo.hidden
+    a_out = torch.empty(L, T, H, dtype=torch.float32, device=DEV)
+    b_out = torch.empty_like(a_out)
+    ws = st.ws()
+    M.stack_forward(st.desc, L, T, st.x, st.xb, st.R, st.rb, slots, st.desc.n_experts * 8, st.pool, st.shared,
+                    st.sb, a_out, T * H * 4, ws)
+    torch.cuda.synchronize()
+    with pytest.raises(M.MoeError) as ei:
+        M.status_check(ws)
+    assert ei.value.code == -5
+    for l in range(L):
+        M.layer_forward_staged(st.desc, T, st.x.data_ptr() + l * st.xb, st.R.data_ptr() + l * st.rb, slots[l],
+                               st.pool, st.shared.data_ptr() + l * st.sb, b_out[l], ws)
+    torch.cuda.synchronize()
+    with pytest.raises(M.MoeError):
+        M.status_check(ws)
+    assert torch.equal(a_out, b_out)
+
+
+def test_stack_one_and_many_tokens_share_a_workspace():
+    """The one-token and the multi-token stack kernels keep their exchange
+    words in one workspace region; calls of both, alternating on one
+    workspace, keep giving the same bits."""
+    geo = synth.PRESETS["35b"]
+    s1, s4 = Stack(geo, 2, 1, 81), Stack(geo, 2, 4, 82)
+    H = geo.hidden
+    ws = torch.zeros(M.workspace_bytes(s4.desc, 4), dtype=torch.uint8, device=DEV)
+    M.workspace_init(ws)
+    first = {}
+    for rep in range(3):
+        for st in (s4, s1, s4):
+            out = torch.empty(st.L, st.T, H, dtype=torch.float32, device=DEV)
+            M.stack_forward(st.desc, st.L, st.T, st.x, st.xb, st.R, st.rb, st.slots, st.desc.n_experts * 8, st.pool,
+                            st.shared, st.sb, out, st.T * H * 4, ws)
+            torch.cuda.synchronize()
+            M.status_check(ws)
+            if st.T not in first:
+                first[st.T] = out
+            assert torch.equal(out, first[st.T])
+    assert torch.equal(first[4], s4.run_layers()[0])
