@@ -72,6 +72,10 @@ extern "C" {
                              shared with other work); the output is invalid    */
 #define MOE_EIO (-8)      /* expert store: a file could not be opened, read or
                              written, or it is not a store of the stated shape */
+#define MOE_EOVERFLOW (-9) /* the MFMA prefill path rounded a value outside the
+                             float16 range (an input, an h value or a partial
+                             down row; see its precision notes): the output
+                             holds inf or NaN                                   */
 
 /* Storage dtypes. */
 #define MOE_F32 0
@@ -236,7 +240,8 @@ int moe_set_launch_events(void* const* events, int32_t capacity, int32_t* n_reco
  * Synchronises `stream`, then reports and clears the device-side error flags
  * of `workspace`: MOE_ETIMEOUT if a fused-kernel wait expired, else MOE_ERANGE
  * if any kernel since the last check skipped a pair for a bad slot offset or
- * expert id, else MOE_OK.  Blocking.
+ * expert id, else MOE_EOVERFLOW if the prefill path met a value outside the
+ * float16 range, else MOE_OK.  Blocking.
  */
 int moe_status_check(void* workspace, void* stream);
 
@@ -315,7 +320,9 @@ int moe_stack_forward(const moe_desc* d, int32_t n_layers, int32_t T, const void
  *   status  optional (NULL or 4-byte aligned device pointer): after the
  *           layer, receives this GPU's device error flags (bit 0: a pair
  *           skipped for a bad slot offset or id, MOE_ERANGE; bit 1: a
- *           bounded wait expired, MOE_ETIMEOUT), which are then cleared.
+ *           bounded wait expired, MOE_ETIMEOUT; bit 2: a value outside the
+ *           float16 range in the prefill path, MOE_EOVERFLOW), which are
+ *           then cleared.
  *           With NULL they accumulate unreported.
  * All calls on one GPU share its array: calls that may overlap on one GPU
  * (several streams, several host threads) race and must not be made.

@@ -26,6 +26,7 @@ ERRORS = {
     -6: "MOE_ENOSPC",
     -7: "MOE_ETIMEOUT",
     -8: "MOE_EIO",
+    -9: "MOE_EOVERFLOW",
 }
 
 

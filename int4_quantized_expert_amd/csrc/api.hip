@@ -603,7 +603,9 @@ int moe_status_check(void* workspace, void* stream) {
       return fail(MOE_EHIP, "status clear failed: %s", hipGetErrorString(hipGetLastError()));
     if (flags & 2u)
       return fail(MOE_ETIMEOUT, "a bounded in-kernel wait of the fused decode kernel expired; its output is invalid");
-    return fail(MOE_ERANGE, "a kernel skipped a pair: slot offset outside the pool or expert id outside [0, E)");
+    if (flags & 1u)
+      return fail(MOE_ERANGE, "a kernel skipped a pair: slot offset outside the pool or expert id outside [0, E)");
+    return fail(MOE_EOVERFLOW, "the prefill path rounded a value outside the float16 range; the output holds inf or NaN");
   }
   return ok();
 }

@@ -30,6 +30,7 @@ constexpr int kSegCodes = 32;
 // Error flag bits kept in the workspace control words.
 constexpr uint32_t kErrRange = 1u;     // bad slot offset or expert id; pair skipped
 constexpr uint32_t kErrTimeout = 2u;   // a bounded in-kernel wait expired
+constexpr uint32_t kErrF16 = 4u;       // prefill: a value rounded to float16 left its range (inf or NaN)
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

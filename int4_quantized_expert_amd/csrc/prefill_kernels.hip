@@ -128,6 +128,12 @@ __device__ __forceinline__ h8v dq_int8(uint32_t w0, uint32_t w1, h2v s, h2v b, u
   return __builtin_bit_cast(h8v, o);
 }
 
+// True if either float16 half of w is inf or NaN (exponent all ones): a value
+// rounded to float16 here left the range the prefill path needs.
+__device__ __forceinline__ bool f16_bad(uint32_t w) {
+  return (w & 0x7c00u) == 0x7c00u || (w & 0x7c000000u) == 0x7c000000u;
+}
+
 __device__ __forceinline__ f4v mfma16(h8v a, h8v b, f4v c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
 // ---------------------------------------------------------------------------
@@ -244,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void k_pf_xprep(const uint16_t* __restric
                                                       int H, const int32_t* __restrict__ ids,
                                                       const int32_t* __restrict__ erank,
                                                       const int32_t* __restrict__ estart, int np,
-                                                      int32_t* __restrict__ plist) {
+                                                      int32_t* __restrict__ plist, uint32_t* __restrict__ flags) {
   const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   for (size_t p = i; p < static_cast<size_t>(np); p += static_cast<size_t>(gridDim.x) * blockDim.x) {
     const int r = erank[p];
@@ -262,6 +268,7 @@ __global__ __launch_bounds__(kThreads) void k_pf_xprep(const uint16_t* __restric
     const _Float16 hi = static_cast<_Float16>(__uint_as_float(v[m] & 0xffff0000u));
     h[m] = h2_bits(h2v{lo, hi});
   }
+  if (f16_bad(h[0]) || f16_bad(h[1]) || f16_bad(h[2]) || f16_bad(h[3])) raise_error(flags, kErrF16);
   x16[t * g_row + chunk_of(g8)] = permute8<BITS>(h);
 }
 
@@ -884,6 +891,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
             const _Float16 h1 = static_cast<_Float16>(silu(acc[0][rr][ct][2 * i + 1]) * acc[1][rr][ct][2 * i + 1]);
             o[i] = h2_bits(h2v{h0, h1});
           }
+          if (f16_bad(o[0]) || f16_bad(o[1])) raise_error(a.flags, kErrF16);
           *reinterpret_cast<uint2*>(hr + 8 * chunk_of(g8) + 4 * (q & 1)) = make_uint2(o[0], o[1]);
         }
       }
@@ -1014,6 +1022,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_down(PfArgs a) {
           for (int rr = 0; rr < 4; ++rr) {
             const h2v lo = {static_cast<_Float16>(acc[rr][ct][0]), static_cast<_Float16>(acc[rr][ct][1])};
             const h2v hi = {static_cast<_Float16>(acc[rr][ct][2]), static_cast<_Float16>(acc[rr][ct][3])};
+            if (f16_bad(h2_bits(lo)) || f16_bad(h2_bits(hi))) raise_error(a.flags, kErrF16);
             *reinterpret_cast<uint2*>(pr + 16 * rr) = make_uint2(h2_bits(lo), h2_bits(hi));
           }
         }
@@ -1212,10 +1221,10 @@ int launch_prefill_experts(const Call& c) {
   int32_t* plist = const_cast<int32_t*>(a.plist);
   if (d.bits == 4)
     launch_kernel(k_pf_xprep<4>, xgrid, dim3(kThreads), 0, c.stream, x, x16, c.T, d.hidden, c.ids,
-                  static_cast<const int32_t*>(erank), static_cast<const int32_t*>(estart), np, plist);
+                  static_cast<const int32_t*>(erank), static_cast<const int32_t*>(estart), np, plist, a.flags);
   else
     launch_kernel(k_pf_xprep<8>, xgrid, dim3(kThreads), 0, c.stream, x, x16, c.T, d.hidden, c.ids,
-                  static_cast<const int32_t*>(erank), static_cast<const int32_t*>(estart), np, plist);
+                  static_cast<const int32_t*>(erank), static_cast<const int32_t*>(estart), np, plist, a.flags);
   if (d.bits == 4 && d.sb_dtype == kBF16) launch_tiles<4, kBF16>(a, c);
   else if (d.bits == 4) launch_tiles<4, kF32>(a, c);
   else if (d.sb_dtype == kBF16) launch_tiles<8, kBF16>(a, c);

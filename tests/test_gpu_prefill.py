@@ -178,3 +178,25 @@ def test_prefill_bad_expert_id_reports_erange_and_drops_only_that_pair():
     torch.cuda.synchronize()
     M.status_check(ws2)
     assert torch.equal(out_bad, out_zero)
+
+
+@pytest.mark.parametrize("where", ["input", "h"])
+def test_prefill_float16_range_reports_eoverflow(where):
+    """The prefill path keeps x, h and the partial down rows in float16, so
+    they must stay inside its range (reading R11).  A value that leaves it is
+    reported by the status check (MOE_EOVERFLOW) instead of passing silently
+    as inf: an input of 1e5 (over 65504), or inputs of about 3000 on one
+    token, whose h products reach about 1e6 while every input fits."""
+    geo = synth.Geometry(256, 16, 2, 256, 256, 4, "bf16", "bf16")
+    data = make_layer(geo, 23, 0, 32, n_cand=128, margin_scale=PF)
+    dl = upload(data)
+    run(dl, 32)                                   # in range: no flag
+    x = dl.x.clone().view(torch.int16)
+    if where == "input":
+        x[5 * geo.hidden + 17] = 0x47C3           # bf16 1.0e5
+    else:
+        x[:geo.hidden] = 0x453B                   # bf16 2992 on token 0
+    with pytest.raises(M.MoeError) as ei:
+        run(dl, 32, x=x.view(torch.uint8))
+    assert ei.value.code == -9
+    run(dl, 32)                                   # the flag was cleared by the check
