@@ -9,7 +9,8 @@ every odd expert above byte offset 2^32 and the rest below, at a permuted
 placement: outputs, ids and weights must be bitwise equal, and the relocated
 run must also match the oracle.  The cases cover the single-launch T = 1
 decode kernel, the two-launch T = 8 decode, the int8 decode, the staged
-kernels and the MFMA prefill kernels (int4 and int8).
+kernels, the MFMA prefill kernels (int4 and int8) and the stack kernel for
+2..8 tokens.
 """
 
 import numpy as np
@@ -48,5 +49,41 @@ def test_offsets_beyond_4gib_bitwise(preset, T, routing, out, staged, tokens):
     y_ref, ids_ref, w_ref, _ = oracle_run(data, tokens=tokens)
     check_routing(i1, w1, ids_ref, w_ref, tokens=tokens)
     check_close(y1, y_ref, data.geo.act, tokens=tokens)
+    del big, dl2
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T", [2, 8])
+def test_stack_kernel_offsets_beyond_4gib_bitwise(T):
+    """The stack kernel for 2..8 tokens (moe_stack_forward, one layer) at the
+    identity placement and relocated into one pool of more than 4 GiB: the
+    same bits, and the oracle."""
+    import int4_quantized_expert_amd as M
+    from gpu_util import DEV
+    data = make_layer(synth.PRESETS["80b"], 43, T, T, routing="zipf", n_cand=max(96, 16 * T))
+    dl = upload(data)
+    H, k = dl.desc.hidden, dl.desc.top_k
+
+    def stack(d):
+        out = torch.full((1, T, H), float("nan"), dtype=torch.float32, device=DEV)
+        ids = torch.full((1, T, k), -7, dtype=torch.int32, device=DEV)
+        wts = torch.full((1, T, k), float("nan"), dtype=torch.float32, device=DEV)
+        ws = torch.zeros(M.workspace_bytes(d.desc, T), dtype=torch.uint8, device=DEV)
+        M.workspace_init(ws)
+        M.stack_forward(d.desc, 1, T, d.x, 0, d.R, 0, d.slots, 0, d.pool, d.shared, 0, out, 0, ws,
+                        topk_ids=ids, topk_w=wts)
+        torch.cuda.synchronize()
+        M.status_check(ws)
+        return out[0], ids[0], wts[0]
+
+    y0, i0, w0 = stack(dl)
+    big, slots = relocate(dl, data, seed=100 + T)
+    dl2 = upload(data, pool=big, slots=slots)
+    assert dl2.desc.pool_bytes > (1 << 32) and int(dl2.slots.max().item()) > (1 << 32)
+    y1, i1, w1 = stack(dl2)
+    assert torch.equal(y0, y1) and torch.equal(i0, i1) and torch.equal(w0, w1)
+    y_ref, ids_ref, w_ref, _ = oracle_run(data)
+    check_routing(i1, w1, ids_ref, w_ref)
+    check_close(y1, y_ref, data.geo.act)
     del big, dl2
     torch.cuda.empty_cache()
