@@ -285,62 +285,6 @@ __device__ __forceinline__ bool reads_ok(const lds_w32* misc) {
   return ok;
 }
 
-// Block-wide top-k.  Keys are (order key of the logit << 32 | ~id), so a
-// larger key is a larger logit, then a lower id (ties to the lower id); an
-// absent entry is 0 and every real one is at least 1 << 32.
-//
-// The value of lane (lane ^ S) within the wave.
-template <int S>
-__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int lane) {
-  if constexpr (S == 1) {
-    return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xf, 0xf, false);   // quad_perm [1, 0, 3, 2]
-  } else if constexpr (S == 2) {
-    return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xf, 0xf, false);   // quad_perm [2, 3, 0, 1]
-  } else if constexpr (S == 4) {
-    return __builtin_amdgcn_ds_swizzle(v, 0x1F | (4 << 10));     // bit mode, xor 4
-  } else if constexpr (S == 8) {
-    return __builtin_amdgcn_mov_dpp(v, 0x128, 0xf, 0xf, false);  // row_ror:8 (xor 8 within a row)
-  } else if constexpr (S == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return (lane & 16) ? r[0] : r[1];
-  } else {
-    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    return (lane & 32) ? r[0] : r[1];
-  }
-}
-
-// One compare-exchange step of a bitonic sort of the wave's 64 keys into
-// descending lane order: blocks of SIZE lanes, partner at distance S.
-template <int SIZE, int S>
-__device__ __forceinline__ void bitonic_step(uint64_t& key, int lane) {
-  const uint32_t plo = lane_xor<S>(static_cast<uint32_t>(key), lane);
-  const uint32_t phi = lane_xor<S>(static_cast<uint32_t>(key >> 32), lane);
-  const uint64_t pk = (static_cast<uint64_t>(phi) << 32) | plo;
-  const bool desc = (lane & SIZE) == 0;        // this block's direction (all of them for SIZE = 64)
-  const bool lower = (lane & S) == 0;
-  if ((pk > key) == (lower == desc)) key = pk;   // the lower lane keeps the larger key in a descending block
-}
-
-template <int SIZE>
-__device__ __forceinline__ void bitonic_merge(uint64_t& key, int lane) {
-  if constexpr (SIZE >= 64) bitonic_step<SIZE, 32>(key, lane);
-  if constexpr (SIZE >= 32) bitonic_step<SIZE, 16>(key, lane);
-  if constexpr (SIZE >= 16) bitonic_step<SIZE, 8>(key, lane);
-  if constexpr (SIZE >= 8) bitonic_step<SIZE, 4>(key, lane);
-  if constexpr (SIZE >= 4) bitonic_step<SIZE, 2>(key, lane);
-  bitonic_step<SIZE, 1>(key, lane);
-}
-
-__device__ __forceinline__ uint64_t bitonic_sort64(uint64_t key, int lane) {
-  bitonic_merge<2>(key, lane);
-  bitonic_merge<4>(key, lane);
-  bitonic_merge<8>(key, lane);
-  bitonic_merge<16>(key, lane);
-  bitonic_merge<32>(key, lane);
-  bitonic_merge<64>(key, lane);
-  return key;
-}
-
 // Unchained: one wave finishes rows [8 b, 8 b + 8) of layer lf, the ordered
 // combine of the row sums of every unit (tag `tg`) with the weights of that
 // layer.  False if a word never arrived.

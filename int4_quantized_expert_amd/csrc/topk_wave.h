@@ -27,6 +27,44 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 __device__ __forceinline__ uint64_t lane_mask_lt(int lane) { return lane == 0 ? 0ull : (~0ull >> (64 - lane)); }
 
+// The value of lane (lane ^ S) within the wave, by lane moves (DPP, a
+// swizzle, lane swaps) rather than an LDS round trip.
+template <int S>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int lane) {
+  if constexpr (S == 1) {
+    return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xf, 0xf, false);   // quad_perm [1, 0, 3, 2]
+  } else if constexpr (S == 2) {
+    return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xf, 0xf, false);   // quad_perm [2, 3, 0, 1]
+  } else if constexpr (S == 4) {
+    return __builtin_amdgcn_ds_swizzle(v, 0x1F | (4 << 10));     // bit mode, xor 4
+  } else if constexpr (S == 8) {
+    return __builtin_amdgcn_mov_dpp(v, 0x128, 0xf, 0xf, false);  // row_ror:8 (xor 8 within a row)
+  } else if constexpr (S == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
+
+// Largest 64-bit word over the wave; every lane ends with it.
+template <int S>
+__device__ __forceinline__ uint64_t max_step(uint64_t c, int lane) {
+  const uint64_t p = (static_cast<uint64_t>(lane_xor<S>(static_cast<uint32_t>(c >> 32), lane)) << 32) |
+                     lane_xor<S>(static_cast<uint32_t>(c), lane);
+  return p > c ? p : c;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t c, int lane) {
+  c = max_step<1>(c, lane);
+  c = max_step<2>(c, lane);
+  c = max_step<4>(c, lane);
+  c = max_step<8>(c, lane);
+  c = max_step<16>(c, lane);
+  return max_step<32>(c, lane);
+}
+
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -115,22 +153,23 @@ __device__ __forceinline__ void topk_wave_n(const float* lg_, int E, int k, int 
       vals[rank] = lg[id];
     }
   } else {
-    // rare: many candidates lie above the bound
+    // rare: more than kCandMax entries lie at or above the bound (many equal
+    // logits, e.g. a zero input, where every logit is 0).  k rounds of a wave
+    // arg-max over the unique words (key << 32 | ~id): larger key first, then
+    // lower id; each round's maximum travels by lane moves, not through LDS.
     uint32_t taken = 0;
     for (int i = 0; i < k; ++i) {
-      uint32_t bk = 0;
-      int bid = 0x7fffffff;
+      uint64_t best = 0;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int e = lane + j * kWave;
-        if (!((taken >> j) & 1u) && e < E && (key[j] > bk || (key[j] == bk && e < bid))) { bk = key[j]; bid = e; }
+        const uint64_t c = ((taken >> j) & 1u) || key[j] == 0u
+                               ? 0ull
+                               : (static_cast<uint64_t>(key[j]) << 32) | static_cast<uint32_t>(~e);
+        best = c > best ? c : best;
       }
-#pragma unroll
-      for (int mm = kWave / 2; mm > 0; mm >>= 1) {
-        const uint32_t ok = __shfl_xor(bk, mm, kWave);
-        const int oid = __shfl_xor(bid, mm, kWave);
-        if (ok > bk || (ok == bk && oid < bid)) { bk = ok; bid = oid; }
-      }
+      best = wave_max_u64(best, lane);
+      const int bid = static_cast<int>(~static_cast<uint32_t>(best));
       if ((bid & (kWave - 1)) == lane) taken |= 1u << (bid / kWave);
       if (lane == 0) { ids[i] = bid; vals[i] = lg[bid]; }
     }

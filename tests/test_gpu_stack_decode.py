@@ -257,3 +257,20 @@ def test_stack_one_and_many_tokens_share_a_workspace():
                 first[st.T] = out
             assert torch.equal(out, first[st.T])
     assert torch.equal(first[4], s4.run_layers()[0])
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_stack_zero_input_ties_go_to_lowest_ids(T):
+    """A zero token gives E equal logits (all 0), which the top-k takes by its
+    tie path: experts 0..k-1 in order with weights 1/k, and y = 0 (h = 0 for
+    every expert).  Both stack kernels equal the staged ones bit for bit."""
+    st = Stack(synth.PRESETS["80b"], 2, T, 90 + T)
+    st.x.zero_()
+    a = st.run_stack()
+    b = st.run_layers()
+    for p, q in zip(a[:3], b[:3]):
+        assert torch.equal(p, q)
+    k = st.geo.top_k
+    assert torch.equal(a[1].cpu(), torch.arange(k, dtype=torch.int32).expand(st.L, T, k))
+    assert torch.equal(a[2].cpu(), torch.full((st.L, T, k), 1.0 / k, dtype=torch.float32))
+    assert torch.count_nonzero(a[0]).item() == 0
