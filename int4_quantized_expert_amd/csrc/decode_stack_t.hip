@@ -21,10 +21,10 @@
 //      chosen ids), each unit's tokens and their ranks, and the h rows its
 //      down range needs; meanwhile waves 1..7 read the previous layer's row
 //      sums of the block's 8 output rows
-//   G  waves 0..6 stream the block's gate/up pairs in batches of four (the
-//      next batch requested before the current one is computed) and store h
-//      per (token, rank) as tagged words; wave 7 finishes the previous
-//      layer's 8 output rows of every token and copies the next layer's
+//   G  all eight waves stream the block's gate/up pairs (batches of two, of
+//      one unit, in a three-deep ring) and store h per (token, rank) as
+//      tagged words; wave 7 first finishes the previous layer's 8 output
+//      rows of every token, and after its pairs copies the next layer's
 //      static operands into the other LDS copy (then, after G, its x)
 //   H  waves 0..6 request their first down batch, then read the h rows of
 //      their down units into LDS
@@ -72,7 +72,7 @@ constexpr int kMaxK = 10;
 constexpr int kMaxE = 512;
 constexpr int kMaxRpb = kMaxE / kNB;
 constexpr int kMaxU = kMaxT * kMaxK;       // routed units of a layer, at most
-constexpr int kCW = 7;                     // waves 0..6 compute phases G and D
+constexpr int kCW = 7;                     // waves 0..6 compute phase D and read h (phase G: all 8)
 constexpr int kWaveCopy = 7;               // copies operands, finishes the previous layer
 constexpr int kSpb = kI / kNB;             // shared gate/up pairs per block (2)
 constexpr int kSegI = kI / kSegCodes;      // 16 segments per down row
@@ -598,18 +598,18 @@ __global__ __launch_bounds__(kThr) void k_decode_stack_t(StackTArgs a) {
     const int nu = uni(static_cast<int>(misc[kMNU]));
 
     // ------------------------------------------------------------------ G
-    if (wave == kWaveCopy) {
-      if (l > 0 && !dead) finish_combine_t<OUT>(a, S, lds, l - 1, lane);
-      // the next layer's static operands into the other copy, free since
-      // the layer before this one ended (waited for at the end of this one)
-      if (l + 1 < a.L) issue_static_t(a, S, lds, p ^ 1, l + 1, lane);
-    } else {
+    // every wave streams gate/up pairs; wave 7 first finishes the previous
+    // layer's rows and, after its pairs, copies the next layer's static
+    // operands into the other copy (free since the layer before this one
+    // ended; waited for at the end of this one)
+    if (wave == kWaveCopy && l > 0 && !dead) finish_combine_t<OUT>(a, S, lds, l - 1, lane);
+    {
       const int q0 = uni(static_cast<int>(misc[kMRange + 0]));   // this block's pairs, flattened over the units
       const int np = uni(static_cast<int>(misc[kMRange + 1])) - q0;
       const int ug = q0 / kI;                // its unit; pairs from (ug + 1) 512 on are of the next
-      const int npw = wave < np ? (np - wave + kCW - 1) / kCW : 0;   // this wave's pairs: wave + 7 j
+      const int npw = wave < np ? (np - wave + kNW - 1) / kNW : 0;   // this wave's pairs: wave + 8 j
       const int ib = (ug + 1) * kI - q0;     // first local pair of the next unit
-      const int jb = ib <= wave ? 0 : (ib - wave + kCW - 1) / kCW < npw ? (ib - wave + kCW - 1) / kCW : npw;
+      const int jb = ib <= wave ? 0 : (ib - wave + kNW - 1) / kNW < npw ? (ib - wave + kNW - 1) / kNW : npw;
       // every pair of a batch is requested before any is used
       auto load_g = [&](GBatch& B, int j0) {
         const int u = j0 < jb ? ug : ug + 1;
@@ -626,7 +626,7 @@ __global__ __launch_bounds__(kThr) void k_decode_stack_t(StackTArgs a) {
 #pragma unroll
         for (int bb = 0; bb < kGB; ++bb) {
           const int j = j0 + (bb < B.n ? bb : 0);
-          const int row = q0 + wave + kCW * j - u * kI;
+          const int row = q0 + wave + kNW * j - u * kI;
           const int qo = row * kRowQ + 16 * lane;
           B.cg[bb].w[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, qo, 0, 2));
           B.cu[bb].w[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, qo, kQ, 2));
@@ -673,7 +673,7 @@ __global__ __launch_bounds__(kThr) void k_decode_stack_t(StackTArgs a) {
 #pragma unroll
             for (int bb = 0; bb < kGB; ++bb)
               if (bb < B.n)
-                store_tag(huw + (static_cast<size_t>(t) * k + r) * kI + q0 + wave + kCW * (B.j0 + bb) - u * kI,
+                store_tag(huw + (static_cast<size_t>(t) * k + r) * kI + q0 + wave + kNW * (B.j0 + bb) - u * kI,
                           __float_as_uint(h[bb]), tag);
           }
         }
@@ -686,6 +686,7 @@ __global__ __launch_bounds__(kThr) void k_decode_stack_t(StackTArgs a) {
         ring3(npw, j, h1, b0, b1, b2, load_g, compute_g);
       }
     }
+    if (wave == kWaveCopy && l + 1 < a.L) issue_static_t(a, S, lds, p ^ 1, l + 1, lane);
 
     // ------------------------------------------------------------------ H
     __syncthreads();                 // every h store is issued; x is no longer read
