@@ -25,10 +25,11 @@
 //      one unit, in a three-deep ring) and store h per (token, rank) as
 //      tagged words; wave 7 first finishes the previous layer's 8 output
 //      rows of every token, and after its pairs copies the next layer's
-//      static operands into the other LDS copy (then, after G, its x)
-//   H  waves 0..6 request their first down batch, then read the h rows of
-//      their down units into LDS
-//   D  waves 0..6 stream the block's down rows in passes of four, each row
+//      static operands into the other LDS copy
+//   H  every wave requests its share of the next layer's x and its first
+//      two down batches, then reads its share of the down units' h rows
+//      into LDS
+//   D  all eight waves stream the block's down rows in passes of four, each row
 //      against the h of every token of its unit; row sums go out as tagged
 //      words by (token, rank)
 // The combine of layer l (ranks ascending, then sigma times the shared unit)
@@ -72,7 +73,7 @@ constexpr int kMaxK = 10;
 constexpr int kMaxE = 512;
 constexpr int kMaxRpb = kMaxE / kNB;
 constexpr int kMaxU = kMaxT * kMaxK;       // routed units of a layer, at most
-constexpr int kCW = 7;                     // waves 0..6 compute phase D and read h (phase G: all 8)
+constexpr int kCW = 8;                     // waves that read h and compute phase D
 constexpr int kWaveCopy = 7;               // copies operands, finishes the previous layer
 constexpr int kSpb = kI / kNB;             // shared gate/up pairs per block (2)
 constexpr int kSegI = kI / kSegCodes;      // 16 segments per down row
@@ -226,10 +227,13 @@ __device__ __forceinline__ void issue_static_t(const StackTArgs& a, const TLds& 
 }
 
 // Layer l's T inputs into LDS (one copy: requested once the current layer's
-// gate/up phase no longer reads it).
-__device__ __forceinline__ void issue_x_t(const StackTArgs& a, const TLds& S, uint8_t* lds, int l, int lane) {
-  const uint32_t bytes = static_cast<uint32_t>(a.T) * kH * 2;
-  copy_lds<16>(raw_rsrc(a.x + l * a.x_stride, bytes), lds + S.x, 0, bytes, lane);
+// gate/up phase no longer reads it), 1 KB rounds w0, w0 + nw, ... of them.
+__device__ __forceinline__ void issue_x_t(const StackTArgs& a, const TLds& S, uint8_t* lds, int l, int w0, int nw,
+                                          int lane) {
+  const uint32_t bytes = static_cast<uint32_t>(a.T) * kH * 2;   // a multiple of 1 KB
+  const u32x4 rs = raw_rsrc(a.x + l * a.x_stride, bytes);
+  for (uint32_t j = static_cast<uint32_t>(w0) * 1024u; j < bytes; j += static_cast<uint32_t>(nw) * 1024u)
+    lds_load<16>(rs, lds + S.x + j, j + static_cast<uint32_t>(lane) * 16u, 0);
 }
 
 // Blob of routed unit u and whether its offset is usable (an unusable blob
@@ -445,7 +449,7 @@ __global__ __launch_bounds__(kThr) void k_decode_stack_t(StackTArgs a) {
 
   if (wave == kWaveCopy) {
     issue_static_t(a, S, lds, 0, 0, lane);
-    issue_x_t(a, S, lds, 0, lane);
+    issue_x_t(a, S, lds, 0, 0, 1, lane);
     wait_vm0();
   }
   __syncthreads();
@@ -690,7 +694,7 @@ __global__ __launch_bounds__(kThr) void k_decode_stack_t(StackTArgs a) {
 
     // ------------------------------------------------------------------ H
     __syncthreads();                 // every h store is issued; x is no longer read
-    if (wave == kWaveCopy && l + 1 < a.L) issue_x_t(a, S, lds, l + 1, lane);
+    if (l + 1 < a.L) issue_x_t(a, S, lds, l + 1, wave, kNW, lane);
     const int pa = uni(static_cast<int>(misc[kMRange + 2]));   // this block's down passes, flattened
     const int npass = uni(static_cast<int>(misc[kMRange + 3])) - pa;
     const int r0 = kRpp * pa;                     // its first row
@@ -727,7 +731,8 @@ __global__ __launch_bounds__(kThr) void k_decode_stack_t(StackTArgs a) {
     const bool hd1 = npw_d > 0 && jd < npw_d;
     if (hd1) jd += load_d(d1, jd);
     {
-      // waves 0..6 read the staged h rows (wave 7 has copies in flight)
+      // every wave reads a share of the staged h rows (the wait for them
+      // also covers the wave's input copy and first down batches)
       lds_f32* hs = (lds_f32*)(lds + S.hs);
       const int nh = uni(static_cast<int>(misc[kMNH]));
       bool ok = !dead;
@@ -750,6 +755,7 @@ __global__ __launch_bounds__(kThr) void k_decode_stack_t(StackTArgs a) {
         }
         if (lane == 0) misc[kMRd + wave] = r ? 1u : 0u;
       }
+      wait_vm0();   // this wave's share of the next layer's inputs has landed
       __syncthreads();
       dead = dead || !(ok && reads_ok_w(misc, 0, kCW));
       if (tid < nh * kSegI) {
