@@ -13,13 +13,14 @@
 //     block, from LDS), its down rows 8 per block.
 // Per layer:
 //   R  two router rows and two shared gate/up rows per block, from LDS
-//      (copied there while the previous layer ran); block 0 also sigma(g . x)
+//      (copied there while the previous layer ran); block 0 also sigma(g . x);
+//      meanwhile one wave requests the next layer's static operands into the
+//      other LDS copy
 //   K  every block reads the E logits and takes top-k and the renormalised
 //      weights itself (one wave)
 //   G  the block's gate/up row pairs of its whole and split unit, every load
 //      of a wave requested at once; meanwhile one wave copies the block's
-//      down rows of its three units into LDS and another the next layer's
-//      static operands
+//      down rows of its three units into LDS
 //   H  h of the whole unit (from the group), the split unit (from its four
 //      groups) and the shared expert (from R)
 //   D  the block's 88 down rows, stored as row sums per unit
@@ -123,6 +124,7 @@ struct SLds {
   uint32_t d[3];   // down rows of the whole, split and shared unit: codes [n][256 B], scales [n][16 B],
                    // biases [n][16 B] (n = 64, 16, 8)
   uint32_t hs;     // [3][kSegI][kPad] floats: h of the whole, split and shared unit
+  uint32_t hsum;   // [3][kSegI] floats: the segment sums of hs
   uint32_t lg;     // [kMaxE] logits
   uint32_t cand;   // [8 waves][16] top-k candidates
   uint32_t misc;   // see below
@@ -155,6 +157,7 @@ __host__ __device__ inline SLds stack_lds(int E, int rpb) {
   s.d[1] = t;   t += kSDR * kDRowB;
   s.d[2] = t;   t += kFR * kDRowB;
   s.hs = t;     t += 3 * kSegI * kPad * 4;
+  s.hsum = t;   t += r256(3 * kSegI * 4);
   s.lg = t;     t += kMaxE * 4;
   s.cand = t;   t += kNW * kTopC * 8;
   s.misc = t;   t += r256(kMWords * 4);
@@ -330,31 +333,12 @@ __device__ __forceinline__ bool finish_rows(const StackArgs& a, const SLds& S, u
   return true;
 }
 
-// One pass of four down rows: LDS rows lr (this lane's row, lane / 16 of
-// the pass) of the nrow staged at Dq (codes, then scales, then biases), the
-// lane's segment lane % 16 against its h segment hv (sum hsv).  Every lane of
-// the row ends with the row's sum.
-__device__ __forceinline__ float down_row(const uint8_t* Dq, int nrow, int lr, int seg, const float (&hv)[1][kSegCodes],
-                                          float hsv) {
-  const lds_w16* sbw = (const lds_w16*)(Dq + nrow * kDRowQ);
-  Seg<4> code;
-  code.w[0] = *(const lds_u32x4*)((const lds_u8*)(Dq) + lr * kDRowQ + 16 * seg);
-  const int gi = lr * (kI / 64) + seg / 2;
-  const float sc = bf16_to_f32(sbw[gi]);
-  const float bi = bf16_to_f32(sbw[nrow * (kI / 64) + gi]);
-  float qv[1];
-  seg_qdot_nt<4, 1>(code, hv, qv);
-  float acc = 0.f;
-  acc += seg_value(sc, bi, qv[0], hsv);
-  return group_sum(acc, kSegI);
-}
-
 template <int OUT>
 __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
   const SLds S = stack_lds(a.E, a.rpb);
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
+  int tid = threadIdx.x;
+  int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int b = blockIdx.x;
   const int grp = b % kNG, mem = b / kNG;
@@ -378,6 +362,9 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
   __syncthreads();
 
   for (int l = 0; l < a.L; ++l) {
+    // lane-derived addresses are formed again in every layer instead of being
+    // held in registers across the loop (which spills them to scratch)
+    asm volatile("" : "+v"(lane), "+v"(tid));
     const uint32_t tag = epoch + 1u + static_cast<uint32_t>(l);
     const int p = l & 1;                                     // copy of the exchange regions
     uint8_t* P = lds + p * S.p_bytes;                        // this layer's static operands
@@ -387,6 +374,9 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
     uint64_t* const part = a.xw + kXPart + static_cast<size_t>(p) * kPartW;
 
     // ------------------------------------------------------------------ R
+    // the next layer's static operands into the other copy, free since the
+    // layer before this one ended (waited for at the end of this one)
+    if (wave == kWaveStatic && l + 1 < a.L) issue_static(a, S, lds, p ^ 1, l + 1, lane);
     // per lane: its 32-value segment of x (lane = segment for H = 2048)
     ActRaw<kBF16> xr;
     load_lds_act_bf16(xl, lane, xr);
@@ -545,10 +535,6 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
             }
           }
         }
-      } else if (wave == kWaveStatic) {
-        // the next layer's static operands into the other copy, free since
-        // the layer before this one ended (waited for at the end of this one)
-        if (l + 1 < a.L) issue_static(a, S, lds, p ^ 1, l + 1, lane);
       } else if (wave == kWaveDown) {
         issue_down(a, S, lds, misc, grp, mem, has_w, has_s, l, lane);
       }
@@ -579,18 +565,29 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
       }
       __syncthreads();
       dead = dead || !(ok && reads_ok(misc));
+      if (tid < 3 * kSegI) {
+        float v[kSegCodes];
+        load_lds_seg(hs + static_cast<size_t>(tid) * kPad, 0, v);
+        ((lds_f32*)(lds + S.hsum))[tid] = seg_sum(v);
+      }
+      __syncthreads();
     }
     if (!dead) {
       // passes of four rows: 16 of the whole unit, 4 of the split unit, 2 of
       // the shared expert (absent units take none); wave w takes passes w,
       // w + 8, w + 16.  Lane: segment lane % 16 of row lane / 16 of the pass.
+      // The h segment sums were formed once in phase H.
       const int npw_ = has_w ? kDPM / kRpp : 0, nps = has_s ? kSDR / kRpp : 0;
       const int npass = npw_ + nps + kFR / kRpp;
       const int sub = lane / kSegI, seg = lane % kSegI;
       const float* hs = reinterpret_cast<const float*>(lds + S.hs);
+      const lds_f32* hsum = (const lds_f32*)(lds + S.hsum);
+      auto unit_of = [&](int pp) { return pp < npw_ ? 0 : pp < npw_ + nps ? 1 : 2; };   // wave-uniform
+      auto row_of = [&](int pp, int t) {   // row in the unit's LDS rows
+        return (pp - (t == 0 ? 0 : t == 1 ? npw_ : npw_ + nps)) * kRpp + sub;
+      };
       for (int pp = wave; pp < npass; pp += kNW) {
-        const int t = pp < npw_ ? 0 : pp < npw_ + nps ? 1 : 2;                         // wave-uniform
-        const int lr = (pp - (t == 0 ? 0 : t == 1 ? npw_ : npw_ + nps)) * kRpp + sub;   // row in the unit's LDS rows
+        const int t = unit_of(pp), lr = row_of(pp, t);
         const int nrow = t == 0 ? kDPM : t == 1 ? kSDR : kFR;
         const int u = t == 0 ? grp : t == 1 ? ur_s : k;
         const int row = t == 0 ? mem * kDPM + lr
@@ -598,10 +595,20 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
                                  : grp * (kH / kNG) + mem * kFR + lr;
         bool valid = true;
         if (t < 2) (void)unit_blob(a, misc, u, l, valid);
+        const uint8_t* Dq = lds + (t == 0 ? S.d[0] : t == 1 ? S.d[1] : S.d[2]);
+        const lds_w16* sbw = (const lds_w16*)(Dq + nrow * kDRowQ);
         float hv[1][kSegCodes];
         load_lds_seg(hs + (static_cast<size_t>(t) * kSegI + seg) * kPad, 0, hv[0]);
-        const float hsv = seg_sum(hv[0]);
-        const float v = down_row(lds + (t == 0 ? S.d[0] : t == 1 ? S.d[1] : S.d[2]), nrow, lr, seg, hv, hsv);
+        const float hsv = hsum[t * kSegI + seg];
+        Seg<4> code;
+        code.w[0] = *(const lds_u32x4*)((const lds_u8*)(Dq) + lr * kDRowQ + 16 * seg);
+        const int gi = lr * (kI / 64) + seg / 2;
+        const float sc = bf16_to_f32(sbw[gi]), bi = bf16_to_f32(sbw[nrow * (kI / 64) + gi]);
+        float qv[1];
+        seg_qdot_nt<4, 1>(code, hv, qv);
+        float acc = 0.f;
+        acc += seg_value(sc, bi, qv[0], hsv);
+        const float v = group_sum(acc, kSegI);
         if (seg == 0) store_tag(part + static_cast<size_t>(u) * kH + row, __float_as_uint(valid ? v : 0.f), tag);
       }
     }
