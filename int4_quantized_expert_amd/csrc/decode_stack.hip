@@ -81,9 +81,8 @@ constexpr int kSHP = kI / (kQG * kNM);     // gate/up row pairs of a split unit 
 constexpr int kSDR = kH / (kQG * kNM);     // down rows of a split unit per block (16)
 constexpr int kFR = kH / kNB;              // shared down rows per block, and output rows a block
                                            // finishes when unchained (8)
-constexpr int kWGW = 5;                    // waves 0..4 take the whole unit's pairs, wave 5 the split unit's
-constexpr int kGW = kWGW + 1;
-constexpr int kMaxG = (kHPM + kWGW - 1) / kWGW;        // pairs per wave, at most (4)
+constexpr int kGA = 4;                     // waves 0..3 compute phase G
+constexpr int kPW = kHPM / kGA;            // whole-unit pairs per phase-G wave (4), plus one split pair
 constexpr int kWaveStatic = 6;             // copies the next layer's static operands
 constexpr int kWaveDown = 7;               // copies the down operands
 constexpr int kWaveFin = 1;                // finishes the previous layer's rows (unchained)
@@ -104,7 +103,7 @@ constexpr int kRdWaves = 6;                // waves that read exchanged words (0
 constexpr int kRdThr = kRdWaves * kWave;
 constexpr int kSigW = (kMaxK + 1) * kH;    // sigma's word in a row-sum copy
 constexpr int kPartW = kSigW + 64;         // words of one row-sum copy
-static_assert(kSpb == 2 && kMaxG == kSHP && kMaxK <= kNG + kQuads && kFR == 8, "grid shape");
+static_assert(kSpb == 2 && kSHP == kGA && kPW % 2 == 0 && kMaxK <= kNG + kQuads && kFR == 8, "grid shape");
 
 // Exchange regions (word offsets into the one tagged-word buffer).
 constexpr size_t kXLg = 0;                                      // [2][kLgRep][kMaxE] logits
@@ -473,67 +472,70 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
 
     // ------------------------------------------------------------------ G
     {
-      // waves 0..4: the whole unit's row pairs [16 m, 16 m + 16), every fifth
-      // from w; wave 5: the split unit's four pairs [128 (g % 4) + 4 m, + 4).
-      // One descriptor per wave, every load requested before any compute.
-      const bool split = wave == kWGW;
-      const bool gw = wave < kWGW ? has_w : (split && has_s);
-      const int q0 = split ? (grp % kQG) * (kI / kQG) + mem * kSHP : mem * kHPM + wave;
-      const int qs = split ? 1 : kWGW;
-      const int npw = !gw ? 0 : split ? kSHP : (kHPM - wave + kWGW - 1) / kWGW;   // this wave's pairs
-      Seg<4> cg[kMaxG], cu[kMaxG];
-      uint32_t sg[kMaxG], su[kMaxG], bg[kMaxG], bu[kMaxG];
-      bool vv = false;
+      // waves 0..3 (the older wave of each SIMD, which issues first): pairs
+      // w + 4 j (j < 4) of the whole unit's [16 m, 16 m + 16) and pair w of
+      // the split unit's [128 (g % 4) + 4 m, + 4).  One descriptor per unit,
+      // every load requested before any compute; an absent unit's descriptor
+      // is empty and reads zeros.
+      const bool gw = wave < kGA && (has_w || has_s);
+      auto pair_row = [&](int j) {
+        return j < kPW ? mem * kHPM + wave + kGA * j : (grp % kQG) * (kI / kQG) + mem * kSHP + wave;
+      };
+      Seg<4> cg[kPW + 1], cu[kPW + 1];
+      uint32_t sg[kPW + 1], su[kPW + 1], bg[kPW + 1], bu[kPW + 1];
+      bool vw = false, vs = false;
       if (gw) {
-        bool ok;
-        const uint8_t* blob = unit_blob(a, misc, split ? ur_s : grp, l, ok);
-        vv = ok;
-        if (!ok) bad = true;
-        // one descriptor over the blob (an unusable one reads zeros); the
-        // plane offsets go in the scalar offset, the lane's in the vector one
-        const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blob), 0, ok ? static_cast<int>(kBlob) : 0, 0x00020000);
+        bool okw = false, oks = false;
+        const uint8_t* blw = has_w ? unit_blob(a, misc, grp, l, okw) : a.pool;
+        const uint8_t* bls = has_s ? unit_blob(a, misc, ur_s, l, oks) : a.pool;
+        if ((has_w && !okw) || (has_s && !oks)) bad = true;
+        vw = okw;
+        vs = oks;
+        // the plane offsets go in the scalar offset, the lane's in the vector one
+        const __amdgpu_buffer_rsrc_t rsw =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blw), 0, okw ? static_cast<int>(kBlob) : 0, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rss =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(bls), 0, oks ? static_cast<int>(kBlob) : 0, 0x00020000);
 #pragma unroll
-        for (int j = 0; j < kMaxG; ++j) {
-          cg[j].w[0] = u32x4{0u, 0u, 0u, 0u};
-          cu[j].w[0] = u32x4{0u, 0u, 0u, 0u};
-          sg[j] = su[j] = bg[j] = bu[j] = 0u;
-          if (j < npw) {
-            const int rr = q0 + qs * j;
-            const int qo = rr * kRowQ + 16 * lane;
-            cg[j].w[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, qo, 0, 2));
-            cu[j].w[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, qo, kQ, 2));
-            const int si = (rr * (kH / 64) + lane / 2) * 2;
-            sg[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, si, 3 * kQ, 0);
-            su[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, si, 3 * kQ + kS, 0);
-            bg[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, si, 3 * kQ + 3 * kS, 0);
-            bu[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, si, 3 * kQ + 4 * kS, 0);
-          }
+        for (int j = 0; j <= kPW; ++j) {
+          const __amdgpu_buffer_rsrc_t rs = j < kPW ? rsw : rss;
+          const int rr = pair_row(j);
+          const int qo = rr * kRowQ + 16 * lane;
+          cg[j].w[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, qo, 0, 2));
+          cu[j].w[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, qo, kQ, 2));
+          const int si = (rr * (kH / 64) + lane / 2) * 2;
+          sg[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, si, 3 * kQ, 0);
+          su[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, si, 3 * kQ + kS, 0);
+          bg[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, si, 3 * kQ + 3 * kS, 0);
+          bu[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, si, 3 * kQ + 4 * kS, 0);
         }
       }
       __syncthreads();   // the down copies start after every phase-G load is requested
       if (gw) {
-        uint64_t* const hx = split ? a.xw + kXHq + static_cast<size_t>(grp / kQG) * kI : a.xw + kXHx + static_cast<size_t>(grp) * kI;
-        // two pairs at a time, with no branch between them
+        uint64_t* const hw = a.xw + kXHx + static_cast<size_t>(grp) * kI;
+        uint64_t* const hq = a.xw + kXHq + static_cast<size_t>(grp / kQG) * kI;
+        auto pair_h = [&](int j, bool v) {
+          const QPairs pg = qpairs_bf16(cg[j]), pu = qpairs_bf16(cu[j]);
+          float accg = 0.f, accu = 0.f, g, uu;
+          accg += seg_value_d2(raw_value<kBF16>(sg[j]), raw_value<kBF16>(bg[j]), dot2_seg(pg, xr), xs);
+          accu += seg_value_d2(raw_value<kBF16>(su[j]), raw_value<kBF16>(bu[j]), dot2_seg(pu, xr), xs);
+          gu_sums_w<kWave>(accg, accu, kWave, g, uu);
+          return v ? silu(g) * uu : 0.f;
+        };
+        if (has_w) {
+          // two pairs at a time, with no branch between them
 #pragma unroll
-        for (int j = 0; j < kMaxG; j += 2) {
-          if (j < npw) {
-            float g[2], uu[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              const QPairs pg = qpairs_bf16(cg[j + t]), pu = qpairs_bf16(cu[j + t]);
-              float accg = 0.f, accu = 0.f;
-              accg += seg_value_d2(raw_value<kBF16>(sg[j + t]), raw_value<kBF16>(bg[j + t]), dot2_seg(pg, xr), xs);
-              accu += seg_value_d2(raw_value<kBF16>(su[j + t]), raw_value<kBF16>(bu[j + t]), dot2_seg(pu, xr), xs);
-              gu_sums_w<kWave>(accg, accu, kWave, g[t], uu[t]);
-            }
-            const float h0 = vv ? silu(g[0]) * uu[0] : 0.f;
-            const float h1 = vv ? silu(g[1]) * uu[1] : 0.f;
+          for (int j = 0; j < kPW; j += 2) {
+            const float h0 = pair_h(j, vw), h1 = pair_h(j + 1, vw);
             if (lane == 0) {
-              store_tag(hx + q0 + qs * j, __float_as_uint(h0), tag);
-              if (j + 1 < npw) store_tag(hx + q0 + qs * (j + 1), __float_as_uint(h1), tag);
+              store_tag(hw + pair_row(j), __float_as_uint(h0), tag);
+              store_tag(hw + pair_row(j + 1), __float_as_uint(h1), tag);
             }
           }
+        }
+        if (has_s) {
+          const float h = pair_h(kPW, vs);
+          if (lane == 0) store_tag(hq + pair_row(kPW), __float_as_uint(h), tag);
         }
       } else if (wave == kWaveDown) {
         issue_down(a, S, lds, misc, grp, mem, has_w, has_s, l, lane);
