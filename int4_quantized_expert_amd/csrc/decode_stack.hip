@@ -449,12 +449,11 @@ __global__ __launch_bounds__(kThr) void k_decode_stack(StackArgs a) {
     // ranked exactly, the weights in rank order), then the chosen experts'
     // blob offsets; meanwhile wave 1 finishes the previous layer's rows
     if (wave == 0) {
-      topk_wave_n<8>(lg, E, k, lane, reinterpret_cast<uint64_t*>(lds + S.cand),
-                     reinterpret_cast<int32_t*>(reinterpret_cast<uint32_t*>(lds + S.misc) + kMIds),
-                     reinterpret_cast<float*>(reinterpret_cast<uint32_t*>(lds + S.misc) + kMVals + p * kMaxK));
+      const int e = topk_wave_n<8>(lg, E, k, lane, reinterpret_cast<uint64_t*>(lds + S.cand),
+                                   reinterpret_cast<int32_t*>(reinterpret_cast<uint32_t*>(lds + S.misc) + kMIds),
+                                   reinterpret_cast<float*>(reinterpret_cast<uint32_t*>(lds + S.misc) + kMVals + p * kMaxK));
       const lds_i64* slot = (const lds_i64*)(P + S.p_slot);
-      if (lane < k) {
-        const int e = static_cast<int>(misc[kMIds + lane]);
+      if (lane < k) {   // lane r holds rank r's id
         ((lds_i64*)(misc + kMOff))[lane] = slot[e];
         if (b == 0) {
           if (a.ids_out) a.ids_out[static_cast<size_t>(l) * k + lane] = e;

@@ -74,23 +74,29 @@ __device__ __forceinline__ void wave_sync_lds() {
 // ---------------------------------------------------------------------------
 // Top-k of one token on one wave.
 //  1. A threshold from the per-lane maxima: the k-th largest lane maximum,
-//     found by bisection on the top 16 bits of the order key, is a lower
-//     bound of the k-th largest logit, so every top-k logit is at or above it.
+//     found on the top 16 bits of the order key two bits a step (three
+//     independent ballots per step), is a lower bound of the k-th largest
+//     logit, so every top-k logit is at or above it.
 //  2. The candidates at or above it (usually a few more than k) are packed as
 //     64-bit (key << 32 | ~id) words, so that "larger word" means "larger
-//     logit, then lower id", and ranked exactly against each other.
+//     logit, then lower id", and ranked exactly against each other.  The
+//     ranks of the candidates and the indices of the other lanes form a
+//     permutation of the lanes, so one lane permute hands rank r's logit and
+//     id to lane r without a trip through LDS memory.
 //  3. If more than kCandMax candidates qualify, k rounds of a wave arg-max
 //     finish the job.
 // Output: ids[0..k) and vals[0..k) = renormalised weights p_i, formed with the
-// same operations and order as the staged kernel.  lg, cand, ids and vals
-// must be in LDS.  NJ = logits per lane (E <= 64 NJ); the code is straight-
-// line over NJ so that every load and ballot is issued without waiting.
+// same operations and order as the staged kernel; lane r < k also returns the
+// id of rank r.  lg, cand, ids and vals must be in LDS.  NJ = logits per lane
+// (E <= 64 NJ); the code is straight-line over NJ so that every load and
+// ballot is issued without waiting.
 template <int NJ>
-__device__ __forceinline__ void topk_wave_n(const float* lg_, int E, int k, int lane, uint64_t* cand_, int32_t* ids_,
-                                            float* vals_) {
+__device__ __forceinline__ int topk_wave_n(const float* lg_, int E, int k, int lane, uint64_t* cand_, int32_t* ids_,
+                                           float* vals_) {
   const lds_f32* lg = (const lds_f32*)(lg_);
   typedef __attribute__((address_space(3))) uint64_t lds_u64;
   typedef __attribute__((address_space(3))) int32_t lds_i32;
+  typedef __attribute__((address_space(3))) u32x4 lds_v4;
   lds_u64* cand = (lds_u64*)(cand_);
   lds_i32* ids = (lds_i32*)(ids_);
   lds_f32* vals = (lds_f32*)(vals_);
@@ -109,49 +115,63 @@ __device__ __forceinline__ void topk_wave_n(const float* lg_, int E, int k, int 
     key[j] = e < E ? (kv > 1u ? kv : 1u) : 0u;   // every real entry ranks above "no entry"
     lm = key[j] > lm ? key[j] : lm;
   }
+  // the largest theta (top 16 bits) with at least k lane maxima at or above
+  // it; a step settles two bits from the counts at three thresholds
   uint32_t theta = 0;
-  for (int b = 31; b >= 16; --b) {
-    const uint32_t c = theta | (1u << b);
-    if (__popcll(__ballot(lm >= c)) >= static_cast<unsigned>(k)) theta = c;
-  }
-  uint64_t m[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) m[j] = __ballot(key[j] != 0u && key[j] >= theta);
+  for (int b = 30; b >= 16; b -= 2) {
+    const uint32_t c1 = theta | (1u << b), c2 = theta | (2u << b), c3 = theta | (3u << b);
+    const unsigned n1 = __popcll(__ballot(lm >= c1)), n2 = __popcll(__ballot(lm >= c2)),
+                   n3 = __popcll(__ballot(lm >= c3));
+    const unsigned kk = static_cast<unsigned>(k);
+    theta = n3 >= kk ? c3 : n2 >= kk ? c2 : n1 >= kk ? c1 : theta;
+  }
+  // padding first (a wave's LDS writes land in program order, so the
+  // candidates overwrite it): padding never outranks a candidate
+  cand[lane] = 0ull;
   int cnt = 0;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const bool in = (m[j] >> lane) & 1ull;
-    const int pos = cnt + __popcll(m[j] & lane_mask_lt(lane));
+    const bool in = key[j] != 0u && key[j] >= theta;
+    const uint64_t m = __ballot(in);
+    const int pos = cnt + static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
     const int id = lane + j * kWave;
     if (in && pos < kCandMax) cand[pos] = (static_cast<uint64_t>(key[j]) << 32) | static_cast<uint32_t>(~id);
-    cnt += __popcll(m[j]);
+    cnt += __popcll(m);
   }
+  float v = 0.f;   // lane r < k: rank r's logit
+  int myid = 0;    // lane r < k: rank r's id
   if (cnt <= kCandMax) {
     wave_sync_lds();
-    if (lane >= cnt) cand[lane] = 0ull;                 // padding never outranks a candidate
-    wave_sync_lds();
     const uint64_t mine = cand[lane];
-    int rank = 0;
-    const int cnt8 = (cnt + 7) & ~7;
-    typedef __attribute__((address_space(3))) u32x4 lds_v4;
     const lds_v4* c4 = (const lds_v4*)(cand);
-    for (int d0 = 0; d0 < cnt8; d0 += 8) {
-      u32x4 q[4];
+    int rank = 0;
+    // sixteen candidates per round, all eight reads requested together
+    for (int d0 = 0; d0 < cnt; d0 += 16) {
+      u32x4 q[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) q[i] = c4[d0 / 2 + i];
+      for (int i = 0; i < 8; ++i) q[i] = c4[d0 / 2 + i];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 8; ++i) {
         const uint64_t w0 = (static_cast<uint64_t>(q[i][1]) << 32) | q[i][0];
         const uint64_t w1 = (static_cast<uint64_t>(q[i][3]) << 32) | q[i][2];
         rank += (w0 > mine) ? 1 : 0;
         rank += (w1 > mine) ? 1 : 0;
       }
     }
-    if (lane < cnt && rank < k) {
-      const int id = static_cast<int>(~static_cast<uint32_t>(mine));
+    // candidates go to lane `rank` (ranks 0..cnt-1 are distinct), the other
+    // lanes to themselves: a permutation of the lanes
+    const bool cd = lane < cnt;
+    const int id = static_cast<int>(~static_cast<uint32_t>(mine));
+    float val = 0.f;
+    if (cd && rank < k) {
       ids[rank] = id;
-      vals[rank] = lg[id];
+      val = lg[id];
     }
+    const int dst = 4 * (cd ? rank : lane);
+    v = __int_as_float(__builtin_amdgcn_ds_permute(dst, __float_as_int(val)));
+    myid = __builtin_amdgcn_ds_permute(dst, id);
   } else {
     // rare: more than kCandMax entries lie at or above the bound (many equal
     // logits, e.g. a zero input, where every logit is 0).  k rounds of a wave
@@ -171,16 +191,18 @@ __device__ __forceinline__ void topk_wave_n(const float* lg_, int E, int k, int 
       best = wave_max_u64(best, lane);
       const int bid = static_cast<int>(~static_cast<uint32_t>(best));
       if ((bid & (kWave - 1)) == lane) taken |= 1u << (bid / kWave);
-      if (lane == 0) { ids[i] = bid; vals[i] = lg[bid]; }
+      if (lane == 0) ids[i] = bid;
+      if (lane == i) myid = bid;
     }
+    v = lg[lane < k ? myid : 0];
   }
-  wave_sync_lds();
   // p_i = exp(l_i - l_0) / sum_j exp(l_j - l_0), the sum in rank order from 0
-  const float top = vals[0];
-  const float ex = lane < k ? expf(vals[lane] - top) : 0.f;
+  const float top = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float ex = lane < k ? expf(v - top) : 0.f;
   float sum = 0.f;
   for (int i = 0; i < k; ++i) sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), i));
   if (lane < k) vals[lane] = ex / sum;
+  return myid;
 }
 
 __device__ __forceinline__ void topk_wave(const float* lg, int E, int k, int lane, uint64_t* cand, int32_t* ids,
