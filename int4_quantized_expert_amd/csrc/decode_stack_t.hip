@@ -251,35 +251,38 @@ __device__ __forceinline__ int unit_rank(const lds_w32* misc, int u, int t) {
   return ((const __attribute__((address_space(3))) uint8_t*)(misc + kMUrank))[u * kMaxT + t];
 }
 
+// Inclusive prefix sum over the wave by DPP moves (no LDS crossbar): within
+// each row of 16 lanes by shifts of 1, 2, 4 and 8, then across rows by the
+// broadcasts of lanes 15 and 31.
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 // Wave 0: the layer's units from the chosen ids, each unit's tokens and
 // ranks, the h rows the block's down range needs, and (block 0) the routing
-// record.
+// record.  Every step runs across the lanes (no per-lane loops over bits).
 __device__ __forceinline__ void dispatch_t(const StackTArgs& a, const TLds& S, uint8_t* lds, int p, int l, int lane) {
   lds_w32* misc = (lds_w32*)(lds + S.misc);
   const lds_i64* slot = (const lds_i64*)(lds + p * S.p_bytes + S.p_slot);
   const int T = a.T, k = a.k, b = blockIdx.x;
+  // units in ascending id: lane i < 16 counts the chosen ids in bitmap word i
   const uint32_t word = lane < 16 ? misc[kMBits + lane] : 0u;
-  int pref = 0, nu = 0;
-  for (int i = 0; i < 16; ++i) {
-    const int c = __popc(misc[kMBits + i]);
-    if (i < lane) pref += c;
-    nu += c;
-  }
-  if (lane < 16) {
-    misc[kMPref + lane] = static_cast<uint32_t>(pref);
-    uint32_t w = word;
-    int u = pref;
-    while (w != 0u) {
-      const int bit = __builtin_ctz(w);
-      w &= w - 1u;
-      ((lds_i64*)(misc + kMUoff))[u] = slot[lane * 32 + bit];
-      ++u;
-    }
-  }
+  const int cw = __popc(word);
+  const int incl = wave_scan_incl(cw);
+  const int nu = __builtin_amdgcn_readlane(incl, 15);
+  if (lane < 16) misc[kMPref + lane] = static_cast<uint32_t>(incl - cw);
   for (int u = lane; u <= nu; u += kWave) misc[kMUmask + u] = u == nu ? (1u << T) - 1u : 0u;
   if (lane < T) ((__attribute__((address_space(3))) uint8_t*)(misc + kMUrank))[nu * kMaxT + lane] = static_cast<uint8_t>(k);
   if (lane == 0) misc[kMNU] = static_cast<uint32_t>(nu);
   wave_sync_lds();
+  // every choice (t, r): its unit's token mask, rank and blob offset (a unit
+  // chosen by several tokens writes the same offset several times)
   for (int i = lane; i < T * k; i += kWave) {
     const int t = i / k, r = i - t * k;
     const int e = static_cast<int>(misc[kMIds + t * kMaxK + r]);
@@ -287,6 +290,7 @@ __device__ __forceinline__ void dispatch_t(const StackTArgs& a, const TLds& S, u
     const int u = static_cast<int>(misc[kMPref + (e >> 5)]) + __popc(w & ((1u << (e & 31)) - 1u));
     __hip_atomic_fetch_or(misc + kMUmask + u, 1u << t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     ((__attribute__((address_space(3))) uint8_t*)(misc + kMUrank))[u * kMaxT + t] = static_cast<uint8_t>(r);
+    ((lds_i64*)(misc + kMUoff))[u] = slot[e];
     if (b == 0) {
       const size_t o = (static_cast<size_t>(l) * T + t) * k + r;
       if (a.ids_out) a.ids_out[o] = e;
@@ -297,59 +301,61 @@ __device__ __forceinline__ void dispatch_t(const StackTArgs& a, const TLds& S, u
   // the block's share of the gate/up pairs (units 0..U-1, 512 pairs each) and
   // of the down passes (units 0..U, 512 passes each), equal in cost
   int rng[4];
-#pragma unroll
-  for (int d = 0; d < 2; ++d) {
-    const int nun = d == 0 ? nu : nu + 1;
-    const int base = d == 0 ? kCostG : kCostD;
-    // lane i: units 2i and 2i + 1
+  {
+    // lane i: units 2i and 2i + 1, gate/up (d = 0) and down (d = 1) costs
     const int ua = 2 * lane, ub = 2 * lane + 1;
-    const int ca = ua < nun ? base + __popc(misc[kMUmask + ua]) : 0;
-    const int cb = ub < nun ? base + __popc(misc[kMUmask + ub]) : 0;
-    int incl = ca + cb;
+    const int ma = ua <= nu ? __popc(misc[kMUmask + ua]) : 0, mb = ub <= nu ? __popc(misc[kMUmask + ub]) : 0;
+    int ca[2], cb[2], inc[2];
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int v = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += v;
+    for (int d = 0; d < 2; ++d) {
+      const int nun = d == 0 ? nu : nu + 1;
+      const int base = d == 0 ? kCostG : kCostD;
+      ca[d] = ua < nun ? base + ma : 0;
+      cb[d] = ub < nun ? base + mb : 0;
+      inc[d] = wave_scan_incl(ca[d] + cb[d]);
     }
-    const int total = __shfl(incl, kWave - 1, kWave);
-    const int pa = (incl - ca - cb) * 512, pb = pa + ca * 512;   // cost before units ua and ub
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int bb = b + e;
-      int q = nun * 512;                                          // the end, for bb = 256
-      if (bb < kNB) {
-        const int B = static_cast<int>((static_cast<int64_t>(total) * 512 * bb) / kNB);
-        int cand = -1;
-        if (ca > 0 && pa <= B && B < pa + 512 * ca) cand = ua * 512 + (B - pa + ca - 1) / ca;
-        if (cb > 0 && pb <= B && B < pb + 512 * cb) cand = ub * 512 + (B - pb + cb - 1) / cb;
-        const uint64_t hit = __ballot(cand >= 0);
-        q = __shfl(cand, static_cast<int>(__builtin_ctzll(hit)), kWave);
+    for (int d = 0; d < 2; ++d) {
+      const int nun = d == 0 ? nu : nu + 1;
+      const int total = __builtin_amdgcn_readlane(inc[d], kWave - 1);
+      const int pa = (inc[d] - ca[d] - cb[d]) * 512, pb = pa + ca[d] * 512;   // cost before units ua and ub
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int bb = b + e;
+        int q = nun * 512;                                          // the end, for bb = 256
+        if (bb < kNB) {
+          const int B = static_cast<int>((static_cast<int64_t>(total) * 512 * bb) / kNB);
+          int cand = -1;
+          if (ca[d] > 0 && pa <= B && B < pa + 512 * ca[d]) cand = ua * 512 + (B - pa + ca[d] - 1) / ca[d];
+          if (cb[d] > 0 && pb <= B && B < pb + 512 * cb[d]) cand = ub * 512 + (B - pb + cb[d] - 1) / cb[d];
+          const uint64_t hit = __ballot(cand >= 0);
+          q = __builtin_amdgcn_readlane(cand, static_cast<int>(__builtin_ctzll(hit)));
+        }
+        rng[2 * d + e] = q;
       }
-      rng[2 * d + e] = q;
     }
   }
   if (lane < 4) misc[kMRange + lane] = static_cast<uint32_t>(lane == 0 ? rng[0] : lane == 1 ? rng[1] : lane == 2 ? rng[2] : rng[3]);
-  if (lane == 0) {
-    // the h rows of the down range's units: routed rows by (token, rank), the
-    // shared unit's by token
+  // the h rows of the down range's units (at most two): routed rows by
+  // (token, rank), the shared unit's by token; lane s 8 + t takes token t of
+  // the range's unit s
+  {
     const int r0 = kRpp * rng[2], r1 = kRpp * rng[3];
     const int u0 = r0 / kH, u1 = r1 > r0 ? (r1 - 1) / kH : u0;
-    int j = 0;
-    for (int s = 0; s < 2; ++s) {
+    const bool any = r1 > r0 && u0 <= nu, two = any && u1 != u0 && u1 <= nu;
+    const uint32_t m0 = any ? misc[kMUmask + u0] : 0u, m1 = two ? misc[kMUmask + u1] : 0u;
+    if (lane < 2 * kMaxT) {
+      const int s = lane / kMaxT, t = lane % kMaxT;
       const int u = s == 0 ? u0 : u1;
-      if (s == 1 && u1 == u0) break;
-      if (r1 == r0 || u > nu) break;
-      uint32_t m = misc[kMUmask + u];
-      while (m != 0u) {
-        const int t = __builtin_ctz(m);
-        m &= m - 1u;
+      const uint32_t ms = s == 0 ? m0 : m1;
+      if ((ms >> t) & 1u) {
+        const int j = (s == 1 ? __popc(m0) : 0) + __popc(ms & ((1u << t) - 1u));
         misc[kMHSrc + j] = u == nu ? static_cast<uint32_t>(kTSh + (size_t(p) * kMaxT + t) * kI)
                                    : static_cast<uint32_t>(kTHu + (size_t(t) * k + unit_rank(misc, u, t)) * kI);
         misc[kMHJ + s * kMaxT + t] = static_cast<uint32_t>(j);
-        ++j;
       }
     }
-    misc[kMNH] = static_cast<uint32_t>(j);
+    if (lane == 0) misc[kMNH] = static_cast<uint32_t>(__popc(m0) + __popc(m1));
   }
 }
 
