@@ -13,14 +13,13 @@
 // A row is read once per layer and used for every token that routes to its
 // unit.
 // Per layer:
-//   R  the block's router rows and shared gate/up pairs for every token
-//      (block 0 also sigma(g . x_t)); logits and shared h go out as tagged
-//      words
+//   R  the block's router rows and shared gate/up pairs for every token;
+//      logits and shared h go out as tagged words
 //   K  every block reads the T E logits; wave t takes token t's top-k and
 //      renormalised weights; wave 0 then forms the unit list (a bitmap of the
 //      chosen ids), each unit's tokens and their ranks, and the h rows its
 //      down range needs; meanwhile waves 1..7 read the previous layer's row
-//      sums of the block's 8 output rows
+//      sums of the block's 8 output rows (and on block 0 form sigma(g . x_t))
 //   G  all eight waves stream the block's gate/up pairs (batches of two, of
 //      one unit, in a three-deep ring) and store h per (token, rank) as
 //      tagged words; wave 7 first finishes the previous layer's 8 output
@@ -483,9 +482,9 @@ __global__ __launch_bounds__(kThr) void k_decode_stack_t(StackTArgs a) {
       // items of two tokens each (their chains side by side); an odd last
       // item repeats its token and stores once
       const int ntp = (T + 1) / 2;
-      const int nr = a.rpb * ntp, ns = kSpb * ntp, ng = b == 0 ? T : 0;
-      for (int i = wave; i < nr + ns + ng; i += kNW) {
-        if (i < nr + ns) {
+      const int nr = a.rpb * ntp, ns = kSpb * ntp;
+      for (int i = wave; i < nr + ns; i += kNW) {
+        {
           const bool router = i < nr;
           const int q = router ? i : i - nr;
           const int j = q / ntp, tp = q - j * ntp;
@@ -541,20 +540,6 @@ __global__ __launch_bounds__(kThr) void k_decode_stack_t(StackTArgs a) {
               if (t1 != t0) store_tag(shw + static_cast<size_t>(t1) * kI + r, __float_as_uint(h1), tag);
             }
           }
-        } else {
-          // block 0: sigmoid(g . x_t)
-          const int t = i - nr - ns;
-          ActRaw<kBF16> xr, gw;
-          load_lds_act_bf16(X + t * kH * 2, lane, xr);
-          load_lds_act_bf16(P + S.p_gv, lane, gw);
-          float xv[kSegCodes], gv[kSegCodes];
-          act_raw_f32<kBF16>(xr, xv);
-          act_raw_f32<kBF16>(gw, gv);
-          float acc = 0.f;
-#pragma unroll
-          for (int c = 0; c < kSegCodes; ++c) acc = fmaf(xv[c], gv[c], acc);
-          acc = group_sum(acc, kWave);
-          if (lane == 0) misc[kMSig + t] = __float_as_uint(sigmoid(acc));
         }
       }
     }
@@ -602,6 +587,23 @@ __global__ __launch_bounds__(kThr) void k_decode_stack_t(StackTArgs a) {
       bool r = true;
       if (l > 0 && !dead) r = finish_read_t(a, S, lds, l - 1, tag - 1u, tid - kWave);
       if (lane == 0) misc[kMRd + wave] = r ? 1u : 0u;
+      // block 0: sigmoid(g . x_t) of this layer's tokens (stored with the row
+      // sums at the end of the layer), here rather than in phase R so that
+      // block 0's logits are not later than the others'
+      if (b == 0)
+        for (int t = wave - 1; t < T; t += kNW - 1) {
+          ActRaw<kBF16> xr, gw;
+          load_lds_act_bf16(X + t * kH * 2, lane, xr);
+          load_lds_act_bf16(P + S.p_gv, lane, gw);
+          float xv[kSegCodes], gv[kSegCodes];
+          act_raw_f32<kBF16>(xr, xv);
+          act_raw_f32<kBF16>(gw, gv);
+          float acc = 0.f;
+#pragma unroll
+          for (int c = 0; c < kSegCodes; ++c) acc = fmaf(xv[c], gv[c], acc);
+          acc = group_sum(acc, kWave);
+          if (lane == 0) misc[kMSig + t] = __float_as_uint(sigmoid(acc));
+        }
     }
     __syncthreads();
     dead = dead || !reads_ok_w(misc, 1, kNW);
