@@ -25,6 +25,12 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// The float behind an order key (both zeros come back as +0, which leaves
+// every difference taken with it unchanged; a NaN comes back as a NaN).
+__device__ __forceinline__ float key_float(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
 __device__ __forceinline__ uint64_t lane_mask_lt(int lane) { return lane == 0 ? 0ull : (~0ull >> (64 - lane)); }
 
 // The value of lane (lane ^ S) within the wave, by lane moves (DPP, a
@@ -74,7 +80,7 @@ __device__ __forceinline__ void wave_sync_lds() {
 // ---------------------------------------------------------------------------
 // Top-k of one token on one wave.
 //  1. A threshold from the per-lane maxima: the k-th largest lane maximum,
-//     found on the top 16 bits of the order key two bits a step (three
+//     found on the top 14 bits of the order key two bits a step (three
 //     independent ballots per step), is a lower bound of the k-th largest
 //     logit, so every top-k logit is at or above it.
 //  2. The candidates at or above it (usually a few more than k) are packed as
@@ -115,11 +121,12 @@ __device__ __forceinline__ int topk_wave_n(const float* lg_, int E, int k, int l
     key[j] = e < E ? (kv > 1u ? kv : 1u) : 0u;   // every real entry ranks above "no entry"
     lm = key[j] > lm ? key[j] : lm;
   }
-  // the largest theta (top 16 bits) with at least k lane maxima at or above
+  // the largest theta (top 14 bits: sign, exponent and five mantissa bits,
+  // candidates within about 3% of the bound) with at least k lane maxima at or above
   // it; a step settles two bits from the counts at three thresholds
   uint32_t theta = 0;
 #pragma unroll
-  for (int b = 30; b >= 16; b -= 2) {
+  for (int b = 30; b >= 18; b -= 2) {
     const uint32_t c1 = theta | (1u << b), c2 = theta | (2u << b), c3 = theta | (3u << b);
     const unsigned n1 = __popcll(__ballot(lm >= c1)), n2 = __popcll(__ballot(lm >= c2)),
                    n3 = __popcll(__ballot(lm >= c3));
@@ -167,7 +174,7 @@ __device__ __forceinline__ int topk_wave_n(const float* lg_, int E, int k, int l
     float val = 0.f;
     if (cd && rank < k) {
       ids[rank] = id;
-      val = lg[id];
+      val = key_float(static_cast<uint32_t>(mine >> 32));   // the logit, from its key
     }
     const int dst = 4 * (cd ? rank : lane);
     v = __int_as_float(__builtin_amdgcn_ds_permute(dst, __float_as_int(val)));
@@ -200,7 +207,15 @@ __device__ __forceinline__ int topk_wave_n(const float* lg_, int E, int k, int l
   const float top = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
   const float ex = lane < k ? expf(v - top) : 0.f;
   float sum = 0.f;
-  for (int i = 0; i < k; ++i) sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), i));
+  if (k <= 16) {
+    // fixed lanes, no branches: lanes k..15 hold +0, and adding +0 to a sum
+    // of non-negative terms leaves it unchanged, so the sum is the one in
+    // rank order; the reads are independent, only the adds are chained
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), i));
+  } else {
+    for (int i = 0; i < k; ++i) sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), i));
+  }
   if (lane < k) vals[lane] = ex / sum;
   return myid;
 }
