@@ -293,6 +293,7 @@ struct PfArgs {
   int T, k, H, E, I, SI, hs;
   int n_rt;                // blocks per tile in this launch
   int n_g;                 // down: 256-row blocks per block
+  int slots_x;             // blocks resident at once on one XCD (0: no half blocks)
 };
 
 struct Tile {
@@ -308,16 +309,31 @@ struct Tile {
 // each XCD has its own L2.  Blocks are renumbered so that XCD x runs a
 // contiguous range of (tile, row block) pairs in order: the row blocks of one
 // tile then run on one XCD at about the same time and read the tile's
-// activations through the same L2.  The grid is a multiple of kXcds blocks
-// with at least meta[0] * n_rt of them; the spare ones return at once.
+// activations through the same L2.  An XCD holds slots_x blocks at once, so
+// the last (per mod slots_x) pairs of its range would run as a part-empty
+// round; when that is at most half a round they run instead as twice as many
+// half blocks (half = 0, 1; -1 for a whole block), which halves that round's
+// length.  The grid is a multiple of kXcds blocks with at least
+// kXcds (per + slots_x) of them; the spare ones return at once.
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ bool block_map(const PfArgs& a, int* ti, int* rb) {
+__device__ __forceinline__ bool block_map(const PfArgs& a, int* ti, int* rb, int* half) {
   const int nb = a.meta[0] * a.n_rt;
   const int per = (nb + kXcds - 1) / kXcds;
   const int idx = blockIdx.x / kXcds;
-  if (idx >= per) return false;
-  const int logical = (blockIdx.x % kXcds) * per + idx;
+  const int tail = a.slots_x > 0 && per % a.slots_x <= a.slots_x / 2 ? per % a.slots_x : 0;
+  const int full = per - tail;
+  int item;
+  if (idx < full) {
+    item = idx;
+    *half = -1;
+  } else if (idx < full + 2 * tail) {
+    item = full + (idx - full) / 2;
+    *half = (idx - full) % 2;
+  } else {
+    return false;
+  }
+  const int logical = (blockIdx.x % kXcds) * per + item;
   if (logical >= nb) return false;
   *ti = logical / a.n_rt;
   *rb = logical % a.n_rt;
@@ -702,8 +718,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
   __shared__ int s_pair[kChunk], s_tok[kChunk];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
-  int ti, rb;
-  if (!block_map(a, &ti, &rb)) return;
+  int ti, rb, half;
+  if (!block_map(a, &ti, &rb, &half)) return;
   Tile tl;
   if (!tile_of<BITS, SB>(a, ti, &tl)) return;
   const int rows = tl.rows_or_k;
@@ -721,182 +737,189 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_gateup(PfArgs a) {
   constexpr int sbsz = SB == kF32 ? 4 : 2;
   const int rbytes = a.H * BITS / 8;
   const int sbrow = (a.H / 64) * sbsz;
-  const int wrow = rb * kGuRows + w * 32;                       // first row of the wave (uniform)
   const int lrow = 8 * (r >> 3) + slot_k<BITS>(r & 7);          // this lane's row inside a 16-row block
   const LaneOffsets lo = lane_offsets<BITS, SB>(lrow, rbytes, sbrow, q);
-  BlockOffsets bo[2][2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int row = wrow + 16 * rr;
-      bo[m][rr] = {static_cast<int>(m * P.q) + row * rbytes, static_cast<int>(3 * P.q + m * P.s) + row * sbrow,
-                   static_cast<int>(3 * P.q + (3 + m) * P.s) + row * sbrow};
-    }
-  __syncthreads();   // s_tok ready
-  const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(a.x16) +
-                        static_cast<size_t>(s_tok[lane < n ? lane : 0]) * a.H * 2 + w * 8 * 16;
-  // int4 with bf16 scales: activations staged as row pairs (whole lines per
-  // direct load)
-  const u32x4 xrs = raw_rsrc(a.x16, static_cast<int64_t>(a.T) * a.H * 2);
-  const u32x4 rsa = raw_rsrc(tl.blob, P.blob);
-  PairOffs xo;
-  if constexpr (kLsb)
-    xo = pair_offsets(w, lane, [&](int row) {
-      return static_cast<uint32_t>(s_tok[row < n ? row : 0]) * static_cast<uint32_t>(a.H * 2);
-    });
-  const PairRead prd = pair_read(r, q);
-  auto stage_x = [&](int ks, uint8_t* stage) {
-    if constexpr (kLsb) stage_pairs(xrs, xo, ks, stage, w);
-    else stage_slice(xsrc, ks, stage, w);
-  };
-  auto load_w = [&](StepW<BITS> (&dst)[2][2], int kb) {
+  // RR 16-row MFMA blocks of gate and of up per wave: 2 for a whole block of
+  // 128 rows, 1 for a half block (rows 64 half .. +64 of the row block)
+  auto body = [&](auto rrc) {
+    constexpr int RR = decltype(rrc)::value;
+    const int wrow = rb * kGuRows + (half < 0 ? 0 : 64 * half) + w * 16 * RR;   // first row of the wave (uniform)
+    BlockOffsets bo[2][RR];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr) load_step<BITS, SB>(dst[m][rr], rs, lo, bo[m][rr], kb);
-  };
-  auto load_w2 = [&](StepW<BITS> (&d0)[2][2], StepW<BITS> (&d1)[2][2], int kb) {
-    if constexpr (kLsb) {
+      for (int rr = 0; rr < RR; ++rr) {
+        const int row = wrow + 16 * rr;
+        bo[m][rr] = {static_cast<int>(m * P.q) + row * rbytes, static_cast<int>(3 * P.q + m * P.s) + row * sbrow,
+                     static_cast<int>(3 * P.q + (3 + m) * P.s) + row * sbrow};
+      }
+    __syncthreads();   // s_tok ready
+    const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(a.x16) +
+                          static_cast<size_t>(s_tok[lane < n ? lane : 0]) * a.H * 2 + w * 8 * 16;
+    // int4 with bf16 scales: activations staged as row pairs (whole lines per
+    // direct load)
+    const u32x4 xrs = raw_rsrc(a.x16, static_cast<int64_t>(a.T) * a.H * 2);
+    const u32x4 rsa = raw_rsrc(tl.blob, P.blob);
+    PairOffs xo;
+    if constexpr (kLsb)
+      xo = pair_offsets(w, lane, [&](int row) {
+        return static_cast<uint32_t>(s_tok[row < n ? row : 0]) * static_cast<uint32_t>(a.H * 2);
+      });
+    const PairRead prd = pair_read(r, q);
+    auto stage_x = [&](int ks, uint8_t* stage) {
+      if constexpr (kLsb) stage_pairs(xrs, xo, ks, stage, w);
+      else stage_slice(xsrc, ks, stage, w);
+    };
+    auto load_w = [&](StepW<BITS> (&dst)[2][RR], int kb) {
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr) load_codes4(d0[m][rr], d1[m][rr], rs, lo, bo[m][rr], kb);
-    } else if constexpr (BITS == 4) {
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) load_slice4<SB>(d0[m][rr], d1[m][rr], rs, lo, bo[m][rr], kb);
-    }
-  };
-  // the wave's 32 rows' scale and bias words of the slice at kb: lane l
-  // copies word l % 2 of row l / 2 of one plane
-  const uint32_t sb_lane = static_cast<uint32_t>((lane >> 1) * sbrow + 4 * (lane & 1));
-  auto stage_sb = [&](int kb, uint8_t* stage) {
-    if constexpr (kLsb) {
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          const int soff = static_cast<int>(3 * P.q + (sb ? 3 + m : m) * P.s) + wrow * sbrow + (kb / 64) * 2;
-          lds_load<4>(rsa, stage + kStageBytes + w * kSbWave + (2 * m + sb) * 256, sb_lane, soff);
-        }
-    }
-  };
-  with_nt((n + 15) / 16, [&](auto ntc) {
-    constexpr int NT = decltype(ntc)::value;
-    f4v acc[2][2][NT];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr)
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct) acc[m][rr][ct] = f4v{0.f, 0.f, 0.f, 0.f};
-    // One 128-k step S (0 or 1) of the slice staged in `stage`.
-    auto mult = [&](int S, const uint8_t* stage, const StepW<BITS> (&wv)[2][2]) {
-      h2v sc[2][2], bc[2][2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-          if constexpr (kLsb) {
-            const uint8_t* sw = stage + kStageBytes + w * kSbWave + 2 * m * 256 + (16 * rr + lrow) * 8;
-            const uint2 sv = *reinterpret_cast<const uint2*>(sw), bv = *reinterpret_cast<const uint2*>(sw + 256);
-            sc[m][rr] = splat_h2(sb_value<SB>(S ? sv.y : sv.x, lo.sel));
-            bc[m][rr] = splat_h2(sb_value<SB>(S ? bv.y : bv.x, lo.sel));
-          } else {
-            sc[m][rr] = splat_h2(sb_value<SB>(wv[m][rr].s, lo.sel));
-            bc[m][rr] = splat_h2(sb_value<SB>(wv[m][rr].b, lo.sel));
-          }
-        }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        h8v B[NT];
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct)
-          B[ct] = kLsb ? stage_b_pair(stage, prd, S, j, ct) : stage_b(stage, S, j, ct, r, q);
+        for (int rr = 0; rr < RR; ++rr) load_step<BITS, SB>(dst[m][rr], rs, lo, bo[m][rr], kb);
+    };
+    auto load_w2 = [&](StepW<BITS> (&d0)[2][RR], StepW<BITS> (&d1)[2][RR], int kb) {
+      if constexpr (kLsb) {
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-          for (int rr = 0; rr < 2; ++rr) {
-            const h8v A = step_operand<BITS>(wv[m][rr], j, sc[m][rr], bc[m][rr], magic_v);
+          for (int rr = 0; rr < RR; ++rr) load_codes4(d0[m][rr], d1[m][rr], rs, lo, bo[m][rr], kb);
+      } else if constexpr (BITS == 4) {
 #pragma unroll
-            for (int ct = 0; ct < NT; ++ct) acc[m][rr][ct] = mfma16(A, B[ct], acc[m][rr][ct]);
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int rr = 0; rr < RR; ++rr) load_slice4<SB>(d0[m][rr], d1[m][rr], rs, lo, bo[m][rr], kb);
+      }
+    };
+    // the wave's 32 rows' scale and bias words of the slice at kb: lane l
+    // copies word l % 2 of row l / 2 of one plane
+    const uint32_t sb_lane = static_cast<uint32_t>((lane >> 1) * sbrow + 4 * (lane & 1));
+    auto stage_sb = [&](int kb, uint8_t* stage) {
+      if constexpr (kLsb) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb) {
+            const int soff = static_cast<int>(3 * P.q + (sb ? 3 + m : m) * P.s) + wrow * sbrow + (kb / 64) * 2;
+            lds_load<4>(rsa, stage + kStageBytes + w * kSbWave + (2 * m + sb) * 256, sb_lane, soff);
           }
       }
     };
-    if constexpr (BITS == 4) {
-      // int4: a 128-k step is half of each row's 128-byte line; both steps of
-      // the next slice are requested together so that lines are fetched whole.
-      // The two register sets alternate roles from slice to slice.
-      StepW<BITS> wa[2][2], wa2[2][2], wb[2][2], wb2[2][2];
-      const int nsl = a.H / kSlice;
-      auto slice = [&](int sl, const uint8_t* cur, uint8_t* nxt, const StepW<BITS> (&c1)[2][2],
-                       const StepW<BITS> (&c2)[2][2], StepW<BITS> (&n1)[2][2], StepW<BITS> (&n2)[2][2]) {
-        const bool more = sl + 1 < nsl;
-        if (more) {
-          stage_x((sl + 1) * kSlice, nxt);
-          stage_sb((sl + 1) * kSlice, nxt);
-          load_w2(n1, n2, (sl + 1) * kSlice);
-        }
-        mult(0, cur, c1);
-        mult(1, cur, c2);
-        stage_barrier();
-      };
-      stage_x(0, xs0);
-      stage_sb(0, xs0);
-      load_w2(wa, wa2, 0);
-      stage_barrier();
-      for (int sl = 0; sl < nsl; sl += 2) {
-        slice(sl, xs0, xs1, wa, wa2, wb, wb2);
-        if (sl + 1 < nsl) slice(sl + 1, xs1, xs0, wb, wb2, wa, wa2);
-      }
-    } else {
-      // int8: one 128-k step already covers whole lines; prefetch one step
-      // ahead, alternating two register sets.  The number of steps is even.
-      StepW<BITS> wa[2][2], wb[2][2];
-      const int nst = a.H / 128;
-      auto step = [&](int st, int S, const uint8_t* cur, uint8_t* nxt, const StepW<BITS> (&cw)[2][2],
-                      StepW<BITS> (&nw)[2][2]) {
-        if (S == 0 && st + 2 < nst) stage_slice(xsrc, (st + 2) * 128, nxt, w);
-        if (st + 1 < nst) load_w(nw, (st + 1) * 128);
-        mult(S, cur, cw);
-        if (S == 1) stage_barrier();
-      };
-      stage_slice(xsrc, 0, xs0, w);
-      load_w(wa, 0);
-      stage_barrier();
-      for (int st = 0; st < nst; st += 4) {
-        step(st, 0, xs0, xs1, wa, wb);
-        step(st + 1, 1, xs0, xs1, wb, wa);
-        if (st + 2 < nst) {
-          step(st + 2, 0, xs1, xs0, wa, wb);
-          step(st + 3, 1, xs1, xs0, wb, wa);
-        }
-      }
-    }
-    // h = silu(gate) * up, float16, four consecutive slots per lane
+    with_nt((n + 15) / 16, [&](auto ntc) {
+      constexpr int NT = decltype(ntc)::value;
+      f4v acc[2][RR][NT];
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      const int c = 16 * ct + r;
-      if (c < n) {
-        _Float16* hr = a.h + static_cast<size_t>(s_pair[c]) * a.hs;
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-          const int g8 = (wrow + 16 * rr) / 8 + (q >> 1);
-          uint32_t o[2];
+        for (int rr = 0; rr < RR; ++rr)
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const _Float16 h0 = static_cast<_Float16>(silu(acc[0][rr][ct][2 * i]) * acc[1][rr][ct][2 * i]);
-            const _Float16 h1 = static_cast<_Float16>(silu(acc[0][rr][ct][2 * i + 1]) * acc[1][rr][ct][2 * i + 1]);
-            o[i] = h2_bits(h2v{h0, h1});
+          for (int ct = 0; ct < NT; ++ct) acc[m][rr][ct] = f4v{0.f, 0.f, 0.f, 0.f};
+      // One 128-k step S (0 or 1) of the slice staged in `stage`.
+      auto mult = [&](int S, const uint8_t* stage, const StepW<BITS> (&wv)[2][RR]) {
+        h2v sc[2][RR], bc[2][RR];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int rr = 0; rr < RR; ++rr) {
+            if constexpr (kLsb) {
+              const uint8_t* sw = stage + kStageBytes + w * kSbWave + 2 * m * 256 + (16 * rr + lrow) * 8;
+              const uint2 sv = *reinterpret_cast<const uint2*>(sw), bv = *reinterpret_cast<const uint2*>(sw + 256);
+              sc[m][rr] = splat_h2(sb_value<SB>(S ? sv.y : sv.x, lo.sel));
+              bc[m][rr] = splat_h2(sb_value<SB>(S ? bv.y : bv.x, lo.sel));
+            } else {
+              sc[m][rr] = splat_h2(sb_value<SB>(wv[m][rr].s, lo.sel));
+              bc[m][rr] = splat_h2(sb_value<SB>(wv[m][rr].b, lo.sel));
+            }
           }
-          if (f16_bad(o[0]) || f16_bad(o[1])) raise_error(a.flags, kErrF16);
-          *reinterpret_cast<uint2*>(hr + 8 * chunk_of(g8) + 4 * (q & 1)) = make_uint2(o[0], o[1]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          h8v B[NT];
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct)
+            B[ct] = kLsb ? stage_b_pair(stage, prd, S, j, ct) : stage_b(stage, S, j, ct, r, q);
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int rr = 0; rr < RR; ++rr) {
+              const h8v A = step_operand<BITS>(wv[m][rr], j, sc[m][rr], bc[m][rr], magic_v);
+#pragma unroll
+              for (int ct = 0; ct < NT; ++ct) acc[m][rr][ct] = mfma16(A, B[ct], acc[m][rr][ct]);
+            }
+        }
+      };
+      if constexpr (BITS == 4) {
+        // int4: a 128-k step is half of each row's 128-byte line; both steps of
+        // the next slice are requested together so that lines are fetched whole.
+        // The two register sets alternate roles from slice to slice.
+        StepW<BITS> wa[2][RR], wa2[2][RR], wb[2][RR], wb2[2][RR];
+        const int nsl = a.H / kSlice;
+        auto slice = [&](int sl, const uint8_t* cur, uint8_t* nxt, const StepW<BITS> (&c1)[2][RR],
+                         const StepW<BITS> (&c2)[2][RR], StepW<BITS> (&n1)[2][RR], StepW<BITS> (&n2)[2][RR]) {
+          const bool more = sl + 1 < nsl;
+          if (more) {
+            stage_x((sl + 1) * kSlice, nxt);
+            stage_sb((sl + 1) * kSlice, nxt);
+            load_w2(n1, n2, (sl + 1) * kSlice);
+          }
+          mult(0, cur, c1);
+          mult(1, cur, c2);
+          stage_barrier();
+        };
+        stage_x(0, xs0);
+        stage_sb(0, xs0);
+        load_w2(wa, wa2, 0);
+        stage_barrier();
+        for (int sl = 0; sl < nsl; sl += 2) {
+          slice(sl, xs0, xs1, wa, wa2, wb, wb2);
+          if (sl + 1 < nsl) slice(sl + 1, xs1, xs0, wb, wb2, wa, wa2);
+        }
+      } else {
+        // int8: one 128-k step already covers whole lines; prefetch one step
+        // ahead, alternating two register sets.  The number of steps is even.
+        StepW<BITS> wa[2][RR], wb[2][RR];
+        const int nst = a.H / 128;
+        auto step = [&](int st, int S, const uint8_t* cur, uint8_t* nxt, const StepW<BITS> (&cw)[2][RR],
+                        StepW<BITS> (&nw)[2][RR]) {
+          if (S == 0 && st + 2 < nst) stage_slice(xsrc, (st + 2) * 128, nxt, w);
+          if (st + 1 < nst) load_w(nw, (st + 1) * 128);
+          mult(S, cur, cw);
+          if (S == 1) stage_barrier();
+        };
+        stage_slice(xsrc, 0, xs0, w);
+        load_w(wa, 0);
+        stage_barrier();
+        for (int st = 0; st < nst; st += 4) {
+          step(st, 0, xs0, xs1, wa, wb);
+          step(st + 1, 1, xs0, xs1, wb, wa);
+          if (st + 2 < nst) {
+            step(st + 2, 0, xs1, xs0, wa, wb);
+            step(st + 3, 1, xs1, xs0, wb, wa);
+          }
         }
       }
-    }
-  });
+      // h = silu(gate) * up, float16, four consecutive slots per lane
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
+        const int c = 16 * ct + r;
+        if (c < n) {
+          _Float16* hr = a.h + static_cast<size_t>(s_pair[c]) * a.hs;
+#pragma unroll
+          for (int rr = 0; rr < RR; ++rr) {
+            const int g8 = (wrow + 16 * rr) / 8 + (q >> 1);
+            uint32_t o[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const _Float16 h0 = static_cast<_Float16>(silu(acc[0][rr][ct][2 * i]) * acc[1][rr][ct][2 * i]);
+              const _Float16 h1 = static_cast<_Float16>(silu(acc[0][rr][ct][2 * i + 1]) * acc[1][rr][ct][2 * i + 1]);
+              o[i] = h2_bits(h2v{h0, h1});
+            }
+            if (f16_bad(o[0]) || f16_bad(o[1])) raise_error(a.flags, kErrF16);
+            *reinterpret_cast<uint2*>(hr + 8 * chunk_of(g8) + 4 * (q & 1)) = make_uint2(o[0], o[1]);
+          }
+        }
+      }
+    });
+  };
+  if (half < 0) body(IntC<2>{});
+  else body(IntC<1>{});
 }
 
 // Down: block = (tile, n_g consecutive 256-row blocks of H); wave w owns
@@ -919,13 +942,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_pf_down(PfArgs a) {
   __shared__ int s_pair[kChunk], s_tok[kChunk];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
-  int ti, rb;
-  if (!block_map(a, &ti, &rb)) return;
+  int ti, rb, half;
+  if (!block_map(a, &ti, &rb, &half)) return;
   Tile tl;
   if (!tile_of<BITS, SB>(a, ti, &tl)) return;
   const int K = tl.rows_or_k;
   const int n = tl.n;
-  const int G = a.n_g;
+  // a half block is one of the n_g = 2 row blocks (rb counts row blocks then)
+  const int G = half < 0 ? a.n_g : 1;
+  if (half >= 0) rb = rb * a.n_g + half;
   tile_pairs(a, tl, tid, s_pair, s_tok);
   __syncthreads();
   const int r = lane & 15, q = lane >> 4;
@@ -1156,10 +1181,24 @@ int launch_prefill_router(const Call& c, int32_t* ids2, float* wts2) {
 }
 
 // Blocks for up to max_tiles tiles of n_rt row blocks, rounded up to a
-// multiple of the XCD count (see block_map).
-static unsigned xcd_grid(int max_tiles, int n_rt) {
+// multiple of the XCD count, plus room for the half blocks (see block_map).
+static unsigned xcd_grid(int max_tiles, int n_rt, int slots_x) {
   const unsigned nb = static_cast<unsigned>(max_tiles) * n_rt;
-  return (nb + kXcds - 1) / kXcds * kXcds;
+  return (nb + kXcds - 1) / kXcds * kXcds + kXcds * static_cast<unsigned>(slots_x);
+}
+
+// Blocks of a prefill GEMM kernel resident at once on one XCD (two per CU),
+// per device; 0 if the device cannot be queried.
+static int xcd_slots() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < kXcds) return 0;
+    cached[dev] = 2 * cus / kXcds;
+  }
+  return cached[dev];
 }
 
 template <int BITS, int SB>
@@ -1167,10 +1206,14 @@ static void launch_tiles(const PfArgs& base, const Call& c) {
   const moe_desc& d = c.d;
   PfArgs a = base;
   a.n_rt = (d.inter > d.shared_inter ? d.inter : d.shared_inter) / kGuRows;
-  launch_kernel(k_pf_gateup<BITS, SB>, dim3(xcd_grid(c.L.max_tiles, a.n_rt)), dim3(kThreads), 0, c.stream, a);
+  a.slots_x = xcd_slots();
+  launch_kernel(k_pf_gateup<BITS, SB>, dim3(xcd_grid(c.L.max_tiles, a.n_rt, a.slots_x)), dim3(kThreads), 0,
+                c.stream, a);
   a.n_g = kLdsSb<BITS, SB> && (d.hidden / kDnRows) % kDownGroup == 0 ? kDownGroup : 1;
   a.n_rt = d.hidden / (kDnRows * a.n_g);
-  launch_kernel(k_pf_down<BITS, SB>, dim3(xcd_grid(c.L.max_tiles, a.n_rt)), dim3(kThreads), 0, c.stream, a);
+  a.slots_x = a.n_g == 2 ? xcd_slots() : 0;   // a half block is one of two row blocks
+  launch_kernel(k_pf_down<BITS, SB>, dim3(xcd_grid(c.L.max_tiles, a.n_rt, a.slots_x)), dim3(kThreads), 0,
+                c.stream, a);
 }
 
 int launch_prefill_experts(const Call& c) {
@@ -1205,6 +1248,7 @@ int launch_prefill_experts(const Call& c) {
   a.hs = L.hstride;
   a.n_rt = 1;
   a.n_g = 1;
+  a.slots_x = 0;
 
   const void* gvec = c.shared + d.shared_stride;
   int32_t* estart = reinterpret_cast<int32_t*>(ws + L.p_estart);
