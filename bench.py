@@ -809,9 +809,8 @@ def kernel_work(desc, geo, T, n_kernels, uniq, prefill, out_bytes, stack=False, 
         table = [
             ("k_pf_router", router * nl, 2.0 * T * E * H * nl),
             ("k_topk", None, None),
-            ("k_pf_gate", (gvec + T * H * act) * nl, None),
             ("k_pf_dispatch", None, None),
-            ("k_pf_xprep", T * H * act * nl, None),
+            ("k_pf_xprep", (gvec + T * H * act) * nl, None),   # also the shared-expert gates
             ("k_pf_gateup", 2 * p_s * nl + 2 * p_r * u, 4.0 * (pairs * I + T * SI) * H * nl),
             ("k_pf_down", p_s * nl + p_r * u, 2.0 * (pairs * I + T * SI) * H * nl),
             ("k_combine", out * nl, None),

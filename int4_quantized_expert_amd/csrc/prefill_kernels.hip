@@ -9,7 +9,6 @@
 //   k_pf_router    logits = x R^T on v_mfma_f32_16x16x32_bf16 (exact bf16
 //                  products, fp32 accumulation)
 //   (k_topk)       the staged path's per-token top-k and renormalisation
-//   k_pf_gate      sigmoid(g . x) per token, fp32
 //   k_pf_dispatch  each pair's place in its expert's list, the list starts
 //                  and a table of tiles of up to 64 pairs of one expert
 //   k_pf_xprep     x to float16, stored in the k order the MFMA operands use;
@@ -137,12 +136,10 @@ __device__ __forceinline__ bool f16_bad(uint32_t w) {
 __device__ __forceinline__ f4v mfma16(h8v a, h8v b, f4v c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
 // ---------------------------------------------------------------------------
-// Shared-expert gate sigmoid(g . x_t), one wave per token, fp32.
-__global__ __launch_bounds__(kThreads) void k_pf_gate(const void* __restrict__ x, const void* __restrict__ gvec,
-                                                     float* __restrict__ gate, int T, int H) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int t = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
-  if (t >= T) return;
+// Shared-expert gate sigmoid(g . x_t) of token t, on one wave, fp32 (the
+// staged path's order: a segment's FMA chain per lane, then the wave sum).
+__device__ __forceinline__ void pf_gate_token(const void* __restrict__ x, const void* __restrict__ gvec,
+                                              float* __restrict__ gate, int t, int H, int lane) {
   const uint8_t* xr = static_cast<const uint8_t*>(x) + static_cast<size_t>(t) * H * 2;
   float acc = 0.f;
   for (int sg = lane; sg < H / kSegCodes; sg += kWave) {
@@ -250,12 +247,16 @@ __global__ __launch_bounds__(kThreads) void k_pf_xprep(const uint16_t* __restric
                                                       int H, const int32_t* __restrict__ ids,
                                                       const int32_t* __restrict__ erank,
                                                       const int32_t* __restrict__ estart, int np,
-                                                      int32_t* __restrict__ plist, uint32_t* __restrict__ flags) {
+                                                      int32_t* __restrict__ plist, const void* __restrict__ gvec,
+                                                      float* __restrict__ gate, uint32_t* __restrict__ flags) {
   const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   for (size_t p = i; p < static_cast<size_t>(np); p += static_cast<size_t>(gridDim.x) * blockDim.x) {
     const int r = erank[p];
     if (r >= 0) plist[estart[ids[p]] + r] = static_cast<int32_t>(p);
   }
+  // the shared-expert gates: wave 0 of block b takes tokens b, b + grid, ...
+  if (threadIdx.x < kWave)
+    for (int t = blockIdx.x; t < T; t += gridDim.x) pf_gate_token(x, gvec, gate, t, H, threadIdx.x);
   const int g_row = H / 8;
   if (i >= static_cast<size_t>(T) * g_row) return;
   const size_t t = i / g_row;
@@ -1253,7 +1254,6 @@ int launch_prefill_experts(const Call& c) {
   const void* gvec = c.shared + d.shared_stride;
   int32_t* estart = reinterpret_cast<int32_t*>(ws + L.p_estart);
   int32_t* erank = reinterpret_cast<int32_t*>(ws + L.p_erank);
-  launch_kernel(k_pf_gate, dim3((c.T + 3) / 4), dim3(kThreads), 0, c.stream, c.x, gvec, gate, c.T, d.hidden);
   launch_kernel(k_pf_dispatch, dim3(1), dim3(kDispThreads), 0, c.stream, c.ids, c.T, d.top_k, d.n_experts, erank,
                 estart, const_cast<int32_t*>(a.ucount), const_cast<int32_t*>(a.uniq), const_cast<int32_t*>(a.ustart),
                 const_cast<int32_t*>(a.tstart), const_cast<int32_t*>(a.tile_u), const_cast<int32_t*>(a.meta), flags);
@@ -1265,10 +1265,10 @@ int launch_prefill_experts(const Call& c) {
   int32_t* plist = const_cast<int32_t*>(a.plist);
   if (d.bits == 4)
     launch_kernel(k_pf_xprep<4>, xgrid, dim3(kThreads), 0, c.stream, x, x16, c.T, d.hidden, c.ids,
-                  static_cast<const int32_t*>(erank), static_cast<const int32_t*>(estart), np, plist, a.flags);
+                  static_cast<const int32_t*>(erank), static_cast<const int32_t*>(estart), np, plist, gvec, gate, a.flags);
   else
     launch_kernel(k_pf_xprep<8>, xgrid, dim3(kThreads), 0, c.stream, x, x16, c.T, d.hidden, c.ids,
-                  static_cast<const int32_t*>(erank), static_cast<const int32_t*>(estart), np, plist, a.flags);
+                  static_cast<const int32_t*>(erank), static_cast<const int32_t*>(estart), np, plist, gvec, gate, a.flags);
   if (d.bits == 4 && d.sb_dtype == kBF16) launch_tiles<4, kBF16>(a, c);
   else if (d.bits == 4) launch_tiles<4, kF32>(a, c);
   else if (d.sb_dtype == kBF16) launch_tiles<8, kBF16>(a, c);
